@@ -1,0 +1,87 @@
+"""Occupancy-pinned split-KV plan (integer algorithm).
+
+Test infrastructure only (see ``oracle/__init__``).
+
+[T5] module docstring ("Split-KV scheduling is occupancy-pinned") and
+``plan_split_kv`` / ``SplitPlan``. In units of 128-key tiles:
+  * tiles_b = max(1, ceil(L_b / 128)), T = max_b tiles_b
+  * one wave of the (work items, q-row tiles, kv heads) grid holds
+    slots = max(1, cu_count * wg_per_cu // (h_k * n_q_tiles)) work items
+  * lo = max(min_chunk_tiles, ceil(T / max_splits)) caps chunks per sequence
+  * chunk = max(lo, ceil(T / force_splits)) when force_splits > 0;
+    else chunk = T when the batch alone fills the wave (num_seqs >= slots)
+    or max_splits == 1; else the smallest chunk >= lo whose chunk count
+    sum_b ceil(tiles_b / chunk) fits in ``slots``
+  * sequence b becomes work items (b, j*chunk, min((j+1)*chunk, tiles_b), j)
+    for j < ceil(tiles_b / chunk); n_splits[b] is that count
+  * work items are ordered longest first, ties keeping their order
+  * pad_to > 0 appends empty items (0, 0, 0, 0) up to pad_to entries.
+
+Errors (ValueError) where the page's asserts fire: pad_to below the number of
+work items, more chunks than max_splits. Also rejected here: an empty batch,
+negative lengths, non-positive sizes (the page never passes them).
+
+Pinned by tests/test_plan_oracle.py: hand-worked examples, the minimality of
+the chunk against a linear scan, coverage/contiguity of every sequence's
+chunks, the wave bound, the ordering and the padding.
+"""
+
+TILE_KEYS = 128
+
+
+def _ceil_div(a, b):
+    return -(-a // b)
+
+
+def plan_split_kv(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16, force_splits=0,
+                  min_chunk_tiles=1, pad_to=0):
+    """Returns (work list of (seq, tile_begin, tile_end, split_slot), n_splits
+    per sequence, chunk_tiles, slots)."""
+    seq_lens = [int(x) for x in seq_lens]
+    if not seq_lens:
+        raise ValueError("empty batch")
+    if any(x < 0 for x in seq_lens):
+        raise ValueError("negative sequence length")
+    if min(h_k, n_q_tiles, cu_count, wg_per_cu, max_splits, min_chunk_tiles) < 1:
+        raise ValueError("sizes must be positive")
+    if force_splits < 0 or pad_to < 0:
+        raise ValueError("force_splits and pad_to must be >= 0")
+
+    tiles = [max(1, _ceil_div(L, TILE_KEYS)) for L in seq_lens]
+    t_max = max(tiles)
+    slots = max(1, (cu_count * wg_per_cu) // (h_k * n_q_tiles))
+    lo = max(min_chunk_tiles, _ceil_div(t_max, max_splits))
+
+    def n_chunks(chunk):
+        return sum(_ceil_div(t, chunk) for t in tiles)
+
+    if force_splits > 0:
+        chunk = max(lo, _ceil_div(t_max, force_splits))
+    elif len(tiles) >= slots or max_splits == 1:
+        chunk = t_max
+    else:
+        # n_chunks is non-increasing in the chunk size: bisect for the
+        # smallest chunk in [lo, t_max] that fits one wave (t_max always fits
+        # here, since it gives one chunk per sequence and num_seqs < slots).
+        a, z = lo, t_max
+        while a < z:
+            mid = (a + z) // 2
+            if n_chunks(mid) <= slots:
+                z = mid
+            else:
+                a = mid + 1
+        chunk = a
+
+    work, n_splits = [], []
+    for b, t in enumerate(tiles):
+        k = _ceil_div(t, chunk)
+        n_splits.append(k)
+        work.extend((b, j * chunk, min((j + 1) * chunk, t), j) for j in range(k))
+    work.sort(key=lambda w: w[1] - w[2])  # longest first; sort is stable
+    if max(n_splits) > max_splits:
+        raise ValueError(f"{max(n_splits)} chunks exceed max_splits={max_splits}")
+    if pad_to:
+        if pad_to < len(work):
+            raise ValueError(f"pad_to {pad_to} < {len(work)} work items")
+        work += [(0, 0, 0, 0)] * (pad_to - len(work))
+    return work, n_splits, chunk, slots

@@ -1,0 +1,274 @@
+"""Seeded synthetic decode batches in the paged-KV tensor contract.
+
+This module only draws random numbers and stores them in the formats the
+contract names: sequence lengths, a shuffled page pool with a block table,
+bf16 or e4m3 queries, e4m3 K/V codes with per-(sequence, kv-head) descales,
+or latent records with per-128 block scales. It holds none of the attention
+arithmetic. Both sides of a parity check (the HIP path and the CPU oracle)
+receive the same bytes from here.
+
+Tensor contract ("mjolnir-kernel 0.1.0 wheel: mjolnir/t5_decode.py", module
+docstring; "MiniMax MSA fmha_sm100/cute README", Paged FP8 Decode):
+  q           (num_seqs * q_len, h_q, d)     bf16, or e4m3 codes (uint8) + q_descale
+  k/v cache   (num_pages, page_size, h_k, d) e4m3 codes (uint8), any strides, d contiguous
+  block_table (num_seqs, max_blocks)         int32
+  seq_lens    (num_seqs,)                    int32, including the new tokens
+  descales    (num_seqs, h_k)                float32
+
+Data recipe (following the t5_decode page's harness, ``run``):
+  * seq_lens from the workload's distribution, drawn with numpy PCG64;
+  * num_pages = used + max(4, used // 4); pages handed out from a seeded
+    random permutation (or in order for ``contiguous_pages``);
+  * every byte of a page no sequence references, and every row at or past
+    L in a sequence's last page, holds the e4m3 NaN 0x7F, so a stray read
+    shows up as NaN; block-table entries past a sequence's last block point
+    at such a poisoned page (never out of bounds);
+  * Q ~ N(0, 1) rounded to bf16; for e4m3 Q, quantised per (sequence, kv
+    head) with descale = max(amax over (q_len, h_r, d), 1e-6) / 448
+    (the page's ``quantize_q_fp8``);
+  * K, V ~ N(0, 1) quantised per (sequence, kv head): descale = max(amax over
+    that sequence's L tokens and d, 1e-6) / 448, codes = e4m3(x / descale)
+    (round to nearest even, |x / descale| <= 448 by construction);
+  * latent records: 512 latent values ~ N(0, 1) with one descale per token
+    and 128-value block (amax / 448), 64 rope values ~ N(0, 1) in bf16.
+Random tensors come from a torch generator on the target device, seeded per
+workload, so a GPU batch is generated on the GPU.
+"""
+
+import math
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+import torch
+
+E4M3_MAX = 448.0
+E4M3_NAN = 0x7F
+MLA_LATENT, MLA_ROPE, MLA_BLOCK = 512, 64, 128
+MLA_RECORD_BYTES = MLA_LATENT + 2 * MLA_ROPE + 4 * (MLA_LATENT // MLA_BLOCK)  # 656
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    num_seqs: int
+    q_len: int
+    h_q: int
+    h_k: int
+    d_qk: int
+    d_v: int
+    page_size: int
+    seq_len_dist: tuple  # ("fixed", [..]) | ("uniform", lo, hi) | ("lognormal", median, sigma, lo, hi) | ("mix", ...)
+    max_splits: int = 16
+    q_format: str = "bf16"  # "bf16" | "e4m3"
+    kv_format: str = "e4m3"  # "e4m3" | "mla"
+    causal: bool = True
+    seed: int = 1111
+    num_pages: int = 0  # 0: used + max(4, used // 4)
+    softmax_scale: float = 0.0  # 0: 1 / sqrt(d_qk)
+    kv_layout: str = "nhd"  # "nhd" (pages, PS, h_k, d) or "hnd" (pages, 2, h_k, PS, d)
+    contiguous_pages: bool = False
+
+    @property
+    def h_r(self):
+        return self.h_q // self.h_k
+
+    @property
+    def rows(self):  # packed query rows per (sequence, kv head)
+        return self.q_len * self.h_r
+
+    @property
+    def scale(self):
+        s = self.softmax_scale or 1.0 / math.sqrt(self.d_qk)
+        return float(np.float32(s))
+
+
+# The five synthetic workloads the decode path is specified on.
+WORKLOADS = {
+    1: Workload("tiny_gqa_b2_hq8_hk1_ps16", 2, 1, 8, 1, 128, 128, 16, ("fixed", [37, 100]),
+                max_splits=1, seed=1112, num_pages=16),
+    2: Workload("gqa_b64_hq32_hk8_d128_ps16_L512-8192", 64, 1, 32, 8, 128, 128, 16,
+                ("uniform", 512, 8192), max_splits=16, seed=1113),
+    3: Workload("specverify_b32_q4_hq64_hk8_d128_ps64_lognormal4096", 32, 4, 64, 8, 128, 128, 64,
+                ("lognormal", 4096, 1.0, 256, 32768), max_splits=16, seed=1114),
+    4: Workload("fp8_b128_hq64_hk4_d128_ps128_mix1k-4k_32k-64k", 128, 1, 64, 4, 128, 128, 128,
+                ("mix", 0.1, (32768, 65536), (1024, 4096)), max_splits=16, q_format="e4m3", seed=1115),
+    5: Workload("mla_b32_hq16_hk1_d576-512_ps64_L2k-16k", 32, 1, 16, 1, 576, 512, 64,
+                ("uniform", 2048, 16384), max_splits=16, kv_format="mla", seed=1116),
+}
+
+
+def workload(index, **overrides):
+    """A named workload, optionally with fields replaced (q_len, causal,
+    num_seqs, seq_len_dist, kv_layout, ...)."""
+    return replace(WORKLOADS[index], **overrides)
+
+
+def draw_seq_lens(w: Workload) -> np.ndarray:
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    kind = w.seq_len_dist[0]
+    b = w.num_seqs
+    if kind == "fixed":
+        lens = np.asarray(w.seq_len_dist[1], dtype=np.int64)
+        assert lens.shape == (b,)
+    elif kind == "uniform":
+        lens = rng.integers(w.seq_len_dist[1], w.seq_len_dist[2] + 1, size=b)
+    elif kind == "lognormal":
+        _, median, sigma, lo, hi = w.seq_len_dist
+        lens = np.clip(np.rint(np.exp(rng.normal(math.log(median), sigma, size=b))), lo, hi)
+    elif kind == "mix":  # a fraction of long sequences at shuffled positions
+        _, frac, long_rng, short_rng = w.seq_len_dist
+        n_long = int(round(frac * b))
+        lens = np.concatenate([rng.integers(long_rng[0], long_rng[1] + 1, size=n_long),
+                               rng.integers(short_rng[0], short_rng[1] + 1, size=b - n_long)])
+        lens = lens[rng.permutation(b)]
+    else:
+        raise ValueError(f"unknown length distribution {kind}")
+    return lens.astype(np.int32)
+
+
+@dataclass
+class Batch:
+    """One synthetic decode batch resident on ``device``."""
+    spec: Workload
+    seq_lens: torch.Tensor  # (b,) int32
+    block_table: torch.Tensor  # (b, max_blocks) int32
+    num_pages: int
+    q: torch.Tensor  # (b*q_len, h_q, d_qk) bf16, or uint8 e4m3 codes
+    q_descale: torch.Tensor  # (b, h_k) float32 (ones for bf16 q)
+    k_cache: torch.Tensor = None  # (pages, PS, h_k, d) uint8 logical view
+    v_cache: torch.Tensor = None
+    k_descale: torch.Tensor = None  # (b, h_k) float32
+    v_descale: torch.Tensor = None
+    kv_buffer: torch.Tensor = None  # physical storage behind the views
+    mla_latent: torch.Tensor = None  # (pages, PS, 1, 512) uint8 view of the records
+    mla_rope: torch.Tensor = None  # (pages, PS, 1, 64) bf16 view
+    mla_scales: torch.Tensor = None  # (pages, PS, 1, 4) float32 view
+    unused_pages: list = field(default_factory=list)
+
+    @property
+    def kv_bytes(self):
+        """Bytes of cache the decode must stream: every visible token's K and
+        V rows of every kv head (latent records are read once)."""
+        toks = int(self.seq_lens.sum())
+        w = self.spec
+        if w.kv_format == "mla":
+            return toks * MLA_RECORD_BYTES
+        return toks * w.h_k * (w.d_qk + w.d_v)
+
+    def to_numpy(self):
+        """Host copies in the oracle's formats: bf16 as uint16 bit patterns,
+        e4m3 as uint8 codes, logical (strided) views kept."""
+        def u16(t):
+            return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+        out = dict(seq_lens=self.seq_lens.cpu().numpy(), block_table=self.block_table.cpu().numpy())
+        out["q"] = u16(self.q) if self.q.dtype == torch.bfloat16 else self.q.cpu().numpy()
+        out["q_descale"] = self.q_descale.cpu().numpy()
+        if self.spec.kv_format == "mla":
+            out["latent"] = self.mla_latent.contiguous().cpu().numpy()
+            out["rope"] = u16(self.mla_rope)
+            out["scales"] = self.mla_scales.contiguous().cpu().numpy()
+        else:
+            out["k_cache"] = self.k_cache.contiguous().cpu().numpy()
+            out["v_cache"] = self.v_cache.contiguous().cpu().numpy()
+            out["k_descale"] = self.k_descale.cpu().numpy()
+            out["v_descale"] = self.v_descale.cpu().numpy()
+        return out
+
+
+def _page_assignment(w, lens, rng):
+    ps = w.page_size
+    blocks = [-(-int(L) // ps) for L in lens]
+    used = sum(blocks)
+    num_pages = w.num_pages or used + max(4, used // 4)
+    if num_pages <= used:
+        raise ValueError("page pool must hold at least one unused (poisoned) page")
+    perm = np.arange(num_pages) if w.contiguous_pages else rng.permutation(num_pages)
+    max_blocks = max(1, max(blocks))
+    unused = [int(p) for p in perm[used:]]
+    bt = np.empty((w.num_seqs, max_blocks), dtype=np.int32)
+    cursor = 0
+    for b, nb in enumerate(blocks):
+        bt[b, :nb] = perm[cursor:cursor + nb]
+        bt[b, nb:] = unused[b % len(unused)]  # padding -> a poisoned page
+        cursor += nb
+    return bt, num_pages, unused
+
+
+def _token_slots(lens, bt, ps, device):
+    """Flat (page * PS + row) slot of every token, sequences concatenated."""
+    seg = np.repeat(np.arange(len(lens)), lens)
+    pos = np.concatenate([np.arange(L) for L in lens]) if len(lens) else np.zeros(0, np.int64)
+    slot = bt[seg, pos // ps].astype(np.int64) * ps + pos % ps
+    return torch.from_numpy(seg).to(device), torch.from_numpy(slot).to(device)
+
+
+def _quantise_per_seq_head(x, seg, num_seqs):
+    """x (tokens, h_k, d) float32 -> (codes uint8, descale (b, h_k))."""
+    h_k = x.shape[1]
+    amax = torch.zeros(num_seqs, h_k, device=x.device)
+    amax.scatter_reduce_(0, seg[:, None].expand(-1, h_k), x.abs().amax(dim=-1), "amax")
+    desc = amax.clamp(min=1e-6) / E4M3_MAX
+    y = (x / desc[seg][:, :, None]).clamp(-E4M3_MAX, E4M3_MAX)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8), desc.contiguous()
+
+
+def make_batch(w: Workload, device="cpu", seq_lens=None) -> Batch:
+    """Generate the batch of workload ``w`` on ``device``."""
+    rng = np.random.Generator(np.random.PCG64(w.seed + 7))
+    lens = np.asarray(draw_seq_lens(w) if seq_lens is None else seq_lens, dtype=np.int32)
+    assert lens.shape == (w.num_seqs,)
+    bt, num_pages, unused = _page_assignment(w, lens, rng)
+    gen = torch.Generator(device=device).manual_seed(w.seed)
+    ps, b, h_k = w.page_size, w.num_seqs, w.h_k
+    seg, slot = _token_slots(lens, bt, ps, device)
+    n_tok = int(lens.sum())
+
+    q = torch.randn(b * w.q_len, w.h_q, w.d_qk, generator=gen, device=device).to(torch.bfloat16)
+    q_descale = torch.ones(b, h_k, device=device)
+    if w.q_format == "e4m3":
+        qg = q.float().view(b, w.q_len, h_k, w.h_r, w.d_qk)
+        amax = qg.abs().amax(dim=(1, 3, 4)).clamp(min=1e-6)
+        q_descale = (amax / E4M3_MAX).contiguous()
+        q = (qg / q_descale[:, None, :, None, None]).clamp(-E4M3_MAX, E4M3_MAX)
+        q = q.to(torch.float8_e4m3fn).view(torch.uint8).view(b * w.q_len, w.h_q, w.d_qk).contiguous()
+
+    batch = Batch(spec=w, seq_lens=torch.from_numpy(lens).to(device),
+                  block_table=torch.from_numpy(bt).to(device), num_pages=num_pages, q=q,
+                  q_descale=q_descale, unused_pages=unused)
+
+    if w.kv_format == "mla":
+        rec = torch.full((num_pages * ps, MLA_RECORD_BYTES), E4M3_NAN, dtype=torch.uint8, device=device)
+        lat = torch.randn(n_tok, MLA_LATENT // MLA_BLOCK, MLA_BLOCK, generator=gen, device=device)
+        desc = lat.abs().amax(dim=-1).clamp(min=1e-6) / E4M3_MAX  # (tokens, 4)
+        codes = (lat / desc[:, :, None]).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+        rope = torch.randn(n_tok, MLA_ROPE, generator=gen, device=device).to(torch.bfloat16)
+        rec[slot, :MLA_LATENT] = codes.view(torch.uint8).view(n_tok, MLA_LATENT)
+        rec[slot, MLA_LATENT:MLA_LATENT + 2 * MLA_ROPE] = rope.view(torch.uint8).view(n_tok, 2 * MLA_ROPE)
+        rec[slot, MLA_LATENT + 2 * MLA_ROPE:] = desc.float().contiguous().view(torch.uint8).view(n_tok, 16)
+        rec = rec.view(num_pages, ps, 1, MLA_RECORD_BYTES)
+        batch.kv_buffer = rec
+        batch.mla_latent = rec[..., :MLA_LATENT]
+        batch.mla_rope = rec[..., MLA_LATENT:MLA_LATENT + 2 * MLA_ROPE].view(torch.bfloat16)
+        batch.mla_scales = rec[..., MLA_LATENT + 2 * MLA_ROPE:].view(torch.float32)
+        return batch
+
+    d = w.d_qk
+    if w.kv_layout == "nhd":
+        kbuf = torch.full((2, num_pages, ps, h_k, d), E4M3_NAN, dtype=torch.uint8, device=device)
+        k_view, v_view = kbuf[0], kbuf[1]
+    elif w.kv_layout == "hnd":
+        kbuf = torch.full((num_pages, 2, h_k, ps, d), E4M3_NAN, dtype=torch.uint8, device=device)
+        k_view, v_view = kbuf[:, 0].transpose(1, 2), kbuf[:, 1].transpose(1, 2)
+    else:
+        raise ValueError(f"unknown kv_layout {w.kv_layout}")
+    for view, name in ((k_view, "k"), (v_view, "v")):
+        x = torch.randn(n_tok, h_k, d, generator=gen, device=device)
+        codes, desc = _quantise_per_seq_head(x, seg, b)
+        del x
+        pages, rows = slot // ps, slot % ps
+        view[pages, rows] = codes
+        setattr(batch, f"{name}_cache", view)
+        setattr(batch, f"{name}_descale", desc)
+    batch.kv_buffer = kbuf
+    return batch

@@ -1,0 +1,102 @@
+"""Pins of the split-KV plan oracle (no GPU): hand-worked examples of the
+rule on the t5_decode page (``plan_split_kv``), a linear-scan check of the
+chunk's minimality, and the structural invariants of every plan."""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle.plan import plan_split_kv
+
+
+def test_hand_worked_split():
+    # tiles [3, 8, 2, 1], slots = 5*2 // 2 = 5, lo = 1.
+    # chunk 1 -> 14 items, 2 -> 8, 3 -> 6, 4 -> 5 <= 5: chunk = 4.
+    work, ns, chunk, slots = plan_split_kv([300, 1000, 129, 50], h_k=2, n_q_tiles=1, cu_count=5, wg_per_cu=2)
+    assert (chunk, slots, ns) == (4, 5, [1, 2, 1, 1])
+    assert work == [(1, 0, 4, 0), (1, 4, 8, 1), (0, 0, 3, 0), (2, 0, 2, 0), (3, 0, 1, 0)]
+
+
+def test_hand_worked_batch_fills_wave():
+    # slots = 4 // 4 = 1 <= 8 sequences: nothing is split.
+    work, ns, chunk, slots = plan_split_kv([5000] * 8, h_k=4, n_q_tiles=1, cu_count=4, wg_per_cu=1)
+    assert (chunk, slots) == (40, 1)
+    assert work == [(b, 0, 40, 0) for b in range(8)] and ns == [1] * 8
+
+
+def test_hand_worked_force_splits_and_stable_order():
+    # tiles [8, 2]; chunk = max(1, ceil(8 / 3)) = 3.
+    work, ns, chunk, _ = plan_split_kv([1000, 200], h_k=1, n_q_tiles=1, cu_count=64, force_splits=3)
+    assert chunk == 3 and ns == [3, 1]
+    assert work == [(0, 0, 3, 0), (0, 3, 6, 1), (0, 6, 8, 2), (1, 0, 2, 0)]
+
+
+def test_hand_worked_max_splits_cap():
+    # tiles [64, 1]; lo = ceil(64 / 16) = 4 and 4 already fits 1024 slots.
+    work, ns, chunk, slots = plan_split_kv([128 * 64, 128], h_k=1, n_q_tiles=1, cu_count=256, wg_per_cu=4)
+    assert (chunk, slots, ns) == (4, 1024, [16, 1])
+    assert len(work) == 17 and work[-1] == (1, 0, 1, 0)
+
+
+def test_hand_worked_single_split_and_empty_sequence():
+    work, ns, chunk, _ = plan_split_kv([0, 130, 37], h_k=1, n_q_tiles=1, cu_count=256, max_splits=1)
+    assert chunk == 2 and ns == [1, 1, 1]
+    assert work == [(1, 0, 2, 0), (0, 0, 1, 0), (2, 0, 1, 0)]
+
+
+def test_padding_and_errors():
+    work, *_ = plan_split_kv([300, 1000, 129, 50], h_k=2, n_q_tiles=1, cu_count=5, wg_per_cu=2, pad_to=8)
+    assert work[5:] == [(0, 0, 0, 0)] * 3 and len(work) == 8
+    with pytest.raises(ValueError):
+        plan_split_kv([300, 1000, 129, 50], h_k=2, n_q_tiles=1, cu_count=5, wg_per_cu=2, pad_to=4)
+    with pytest.raises(ValueError):
+        plan_split_kv([], h_k=1, n_q_tiles=1, cu_count=1)
+    with pytest.raises(ValueError):
+        plan_split_kv([-1], h_k=1, n_q_tiles=1, cu_count=1)
+    with pytest.raises(ValueError):
+        plan_split_kv([10], h_k=0, n_q_tiles=1, cu_count=1)
+
+
+def _check_invariants(lens, kw, work, ns, chunk, slots):
+    tiles = [max(1, math.ceil(L / 128)) for L in lens]
+    real = [w for w in work if w[2] > w[1]]
+    per_seq = {}
+    for w in real:
+        per_seq.setdefault(w[0], []).append(w)
+    for b, t in enumerate(tiles):
+        items = sorted(per_seq[b], key=lambda w: w[3])
+        assert [w[3] for w in items] == list(range(ns[b]))
+        assert items[0][1] == 0 and items[-1][2] == t
+        for a, c in zip(items, items[1:]):
+            assert a[2] == c[1]
+        assert all(w[2] - w[1] <= chunk for w in items)
+    assert max(ns) <= kw.get("max_splits", 16)
+    lengths = [w[2] - w[1] for w in real]
+    assert lengths == sorted(lengths, reverse=True)
+    assert all(w == (0, 0, 0, 0) for w in work[len(real):])
+    # ties keep generation order (sequence-major, split-slot minor)
+    for a, c in zip(real, real[1:]):
+        if a[2] - a[1] == c[2] - c[1]:
+            assert (a[0], a[3]) < (c[0], c[3])
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_plans_invariants_and_minimal_chunk(seed):
+    rng = np.random.default_rng(seed)
+    b = int(rng.integers(1, 80))
+    lens = rng.integers(0, 70000, size=b).tolist()
+    kw = dict(h_k=int(rng.choice([1, 2, 4, 8])), n_q_tiles=int(rng.integers(1, 3)), cu_count=256,
+              wg_per_cu=int(rng.integers(1, 17)), max_splits=int(rng.choice([1, 4, 16, 64])),
+              min_chunk_tiles=int(rng.choice([1, 1, 2, 8])))
+    work, ns, chunk, slots = plan_split_kv(lens, **kw)
+    _check_invariants(lens, kw, work, ns, chunk, slots)
+    tiles = [max(1, math.ceil(L / 128)) for L in lens]
+    assert slots == max(1, 256 * kw["wg_per_cu"] // (kw["h_k"] * kw["n_q_tiles"]))
+    lo = max(kw["min_chunk_tiles"], math.ceil(max(tiles) / kw["max_splits"]))
+    if len(tiles) >= slots or kw["max_splits"] == 1:
+        assert chunk == max(tiles)
+    else:
+        scan = next(c for c in range(lo, max(max(tiles), lo) + 1)
+                    if sum(math.ceil(t / c) for t in tiles) <= slots)
+        assert chunk == scan
