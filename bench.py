@@ -1,0 +1,194 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV e4m3 decode path on one MI355X.
+
+A step is one pass of the whole hot path over one synthetic batch:
+pkv_paged_decode_attn (+ pkv_merge_splits when the plan split a sequence),
+launched through the C ABI on torch's current stream. The plan is made once
+(host planner) before timing, as a serving loop would. Steps rotate over
+several independent KV pools (>= 1 GiB in total) so that no step finds its
+cache in the 256 MB last-level cache. W untimed warmup steps, then exactly K
+timed steps between two synchronisations; HIP events on the launch stream
+time every decode and merge launch.
+
+Printed (one JSON line on stdout): value = KV bytes per step / time per step
+(GB/s, the metric), the time per step, the decode kernel's roofline fraction
+against the 8 TB/s HBM peak, and the fp64 CPU oracle timed on a bounded
+sample of the same batch on the host cores. Diagnostics go to stderr.
+
+Default workload: 64 sequences, q_len 1, 32 query heads on 8 e4m3 KV heads,
+d = 128, 16-key pages, lengths uniform in [512, 8192], split-KV up to 16
+chunks (``--config 2``). ``--config 1..4`` selects the other workloads.
+"""
+
+import argparse
+import dataclasses
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(batch, dec):
+    """Bytes the decode kernel must move once: every visible K and V row, the
+    query rows, the block-table entries, and its outputs (final bf16 O + LSE
+    for unsplit sequences, fp32 partial O + (max, sum) for split ones)."""
+    import numpy as np
+
+    w = batch.spec
+    lens = batch.seq_lens.cpu().numpy().astype(np.int64)
+    ns = dec.n_splits.cpu().numpy().astype(np.int64)
+    q_elem = 1 if w.q_format == "e4m3" else 2
+    kv = batch.kv_bytes
+    q = w.num_seqs * w.q_len * w.h_q * w.d_qk * q_elem
+    bt = int((-(-lens // w.page_size)).sum()) * 4 * w.h_k
+    rows = w.num_seqs * w.h_k * w.rows
+    direct = ns <= 1
+    out_direct = int(direct.sum()) * w.h_k * w.rows * (w.d_v * 2 + 4)
+    out_split = int(ns[~direct].sum()) * w.h_k * w.rows * (w.d_v + 2) * 4
+    return dict(kv=kv, q=q, block_table=bt, out=out_direct + out_split, rows=rows,
+                total=kv + q + bt + out_direct + out_split)
+
+
+def cpu_oracle_baseline(batch, budget_s):
+    """Time the fp64 oracle (single BLAS thread) on whole sequences of the
+    batch until ``budget_s`` seconds of CPU work are spent."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle.attention import decode_attention
+
+    w = batch.spec
+    nb = batch.to_numpy()
+    lens = nb["seq_lens"]
+    done, kv = 0, 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for b in range(w.num_seqs):
+            sl = slice(b * w.q_len, (b + 1) * w.q_len)
+            decode_attention(nb["q"][sl], nb["k_cache"], nb["v_cache"], nb["block_table"][b:b + 1],
+                             lens[b:b + 1], nb["q_descale"][b:b + 1], nb["k_descale"][b:b + 1],
+                             nb["v_descale"][b:b + 1], q_len=w.q_len, h_k=w.h_k, softmax_scale=w.scale,
+                             causal=w.causal)
+            done += 1
+            kv += int(lens[b]) * w.h_k * (w.d_qk + w.d_v)
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} of {w.num_seqs} sequences ({kv} KV bytes, all heads and rows) in {dt:.1f} s, "
+                      f"numpy fp64, one BLAS thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
+    ap.add_argument("--causal", type=int, default=None, help="override the workload's causal flag (0/1)")
+    ap.add_argument("--pools", type=int, default=0, help="KV pools to rotate (0: enough for >= 1 GiB, min 3)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--wg-per-cu", type=int, default=None, help="override the occupancy the planner uses")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the decode path has no multi-GPU leg (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from paged_kv_fp8_amd import decode
+    from paged_kv_fp8_amd.workloads import make_batch, workload
+
+    over = {} if args.causal is None else {"causal": bool(args.causal)}
+    w = workload(args.config, **over)
+    torch.cuda.set_device(0)
+    first = make_batch(w, device="cuda")
+    pools = args.pools or max(3, -(-(1 << 30) // max(1, first.kv_bytes)))
+    lens = first.seq_lens.cpu().numpy()
+    batches = [first] + [make_batch(dataclasses.replace(w, seed=w.seed + 1000 * i), device="cuda", seq_lens=lens)
+                         for i in range(1, pools)]
+    decs = [decode.for_batch(b, wg_per_cu=args.wg_per_cu) for b in batches]
+    info = decs[0].plan_info
+    ab = algorithmic_bytes(first, decs[0])
+    log(f"workload {w.name}: {w.num_seqs} seqs, {int(lens.sum())} tokens, KV {ab['kv'] / 1e6:.1f} MB, "
+        f"pools {pools}, plan chunk={info.chunk_tiles} tiles work={info.num_real} slots={info.slots} "
+        f"max_splits_used={info.max_n_splits} wg/cu={decs[0].wg_per_cu} cu={decs[0].cu_count}")
+
+    for i in range(args.warmup):
+        decs[i % pools].run()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        d = decs[i % pools]
+        ev[i][0].record()
+        d.run_decode_only()
+        ev[i][1].record()
+        d.run_merge_only()
+        ev[i][2].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / K
+    dec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    mrg_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    value = ab["kv"] / (ms_step * 1e-3) / 1e9
+    achieved = ab["total"] / (dec_ms * 1e-3) / 1e9
+    log(f"step {ms_step * 1e3:.1f} us (decode {dec_ms * 1e3:.1f} us, merge {mrg_ms * 1e3:.1f} us), "
+        f"host wall {wall / K * 1e6:.1f} us/step; KV {value:.0f} GB/s; decode kernel {achieved:.0f} GB/s "
+        f"= {achieved / HBM_PEAK_GBS:.3f} of peak")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_oracle_baseline(first, args.cpu_seconds)
+        log(f"cpu oracle: {cpu}")
+
+    line = {
+        "metric": "achieved HBM GB/s (KV bytes / decode-step time), us per decode step",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "us_per_step": round(ms_step * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if w.q_format == "e4m3" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "q_len": w.q_len, "h_q": w.h_q, "h_k": w.h_k,
+                   "d": w.d_qk, "page_size": w.page_size, "causal": w.causal, "kv_tokens": int(lens.sum()),
+                   "kv_bytes": ab["kv"], "max_splits": w.max_splits, "pools": pools,
+                   "plan": {"chunk_tiles": info.chunk_tiles, "work_items": info.num_real, "slots": info.slots,
+                            "max_n_splits": info.max_n_splits, "wg_per_cu": decs[0].wg_per_cu}},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gqa_decode_kernel", "kernel_us": round(dec_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": ab["total"], "merge_us": round(mrg_ms * 1e3, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,243 @@
+/*
+ * pkv_fp8.h -- C ABI of libpkvfp8.so: paged-KV e4m3 decode attention for
+ * AMD MI355X (gfx950).
+ *
+ * What is computed. For every sequence b, KV head g and packed query row
+ * n = qi * h_r + hr (h_r = h_q / h_k, qi-major: "mjolnir-kernel 0.1.0 wheel:
+ * mjolnir/t5_decode.py", module docstring, "Query packing"), the row attends
+ * to the keys j = 0 .. lim(n) of its sequence, lim(n) = L - q_len + qi under
+ * the causal tail (q_len > 1, causal != 0) and L - 1 otherwise (block mode),
+ * L = seq_lens[b] including the new tokens. Key j is row j % page_size of
+ * page block_table[b][j / page_size]. With per-(sequence, kv-head) descales
+ * qd, kd, vd ("Inputs follow vLLM's paged KV cache", same docstring):
+ *   s_j = softmax_scale * qd * kd * <q, k_j>
+ *   O[n] = o_scale * vd * sum_j exp(s_j - M) v_j / sum_j exp(s_j - M)
+ *   LSE[n] = M + ln sum_j exp(s_j - M),   M = max_j s_j   (natural log)
+ * A row that sees no key gets O = 0 and LSE = -inf (the page's epilogue and
+ * reduction kernel). The latent-record variant (kv_format = PKV_KV_MLA;
+ * "vLLM PR #62633", Kernel design) has one KV head whose key is 512 e4m3
+ * latent values times one fp32 scale per 128-value block followed by 64 bf16
+ * rope values, and whose value is the scaled latent part.
+ *
+ * Call sequence (the page's module docstring, "Split-KV scheduling" and
+ * "Workspace"; "MiniMax MSA fmha_sm100/cute README", Paged FP8 Decode,
+ * plan() then run()):
+ *   1. pkv_decode_slots()   -> CU count, resident workgroups per CU, q-row tiles
+ *   2. pkv_plan_split_kv()  -> host work list + n_splits (pure host code)
+ *   3. copy work / n_splits to the device once (the caller's job)
+ *   4. pkv_paged_decode_attn(); then pkv_merge_splits() when any sequence
+ *      was split (info.max_n_splits > 1). Both only enqueue on `stream`:
+ *      they never allocate, never synchronise and are capturable in a HIP
+ *      graph; a plan made for upper-bound lengths stays valid for shorter
+ *      runtime seq_lens.
+ *
+ * Ownership. The caller owns every buffer; the library keeps no state
+ * between calls and never frees or retains a pointer. Device pointers are
+ * plain device addresses (e.g. torch's data_ptr()).
+ *
+ * Errors. Every entry point returns a pkv_status. A call that fails
+ * validation launches nothing and returns a negative code; nothing aborts or
+ * throws across the ABI. pkv_last_error() gives a one-line reason for the
+ * calling thread's most recent failure.
+ *
+ * Preconditions not checked on the device (a violation gives unspecified
+ * results but no out-of-bounds access: page indices are clamped into
+ * [0, num_pages) and L into [0, max_blocks * page_size], work items whose
+ * sequence or split slot is out of range are skipped):
+ *   block_table[b][i] in [0, num_pages) for i < ceil(L / page_size);
+ *   descales positive and finite; the device work list and n_splits come
+ *   from pkv_plan_split_kv with lengths >= the runtime seq_lens and the same
+ *   max_splits.
+ */
+#ifndef PKV_FP8_H
+#define PKV_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pkv_status;
+#define PKV_OK 0
+#define PKV_ERR_INVALID_ARG (-1) /* null pointer, bad size, misaligned pointer or stride */
+#define PKV_ERR_UNSUPPORTED (-2) /* valid request this build has no kernel for */
+#define PKV_ERR_CAPACITY (-3)    /* an output array is too small (work_cap, pad_to) */
+#define PKV_ERR_WORKSPACE (-4)   /* split workspace missing or too small */
+#define PKV_ERR_HIP (-5)         /* the HIP runtime reported an error */
+
+/* Static name of a status code ("PKV_OK", ...). Never NULL. */
+const char* pkv_status_string(pkv_status s);
+
+/* Reason for the calling thread's most recent failing call (empty string if
+ * none). The pointer stays valid until the thread's next failing call. */
+const char* pkv_last_error(void);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int32_t pkv_version(void);
+
+/* sizeof(pkv_decode_args) as compiled into the library, so that a binding
+ * can check its own copy of the struct layout before the first call. */
+size_t pkv_decode_args_size(void);
+
+/* ------------------------------------------------------------------------ */
+/* Split-KV planner (host only, pure: no GPU needed).                       */
+/* ------------------------------------------------------------------------ */
+typedef struct pkv_plan_info {
+  int32_t num_work;     /* entries written to work_out (real + padding) */
+  int32_t num_real;     /* non-empty work items */
+  int32_t chunk_tiles;  /* 128-key tiles per chunk (a sequence's last chunk may be shorter) */
+  int32_t slots;        /* work items that fit one wave of the grid */
+  int32_t max_n_splits; /* largest n_splits over the batch */
+} pkv_plan_info;
+
+/*
+ * Occupancy-pinned split-KV plan ("mjolnir-kernel 0.1.0 wheel:
+ * mjolnir/t5_decode.py", plan_split_kv and the module docstring). In units
+ * of 128-key tiles, tiles_b = max(1, ceil(L_b / 128)), T = max tiles_b:
+ *   slots = max(1, cu_count * wg_per_cu / (h_k * n_q_tiles))
+ *   lo    = max(min_chunk_tiles, ceil(T / max_splits))
+ *   chunk = max(lo, ceil(T / force_splits))          if force_splits > 0
+ *         = T                                         if num_seqs >= slots or max_splits == 1
+ *         = smallest c >= lo with sum_b ceil(tiles_b / c) <= slots   otherwise
+ * Sequence b becomes items (b, j*chunk, min((j+1)*chunk, tiles_b), j) for
+ * j < n_splits[b] = ceil(tiles_b / chunk); items are ordered longest first
+ * (ties keep sequence-major order); pad_to > 0 appends (0,0,0,0) items up to
+ * pad_to entries, so a captured grid keeps one size.
+ *
+ * seq_lens      host int32[num_seqs], each >= 0
+ * work_out      host int32[work_cap][4] (seq, tile_begin, tile_end, split_slot)
+ * n_splits_out  host int32[num_seqs]
+ * info          host, may be NULL
+ * Errors: INVALID_ARG for num_seqs < 1, negative lengths, sizes < 1,
+ * force_splits / pad_to < 0, NULL arrays; CAPACITY when the items do not fit
+ * work_cap or exceed pad_to; UNSUPPORTED when a sequence would need more than
+ * max_splits chunks (cannot happen for max_splits >= 1, kept as a guard) or
+ * max_splits > PKV_MAX_SPLITS.
+ */
+#define PKV_MAX_SPLITS 256
+pkv_status pkv_plan_split_kv(const int32_t* seq_lens, int32_t num_seqs, int32_t h_k, int32_t n_q_tiles,
+                             int32_t cu_count, int32_t wg_per_cu, int32_t max_splits, int32_t force_splits,
+                             int32_t min_chunk_tiles, int32_t pad_to, int32_t* work_out, int32_t work_cap,
+                             int32_t* n_splits_out, pkv_plan_info* info);
+
+/* ------------------------------------------------------------------------ */
+/* Decode launch arguments                                                   */
+/* ------------------------------------------------------------------------ */
+#define PKV_Q_BF16 0 /* q is bf16; q_descale is ignored */
+#define PKV_Q_E4M3 1 /* q is e4m3 codes with q_descale */
+
+#define PKV_KV_E4M3 0 /* K and V caches of e4m3 codes, d_qk = d_v = 128 */
+#define PKV_KV_MLA 1  /* latent records: h_k = 1, d_qk = 576 (512 latent + 64 rope), d_v = 512 */
+
+/*
+ * All strides are in ELEMENTS of the pointed-to type, >= 0; a descale
+ * stride of 0 broadcasts (per-tensor, per-head or per-(seq, head) scales).
+ * Tensor layouts ("mjolnir-kernel 0.1.0 wheel: mjolnir/t5_decode.py", module
+ * docstring and kernel_strides; logical views of any physical layout with
+ * the last dimension contiguous):
+ *   q      [num_seqs * q_len][h_q][d_qk]     bf16 or e4m3  (q_tok_stride, q_head_stride)
+ *   k, v   [num_pages][page_size][h_k][d]    e4m3 codes    (page, row, head strides, bytes)
+ *          MLA: k = v = latent [pages][PS][1][512] e4m3 (v may be NULL or equal k)
+ *   k_rope MLA only: [pages][PS][1][64] bf16 (page, row strides)
+ *   k_blk_scale MLA only: [pages][PS][1][4] fp32, one scale per 128 latent values
+ *   block_table [num_seqs][max_blocks] int32 (bt_row_stride)
+ *   seq_lens    [num_seqs] int32
+ *   q/k/v_descale fp32 at [b * seq_stride + g * head_stride] (unused for MLA)
+ *   o      [num_seqs * q_len][h_q][d_v] bf16 (o_tok_stride, o_head_stride)
+ *   lse    [num_seqs][h_k][q_len * h_r] fp32, contiguous
+ *   work   [num_work][4] int32 from pkv_plan_split_kv (device copy)
+ *   n_splits [num_seqs] int32 from pkv_plan_split_kv (device copy)
+ *   workspace  >= pkv_workspace_bytes(...) bytes of device memory, 256-B
+ *          aligned, NOT initialised (only the splits a sequence used are
+ *          read back); may be NULL when max_splits == 1.
+ * Alignment: q, k, v, o and workspace 16-byte aligned, and every stride of
+ * q, k, v and o a multiple of 16 bytes (8-byte multiples for e4m3 q).
+ */
+typedef struct pkv_decode_args {
+  int32_t num_seqs, q_len, h_q, h_k, d_qk, d_v;
+  int32_t page_size, num_pages, max_blocks;
+  int32_t causal;    /* nonzero: causal tail for q_len > 1; zero: block mode */
+  int32_t q_format;  /* PKV_Q_* */
+  int32_t kv_format; /* PKV_KV_* */
+  float softmax_scale;
+  float o_scale; /* output multiplier (1.0 for plain attention) */
+
+  const void* q;
+  int64_t q_tok_stride, q_head_stride;
+  const uint8_t* k;
+  int64_t k_page_stride, k_row_stride, k_head_stride;
+  const uint8_t* v;
+  int64_t v_page_stride, v_row_stride, v_head_stride;
+  const uint16_t* k_rope;
+  int64_t rope_page_stride, rope_row_stride;
+  const float* k_blk_scale;
+  int64_t scale_page_stride, scale_row_stride;
+
+  const int32_t* block_table;
+  int64_t bt_row_stride;
+  const int32_t* seq_lens;
+
+  const float* q_descale;
+  int64_t qd_seq_stride, qd_head_stride;
+  const float* k_descale;
+  int64_t kd_seq_stride, kd_head_stride;
+  const float* v_descale;
+  int64_t vd_seq_stride, vd_head_stride;
+
+  void* o;
+  int64_t o_tok_stride, o_head_stride;
+  float* lse;
+
+  const int32_t* work;
+  int32_t num_work;
+  const int32_t* n_splits;
+  int32_t max_splits;
+  void* workspace;
+  size_t workspace_bytes;
+} pkv_decode_args;
+
+/* Bytes of split workspace: max_splits * num_seqs * h_k * n_rows * (d_v + 2)
+ * fp32 values (partial O, max and sum per row and split), rounded up to 256. */
+size_t pkv_workspace_bytes(int32_t num_seqs, int32_t h_k, int32_t n_rows, int32_t d_v, int32_t max_splits);
+
+/*
+ * Occupancy facts the planner needs for these arguments (shapes, formats,
+ * mode; pointers are not read): the current device's compute-unit count,
+ * how many decode workgroups of the selected kernel are resident per CU,
+ * and the number of q-row tiles of the grid. Queries the HIP runtime; no
+ * launch. Errors: INVALID_ARG / UNSUPPORTED as pkv_paged_decode_attn would
+ * return for the shapes, HIP on a runtime failure.
+ */
+pkv_status pkv_decode_slots(const pkv_decode_args* a, int32_t* cu_count, int32_t* wg_per_cu,
+                            int32_t* n_q_tiles);
+
+/*
+ * Split-KV decode ("mjolnir-kernel 0.1.0 wheel: mjolnir/t5_decode.py",
+ * decode kernel: online softmax over the work item's contiguous key range,
+ * then its epilogue). One workgroup per (work item, kv head, q-row tile).
+ * A sequence with n_splits == 1 writes its final bf16 O and LSE directly; a
+ * split one writes fp32 partials (O * vd, max in natural-log units, sum) to
+ * its split slot of the workspace. Empty (padding) items exit at once.
+ * `stream` is a hipStream_t (NULL = the null stream). Validates everything
+ * before launching; returns HIP if the launch itself fails.
+ */
+pkv_status pkv_paged_decode_attn(const pkv_decode_args* a, void* stream);
+
+/*
+ * Combine of split partials ("mjolnir-kernel 0.1.0 wheel:
+ * mjolnir/t5_decode.py", reduction kernel): for every sequence with
+ * n_splits > 1 and every row, m* = max_j m_j, w_j = exp(m_j - m*) (0 for
+ * m_j = -inf), O = o_scale * sum_j w_j O_j / sum_j w_j l_j (0 if the sum is
+ * 0), LSE = m* + ln sum_j w_j l_j, over j < n_splits[b] in index order.
+ * Sequences with n_splits <= 1 are left as the decode wrote them. A no-op
+ * (nothing launched) when max_splits == 1. Same arguments as the decode.
+ */
+pkv_status pkv_merge_splits(const pkv_decode_args* a, void* stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* PKV_FP8_H */

@@ -1,0 +1,194 @@
+// Host entry points of libpkvfp8.so: argument validation and dispatch to
+// the kernel launchers. Every check runs before any HIP call, so an invalid
+// request returns its error code without touching the GPU.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+
+namespace {
+thread_local char g_last_error[512] = "";
+}
+
+pkv_status fail(pkv_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+namespace {
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+bool pow2_page(int ps) { return ps == 16 || ps == 32 || ps == 64 || ps == 128; }
+
+// Shape and mode checks shared by the slot query, the decode and the merge.
+pkv_status check_shapes(const pkv_decode_args* a) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "args is NULL");
+  if (a->num_seqs < 1 || a->q_len < 1 || a->h_q < 1 || a->h_k < 1)
+    return fail(PKV_ERR_INVALID_ARG, "num_seqs=%d q_len=%d h_q=%d h_k=%d must be >= 1", a->num_seqs, a->q_len,
+                a->h_q, a->h_k);
+  if (a->h_q % a->h_k) return fail(PKV_ERR_INVALID_ARG, "h_q=%d is not a multiple of h_k=%d", a->h_q, a->h_k);
+  if (a->num_pages < 1 || a->max_blocks < 1)
+    return fail(PKV_ERR_INVALID_ARG, "num_pages=%d max_blocks=%d must be >= 1", a->num_pages, a->max_blocks);
+  if (!pow2_page(a->page_size)) return fail(PKV_ERR_UNSUPPORTED, "page_size=%d not in {16,32,64,128}", a->page_size);
+  if ((int64_t)a->max_blocks * a->page_size > INT32_MAX)
+    return fail(PKV_ERR_INVALID_ARG, "max_blocks * page_size exceeds int32");
+  if (a->q_format != PKV_Q_BF16 && a->q_format != PKV_Q_E4M3)
+    return fail(PKV_ERR_INVALID_ARG, "q_format=%d unknown", a->q_format);
+  if (a->max_splits < 1 || a->max_splits > PKV_MAX_SPLITS)
+    return fail(PKV_ERR_INVALID_ARG, "max_splits=%d not in [1, %d]", a->max_splits, PKV_MAX_SPLITS);
+  if (!std::isfinite(a->softmax_scale) || !std::isfinite(a->o_scale))
+    return fail(PKV_ERR_INVALID_ARG, "softmax_scale and o_scale must be finite");
+  const int64_t rows = (int64_t)a->q_len * (a->h_q / a->h_k);
+  if (a->kv_format == PKV_KV_E4M3) {
+    if (a->d_qk != 128 || a->d_v != 128)
+      return fail(PKV_ERR_UNSUPPORTED, "e4m3 cache: d_qk=%d d_v=%d, only 128/128 is built", a->d_qk, a->d_v);
+    if (rows > 4096) return fail(PKV_ERR_UNSUPPORTED, "q_len * h_r = %lld rows > 4096", (long long)rows);
+  } else if (a->kv_format == PKV_KV_MLA) {
+    if (a->d_qk != 576 || a->d_v != 512 || a->h_k != 1)
+      return fail(PKV_ERR_UNSUPPORTED, "latent cache needs h_k=1, d_qk=576, d_v=512 (got %d, %d, %d)", a->h_k,
+                  a->d_qk, a->d_v);
+    if (a->q_format != PKV_Q_BF16) return fail(PKV_ERR_UNSUPPORTED, "latent cache: only bf16 q is built");
+    if (rows > 256) return fail(PKV_ERR_UNSUPPORTED, "latent cache: q_len * h_q = %lld rows > 256", (long long)rows);
+    return fail(PKV_ERR_UNSUPPORTED, "latent cache decode is not built in this version");
+  } else {
+    return fail(PKV_ERR_INVALID_ARG, "kv_format=%d unknown", a->kv_format);
+  }
+  return PKV_OK;
+}
+
+bool bad_stride(int64_t s, int64_t elem_bytes, int64_t multiple) {
+  return s < 0 || ((s * elem_bytes) % multiple) != 0;
+}
+
+pkv_status check_pointers(const pkv_decode_args* a, bool for_merge) {
+  const bool mla = a->kv_format == PKV_KV_MLA;
+  const int64_t q_elem = a->q_format == PKV_Q_BF16 ? 2 : 1;
+  const int64_t q_mult = a->q_format == PKV_Q_BF16 ? 16 : 8;
+  if (!a->o || !a->lse || !a->seq_lens || !a->n_splits)
+    return fail(PKV_ERR_INVALID_ARG, "o, lse, seq_lens and n_splits must be non-NULL");
+  if (!aligned(a->o, 16) || !aligned(a->lse, 4) || bad_stride(a->o_tok_stride, 2, 16) ||
+      bad_stride(a->o_head_stride, 2, 16))
+    return fail(PKV_ERR_INVALID_ARG, "o must be 16-B aligned with 16-B multiple strides");
+  if (a->max_splits > 1) {
+    const size_t need = pkv_workspace_bytes(a->num_seqs, a->h_k, a->q_len * (a->h_q / a->h_k), a->d_v, a->max_splits);
+    if (!a->workspace || a->workspace_bytes < need)
+      return fail(PKV_ERR_WORKSPACE, "workspace %zu bytes < %zu needed for max_splits=%d", a->workspace_bytes, need,
+                  a->max_splits);
+    if (!aligned(a->workspace, 16)) return fail(PKV_ERR_INVALID_ARG, "workspace must be 16-B aligned");
+  }
+  if (for_merge) return PKV_OK;
+  if (!a->q || !a->k || !a->block_table || !a->work)
+    return fail(PKV_ERR_INVALID_ARG, "q, k, block_table and work must be non-NULL");
+  if (a->num_work < 1) return fail(PKV_ERR_INVALID_ARG, "num_work=%d < 1", a->num_work);
+  if (!aligned(a->q, 16) || bad_stride(a->q_tok_stride, q_elem, q_mult) || bad_stride(a->q_head_stride, q_elem, q_mult))
+    return fail(PKV_ERR_INVALID_ARG, "q must be 16-B aligned with %lld-B multiple strides", (long long)q_mult);
+  if (!aligned(a->work, 16)) return fail(PKV_ERR_INVALID_ARG, "work must be 16-B aligned");
+  if (a->bt_row_stride < a->max_blocks)
+    return fail(PKV_ERR_INVALID_ARG, "bt_row_stride=%lld < max_blocks=%d", (long long)a->bt_row_stride,
+                a->max_blocks);
+  if (!aligned(a->k, 16) || bad_stride(a->k_page_stride, 1, 16) || bad_stride(a->k_row_stride, 1, 16) ||
+      bad_stride(a->k_head_stride, 1, 16))
+    return fail(PKV_ERR_INVALID_ARG, "k must be 16-B aligned with 16-B multiple strides");
+  if (mla) {
+    if (a->v && a->v != a->k) return fail(PKV_ERR_INVALID_ARG, "latent cache: v must be NULL or equal k");
+    if (!a->k_rope || !a->k_blk_scale) return fail(PKV_ERR_INVALID_ARG, "latent cache: k_rope, k_blk_scale NULL");
+    if (!aligned(a->k_rope, 16) || bad_stride(a->rope_page_stride, 2, 16) || bad_stride(a->rope_row_stride, 2, 16))
+      return fail(PKV_ERR_INVALID_ARG, "k_rope must be 16-B aligned with 16-B multiple strides");
+    if (!aligned(a->k_blk_scale, 16) || bad_stride(a->scale_page_stride, 4, 16) ||
+        bad_stride(a->scale_row_stride, 4, 16))
+      return fail(PKV_ERR_INVALID_ARG, "k_blk_scale must be 16-B aligned with 16-B multiple strides");
+    return PKV_OK;
+  }
+  if (!a->v || !aligned(a->v, 16) || bad_stride(a->v_page_stride, 1, 16) || bad_stride(a->v_row_stride, 1, 16) ||
+      bad_stride(a->v_head_stride, 1, 16))
+    return fail(PKV_ERR_INVALID_ARG, "v must be non-NULL, 16-B aligned, with 16-B multiple strides");
+  if (!a->k_descale || !a->v_descale || (a->q_format == PKV_Q_E4M3 && !a->q_descale))
+    return fail(PKV_ERR_INVALID_ARG, "k/v descale (and q descale for e4m3 q) must be non-NULL");
+  if (a->kd_seq_stride < 0 || a->kd_head_stride < 0 || a->vd_seq_stride < 0 || a->vd_head_stride < 0 ||
+      a->qd_seq_stride < 0 || a->qd_head_stride < 0)
+    return fail(PKV_ERR_INVALID_ARG, "descale strides must be >= 0");
+  return PKV_OK;
+}
+
+pkv_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PKV_OK;
+  return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" const char* pkv_status_string(pkv_status s) {
+  switch (s) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_ERR_INVALID_ARG: return "PKV_ERR_INVALID_ARG";
+    case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED";
+    case PKV_ERR_CAPACITY: return "PKV_ERR_CAPACITY";
+    case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
+    case PKV_ERR_HIP: return "PKV_ERR_HIP";
+    default: return "PKV_ERR_UNKNOWN";
+  }
+}
+
+extern "C" const char* pkv_last_error(void) { return g_last_error; }
+
+extern "C" int32_t pkv_version(void) { return 100; }
+
+extern "C" size_t pkv_decode_args_size(void) { return sizeof(pkv_decode_args); }
+
+extern "C" size_t pkv_workspace_bytes(int32_t num_seqs, int32_t h_k, int32_t n_rows, int32_t d_v, int32_t max_splits) {
+  if (num_seqs < 1 || h_k < 1 || n_rows < 1 || d_v < 1 || max_splits < 1) return 0;
+  const size_t floats = (size_t)max_splits * num_seqs * h_k * n_rows * ((size_t)d_v + 2);
+  return (floats * 4 + 255) / 256 * 256;
+}
+
+extern "C" pkv_status pkv_decode_slots(const pkv_decode_args* a, int32_t* cu_count, int32_t* wg_per_cu,
+                                       int32_t* n_q_tiles) {
+  pkv_status st = check_shapes(a);
+  if (st != PKV_OK) return st;
+  if (!cu_count || !wg_per_cu || !n_q_tiles) return fail(PKV_ERR_INVALID_ARG, "slot outputs must be non-NULL");
+  int dev = 0, cus = 0, wgs = 0;
+  if ((st = hip_status(hipGetDevice(&dev), "hipGetDevice")) != PKV_OK) return st;
+  if ((st = hip_status(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "CU count")) != PKV_OK)
+    return st;
+  const int64_t rows = (int64_t)a->q_len * (a->h_q / a->h_k);
+  int per_tile;
+  if (a->kv_format == PKV_KV_MLA) {
+    per_tile = mla_rows_per_tile(*a);
+    st = hip_status(mla_occupancy(*a, &wgs), "occupancy");
+  } else {
+    const GqaVariant v = gqa_variant(*a);
+    per_tile = gqa_rows_per_tile(v);
+    st = hip_status(gqa_occupancy(v, &wgs), "occupancy");
+  }
+  if (st != PKV_OK) return st;
+  *cu_count = cus;
+  *wg_per_cu = wgs < 1 ? 1 : wgs;
+  *n_q_tiles = (int32_t)((rows + per_tile - 1) / per_tile);
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_paged_decode_attn(const pkv_decode_args* a, void* stream) {
+  pkv_status st = check_shapes(a);
+  if (st != PKV_OK) return st;
+  if ((st = check_pointers(a, false)) != PKV_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a->kv_format == PKV_KV_MLA) return hip_status(mla_launch(*a, s), "latent decode launch");
+  return hip_status(gqa_launch(*a, gqa_variant(*a), s), "decode launch");
+}
+
+extern "C" pkv_status pkv_merge_splits(const pkv_decode_args* a, void* stream) {
+  pkv_status st = check_shapes(a);
+  if (st != PKV_OK) return st;
+  if ((st = check_pointers(a, true)) != PKV_OK) return st;
+  if (a->max_splits == 1) return PKV_OK;
+  return hip_status(merge_launch(*a, static_cast<hipStream_t>(stream)), "merge launch");
+}

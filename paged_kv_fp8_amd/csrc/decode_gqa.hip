@@ -1,0 +1,476 @@
+// Split-KV paged decode attention over an e4m3 K/V cache, d = 128, for
+// gfx950 (MI355X).
+//
+// Method: "mjolnir-kernel 0.1.0 wheel: mjolnir/t5_decode.py", module
+// docstring (tensor contract, qi-major query packing, causal tail / block
+// mode, split-KV work items, direct write of unsplit sequences) and its
+// decode kernel (online softmax with the running max kept in raw-score
+// units, the -inf guard, the sum of unrounded probabilities, descales folded
+// into the exponent and the output scale, lazy rescale of O). The MMA
+// orientation -- keys on the M side, the few query rows of a GQA group on N
+// -- is the swap-AB idea of "vLLM PR #62633" (Kernel design, MMA shape).
+//
+// gfx950 design (not the pages'):
+//  * One wavefront per workgroup, one workgroup per (work item, kv head,
+//    q-row tile). Each wave streams its chunk of keys 32 at a time straight
+//    from HBM into registers, one 32-key block ahead of the math; there is no
+//    LDS staging and no barrier.
+//  * QK^T: v_mfma_f32_16x16x32_{bf16,fp8}, A = 16 keys x 32 head-dim slots,
+//    B = the q rows. Because the head-dim contraction is order-free, a lane's
+//    A slots are whatever 32 bytes of its key row it loaded with two 16-byte
+//    loads (bytes 16*g4.. and 64+16*g4..); q is loaded once with the same
+//    permutation.
+//  * PV: O^T (d_v x rows) += V^T (d_v x 32 keys) * P^T (32 keys x rows). The
+//    key order of the contraction is chosen equal to the order in which the
+//    QK^T accumulator already holds P (lane (n, g4) holds keys 4*g4+i and
+//    16+4*g4+i), so P needs no lane exchange. V^T is built in registers: a
+//    lane loads 8 consecutive d_v bytes of each of its 8 keys (coalesced: 4
+//    rows x 128 B per load instruction) and transposes them with v_perm_b32
+//    (plus the exact e4m3 -> bf16 converts on the bf16 path). dv-tile mt row
+//    m is d_v index 8*m + mt, which makes each lane's final O a run of 32
+//    contiguous d_v values of one query row.
+//  * Row statistics: the max needs two cross-lane steps (lanes 16 and 32
+//    apart); the sum stays per lane until the epilogue.
+//  * Page lookups: a lane holds the page of one 16-key group for a window of
+//    64 groups (1024 keys); the block's two pages are read with readlane.
+//    Keys past L are clamped to L - 1 (a real, finite row; masked), so no
+//    block-table entry at or past ceil(L / page_size) and no cache row at or
+//    past L is ever read.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kD = 128;          // head dim (qk and v)
+constexpr int kTileKeys = 128;   // planner tile
+constexpr int kBlockKeys = 32;   // keys per main-loop step
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kP8Scale = 448.0f;  // fp8 P is stored as e4m3(p * 448)
+
+struct GqaParams {
+  const uint8_t* q;   // byte address
+  int64_t q_tok, q_head;  // bytes
+  const uint8_t* k;
+  int64_t k_page, k_row, k_head;  // bytes
+  const uint8_t* v;
+  int64_t v_page, v_row, v_head;
+  const int32_t* block_table;
+  int64_t bt_row;
+  const int32_t* seq_lens;
+  const float* qd;
+  int64_t qd_seq, qd_head;
+  const float* kd;
+  int64_t kd_seq, kd_head;
+  const float* vd;
+  int64_t vd_seq, vd_head;
+  uint8_t* o;
+  int64_t o_tok, o_head;  // bytes
+  float* lse;
+  const int4* work;
+  const int32_t* n_splits;
+  float* ws_o;   // [max_splits][num_seqs][h_k][rows][128]
+  float2* ws_ml; // [max_splits][num_seqs][h_k][rows]
+  float scale_log2e, scale, o_scale;
+  int num_seqs, q_len, h_k, h_r, rows, page_shift, num_pages, max_blocks, max_splits;
+};
+
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint2 x) {
+  // exact: every e4m3 value is a bf16 value
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, false);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, true);
+  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, false);
+  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ uint2 half_of(uint4 x, int h) { return h ? uint2{x.z, x.w} : uint2{x.x, x.y}; }
+
+__device__ __forceinline__ long as_long(uint2 x) {
+  return (long)(((unsigned long long)x.y << 32) | x.x);
+}
+
+__device__ __forceinline__ float wave_max16(float x) {
+  // max over the four lanes {l, l^16, l^32, l^48} holding one query row
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum16(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Raw bytes of one 32-key block as this lane loads them.
+struct RawBlock {
+  uint4 k[2][2];  // [M tile t][half]: key kb+16t+r16, bytes 16*g4.. and 64+16*g4..
+  uint2 v[8];     // key kb+16*(j>>2)+4*g4+(j&3), bytes 8*r16 .. 8*r16+7
+};
+
+template <bool FP8Q, int NB, bool CAUSAL_TAIL>
+__global__ __launch_bounds__(64) void gqa_decode_kernel(GqaParams p) {
+  const int lane = threadIdx.x;
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+
+  const int4 w = p.work[blockIdx.x];
+  const int b = w.x;
+  if (w.z <= w.y || b < 0 || b >= p.num_seqs) return;  // padding item / bad entry
+  const int ns = p.n_splits[b];
+  const bool direct = ns <= 1;
+  const int slot = w.w;
+  if (!direct && (slot < 0 || slot >= p.max_splits)) return;
+  const int g = blockIdx.y;
+  const int row0 = blockIdx.z * (16 * NB);
+
+  const int page_size = 1 << p.page_shift;
+  int L = p.seq_lens[b];
+  L = max(0, min(L, p.max_blocks * page_size));
+  const int k_begin = w.y * kTileKeys;
+  const int k_end = min(w.z * kTileKeys, L);
+
+  // ---- query rows of this wave --------------------------------------------
+  int lim[NB];
+  bool row_ok[NB];
+  int qtok[NB], qhead[NB];
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = row0 + 16 * nb + r16;
+    row_ok[nb] = n < p.rows;
+    const int qi = n / p.h_r;
+    qtok[nb] = b * p.q_len + qi;
+    qhead[nb] = g * p.h_r + (n - qi * p.h_r);
+    lim[nb] = CAUSAL_TAIL ? L - p.q_len + qi : L - 1;
+  }
+  const int lim_min = CAUSAL_TAIL ? L - p.q_len : L - 1;
+
+  const float qd = FP8Q ? p.qd[b * p.qd_seq + g * p.qd_head] : 1.0f;
+  const float kdv = p.kd[b * p.kd_seq + g * p.kd_head];
+  const float vdv = p.vd[b * p.vd_seq + g * p.vd_head];
+  const float c2 = p.scale_log2e * qd * kdv;  // exponent scale (base 2) on raw scores
+  const float cs = p.scale * qd * kdv;        // natural-log scale of the running max
+
+  // B operand of QK^T: lane (n = r16, g4), k-step s holds q[n][64*(s>>1) + 16*g4 + 8*(s&1) + 0..7]
+  bf16x8 qb[NB][4];
+  long q8[NB][4];
+  for (int nb = 0; nb < NB; ++nb) {
+    const uint8_t* qrow = p.q + (int64_t)qtok[nb] * p.q_tok + (int64_t)qhead[nb] * p.q_head;
+    for (int s = 0; s < 4; ++s) {
+      const int d = 64 * (s >> 1) + 16 * g4 + 8 * (s & 1);
+      if (FP8Q) {
+        q8[nb][s] = row_ok[nb] ? *reinterpret_cast<const long*>(qrow + d) : 0;
+      } else {
+        if (row_ok[nb]) {
+          qb[nb][s] = *reinterpret_cast<const bf16x8*>(qrow + 2 * d);
+        } else {
+          for (int e = 0; e < 8; ++e) qb[nb][s][e] = (__bf16)0.0f;
+        }
+      }
+    }
+  }
+
+  f32x4 oacc[NB][8];
+  float m_run[NB], l_part[NB];
+  for (int nb = 0; nb < NB; ++nb) {
+    for (int mt = 0; mt < 8; ++mt) oacc[nb][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[nb] = -INFINITY;
+    l_part[nb] = 0.f;
+  }
+
+  if (k_end > k_begin) {
+    const int32_t* bt = p.block_table + (int64_t)b * p.bt_row;
+    // page of 16-key group G0 + lane (clamped into the sequence and the pool)
+    auto load_window = [&](int key0) -> int {
+      const int key = min(key0 + 16 * lane, L - 1);
+      const int pg = bt[key >> p.page_shift];
+      return min(max(pg, 0), p.num_pages - 1);
+    };
+    auto load_block = [&](int kb, int win, int win_base) {
+      RawBlock r;
+      const int gi = (kb - win_base) >> 4;  // group index of the block inside the window (even)
+      const int pg0 = __builtin_amdgcn_readlane(win, gi);
+      const int pg1 = __builtin_amdgcn_readlane(win, gi + 1);
+      const uint8_t* kbase0 = p.k + (int64_t)pg0 * p.k_page + (int64_t)g * p.k_head;
+      const uint8_t* kbase1 = p.k + (int64_t)pg1 * p.k_page + (int64_t)g * p.k_head;
+      const uint8_t* vbase0 = p.v + (int64_t)pg0 * p.v_page + (int64_t)g * p.v_head;
+      const uint8_t* vbase1 = p.v + (int64_t)pg1 * p.v_page + (int64_t)g * p.v_head;
+      const int pmask = page_size - 1;
+      for (int t = 0; t < 2; ++t) {
+        const int row = min(kb + 16 * t + r16, L - 1) & pmask;
+        const uint8_t* kp = (t ? kbase1 : kbase0) + (int64_t)row * p.k_row;
+        r.k[t][0] = *reinterpret_cast<const uint4*>(kp + 16 * g4);
+        r.k[t][1] = *reinterpret_cast<const uint4*>(kp + 64 + 16 * g4);
+      }
+      for (int j = 0; j < 8; ++j) {
+        const int t = j >> 2;
+        const int row = min(kb + 16 * t + 4 * g4 + (j & 3), L - 1) & pmask;
+        const uint8_t* vp = (t ? vbase1 : vbase0) + (int64_t)row * p.v_row;
+        r.v[j] = *reinterpret_cast<const uint2*>(vp + 8 * r16);
+      }
+      return r;
+    };
+
+    int win_base = k_begin;
+    int win_cur = load_window(win_base);
+    int win_nxt = (win_base + 1024 < k_end) ? load_window(win_base + 1024) : win_cur;
+    RawBlock cur = load_block(k_begin, win_cur, win_base);
+
+    for (int kb = k_begin; kb < k_end; kb += kBlockKeys) {
+      // ---- prefetch the next block (and the next page window) ------------
+      RawBlock nxt;
+      const int kn = kb + kBlockKeys;
+      if (kn < k_end) {
+        if (kn - win_base >= 1024) {
+          win_base += 1024;
+          win_cur = win_nxt;
+          if (win_base + 1024 < k_end) win_nxt = load_window(win_base + 1024);
+        }
+        nxt = load_block(kn, win_cur, win_base);
+      }
+
+      // ---- S = K Q^T (keys on M) -----------------------------------------
+      f32x4 sacc[NB][2];
+      for (int nb = 0; nb < NB; ++nb)
+        for (int t = 0; t < 2; ++t) sacc[nb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < 2; ++t) {
+        for (int s = 0; s < 4; ++s) {
+          const uint2 kraw = half_of(cur.k[t][s >> 1], s & 1);
+          if (FP8Q) {
+            const long a = as_long(kraw);
+            for (int nb = 0; nb < NB; ++nb)
+              sacc[nb][t] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, q8[nb][s], sacc[nb][t], 0, 0, 0);
+          } else {
+            const bf16x8 a = e4m3x8_to_bf16(kraw);
+            for (int nb = 0; nb < NB; ++nb)
+              sacc[nb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[nb][s], sacc[nb][t], 0, 0, 0);
+          }
+        }
+      }
+
+      // ---- online softmax (per query row = lane column r16) --------------
+      bf16x8 pb[NB];
+      long p8[NB];
+      const bool need_mask = kb + kBlockKeys - 1 > lim_min;
+      for (int nb = 0; nb < NB; ++nb) {
+        if (need_mask) {
+          for (int t = 0; t < 2; ++t)
+            for (int i = 0; i < 4; ++i)
+              if (kb + 16 * t + 4 * g4 + i > lim[nb]) sacc[nb][t][i] = -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(fmaxf(sacc[nb][0][0], sacc[nb][0][1]), fmaxf(sacc[nb][0][2], sacc[nb][0][3])),
+                         fmaxf(fmaxf(sacc[nb][1][0], sacc[nb][1][1]), fmaxf(sacc[nb][1][2], sacc[nb][1][3])));
+        mx = wave_max16(mx);
+        const float m_new = fmaxf(m_run[nb], mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;  // no visible key yet: exp2(-inf) = 0
+        const float corr = __builtin_amdgcn_exp2f((m_run[nb] - m_use) * c2);
+        float pr[8];
+        float psum = 0.f;
+        for (int t = 0; t < 2; ++t)
+          for (int i = 0; i < 4; ++i) {
+            pr[4 * t + i] = __builtin_amdgcn_exp2f((sacc[nb][t][i] - m_use) * c2);
+            psum += pr[4 * t + i];
+          }
+        l_part[nb] = l_part[nb] * corr + psum;
+        // rescale O only if some row's max moved (otherwise corr == 1 exactly)
+        if (__builtin_amdgcn_ballot_w64(m_new != m_run[nb])) {
+          for (int mt = 0; mt < 8; ++mt) oacc[nb][mt] *= corr;
+        }
+        m_run[nb] = m_new;
+        if (FP8Q) {
+          int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0] * kP8Scale, pr[1] * kP8Scale, 0, false);
+          lo = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2] * kP8Scale, pr[3] * kP8Scale, lo, true);
+          int hi = __builtin_amdgcn_cvt_pk_fp8_f32(pr[4] * kP8Scale, pr[5] * kP8Scale, 0, false);
+          hi = __builtin_amdgcn_cvt_pk_fp8_f32(pr[6] * kP8Scale, pr[7] * kP8Scale, hi, true);
+          p8[nb] = as_long(uint2{(unsigned)lo, (unsigned)hi});
+        } else {
+          for (int e = 0; e < 8; ++e) pb[nb][e] = (__bf16)pr[e];
+        }
+      }
+
+      // ---- O^T += V^T P^T --------------------------------------------------
+      if (FP8Q) {
+        // 4x4 byte transposes: quad kq of keys, word w of d_v bytes
+        for (int w2 = 0; w2 < 2; ++w2) {
+          unsigned col[2][4];  // [kq][e]: keys 4kq..4kq+3 at d_v 8*r16 + 4*w2 + e
+          for (int kq = 0; kq < 2; ++kq) {
+            const unsigned r0 = w2 ? cur.v[4 * kq + 0].y : cur.v[4 * kq + 0].x;
+            const unsigned r1 = w2 ? cur.v[4 * kq + 1].y : cur.v[4 * kq + 1].x;
+            const unsigned r2 = w2 ? cur.v[4 * kq + 2].y : cur.v[4 * kq + 2].x;
+            const unsigned r3 = w2 ? cur.v[4 * kq + 3].y : cur.v[4 * kq + 3].x;
+            const unsigned t0 = __builtin_amdgcn_perm(r0, r1, 0x01050004u);
+            const unsigned t1 = __builtin_amdgcn_perm(r0, r1, 0x03070206u);
+            const unsigned t2 = __builtin_amdgcn_perm(r2, r3, 0x01050004u);
+            const unsigned t3 = __builtin_amdgcn_perm(r2, r3, 0x03070206u);
+            col[kq][0] = __builtin_amdgcn_perm(t0, t2, 0x01000504u);
+            col[kq][1] = __builtin_amdgcn_perm(t0, t2, 0x03020706u);
+            col[kq][2] = __builtin_amdgcn_perm(t1, t3, 0x01000504u);
+            col[kq][3] = __builtin_amdgcn_perm(t1, t3, 0x03020706u);
+          }
+          for (int e = 0; e < 4; ++e) {
+            const long a = as_long(uint2{col[0][e], col[1][e]});
+            const int mt = 4 * w2 + e;
+            for (int nb = 0; nb < NB; ++nb)
+              oacc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, p8[nb], oacc[nb][mt], 0, 0, 0);
+          }
+        }
+      } else {
+        for (int w2 = 0; w2 < 2; ++w2) {
+          unsigned xy[4][2];  // [key pair pp][0: d_v bytes 0,1 / 1: bytes 2,3 of the word], interleaved by key
+          for (int pp = 0; pp < 4; ++pp) {
+            const unsigned a0 = w2 ? cur.v[2 * pp].y : cur.v[2 * pp].x;
+            const unsigned a1 = w2 ? cur.v[2 * pp + 1].y : cur.v[2 * pp + 1].x;
+            xy[pp][0] = __builtin_amdgcn_perm(a0, a1, 0x01050004u);
+            xy[pp][1] = __builtin_amdgcn_perm(a0, a1, 0x03070206u);
+          }
+          for (int e = 0; e < 4; ++e) {
+            bf16x8 a;
+            for (int pp = 0; pp < 4; ++pp) {
+              const bf16x2 two = (e & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(xy[pp][e >> 1], 1.0f, true)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(xy[pp][e >> 1], 1.0f, false);
+              a[2 * pp] = two[0];
+              a[2 * pp + 1] = two[1];
+            }
+            const int mt = 4 * w2 + e;
+            for (int nb = 0; nb < NB; ++nb)
+              oacc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[nb], oacc[nb][mt], 0, 0, 0);
+          }
+        }
+      }
+      cur = nxt;
+    }
+  }
+
+  // ---- epilogue -------------------------------------------------------------
+  const float p_scale = FP8Q ? kP8Scale : 1.0f;
+  for (int nb = 0; nb < NB; ++nb) {
+    const float l = wave_sum16(l_part[nb]);
+    if (!row_ok[nb]) continue;
+    const int n = row0 + 16 * nb + r16;
+    const int64_t stat_row = ((int64_t)b * p.h_k + g) * p.rows + n;
+    const float m_nat = m_run[nb] == -INFINITY ? -INFINITY : m_run[nb] * cs;
+    // lane holds O^T[d_v = 32*g4 + 8*i + mt][n] in oacc[nb][mt][i]
+    if (direct) {
+      const float inv = l > 0.f ? (p.o_scale * vdv / p_scale) / l : 0.f;
+      uint8_t* orow = p.o + (int64_t)qtok[nb] * p.o_tok + (int64_t)qhead[nb] * p.o_head;
+      for (int i = 0; i < 4; ++i) {
+        bf16x8 out;
+        for (int mt = 0; mt < 8; ++mt) out[mt] = (__bf16)(oacc[nb][mt][i] * inv);
+        *reinterpret_cast<bf16x8*>(orow + 2 * (32 * g4 + 8 * i)) = out;
+      }
+      if (g4 == 0) p.lse[stat_row] = l > 0.f ? m_nat + logf(l) : -INFINITY;
+    } else {
+      const int64_t prow = (int64_t)slot * p.num_seqs * p.h_k * p.rows + stat_row;
+      const float ps = vdv / p_scale;
+      float* dst = p.ws_o + prow * kD + 32 * g4;
+      for (int i = 0; i < 4; ++i) {
+        f32x4 lo4 = {oacc[nb][0][i], oacc[nb][1][i], oacc[nb][2][i], oacc[nb][3][i]};
+        f32x4 hi4 = {oacc[nb][4][i], oacc[nb][5][i], oacc[nb][6][i], oacc[nb][7][i]};
+        *reinterpret_cast<f32x4*>(dst + 8 * i) = lo4 * ps;
+        *reinterpret_cast<f32x4*>(dst + 8 * i + 4) = hi4 * ps;
+      }
+      if (g4 == 0) p.ws_ml[prow] = float2{m_nat, l};
+    }
+  }
+}
+
+template <bool FP8Q, int NB, bool CT>
+const void* kernel_ptr() {
+  return reinterpret_cast<const void*>(&gqa_decode_kernel<FP8Q, NB, CT>);
+}
+
+const void* select_kernel(const GqaVariant& v) {
+  const int nb = v.n_blocks;
+  if (v.fp8_q) {
+    if (nb == 1) return v.causal_tail ? kernel_ptr<true, 1, true>() : kernel_ptr<true, 1, false>();
+    return v.causal_tail ? kernel_ptr<true, 2, true>() : kernel_ptr<true, 2, false>();
+  }
+  if (nb == 1) return v.causal_tail ? kernel_ptr<false, 1, true>() : kernel_ptr<false, 1, false>();
+  return v.causal_tail ? kernel_ptr<false, 2, true>() : kernel_ptr<false, 2, false>();
+}
+
+int log2_exact(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+}  // namespace
+
+GqaVariant gqa_variant(const pkv_decode_args& a) {
+  GqaVariant v;
+  v.fp8_q = a.q_format == PKV_Q_E4M3;
+  const int rows = a.q_len * (a.h_q / a.h_k);
+  v.n_blocks = rows <= 16 ? 1 : 2;
+  v.causal_tail = a.causal && a.q_len > 1;
+  return v;
+}
+
+int gqa_rows_per_tile(const GqaVariant& v) { return 16 * v.n_blocks; }
+
+hipError_t gqa_occupancy(const GqaVariant& v, int* wg_per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(wg_per_cu, select_kernel(v), 64, 0);
+}
+
+hipError_t gqa_launch(const pkv_decode_args& a, const GqaVariant& v, hipStream_t stream) {
+  GqaParams p;
+  const int64_t qe = a.q_format == PKV_Q_BF16 ? 2 : 1;
+  p.q = static_cast<const uint8_t*>(a.q);
+  p.q_tok = a.q_tok_stride * qe;
+  p.q_head = a.q_head_stride * qe;
+  p.k = a.k;
+  p.k_page = a.k_page_stride;
+  p.k_row = a.k_row_stride;
+  p.k_head = a.k_head_stride;
+  p.v = a.v;
+  p.v_page = a.v_page_stride;
+  p.v_row = a.v_row_stride;
+  p.v_head = a.v_head_stride;
+  p.block_table = a.block_table;
+  p.bt_row = a.bt_row_stride;
+  p.seq_lens = a.seq_lens;
+  p.qd = a.q_descale ? a.q_descale : a.k_descale;  // unused for bf16 q
+  p.qd_seq = a.q_descale ? a.qd_seq_stride : 0;
+  p.qd_head = a.q_descale ? a.qd_head_stride : 0;
+  p.kd = a.k_descale;
+  p.kd_seq = a.kd_seq_stride;
+  p.kd_head = a.kd_head_stride;
+  p.vd = a.v_descale;
+  p.vd_seq = a.vd_seq_stride;
+  p.vd_head = a.vd_head_stride;
+  p.o = static_cast<uint8_t*>(a.o);
+  p.o_tok = a.o_tok_stride * 2;
+  p.o_head = a.o_head_stride * 2;
+  p.lse = a.lse;
+  p.work = reinterpret_cast<const int4*>(a.work);
+  p.n_splits = a.n_splits;
+  const int64_t rows_all = ws_rows(a);
+  p.ws_o = static_cast<float*>(a.workspace);
+  p.ws_ml = a.workspace ? reinterpret_cast<float2*>(p.ws_o + (int64_t)a.max_splits * rows_all * kD) : nullptr;
+  p.scale_log2e = (float)((double)a.softmax_scale * 1.4426950408889634);
+  p.scale = a.softmax_scale;
+  p.o_scale = a.o_scale;
+  p.num_seqs = a.num_seqs;
+  p.q_len = a.q_len;
+  p.h_k = a.h_k;
+  p.h_r = a.h_q / a.h_k;
+  p.rows = a.q_len * p.h_r;
+  p.page_shift = log2_exact(a.page_size);
+  p.num_pages = a.num_pages;
+  p.max_blocks = a.max_blocks;
+  p.max_splits = a.max_splits;
+  const int tiles = (p.rows + gqa_rows_per_tile(v) - 1) / gqa_rows_per_tile(v);
+  dim3 grid(a.num_work, a.h_k, tiles);
+  void* args[] = {&p};
+  return hipLaunchKernel(select_kernel(v), grid, dim3(64), args, 0, stream);
+}
+
+}  // namespace pkv

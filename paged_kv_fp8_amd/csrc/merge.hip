@@ -1,0 +1,115 @@
+// Combine of split-KV partials ("mjolnir-kernel 0.1.0 wheel:
+// mjolnir/t5_decode.py", reduction kernel and the module docstring's
+// "Workspace" paragraph): per row of a split sequence, the partials of the
+// splits it used are weighted by exp(m_j - max m) and normalised by the
+// weighted sum of the l_j. Only the splits a sequence used are read, so the
+// workspace needs no initialisation; sequences with one split were written
+// by the decode and are skipped. The j order is fixed, so the result is
+// deterministic.
+//
+// gfx950 layout: one thread owns 8 consecutive d_v values of one row
+// (two 16-byte loads per split, one 16-byte bf16 store), 256 threads per
+// workgroup; the (max, sum) pairs of a row are read by all its threads from
+// the same cache lines.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct MergeParams {
+  const float* ws_o;
+  const float2* ws_ml;
+  const int32_t* n_splits;
+  uint8_t* o;
+  int64_t o_tok, o_head;  // bytes
+  float* lse;
+  int64_t total_rows;  // num_seqs * h_k * rows
+  int64_t split_stride;  // rows between consecutive split slots (= total_rows)
+  float o_scale;
+  int h_k, rows, h_r, q_len, d_v, max_splits;
+};
+
+template <int DV>
+__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
+  constexpr int kThreadsPerRow = DV / 8;
+  constexpr int kRowsPerBlock = 256 / kThreadsPerRow;
+  const int tr = threadIdx.x / kThreadsPerRow;
+  const int tc = threadIdx.x % kThreadsPerRow;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + tr;
+  if (row >= p.total_rows) return;
+  const int b = (int)(row / ((int64_t)p.h_k * p.rows));
+  const int rem = (int)(row - (int64_t)b * p.h_k * p.rows);
+  const int g = rem / p.rows;
+  const int n = rem - g * p.rows;
+  int ns = p.n_splits[b];
+  if (ns <= 1) return;  // written by the decode
+  ns = min(ns, p.max_splits);
+
+  float m_star = -INFINITY;
+  for (int j = 0; j < ns; ++j) m_star = fmaxf(m_star, p.ws_ml[j * p.split_stride + row].x);
+
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  for (int j = 0; j < ns; ++j) {
+    const float2 ml = p.ws_ml[j * p.split_stride + row];
+    const float wgt = ml.x == -INFINITY ? 0.f : __expf(ml.x - m_star);
+    const float* src = p.ws_o + (j * p.split_stride + row) * DV + 8 * tc;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+    const f32x4 c = *reinterpret_cast<const f32x4*>(src + 4);
+    den += wgt * ml.y;
+    acc0 += wgt * a;
+    acc1 += wgt * c;
+  }
+  const float inv = den > 0.f ? p.o_scale / den : 0.f;
+  const int qi = n / p.h_r;
+  const int hr = n - qi * p.h_r;
+  uint8_t* orow = p.o + (int64_t)(b * p.q_len + qi) * p.o_tok + (int64_t)(g * p.h_r + hr) * p.o_head;
+  bf16x8 out;
+  for (int e = 0; e < 4; ++e) {
+    out[e] = (__bf16)(acc0[e] * inv);
+    out[4 + e] = (__bf16)(acc1[e] * inv);
+  }
+  *reinterpret_cast<bf16x8*>(orow + 2 * (8 * tc)) = out;
+  if (tc == 0) p.lse[row] = den > 0.f ? m_star + logf(den) : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t merge_launch(const pkv_decode_args& a, hipStream_t stream) {
+  MergeParams p;
+  const int64_t rows_all = ws_rows(a);
+  p.ws_o = static_cast<const float*>(a.workspace);
+  p.ws_ml = reinterpret_cast<const float2*>(p.ws_o + (int64_t)a.max_splits * rows_all * a.d_v);
+  p.n_splits = a.n_splits;
+  p.o = static_cast<uint8_t*>(a.o);
+  p.o_tok = a.o_tok_stride * 2;
+  p.o_head = a.o_head_stride * 2;
+  p.lse = a.lse;
+  p.total_rows = rows_all;
+  p.split_stride = rows_all;
+  p.o_scale = a.o_scale;
+  p.h_k = a.h_k;
+  p.h_r = a.h_q / a.h_k;
+  p.q_len = a.q_len;
+  p.rows = a.q_len * p.h_r;
+  p.d_v = a.d_v;
+  p.max_splits = a.max_splits;
+  void* args[] = {&p};
+  if (a.d_v == 128) {
+    const int64_t blocks = (rows_all + 15) / 16;
+    return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<128>), dim3((unsigned)blocks), dim3(256),
+                           args, 0, stream);
+  }
+  const int64_t blocks = (rows_all + 3) / 4;
+  return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<512>), dim3((unsigned)blocks), dim3(256), args,
+                         0, stream);
+}
+
+}  // namespace pkv

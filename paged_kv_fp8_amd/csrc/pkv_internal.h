@@ -1,0 +1,42 @@
+// Internal declarations shared by the host entry points and the kernel
+// launchers of libpkvfp8.so. Not installed; the public ABI is pkv_fp8.h.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+#include "pkv_fp8.h"
+
+namespace pkv {
+
+// Records a one-line reason for the calling thread's current failure and
+// returns `code`, so call sites read `return fail(PKV_ERR_..., "...", ...)`.
+pkv_status fail(pkv_status code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+// Kernel selection for the e4m3 K/V cache (d = 128) family.
+struct GqaVariant {
+  bool fp8_q;       // e4m3 Q, e4m3 P, fp8 MFMA; else bf16 Q, bf16 P, bf16 MFMA
+  int n_blocks;     // 16-row N blocks per wave (1 or 2)
+  bool causal_tail; // q_len > 1 && causal
+};
+GqaVariant gqa_variant(const pkv_decode_args& a);
+int gqa_rows_per_tile(const GqaVariant& v);
+hipError_t gqa_occupancy(const GqaVariant& v, int* wg_per_cu);
+hipError_t gqa_launch(const pkv_decode_args& a, const GqaVariant& v, hipStream_t stream);
+
+// Latent-record (MLA) family.
+int mla_rows_per_tile(const pkv_decode_args& a);
+hipError_t mla_occupancy(const pkv_decode_args& a, int* wg_per_cu);
+hipError_t mla_launch(const pkv_decode_args& a, hipStream_t stream);
+
+// Combine of split partials.
+hipError_t merge_launch(const pkv_decode_args& a, hipStream_t stream);
+
+// Workspace partition, in floats: partial O of every (split, seq, head,
+// row) first, then its (max, sum) pair.
+inline int64_t ws_rows(const pkv_decode_args& a) {
+  return (int64_t)a.num_seqs * a.h_k * a.q_len * (a.h_q / a.h_k);
+}
+
+}  // namespace pkv

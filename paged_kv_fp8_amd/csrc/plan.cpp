@@ -1,0 +1,111 @@
+// Occupancy-pinned split-KV planner (host only).
+//
+// Rule of "mjolnir-kernel 0.1.0 wheel: mjolnir/t5_decode.py", plan_split_kv
+// and its module docstring ("Split-KV scheduling is occupancy-pinned"): pick
+// the smallest contiguous chunk of 128-key tiles such that the chunks of all
+// sequences fit one wave of workgroup slots, capped at max_splits chunks per
+// sequence; emit one work item per chunk, longest first.
+#include <algorithm>
+#include <cstdint>
+#include <vector>
+
+#include "pkv_internal.h"
+
+namespace {
+
+constexpr int64_t kTileKeys = 128;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Item {
+  int32_t seq, begin, end, slot;
+};
+
+}  // namespace
+
+extern "C" pkv_status pkv_plan_split_kv(const int32_t* seq_lens, int32_t num_seqs, int32_t h_k, int32_t n_q_tiles,
+                                        int32_t cu_count, int32_t wg_per_cu, int32_t max_splits,
+                                        int32_t force_splits, int32_t min_chunk_tiles, int32_t pad_to,
+                                        int32_t* work_out, int32_t work_cap, int32_t* n_splits_out,
+                                        pkv_plan_info* info) {
+  using pkv::fail;
+  if (!seq_lens || !work_out || !n_splits_out) return fail(PKV_ERR_INVALID_ARG, "plan: NULL array");
+  if (num_seqs < 1) return fail(PKV_ERR_INVALID_ARG, "plan: num_seqs=%d < 1", num_seqs);
+  if (h_k < 1 || n_q_tiles < 1 || cu_count < 1 || wg_per_cu < 1 || max_splits < 1 || min_chunk_tiles < 1)
+    return fail(PKV_ERR_INVALID_ARG, "plan: sizes must be >= 1 (h_k=%d n_q_tiles=%d cu=%d wg/cu=%d max_splits=%d "
+                "min_chunk=%d)", h_k, n_q_tiles, cu_count, wg_per_cu, max_splits, min_chunk_tiles);
+  if (force_splits < 0 || pad_to < 0 || work_cap < 0)
+    return fail(PKV_ERR_INVALID_ARG, "plan: force_splits, pad_to and work_cap must be >= 0");
+  if (max_splits > PKV_MAX_SPLITS)
+    return fail(PKV_ERR_UNSUPPORTED, "plan: max_splits=%d > %d", max_splits, PKV_MAX_SPLITS);
+
+  std::vector<int64_t> tiles(num_seqs);
+  int64_t t_max = 1;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    if (seq_lens[b] < 0) return fail(PKV_ERR_INVALID_ARG, "plan: seq_lens[%d]=%d < 0", b, seq_lens[b]);
+    tiles[b] = std::max<int64_t>(1, ceil_div(seq_lens[b], kTileKeys));
+    t_max = std::max(t_max, tiles[b]);
+  }
+  const int64_t slots = std::max<int64_t>(1, ((int64_t)cu_count * wg_per_cu) / ((int64_t)h_k * n_q_tiles));
+  const int64_t lo = std::max<int64_t>(min_chunk_tiles, ceil_div(t_max, max_splits));
+  auto n_chunks = [&](int64_t c) {
+    int64_t s = 0;
+    for (int64_t t : tiles) s += ceil_div(t, c);
+    return s;
+  };
+
+  int64_t chunk;
+  if (force_splits > 0) {
+    chunk = std::max(lo, ceil_div(t_max, force_splits));
+  } else if (num_seqs >= slots || max_splits == 1) {
+    chunk = t_max;
+  } else {
+    // n_chunks is non-increasing in c and t_max always fits (one chunk per
+    // sequence, num_seqs < slots): bisect for the smallest fitting c.
+    int64_t a = lo, z = t_max;
+    while (a < z) {
+      const int64_t mid = a + (z - a) / 2;
+      if (n_chunks(mid) <= slots)
+        z = mid;
+      else
+        a = mid + 1;
+    }
+    chunk = a;
+  }
+
+  std::vector<Item> items;
+  int32_t max_ns = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t k = ceil_div(tiles[b], chunk);
+    if (k > max_splits)
+      return fail(PKV_ERR_UNSUPPORTED, "plan: sequence %d needs %lld chunks > max_splits=%d", b, (long long)k,
+                  max_splits);
+    n_splits_out[b] = (int32_t)k;
+    max_ns = std::max<int32_t>(max_ns, (int32_t)k);
+    for (int64_t j = 0; j < k; ++j)
+      items.push_back({b, (int32_t)(j * chunk), (int32_t)std::min((j + 1) * chunk, tiles[b]), (int32_t)j});
+  }
+  std::stable_sort(items.begin(), items.end(),
+                   [](const Item& x, const Item& y) { return (x.end - x.begin) > (y.end - y.begin); });
+  const int64_t n_real = (int64_t)items.size();
+  if (pad_to && pad_to < n_real)
+    return fail(PKV_ERR_CAPACITY, "plan: pad_to=%d < %lld work items", pad_to, (long long)n_real);
+  const int64_t n_total = pad_to ? pad_to : n_real;
+  if (n_total > work_cap)
+    return fail(PKV_ERR_CAPACITY, "plan: %lld work items > work_cap=%d", (long long)n_total, work_cap);
+  for (int64_t i = 0; i < n_total; ++i) {
+    const Item it = i < n_real ? items[i] : Item{0, 0, 0, 0};
+    work_out[4 * i + 0] = it.seq;
+    work_out[4 * i + 1] = it.begin;
+    work_out[4 * i + 2] = it.end;
+    work_out[4 * i + 3] = it.slot;
+  }
+  if (info) {
+    info->num_work = (int32_t)n_total;
+    info->num_real = (int32_t)n_real;
+    info->chunk_tiles = (int32_t)chunk;
+    info->slots = (int32_t)std::min<int64_t>(slots, INT32_MAX);
+    info->max_n_splits = max_ns;
+  }
+  return PKV_OK;
+}

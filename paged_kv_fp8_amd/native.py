@@ -1,0 +1,147 @@
+"""ctypes binding of libpkvfp8.so (include/pkv_fp8.h), same entry-point names.
+
+Argument marshalling only: every step of the decode runs in the library's
+HIP kernels (or, for the planner, its host C++). Importing this module loads
+the library and raises ImportError if it is missing or does not match the
+header's struct layout; there is no fallback path.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkvfp8.so")
+
+PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_CAPACITY, PKV_ERR_WORKSPACE, PKV_ERR_HIP = 0, -1, -2, -3, -4, -5
+PKV_Q_BF16, PKV_Q_E4M3 = 0, 1
+PKV_KV_E4M3, PKV_KV_MLA = 0, 1
+PKV_MAX_SPLITS = 256
+
+# Every function the header declares, in declaration order.
+EXPORTS = ("pkv_status_string", "pkv_last_error", "pkv_version", "pkv_decode_args_size", "pkv_plan_split_kv",
+           "pkv_workspace_bytes", "pkv_decode_slots", "pkv_paged_decode_attn", "pkv_merge_splits")
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status, where, detail):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({detail})")
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("num_work", ctypes.c_int32), ("num_real", ctypes.c_int32), ("chunk_tiles", ctypes.c_int32),
+                ("slots", ctypes.c_int32), ("max_n_splits", ctypes.c_int32)]
+
+
+_i32, _i64, _f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+
+
+class DecodeArgs(ctypes.Structure):
+    """Mirror of ``pkv_decode_args`` (field for field, same order)."""
+    _fields_ = [
+        ("num_seqs", _i32), ("q_len", _i32), ("h_q", _i32), ("h_k", _i32), ("d_qk", _i32), ("d_v", _i32),
+        ("page_size", _i32), ("num_pages", _i32), ("max_blocks", _i32),
+        ("causal", _i32), ("q_format", _i32), ("kv_format", _i32),
+        ("softmax_scale", _f32), ("o_scale", _f32),
+        ("q", _vp), ("q_tok_stride", _i64), ("q_head_stride", _i64),
+        ("k", _vp), ("k_page_stride", _i64), ("k_row_stride", _i64), ("k_head_stride", _i64),
+        ("v", _vp), ("v_page_stride", _i64), ("v_row_stride", _i64), ("v_head_stride", _i64),
+        ("k_rope", _vp), ("rope_page_stride", _i64), ("rope_row_stride", _i64),
+        ("k_blk_scale", _vp), ("scale_page_stride", _i64), ("scale_row_stride", _i64),
+        ("block_table", _vp), ("bt_row_stride", _i64),
+        ("seq_lens", _vp),
+        ("q_descale", _vp), ("qd_seq_stride", _i64), ("qd_head_stride", _i64),
+        ("k_descale", _vp), ("kd_seq_stride", _i64), ("kd_head_stride", _i64),
+        ("v_descale", _vp), ("vd_seq_stride", _i64), ("vd_head_stride", _i64),
+        ("o", _vp), ("o_tok_stride", _i64), ("o_head_stride", _i64),
+        ("lse", _vp),
+        ("work", _vp), ("num_work", _i32),
+        ("n_splits", _vp), ("max_splits", _i32),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m paged_kv_fp8_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.pkv_status_string.argtypes = [_i32]
+    lib.pkv_last_error.restype = ctypes.c_char_p
+    lib.pkv_last_error.argtypes = []
+    lib.pkv_version.restype = _i32
+    lib.pkv_decode_args_size.restype = ctypes.c_size_t
+    P = ctypes.POINTER
+    lib.pkv_plan_split_kv.restype = _i32
+    lib.pkv_plan_split_kv.argtypes = [P(_i32), _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, P(_i32), _i32,
+                                      P(_i32), P(PlanInfo)]
+    lib.pkv_workspace_bytes.restype = ctypes.c_size_t
+    lib.pkv_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
+    lib.pkv_decode_slots.restype = _i32
+    lib.pkv_decode_slots.argtypes = [P(DecodeArgs), P(_i32), P(_i32), P(_i32)]
+    lib.pkv_paged_decode_attn.restype = _i32
+    lib.pkv_paged_decode_attn.argtypes = [P(DecodeArgs), _vp]
+    lib.pkv_merge_splits.restype = _i32
+    lib.pkv_merge_splits.argtypes = [P(DecodeArgs), _vp]
+    if lib.pkv_decode_args_size() != ctypes.sizeof(DecodeArgs):
+        raise ImportError(f"pkv_decode_args layout mismatch: library {lib.pkv_decode_args_size()} B, "
+                          f"binding {ctypes.sizeof(DecodeArgs)} B")
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status):
+    return lib.pkv_status_string(status).decode()
+
+
+def last_error():
+    return lib.pkv_last_error().decode()
+
+
+def _check(status, where):
+    if status != PKV_OK:
+        raise PkvError(status, where, last_error())
+
+
+def version():
+    return lib.pkv_version()
+
+
+def plan_split_kv(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16, force_splits=0, min_chunk_tiles=1,
+                  pad_to=0, work_cap=None):
+    """Host planner. Returns (work int32[num_work, 4], n_splits int32[num_seqs], PlanInfo)."""
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    nseq = lens.shape[0]
+    if work_cap is None:
+        work_cap = max(pad_to, int(max(1, nseq) * max(1, max_splits)))
+    work = np.zeros((max(work_cap, 1), 4), dtype=np.int32)
+    ns = np.zeros(max(nseq, 1), dtype=np.int32)
+    info = PlanInfo()
+    P = ctypes.POINTER(_i32)
+    st = lib.pkv_plan_split_kv(lens.ctypes.data_as(P), nseq, h_k, n_q_tiles, cu_count, wg_per_cu, max_splits,
+                               force_splits, min_chunk_tiles, pad_to, work.ctypes.data_as(P), work_cap,
+                               ns.ctypes.data_as(P), ctypes.byref(info))
+    _check(st, "pkv_plan_split_kv")
+    return work[:info.num_work].copy(), ns[:nseq].copy(), info
+
+
+def workspace_bytes(num_seqs, h_k, n_rows, d_v, max_splits):
+    return lib.pkv_workspace_bytes(num_seqs, h_k, n_rows, d_v, max_splits)
+
+
+def decode_slots(args):
+    cu, wg, nt = _i32(), _i32(), _i32()
+    _check(lib.pkv_decode_slots(ctypes.byref(args), ctypes.byref(cu), ctypes.byref(wg), ctypes.byref(nt)),
+           "pkv_decode_slots")
+    return cu.value, wg.value, nt.value
+
+
+def paged_decode_attn(args, stream=None):
+    _check(lib.pkv_paged_decode_attn(ctypes.byref(args), stream), "pkv_paged_decode_attn")
+
+
+def merge_splits(args, stream=None):
+    _check(lib.pkv_merge_splits(ctypes.byref(args), stream), "pkv_merge_splits")

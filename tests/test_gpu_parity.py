@@ -1,0 +1,245 @@
+"""GPU parity of the HIP decode path against the fp64 oracle, through the C ABI.
+
+Bars: max|dO| <= 1e-2 * max|V| and max|dLSE| <= 1e-3 on every workload
+(the decode path's accuracy contract); rows with no visible key exactly
+O = 0 / LSE = -inf; bit-identical results across repeats, graph replays,
+physical layouts and page permutations. Small variants of each workload are
+compared on every output (several 128-key tiles, ragged tails, split and
+unsplit sequences); the full-size workloads run with the same plan and launch
+configuration as bench.py and are compared on sampled sequences (the
+longest, the shortest and random ones), all rows and heads of each.
+
+The fp8-query path rounds P to e4m3(p * 448) as its design states; for the
+short edge-case sequences below (L < 1024, not a stated workload) its bound is
+derived instead: |dO| <= (2^-4 + 2^-9) * max|V| (relative e4m3 rounding of
+each p, plus bf16 output rounding), used as 0.07 * max|V|.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import LSE_TOL, O_TOL, assert_matches, gpu_rows, max_abs_v, nan_fill_, oracle_for
+from paged_kv_fp8_amd.workloads import make_batch, workload
+
+pytestmark = pytest.mark.gpu
+
+FP8_SHORT_TOL = 0.07
+
+
+def _decode():
+    from paged_kv_fp8_amd import decode  # loads the HIP library; fails loudly if missing
+    return decode
+
+
+def run_batch(batch, **kw):
+    dec = _decode().for_batch(batch, **kw)
+    if dec.has_splits:
+        nan_fill_(dec.workspace)
+    dec.run()
+    torch.cuda.synchronize()
+    return dec
+
+
+def compare(batch, dec, seqs=None, causal=None, o_tol=O_TOL, what=""):
+    spec = batch.spec
+    nb = batch.to_numpy()
+    o_ref, lse_ref = oracle_for(nb, spec, seqs, causal)
+    o_g, lse_g = gpu_rows(dec.o, dec.lse, spec, seqs)
+    vmax = max_abs_v(nb, spec, seqs)
+    return assert_matches(o_g, lse_g, o_ref, lse_ref, vmax, o_tol=o_tol, what=what)
+
+
+SMALL = {
+    "cfg1": dict(index=1),
+    "cfg2_small": dict(index=2, num_seqs=6, seq_len_dist=("uniform", 100, 1500)),
+    "cfg3_small_causal": dict(index=3, num_seqs=5, seq_len_dist=("lognormal", 700, 1.0, 5, 3000)),
+    "cfg3_small_block": dict(index=3, num_seqs=5, seq_len_dist=("lognormal", 700, 1.0, 5, 3000), causal=False),
+    "cfg4_small": dict(index=4, num_seqs=6, seq_len_dist=("mix", 0.34, (3000, 9000), (1024, 2000))),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_workloads_every_output(name):
+    kw = dict(SMALL[name])
+    w = workload(kw.pop("index"), **kw)
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch)
+    err_o, err_l, _ = compare(batch, dec, what=name)
+    print(f"{name}: splits={dec.plan_info.max_n_splits} work={dec.plan_info.num_real} "
+          f"max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
+
+
+FULL = {"cfg1": (1, {}), "cfg2": (2, {}), "cfg3_causal": (3, {}), "cfg3_block": (3, {"causal": False}),
+        "cfg4": (4, {})}
+
+
+def _sample(lens, rng, k=6):
+    order = np.argsort(lens)
+    pick = {int(order[0]), int(order[-1])}
+    pick.update(int(x) for x in rng.choice(len(lens), size=min(k, len(lens)), replace=False))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_workloads_sampled(name):
+    idx, over = FULL[name]
+    w = workload(idx, **over)
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch)
+    lens = batch.seq_lens.cpu().numpy()
+    seqs = _sample(lens, np.random.default_rng(idx))
+    err_o, err_l, _ = compare(batch, dec, seqs=seqs, what=name)
+    print(f"{name}: seqs={seqs} splits={dec.plan_info.max_n_splits} chunk={dec.plan_info.chunk_tiles} "
+          f"work={dec.plan_info.num_real} wg/cu={dec.wg_per_cu} max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
+
+
+EDGE_LENS = [0, 1, 2, 3, 15, 16, 17, 31, 32, 33, 127, 128, 129, 255, 256, 257, 1000, 1025]
+
+
+@pytest.mark.parametrize("q_format,q_len,causal,ps,force", [
+    ("bf16", 1, True, 16, 0), ("bf16", 1, True, 128, 3), ("bf16", 4, True, 16, 2), ("bf16", 4, False, 64, 0),
+    ("bf16", 3, True, 32, 4), ("e4m3", 1, True, 128, 0), ("e4m3", 4, True, 16, 3), ("e4m3", 2, False, 64, 2)])
+def test_edge_lengths(q_format, q_len, causal, ps, force):
+    idx = 4 if q_format == "e4m3" else 2
+    h_q, h_k = (64, 4) if q_format == "e4m3" else (16, 2)
+    w = workload(idx, num_seqs=len(EDGE_LENS), q_len=q_len, h_q=h_q, h_k=h_k, page_size=ps, causal=causal,
+                 seq_len_dist=("fixed", EDGE_LENS), max_splits=8)
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch, force_splits=force)
+    tol = FP8_SHORT_TOL if q_format == "e4m3" else O_TOL
+    compare(batch, dec, o_tol=tol, what=f"edge {q_format} q_len={q_len} causal={causal} ps={ps} force={force}")
+
+
+def test_workspace_needs_no_init_and_runs_are_bitwise_stable():
+    w = workload(2, num_seqs=8, seq_len_dist=("uniform", 300, 5000))
+    batch = make_batch(w, device="cuda")
+    o1 = torch.empty(w.num_seqs, w.h_q, 128, dtype=torch.bfloat16, device="cuda")
+    l1 = torch.empty(w.num_seqs, w.h_k, w.rows, device="cuda")
+    dec = _decode().for_batch(batch, o=o1, lse=l1)
+    assert dec.has_splits
+    results = []
+    for fill in (0xFF, 0x00, 0x7F, 0xFF):
+        dec.workspace.fill_(fill)
+        o1.fill_(0)
+        l1.fill_(0)
+        dec.run()
+        torch.cuda.synchronize()
+        results.append((o1.clone(), l1.clone()))
+    for o, l in results[1:]:
+        assert torch.equal(o.view(torch.int16), results[0][0].view(torch.int16))
+        assert torch.equal(l.view(torch.int32), results[0][1].view(torch.int32))
+
+
+def test_graph_replay_bitwise_and_follows_inputs():
+    w = workload(3, num_seqs=6, seq_len_dist=("lognormal", 900, 0.8, 100, 4000))
+    batch = make_batch(w, device="cuda")
+    o = torch.zeros(w.num_seqs * w.q_len, w.h_q, 128, dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros(w.num_seqs, w.h_k, w.rows, device="cuda")
+    dec = _decode().for_batch(batch, o=o, lse=lse)
+    assert dec.has_splits
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        dec.run(stream)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    eager_o, eager_l = o.clone(), lse.clone()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dec.run()
+    for rep in range(3):
+        o.zero_()
+        lse.zero_()
+        _ = (batch.q.float() * 2).sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), eager_o.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(lse.view(torch.int32), eager_l.view(torch.int32)), f"replay {rep}"
+    # change the inputs in place: the replay must follow them
+    batch.q.mul_(-1)
+    g.replay()
+    torch.cuda.synchronize()
+    o_replay, l_replay = o.clone(), lse.clone()
+    dec.run()
+    torch.cuda.synchronize()
+    assert torch.equal(o_replay.view(torch.int16), o.view(torch.int16))
+    assert torch.equal(l_replay.view(torch.int32), lse.view(torch.int32))
+    assert not torch.equal(o_replay.view(torch.int16), eager_o.view(torch.int16))
+    compare(batch, dec, what="after in-place q change")
+
+
+def test_hnd_layout_equals_nhd_bitwise():
+    common = dict(num_seqs=5, seq_len_dist=("uniform", 200, 3000))
+    outs = []
+    for layout in ("nhd", "hnd"):
+        batch = make_batch(workload(3, kv_layout=layout, **common), device="cuda")
+        dec = run_batch(batch)
+        outs.append((dec.o.clone(), dec.lse.clone()))
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1].view(torch.int32), outs[1][1].view(torch.int32))
+
+
+def test_page_permutation_invariance_bitwise():
+    w = workload(2, num_seqs=5, seq_len_dist=("uniform", 100, 2000))
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch)
+    ref_o, ref_l = dec.o.clone(), dec.lse.clone()
+    P = batch.num_pages
+    perm = torch.randperm(P, generator=torch.Generator().manual_seed(5)).to("cuda")
+    for name in ("k_cache", "v_cache"):
+        src = getattr(batch, name)
+        moved = torch.empty_like(src)
+        moved[perm] = src
+        setattr(batch, name, moved)
+    batch.block_table = perm[batch.block_table.long()].to(torch.int32)
+    dec2 = run_batch(batch)
+    assert torch.equal(dec2.o.view(torch.int16), ref_o.view(torch.int16))
+    assert torch.equal(dec2.lse.view(torch.int32), ref_l.view(torch.int32))
+
+
+def test_descale_broadcast_equals_full():
+    w = workload(4, num_seqs=4, seq_len_dist=("uniform", 1024, 3000))
+    batch = make_batch(w, device="cuda")
+    batch.k_descale.fill_(0.0123)
+    batch.v_descale.fill_(0.0456)
+    full = run_batch(batch)
+    ref = (full.o.clone(), full.lse.clone())
+    batch.k_descale = torch.tensor([0.0123], device="cuda")
+    batch.v_descale = torch.full((w.h_k,), 0.0456, device="cuda")
+    bc = run_batch(batch)
+    assert torch.equal(bc.o.view(torch.int16), ref[0].view(torch.int16))
+    assert torch.equal(bc.lse.view(torch.int32), ref[1].view(torch.int32))
+
+
+def test_outputs_outside_the_rows_are_untouched():
+    w = workload(2, num_seqs=4, seq_len_dist=("uniform", 100, 3000))
+    batch = make_batch(w, device="cuda")
+    wide = torch.full((w.num_seqs, w.h_q * 128 + 256), 12345, dtype=torch.int16, device="cuda")
+    o = wide[:, :w.h_q * 128].view(torch.bfloat16).view(w.num_seqs, w.h_q, 128)
+    dec = run_batch(batch, o=o)
+    assert torch.all(wide[:, w.h_q * 128:] == 12345)
+    compare(batch, dec, what="strided o")
+
+
+def test_plan_for_upper_bounds_runs_shorter_lengths():
+    w = workload(2, num_seqs=6, seq_len_dist=("uniform", 1000, 4000))
+    batch = make_batch(w, device="cuda")
+    upper = batch.seq_lens.cpu().numpy()
+    shorter = np.maximum(upper - np.array([0, 1, 500, 999, 3, 128]), 0).astype(np.int32)
+    batch.seq_lens.copy_(torch.from_numpy(shorter))
+    dec = run_batch(batch, plan_seq_lens=upper, pad_to=0)
+    compare(batch, dec, what="shorter runtime lengths")
+
+
+def test_padded_work_list_same_result():
+    w = workload(2, num_seqs=5, seq_len_dist=("uniform", 100, 3000))
+    batch = make_batch(w, device="cuda")
+    d1 = run_batch(batch)
+    r1 = (d1.o.clone(), d1.lse.clone())
+    d2 = run_batch(batch, pad_to=d1.plan_info.num_work + 37)
+    assert d2.plan_info.num_work == d1.plan_info.num_work + 37
+    assert torch.equal(d2.o.view(torch.int16), r1[0].view(torch.int16))
+    assert torch.equal(d2.lse.view(torch.int32), r1[1].view(torch.int32))
