@@ -59,6 +59,28 @@ def algorithmic_bytes(batch, dec):
                 total=kv + q + bt + out_direct + out_split)
 
 
+def measured_traffic(workload_name):
+    """HBM bytes per decode launch from the committed counter summary of this
+    workload, or None if there is none or the kernel source changed since."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"gqa_decode_{workload_name}_hbm_bytes.md")
+    src = os.path.join(ROOT, "paged_kv_fp8_amd", "csrc", "decode_gqa.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            k, _, v = line.strip().partition(":")
+            fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_oracle_baseline(batch, budget_s):
     """Time the fp64 oracle (single BLAS thread) on whole sequences of the
     batch until ``budget_s`` seconds of CPU work are spent."""
@@ -100,6 +122,14 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--wg-per-cu", type=int, default=None, help="override the occupancy the planner uses")
+    ap.add_argument("--kv-layout", default=None, choices=["nhd", "hnd"],
+                    help="physical cache layout (default nhd: [pages][page_size][h_k][d])")
+    ap.add_argument("--max-splits", type=int, default=None, help="override the workload's split cap")
+    ap.add_argument("--page-size", type=int, default=None, help="override the workload's page size")
+    ap.add_argument("--contiguous-pages", action="store_true", help="hand out pages in order instead of shuffled")
+    ap.add_argument("--seq-len", type=int, default=None, help="give every sequence this length")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 8 plain 256 MiB device-to-device copies (scale reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -109,14 +139,33 @@ def main():
     import numpy as np
     import torch
 
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied 8 x 256 MiB")
+        return
+
     from paged_kv_fp8_amd import decode
     from paged_kv_fp8_amd.workloads import make_batch, workload
 
     over = {} if args.causal is None else {"causal": bool(args.causal)}
+    if args.kv_layout:
+        over["kv_layout"] = args.kv_layout
+    if args.max_splits:
+        over["max_splits"] = args.max_splits
+    if args.page_size:
+        over["page_size"] = args.page_size
+    if args.contiguous_pages:
+        over["contiguous_pages"] = True
+    if args.seq_len:
+        over["seq_len_dist"] = ("fixed", [args.seq_len] * workload(args.config).num_seqs)
     w = workload(args.config, **over)
     torch.cuda.set_device(0)
     first = make_batch(w, device="cuda")
-    pools = args.pools or max(3, -(-(1 << 30) // max(1, first.kv_bytes)))
+    pools = args.pools or min(64, max(3, -(-(1 << 30) // max(1, first.kv_bytes))))
     lens = first.seq_lens.cpu().numpy()
     batches = [first] + [make_batch(dataclasses.replace(w, seed=w.seed + 1000 * i), device="cuda", seq_lens=lens)
                          for i in range(1, pools)]
@@ -177,12 +226,13 @@ def main():
         "dtype": "fp8" if w.q_format == "e4m3" else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "q_len": w.q_len, "h_q": w.h_q, "h_k": w.h_k,
-                   "d": w.d_qk, "page_size": w.page_size, "causal": w.causal, "kv_tokens": int(lens.sum()),
+                   "d": w.d_qk, "page_size": w.page_size, "causal": w.causal, "kv_layout": w.kv_layout,
+                   "contiguous_pages": w.contiguous_pages, "kv_tokens": int(lens.sum()),
                    "kv_bytes": ab["kv"], "max_splits": w.max_splits, "pools": pools,
                    "plan": {"chunk_tiles": info.chunk_tiles, "work_items": info.num_real, "slots": info.slots,
                             "max_n_splits": info.max_n_splits, "wg_per_cu": decs[0].wg_per_cu}},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
                      "kernel": "gqa_decode_kernel", "kernel_us": round(dec_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": ab["total"], "merge_us": round(mrg_ms * 1e3, 2)},
         "cpu_baseline": cpu,

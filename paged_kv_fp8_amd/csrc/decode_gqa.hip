@@ -31,11 +31,14 @@
 //    contiguous d_v values of one query row.
 //  * Row statistics: the max needs two cross-lane steps (lanes 16 and 32
 //    apart); the sum stays per lane until the epilogue.
-//  * Page lookups: a lane holds the page of one 16-key group for a window of
-//    64 groups (1024 keys); the block's two pages are read with readlane.
-//    Keys past L are clamped to L - 1 (a real, finite row; masked), so no
-//    block-table entry at or past ceil(L / page_size) and no cache row at or
-//    past L is ever read.
+//  * Page lookups: the two pages of a 32-key block (page_size >= 16, so a
+//    16-key group never straddles pages) come from a small vector load
+//    issued two blocks ahead and are read with readlane. Keys are clamped to the chunk's last key (a
+//    real, finite row; masked), so no block-table entry at or past
+//    ceil(L / page_size) and no cache row at or past L is ever read.
+//  * Every main-loop step issues the same 13 loads whether or not its block
+//    exists, so the wait before consuming a block covers that block only and
+//    the ring of STAGES blocks stays in flight.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -98,18 +101,24 @@ __device__ __forceinline__ long as_long(uint2 x) {
   return (long)(((unsigned long long)x.y << 32) | x.x);
 }
 
-__device__ __forceinline__ float wave_max16(float x) {
-  // max over the four lanes {l, l^16, l^32, l^48} holding one query row
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+// Butterfly steps across the four lanes {l, l^16, l^32, l^48} that hold one
+// query row. v_permlane{16,32}_swap with both operands = x return the pair
+// {x[l], x[l^16]} (resp. l^32) in an order that is the same on both partner
+// lanes, so max/sum of the pair is bit-identical on the two lanes. Plain VALU
+// ops: no LDS permute, so no lgkmcnt wait that would also wait for the
+// scalar page loads.
+__device__ __forceinline__ float pair16(float x, bool take_max) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return take_max ? fmaxf(a, b) : a + b;
 }
-
-__device__ __forceinline__ float wave_sum16(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+__device__ __forceinline__ float pair32(float x, bool take_max) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return take_max ? fmaxf(a, b) : a + b;
 }
+__device__ __forceinline__ float wave_max16(float x) { return pair32(pair16(x, true), true); }
+__device__ __forceinline__ float wave_sum16(float x) { return pair32(pair16(x, false), false); }
 
 // Raw bytes of one 32-key block as this lane loads them.
 struct RawBlock {
@@ -117,9 +126,13 @@ struct RawBlock {
   uint2 v[8];     // key kb+16*(j>>2)+4*g4+(j&3), bytes 8*r16 .. 8*r16+7
 };
 
-template <bool FP8Q, int NB, bool CAUSAL_TAIL>
-__global__ __launch_bounds__(64) void gqa_decode_kernel(GqaParams p) {
-  const int lane = threadIdx.x;
+template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES, int HW>
+__global__ __launch_bounds__(64 * HW) void gqa_decode_kernel(GqaParams p) {
+  // HW waves per workgroup, one per kv head of the same work item: together
+  // they stream the same pages (every head's rows of a key range), which
+  // keeps the number of concurrent DRAM streams per key range at two (K, V).
+  const int lane = threadIdx.x & 63;
+  const int g = blockIdx.y * HW + (threadIdx.x >> 6);
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
 
@@ -130,7 +143,7 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(GqaParams p) {
   const bool direct = ns <= 1;
   const int slot = w.w;
   if (!direct && (slot < 0 || slot >= p.max_splits)) return;
-  const int g = blockIdx.y;
+  if (g >= p.h_k) return;
   const int row0 = blockIdx.z * (16 * NB);
 
   const int page_size = 1 << p.page_shift;
@@ -149,9 +162,10 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(GqaParams p) {
     const int qi = n / p.h_r;
     qtok[nb] = b * p.q_len + qi;
     qhead[nb] = g * p.h_r + (n - qi * p.h_r);
-    lim[nb] = CAUSAL_TAIL ? L - p.q_len + qi : L - 1;
+    // last key this row may see inside this work item's chunk
+    lim[nb] = min(CAUSAL_TAIL ? L - p.q_len + qi : L - 1, k_end - 1);
   }
-  const int lim_min = CAUSAL_TAIL ? L - p.q_len : L - 1;
+  const int lim_min = min(CAUSAL_TAIL ? L - p.q_len : L - 1, k_end - 1);
 
   const float qd = FP8Q ? p.qd[b * p.qd_seq + g * p.qd_head] : 1.0f;
   const float kdv = p.kd[b * p.kd_seq + g * p.kd_head];
@@ -188,164 +202,181 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(GqaParams p) {
 
   if (k_end > k_begin) {
     const int32_t* bt = p.block_table + (int64_t)b * p.bt_row;
-    // page of 16-key group G0 + lane (clamped into the sequence and the pool)
-    auto load_window = [&](int key0) -> int {
-      const int key = min(key0 + 16 * lane, L - 1);
-      const int pg = bt[key >> p.page_shift];
-      return min(max(pg, 0), p.num_pages - 1);
-    };
-    auto load_block = [&](int kb, int win, int win_base) {
+    const int last_key = k_end - 1;  // loads never go past the chunk (and so never past L)
+    // Pages of one 32-key block (page_size >= 16, so each 16-key group lies
+    // in one page): lane l loads the entry of group l & 1, so lanes 0 and 1
+    // hold the block's two pages. A vector load, so waiting for it (in
+    // order) never waits for the KV loads issued after it.
+    auto page_pair = [&](int kb) -> int { return bt[min(kb + 16 * (lane & 1), last_key) >> p.page_shift]; };
+    auto clamp_page = [&](int pg) -> int { return min(max(pg, 0), p.num_pages - 1); };
+    auto load_block = [&](int kb, int pg0, int pg1) {
       RawBlock r;
-      const int gi = (kb - win_base) >> 4;  // group index of the block inside the window (even)
-      const int pg0 = __builtin_amdgcn_readlane(win, gi);
-      const int pg1 = __builtin_amdgcn_readlane(win, gi + 1);
       const uint8_t* kbase0 = p.k + (int64_t)pg0 * p.k_page + (int64_t)g * p.k_head;
       const uint8_t* kbase1 = p.k + (int64_t)pg1 * p.k_page + (int64_t)g * p.k_head;
       const uint8_t* vbase0 = p.v + (int64_t)pg0 * p.v_page + (int64_t)g * p.v_head;
       const uint8_t* vbase1 = p.v + (int64_t)pg1 * p.v_page + (int64_t)g * p.v_head;
       const int pmask = page_size - 1;
       for (int t = 0; t < 2; ++t) {
-        const int row = min(kb + 16 * t + r16, L - 1) & pmask;
+        const int row = min(kb + 16 * t + r16, last_key) & pmask;
         const uint8_t* kp = (t ? kbase1 : kbase0) + (int64_t)row * p.k_row;
         r.k[t][0] = *reinterpret_cast<const uint4*>(kp + 16 * g4);
         r.k[t][1] = *reinterpret_cast<const uint4*>(kp + 64 + 16 * g4);
       }
       for (int j = 0; j < 8; ++j) {
         const int t = j >> 2;
-        const int row = min(kb + 16 * t + 4 * g4 + (j & 3), L - 1) & pmask;
+        const int row = min(kb + 16 * t + 4 * g4 + (j & 3), last_key) & pmask;
         const uint8_t* vp = (t ? vbase1 : vbase0) + (int64_t)row * p.v_row;
         r.v[j] = *reinterpret_cast<const uint2*>(vp + 8 * r16);
       }
       return r;
     };
 
-    int win_base = k_begin;
-    int win_cur = load_window(win_base);
-    int win_nxt = (win_base + 1024 < k_end) ? load_window(win_base + 1024) : win_cur;
-    RawBlock cur = load_block(k_begin, win_cur, win_base);
-
-    for (int kb = k_begin; kb < k_end; kb += kBlockKeys) {
-      // ---- prefetch the next block (and the next page window) ------------
-      RawBlock nxt;
-      const int kn = kb + kBlockKeys;
-      if (kn < k_end) {
-        if (kn - win_base >= 1024) {
-          win_base += 1024;
-          win_cur = win_nxt;
-          if (win_base + 1024 < k_end) win_nxt = load_window(win_base + 1024);
-        }
-        nxt = load_block(kn, win_cur, win_base);
-      }
-
-      // ---- S = K Q^T (keys on M) -----------------------------------------
-      f32x4 sacc[NB][2];
-      for (int nb = 0; nb < NB; ++nb)
-        for (int t = 0; t < 2; ++t) sacc[nb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int t = 0; t < 2; ++t) {
-        for (int s = 0; s < 4; ++s) {
-          const uint2 kraw = half_of(cur.k[t][s >> 1], s & 1);
-          if (FP8Q) {
-            const long a = as_long(kraw);
-            for (int nb = 0; nb < NB; ++nb)
-              sacc[nb][t] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, q8[nb][s], sacc[nb][t], 0, 0, 0);
-          } else {
-            const bf16x8 a = e4m3x8_to_bf16(kraw);
-            for (int nb = 0; nb < NB; ++nb)
-              sacc[nb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[nb][s], sacc[nb][t], 0, 0, 0);
-          }
-        }
-      }
-
-      // ---- online softmax (per query row = lane column r16) --------------
-      bf16x8 pb[NB];
-      long p8[NB];
-      const bool need_mask = kb + kBlockKeys - 1 > lim_min;
-      for (int nb = 0; nb < NB; ++nb) {
-        if (need_mask) {
-          for (int t = 0; t < 2; ++t)
-            for (int i = 0; i < 4; ++i)
-              if (kb + 16 * t + 4 * g4 + i > lim[nb]) sacc[nb][t][i] = -INFINITY;
-        }
-        float mx = fmaxf(fmaxf(fmaxf(sacc[nb][0][0], sacc[nb][0][1]), fmaxf(sacc[nb][0][2], sacc[nb][0][3])),
-                         fmaxf(fmaxf(sacc[nb][1][0], sacc[nb][1][1]), fmaxf(sacc[nb][1][2], sacc[nb][1][3])));
-        mx = wave_max16(mx);
-        const float m_new = fmaxf(m_run[nb], mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;  // no visible key yet: exp2(-inf) = 0
-        const float corr = __builtin_amdgcn_exp2f((m_run[nb] - m_use) * c2);
-        float pr[8];
-        float psum = 0.f;
-        for (int t = 0; t < 2; ++t)
-          for (int i = 0; i < 4; ++i) {
-            pr[4 * t + i] = __builtin_amdgcn_exp2f((sacc[nb][t][i] - m_use) * c2);
-            psum += pr[4 * t + i];
-          }
-        l_part[nb] = l_part[nb] * corr + psum;
-        // rescale O only if some row's max moved (otherwise corr == 1 exactly)
-        if (__builtin_amdgcn_ballot_w64(m_new != m_run[nb])) {
-          for (int mt = 0; mt < 8; ++mt) oacc[nb][mt] *= corr;
-        }
-        m_run[nb] = m_new;
-        if (FP8Q) {
-          int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0] * kP8Scale, pr[1] * kP8Scale, 0, false);
-          lo = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2] * kP8Scale, pr[3] * kP8Scale, lo, true);
-          int hi = __builtin_amdgcn_cvt_pk_fp8_f32(pr[4] * kP8Scale, pr[5] * kP8Scale, 0, false);
-          hi = __builtin_amdgcn_cvt_pk_fp8_f32(pr[6] * kP8Scale, pr[7] * kP8Scale, hi, true);
-          p8[nb] = as_long(uint2{(unsigned)lo, (unsigned)hi});
-        } else {
-          for (int e = 0; e < 8; ++e) pb[nb][e] = (__bf16)pr[e];
-        }
-      }
-
-      // ---- O^T += V^T P^T --------------------------------------------------
-      if (FP8Q) {
-        // 4x4 byte transposes: quad kq of keys, word w of d_v bytes
-        for (int w2 = 0; w2 < 2; ++w2) {
-          unsigned col[2][4];  // [kq][e]: keys 4kq..4kq+3 at d_v 8*r16 + 4*w2 + e
-          for (int kq = 0; kq < 2; ++kq) {
-            const unsigned r0 = w2 ? cur.v[4 * kq + 0].y : cur.v[4 * kq + 0].x;
-            const unsigned r1 = w2 ? cur.v[4 * kq + 1].y : cur.v[4 * kq + 1].x;
-            const unsigned r2 = w2 ? cur.v[4 * kq + 2].y : cur.v[4 * kq + 2].x;
-            const unsigned r3 = w2 ? cur.v[4 * kq + 3].y : cur.v[4 * kq + 3].x;
-            const unsigned t0 = __builtin_amdgcn_perm(r0, r1, 0x01050004u);
-            const unsigned t1 = __builtin_amdgcn_perm(r0, r1, 0x03070206u);
-            const unsigned t2 = __builtin_amdgcn_perm(r2, r3, 0x01050004u);
-            const unsigned t3 = __builtin_amdgcn_perm(r2, r3, 0x03070206u);
-            col[kq][0] = __builtin_amdgcn_perm(t0, t2, 0x01000504u);
-            col[kq][1] = __builtin_amdgcn_perm(t0, t2, 0x03020706u);
-            col[kq][2] = __builtin_amdgcn_perm(t1, t3, 0x01000504u);
-            col[kq][3] = __builtin_amdgcn_perm(t1, t3, 0x03020706u);
-          }
-          for (int e = 0; e < 4; ++e) {
-            const long a = as_long(uint2{col[0][e], col[1][e]});
-            const int mt = 4 * w2 + e;
-            for (int nb = 0; nb < NB; ++nb)
-              oacc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, p8[nb], oacc[nb][mt], 0, 0, 0);
-          }
-        }
-      } else {
-        for (int w2 = 0; w2 < 2; ++w2) {
-          unsigned xy[4][2];  // [key pair pp][0: d_v bytes 0,1 / 1: bytes 2,3 of the word], interleaved by key
-          for (int pp = 0; pp < 4; ++pp) {
-            const unsigned a0 = w2 ? cur.v[2 * pp].y : cur.v[2 * pp].x;
-            const unsigned a1 = w2 ? cur.v[2 * pp + 1].y : cur.v[2 * pp + 1].x;
-            xy[pp][0] = __builtin_amdgcn_perm(a0, a1, 0x01050004u);
-            xy[pp][1] = __builtin_amdgcn_perm(a0, a1, 0x03070206u);
-          }
-          for (int e = 0; e < 4; ++e) {
-            bf16x8 a;
-            for (int pp = 0; pp < 4; ++pp) {
-              const bf16x2 two = (e & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(xy[pp][e >> 1], 1.0f, true)
-                                         : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(xy[pp][e >> 1], 1.0f, false);
-              a[2 * pp] = two[0];
-              a[2 * pp + 1] = two[1];
+    // Fetch u loads block k_begin + 32u into ring slot u % STAGES. Every
+    // fetch issues the same 13 loads whether or not its block exists (a
+    // block past the chunk re-reads the chunk's last row, a cache hit), so
+    // the compiler counts the loads in flight exactly and each wait covers
+    // only the block being consumed. Fetch u takes its two pages from page
+    // slot u % STAGES (loaded two fetches earlier) and loads the pages of
+    // fetch u + 2 into slot (u + 2) % STAGES; slot indices are compile-time
+    // constants of the unrolled stage loop.
+    int pv[STAGES];
+    pv[0] = page_pair(k_begin);
+    pv[1 % STAGES] = page_pair(k_begin + kBlockKeys);
+    auto fetch = [&](RawBlock& r, int kb, const int slot) {
+      const int pg0 = clamp_page(__builtin_amdgcn_readlane(pv[slot], 0));
+      const int pg1 = clamp_page(__builtin_amdgcn_readlane(pv[slot], 1));
+      r = load_block(kb, pg0, pg1);
+      pv[(slot + 2) % STAGES] = page_pair(kb + 2 * kBlockKeys);
+    };
+    auto process = [&](const RawBlock& cur, int kb) {
+        // ---- S = K Q^T (keys on M) -----------------------------------------
+        f32x4 sacc[NB][2];
+        for (int nb = 0; nb < NB; ++nb)
+          for (int t = 0; t < 2; ++t) sacc[nb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < 2; ++t) {
+          for (int s = 0; s < 4; ++s) {
+            const uint2 kraw = half_of(cur.k[t][s >> 1], s & 1);
+            if (FP8Q) {
+              const long a = as_long(kraw);
+              for (int nb = 0; nb < NB; ++nb)
+                sacc[nb][t] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, q8[nb][s], sacc[nb][t], 0, 0, 0);
+            } else {
+              const bf16x8 a = e4m3x8_to_bf16(kraw);
+              for (int nb = 0; nb < NB; ++nb)
+                sacc[nb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[nb][s], sacc[nb][t], 0, 0, 0);
             }
-            const int mt = 4 * w2 + e;
-            for (int nb = 0; nb < NB; ++nb)
-              oacc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[nb], oacc[nb][mt], 0, 0, 0);
           }
         }
+
+        // ---- online softmax (per query row = lane column r16) --------------
+        bf16x8 pb[NB];
+        long p8[NB];
+        const bool need_mask = kb + kBlockKeys - 1 > lim_min;
+        for (int nb = 0; nb < NB; ++nb) {
+          if (need_mask) {
+            for (int t = 0; t < 2; ++t)
+              for (int i = 0; i < 4; ++i)
+                if (kb + 16 * t + 4 * g4 + i > lim[nb]) sacc[nb][t][i] = -INFINITY;
+          }
+          float mx = fmaxf(fmaxf(fmaxf(sacc[nb][0][0], sacc[nb][0][1]), fmaxf(sacc[nb][0][2], sacc[nb][0][3])),
+                           fmaxf(fmaxf(sacc[nb][1][0], sacc[nb][1][1]), fmaxf(sacc[nb][1][2], sacc[nb][1][3])));
+          mx = wave_max16(mx);
+          const float m_new = fmaxf(m_run[nb], mx);
+          const float m_use = m_new == -INFINITY ? 0.f : m_new;  // no visible key yet: exp2(-inf) = 0
+          const float corr = __builtin_amdgcn_exp2f((m_run[nb] - m_use) * c2);
+          float pr[8];
+          float psum = 0.f;
+          for (int t = 0; t < 2; ++t)
+            for (int i = 0; i < 4; ++i) {
+              pr[4 * t + i] = __builtin_amdgcn_exp2f((sacc[nb][t][i] - m_use) * c2);
+              psum += pr[4 * t + i];
+            }
+          l_part[nb] = l_part[nb] * corr + psum;
+          // rescale O only if some row's max moved (otherwise corr == 1 exactly)
+          if (__builtin_amdgcn_ballot_w64(m_new != m_run[nb])) {
+            for (int mt = 0; mt < 8; ++mt) oacc[nb][mt] *= corr;
+          }
+          m_run[nb] = m_new;
+          if (FP8Q) {
+            int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0] * kP8Scale, pr[1] * kP8Scale, 0, false);
+            lo = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2] * kP8Scale, pr[3] * kP8Scale, lo, true);
+            int hi = __builtin_amdgcn_cvt_pk_fp8_f32(pr[4] * kP8Scale, pr[5] * kP8Scale, 0, false);
+            hi = __builtin_amdgcn_cvt_pk_fp8_f32(pr[6] * kP8Scale, pr[7] * kP8Scale, hi, true);
+            p8[nb] = as_long(uint2{(unsigned)lo, (unsigned)hi});
+          } else {
+            for (int e = 0; e < 8; ++e) pb[nb][e] = (__bf16)pr[e];
+          }
+        }
+
+        // ---- O^T += V^T P^T --------------------------------------------------
+        if (FP8Q) {
+          // 4x4 byte transposes: quad kq of keys, word w of d_v bytes
+          for (int w2 = 0; w2 < 2; ++w2) {
+            unsigned col[2][4];  // [kq][e]: keys 4kq..4kq+3 at d_v 8*r16 + 4*w2 + e
+            for (int kq = 0; kq < 2; ++kq) {
+              const unsigned r0 = w2 ? cur.v[4 * kq + 0].y : cur.v[4 * kq + 0].x;
+              const unsigned r1 = w2 ? cur.v[4 * kq + 1].y : cur.v[4 * kq + 1].x;
+              const unsigned r2 = w2 ? cur.v[4 * kq + 2].y : cur.v[4 * kq + 2].x;
+              const unsigned r3 = w2 ? cur.v[4 * kq + 3].y : cur.v[4 * kq + 3].x;
+              const unsigned t0 = __builtin_amdgcn_perm(r0, r1, 0x01050004u);
+              const unsigned t1 = __builtin_amdgcn_perm(r0, r1, 0x03070206u);
+              const unsigned t2 = __builtin_amdgcn_perm(r2, r3, 0x01050004u);
+              const unsigned t3 = __builtin_amdgcn_perm(r2, r3, 0x03070206u);
+              col[kq][0] = __builtin_amdgcn_perm(t0, t2, 0x01000504u);
+              col[kq][1] = __builtin_amdgcn_perm(t0, t2, 0x03020706u);
+              col[kq][2] = __builtin_amdgcn_perm(t1, t3, 0x01000504u);
+              col[kq][3] = __builtin_amdgcn_perm(t1, t3, 0x03020706u);
+            }
+            for (int e = 0; e < 4; ++e) {
+              const long a = as_long(uint2{col[0][e], col[1][e]});
+              const int mt = 4 * w2 + e;
+              for (int nb = 0; nb < NB; ++nb)
+                oacc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, p8[nb], oacc[nb][mt], 0, 0, 0);
+            }
+          }
+        } else {
+          for (int w2 = 0; w2 < 2; ++w2) {
+            unsigned xy[4][2];  // [key pair pp][0: d_v bytes 0,1 / 1: bytes 2,3 of the word], interleaved by key
+            for (int pp = 0; pp < 4; ++pp) {
+              const unsigned a0 = w2 ? cur.v[2 * pp].y : cur.v[2 * pp].x;
+              const unsigned a1 = w2 ? cur.v[2 * pp + 1].y : cur.v[2 * pp + 1].x;
+              xy[pp][0] = __builtin_amdgcn_perm(a0, a1, 0x01050004u);
+              xy[pp][1] = __builtin_amdgcn_perm(a0, a1, 0x03070206u);
+            }
+            for (int e = 0; e < 4; ++e) {
+              bf16x8 a;
+              for (int pp = 0; pp < 4; ++pp) {
+                const bf16x2 two = (e & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(xy[pp][e >> 1], 1.0f, true)
+                                           : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(xy[pp][e >> 1], 1.0f, false);
+                a[2 * pp] = two[0];
+                a[2 * pp + 1] = two[1];
+              }
+              const int mt = 4 * w2 + e;
+              for (int nb = 0; nb < NB; ++nb)
+                oacc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[nb], oacc[nb][mt], 0, 0, 0);
+            }
+          }
+        }
+    };
+
+    // Ring of STAGES register buffers: while block i is processed, blocks
+    // i+1 .. i+STAGES-1 are in flight.
+    // The loop runs whole rounds of STAGES blocks with no early exit, so
+    // entry and back edge see the same loads in flight. Blocks past the
+    // chunk (at most STAGES - 1 per work item) re-read its last row and are
+    // masked out entirely (P = 0 on finite data): they change nothing.
+    RawBlock ring[STAGES];
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) fetch(ring[s], k_begin + kBlockKeys * s, s);
+    const int rounds = (k_end - k_begin + kBlockKeys * STAGES - 1) / (kBlockKeys * STAGES);
+    for (int r = 0; r < rounds; ++r) {
+      const int kb0 = k_begin + r * kBlockKeys * STAGES;
+#pragma unroll
+      for (int s = 0; s < STAGES; ++s) {
+        const int kb = kb0 + kBlockKeys * s;
+        fetch(ring[(s + STAGES - 1) % STAGES], kb + kBlockKeys * (STAGES - 1), (s + STAGES - 1) % STAGES);
+        process(ring[s], kb);
       }
-      cur = nxt;
     }
   }
 
@@ -382,19 +413,30 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(GqaParams p) {
   }
 }
 
-template <bool FP8Q, int NB, bool CT>
+template <bool FP8Q, int NB, bool CT, int ST, int HW>
 const void* kernel_ptr() {
-  return reinterpret_cast<const void*>(&gqa_decode_kernel<FP8Q, NB, CT>);
+  return reinterpret_cast<const void*>(&gqa_decode_kernel<FP8Q, NB, CT, ST, HW>);
+}
+
+template <bool FP8Q, int NB, bool CT>
+const void* select_heads(const GqaVariant& v) {
+  constexpr int ST = NB == 1 ? 3 : 6;
+  switch (v.heads_per_wg) {
+    case 1: return kernel_ptr<FP8Q, NB, CT, ST, 1>();
+    case 2: return kernel_ptr<FP8Q, NB, CT, ST, 2>();
+    case 4: return kernel_ptr<FP8Q, NB, CT, ST, 4>();
+    default: return kernel_ptr<FP8Q, NB, CT, ST, NB == 1 ? 8 : 4>();
+  }
+}
+
+template <bool FP8Q, int NB>
+const void* select_tail(const GqaVariant& v) {
+  return v.causal_tail ? select_heads<FP8Q, NB, true>(v) : select_heads<FP8Q, NB, false>(v);
 }
 
 const void* select_kernel(const GqaVariant& v) {
-  const int nb = v.n_blocks;
-  if (v.fp8_q) {
-    if (nb == 1) return v.causal_tail ? kernel_ptr<true, 1, true>() : kernel_ptr<true, 1, false>();
-    return v.causal_tail ? kernel_ptr<true, 2, true>() : kernel_ptr<true, 2, false>();
-  }
-  if (nb == 1) return v.causal_tail ? kernel_ptr<false, 1, true>() : kernel_ptr<false, 1, false>();
-  return v.causal_tail ? kernel_ptr<false, 2, true>() : kernel_ptr<false, 2, false>();
+  if (v.fp8_q) return v.n_blocks == 1 ? select_tail<true, 1>(v) : select_tail<true, 2>(v);
+  return v.n_blocks == 1 ? select_tail<false, 1>(v) : select_tail<false, 2>(v);
 }
 
 int log2_exact(int x) {
@@ -411,13 +453,23 @@ GqaVariant gqa_variant(const pkv_decode_args& a) {
   const int rows = a.q_len * (a.h_q / a.h_k);
   v.n_blocks = rows <= 16 ? 1 : 2;
   v.causal_tail = a.causal && a.q_len > 1;
+  v.stages = v.n_blocks == 1 ? 3 : 6;
+  // kv heads per workgroup: the largest power of two dividing h_k, up to 8
+  // (4 for two row blocks, whose waves need more than half the registers)
+  const int cap = v.n_blocks == 1 ? 8 : 4;
+  v.heads_per_wg = 1;
+  while (v.heads_per_wg * 2 <= cap && a.h_k % (v.heads_per_wg * 2) == 0) v.heads_per_wg *= 2;
   return v;
 }
 
 int gqa_rows_per_tile(const GqaVariant& v) { return 16 * v.n_blocks; }
 
-hipError_t gqa_occupancy(const GqaVariant& v, int* wg_per_cu) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(wg_per_cu, select_kernel(v), 64, 0);
+hipError_t gqa_occupancy(const GqaVariant& v, int* units_per_cu) {
+  // resident (work item, kv head, q tile) units per CU = resident waves
+  int wgs = 0;
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&wgs, select_kernel(v), 64 * v.heads_per_wg, 0);
+  *units_per_cu = wgs * v.heads_per_wg;
+  return e;
 }
 
 hipError_t gqa_launch(const pkv_decode_args& a, const GqaVariant& v, hipStream_t stream) {
@@ -468,9 +520,10 @@ hipError_t gqa_launch(const pkv_decode_args& a, const GqaVariant& v, hipStream_t
   p.max_blocks = a.max_blocks;
   p.max_splits = a.max_splits;
   const int tiles = (p.rows + gqa_rows_per_tile(v) - 1) / gqa_rows_per_tile(v);
-  dim3 grid(a.num_work, a.h_k, tiles);
+  const int hw = v.heads_per_wg;
+  dim3 grid(a.num_work, (a.h_k + hw - 1) / hw, tiles);
   void* args[] = {&p};
-  return hipLaunchKernel(select_kernel(v), grid, dim3(64), args, 0, stream);
+  return hipLaunchKernel(select_kernel(v), grid, dim3(64 * hw), args, 0, stream);
 }
 
 }  // namespace pkv

@@ -19,10 +19,12 @@ struct GqaVariant {
   bool fp8_q;       // e4m3 Q, e4m3 P, fp8 MFMA; else bf16 Q, bf16 P, bf16 MFMA
   int n_blocks;     // 16-row N blocks per wave (1 or 2)
   bool causal_tail; // q_len > 1 && causal
+  int stages;       // register ring depth of the KV stream (blocks of 32 keys)
+  int heads_per_wg; // kv heads (one wave each) per workgroup
 };
 GqaVariant gqa_variant(const pkv_decode_args& a);
 int gqa_rows_per_tile(const GqaVariant& v);
-hipError_t gqa_occupancy(const GqaVariant& v, int* wg_per_cu);
+hipError_t gqa_occupancy(const GqaVariant& v, int* units_per_cu);
 hipError_t gqa_launch(const pkv_decode_args& a, const GqaVariant& v, hipStream_t stream);
 
 // Latent-record (MLA) family.
