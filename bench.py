@@ -32,6 +32,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # dense
 
 
 def log(*a):
@@ -55,7 +56,14 @@ def algorithmic_bytes(batch, dec):
     direct = ns <= 1
     out_direct = int(direct.sum()) * w.h_k * w.rows * (w.d_v * 2 + 4)
     out_split = int(ns[~direct].sum()) * w.h_k * w.rows * (w.d_v + 2) * 4
-    return dict(kv=kv, q=q, block_table=bt, out=out_direct + out_split, rows=rows,
+    # MFMA work: every (row, visible key) pair costs 2*d_qk (QK^T) + 2*d_v (PV) flops
+    vis = 0
+    for L in lens:
+        qi = np.arange(w.q_len)
+        lim = (L - w.q_len + qi) if (w.causal and w.q_len > 1) else np.full(w.q_len, L - 1)
+        vis += int(np.clip(lim + 1, 0, None).sum()) * w.h_q
+    flops = vis * (2 * w.d_qk + 2 * w.d_v)
+    return dict(kv=kv, q=q, block_table=bt, out=out_direct + out_split, rows=rows, flops=flops,
                 total=kv + q + bt + out_direct + out_split)
 
 
@@ -87,7 +95,7 @@ def cpu_oracle_baseline(batch, budget_s):
     import numpy as np
     from threadpoolctl import threadpool_limits
 
-    from oracle.attention import decode_attention
+    from oracle.attention import decode_attention, mla_decode_attention
 
     w = batch.spec
     nb = batch.to_numpy()
@@ -97,12 +105,17 @@ def cpu_oracle_baseline(batch, budget_s):
         t0 = time.perf_counter()
         for b in range(w.num_seqs):
             sl = slice(b * w.q_len, (b + 1) * w.q_len)
-            decode_attention(nb["q"][sl], nb["k_cache"], nb["v_cache"], nb["block_table"][b:b + 1],
-                             lens[b:b + 1], nb["q_descale"][b:b + 1], nb["k_descale"][b:b + 1],
-                             nb["v_descale"][b:b + 1], q_len=w.q_len, h_k=w.h_k, softmax_scale=w.scale,
-                             causal=w.causal)
+            if w.kv_format == "mla":
+                mla_decode_attention(nb["q"][sl], nb["latent"], nb["rope"], nb["scales"], nb["block_table"][b:b + 1],
+                                     lens[b:b + 1], q_len=w.q_len, softmax_scale=w.scale, causal=w.causal)
+                kv += int(lens[b]) * 656
+            else:
+                decode_attention(nb["q"][sl], nb["k_cache"], nb["v_cache"], nb["block_table"][b:b + 1],
+                                 lens[b:b + 1], nb["q_descale"][b:b + 1], nb["k_descale"][b:b + 1],
+                                 nb["v_descale"][b:b + 1], q_len=w.q_len, h_k=w.h_k, softmax_scale=w.scale,
+                                 causal=w.causal)
+                kv += int(lens[b]) * w.h_k * (w.d_qk + w.d_v)
             done += 1
-            kv += int(lens[b]) * w.h_k * (w.d_qk + w.d_v)
             if time.perf_counter() - t0 >= budget_s:
                 break
         dt = time.perf_counter() - t0
@@ -116,7 +129,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--q-len", type=int, default=None, help="query tokens per sequence (latent workload: 1..16)")
     ap.add_argument("--causal", type=int, default=None, help="override the workload's causal flag (0/1)")
     ap.add_argument("--pools", type=int, default=0, help="KV pools to rotate (0: enough for >= 1 GiB, min 3)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -152,6 +166,8 @@ def main():
     from paged_kv_fp8_amd.workloads import make_batch, workload
 
     over = {} if args.causal is None else {"causal": bool(args.causal)}
+    if args.q_len:
+        over["q_len"] = args.q_len
     if args.kv_layout:
         over["kv_layout"] = args.kv_layout
     if args.max_splits:
@@ -201,16 +217,32 @@ def main():
     dec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     mrg_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     value = ab["kv"] / (ms_step * 1e-3) / 1e9
+    dtype = "fp8" if w.q_format == "e4m3" else "bf16"
+    t_hbm = ab["total"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = ab["flops"] / (MFMA_PEAK_TFLOPS[dtype] * 1e12)
     achieved = ab["total"] / (dec_ms * 1e-3) / 1e9
+    tflops = ab["flops"] / (dec_ms * 1e-3) / 1e12
     log(f"step {ms_step * 1e3:.1f} us (decode {dec_ms * 1e3:.1f} us, merge {mrg_ms * 1e3:.1f} us), "
         f"host wall {wall / K * 1e6:.1f} us/step; KV {value:.0f} GB/s; decode kernel {achieved:.0f} GB/s "
-        f"= {achieved / HBM_PEAK_GBS:.3f} of peak")
+        f"= {achieved / HBM_PEAK_GBS:.3f} of peak; {tflops:.1f} TFLOP/s = "
+        f"{tflops / MFMA_PEAK_TFLOPS[dtype]:.3f} of {dtype} MFMA peak; roofline time "
+        f"{max(t_hbm, t_mfma) * 1e6:.1f} us ({'mfma' if t_mfma > t_hbm else 'hbm'})")
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_oracle_baseline(first, args.cpu_seconds)
         log(f"cpu oracle: {cpu}")
 
+    kernel = "mla_decode_kernel" if w.kv_format == "mla" else "gqa_decode_kernel"
+    if t_mfma > t_hbm:
+        roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS[dtype], "unit": "TFLOP/s",
+                    "frac": round(tflops / MFMA_PEAK_TFLOPS[dtype], 4), "traffic": None}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic(w.name) if kernel == "gqa_decode_kernel" else None}
+    roofline.update({"kernel": kernel, "kernel_us": round(dec_ms * 1e3, 2), "algorithmic_bytes_per_launch": ab["total"],
+                     "algorithmic_flops_per_launch": ab["flops"], "merge_us": round(mrg_ms * 1e3, 2)})
     line = {
         "metric": "achieved HBM GB/s (KV bytes / decode-step time), us per decode step",
         "value": round(value, 2),
@@ -223,7 +255,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if w.q_format == "e4m3" else "bf16",
+        "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "q_len": w.q_len, "h_q": w.h_q, "h_k": w.h_k,
                    "d": w.d_qk, "page_size": w.page_size, "causal": w.causal, "kv_layout": w.kv_layout,
@@ -231,10 +263,7 @@ def main():
                    "kv_bytes": ab["kv"], "max_splits": w.max_splits, "pools": pools,
                    "plan": {"chunk_tiles": info.chunk_tiles, "work_items": info.num_real, "slots": info.slots,
                             "max_n_splits": info.max_n_splits, "wg_per_cu": decs[0].wg_per_cu}},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
-                     "kernel": "gqa_decode_kernel", "kernel_us": round(dec_ms * 1e3, 2),
-                     "algorithmic_bytes_per_launch": ab["total"], "merge_us": round(mrg_ms * 1e3, 2)},
+        "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -55,7 +55,6 @@ pkv_status check_shapes(const pkv_decode_args* a) {
                   a->d_qk, a->d_v);
     if (a->q_format != PKV_Q_BF16) return fail(PKV_ERR_UNSUPPORTED, "latent cache: only bf16 q is built");
     if (rows > 256) return fail(PKV_ERR_UNSUPPORTED, "latent cache: q_len * h_q = %lld rows > 256", (long long)rows);
-    return fail(PKV_ERR_UNSUPPORTED, "latent cache decode is not built in this version");
   } else {
     return fail(PKV_ERR_INVALID_ARG, "kv_format=%d unknown", a->kv_format);
   }

@@ -1,18 +1,405 @@
-// Latent-record (MLA-like) decode: not built yet; the entry points reject
-// PKV_KV_MLA with PKV_ERR_UNSUPPORTED before reaching these launchers.
+// Split-KV paged decode over latent records (MLA-like), gfx950.
+//
+// Method: the decode of "mjolnir-kernel 0.1.0 wheel: mjolnir/t5_decode.py"
+// (module docstring: work items, causal tail, direct write / partials; the
+// decode kernel's online softmax) applied to the record cache of "vLLM PR
+// #62633" (Kernel design): one KV head whose key j is its 512 e4m3 latent
+// values times one fp32 scale per 128-value block, followed by 64 bf16 rope
+// values, and whose value is the scaled latent part. Row n = qi * h_q + h
+// (qi-major) sees keys 0 .. lim(n) as in the GQA path.
+//
+// gfx950 design:
+//  * One wave per 16 query rows (= the 16 heads of one query token); up to 4
+//    waves (64 rows) per workgroup; more rows use more q-row tiles. Each wave
+//    streams the chunk's records 16 keys at a time into registers; the waves
+//    of a workgroup read the same records, which the L1/L2 serve after the
+//    first.
+//  * The per-128 block scales are not multiplied into the e4m3 codes (the
+//    product is not a bf16 value in general): QK^T keeps one fp32
+//    accumulator per 128-value block and combines them with each key's four
+//    scales, s = sum_blk scale_blk * <q_blk, code_blk> + <q_rope, rope>; PV
+//    multiplies P by the key's block scale (one bf16 P operand per 128-value
+//    block of d_v), so V stays the exact codes. The codes convert to bf16
+//    exactly (v_cvt_scalef32_pk_bf16_fp8 with scale 1).
+//  * QK^T on v_mfma_f32_16x16x32_bf16 with keys on M (16 latent + 2 rope
+//    k-steps per 16-key tile); PV on v_mfma_f32_16x16x16_bf16 (16 keys per
+//    step), O^T[d_v][rows] with dv-tile (g, mt) row m = d_v 128 g + 8 m + mt,
+//    so a lane ends with 32 contiguous d_v values per 128-block. V^T is
+//    transposed in registers with v_perm_b32; P stays in the lanes that
+//    computed it.
+//  * Same load discipline as the GQA kernel: every fetch issues the same
+//    loads (keys clamped to the chunk's last key), the page of a block comes
+//    from a one-dword vector load two blocks ahead, the loop runs whole
+//    rounds, so waits cover only the block being consumed.
 #include <hip/hip_runtime.h>
+
+#include <cmath>
 
 #include "pkv_internal.h"
 
 namespace pkv {
+namespace {
 
-int mla_rows_per_tile(const pkv_decode_args&) { return 16; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-hipError_t mla_occupancy(const pkv_decode_args&, int* wg_per_cu) {
-  *wg_per_cu = 1;
-  return hipSuccess;
+constexpr int kLatent = 512;
+constexpr int kRope = 64;
+constexpr int kDv = 512;
+constexpr int kTileKeys = 128;  // planner tile
+constexpr int kBlockKeys = 16;  // keys per main-loop step
+constexpr int kStages = 2;
+constexpr int kMaxWaves = 4;    // 16-row waves per workgroup
+constexpr int kQSteps = 18;     // 16 latent + 2 rope k-steps of 32
+
+struct MlaParams {
+  const uint8_t* q;
+  int64_t q_tok, q_head;  // bytes
+  const uint8_t* lat;
+  int64_t lat_page, lat_row;  // bytes
+  const uint8_t* rope;
+  int64_t rope_page, rope_row;  // bytes
+  const uint8_t* scl;
+  int64_t scl_page, scl_row;  // bytes
+  const int32_t* block_table;
+  int64_t bt_row;
+  const int32_t* seq_lens;
+  uint8_t* o;
+  int64_t o_tok, o_head;  // bytes
+  float* lse;
+  const int4* work;
+  const int32_t* n_splits;
+  float* ws_o;    // [max_splits][num_seqs][rows][512]
+  float2* ws_ml;  // [max_splits][num_seqs][rows]
+  float scale_log2e, scale, o_scale;
+  int num_seqs, q_len, h_q, rows, page_shift, num_pages, max_blocks, max_splits;
+};
+
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint2 x) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-hipError_t mla_launch(const pkv_decode_args&, hipStream_t) { return hipErrorNotSupported; }
+__device__ __forceinline__ uint2 half_of(uint4 x, int h) { return h ? uint2{x.z, x.w} : uint2{x.x, x.y}; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &x, 16);
+  return r;
+}
+
+__device__ __forceinline__ float pair16(float x, bool take_max) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return take_max ? fmaxf(a, b) : a + b;
+}
+__device__ __forceinline__ float pair32(float x, bool take_max) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return take_max ? fmaxf(a, b) : a + b;
+}
+
+// Raw bytes of one 16-key block as this lane loads them.
+struct RawRec {
+  uint4 kl[4][2];  // key kb + r16: latent bytes 128 blk + 64 h + 16 g4 .. +15
+  uint4 kr[2];     // key kb + r16: rope values 32 t + 8 g4 .. +7
+  float4 sc[4];    // key kb + 4 g4 + i: the four block scales
+  uint2 v[4][4];   // key kb + 4 g4 + i, latent bytes 128 gr + 8 r16 .. +7
+};
+
+template <bool CAUSAL_TAIL>
+__global__ __launch_bounds__(64 * kMaxWaves) void mla_decode_kernel(MlaParams p) {
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+  const int row_block = blockIdx.y * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int row0 = 16 * row_block;
+
+  const int4 w = p.work[blockIdx.x];
+  const int b = w.x;
+  if (w.z <= w.y || b < 0 || b >= p.num_seqs) return;
+  const int ns = p.n_splits[b];
+  const bool direct = ns <= 1;
+  const int slot = w.w;
+  if (!direct && (slot < 0 || slot >= p.max_splits)) return;
+  if (row0 >= p.rows) return;
+
+  const int page_size = 1 << p.page_shift;
+  int L = p.seq_lens[b];
+  L = max(0, min(L, p.max_blocks * page_size));
+  const int k_begin = w.y * kTileKeys;
+  const int k_end = min(w.z * kTileKeys, L);
+
+  // rows of this wave: n = row0 + r16 (token qi = n / h_q, head n % h_q)
+  const int n = row0 + r16;
+  const bool row_ok = n < p.rows;
+  const int qi = n / p.h_q;
+  const int qtok = b * p.q_len + qi;
+  const int qhead = n - qi * p.h_q;
+  const int lim = min(CAUSAL_TAIL ? L - p.q_len + qi : L - 1, k_end - 1);
+  const int qi_min = row0 / p.h_q;
+  const int lim_min = min(CAUSAL_TAIL ? L - p.q_len + qi_min : L - 1, k_end - 1);
+  const float c2 = p.scale_log2e;
+
+  // Q as the B operand of QK^T, same head-dim permutation as the K loads,
+  // parked in this wave's LDS region (k-step major, one 16-byte slot per
+  // lane, so each k-step is one conflict-free 16-byte read per lane). Only
+  // this wave reads its region, and LDS operations of a wave are ordered.
+  // dynamic LDS: blockDim.x / 64 waves x kQSteps x 64 lanes x 16 bytes
+  extern __shared__ bf16x8 q_lds[];
+  bf16x8(*qw)[64] = reinterpret_cast<bf16x8(*)[64]>(q_lds + (threadIdx.x >> 6) * kQSteps * 64);
+  {
+    const uint8_t* qrow = p.q + (int64_t)qtok * p.q_tok + (int64_t)qhead * p.q_head;
+    for (int k = 0; k < kQSteps; ++k) {
+      // k < 16: latent block k / 4, k-step k % 4; k >= 16: rope k-step k - 16
+      const int blk = k >> 2, s = k & 3;
+      const int d = k < 16 ? 128 * blk + 64 * (s >> 1) + 16 * g4 + 8 * (s & 1) : kLatent + 32 * (k - 16) + 8 * g4;
+      bf16x8 v;
+      if (row_ok) {
+        v = *reinterpret_cast<const bf16x8*>(qrow + 2 * d);
+      } else {
+        for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
+      }
+      qw[k][lane] = v;
+    }
+  }
+
+  f32x4 oacc[4][8];  // [d_v block gr][mt]: O^T[128 gr + 8 (4 g4 + i) + mt][n]
+  for (int gr = 0; gr < 4; ++gr)
+    for (int mt = 0; mt < 8; ++mt) oacc[gr][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
+
+  if (k_end > k_begin) {
+    const int32_t* bt = p.block_table + (int64_t)b * p.bt_row;
+    const int last_key = k_end - 1;
+    const int pmask = page_size - 1;
+    auto page_of = [&](int kb) -> int { return bt[min(kb, last_key) >> p.page_shift]; };
+    auto clamp_page = [&](int pg) -> int { return min(max(pg, 0), p.num_pages - 1); };
+    auto load_block = [&](int kb, int pg) {
+      RawRec r;
+      const uint8_t* lat0 = p.lat + (int64_t)pg * p.lat_page;
+      const uint8_t* rope0 = p.rope + (int64_t)pg * p.rope_page;
+      const uint8_t* scl0 = p.scl + (int64_t)pg * p.scl_page;
+      {
+        const int row = min(kb + r16, last_key) & pmask;
+        const uint8_t* lr = lat0 + (int64_t)row * p.lat_row;
+        for (int blk = 0; blk < 4; ++blk)
+          for (int h = 0; h < 2; ++h) r.kl[blk][h] = *reinterpret_cast<const uint4*>(lr + 128 * blk + 64 * h + 16 * g4);
+        const uint8_t* rr = rope0 + (int64_t)row * p.rope_row;
+        for (int t = 0; t < 2; ++t) r.kr[t] = *reinterpret_cast<const uint4*>(rr + 2 * (32 * t + 8 * g4));
+      }
+      for (int i = 0; i < 4; ++i) {
+        const int row = min(kb + 4 * g4 + i, last_key) & pmask;
+        r.sc[i] = *reinterpret_cast<const float4*>(scl0 + (int64_t)row * p.scl_row);
+        const uint8_t* lr = lat0 + (int64_t)row * p.lat_row;
+        for (int gr = 0; gr < 4; ++gr) r.v[i][gr] = *reinterpret_cast<const uint2*>(lr + 128 * gr + 8 * r16);
+      }
+      return r;
+    };
+
+    // page ring: fetch u reads slot u % kStages and loads the page of fetch
+    // u + 2 into slot (u + 2) % kStages (slot indices are compile-time)
+    int pv[kStages];
+    pv[0] = page_of(k_begin);
+    pv[1 % kStages] = page_of(k_begin + kBlockKeys);
+    auto fetch = [&](RawRec& r, int kb, const int s) {
+      const int pg = clamp_page(__builtin_amdgcn_readlane(pv[s], 0));
+      r = load_block(kb, pg);
+      pv[(s + 2) % kStages] = page_of(kb + 2 * kBlockKeys);
+    };
+
+    auto process = [&](const RawRec& cur, int kb) {
+      // keep the q reads from LDS inside the loop (hoisting them would hold
+      // all 18 k-steps of q in registers again)
+      asm volatile("" ::: "memory");
+      // ---- S = K Q^T: one accumulator per 128-value block + rope -----------
+      f32x4 acc[4], accr = {0.f, 0.f, 0.f, 0.f};
+      for (int blk = 0; blk < 4; ++blk) {
+        acc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 a = e4m3x8_to_bf16(half_of(cur.kl[blk][s >> 1], s & 1));
+          acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qw[4 * blk + s][lane], acc[blk], 0, 0, 0);
+        }
+      }
+      for (int t = 0; t < 2; ++t)
+        accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.kr[t]), qw[16 + t][lane], accr, 0, 0, 0);
+      // lane holds S[key kb + 4 g4 + i][row n]
+      float sv[4];
+      for (int i = 0; i < 4; ++i) {
+        const float4 sc = cur.sc[i];
+        sv[i] = accr[i] + sc.x * acc[0][i] + sc.y * acc[1][i] + sc.z * acc[2][i] + sc.w * acc[3][i];
+      }
+      if (kb + kBlockKeys - 1 > lim_min) {
+        for (int i = 0; i < 4; ++i)
+          if (kb + 4 * g4 + i > lim) sv[i] = -INFINITY;
+      }
+      // ---- online softmax ---------------------------------------------------
+      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      mx = pair32(pair16(mx, true), true);
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float corr = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
+      float pr[4], psum = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f((sv[i] - m_use) * c2);
+        psum += pr[i];
+      }
+      l_part = l_part * corr + psum;
+      if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
+        for (int gr = 0; gr < 4; ++gr)
+          for (int mt = 0; mt < 8; ++mt) oacc[gr][mt] *= corr;
+      }
+      m_run = m_new;
+      // ---- O^T += V^T (P * scale)^T per 128-value block of d_v --------------
+      for (int gr = 0; gr < 4; ++gr) {
+        const float s0 = gr == 0 ? cur.sc[0].x : gr == 1 ? cur.sc[0].y : gr == 2 ? cur.sc[0].z : cur.sc[0].w;
+        const float s1 = gr == 0 ? cur.sc[1].x : gr == 1 ? cur.sc[1].y : gr == 2 ? cur.sc[1].z : cur.sc[1].w;
+        const float s2 = gr == 0 ? cur.sc[2].x : gr == 1 ? cur.sc[2].y : gr == 2 ? cur.sc[2].z : cur.sc[2].w;
+        const float s3 = gr == 0 ? cur.sc[3].x : gr == 1 ? cur.sc[3].y : gr == 2 ? cur.sc[3].z : cur.sc[3].w;
+        const bf16x4 pb = {(__bf16)(pr[0] * s0), (__bf16)(pr[1] * s1), (__bf16)(pr[2] * s2), (__bf16)(pr[3] * s3)};
+        for (int w2 = 0; w2 < 2; ++w2) {
+          const unsigned a0 = w2 ? cur.v[0][gr].y : cur.v[0][gr].x;
+          const unsigned a1 = w2 ? cur.v[1][gr].y : cur.v[1][gr].x;
+          const unsigned a2 = w2 ? cur.v[2][gr].y : cur.v[2][gr].x;
+          const unsigned a3 = w2 ? cur.v[3][gr].y : cur.v[3][gr].x;
+          const unsigned x01 = __builtin_amdgcn_perm(a0, a1, 0x01050004u);
+          const unsigned y01 = __builtin_amdgcn_perm(a0, a1, 0x03070206u);
+          const unsigned x23 = __builtin_amdgcn_perm(a2, a3, 0x01050004u);
+          const unsigned y23 = __builtin_amdgcn_perm(a2, a3, 0x03070206u);
+          for (int e = 0; e < 4; ++e) {
+            const unsigned s01 = (e >> 1) ? y01 : x01;
+            const unsigned s23 = (e >> 1) ? y23 : x23;
+            const bf16x2 lo = (e & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(s01, 1.0f, true)
+                                      : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(s01, 1.0f, false);
+            const bf16x2 hi = (e & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(s23, 1.0f, true)
+                                      : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(s23, 1.0f, false);
+            const bf16x4 a = {lo[0], lo[1], hi[0], hi[1]};
+            const int mt = 4 * w2 + e;
+            oacc[gr][mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, oacc[gr][mt], 0, 0, 0);
+          }
+        }
+      }
+    };
+
+    RawRec ring[kStages];
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s) fetch(ring[s], k_begin + kBlockKeys * s, s);
+    const int rounds = (k_end - k_begin + kBlockKeys * kStages - 1) / (kBlockKeys * kStages);
+    for (int r = 0; r < rounds; ++r) {
+      const int kb0 = k_begin + r * kBlockKeys * kStages;
+#pragma unroll
+      for (int s = 0; s < kStages; ++s) {
+        const int kb = kb0 + kBlockKeys * s;
+        fetch(ring[(s + kStages - 1) % kStages], kb + kBlockKeys * (kStages - 1), (s + kStages - 1) % kStages);
+        process(ring[s], kb);
+      }
+    }
+  }
+
+  // ---- epilogue ---------------------------------------------------------------
+  const float l = pair32(pair16(l_part, false), false);
+  if (!row_ok) return;
+  const int64_t stat_row = (int64_t)b * p.rows + n;
+  const float m_nat = m_run == -INFINITY ? -INFINITY : m_run * p.scale;
+  if (direct) {
+    const float inv = l > 0.f ? p.o_scale / l : 0.f;
+    uint8_t* orow = p.o + (int64_t)qtok * p.o_tok + (int64_t)qhead * p.o_head;
+    for (int gr = 0; gr < 4; ++gr)
+      for (int i = 0; i < 4; ++i) {
+        bf16x8 out;
+        for (int mt = 0; mt < 8; ++mt) out[mt] = (__bf16)(oacc[gr][mt][i] * inv);
+        *reinterpret_cast<bf16x8*>(orow + 2 * (128 * gr + 32 * g4 + 8 * i)) = out;
+      }
+    if (g4 == 0) p.lse[stat_row] = l > 0.f ? m_nat + logf(l) : -INFINITY;
+  } else {
+    const int64_t prow = (int64_t)slot * p.num_seqs * p.rows + stat_row;
+    float* dst = p.ws_o + prow * kDv + 32 * g4;
+    for (int gr = 0; gr < 4; ++gr)
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 lo4 = {oacc[gr][0][i], oacc[gr][1][i], oacc[gr][2][i], oacc[gr][3][i]};
+        const f32x4 hi4 = {oacc[gr][4][i], oacc[gr][5][i], oacc[gr][6][i], oacc[gr][7][i]};
+        *reinterpret_cast<f32x4*>(dst + 128 * gr + 8 * i) = lo4;
+        *reinterpret_cast<f32x4*>(dst + 128 * gr + 8 * i + 4) = hi4;
+      }
+    if (g4 == 0) p.ws_ml[prow] = float2{m_nat, l};
+  }
+}
+
+const void* select_kernel(bool causal_tail) {
+  return causal_tail ? reinterpret_cast<const void*>(&mla_decode_kernel<true>)
+                     : reinterpret_cast<const void*>(&mla_decode_kernel<false>);
+}
+
+int waves_per_wg(const pkv_decode_args& a) {
+  const int blocks = (a.q_len * a.h_q + 15) / 16;
+  return blocks < kMaxWaves ? blocks : kMaxWaves;
+}
+
+int log2_exact(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+}  // namespace
+
+int mla_rows_per_tile(const pkv_decode_args& a) { return 16 * waves_per_wg(a); }
+
+hipError_t mla_occupancy(const pkv_decode_args& a, int* units_per_cu) {
+  // one unit = one workgroup (all rows of one q-row tile of a work item)
+  const int wpw = waves_per_wg(a);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(units_per_cu, select_kernel(a.causal && a.q_len > 1), 64 * wpw,
+                                                      (size_t)wpw * kQSteps * 64 * 16);
+}
+
+hipError_t mla_launch(const pkv_decode_args& a, hipStream_t stream) {
+  MlaParams p;
+  p.q = static_cast<const uint8_t*>(a.q);
+  p.q_tok = a.q_tok_stride * 2;
+  p.q_head = a.q_head_stride * 2;
+  p.lat = a.k;
+  p.lat_page = a.k_page_stride;
+  p.lat_row = a.k_row_stride;
+  p.rope = reinterpret_cast<const uint8_t*>(a.k_rope);
+  p.rope_page = a.rope_page_stride * 2;
+  p.rope_row = a.rope_row_stride * 2;
+  p.scl = reinterpret_cast<const uint8_t*>(a.k_blk_scale);
+  p.scl_page = a.scale_page_stride * 4;
+  p.scl_row = a.scale_row_stride * 4;
+  p.block_table = a.block_table;
+  p.bt_row = a.bt_row_stride;
+  p.seq_lens = a.seq_lens;
+  p.o = static_cast<uint8_t*>(a.o);
+  p.o_tok = a.o_tok_stride * 2;
+  p.o_head = a.o_head_stride * 2;
+  p.lse = a.lse;
+  p.work = reinterpret_cast<const int4*>(a.work);
+  p.n_splits = a.n_splits;
+  const int64_t rows_all = ws_rows(a);
+  p.ws_o = static_cast<float*>(a.workspace);
+  p.ws_ml = a.workspace ? reinterpret_cast<float2*>(p.ws_o + (int64_t)a.max_splits * rows_all * kDv) : nullptr;
+  p.scale_log2e = (float)((double)a.softmax_scale * 1.4426950408889634);
+  p.scale = a.softmax_scale;
+  p.o_scale = a.o_scale;
+  p.num_seqs = a.num_seqs;
+  p.q_len = a.q_len;
+  p.h_q = a.h_q;
+  p.rows = a.q_len * a.h_q;
+  p.page_shift = log2_exact(a.page_size);
+  p.num_pages = a.num_pages;
+  p.max_blocks = a.max_blocks;
+  p.max_splits = a.max_splits;
+  const int wpw = waves_per_wg(a);
+  const int tiles = (p.rows + 16 * wpw - 1) / (16 * wpw);
+  dim3 grid(a.num_work, tiles, 1);
+  void* args[] = {&p};
+  return hipLaunchKernel(select_kernel(a.causal && a.q_len > 1), grid, dim3(64 * wpw), args,
+                         (size_t)wpw * kQSteps * 64 * 16, stream);
+}
 
 }  // namespace pkv

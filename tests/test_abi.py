@@ -143,8 +143,12 @@ BAD = [
     (dict(q_format=1, q_descale=None), -1),
     (dict(max_splits=4), -4),
     (dict(max_splits=4, workspace=1 << 41, workspace_bytes=100), -4),
-    (dict(kv_format=1, h_k=1, d_qk=576, d_v=512), -2),
     (dict(kv_format=1, h_k=2, h_q=8, d_qk=576, d_v=512), -2),
+    (dict(kv_format=1, h_k=1, h_q=16, d_qk=576, d_v=512, q_format=1, q_descale=1 << 42), -2),
+    (dict(kv_format=1, h_k=1, h_q=16, q_len=17, d_qk=576, d_v=512), -2),
+    (dict(kv_format=1, h_k=1, h_q=16, d_qk=512, d_v=512), -2),
+    (dict(kv_format=1, h_k=1, h_q=16, d_qk=576, d_v=512), -1),  # v differs from k
+    (dict(kv_format=1, h_k=1, h_q=16, d_qk=576, d_v=512, v=None), -1),  # no rope / scales
 ]
 
 

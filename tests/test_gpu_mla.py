@@ -1,0 +1,82 @@
+"""GPU parity of the latent-record (MLA-like) decode against the fp64 oracle.
+
+One KV head of 656-byte records (512 e4m3 latent values, 64 bf16 rope values,
+four fp32 scales, one per 128 latent values), 16 query heads, q tokens
+T in {1, 2, 4, 8, 16} with the causal tail, 64-key pages. Bars as for the
+GQA path: max|dO| <= 1e-2 * max|V| (V = scaled latent), max|dLSE| <= 1e-3,
+empty rows exactly O = 0 / LSE = -inf.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import O_TOL, assert_matches, gpu_rows, max_abs_v, nan_fill_, oracle_for
+from paged_kv_fp8_amd.workloads import make_batch, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def run_batch(batch, **kw):
+    from paged_kv_fp8_amd import decode
+
+    dec = decode.for_batch(batch, **kw)
+    if dec.has_splits:
+        nan_fill_(dec.workspace)
+    dec.run()
+    torch.cuda.synchronize()
+    return dec
+
+
+def compare(batch, dec, seqs=None, what=""):
+    spec = batch.spec
+    nb = batch.to_numpy()
+    o_ref, lse_ref = oracle_for(nb, spec, seqs)
+    o_g, lse_g = gpu_rows(dec.o, dec.lse, spec, seqs)
+    return assert_matches(o_g, lse_g, o_ref, lse_ref, max_abs_v(nb, spec, seqs), what=what)
+
+
+@pytest.mark.parametrize("T,causal", [(1, True), (2, True), (4, True), (4, False), (8, True), (16, True)])
+def test_small_latent_every_output(T, causal):
+    w = workload(5, q_len=T, causal=causal, num_seqs=4, seq_len_dist=("uniform", 40, 700))
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch)
+    err_o, err_l, _ = compare(batch, dec, what=f"latent T={T} causal={causal}")
+    print(f"T={T} causal={causal}: splits={dec.plan_info.max_n_splits} max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 8, 16])
+def test_full_latent_sampled(T):
+    w = workload(5, q_len=T)
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch)
+    lens = batch.seq_lens.cpu().numpy()
+    order = np.argsort(lens)
+    seqs = sorted({int(order[0]), int(order[-1]), 3, 17})
+    err_o, err_l, _ = compare(batch, dec, seqs=seqs, what=f"latent full T={T}")
+    print(f"T={T}: seqs={seqs} splits={dec.plan_info.max_n_splits} chunk={dec.plan_info.chunk_tiles} "
+          f"work={dec.plan_info.num_real} max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
+
+
+EDGE = [0, 1, 2, 15, 16, 17, 63, 64, 65, 127, 128, 129, 1000]
+
+
+@pytest.mark.parametrize("T,force", [(1, 0), (2, 3), (4, 2)])
+def test_latent_edge_lengths(T, force):
+    w = workload(5, q_len=T, num_seqs=len(EDGE), seq_len_dist=("fixed", EDGE), max_splits=8)
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch, force_splits=force)
+    compare(batch, dec, what=f"latent edge T={T} force={force}")
+
+
+def test_latent_repeat_bitwise():
+    w = workload(5, q_len=2, num_seqs=6, seq_len_dist=("uniform", 100, 3000))
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch)
+    o1, l1 = dec.o.clone(), dec.lse.clone()
+    for fill in (0x00, 0x7F):
+        dec.workspace.fill_(fill)
+        dec.run()
+        torch.cuda.synchronize()
+        assert torch.equal(dec.o.view(torch.int16), o1.view(torch.int16))
+        assert torch.equal(dec.lse.view(torch.int32), l1.view(torch.int32))
