@@ -142,6 +142,8 @@ def main():
     ap.add_argument("--page-size", type=int, default=None, help="override the workload's page size")
     ap.add_argument("--contiguous-pages", action="store_true", help="hand out pages in order instead of shuffled")
     ap.add_argument("--seq-len", type=int, default=None, help="give every sequence this length")
+    ap.add_argument("--fused-merge", action="store_true",
+                    help="merge split sequences inside the decode kernel (last split merges) instead of a second launch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 8 plain 256 MiB device-to-device copies (scale reference for HBM byte counters)")
     args = ap.parse_args()
@@ -185,7 +187,7 @@ def main():
     lens = first.seq_lens.cpu().numpy()
     batches = [first] + [make_batch(dataclasses.replace(w, seed=w.seed + 1000 * i), device="cuda", seq_lens=lens)
                          for i in range(1, pools)]
-    decs = [decode.for_batch(b, wg_per_cu=args.wg_per_cu) for b in batches]
+    decs = [decode.for_batch(b, wg_per_cu=args.wg_per_cu, fused_merge=args.fused_merge) for b in batches]
     info = decs[0].plan_info
     ab = algorithmic_bytes(first, decs[0])
     log(f"workload {w.name}: {w.num_seqs} seqs, {int(lens.sum())} tokens, KV {ab['kv'] / 1e6:.1f} MB, "
@@ -261,6 +263,7 @@ def main():
                    "d": w.d_qk, "page_size": w.page_size, "causal": w.causal, "kv_layout": w.kv_layout,
                    "contiguous_pages": w.contiguous_pages, "kv_tokens": int(lens.sum()),
                    "kv_bytes": ab["kv"], "max_splits": w.max_splits, "pools": pools,
+                   "merge": "separate launch" if not decs[0].fused_merge else "in decode kernel",
                    "plan": {"chunk_tiles": info.chunk_tiles, "work_items": info.num_real, "slots": info.slots,
                             "max_n_splits": info.max_n_splits, "wg_per_cu": decs[0].wg_per_cu}},
         "roofline": roofline,

@@ -196,6 +196,15 @@ typedef struct pkv_decode_args {
   int32_t max_splits;
   void* workspace;
   size_t workspace_bytes;
+  /* Optional, device int32[num_seqs * h_k * n_q_tiles] (e4m3 K/V cache only;
+   * ignored for the latent cache): when non-NULL the decode merges split
+   * sequences itself (the last split of each (sequence,
+   * kv head, q-row tile) to finish combines the partials, same rule and
+   * order as pkv_merge_splits) and pkv_merge_splits does nothing. The
+   * counters must be zero before the first call; every completed call
+   * leaves them zero, so no per-call clearing is needed. NULL: partials are
+   * left for pkv_merge_splits. Calls that overlap on one counter array race. */
+  int32_t* merge_counters;
 } pkv_decode_args;
 
 /* Bytes of split workspace: max_splits * num_seqs * h_k * n_rows * (d_v + 2)
@@ -205,8 +214,11 @@ size_t pkv_workspace_bytes(int32_t num_seqs, int32_t h_k, int32_t n_rows, int32_
 /*
  * Occupancy facts the planner needs for these arguments (shapes, formats,
  * mode; pointers are not read): the current device's compute-unit count,
- * how many decode workgroups of the selected kernel are resident per CU,
- * and the number of q-row tiles of the grid. Queries the HIP runtime; no
+ * how many (work item, kv head, q-row tile) units to plan per CU, and the
+ * number of q-row tiles of the grid. For the e4m3 cache a unit is one wave
+ * and the count targets about four streaming waves per CU (at least one
+ * workgroup, at most what fits); for the latent cache a unit is one
+ * workgroup and the count is the resident maximum. Queries the HIP runtime; no
  * launch. Errors: INVALID_ARG / UNSUPPORTED as pkv_paged_decode_attn would
  * return for the shapes, HIP on a runtime failure.
  */
@@ -232,7 +244,8 @@ pkv_status pkv_paged_decode_attn(const pkv_decode_args* a, void* stream);
  * m_j = -inf), O = o_scale * sum_j w_j O_j / sum_j w_j l_j (0 if the sum is
  * 0), LSE = m* + ln sum_j w_j l_j, over j < n_splits[b] in index order.
  * Sequences with n_splits <= 1 are left as the decode wrote them. A no-op
- * (nothing launched) when max_splits == 1. Same arguments as the decode.
+ * (nothing launched) when max_splits == 1 or when merge_counters is set (the
+ * decode merged already). Same arguments as the decode.
  */
 pkv_status pkv_merge_splits(const pkv_decode_args* a, void* stream);
 

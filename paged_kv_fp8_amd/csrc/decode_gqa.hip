@@ -82,6 +82,7 @@ struct GqaParams {
   const int32_t* n_splits;
   float* ws_o;   // [max_splits][num_seqs][h_k][rows][128]
   float2* ws_ml; // [max_splits][num_seqs][h_k][rows]
+  int32_t* counters;  // [num_seqs][h_k][q-row tiles] or null: merge in a separate launch
   float scale_log2e, scale, o_scale;
   int num_seqs, q_len, h_k, h_r, rows, page_shift, num_pages, max_blocks, max_splits;
 };
@@ -119,6 +120,57 @@ __device__ __forceinline__ float pair32(float x, bool take_max) {
 }
 __device__ __forceinline__ float wave_max16(float x) { return pair32(pair16(x, true), true); }
 __device__ __forceinline__ float wave_sum16(float x) { return pair32(pair16(x, false), false); }
+
+// 8-byte stores / loads that are coherent across the XCDs of the device
+// (agent-scope relaxed atomics: they go past the XCD-local L2).
+__device__ __forceinline__ void store_coherent(float* dst, float a, float b) {
+  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(dst), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_coherent(const float* src) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(src), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return float2{__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32))};
+}
+
+// Combine the partials of splits 0 .. ns-1 for this wave's rows, with the
+// rule and the arithmetic order of the separate merge kernel: m* = max m_j,
+// w_j = exp(m_j - m*) (0 for m_j = -inf), O = o_scale * sum w_j O_j / sum
+// w_j l_j, LSE = m* + ln sum w_j l_j. Lane (r16, g4) owns row r16 of each
+// 16-row block and d_v values 32*g4 .. 32*g4+31.
+template <int NB>
+__device__ __forceinline__ void merge_rows(const GqaParams& p, int b, int g, int row0, int r16, int g4, int ns,
+                                           const int* qtok, const int* qhead) {
+  const int64_t split_stride = (int64_t)p.num_seqs * p.h_k * p.rows;
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = row0 + 16 * nb + r16;
+    if (n >= p.rows) continue;
+    const int64_t row = ((int64_t)b * p.h_k + g) * p.rows + n;
+    float m_star = -INFINITY;
+    for (int j = 0; j < ns; ++j) m_star = fmaxf(m_star, load_coherent(reinterpret_cast<const float*>(p.ws_ml + j * split_stride + row)).x);
+    float acc[32];
+    for (int e = 0; e < 32; ++e) acc[e] = 0.f;
+    float den = 0.f;
+    for (int j = 0; j < ns; ++j) {
+      const float2 ml = load_coherent(reinterpret_cast<const float*>(p.ws_ml + j * split_stride + row));
+      const float wgt = ml.x == -INFINITY ? 0.f : __expf(ml.x - m_star);
+      const float* src = p.ws_o + (j * split_stride + row) * kD + 32 * g4;
+      den += wgt * ml.y;
+      for (int e = 0; e < 32; e += 2) {
+        const float2 v = load_coherent(src + e);
+        acc[e] += wgt * v.x;
+        acc[e + 1] += wgt * v.y;
+      }
+    }
+    const float inv = den > 0.f ? p.o_scale / den : 0.f;
+    uint8_t* orow = p.o + (int64_t)qtok[nb] * p.o_tok + (int64_t)qhead[nb] * p.o_head;
+    for (int e0 = 0; e0 < 32; e0 += 8) {
+      bf16x8 out;
+      for (int e = 0; e < 8; ++e) out[e] = (__bf16)(acc[e0 + e] * inv);
+      *reinterpret_cast<bf16x8*>(orow + 2 * (32 * g4 + e0)) = out;
+    }
+    if (g4 == 0) p.lse[row] = den > 0.f ? m_star + logf(den) : -INFINITY;
+  }
+}
 
 // Raw bytes of one 32-key block as this lane loads them.
 struct RawBlock {
@@ -402,13 +454,42 @@ __global__ __launch_bounds__(64 * HW) void gqa_decode_kernel(GqaParams p) {
       const int64_t prow = (int64_t)slot * p.num_seqs * p.h_k * p.rows + stat_row;
       const float ps = vdv / p_scale;
       float* dst = p.ws_o + prow * kD + 32 * g4;
-      for (int i = 0; i < 4; ++i) {
-        f32x4 lo4 = {oacc[nb][0][i], oacc[nb][1][i], oacc[nb][2][i], oacc[nb][3][i]};
-        f32x4 hi4 = {oacc[nb][4][i], oacc[nb][5][i], oacc[nb][6][i], oacc[nb][7][i]};
-        *reinterpret_cast<f32x4*>(dst + 8 * i) = lo4 * ps;
-        *reinterpret_cast<f32x4*>(dst + 8 * i + 4) = hi4 * ps;
+      if (p.counters) {
+        // read back by whichever split of this row finishes last, maybe on
+        // another XCD: agent-coherent stores (past the XCD's own L2)
+        for (int i = 0; i < 4; ++i)
+          for (int mt = 0; mt < 8; mt += 2)
+            store_coherent(dst + 8 * i + mt, oacc[nb][mt][i] * ps, oacc[nb][mt + 1][i] * ps);
+        if (g4 == 0) store_coherent(reinterpret_cast<float*>(p.ws_ml + prow), m_nat, l);
+      } else {
+        for (int i = 0; i < 4; ++i) {
+          f32x4 lo4 = {oacc[nb][0][i], oacc[nb][1][i], oacc[nb][2][i], oacc[nb][3][i]};
+          f32x4 hi4 = {oacc[nb][4][i], oacc[nb][5][i], oacc[nb][6][i], oacc[nb][7][i]};
+          *reinterpret_cast<f32x4*>(dst + 8 * i) = lo4 * ps;
+          *reinterpret_cast<f32x4*>(dst + 8 * i + 4) = hi4 * ps;
+        }
+        if (g4 == 0) p.ws_ml[prow] = float2{m_nat, l};
       }
-      if (g4 == 0) p.ws_ml[prow] = float2{m_nat, l};
+    }
+  }
+
+  // ---- in-kernel merge: the last split of this (sequence, head, q tile) ------
+  if (!direct && p.counters) {
+    // The partials above were written with agent-coherent stores; wait until
+    // they have all completed, then count this split. The split that counts
+    // last reads every partial back with agent-coherent loads. Only the
+    // partials and the counter are shared, so no cache-wide write-back or
+    // invalidate is needed.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    int32_t* ctr = p.counters + ((int64_t)b * p.h_k + g) * gridDim.z + blockIdx.z;
+    int last = 0;
+    if (lane == 0)
+      last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == min(ns, p.max_splits) - 1;
+    last = __builtin_amdgcn_readfirstlane(last);
+    if (last) {
+      asm volatile("" ::: "memory");
+      merge_rows<NB>(p, b, g, row0, r16, g4, min(ns, p.max_splits), qtok, qhead);
+      if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -465,10 +546,17 @@ GqaVariant gqa_variant(const pkv_decode_args& a) {
 int gqa_rows_per_tile(const GqaVariant& v) { return 16 * v.n_blocks; }
 
 hipError_t gqa_occupancy(const GqaVariant& v, int* units_per_cu) {
-  // resident (work item, kv head, q tile) units per CU = resident waves
+  // Units (work item, kv head, q tile) = waves. The plan is sized for about
+  // four streaming waves per CU (at least one workgroup), not for the
+  // register-limited maximum: per-CU read bandwidth saturates at ~32-64 KB
+  // in flight, and a second workgroup on some CUs but not on others leaves
+  // those CUs with twice the bytes (measured on the fully-fp8 workload:
+  // 0.61 -> 0.68 of peak).
   int wgs = 0;
   const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&wgs, select_kernel(v), 64 * v.heads_per_wg, 0);
-  *units_per_cu = wgs * v.heads_per_wg;
+  const int resident = wgs * v.heads_per_wg;
+  const int target = v.heads_per_wg > 4 ? v.heads_per_wg : 4;
+  *units_per_cu = resident < target ? resident : target;
   return e;
 }
 
@@ -507,6 +595,7 @@ hipError_t gqa_launch(const pkv_decode_args& a, const GqaVariant& v, hipStream_t
   const int64_t rows_all = ws_rows(a);
   p.ws_o = static_cast<float*>(a.workspace);
   p.ws_ml = a.workspace ? reinterpret_cast<float2*>(p.ws_o + (int64_t)a.max_splits * rows_all * kD) : nullptr;
+  p.counters = a.max_splits > 1 ? a.merge_counters : nullptr;
   p.scale_log2e = (float)((double)a.softmax_scale * 1.4426950408889634);
   p.scale = a.softmax_scale;
   p.o_scale = a.o_scale;

@@ -7,8 +7,8 @@
 // by the decode and are skipped. The j order is fixed, so the result is
 // deterministic.
 //
-// gfx950 layout: one thread owns 8 consecutive d_v values of one row
-// (two 16-byte loads per split, one 16-byte bf16 store), 256 threads per
+// gfx950 layout: one thread owns 4 consecutive d_v values of one row (one
+// 16-byte load per split, one 8-byte bf16 store), 256 threads per
 // workgroup; the (max, sum) pairs of a row are read by all its threads from
 // the same cache lines.
 #include <hip/hip_runtime.h>
@@ -21,6 +21,7 @@ namespace pkv {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct MergeParams {
@@ -36,9 +37,14 @@ struct MergeParams {
   int h_k, rows, h_r, q_len, d_v, max_splits;
 };
 
+// kSplitsPerRound splits are read per round with independent loads (the
+// (max, sum) pairs first, then the partial rows), so a row costs two memory
+// latencies per round instead of one per split.
+constexpr int kSplitsPerRound = 16;
+
 template <int DV>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
-  constexpr int kThreadsPerRow = DV / 8;
+  constexpr int kThreadsPerRow = DV / 4;  // 4 d_v values (one 16-byte load) per thread
   constexpr int kRowsPerBlock = 256 / kThreadsPerRow;
   const int tr = threadIdx.x / kThreadsPerRow;
   const int tc = threadIdx.x % kThreadsPerRow;
@@ -53,30 +59,41 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   ns = min(ns, p.max_splits);
 
   float m_star = -INFINITY;
-  for (int j = 0; j < ns; ++j) m_star = fmaxf(m_star, p.ws_ml[j * p.split_stride + row].x);
+  for (int j0 = 0; j0 < ns; j0 += kSplitsPerRound) {
+    float mj[kSplitsPerRound];
+#pragma unroll
+    for (int u = 0; u < kSplitsPerRound; ++u)
+      mj[u] = j0 + u < ns ? p.ws_ml[(j0 + u) * p.split_stride + row].x : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kSplitsPerRound; ++u) m_star = fmaxf(m_star, mj[u]);
+  }
 
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  for (int j = 0; j < ns; ++j) {
-    const float2 ml = p.ws_ml[j * p.split_stride + row];
-    const float wgt = ml.x == -INFINITY ? 0.f : __expf(ml.x - m_star);
-    const float* src = p.ws_o + (j * p.split_stride + row) * DV + 8 * tc;
-    const f32x4 a = *reinterpret_cast<const f32x4*>(src);
-    const f32x4 c = *reinterpret_cast<const f32x4*>(src + 4);
-    den += wgt * ml.y;
-    acc0 += wgt * a;
-    acc1 += wgt * c;
+  for (int j0 = 0; j0 < ns; j0 += kSplitsPerRound) {
+    float2 ml[kSplitsPerRound];
+    f32x4 oj[kSplitsPerRound];
+#pragma unroll
+    for (int u = 0; u < kSplitsPerRound; ++u) {
+      const bool ok = j0 + u < ns;
+      const int64_t pr = (int64_t)(j0 + u) * p.split_stride + row;
+      ml[u] = ok ? p.ws_ml[pr] : float2{-INFINITY, 0.f};
+      oj[u] = ok ? *reinterpret_cast<const f32x4*>(p.ws_o + pr * DV + 4 * tc) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < kSplitsPerRound; ++u) {
+      const float wgt = ml[u].x == -INFINITY ? 0.f : __expf(ml[u].x - m_star);
+      den += wgt * ml[u].y;
+      acc += wgt * oj[u];
+    }
   }
   const float inv = den > 0.f ? p.o_scale / den : 0.f;
   const int qi = n / p.h_r;
   const int hr = n - qi * p.h_r;
   uint8_t* orow = p.o + (int64_t)(b * p.q_len + qi) * p.o_tok + (int64_t)(g * p.h_r + hr) * p.o_head;
-  bf16x8 out;
-  for (int e = 0; e < 4; ++e) {
-    out[e] = (__bf16)(acc0[e] * inv);
-    out[4 + e] = (__bf16)(acc1[e] * inv);
-  }
-  *reinterpret_cast<bf16x8*>(orow + 2 * (8 * tc)) = out;
+  bf16x4 out;
+  for (int e = 0; e < 4; ++e) out[e] = (__bf16)(acc[e] * inv);
+  *reinterpret_cast<bf16x4*>(orow + 2 * (4 * tc)) = out;
   if (tc == 0) p.lse[row] = den > 0.f ? m_star + logf(den) : -INFINITY;
 }
 
@@ -103,11 +120,11 @@ hipError_t merge_launch(const pkv_decode_args& a, hipStream_t stream) {
   p.max_splits = a.max_splits;
   void* args[] = {&p};
   if (a.d_v == 128) {
-    const int64_t blocks = (rows_all + 15) / 16;
+    const int64_t blocks = (rows_all + 7) / 8;
     return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<128>), dim3((unsigned)blocks), dim3(256),
                            args, 0, stream);
   }
-  const int64_t blocks = (rows_all + 3) / 4;
+  const int64_t blocks = (rows_all + 1) / 2;
   return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<512>), dim3((unsigned)blocks), dim3(256), args,
                          0, stream);
 }

@@ -49,7 +49,7 @@ class PagedDecode:
     def __init__(self, *, q, block_table, seq_lens, o, lse, q_len, softmax_scale, k_cache=None, v_cache=None,
                  q_descale=None, k_descale=None, v_descale=None, latent=None, rope=None, blk_scale=None,
                  num_pages=None, causal=True, o_scale=1.0, max_splits=16, force_splits=0, min_chunk_tiles=1,
-                 pad_to=0, wg_per_cu=None, plan_seq_lens=None):
+                 pad_to=0, wg_per_cu=None, plan_seq_lens=None, fused_merge=False):
         mla = latent is not None
         a = native.DecodeArgs()
         num_seqs = seq_lens.shape[0]
@@ -105,6 +105,12 @@ class PagedDecode:
         rows = q_len * (h_q // h_k)
         ws = native.workspace_bytes(num_seqs, h_k, rows, d_v, max_splits) if max_splits > 1 else 0
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)  # never initialised
+        # in-kernel merge (e4m3 cache): counters zeroed once here; every call leaves them zero
+        self.fused_merge = bool(fused_merge) and not mla and max_splits > 1
+        self.merge_counters = None
+        if self.fused_merge:
+            self.merge_counters = torch.zeros(num_seqs * h_k * n_q_tiles, dtype=torch.int32, device=dev)
+            a.merge_counters = _ptr(self.merge_counters)
         a.work, a.num_work = _ptr(self.work), int(info.num_work)
         a.n_splits = _ptr(self.n_splits)
         a.workspace, a.workspace_bytes = _ptr(self.workspace), self.workspace.numel()
@@ -123,14 +129,14 @@ class PagedDecode:
         (default: torch's current stream). No allocation, no sync."""
         s = (stream or torch.cuda.current_stream()).cuda_stream
         native.paged_decode_attn(self.args, s)
-        if self.has_splits:
+        if self.has_splits and not self.fused_merge:
             native.merge_splits(self.args, s)
 
     def run_decode_only(self, stream=None):
         native.paged_decode_attn(self.args, (stream or torch.cuda.current_stream()).cuda_stream)
 
     def run_merge_only(self, stream=None):
-        if self.has_splits:
+        if self.has_splits and not self.fused_merge:
             native.merge_splits(self.args, (stream or torch.cuda.current_stream()).cuda_stream)
 
 

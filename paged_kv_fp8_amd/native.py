@@ -59,6 +59,7 @@ class DecodeArgs(ctypes.Structure):
         ("work", _vp), ("num_work", _i32),
         ("n_splits", _vp), ("max_splits", _i32),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+        ("merge_counters", _vp),
     ]
 
 

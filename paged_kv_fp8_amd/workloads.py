@@ -91,7 +91,7 @@ WORKLOADS = {
     3: Workload("specverify_b32_q4_hq64_hk8_d128_ps64_lognormal4096", 32, 4, 64, 8, 128, 128, 64,
                 ("lognormal", 4096, 1.0, 256, 32768), max_splits=16, seed=1114),
     4: Workload("fp8_b128_hq64_hk4_d128_ps128_mix1k-4k_32k-64k", 128, 1, 64, 4, 128, 128, 128,
-                ("mix", 0.1, (32768, 65536), (1024, 4096)), max_splits=16, q_format="e4m3", seed=1115),
+                ("mix", 0.1, (32768, 65536), (1024, 4096)), max_splits=64, q_format="e4m3", seed=1115),
     5: Workload("mla_b32_hq16_hk1_d576-512_ps64_L2k-16k", 32, 1, 16, 1, 576, 512, 64,
                 ("uniform", 2048, 16384), max_splits=16, kv_format="mla", seed=1116),
 }

@@ -243,3 +243,63 @@ def test_padded_work_list_same_result():
     assert d2.plan_info.num_work == d1.plan_info.num_work + 37
     assert torch.equal(d2.o.view(torch.int16), r1[0].view(torch.int16))
     assert torch.equal(d2.lse.view(torch.int32), r1[1].view(torch.int32))
+
+
+# ---------------------------------------------------------------------------
+# in-kernel merge (merge_counters): same result as the separate merge launch
+# ---------------------------------------------------------------------------
+FUSED = {
+    "cfg2_small": dict(index=2, num_seqs=8, seq_len_dist=("uniform", 100, 5000)),
+    "cfg3_small_causal": dict(index=3, num_seqs=5, seq_len_dist=("lognormal", 700, 1.0, 5, 3000)),
+    "cfg3_small_block": dict(index=3, num_seqs=5, seq_len_dist=("lognormal", 700, 1.0, 5, 3000), causal=False),
+    "cfg4_small": dict(index=4, num_seqs=6, seq_len_dist=("mix", 0.34, (3000, 9000), (1024, 2000))),
+    "edge_forced": dict(index=2, num_seqs=len(EDGE_LENS), h_q=16, h_k=2, seq_len_dist=("fixed", EDGE_LENS),
+                        max_splits=8),
+}
+
+
+@pytest.mark.parametrize("name", list(FUSED))
+def test_fused_merge_equals_separate_merge(name):
+    kw = dict(FUSED[name])
+    w = workload(kw.pop("index"), **kw)
+    batch = make_batch(w, device="cuda")
+    force = 3 if name == "edge_forced" else 0
+    sep = run_batch(batch, force_splits=force)
+    ref_o, ref_l = sep.o.clone(), sep.lse.clone()
+    fused = _decode().for_batch(batch, fused_merge=True, force_splits=force)
+    assert fused.has_splits and fused.fused_merge
+    for rep in range(3):  # counters must come back to zero after every call
+        nan_fill_(fused.workspace[: fused.workspace.numel() // 2])
+        fused.o.zero_()
+        fused.lse.zero_()
+        fused.run()
+        torch.cuda.synchronize()
+        assert torch.equal(fused.o.view(torch.int16), ref_o.view(torch.int16)), f"{name} call {rep}"
+        assert torch.equal(fused.lse.view(torch.int32), ref_l.view(torch.int32)), f"{name} call {rep}"
+        assert int(fused.merge_counters.abs().sum()) == 0
+    compare(batch, fused, what=f"fused {name}")
+
+
+def test_fused_merge_graph_replay():
+    w = workload(2, num_seqs=8, seq_len_dist=("uniform", 300, 6000))
+    batch = make_batch(w, device="cuda")
+    dec = _decode().for_batch(batch, fused_merge=True)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        dec.run(stream)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    eager_o, eager_l = dec.o.clone(), dec.lse.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dec.run()
+    for rep in range(4):
+        dec.o.zero_()
+        _ = (batch.q.float() + 1).sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dec.o.view(torch.int16), eager_o.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(dec.lse.view(torch.int32), eager_l.view(torch.int32)), f"replay {rep}"
+    assert int(dec.merge_counters.abs().sum()) == 0
