@@ -142,6 +142,9 @@ def main():
     ap.add_argument("--page-size", type=int, default=None, help="override the workload's page size")
     ap.add_argument("--contiguous-pages", action="store_true", help="hand out pages in order instead of shuffled")
     ap.add_argument("--seq-len", type=int, default=None, help="give every sequence this length")
+    ap.add_argument("--plan", default="wave", choices=["wave", "balanced"],
+                    help="wave: one work item per workgroup (occupancy-pinned split plan); balanced: contiguous "
+                         "equal shares of all keys, one per workgroup")
     ap.add_argument("--fused-merge", action="store_true",
                     help="merge split sequences inside the decode kernel (last split merges) instead of a second launch")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -187,7 +190,7 @@ def main():
     lens = first.seq_lens.cpu().numpy()
     batches = [first] + [make_batch(dataclasses.replace(w, seed=w.seed + 1000 * i), device="cuda", seq_lens=lens)
                          for i in range(1, pools)]
-    decs = [decode.for_batch(b, wg_per_cu=args.wg_per_cu, fused_merge=args.fused_merge) for b in batches]
+    decs = [decode.for_batch(b, wg_per_cu=args.wg_per_cu, fused_merge=args.fused_merge, plan=args.plan) for b in batches]
     info = decs[0].plan_info
     ab = algorithmic_bytes(first, decs[0])
     log(f"workload {w.name}: {w.num_seqs} seqs, {int(lens.sum())} tokens, KV {ab['kv'] / 1e6:.1f} MB, "
@@ -264,8 +267,10 @@ def main():
                    "contiguous_pages": w.contiguous_pages, "kv_tokens": int(lens.sum()),
                    "kv_bytes": ab["kv"], "max_splits": w.max_splits, "pools": pools,
                    "merge": "separate launch" if not decs[0].fused_merge else "in decode kernel",
+                   "plan_kind": args.plan,
                    "plan": {"chunk_tiles": info.chunk_tiles, "work_items": info.num_real, "slots": info.slots,
-                            "max_n_splits": info.max_n_splits, "wg_per_cu": decs[0].wg_per_cu}},
+                            "max_n_splits": info.max_n_splits, "wg_per_cu": decs[0].wg_per_cu,
+                            "bins": info.num_bins}},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

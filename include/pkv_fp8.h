@@ -23,7 +23,8 @@
  * "Workspace"; "MiniMax MSA fmha_sm100/cute README", Paged FP8 Decode,
  * plan() then run()):
  *   1. pkv_decode_slots()   -> CU count, resident workgroups per CU, q-row tiles
- *   2. pkv_plan_split_kv()  -> host work list + n_splits (pure host code)
+ *   2. pkv_plan_split_kv() or pkv_plan_balanced() -> host work list +
+ *      n_splits (+ bin offsets) (pure host code)
  *   3. copy work / n_splits to the device once (the caller's job)
  *   4. pkv_paged_decode_attn(); then pkv_merge_splits() when any sequence
  *      was split (info.max_n_splits > 1). Both only enqueue on `stream`:
@@ -90,6 +91,7 @@ typedef struct pkv_plan_info {
   int32_t chunk_tiles;  /* 128-key tiles per chunk (a sequence's last chunk may be shorter) */
   int32_t slots;        /* work items that fit one wave of the grid */
   int32_t max_n_splits; /* largest n_splits over the batch */
+  int32_t num_bins;     /* balanced plan: workgroups (bins) of the grid; 0 for pkv_plan_split_kv */
 } pkv_plan_info;
 
 /*
@@ -121,6 +123,32 @@ pkv_status pkv_plan_split_kv(const int32_t* seq_lens, int32_t num_seqs, int32_t 
                              int32_t cu_count, int32_t wg_per_cu, int32_t max_splits, int32_t force_splits,
                              int32_t min_chunk_tiles, int32_t pad_to, int32_t* work_out, int32_t work_cap,
                              int32_t* n_splits_out, pkv_plan_info* info);
+
+/*
+ * Balanced contiguous plan (this library's own planner; not from the pages).
+ * The 128-key tiles of all sequences, laid end to end in sequence order, are
+ * cut into `bins` contiguous shares of floor or ceil(total / bins) tiles,
+ * bins = max(1, min(total, cu_count * wg_per_cu / (h_k * n_q_tiles))) -- the
+ * workgroups that run at once -- lowered until no sequence is cut into more
+ * than max_splits pieces. Every overlap of a share and a sequence is a work
+ * item (seq, tile_begin, tile_end, split_slot), split slots numbered in key
+ * order; items are listed bin by bin and bin i owns items
+ * [bin_offsets[i], bin_offsets[i+1]). Each workgroup then carries the same
+ * number of keys (to one tile), whatever the length mix, and sequences are
+ * split only at share boundaries.
+ *
+ * seq_lens        host int32[num_seqs], each >= 0
+ * work_out        host int32[work_cap][4]; at most bins + num_seqs - 1 items
+ * n_splits_out    host int32[num_seqs]
+ * bin_offsets_out host int32[bins_cap], bins + 1 entries are written
+ * info            host, may be NULL (num_bins = bins)
+ * Errors: as pkv_plan_split_kv; CAPACITY when work_cap or bins_cap is too
+ * small.
+ */
+pkv_status pkv_plan_balanced(const int32_t* seq_lens, int32_t num_seqs, int32_t h_k, int32_t n_q_tiles,
+                             int32_t cu_count, int32_t wg_per_cu, int32_t max_splits, int32_t* work_out,
+                             int32_t work_cap, int32_t* n_splits_out, int32_t* bin_offsets_out, int32_t bins_cap,
+                             pkv_plan_info* info);
 
 /* ------------------------------------------------------------------------ */
 /* Decode launch arguments                                                   */
@@ -205,6 +233,12 @@ typedef struct pkv_decode_args {
    * leaves them zero, so no per-call clearing is needed. NULL: partials are
    * left for pkv_merge_splits. Calls that overlap on one counter array race. */
   int32_t* merge_counters;
+  /* Optional, device int32[num_bins + 1] from pkv_plan_balanced: workgroup i
+   * runs work items [bin_offsets[i], bin_offsets[i+1]) in order, and the
+   * grid has num_bins workgroups per (kv-head group, q-row tile). NULL: one
+   * work item per workgroup, num_work workgroups (pkv_plan_split_kv). */
+  const int32_t* bin_offsets;
+  int32_t num_bins;
 } pkv_decode_args;
 
 /* Bytes of split workspace: max_splits * num_seqs * h_k * n_rows * (d_v + 2)

@@ -26,6 +26,8 @@ the chunk against a linear scan, coverage/contiguity of every sequence's
 chunks, the wave bound, the ordering and the padding.
 """
 
+import bisect
+
 TILE_KEYS = 128
 
 
@@ -85,3 +87,56 @@ def plan_split_kv(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16
             raise ValueError(f"pad_to {pad_to} < {len(work)} work items")
         work += [(0, 0, 0, 0)] * (pad_to - len(work))
     return work, n_splits, chunk, slots
+
+
+def plan_balanced(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16):
+    """Balanced contiguous plan (this build's own planner, not the pages'):
+    the 128-key tiles of all sequences, laid end to end in sequence order,
+    are cut into `bins` contiguous shares of floor/ceil(total / bins) tiles,
+    bins = the workgroups that run at once (the ``slots`` of the rule above).
+    Bin i takes global tiles [floor(i * total / bins), floor((i+1) * total /
+    bins)); every (sequence, share) overlap is a work item, split slots
+    numbered in key order. If some sequence would be cut into more than
+    max_splits pieces, bins is lowered until none is. Returns (work ordered
+    by bin, n_splits, bin_offsets[bins + 1], bins).
+    """
+    seq_lens = [int(x) for x in seq_lens]
+    if not seq_lens:
+        raise ValueError("empty batch")
+    if any(x < 0 for x in seq_lens):
+        raise ValueError("negative sequence length")
+    if min(h_k, n_q_tiles, cu_count, wg_per_cu, max_splits) < 1:
+        raise ValueError("sizes must be positive")
+    tiles = [max(1, _ceil_div(L, TILE_KEYS)) for L in seq_lens]
+    total = sum(tiles)
+    starts = [0]
+    for t in tiles:
+        starts.append(starts[-1] + t)
+    bins = max(1, min(total, (cu_count * wg_per_cu) // (h_k * n_q_tiles)))
+
+    def pieces_for(nb):
+        """Shares that overlap each sequence when `total` tiles are cut into nb."""
+        bounds = [(i * total) // nb for i in range(nb + 1)]
+        # share holding global tile x: the last i with bounds[i] <= x
+        share = lambda x: bisect.bisect_right(bounds, x) - 1  # noqa: E731
+        return [share(starts[b + 1] - 1) - share(starts[b]) + 1 for b in range(len(tiles))], bounds
+
+    while True:
+        pieces, bounds = pieces_for(bins)
+        if max(pieces) <= max_splits or bins == 1:
+            break
+        bins -= 1
+    if max(pieces) > max_splits:
+        raise ValueError(f"{max(pieces)} chunks exceed max_splits={max_splits}")
+    per_bin = []
+    for i in range(bins):
+        lo, hi = bounds[i], bounds[i + 1]
+        per_bin.append([(b, max(lo, starts[b]) - starts[b], min(hi, starts[b + 1]) - starts[b])
+                        for b in range(len(tiles)) if max(lo, starts[b]) < min(hi, starts[b + 1])])
+    work, offsets, seen = [], [0], [0] * len(tiles)
+    for items in per_bin:
+        for b, tb, te in items:
+            work.append((b, tb, te, seen[b]))
+            seen[b] += 1
+        offsets.append(len(work))
+    return work, pieces, offsets, bins

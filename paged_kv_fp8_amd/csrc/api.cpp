@@ -90,6 +90,8 @@ pkv_status check_pointers(const pkv_decode_args* a, bool for_merge) {
   if (!aligned(a->q, 16) || bad_stride(a->q_tok_stride, q_elem, q_mult) || bad_stride(a->q_head_stride, q_elem, q_mult))
     return fail(PKV_ERR_INVALID_ARG, "q must be 16-B aligned with %lld-B multiple strides", (long long)q_mult);
   if (!aligned(a->work, 16)) return fail(PKV_ERR_INVALID_ARG, "work must be 16-B aligned");
+  if (a->bin_offsets && (a->num_bins < 1 || !aligned(a->bin_offsets, 4)))
+    return fail(PKV_ERR_INVALID_ARG, "bin_offsets needs num_bins >= 1 and 4-B alignment");
   if (a->bt_row_stride < a->max_blocks)
     return fail(PKV_ERR_INVALID_ARG, "bt_row_stride=%lld < max_blocks=%d", (long long)a->bt_row_stride,
                 a->max_blocks);

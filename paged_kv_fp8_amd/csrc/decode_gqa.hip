@@ -83,6 +83,7 @@ struct GqaParams {
   float* ws_o;   // [max_splits][num_seqs][h_k][rows][128]
   float2* ws_ml; // [max_splits][num_seqs][h_k][rows]
   int32_t* counters;  // [num_seqs][h_k][q-row tiles] or null: merge in a separate launch
+  const int32_t* bin_offsets;  // [bins + 1] or null: one work item per workgroup
   float scale_log2e, scale, o_scale;
   int num_seqs, q_len, h_k, h_r, rows, page_shift, num_pages, max_blocks, max_splits;
 };
@@ -178,24 +179,19 @@ struct RawBlock {
   uint2 v[8];     // key kb+16*(j>>2)+4*g4+(j&3), bytes 8*r16 .. 8*r16+7
 };
 
-template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES, int HW>
-__global__ __launch_bounds__(64 * HW) void gqa_decode_kernel(GqaParams p) {
-  // HW waves per workgroup, one per kv head of the same work item: together
-  // they stream the same pages (every head's rows of a key range), which
-  // keeps the number of concurrent DRAM streams per key range at two (K, V).
-  const int lane = threadIdx.x & 63;
-  const int g = blockIdx.y * HW + (threadIdx.x >> 6);
+// One work item (sequence chunk) for kv head g: the body of the decode.
+template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES>
+__device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, int lane, int g) {
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
 
-  const int4 w = p.work[blockIdx.x];
+  const int4 w = p.work[item];
   const int b = w.x;
   if (w.z <= w.y || b < 0 || b >= p.num_seqs) return;  // padding item / bad entry
   const int ns = p.n_splits[b];
   const bool direct = ns <= 1;
   const int slot = w.w;
   if (!direct && (slot < 0 || slot >= p.max_splits)) return;
-  if (g >= p.h_k) return;
   const int row0 = blockIdx.z * (16 * NB);
 
   const int page_size = 1 << p.page_shift;
@@ -494,6 +490,24 @@ __global__ __launch_bounds__(64 * HW) void gqa_decode_kernel(GqaParams p) {
   }
 }
 
+// HW waves per workgroup, one per kv head of the same work item: together
+// they stream the same pages (every head's rows of a key range), which keeps
+// the number of concurrent DRAM streams per key range at two (K, V). A
+// workgroup runs one work item, or with a balanced plan the items of its
+// bin (a contiguous share of all sequences' keys) one after the other.
+template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES, int HW>
+__global__ __launch_bounds__(64 * HW) void gqa_decode_kernel(GqaParams p) {
+  const int lane = threadIdx.x & 63;
+  const int g = blockIdx.y * HW + (threadIdx.x >> 6);
+  if (g >= p.h_k) return;
+  int it = blockIdx.x, it_end = blockIdx.x + 1;
+  if (p.bin_offsets) {
+    it = p.bin_offsets[blockIdx.x];
+    it_end = p.bin_offsets[blockIdx.x + 1];
+  }
+  for (; it < it_end; ++it) gqa_decode_item<FP8Q, NB, CAUSAL_TAIL, STAGES>(p, it, lane, g);
+}
+
 template <bool FP8Q, int NB, bool CT, int ST, int HW>
 const void* kernel_ptr() {
   return reinterpret_cast<const void*>(&gqa_decode_kernel<FP8Q, NB, CT, ST, HW>);
@@ -596,6 +610,7 @@ hipError_t gqa_launch(const pkv_decode_args& a, const GqaVariant& v, hipStream_t
   p.ws_o = static_cast<float*>(a.workspace);
   p.ws_ml = a.workspace ? reinterpret_cast<float2*>(p.ws_o + (int64_t)a.max_splits * rows_all * kD) : nullptr;
   p.counters = a.max_splits > 1 ? a.merge_counters : nullptr;
+  p.bin_offsets = a.bin_offsets;
   p.scale_log2e = (float)((double)a.softmax_scale * 1.4426950408889634);
   p.scale = a.softmax_scale;
   p.o_scale = a.o_scale;
@@ -610,7 +625,7 @@ hipError_t gqa_launch(const pkv_decode_args& a, const GqaVariant& v, hipStream_t
   p.max_splits = a.max_splits;
   const int tiles = (p.rows + gqa_rows_per_tile(v) - 1) / gqa_rows_per_tile(v);
   const int hw = v.heads_per_wg;
-  dim3 grid(a.num_work, (a.h_k + hw - 1) / hw, tiles);
+  dim3 grid(a.bin_offsets ? a.num_bins : a.num_work, (a.h_k + hw - 1) / hw, tiles);
   void* args[] = {&p};
   return hipLaunchKernel(select_kernel(v), grid, dim3(64 * hw), args, 0, stream);
 }

@@ -73,6 +73,7 @@ struct MlaParams {
   const int32_t* n_splits;
   float* ws_o;    // [max_splits][num_seqs][rows][512]
   float2* ws_ml;  // [max_splits][num_seqs][rows]
+  const int32_t* bin_offsets;  // [bins + 1] or null: one work item per workgroup
   float scale_log2e, scale, o_scale;
   int num_seqs, q_len, h_q, rows, page_shift, num_pages, max_blocks, max_splits;
 };
@@ -112,15 +113,13 @@ struct RawRec {
   uint2 v[4][4];   // key kb + 4 g4 + i, latent bytes 128 gr + 8 r16 .. +7
 };
 
+// One work item (sequence chunk) for this wave's 16 query rows.
 template <bool CAUSAL_TAIL>
-__global__ __launch_bounds__(64 * kMaxWaves) void mla_decode_kernel(MlaParams p) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void mla_decode_item(const MlaParams& p, int item, int lane, int row0) {
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
-  const int row_block = blockIdx.y * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const int row0 = 16 * row_block;
 
-  const int4 w = p.work[blockIdx.x];
+  const int4 w = p.work[item];
   const int b = w.x;
   if (w.z <= w.y || b < 0 || b >= p.num_seqs) return;
   const int ns = p.n_splits[b];
@@ -330,6 +329,20 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mla_decode_kernel(MlaParams p)
   }
 }
 
+// One wave per 16 query rows; a workgroup runs one work item, or with a
+// balanced plan the items of its bin one after the other.
+template <bool CAUSAL_TAIL>
+__global__ __launch_bounds__(64 * kMaxWaves) void mla_decode_kernel(MlaParams p) {
+  const int lane = threadIdx.x & 63;
+  const int row0 = 16 * (blockIdx.y * (blockDim.x >> 6) + (threadIdx.x >> 6));
+  int it = blockIdx.x, it_end = blockIdx.x + 1;
+  if (p.bin_offsets) {
+    it = p.bin_offsets[blockIdx.x];
+    it_end = p.bin_offsets[blockIdx.x + 1];
+  }
+  for (; it < it_end; ++it) mla_decode_item<CAUSAL_TAIL>(p, it, lane, row0);
+}
+
 const void* select_kernel(bool causal_tail) {
   return causal_tail ? reinterpret_cast<const void*>(&mla_decode_kernel<true>)
                      : reinterpret_cast<const void*>(&mla_decode_kernel<false>);
@@ -383,6 +396,7 @@ hipError_t mla_launch(const pkv_decode_args& a, hipStream_t stream) {
   const int64_t rows_all = ws_rows(a);
   p.ws_o = static_cast<float*>(a.workspace);
   p.ws_ml = a.workspace ? reinterpret_cast<float2*>(p.ws_o + (int64_t)a.max_splits * rows_all * kDv) : nullptr;
+  p.bin_offsets = a.bin_offsets;
   p.scale_log2e = (float)((double)a.softmax_scale * 1.4426950408889634);
   p.scale = a.softmax_scale;
   p.o_scale = a.o_scale;
@@ -396,7 +410,7 @@ hipError_t mla_launch(const pkv_decode_args& a, hipStream_t stream) {
   p.max_splits = a.max_splits;
   const int wpw = waves_per_wg(a);
   const int tiles = (p.rows + 16 * wpw - 1) / (16 * wpw);
-  dim3 grid(a.num_work, tiles, 1);
+  dim3 grid(a.bin_offsets ? a.num_bins : a.num_work, tiles, 1);
   void* args[] = {&p};
   return hipLaunchKernel(select_kernel(a.causal && a.q_len > 1), grid, dim3(64 * wpw), args,
                          (size_t)wpw * kQSteps * 64 * 16, stream);

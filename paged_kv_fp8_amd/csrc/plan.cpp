@@ -106,6 +106,83 @@ extern "C" pkv_status pkv_plan_split_kv(const int32_t* seq_lens, int32_t num_seq
     info->chunk_tiles = (int32_t)chunk;
     info->slots = (int32_t)std::min<int64_t>(slots, INT32_MAX);
     info->max_n_splits = max_ns;
+    info->num_bins = 0;
+  }
+  return PKV_OK;
+}
+
+// Balanced contiguous plan (this library's own; see pkv_fp8.h): tiles of all
+// sequences end to end, cut into `bins` equal contiguous shares.
+extern "C" pkv_status pkv_plan_balanced(const int32_t* seq_lens, int32_t num_seqs, int32_t h_k, int32_t n_q_tiles,
+                                        int32_t cu_count, int32_t wg_per_cu, int32_t max_splits, int32_t* work_out,
+                                        int32_t work_cap, int32_t* n_splits_out, int32_t* bin_offsets_out,
+                                        int32_t bins_cap, pkv_plan_info* info) {
+  using pkv::fail;
+  if (!seq_lens || !work_out || !n_splits_out || !bin_offsets_out)
+    return fail(PKV_ERR_INVALID_ARG, "plan: NULL array");
+  if (num_seqs < 1) return fail(PKV_ERR_INVALID_ARG, "plan: num_seqs=%d < 1", num_seqs);
+  if (h_k < 1 || n_q_tiles < 1 || cu_count < 1 || wg_per_cu < 1 || max_splits < 1)
+    return fail(PKV_ERR_INVALID_ARG, "plan: sizes must be >= 1");
+  if (work_cap < 0 || bins_cap < 0) return fail(PKV_ERR_INVALID_ARG, "plan: capacities must be >= 0");
+  if (max_splits > PKV_MAX_SPLITS)
+    return fail(PKV_ERR_UNSUPPORTED, "plan: max_splits=%d > %d", max_splits, PKV_MAX_SPLITS);
+  std::vector<int64_t> start(num_seqs + 1, 0);
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    if (seq_lens[b] < 0) return fail(PKV_ERR_INVALID_ARG, "plan: seq_lens[%d]=%d < 0", b, seq_lens[b]);
+    start[b + 1] = start[b] + std::max<int64_t>(1, ceil_div(seq_lens[b], kTileKeys));
+  }
+  const int64_t total = start[num_seqs];
+  int64_t bins = ((int64_t)cu_count * wg_per_cu) / ((int64_t)h_k * n_q_tiles);
+  bins = std::max<int64_t>(1, std::min(bins, total));
+  // share i covers global tiles [i*total/bins, (i+1)*total/bins); the share
+  // holding tile x is the last i with i*total/bins <= x
+  auto share_of = [&](int64_t x, int64_t nb) {
+    int64_t i = ((x + 1) * nb + total - 1) / total - 1;  // largest i with floor(i*total/nb) <= x
+    while (i + 1 < nb && ((i + 1) * total) / nb <= x) ++i;
+    while (i > 0 && (i * total) / nb > x) --i;
+    return i;
+  };
+  auto max_pieces = [&](int64_t nb) {
+    int64_t m = 0;
+    for (int32_t b = 0; b < num_seqs; ++b) m = std::max(m, share_of(start[b + 1] - 1, nb) - share_of(start[b], nb) + 1);
+    return m;
+  };
+  while (bins > 1 && max_pieces(bins) > max_splits) --bins;
+  if (max_pieces(bins) > max_splits)
+    return fail(PKV_ERR_UNSUPPORTED, "plan: a sequence needs more than max_splits=%d pieces", max_splits);
+  if (bins + 1 > bins_cap) return fail(PKV_ERR_CAPACITY, "plan: %lld bins > bins_cap - 1", (long long)bins);
+
+  std::vector<int32_t> seen(num_seqs, 0);
+  int64_t n = 0;
+  int32_t b = 0;
+  bin_offsets_out[0] = 0;
+  for (int64_t i = 0; i < bins; ++i) {
+    const int64_t lo = (i * total) / bins, hi = ((i + 1) * total) / bins;
+    while (b < num_seqs && start[b + 1] <= lo) ++b;
+    for (int32_t c = b; c < num_seqs && start[c] < hi; ++c) {
+      const int64_t s0 = std::max(lo, start[c]), e0 = std::min(hi, start[c + 1]);
+      if (s0 >= e0) continue;
+      if (n >= work_cap) return fail(PKV_ERR_CAPACITY, "plan: work items exceed work_cap=%d", work_cap);
+      work_out[4 * n + 0] = c;
+      work_out[4 * n + 1] = (int32_t)(s0 - start[c]);
+      work_out[4 * n + 2] = (int32_t)(e0 - start[c]);
+      work_out[4 * n + 3] = seen[c]++;
+      ++n;
+    }
+    bin_offsets_out[i + 1] = (int32_t)n;
+  }
+  int32_t max_ns = 0;
+  for (int32_t c = 0; c < num_seqs; ++c) {
+    n_splits_out[c] = seen[c];
+    max_ns = std::max(max_ns, seen[c]);
+  }
+  if (info) {
+    info->num_work = (int32_t)n;
+    info->num_real = (int32_t)n;
+    info->chunk_tiles = (int32_t)ceil_div(total, bins);
+    info->slots = (int32_t)bins;
+    info->max_n_splits = max_ns;
+    info->num_bins = (int32_t)bins;
   }
   return PKV_OK;
 }

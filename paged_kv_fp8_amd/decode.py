@@ -49,7 +49,7 @@ class PagedDecode:
     def __init__(self, *, q, block_table, seq_lens, o, lse, q_len, softmax_scale, k_cache=None, v_cache=None,
                  q_descale=None, k_descale=None, v_descale=None, latent=None, rope=None, blk_scale=None,
                  num_pages=None, causal=True, o_scale=1.0, max_splits=16, force_splits=0, min_chunk_tiles=1,
-                 pad_to=0, wg_per_cu=None, plan_seq_lens=None, fused_merge=False):
+                 pad_to=0, wg_per_cu=None, plan_seq_lens=None, fused_merge=False, plan="wave"):
         mla = latent is not None
         a = native.DecodeArgs()
         num_seqs = seq_lens.shape[0]
@@ -95,9 +95,17 @@ class PagedDecode:
         cu, wg, n_q_tiles = native.decode_slots(a)
         self.cu_count, self.wg_per_cu, self.n_q_tiles = cu, wg_per_cu or wg, n_q_tiles
         lens = seq_lens.cpu().numpy() if plan_seq_lens is None else np.asarray(plan_seq_lens)
-        work, n_splits, info = native.plan_split_kv(lens, h_k, n_q_tiles, cu, self.wg_per_cu, max_splits,
-                                                    force_splits, min_chunk_tiles, pad_to)
         dev = q.device
+        self.bin_offsets = None
+        if plan == "balanced":  # contiguous equal shares, one per resident workgroup
+            work, n_splits, offs, info = native.plan_balanced(lens, h_k, n_q_tiles, cu, self.wg_per_cu, max_splits)
+            self.bin_offsets = torch.from_numpy(offs).to(dev)
+            a.bin_offsets, a.num_bins = _ptr(self.bin_offsets), int(info.num_bins)
+        elif plan == "wave":  # the occupancy-pinned one-wave plan
+            work, n_splits, info = native.plan_split_kv(lens, h_k, n_q_tiles, cu, self.wg_per_cu, max_splits,
+                                                        force_splits, min_chunk_tiles, pad_to)
+        else:
+            raise ValueError(f"unknown plan {plan!r}")
         self.work = torch.from_numpy(work).to(dev)
         self.n_splits = torch.from_numpy(n_splits).to(dev)
         self.plan_info = info
@@ -119,6 +127,7 @@ class PagedDecode:
         # keep every bound tensor alive as long as the raw pointers are
         self._keep = (q, k_cache, v_cache, q_descale, k_descale, v_descale, latent, rope, blk_scale, block_table,
                       seq_lens, o, lse)
+        self.plan = plan
 
     @property
     def has_splits(self):

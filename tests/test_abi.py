@@ -10,6 +10,7 @@ import re
 import numpy as np
 import pytest
 
+from oracle.plan import plan_balanced as oracle_balanced
 from oracle.plan import plan_split_kv as oracle_plan
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -174,3 +175,18 @@ def test_workspace_bytes_formula(native):
     floats = 16 * 64 * 8 * 4 * (128 + 2)
     assert n == (floats * 4 + 255) // 256 * 256
     assert native.workspace_bytes(0, 8, 4, 128, 16) == 0
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_library_balanced_planner_equals_oracle(native, seed):
+    rng = np.random.default_rng(3000 + seed)
+    b = int(rng.integers(1, 130))
+    lens = np.where(rng.random(b) < 0.15, rng.integers(8192, 70000, size=b), rng.integers(0, 5000, size=b))
+    kw = dict(h_k=int(rng.choice([1, 2, 4, 8])), n_q_tiles=int(rng.integers(1, 3)), cu_count=256,
+              wg_per_cu=int(rng.integers(1, 9)), max_splits=int(rng.choice([2, 8, 16, 64, 256])))
+    work, ns, offs, bins = oracle_balanced(lens.tolist(), **kw)
+    w2, ns2, offs2, info = native.plan_balanced(lens, kw["h_k"], kw["n_q_tiles"], kw["cu_count"], kw["wg_per_cu"],
+                                                kw["max_splits"])
+    assert w2.tolist() == [list(x) for x in work]
+    assert ns2.tolist() == ns and offs2.tolist() == offs
+    assert (info.num_bins, info.num_work, info.max_n_splits) == (bins, len(work), max(ns))

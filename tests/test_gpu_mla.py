@@ -80,3 +80,11 @@ def test_latent_repeat_bitwise():
         torch.cuda.synchronize()
         assert torch.equal(dec.o.view(torch.int16), o1.view(torch.int16))
         assert torch.equal(dec.lse.view(torch.int32), l1.view(torch.int32))
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_latent_balanced_plan(T):
+    w = workload(5, q_len=T, num_seqs=6, seq_len_dist=("uniform", 100, 4000))
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch, plan="balanced")
+    compare(batch, dec, what=f"latent balanced T={T}")

@@ -303,3 +303,68 @@ def test_fused_merge_graph_replay():
         assert torch.equal(dec.o.view(torch.int16), eager_o.view(torch.int16)), f"replay {rep}"
         assert torch.equal(dec.lse.view(torch.int32), eager_l.view(torch.int32)), f"replay {rep}"
     assert int(dec.merge_counters.abs().sum()) == 0
+
+
+# ---------------------------------------------------------------------------
+# balanced contiguous plan: workgroups walk the items of their share
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", list(SMALL))
+def test_balanced_plan_small_workloads(name):
+    kw = dict(SMALL[name])
+    w = workload(kw.pop("index"), **kw)
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch, plan="balanced")
+    assert dec.plan_info.num_bins >= 1
+    compare(batch, dec, what=f"balanced {name}")
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_balanced_plan_full_workloads_sampled(name):
+    idx, over = FULL[name]
+    w = workload(idx, **over)
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch, plan="balanced")
+    lens = batch.seq_lens.cpu().numpy()
+    seqs = _sample(lens, np.random.default_rng(idx + 50))
+    err_o, err_l, _ = compare(batch, dec, seqs=seqs, what=f"balanced {name}")
+    print(f"balanced {name}: bins={dec.plan_info.num_bins} items={dec.plan_info.num_work} "
+          f"max_splits_used={dec.plan_info.max_n_splits} max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
+
+
+@pytest.mark.parametrize("q_format,q_len,causal,ps", [("bf16", 1, True, 16), ("bf16", 4, True, 64),
+                                                      ("e4m3", 2, False, 128)])
+def test_balanced_plan_edge_lengths(q_format, q_len, causal, ps):
+    idx = 4 if q_format == "e4m3" else 2
+    h_q, h_k = (64, 4) if q_format == "e4m3" else (16, 2)
+    w = workload(idx, num_seqs=len(EDGE_LENS), q_len=q_len, h_q=h_q, h_k=h_k, page_size=ps, causal=causal,
+                 seq_len_dist=("fixed", EDGE_LENS), max_splits=8)
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch, plan="balanced", wg_per_cu=1)  # few bins: several items per workgroup
+    tol = FP8_SHORT_TOL if q_format == "e4m3" else O_TOL
+    compare(batch, dec, o_tol=tol, what=f"balanced edge {q_format} q_len={q_len}")
+
+
+def test_balanced_plan_fused_merge_and_graph():
+    w = workload(2, num_seqs=8, seq_len_dist=("uniform", 300, 6000))
+    batch = make_batch(w, device="cuda")
+    ref = run_batch(batch)
+    ref_o, ref_l = ref.o.clone(), ref.lse.clone()
+    dec = _decode().for_batch(batch, plan="balanced", fused_merge=True)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        dec.run(stream)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    compare(batch, dec, what="balanced + fused merge")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dec.run()
+    eager_o = dec.o.clone()
+    for rep in range(3):
+        dec.o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dec.o.view(torch.int16), eager_o.view(torch.int16)), f"replay {rep}"
+    assert int(dec.merge_counters.abs().sum()) == 0

@@ -100,3 +100,53 @@ def test_random_plans_invariants_and_minimal_chunk(seed):
         scan = next(c for c in range(lo, max(max(tiles), lo) + 1)
                     if sum(math.ceil(t / c) for t in tiles) <= slots)
         assert chunk == scan
+
+
+# ---------------------------------------------------------------------------
+# balanced contiguous plan (the build's own planner)
+# ---------------------------------------------------------------------------
+from oracle.plan import plan_balanced  # noqa: E402
+
+
+def test_balanced_hand_worked():
+    # tiles [3, 8, 2, 1], 14 in total, starting at 0, 3, 11, 13; slots = 5*2 // 2 = 5 bins,
+    # cut at 14*i // 5 = 0, 2, 5, 8, 11, 14
+    work, ns, off, bins = plan_balanced([300, 1000, 129, 50], h_k=2, n_q_tiles=1, cu_count=5, wg_per_cu=2)
+    assert bins == 5
+    assert work == [(0, 0, 2, 0),                  # bin 0: global [0, 2)
+                    (0, 2, 3, 1), (1, 0, 2, 0),    # bin 1: [2, 5)
+                    (1, 2, 5, 1),                  # bin 2: [5, 8)
+                    (1, 5, 8, 2),                  # bin 3: [8, 11)
+                    (2, 0, 2, 0), (3, 0, 1, 0)]    # bin 4: [11, 14)
+    assert off == [0, 1, 3, 4, 5, 7] and ns == [2, 3, 1, 1]
+
+
+def test_balanced_lowers_bins_for_max_splits():
+    # one sequence of 64 tiles over 32 bins would be 32 pieces; max_splits 8 -> 8 bins
+    work, ns, off, bins = plan_balanced([64 * 128], h_k=1, n_q_tiles=1, cu_count=32, max_splits=8)
+    assert bins == 8 and ns == [8]
+    assert [w[2] - w[1] for w in work] == [8] * 8
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_balanced_invariants(seed):
+    rng = np.random.default_rng(5000 + seed)
+    b = int(rng.integers(1, 100))
+    lens = rng.integers(0, 70000, size=b).tolist()
+    kw = dict(h_k=int(rng.choice([1, 2, 4, 8])), n_q_tiles=int(rng.integers(1, 3)), cu_count=256,
+              wg_per_cu=int(rng.integers(1, 9)), max_splits=int(rng.choice([4, 16, 64, 256])))
+    work, ns, off, bins = plan_balanced(lens, **kw)
+    tiles = [max(1, math.ceil(L / 128)) for L in lens]
+    total = sum(tiles)
+    assert len(off) == bins + 1 and off[0] == 0 and off[-1] == len(work)
+    # every bin holds floor or ceil of total / bins tiles, contiguous in sequence order
+    loads = [sum(w[2] - w[1] for w in work[off[i]:off[i + 1]]) for i in range(bins)]
+    assert sum(loads) == total and max(loads) - min(loads) <= 1
+    flat = [(w[0], t) for w in work for t in range(w[1], w[2])]
+    assert flat == [(s, t) for s in range(len(tiles)) for t in range(tiles[s])]
+    # split slots count up per sequence; n_splits matches; within the cap
+    for s in range(len(tiles)):
+        items = [w for w in work if w[0] == s]
+        assert [w[3] for w in items] == list(range(len(items))) and ns[s] == len(items)
+    assert max(ns) <= kw["max_splits"]
+    assert bins <= max(1, 256 * kw["wg_per_cu"] // (kw["h_k"] * kw["n_q_tiles"]))
