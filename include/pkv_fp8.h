@@ -126,16 +126,18 @@ pkv_status pkv_plan_split_kv(const int32_t* seq_lens, int32_t num_seqs, int32_t 
 
 /*
  * Balanced contiguous plan (this library's own planner; not from the pages).
- * The 128-key tiles of all sequences, laid end to end in sequence order, are
- * cut into `bins` contiguous shares of floor or ceil(total / bins) tiles,
- * bins = max(1, min(total, cu_count * wg_per_cu / (h_k * n_q_tiles))) -- the
- * workgroups that run at once -- lowered until no sequence is cut into more
- * than max_splits pieces. Every overlap of a share and a sequence is a work
- * item (seq, tile_begin, tile_end, split_slot), split slots numbered in key
- * order; items are listed bin by bin and bin i owns items
- * [bin_offsets[i], bin_offsets[i+1]). Each workgroup then carries the same
- * number of keys (to one tile), whatever the length mix, and sequences are
- * split only at share boundaries.
+ * The 32-key blocks of all sequences (max(1, ceil(L / 32)) each), laid end to
+ * end in sequence order, are cut into `bins` contiguous shares of floor or
+ * ceil(total / bins) blocks, bins = max(1, min(total, cu_count * wg_per_cu /
+ * (h_k * n_q_tiles))) -- the workgroups that run at once -- lowered until no
+ * sequence is cut into more than max_splits pieces. Every overlap of a share
+ * and a sequence is a work item (seq, key_begin, key_end, split_slot) in KEYS
+ * (not tiles): key_begin = 32 * its first block, key_end = min(32 * its end
+ * block, L); split slots are numbered in key order. Items are listed bin by
+ * bin and bin i owns items [bin_offsets[i], bin_offsets[i+1]). Each workgroup
+ * then carries the same number of 32-key blocks (to one), whatever the length
+ * mix; the decode streams a bin's items back to back through one load
+ * pipeline.
  *
  * seq_lens        host int32[num_seqs], each >= 0
  * work_out        host int32[work_cap][4]; at most bins + num_seqs - 1 items
@@ -234,9 +236,11 @@ typedef struct pkv_decode_args {
    * left for pkv_merge_splits. Calls that overlap on one counter array race. */
   int32_t* merge_counters;
   /* Optional, device int32[num_bins + 1] from pkv_plan_balanced: workgroup i
-   * runs work items [bin_offsets[i], bin_offsets[i+1]) in order, and the
-   * grid has num_bins workgroups per (kv-head group, q-row tile). NULL: one
-   * work item per workgroup, num_work workgroups (pkv_plan_split_kv). */
+   * streams work items [bin_offsets[i], bin_offsets[i+1]) in order, the grid
+   * has num_bins workgroups per (kv-head group, q-row tile), and `work` holds
+   * KEY ranges (key_begin a multiple of 32), as pkv_plan_balanced writes
+   * them. NULL: one work item per workgroup, num_work workgroups, and `work`
+   * holds 128-key TILE ranges (pkv_plan_split_kv). */
   const int32_t* bin_offsets;
   int32_t num_bins;
 } pkv_decode_args;

@@ -89,16 +89,21 @@ def plan_split_kv(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16
     return work, n_splits, chunk, slots
 
 
+BALANCE_BLOCK_KEYS = 32
+
+
 def plan_balanced(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16):
     """Balanced contiguous plan (this build's own planner, not the pages'):
-    the 128-key tiles of all sequences, laid end to end in sequence order,
-    are cut into `bins` contiguous shares of floor/ceil(total / bins) tiles,
-    bins = the workgroups that run at once (the ``slots`` of the rule above).
-    Bin i takes global tiles [floor(i * total / bins), floor((i+1) * total /
-    bins)); every (sequence, share) overlap is a work item, split slots
-    numbered in key order. If some sequence would be cut into more than
-    max_splits pieces, bins is lowered until none is. Returns (work ordered
-    by bin, n_splits, bin_offsets[bins + 1], bins).
+    the 32-key blocks of all sequences (max(1, ceil(L / 32)) each), laid end
+    to end in sequence order, are cut into `bins` contiguous shares of
+    floor/ceil(total / bins) blocks, bins = the workgroups that run at once
+    (the ``slots`` of the rule above). Bin i takes global blocks
+    [floor(i * total / bins), floor((i+1) * total / bins)); every (sequence,
+    share) overlap is a work item (seq, key_begin, key_end, slot) in keys:
+    key_begin = 32 * its first block, key_end = min(32 * its end block, L),
+    split slots numbered in key order. If some sequence would be cut into more
+    than max_splits pieces, bins is lowered until none is. Returns (work
+    ordered by bin, n_splits, bin_offsets[bins + 1], bins).
     """
     seq_lens = [int(x) for x in seq_lens]
     if not seq_lens:
@@ -107,19 +112,19 @@ def plan_balanced(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16
         raise ValueError("negative sequence length")
     if min(h_k, n_q_tiles, cu_count, wg_per_cu, max_splits) < 1:
         raise ValueError("sizes must be positive")
-    tiles = [max(1, _ceil_div(L, TILE_KEYS)) for L in seq_lens]
-    total = sum(tiles)
+    blocks = [max(1, _ceil_div(L, BALANCE_BLOCK_KEYS)) for L in seq_lens]
+    total = sum(blocks)
     starts = [0]
-    for t in tiles:
+    for t in blocks:
         starts.append(starts[-1] + t)
     bins = max(1, min(total, (cu_count * wg_per_cu) // (h_k * n_q_tiles)))
 
     def pieces_for(nb):
-        """Shares that overlap each sequence when `total` tiles are cut into nb."""
+        """Shares that overlap each sequence when `total` blocks are cut into nb."""
         bounds = [(i * total) // nb for i in range(nb + 1)]
-        # share holding global tile x: the last i with bounds[i] <= x
+        # share holding global block x: the last i with bounds[i] <= x
         share = lambda x: bisect.bisect_right(bounds, x) - 1  # noqa: E731
-        return [share(starts[b + 1] - 1) - share(starts[b]) + 1 for b in range(len(tiles))], bounds
+        return [share(starts[b + 1] - 1) - share(starts[b]) + 1 for b in range(len(blocks))], bounds
 
     while True:
         pieces, bounds = pieces_for(bins)
@@ -128,15 +133,13 @@ def plan_balanced(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16
         bins -= 1
     if max(pieces) > max_splits:
         raise ValueError(f"{max(pieces)} chunks exceed max_splits={max_splits}")
-    per_bin = []
+    work, offsets, seen = [], [0], [0] * len(blocks)
     for i in range(bins):
         lo, hi = bounds[i], bounds[i + 1]
-        per_bin.append([(b, max(lo, starts[b]) - starts[b], min(hi, starts[b + 1]) - starts[b])
-                        for b in range(len(tiles)) if max(lo, starts[b]) < min(hi, starts[b + 1])])
-    work, offsets, seen = [], [0], [0] * len(tiles)
-    for items in per_bin:
-        for b, tb, te in items:
-            work.append((b, tb, te, seen[b]))
-            seen[b] += 1
+        for b in range(len(blocks)):
+            first, end = max(lo, starts[b]) - starts[b], min(hi, starts[b + 1]) - starts[b]
+            if first < end:
+                work.append((b, BALANCE_BLOCK_KEYS * first, min(BALANCE_BLOCK_KEYS * end, seq_lens[b]), seen[b]))
+                seen[b] += 1
         offsets.append(len(work))
     return work, pieces, offsets, bins

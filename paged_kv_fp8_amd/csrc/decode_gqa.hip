@@ -58,6 +58,7 @@ constexpr int kTileKeys = 128;   // planner tile
 constexpr int kBlockKeys = 32;   // keys per main-loop step
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kP8Scale = 448.0f;  // fp8 P is stored as e4m3(p * 448)
+constexpr float kLazyLog2 = 8.0f;   // bf16 P: reference max may lag until p would exceed 2^8
 
 struct GqaParams {
   const uint8_t* q;   // byte address
@@ -179,270 +180,251 @@ struct RawBlock {
   uint2 v[8];     // key kb+16*(j>>2)+4*g4+(j&3), bytes 8*r16 .. 8*r16+7
 };
 
-// One work item (sequence chunk) for kv head g: the body of the decode.
-template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES>
-__device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, int lane, int g) {
-  const int r16 = lane & 15;
-  const int g4 = lane >> 4;
-
-  const int4 w = p.work[item];
-  const int b = w.x;
-  if (w.z <= w.y || b < 0 || b >= p.num_seqs) return;  // padding item / bad entry
-  const int ns = p.n_splits[b];
-  const bool direct = ns <= 1;
-  const int slot = w.w;
-  if (!direct && (slot < 0 || slot >= p.max_splits)) return;
-  const int row0 = blockIdx.z * (16 * NB);
-
-  const int page_size = 1 << p.page_shift;
-  int L = p.seq_lens[b];
-  L = max(0, min(L, p.max_blocks * page_size));
-  const int k_begin = w.y * kTileKeys;
-  const int k_end = min(w.z * kTileKeys, L);
-
-  // ---- query rows of this wave --------------------------------------------
-  int lim[NB];
-  bool row_ok[NB];
-  int qtok[NB], qhead[NB];
-  for (int nb = 0; nb < NB; ++nb) {
-    const int n = row0 + 16 * nb + r16;
-    row_ok[nb] = n < p.rows;
-    const int qi = n / p.h_r;
-    qtok[nb] = b * p.q_len + qi;
-    qhead[nb] = g * p.h_r + (n - qi * p.h_r);
-    // last key this row may see inside this work item's chunk
-    lim[nb] = min(CAUSAL_TAIL ? L - p.q_len + qi : L - 1, k_end - 1);
-  }
-  const int lim_min = min(CAUSAL_TAIL ? L - p.q_len : L - 1, k_end - 1);
-
-  const float qd = FP8Q ? p.qd[b * p.qd_seq + g * p.qd_head] : 1.0f;
-  const float kdv = p.kd[b * p.kd_seq + g * p.kd_head];
-  const float vdv = p.vd[b * p.vd_seq + g * p.vd_head];
-  const float c2 = p.scale_log2e * qd * kdv;  // exponent scale (base 2) on raw scores
-  const float cs = p.scale * qd * kdv;        // natural-log scale of the running max
-
-  // B operand of QK^T: lane (n = r16, g4), k-step s holds q[n][64*(s>>1) + 16*g4 + 8*(s&1) + 0..7]
+// B operand of QK^T: lane (n = r16, g4), k-step s holds
+// q[n][64*(s>>1) + 16*g4 + 8*(s&1) + 0..7] (bf16 rows, or e4m3 codes).
+template <int NB>
+struct QOperand {
   bf16x8 qb[NB][4];
   long q8[NB][4];
+};
+
+// Running softmax state of a wave's query rows: lane (r16, g4) holds
+// O^T[d_v = 32*g4 + 8*i + mt][row r16] in oacc[nb][mt][i], the row's running
+// max (raw-score units) and its lane-partial sum of probabilities.
+template <int NB>
+struct RowState {
+  f32x4 oacc[NB][8];
+  float m_run[NB], l_part[NB];
+};
+
+template <int NB>
+__device__ __forceinline__ void reset_rows(RowState<NB>& st) {
   for (int nb = 0; nb < NB; ++nb) {
-    const uint8_t* qrow = p.q + (int64_t)qtok[nb] * p.q_tok + (int64_t)qhead[nb] * p.q_head;
+    for (int mt = 0; mt < 8; ++mt) st.oacc[nb][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.m_run[nb] = -INFINITY;
+    st.l_part[nb] = 0.f;
+  }
+}
+
+// Query rows of this wave: packed row n = row0 + 16*nb + r16 is query token
+// qi = n / h_r of sequence b, query head g*h_r + n % h_r.
+template <int NB>
+struct RowMap {
+  bool ok[NB];
+  int qi[NB], hr[NB];
+};
+
+template <int NB>
+__device__ __forceinline__ RowMap<NB> row_map(const GqaParams& p, int row0, int r16) {
+  RowMap<NB> m;
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = row0 + 16 * nb + r16;
+    m.ok[nb] = n < p.rows;
+    m.qi[nb] = n / p.h_r;
+    m.hr[nb] = n - m.qi[nb] * p.h_r;
+  }
+  return m;
+}
+
+template <bool FP8Q, int NB>
+__device__ __forceinline__ void load_q(const GqaParams& p, QOperand<NB>& q, const RowMap<NB>& rm, int b, int g,
+                                       int g4) {
+  for (int nb = 0; nb < NB; ++nb) {
+    const uint8_t* qrow =
+        p.q + (int64_t)(b * p.q_len + rm.qi[nb]) * p.q_tok + (int64_t)(g * p.h_r + rm.hr[nb]) * p.q_head;
     for (int s = 0; s < 4; ++s) {
       const int d = 64 * (s >> 1) + 16 * g4 + 8 * (s & 1);
       if (FP8Q) {
-        q8[nb][s] = row_ok[nb] ? *reinterpret_cast<const long*>(qrow + d) : 0;
+        q.q8[nb][s] = rm.ok[nb] ? *reinterpret_cast<const long*>(qrow + d) : 0;
       } else {
-        if (row_ok[nb]) {
-          qb[nb][s] = *reinterpret_cast<const bf16x8*>(qrow + 2 * d);
+        if (rm.ok[nb]) {
+          q.qb[nb][s] = *reinterpret_cast<const bf16x8*>(qrow + 2 * d);
         } else {
-          for (int e = 0; e < 8; ++e) qb[nb][s][e] = (__bf16)0.0f;
+          for (int e = 0; e < 8; ++e) q.qb[nb][s][e] = (__bf16)0.0f;
         }
       }
     }
   }
+}
 
-  f32x4 oacc[NB][8];
-  float m_run[NB], l_part[NB];
-  for (int nb = 0; nb < NB; ++nb) {
-    for (int mt = 0; mt < 8; ++mt) oacc[nb][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m_run[nb] = -INFINITY;
-    l_part[nb] = 0.f;
+// The 13 loads of one 32-key block (keys kb.. clamped to last_key) of kv
+// head g from the two pages pg0 (keys kb..kb+15) and pg1 (kb+16..kb+31).
+__device__ __forceinline__ RawBlock load_block(const GqaParams& p, int g, int kb, int pg0, int pg1, int last_key,
+                                               int pmask, int r16, int g4) {
+  // Page bases are wave-uniform (scalar registers); lanes add a 32-bit
+  // offset inside the page (page_size * row stride < 2^30, checked by the
+  // library), which the global loads take in their scalar-base form.
+  RawBlock r;
+  const uint8_t* kbase0 = p.k + (int64_t)pg0 * p.k_page + (int64_t)g * p.k_head;
+  const uint8_t* kbase1 = p.k + (int64_t)pg1 * p.k_page + (int64_t)g * p.k_head;
+  const uint8_t* vbase0 = p.v + (int64_t)pg0 * p.v_page + (int64_t)g * p.v_head;
+  const uint8_t* vbase1 = p.v + (int64_t)pg1 * p.v_page + (int64_t)g * p.v_head;
+  const uint32_t k_row = (uint32_t)p.k_row, v_row = (uint32_t)p.v_row;
+  for (int t = 0; t < 2; ++t) {
+    const uint32_t row = (uint32_t)(min(kb + 16 * t + r16, last_key) & pmask);
+    const uint32_t off = row * k_row + 16u * (uint32_t)g4;
+    r.k[t][0] = *reinterpret_cast<const uint4*>((t ? kbase1 : kbase0) + off);
+    r.k[t][1] = *reinterpret_cast<const uint4*>((t ? kbase1 : kbase0) + (off + 64u));
   }
+  for (int j = 0; j < 8; ++j) {
+    const int t = j >> 2;
+    const uint32_t row = (uint32_t)(min(kb + 16 * t + 4 * g4 + (j & 3), last_key) & pmask);
+    r.v[j] = *reinterpret_cast<const uint2*>((t ? vbase1 : vbase0) + (row * v_row + 8u * (uint32_t)r16));
+  }
+  return r;
+}
 
-  if (k_end > k_begin) {
-    const int32_t* bt = p.block_table + (int64_t)b * p.bt_row;
-    const int last_key = k_end - 1;  // loads never go past the chunk (and so never past L)
-    // Pages of one 32-key block (page_size >= 16, so each 16-key group lies
-    // in one page): lane l loads the entry of group l & 1, so lanes 0 and 1
-    // hold the block's two pages. A vector load, so waiting for it (in
-    // order) never waits for the KV loads issued after it.
-    auto page_pair = [&](int kb) -> int { return bt[min(kb + 16 * (lane & 1), last_key) >> p.page_shift]; };
-    auto clamp_page = [&](int pg) -> int { return min(max(pg, 0), p.num_pages - 1); };
-    auto load_block = [&](int kb, int pg0, int pg1) {
-      RawBlock r;
-      const uint8_t* kbase0 = p.k + (int64_t)pg0 * p.k_page + (int64_t)g * p.k_head;
-      const uint8_t* kbase1 = p.k + (int64_t)pg1 * p.k_page + (int64_t)g * p.k_head;
-      const uint8_t* vbase0 = p.v + (int64_t)pg0 * p.v_page + (int64_t)g * p.v_head;
-      const uint8_t* vbase1 = p.v + (int64_t)pg1 * p.v_page + (int64_t)g * p.v_head;
-      const int pmask = page_size - 1;
-      for (int t = 0; t < 2; ++t) {
-        const int row = min(kb + 16 * t + r16, last_key) & pmask;
-        const uint8_t* kp = (t ? kbase1 : kbase0) + (int64_t)row * p.k_row;
-        r.k[t][0] = *reinterpret_cast<const uint4*>(kp + 16 * g4);
-        r.k[t][1] = *reinterpret_cast<const uint4*>(kp + 64 + 16 * g4);
-      }
-      for (int j = 0; j < 8; ++j) {
-        const int t = j >> 2;
-        const int row = min(kb + 16 * t + 4 * g4 + (j & 3), last_key) & pmask;
-        const uint8_t* vp = (t ? vbase1 : vbase0) + (int64_t)row * p.v_row;
-        r.v[j] = *reinterpret_cast<const uint2*>(vp + 8 * r16);
-      }
-      return r;
-    };
-
-    // Fetch u loads block k_begin + 32u into ring slot u % STAGES. Every
-    // fetch issues the same 13 loads whether or not its block exists (a
-    // block past the chunk re-reads the chunk's last row, a cache hit), so
-    // the compiler counts the loads in flight exactly and each wait covers
-    // only the block being consumed. Fetch u takes its two pages from page
-    // slot u % STAGES (loaded two fetches earlier) and loads the pages of
-    // fetch u + 2 into slot (u + 2) % STAGES; slot indices are compile-time
-    // constants of the unrolled stage loop.
-    int pv[STAGES];
-    pv[0] = page_pair(k_begin);
-    pv[1 % STAGES] = page_pair(k_begin + kBlockKeys);
-    auto fetch = [&](RawBlock& r, int kb, const int slot) {
-      const int pg0 = clamp_page(__builtin_amdgcn_readlane(pv[slot], 0));
-      const int pg1 = clamp_page(__builtin_amdgcn_readlane(pv[slot], 1));
-      r = load_block(kb, pg0, pg1);
-      pv[(slot + 2) % STAGES] = page_pair(kb + 2 * kBlockKeys);
-    };
-    auto process = [&](const RawBlock& cur, int kb) {
-        // ---- S = K Q^T (keys on M) -----------------------------------------
-        f32x4 sacc[NB][2];
+// One 32-key block: S = K Q^T, online softmax, O^T += V^T P^T. lim[nb] is
+// the last key row r16 of block nb may see; keys past lim_min need the mask.
+template <bool FP8Q, int NB>
+__device__ __forceinline__ void process_block(const RawBlock& cur, int kb, const QOperand<NB>& q, RowState<NB>& st,
+                                              const int* lim, int lim_min, float c2, int g4) {
+  // ---- S = K Q^T (keys on M) -----------------------------------------------
+  f32x4 sacc[NB][2];
+  for (int nb = 0; nb < NB; ++nb)
+    for (int t = 0; t < 2; ++t) sacc[nb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < 2; ++t) {
+    for (int s = 0; s < 4; ++s) {
+      const uint2 kraw = half_of(cur.k[t][s >> 1], s & 1);
+      if (FP8Q) {
+        const long a = as_long(kraw);
         for (int nb = 0; nb < NB; ++nb)
-          for (int t = 0; t < 2; ++t) sacc[nb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int t = 0; t < 2; ++t) {
-          for (int s = 0; s < 4; ++s) {
-            const uint2 kraw = half_of(cur.k[t][s >> 1], s & 1);
-            if (FP8Q) {
-              const long a = as_long(kraw);
-              for (int nb = 0; nb < NB; ++nb)
-                sacc[nb][t] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, q8[nb][s], sacc[nb][t], 0, 0, 0);
-            } else {
-              const bf16x8 a = e4m3x8_to_bf16(kraw);
-              for (int nb = 0; nb < NB; ++nb)
-                sacc[nb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[nb][s], sacc[nb][t], 0, 0, 0);
-            }
-          }
-        }
-
-        // ---- online softmax (per query row = lane column r16) --------------
-        bf16x8 pb[NB];
-        long p8[NB];
-        const bool need_mask = kb + kBlockKeys - 1 > lim_min;
-        for (int nb = 0; nb < NB; ++nb) {
-          if (need_mask) {
-            for (int t = 0; t < 2; ++t)
-              for (int i = 0; i < 4; ++i)
-                if (kb + 16 * t + 4 * g4 + i > lim[nb]) sacc[nb][t][i] = -INFINITY;
-          }
-          float mx = fmaxf(fmaxf(fmaxf(sacc[nb][0][0], sacc[nb][0][1]), fmaxf(sacc[nb][0][2], sacc[nb][0][3])),
-                           fmaxf(fmaxf(sacc[nb][1][0], sacc[nb][1][1]), fmaxf(sacc[nb][1][2], sacc[nb][1][3])));
-          mx = wave_max16(mx);
-          const float m_new = fmaxf(m_run[nb], mx);
-          const float m_use = m_new == -INFINITY ? 0.f : m_new;  // no visible key yet: exp2(-inf) = 0
-          const float corr = __builtin_amdgcn_exp2f((m_run[nb] - m_use) * c2);
-          float pr[8];
-          float psum = 0.f;
-          for (int t = 0; t < 2; ++t)
-            for (int i = 0; i < 4; ++i) {
-              pr[4 * t + i] = __builtin_amdgcn_exp2f((sacc[nb][t][i] - m_use) * c2);
-              psum += pr[4 * t + i];
-            }
-          l_part[nb] = l_part[nb] * corr + psum;
-          // rescale O only if some row's max moved (otherwise corr == 1 exactly)
-          if (__builtin_amdgcn_ballot_w64(m_new != m_run[nb])) {
-            for (int mt = 0; mt < 8; ++mt) oacc[nb][mt] *= corr;
-          }
-          m_run[nb] = m_new;
-          if (FP8Q) {
-            int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0] * kP8Scale, pr[1] * kP8Scale, 0, false);
-            lo = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2] * kP8Scale, pr[3] * kP8Scale, lo, true);
-            int hi = __builtin_amdgcn_cvt_pk_fp8_f32(pr[4] * kP8Scale, pr[5] * kP8Scale, 0, false);
-            hi = __builtin_amdgcn_cvt_pk_fp8_f32(pr[6] * kP8Scale, pr[7] * kP8Scale, hi, true);
-            p8[nb] = as_long(uint2{(unsigned)lo, (unsigned)hi});
-          } else {
-            for (int e = 0; e < 8; ++e) pb[nb][e] = (__bf16)pr[e];
-          }
-        }
-
-        // ---- O^T += V^T P^T --------------------------------------------------
-        if (FP8Q) {
-          // 4x4 byte transposes: quad kq of keys, word w of d_v bytes
-          for (int w2 = 0; w2 < 2; ++w2) {
-            unsigned col[2][4];  // [kq][e]: keys 4kq..4kq+3 at d_v 8*r16 + 4*w2 + e
-            for (int kq = 0; kq < 2; ++kq) {
-              const unsigned r0 = w2 ? cur.v[4 * kq + 0].y : cur.v[4 * kq + 0].x;
-              const unsigned r1 = w2 ? cur.v[4 * kq + 1].y : cur.v[4 * kq + 1].x;
-              const unsigned r2 = w2 ? cur.v[4 * kq + 2].y : cur.v[4 * kq + 2].x;
-              const unsigned r3 = w2 ? cur.v[4 * kq + 3].y : cur.v[4 * kq + 3].x;
-              const unsigned t0 = __builtin_amdgcn_perm(r0, r1, 0x01050004u);
-              const unsigned t1 = __builtin_amdgcn_perm(r0, r1, 0x03070206u);
-              const unsigned t2 = __builtin_amdgcn_perm(r2, r3, 0x01050004u);
-              const unsigned t3 = __builtin_amdgcn_perm(r2, r3, 0x03070206u);
-              col[kq][0] = __builtin_amdgcn_perm(t0, t2, 0x01000504u);
-              col[kq][1] = __builtin_amdgcn_perm(t0, t2, 0x03020706u);
-              col[kq][2] = __builtin_amdgcn_perm(t1, t3, 0x01000504u);
-              col[kq][3] = __builtin_amdgcn_perm(t1, t3, 0x03020706u);
-            }
-            for (int e = 0; e < 4; ++e) {
-              const long a = as_long(uint2{col[0][e], col[1][e]});
-              const int mt = 4 * w2 + e;
-              for (int nb = 0; nb < NB; ++nb)
-                oacc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, p8[nb], oacc[nb][mt], 0, 0, 0);
-            }
-          }
-        } else {
-          for (int w2 = 0; w2 < 2; ++w2) {
-            unsigned xy[4][2];  // [key pair pp][0: d_v bytes 0,1 / 1: bytes 2,3 of the word], interleaved by key
-            for (int pp = 0; pp < 4; ++pp) {
-              const unsigned a0 = w2 ? cur.v[2 * pp].y : cur.v[2 * pp].x;
-              const unsigned a1 = w2 ? cur.v[2 * pp + 1].y : cur.v[2 * pp + 1].x;
-              xy[pp][0] = __builtin_amdgcn_perm(a0, a1, 0x01050004u);
-              xy[pp][1] = __builtin_amdgcn_perm(a0, a1, 0x03070206u);
-            }
-            for (int e = 0; e < 4; ++e) {
-              bf16x8 a;
-              for (int pp = 0; pp < 4; ++pp) {
-                const bf16x2 two = (e & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(xy[pp][e >> 1], 1.0f, true)
-                                           : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(xy[pp][e >> 1], 1.0f, false);
-                a[2 * pp] = two[0];
-                a[2 * pp + 1] = two[1];
-              }
-              const int mt = 4 * w2 + e;
-              for (int nb = 0; nb < NB; ++nb)
-                oacc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[nb], oacc[nb][mt], 0, 0, 0);
-            }
-          }
-        }
-    };
-
-    // Ring of STAGES register buffers: while block i is processed, blocks
-    // i+1 .. i+STAGES-1 are in flight.
-    // The loop runs whole rounds of STAGES blocks with no early exit, so
-    // entry and back edge see the same loads in flight. Blocks past the
-    // chunk (at most STAGES - 1 per work item) re-read its last row and are
-    // masked out entirely (P = 0 on finite data): they change nothing.
-    RawBlock ring[STAGES];
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) fetch(ring[s], k_begin + kBlockKeys * s, s);
-    const int rounds = (k_end - k_begin + kBlockKeys * STAGES - 1) / (kBlockKeys * STAGES);
-    for (int r = 0; r < rounds; ++r) {
-      const int kb0 = k_begin + r * kBlockKeys * STAGES;
-#pragma unroll
-      for (int s = 0; s < STAGES; ++s) {
-        const int kb = kb0 + kBlockKeys * s;
-        fetch(ring[(s + STAGES - 1) % STAGES], kb + kBlockKeys * (STAGES - 1), (s + STAGES - 1) % STAGES);
-        process(ring[s], kb);
+          sacc[nb][t] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, q.q8[nb][s], sacc[nb][t], 0, 0, 0);
+      } else {
+        const bf16x8 a = e4m3x8_to_bf16(kraw);
+        for (int nb = 0; nb < NB; ++nb)
+          sacc[nb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, q.qb[nb][s], sacc[nb][t], 0, 0, 0);
       }
     }
   }
 
-  // ---- epilogue -------------------------------------------------------------
-  const float p_scale = FP8Q ? kP8Scale : 1.0f;
+  // ---- online softmax (per query row = lane column r16) --------------------
+  bf16x8 pb[NB];
+  long p8[NB];
+  const bool need_mask = kb + kBlockKeys - 1 > lim_min;
   for (int nb = 0; nb < NB; ++nb) {
-    const float l = wave_sum16(l_part[nb]);
-    if (!row_ok[nb]) continue;
+    if (need_mask) {
+      for (int t = 0; t < 2; ++t)
+        for (int i = 0; i < 4; ++i)
+          if (kb + 16 * t + 4 * g4 + i > lim[nb]) sacc[nb][t][i] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sacc[nb][0][0], sacc[nb][0][1]), fmaxf(sacc[nb][0][2], sacc[nb][0][3])),
+                     fmaxf(fmaxf(sacc[nb][1][0], sacc[nb][1][1]), fmaxf(sacc[nb][1][2], sacc[nb][1][3])));
+    mx = wave_max16(mx);
+    // m_run is the row's reference max: P = exp2((s - m_run) * c2), with l
+    // and O kept relative to it. e4m3 P (p * 448 must stay <= 448) moves it to
+    // every new max. bf16 P moves it only once the new max would make some p
+    // exceed 2^kLazyLog2 (or on the first visible key), so rows rarely need
+    // the O rescale; the result is the same softmax, rounded in a different
+    // place.
+    const float m_max = fmaxf(st.m_run[nb], mx);
+    const bool move = FP8Q ? m_max != st.m_run[nb]
+                           : (st.m_run[nb] == -INFINITY ? m_max != -INFINITY
+                                                        : (m_max - st.m_run[nb]) * c2 > kLazyLog2);
+    const float m_new = move ? m_max : st.m_run[nb];
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // no visible key yet: exp2(-inf) = 0
+    const float corr = __builtin_amdgcn_exp2f((st.m_run[nb] - m_use) * c2);
+    float pr[8];
+    float psum = 0.f;
+    for (int t = 0; t < 2; ++t)
+      for (int i = 0; i < 4; ++i) {
+        pr[4 * t + i] = __builtin_amdgcn_exp2f((sacc[nb][t][i] - m_use) * c2);
+        psum += pr[4 * t + i];
+      }
+    st.l_part[nb] = st.l_part[nb] * corr + psum;
+    // rescale O only if some row's reference moved (otherwise corr == 1 exactly)
+    if (__builtin_amdgcn_ballot_w64(move)) {
+      for (int mt = 0; mt < 8; ++mt) st.oacc[nb][mt] *= corr;
+    }
+    st.m_run[nb] = m_new;
+    if (FP8Q) {
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0] * kP8Scale, pr[1] * kP8Scale, 0, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2] * kP8Scale, pr[3] * kP8Scale, lo, true);
+      int hi = __builtin_amdgcn_cvt_pk_fp8_f32(pr[4] * kP8Scale, pr[5] * kP8Scale, 0, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(pr[6] * kP8Scale, pr[7] * kP8Scale, hi, true);
+      p8[nb] = as_long(uint2{(unsigned)lo, (unsigned)hi});
+    } else {
+      for (int e = 0; e < 8; ++e) pb[nb][e] = (__bf16)pr[e];
+    }
+  }
+
+  // ---- O^T += V^T P^T --------------------------------------------------------
+  if (FP8Q) {
+    // 4x4 byte transposes: quad kq of keys, word w of d_v bytes
+    for (int w2 = 0; w2 < 2; ++w2) {
+      unsigned col[2][4];  // [kq][e]: keys 4kq..4kq+3 at d_v 8*r16 + 4*w2 + e
+      for (int kq = 0; kq < 2; ++kq) {
+        const unsigned r0 = w2 ? cur.v[4 * kq + 0].y : cur.v[4 * kq + 0].x;
+        const unsigned r1 = w2 ? cur.v[4 * kq + 1].y : cur.v[4 * kq + 1].x;
+        const unsigned r2 = w2 ? cur.v[4 * kq + 2].y : cur.v[4 * kq + 2].x;
+        const unsigned r3 = w2 ? cur.v[4 * kq + 3].y : cur.v[4 * kq + 3].x;
+        const unsigned t0 = __builtin_amdgcn_perm(r0, r1, 0x01050004u);
+        const unsigned t1 = __builtin_amdgcn_perm(r0, r1, 0x03070206u);
+        const unsigned t2 = __builtin_amdgcn_perm(r2, r3, 0x01050004u);
+        const unsigned t3 = __builtin_amdgcn_perm(r2, r3, 0x03070206u);
+        col[kq][0] = __builtin_amdgcn_perm(t0, t2, 0x01000504u);
+        col[kq][1] = __builtin_amdgcn_perm(t0, t2, 0x03020706u);
+        col[kq][2] = __builtin_amdgcn_perm(t1, t3, 0x01000504u);
+        col[kq][3] = __builtin_amdgcn_perm(t1, t3, 0x03020706u);
+      }
+      for (int e = 0; e < 4; ++e) {
+        const long a = as_long(uint2{col[0][e], col[1][e]});
+        const int mt = 4 * w2 + e;
+        for (int nb = 0; nb < NB; ++nb)
+          st.oacc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, p8[nb], st.oacc[nb][mt], 0, 0, 0);
+      }
+    }
+  } else {
+    for (int w2 = 0; w2 < 2; ++w2) {
+      unsigned xy[4][2];  // [key pair pp][0: d_v bytes 0,1 / 1: bytes 2,3 of the word], interleaved by key
+      for (int pp = 0; pp < 4; ++pp) {
+        const unsigned a0 = w2 ? cur.v[2 * pp].y : cur.v[2 * pp].x;
+        const unsigned a1 = w2 ? cur.v[2 * pp + 1].y : cur.v[2 * pp + 1].x;
+        xy[pp][0] = __builtin_amdgcn_perm(a0, a1, 0x01050004u);
+        xy[pp][1] = __builtin_amdgcn_perm(a0, a1, 0x03070206u);
+      }
+      for (int e = 0; e < 4; ++e) {
+        bf16x8 a;
+        for (int pp = 0; pp < 4; ++pp) {
+          const bf16x2 two = (e & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(xy[pp][e >> 1], 1.0f, true)
+                                     : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(xy[pp][e >> 1], 1.0f, false);
+          a[2 * pp] = two[0];
+          a[2 * pp + 1] = two[1];
+        }
+        const int mt = 4 * w2 + e;
+        for (int nb = 0; nb < NB; ++nb)
+          st.oacc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[nb], st.oacc[nb][mt], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Epilogue of one work item for kv head g of sequence b: a sequence with one
+// split writes O and LSE itself; otherwise the rows go to split slot `slot`
+// of the workspace, and with merge counters the split that finishes last for
+// this (sequence, head, q tile) combines all of them.
+template <bool FP8Q, int NB>
+__device__ __forceinline__ void finish_item(const GqaParams& p, const RowState<NB>& st, const RowMap<NB>& rm, int b,
+                                            int g, int row0, int r16, int g4, int ns, int slot, float cs, float vdv) {
+  const bool direct = ns <= 1;
+  const float p_scale = FP8Q ? kP8Scale : 1.0f;
+  int qtok[NB], qhead[NB];
+  for (int nb = 0; nb < NB; ++nb) {
+    qtok[nb] = b * p.q_len + rm.qi[nb];
+    qhead[nb] = g * p.h_r + rm.hr[nb];
+  }
+  for (int nb = 0; nb < NB; ++nb) {
+    const float l = wave_sum16(st.l_part[nb]);
+    if (!rm.ok[nb]) continue;
     const int n = row0 + 16 * nb + r16;
     const int64_t stat_row = ((int64_t)b * p.h_k + g) * p.rows + n;
-    const float m_nat = m_run[nb] == -INFINITY ? -INFINITY : m_run[nb] * cs;
-    // lane holds O^T[d_v = 32*g4 + 8*i + mt][n] in oacc[nb][mt][i]
+    const float m_nat = st.m_run[nb] == -INFINITY ? -INFINITY : st.m_run[nb] * cs;
     if (direct) {
       const float inv = l > 0.f ? (p.o_scale * vdv / p_scale) / l : 0.f;
       uint8_t* orow = p.o + (int64_t)qtok[nb] * p.o_tok + (int64_t)qhead[nb] * p.o_head;
       for (int i = 0; i < 4; ++i) {
         bf16x8 out;
-        for (int mt = 0; mt < 8; ++mt) out[mt] = (__bf16)(oacc[nb][mt][i] * inv);
+        for (int mt = 0; mt < 8; ++mt) out[mt] = (__bf16)(st.oacc[nb][mt][i] * inv);
         *reinterpret_cast<bf16x8*>(orow + 2 * (32 * g4 + 8 * i)) = out;
       }
       if (g4 == 0) p.lse[stat_row] = l > 0.f ? m_nat + logf(l) : -INFINITY;
@@ -455,12 +437,12 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
         // another XCD: agent-coherent stores (past the XCD's own L2)
         for (int i = 0; i < 4; ++i)
           for (int mt = 0; mt < 8; mt += 2)
-            store_coherent(dst + 8 * i + mt, oacc[nb][mt][i] * ps, oacc[nb][mt + 1][i] * ps);
+            store_coherent(dst + 8 * i + mt, st.oacc[nb][mt][i] * ps, st.oacc[nb][mt + 1][i] * ps);
         if (g4 == 0) store_coherent(reinterpret_cast<float*>(p.ws_ml + prow), m_nat, l);
       } else {
         for (int i = 0; i < 4; ++i) {
-          f32x4 lo4 = {oacc[nb][0][i], oacc[nb][1][i], oacc[nb][2][i], oacc[nb][3][i]};
-          f32x4 hi4 = {oacc[nb][4][i], oacc[nb][5][i], oacc[nb][6][i], oacc[nb][7][i]};
+          f32x4 lo4 = {st.oacc[nb][0][i], st.oacc[nb][1][i], st.oacc[nb][2][i], st.oacc[nb][3][i]};
+          f32x4 hi4 = {st.oacc[nb][4][i], st.oacc[nb][5][i], st.oacc[nb][6][i], st.oacc[nb][7][i]};
           *reinterpret_cast<f32x4*>(dst + 8 * i) = lo4 * ps;
           *reinterpret_cast<f32x4*>(dst + 8 * i + 4) = hi4 * ps;
         }
@@ -479,14 +461,258 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     int32_t* ctr = p.counters + ((int64_t)b * p.h_k + g) * gridDim.z + blockIdx.z;
     int last = 0;
-    if (lane == 0)
+    if ((threadIdx.x & 63) == 0)
       last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == min(ns, p.max_splits) - 1;
     last = __builtin_amdgcn_readfirstlane(last);
     if (last) {
       asm volatile("" ::: "memory");
       merge_rows<NB>(p, b, g, row0, r16, g4, min(ns, p.max_splits), qtok, qhead);
-      if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((threadIdx.x & 63) == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+  }
+}
+
+__device__ __forceinline__ int clamp_page(const GqaParams& p, int pg) { return min(max(pg, 0), p.num_pages - 1); }
+
+// One work item (a chunk of 128-key tiles of one sequence) for kv head g:
+// the one-item-per-workgroup plan.
+template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES>
+__device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, int lane, int g) {
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+
+  const int4 w = p.work[item];
+  const int b = w.x;
+  if (w.z <= w.y || b < 0 || b >= p.num_seqs) return;  // padding item / bad entry
+  const int ns = p.n_splits[b];
+  const int slot = w.w;
+  if (ns > 1 && (slot < 0 || slot >= p.max_splits)) return;
+  const int row0 = blockIdx.z * (16 * NB);
+
+  const int page_size = 1 << p.page_shift;
+  int L = p.seq_lens[b];
+  L = max(0, min(L, p.max_blocks * page_size));
+  const int k_begin = w.y * kTileKeys;
+  const int k_end = min(w.z * kTileKeys, L);
+
+  const RowMap<NB> rm = row_map<NB>(p, row0, r16);
+  int lim[NB];  // last key each row may see inside this work item's chunk
+  for (int nb = 0; nb < NB; ++nb) lim[nb] = min(CAUSAL_TAIL ? L - p.q_len + rm.qi[nb] : L - 1, k_end - 1);
+  const int lim_min = min(CAUSAL_TAIL ? L - p.q_len : L - 1, k_end - 1);
+
+  const float qd = FP8Q ? p.qd[b * p.qd_seq + g * p.qd_head] : 1.0f;
+  const float kdv = p.kd[b * p.kd_seq + g * p.kd_head];
+  const float vdv = p.vd[b * p.vd_seq + g * p.vd_head];
+  const float c2 = p.scale_log2e * qd * kdv;  // exponent scale (base 2) on raw scores
+  const float cs = p.scale * qd * kdv;        // natural-log scale of the running max
+
+  QOperand<NB> q;
+  load_q<FP8Q, NB>(p, q, rm, b, g, g4);
+  RowState<NB> st;
+  reset_rows<NB>(st);
+
+  if (k_end > k_begin) {
+    const int32_t* bt = p.block_table + (int64_t)b * p.bt_row;
+    const int last_key = k_end - 1;  // loads never go past the chunk (and so never past L)
+    const int pmask = page_size - 1;
+    // Pages of one 32-key block (page_size >= 16, so each 16-key group lies
+    // in one page): lane l loads the entry of group l & 1, so lanes 0 and 1
+    // hold the block's two pages. A vector load, so waiting for it (in
+    // order) never waits for the KV loads issued after it.
+    auto page_pair = [&](int kb) -> int { return bt[min(kb + 16 * (lane & 1), last_key) >> p.page_shift]; };
+
+    // Fetch u loads block k_begin + 32u into ring slot u % STAGES. Every
+    // fetch issues the same 13 loads whether or not its block exists (a
+    // block past the chunk re-reads the chunk's last row, a cache hit), so
+    // the compiler counts the loads in flight exactly and each wait covers
+    // only the block being consumed. Fetch u takes its two pages from page
+    // slot u % STAGES (loaded two fetches earlier) and loads the pages of
+    // fetch u + 2 into slot (u + 2) % STAGES; slot indices are compile-time
+    // constants of the unrolled stage loop.
+    int pv[STAGES];
+    pv[0] = page_pair(k_begin);
+    pv[1 % STAGES] = page_pair(k_begin + kBlockKeys);
+    auto fetch = [&](RawBlock& r, int kb, const int slot) {
+      const int pg0 = clamp_page(p, __builtin_amdgcn_readlane(pv[slot], 0));
+      const int pg1 = clamp_page(p, __builtin_amdgcn_readlane(pv[slot], 1));
+      r = load_block(p, g, kb, pg0, pg1, last_key, pmask, r16, g4);
+      pv[(slot + 2) % STAGES] = page_pair(kb + 2 * kBlockKeys);
+    };
+
+    // Ring of STAGES register buffers: while block i is processed, blocks
+    // i+1 .. i+STAGES-1 are in flight.
+    // The loop runs whole rounds of STAGES blocks with no early exit, so
+    // entry and back edge see the same loads in flight. Blocks past the
+    // chunk (at most STAGES - 1 per work item) re-read its last row and are
+    // masked out entirely (P = 0 on finite data): they change nothing.
+    RawBlock ring[STAGES];
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) fetch(ring[s], k_begin + kBlockKeys * s, s);
+    const int rounds = (k_end - k_begin + kBlockKeys * STAGES - 1) / (kBlockKeys * STAGES);
+    for (int r = 0; r < rounds; ++r) {
+      const int kb0 = k_begin + r * kBlockKeys * STAGES;
+#pragma unroll
+      for (int s = 0; s < STAGES; ++s) {
+        const int kb = kb0 + kBlockKeys * s;
+        fetch(ring[(s + STAGES - 1) % STAGES], kb + kBlockKeys * (STAGES - 1), (s + STAGES - 1) % STAGES);
+        process_block<FP8Q, NB>(ring[s], kb, q, st, lim, lim_min, c2, g4);
+      }
+    }
+  }
+  finish_item<FP8Q, NB>(p, st, rm, b, g, row0, r16, g4, ns, slot, cs, vdv);
+}
+
+// The work items of one bin of the balanced plan (key ranges of one or more
+// sequences, in order) for kv head g, streamed through ONE ring: the loads of
+// the next item's first blocks are in flight while the current item's last
+// blocks are processed, so an item boundary costs its epilogue and nothing
+// else.
+//
+// The bin's items are described by a table held one item per lane (up to 64
+// items at a time): sequence, first key, clamped end, and the running count
+// of 32-key blocks. Bin block j belongs to the item whose running count
+// first exceeds j, found with one ballot and a popcount, and item fields are
+// read with readlane -- no LDS, no scalar loads in the loop. Each item's
+// query rows are loaded while the item before it runs.
+template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES>
+__device__ __forceinline__ void gqa_decode_stream(const GqaParams& p, int lane, int g) {
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+  const int row0 = blockIdx.z * (16 * NB);
+  const int page_size = 1 << p.page_shift;
+  const int pmask = page_size - 1;
+  const int key_cap = p.max_blocks * page_size;
+  const RowMap<NB> rm = row_map<NB>(p, row0, r16);
+  const int it_lo = p.bin_offsets[blockIdx.x];
+  const int it_hi = p.bin_offsets[blockIdx.x + 1];
+
+  for (int seg = it_lo; seg < it_hi; seg += 64) {
+    const int np = min(64, it_hi - seg);
+    // ---- item table: lane i describes item seg + i ---------------------------
+    int t_b = 0, t_k0 = 0, t_end = 0, t_L = 0, t_slot = 0, t_ns = 1, t_ok = 0, nblk = 0;
+    float t_kd = 0.f, t_vd = 0.f, t_qd = 1.f;
+    if (lane < np) {
+      const int4 w = p.work[seg + lane];
+      if (w.x >= 0 && w.x < p.num_seqs && w.y >= 0 && w.z >= w.y) {
+        t_b = w.x;
+        t_k0 = w.y;
+        t_L = max(0, min(p.seq_lens[t_b], key_cap));
+        t_end = min(w.z, t_L);
+        t_ns = p.n_splits[t_b];
+        t_slot = w.w;
+        t_ok = t_ns <= 1 || (t_slot >= 0 && t_slot < p.max_splits);
+        // blocks of the planned range; keys past L are loaded clamped and masked
+        nblk = t_ok ? (min(w.z, key_cap) - w.y + kBlockKeys - 1) / kBlockKeys : 0;
+        nblk = max(nblk, 0);
+        t_kd = p.kd[t_b * p.kd_seq + g * p.kd_head];
+        t_vd = p.vd[t_b * p.vd_seq + g * p.vd_head];
+        if (FP8Q) t_qd = p.qd[t_b * p.qd_seq + g * p.qd_head];
+      }
+    }
+    int cum = nblk;  // inclusive running count of blocks over the items
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(cum, d, 64);
+      if (lane >= d) cum += o;
+    }
+    const int nblocks = __builtin_amdgcn_readlane(cum, 63);
+    const int cum_end = lane < np ? cum : 0x7fffffff;
+    const int t_kbase = t_k0 - kBlockKeys * (cum - nblk);  // key of bin block j = t_kbase + 32 j
+    const int t_last = max(t_end - 1, 0);                   // loads clamp to this key (< L when L > 0)
+    auto item_of = [&](int j) -> int {  // the item holding bin block j < nblocks
+      return (int)__builtin_popcountll(__builtin_amdgcn_ballot_w64(cum_end <= j));
+    };
+
+    // ---- current item ----------------------------------------------------------
+    QOperand<NB> qc, qn;  // query rows of the current item / of the next one
+    RowState<NB> st;
+    reset_rows<NB>(st);
+    int cur = -1;
+    int c_b = 0, c_ns = 1, c_slot = 0, c_ok = 0, lim_min = -1, lim_max = -1;
+    int lim[NB];
+    for (int nb = 0; nb < NB; ++nb) lim[nb] = -1;
+    float c2 = 0.f, cs = 0.f, c_vd = 0.f;
+    auto prefetch_q = [&](int i) {
+      if (i < np) load_q<FP8Q, NB>(p, qn, rm, __builtin_amdgcn_readlane(t_b, i), g, g4);
+    };
+    auto begin_item = [&](int i) {
+      qc = qn;
+      c_b = __builtin_amdgcn_readlane(t_b, i);
+      c_ns = __builtin_amdgcn_readlane(t_ns, i);
+      c_slot = __builtin_amdgcn_readlane(t_slot, i);
+      c_ok = __builtin_amdgcn_readlane(t_ok, i);
+      const int L = __builtin_amdgcn_readlane(t_L, i);
+      const int k_end = __builtin_amdgcn_readlane(t_end, i);
+      for (int nb = 0; nb < NB; ++nb) lim[nb] = min(CAUSAL_TAIL ? L - p.q_len + rm.qi[nb] : L - 1, k_end - 1);
+      lim_min = min(CAUSAL_TAIL ? L - p.q_len : L - 1, k_end - 1);
+      lim_max = k_end - 1;
+      const float qd = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(t_qd), i));
+      const float kd = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(t_kd), i));
+      c_vd = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(t_vd), i));
+      c2 = p.scale_log2e * qd * kd;
+      cs = p.scale * qd * kd;
+      reset_rows<NB>(st);
+      prefetch_q(i + 1);
+    };
+    auto end_item = [&]() {
+      if (c_ok) finish_item<FP8Q, NB>(p, st, rm, c_b, g, row0, r16, g4, c_ns, c_slot, cs, c_vd);
+    };
+    auto advance_to = [&](int i) {  // finish items before i (empty ones too), begin item i
+      while (cur < i) {
+        if (cur >= 0) end_item();
+        ++cur;
+        begin_item(cur);
+      }
+    };
+    prefetch_q(0);
+
+    if (nblocks > 0) {
+      // bin block j (clamped to the last one: blocks past the bin re-read it)
+      auto block_at = [&](int j, int& b, int& kb, int& last) {
+        const int jc = min(j, nblocks - 1);
+        const int i = item_of(jc);
+        b = __builtin_amdgcn_readlane(t_b, i);
+        kb = __builtin_amdgcn_readlane(t_kbase, i) + kBlockKeys * jc;
+        last = __builtin_amdgcn_readlane(t_last, i);
+      };
+      auto page_pair = [&](int j) -> int {  // lanes 0 / 1: pages of the block's two 16-key groups
+        int b, kb, last;
+        block_at(j, b, kb, last);
+        return p.block_table[(int64_t)b * p.bt_row + (min(kb + 16 * (lane & 1), last) >> p.page_shift)];
+      };
+      // Same discipline as the one-item path: every step issues the same
+      // loads, page pairs two fetches ahead in a vector ring.
+      int pv[STAGES];
+      pv[0] = page_pair(0);
+      pv[1 % STAGES] = page_pair(1);
+      auto fetch = [&](RawBlock& r, int j, const int slot) {
+        int b, kb, last;
+        block_at(j, b, kb, last);
+        const int pg0 = clamp_page(p, __builtin_amdgcn_readlane(pv[slot], 0));
+        const int pg1 = clamp_page(p, __builtin_amdgcn_readlane(pv[slot], 1));
+        r = load_block(p, g, kb, pg0, pg1, last, pmask, r16, g4);
+        pv[(slot + 2) % STAGES] = page_pair(j + 2);
+      };
+      RawBlock ring[STAGES];
+#pragma unroll
+      for (int s = 0; s < STAGES - 1; ++s) fetch(ring[s], s, s);
+      const int rounds = (nblocks + STAGES - 1) / STAGES;
+      for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+        for (int s = 0; s < STAGES; ++s) {
+          const int j = r * STAGES + s;
+          fetch(ring[(s + STAGES - 1) % STAGES], j + STAGES - 1, (s + STAGES - 1) % STAGES);
+          if (j < nblocks) {
+            const int i = item_of(j);
+            if (i != cur) advance_to(i);
+            const int kb = __builtin_amdgcn_readlane(t_kbase, i) + kBlockKeys * j;
+            // a block with no key below the item's end (past L) is skipped
+            if (kb <= lim_max) process_block<FP8Q, NB>(ring[s], kb, qc, st, lim, lim_min, c2, g4);
+          }
+        }
+      }
+    }
+    advance_to(np - 1);  // items after the last block (empty ones)
+    end_item();
   }
 }
 
@@ -494,33 +720,44 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
 // they stream the same pages (every head's rows of a key range), which keeps
 // the number of concurrent DRAM streams per key range at two (K, V). A
 // workgroup runs one work item, or with a balanced plan the items of its
-// bin (a contiguous share of all sequences' keys) one after the other.
-template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES, int HW>
-__global__ __launch_bounds__(64 * HW) void gqa_decode_kernel(GqaParams p) {
+// bin (a contiguous share of all sequences' keys) as one stream.
+// One row block fits in 256 registers; capping it at two waves per SIMD keeps
+// the compiler from spilling into AGPRs when the workgroup is small enough
+// to allow one wave per SIMD. Two row blocks get the whole register file.
+template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES, int HW, bool STREAM>
+__global__ __launch_bounds__(64 * HW) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 2 : 1)))
+void gqa_decode_kernel(GqaParams p) {
   const int lane = threadIdx.x & 63;
-  const int g = blockIdx.y * HW + (threadIdx.x >> 6);
+  const int g = __builtin_amdgcn_readfirstlane(blockIdx.y * HW + (threadIdx.x >> 6));  // wave-uniform
   if (g >= p.h_k) return;
-  int it = blockIdx.x, it_end = blockIdx.x + 1;
-  if (p.bin_offsets) {
-    it = p.bin_offsets[blockIdx.x];
-    it_end = p.bin_offsets[blockIdx.x + 1];
-  }
-  for (; it < it_end; ++it) gqa_decode_item<FP8Q, NB, CAUSAL_TAIL, STAGES>(p, it, lane, g);
+  if (STREAM)
+    gqa_decode_stream<FP8Q, NB, CAUSAL_TAIL, STAGES>(p, lane, g);
+  else
+    gqa_decode_item<FP8Q, NB, CAUSAL_TAIL, STAGES>(p, blockIdx.x, lane, g);
 }
 
-template <bool FP8Q, int NB, bool CT, int ST, int HW>
-const void* kernel_ptr() {
-  return reinterpret_cast<const void*>(&gqa_decode_kernel<FP8Q, NB, CT, ST, HW>);
+// Ring depth in 32-key blocks. Three blocks (two in flight while one is
+// processed) for either row-block count: a deeper ring for two row blocks
+// needs more than the 256 VGPRs, and the compiler then shuttles values
+// through AGPRs, which costs more than the extra depth gains.
+template <int NB, bool STREAM>
+constexpr int ring_stages() {
+  return 3;
+}
+
+template <bool FP8Q, int NB, bool CT, int HW>
+const void* kernel_ptr(bool stream) {
+  return stream ? reinterpret_cast<const void*>(&gqa_decode_kernel<FP8Q, NB, CT, ring_stages<NB, true>(), HW, true>)
+                : reinterpret_cast<const void*>(&gqa_decode_kernel<FP8Q, NB, CT, ring_stages<NB, false>(), HW, false>);
 }
 
 template <bool FP8Q, int NB, bool CT>
 const void* select_heads(const GqaVariant& v) {
-  constexpr int ST = NB == 1 ? 3 : 6;
   switch (v.heads_per_wg) {
-    case 1: return kernel_ptr<FP8Q, NB, CT, ST, 1>();
-    case 2: return kernel_ptr<FP8Q, NB, CT, ST, 2>();
-    case 4: return kernel_ptr<FP8Q, NB, CT, ST, 4>();
-    default: return kernel_ptr<FP8Q, NB, CT, ST, NB == 1 ? 8 : 4>();
+    case 1: return kernel_ptr<FP8Q, NB, CT, 1>(v.stream);
+    case 2: return kernel_ptr<FP8Q, NB, CT, 2>(v.stream);
+    case 4: return kernel_ptr<FP8Q, NB, CT, 4>(v.stream);
+    default: return kernel_ptr<FP8Q, NB, CT, NB == 1 ? 8 : 4>(v.stream);
   }
 }
 
@@ -548,7 +785,8 @@ GqaVariant gqa_variant(const pkv_decode_args& a) {
   const int rows = a.q_len * (a.h_q / a.h_k);
   v.n_blocks = rows <= 16 ? 1 : 2;
   v.causal_tail = a.causal && a.q_len > 1;
-  v.stages = v.n_blocks == 1 ? 3 : 6;
+  v.stream = a.bin_offsets != nullptr;
+  v.stages = 3;
   // kv heads per workgroup: the largest power of two dividing h_k, up to 8
   // (4 for two row blocks, whose waves need more than half the registers)
   const int cap = v.n_blocks == 1 ? 8 : 4;

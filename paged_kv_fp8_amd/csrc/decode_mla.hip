@@ -131,8 +131,9 @@ __device__ __forceinline__ void mla_decode_item(const MlaParams& p, int item, in
   const int page_size = 1 << p.page_shift;
   int L = p.seq_lens[b];
   L = max(0, min(L, p.max_blocks * page_size));
-  const int k_begin = w.y * kTileKeys;
-  const int k_end = min(w.z * kTileKeys, L);
+  // balanced plan items are key ranges, the one-item-per-workgroup plan's tile ranges
+  const int k_begin = p.bin_offsets ? w.y : w.y * kTileKeys;
+  const int k_end = min(p.bin_offsets ? w.z : w.z * kTileKeys, L);
 
   // rows of this wave: n = row0 + r16 (token qi = n / h_q, head n % h_q)
   const int n = row0 + r16;

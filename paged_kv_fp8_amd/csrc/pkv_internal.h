@@ -21,6 +21,7 @@ struct GqaVariant {
   bool causal_tail; // q_len > 1 && causal
   int stages;       // register ring depth of the KV stream (blocks of 32 keys)
   int heads_per_wg; // kv heads (one wave each) per workgroup
+  bool stream;      // balanced plan: each workgroup streams the items of its bin
 };
 GqaVariant gqa_variant(const pkv_decode_args& a);
 int gqa_rows_per_tile(const GqaVariant& v);

@@ -14,6 +14,7 @@
 namespace {
 
 constexpr int64_t kTileKeys = 128;
+constexpr int64_t kBalanceBlockKeys = 32;  // cut granularity of the balanced plan
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -129,13 +130,13 @@ extern "C" pkv_status pkv_plan_balanced(const int32_t* seq_lens, int32_t num_seq
   std::vector<int64_t> start(num_seqs + 1, 0);
   for (int32_t b = 0; b < num_seqs; ++b) {
     if (seq_lens[b] < 0) return fail(PKV_ERR_INVALID_ARG, "plan: seq_lens[%d]=%d < 0", b, seq_lens[b]);
-    start[b + 1] = start[b] + std::max<int64_t>(1, ceil_div(seq_lens[b], kTileKeys));
+    start[b + 1] = start[b] + std::max<int64_t>(1, ceil_div(seq_lens[b], kBalanceBlockKeys));
   }
   const int64_t total = start[num_seqs];
   int64_t bins = ((int64_t)cu_count * wg_per_cu) / ((int64_t)h_k * n_q_tiles);
   bins = std::max<int64_t>(1, std::min(bins, total));
-  // share i covers global tiles [i*total/bins, (i+1)*total/bins); the share
-  // holding tile x is the last i with i*total/bins <= x
+  // share i covers global blocks [i*total/bins, (i+1)*total/bins); the share
+  // holding block x is the last i with i*total/bins <= x
   auto share_of = [&](int64_t x, int64_t nb) {
     int64_t i = ((x + 1) * nb + total - 1) / total - 1;  // largest i with floor(i*total/nb) <= x
     while (i + 1 < nb && ((i + 1) * total) / nb <= x) ++i;
@@ -164,8 +165,8 @@ extern "C" pkv_status pkv_plan_balanced(const int32_t* seq_lens, int32_t num_seq
       if (s0 >= e0) continue;
       if (n >= work_cap) return fail(PKV_ERR_CAPACITY, "plan: work items exceed work_cap=%d", work_cap);
       work_out[4 * n + 0] = c;
-      work_out[4 * n + 1] = (int32_t)(s0 - start[c]);
-      work_out[4 * n + 2] = (int32_t)(e0 - start[c]);
+      work_out[4 * n + 1] = (int32_t)(kBalanceBlockKeys * (s0 - start[c]));
+      work_out[4 * n + 2] = (int32_t)std::min<int64_t>(kBalanceBlockKeys * (e0 - start[c]), seq_lens[c]);
       work_out[4 * n + 3] = seen[c]++;
       ++n;
     }
@@ -179,7 +180,7 @@ extern "C" pkv_status pkv_plan_balanced(const int32_t* seq_lens, int32_t num_seq
   if (info) {
     info->num_work = (int32_t)n;
     info->num_real = (int32_t)n;
-    info->chunk_tiles = (int32_t)ceil_div(total, bins);
+    info->chunk_tiles = (int32_t)ceil_div(ceil_div(total, bins), kTileKeys / kBalanceBlockKeys);
     info->slots = (int32_t)bins;
     info->max_n_splits = max_ns;
     info->num_bins = (int32_t)bins;

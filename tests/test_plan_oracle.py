@@ -109,44 +109,62 @@ from oracle.plan import plan_balanced  # noqa: E402
 
 
 def test_balanced_hand_worked():
-    # tiles [3, 8, 2, 1], 14 in total, starting at 0, 3, 11, 13; slots = 5*2 // 2 = 5 bins,
-    # cut at 14*i // 5 = 0, 2, 5, 8, 11, 14
+    # 32-key blocks [10, 32, 5, 2], 49 in total, starting at 0, 10, 42, 47; slots = 5*2 // 2 = 5 bins,
+    # cut at 49*i // 5 = 0, 9, 19, 29, 39, 49
     work, ns, off, bins = plan_balanced([300, 1000, 129, 50], h_k=2, n_q_tiles=1, cu_count=5, wg_per_cu=2)
     assert bins == 5
-    assert work == [(0, 0, 2, 0),                  # bin 0: global [0, 2)
-                    (0, 2, 3, 1), (1, 0, 2, 0),    # bin 1: [2, 5)
-                    (1, 2, 5, 1),                  # bin 2: [5, 8)
-                    (1, 5, 8, 2),                  # bin 3: [8, 11)
-                    (2, 0, 2, 0), (3, 0, 1, 0)]    # bin 4: [11, 14)
-    assert off == [0, 1, 3, 4, 5, 7] and ns == [2, 3, 1, 1]
+    assert work == [(0, 0, 288, 0),                      # bin 0: global blocks [0, 9)
+                    (0, 288, 300, 1), (1, 0, 288, 0),    # bin 1: [9, 19), sequence 0 ends at L = 300
+                    (1, 288, 608, 1),                    # bin 2: [19, 29)
+                    (1, 608, 928, 2),                    # bin 3: [29, 39)
+                    (1, 928, 1000, 3), (2, 0, 129, 0), (3, 0, 50, 0)]  # bin 4: [39, 49)
+    assert off == [0, 1, 3, 4, 5, 8] and ns == [2, 4, 1, 1]
 
 
 def test_balanced_lowers_bins_for_max_splits():
-    # one sequence of 64 tiles over 32 bins would be 32 pieces; max_splits 8 -> 8 bins
+    # one sequence of 256 blocks over 32 bins would be 32 pieces; max_splits 8 -> 8 bins of 1024 keys
     work, ns, off, bins = plan_balanced([64 * 128], h_k=1, n_q_tiles=1, cu_count=32, max_splits=8)
     assert bins == 8 and ns == [8]
-    assert [w[2] - w[1] for w in work] == [8] * 8
+    assert [w[2] - w[1] for w in work] == [1024] * 8
+
+
+def test_balanced_empty_sequence_is_one_block():
+    # L = 0 still takes one block, so its (empty) item exists and its output gets written
+    work, ns, off, bins = plan_balanced([0, 64], h_k=1, n_q_tiles=1, cu_count=3)
+    assert bins == 3 and work == [(0, 0, 0, 0), (1, 0, 32, 0), (1, 32, 64, 1)] and ns == [1, 2]
+    assert off == [0, 1, 2, 3]
 
 
 @pytest.mark.parametrize("seed", range(40))
 def test_balanced_invariants(seed):
     rng = np.random.default_rng(5000 + seed)
     b = int(rng.integers(1, 100))
-    lens = rng.integers(0, 70000, size=b).tolist()
+    lens = rng.integers(0, 70000, size=b)
+    lens[rng.random(b) < 0.1] = 0
+    lens = lens.tolist()
     kw = dict(h_k=int(rng.choice([1, 2, 4, 8])), n_q_tiles=int(rng.integers(1, 3)), cu_count=256,
               wg_per_cu=int(rng.integers(1, 9)), max_splits=int(rng.choice([4, 16, 64, 256])))
     work, ns, off, bins = plan_balanced(lens, **kw)
-    tiles = [max(1, math.ceil(L / 128)) for L in lens]
-    total = sum(tiles)
+    blocks = [max(1, math.ceil(L / 32)) for L in lens]
+    total = sum(blocks)
     assert len(off) == bins + 1 and off[0] == 0 and off[-1] == len(work)
-    # every bin holds floor or ceil of total / bins tiles, contiguous in sequence order
-    loads = [sum(w[2] - w[1] for w in work[off[i]:off[i + 1]]) for i in range(bins)]
+
+    def nblk(w):
+        return 1 if lens[w[0]] == 0 else math.ceil(w[2] / 32) - w[1] // 32
+
+    # every bin holds floor or ceil of total / bins blocks, contiguous in sequence order
+    loads = [sum(nblk(w) for w in work[off[i]:off[i + 1]]) for i in range(bins)]
     assert sum(loads) == total and max(loads) - min(loads) <= 1
-    flat = [(w[0], t) for w in work for t in range(w[1], w[2])]
-    assert flat == [(s, t) for s in range(len(tiles)) for t in range(tiles[s])]
-    # split slots count up per sequence; n_splits matches; within the cap
-    for s in range(len(tiles)):
+    # the items of a sequence tile [0, L) in key order, cut at multiples of 32
+    for s in range(len(lens)):
         items = [w for w in work if w[0] == s]
+        assert items[0][1] == 0 and items[-1][2] == lens[s]
+        assert all(a[2] == c[1] for a, c in zip(items, items[1:]))
+        assert all(w[1] % 32 == 0 and (w[2] % 32 == 0 or w[2] == lens[s]) for w in items)
+        assert all(w[2] > w[1] for w in items) or lens[s] == 0
+        # split slots count up per sequence; n_splits matches
         assert [w[3] for w in items] == list(range(len(items))) and ns[s] == len(items)
+    # items appear in global order (bin by bin, sequence order inside a bin)
+    assert [(w[0], w[1]) for w in work] == sorted((w[0], w[1]) for w in work)
     assert max(ns) <= kw["max_splits"]
     assert bins <= max(1, 256 * kw["wg_per_cu"] // (kw["h_k"] * kw["n_q_tiles"]))
