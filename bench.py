@@ -67,13 +67,21 @@ def algorithmic_bytes(batch, dec):
                 total=kv + q + bt + out_direct + out_split)
 
 
-def measured_traffic(workload_name):
+def profile_key(w, default_q_len):
+    """Name of a workload in the committed counter summaries: the workload's
+    name, with the query length when it is not the workload's own."""
+    return w.name if w.q_len == default_q_len else f"{w.name}_q{w.q_len}"
+
+
+def measured_traffic(kernel, key):
     """HBM bytes per decode launch from the committed counter summary of this
-    workload, or None if there is none or the kernel source changed since."""
+    kernel and workload, or None if there is none or the kernel source changed
+    since it was taken."""
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", f"gqa_decode_{workload_name}_hbm_bytes.md")
-    src = os.path.join(ROOT, "paged_kv_fp8_amd", "csrc", "decode_gqa.hip")
+    source = {"gqa_decode_kernel": "decode_gqa.hip", "mla_decode_kernel": "decode_mla.hip"}[kernel]
+    path = os.path.join(ROOT, "profiles", f"{kernel.replace('_kernel', '')}_{key}_hbm_bytes.md")
+    src = os.path.join(ROOT, "paged_kv_fp8_amd", "csrc", source)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -183,7 +191,11 @@ def main():
         over["contiguous_pages"] = True
     if args.seq_len:
         over["seq_len_dist"] = ("fixed", [args.seq_len] * workload(args.config).num_seqs)
+    base = workload(args.config)
     w = workload(args.config, **over)
+    # counter summaries are taken on the workloads as defined (query length aside)
+    as_profiled = (set(over) <= {"q_len"} and not args.pools and args.wg_per_cu is None and args.plan == "wave"
+                   and not args.fused_merge)
     torch.cuda.set_device(0)
     first = make_batch(w, device="cuda")
     pools = args.pools or min(64, max(3, -(-(1 << 30) // max(1, first.kv_bytes))))
@@ -245,7 +257,7 @@ def main():
     else:
         roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": measured_traffic(w.name) if kernel == "gqa_decode_kernel" else None}
+                    "traffic": measured_traffic(kernel, profile_key(w, base.q_len)) if as_profiled else None}
     roofline.update({"kernel": kernel, "kernel_us": round(dec_ms * 1e3, 2), "algorithmic_bytes_per_launch": ab["total"],
                      "algorithmic_flops_per_launch": ab["flops"], "merge_us": round(mrg_ms * 1e3, 2)})
     line = {
