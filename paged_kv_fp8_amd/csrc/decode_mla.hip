@@ -53,6 +53,7 @@ constexpr int kBlockKeys = 16;  // keys per main-loop step
 constexpr int kStages = 2;
 constexpr int kMaxWaves = 4;    // 16-row waves per workgroup
 constexpr int kQSteps = 18;     // 16 latent + 2 rope k-steps of 32
+constexpr float kLazyLog2 = 8.0f;  // bf16 P: reference max may lag until p would exceed 2^8
 
 struct MlaParams {
   const uint8_t* q;
@@ -239,9 +240,13 @@ __device__ __forceinline__ void mla_decode_item(const MlaParams& p, int item, in
           if (kb + 4 * g4 + i > lim) sv[i] = -INFINITY;
       }
       // ---- online softmax ---------------------------------------------------
+      // bf16 P: the reference max may lag until p would exceed 2^kLazyLog2
+      // (O lives in AGPRs, so a rescale is a full read-multiply-write pass)
       float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
       mx = pair32(pair16(mx, true), true);
-      const float m_new = fmaxf(m_run, mx);
+      const float m_max = fmaxf(m_run, mx);
+      const bool move = m_run == -INFINITY ? m_max != -INFINITY : (m_max - m_run) * c2 > kLazyLog2;
+      const float m_new = move ? m_max : m_run;
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float corr = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
       float pr[4], psum = 0.f;
@@ -250,7 +255,7 @@ __device__ __forceinline__ void mla_decode_item(const MlaParams& p, int item, in
         psum += pr[i];
       }
       l_part = l_part * corr + psum;
-      if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
+      if (__builtin_amdgcn_ballot_w64(move)) {
         for (int gr = 0; gr < 4; ++gr)
           for (int mt = 0; mt < 8; ++mt) oacc[gr][mt] *= corr;
       }
@@ -344,14 +349,327 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mla_decode_kernel(MlaParams p)
   for (; it < it_end; ++it) mla_decode_item<CAUSAL_TAIL>(p, it, lane, row0);
 }
 
-const void* select_kernel(bool causal_tail) {
-  return causal_tail ? reinterpret_cast<const void*>(&mla_decode_kernel<true>)
-                     : reinterpret_cast<const void*>(&mla_decode_kernel<false>);
+
+// ---- multi-token form: records staged once per workgroup ---------------------
+// From 64 query rows on, the latent records of each 32-key block are
+// dequantised ONCE per workgroup into LDS (double-buffered) as bf16 key rows
+// (512 latent codes, exact, then the 64 bf16 rope values) plus the block
+// scales. Both MFMA operands come from there:
+//  * QK^T reads 16-byte pieces of the key rows (keys on M, two 16-key tiles);
+//  * PV reads V^T straight from the same rows with the LDS transpose load
+//    (ds_read_b64_tr_b16): within each 16-lane group, lane i receives element
+//    i % 4 of the 8-byte reads of lanes i/4 + 4k (k = 0..3), so when lane j of
+//    group g4 reads V[key k0 + 4 g4 + j/4][d + 4 (j % 4) ..], lane i holds
+//    V[keys k0 + 4 g4 .. +3][d + i]. Two such reads (k0 = 0 and 16) give the
+//    8 keys of a 16x16x32 A operand in the order in which the QK^T
+//    accumulators hold P (keys 4 g4 + i of each tile), so P needs no lane
+//    exchange.
+// Eight waves (two per SIMD): wave w owns query rows 16 (w & 3) .. +15 of the
+// tile and d_v half w >> 2 (64 accumulator registers); the two waves of a row
+// group both compute S, so their softmax statistics agree bit for bit. The
+// 512 threads split a block's loads (32 latent bytes, one rope pair of dwords
+// and one scale dword each), three blocks ahead of the math in a register
+// ring; one barrier per block: a stage is written one block before it is read
+// and read one block before it is rewritten.
+constexpr int kLdsWaves = 8;
+constexpr int kLdsRows = 64;                            // query rows per workgroup
+constexpr int kStageKeys = 32;                          // keys per step
+constexpr int kKRowBytes = 2 * (kLatent + kRope) + 16;  // bf16 key row + 16 B, so rows sit 4 banks apart
+constexpr int kStageK = 0;
+constexpr int kStageScl = kStageKeys * kKRowBytes;
+constexpr int kStageBytes = kStageScl + kStageKeys * 16;
+constexpr int kRing = 3;  // raw blocks per thread: block j+2 is loaded while block j is processed
+
+struct RawPiece {
+  uint4 lat[2];  // key t >> 4: latent bytes 32 (t & 15) .. +31
+  uint2 rope;    // key t >> 4: rope bytes 8 (t & 15) .. +7
+  float scl;     // key (t & 127) >> 2: scale t & 3
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) uint8_t*)p);
+}
+
+template <bool CAUSAL_TAIL>
+__device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int tile, uint8_t* lds) {
+  const int t = threadIdx.x;
+  const int w = t >> 6;
+  const int lane = t & 63;
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+  const int half = w >> 2;  // d_v 256 half .. 256 half + 255
+
+  const int4 wk = p.work[item];
+  const int b = wk.x;
+  if (wk.z <= wk.y || b < 0 || b >= p.num_seqs) return;  // the whole workgroup returns
+  const int ns = p.n_splits[b];
+  const bool direct = ns <= 1;
+  const int slot = wk.w;
+  if (!direct && (slot < 0 || slot >= p.max_splits)) return;
+
+  const int page_size = 1 << p.page_shift;
+  int L = p.seq_lens[b];
+  L = max(0, min(L, p.max_blocks * page_size));
+  const int k_begin = p.bin_offsets ? wk.y : wk.y * kTileKeys;
+  const int k_end = min(p.bin_offsets ? wk.z : wk.z * kTileKeys, L);
+
+  // rows of this wave: n = row0 + r16; a wave past the last row still loads,
+  // stages and meets every barrier
+  const int row0 = tile * kLdsRows + 16 * (w & 3);
+  const bool wave_rows = row0 < p.rows;
+  const int n = row0 + r16;
+  const bool row_ok = n < p.rows;
+  const int qi = n / p.h_q;
+  const int qtok = b * p.q_len + qi;
+  const int qhead = n - qi * p.h_q;
+  const int lim = min(CAUSAL_TAIL ? L - p.q_len + qi : L - 1, k_end - 1);
+  const int qi_min = row0 / p.h_q;
+  const int lim_min = min(CAUSAL_TAIL ? L - p.q_len + qi_min : L - 1, k_end - 1);
+  const float c2 = p.scale_log2e;
+
+  // Q as the B operand: k-step k holds q[n][32k + 8 g4 .. +7] (latent k < 16,
+  // then rope), the natural order of the bf16 key rows in LDS
+  bf16x8 qv[kQSteps];
+  {
+    const uint8_t* qrow = p.q + (int64_t)qtok * p.q_tok + (int64_t)qhead * p.q_head;
+    for (int k = 0; k < kQSteps; ++k) {
+      if (row_ok) {
+        qv[k] = *reinterpret_cast<const bf16x8*>(qrow + 2 * (32 * k + 8 * g4));
+      } else {
+        for (int e = 0; e < 8; ++e) qv[k][e] = (__bf16)0.0f;
+      }
+    }
+  }
+
+  f32x4 oacc[2][8];  // [128-block gg of this half][16-row tile mt]: O^T[256 half + 128 gg + 16 mt + 4 g4 + i][n]
+  for (int gg = 0; gg < 2; ++gg)
+    for (int mt = 0; mt < 8; ++mt) oacc[gg][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
+
+  if (k_end > k_begin) {
+    const int32_t* bt = p.block_table + (int64_t)b * p.bt_row;
+    const int last_key = k_end - 1;
+    const int pmask = page_size - 1;
+    // pages of a 32-key block's two 16-key halves (page_size >= 16): lanes 0 / 1
+    auto page_pair = [&](int kb) -> int { return bt[min(kb + 16 * (lane & 1), last_key) >> p.page_shift]; };
+    auto clamp_page = [&](int pg) -> int { return min(max(pg, 0), p.num_pages - 1); };
+
+    // fetch u: the loads of block k_begin + 32u into ring slot u % kRing, with
+    // the pages from page slot u % kRing (loaded two fetches earlier); it
+    // loads the pages of fetch u + 2. Waves 0-3 load keys 0-15 (latent, rope),
+    // waves 4-7 keys 16-31; even waves load the scales of keys 0-15, odd
+    // waves those of keys 16-31, so each wave reads one page per load.
+    int pv[kRing];
+    pv[0] = page_pair(k_begin);
+    pv[1] = page_pair(k_begin + kStageKeys);
+    auto fetch = [&](RawPiece& r, int kb, const int s) {
+      const int pg0 = clamp_page(__builtin_amdgcn_readlane(pv[s], 0));
+      const int pg1 = clamp_page(__builtin_amdgcn_readlane(pv[s], 1));
+      const int pgk = (w >> 2) ? pg1 : pg0;
+      const int key = min(kb + (t >> 4), last_key) & pmask;
+      const uint8_t* lat = p.lat + (int64_t)pgk * p.lat_page + (int64_t)key * p.lat_row + 32 * (t & 15);
+      r.lat[0] = *reinterpret_cast<const uint4*>(lat);
+      r.lat[1] = *reinterpret_cast<const uint4*>(lat + 16);
+      r.rope = *reinterpret_cast<const uint2*>(p.rope + (int64_t)pgk * p.rope_page + (int64_t)key * p.rope_row +
+                                               8 * (t & 15));
+      const int pgs = (w & 1) ? pg1 : pg0;
+      const int skey = min(kb + ((t & 127) >> 2), last_key) & pmask;
+      r.scl = *reinterpret_cast<const float*>(p.scl + (int64_t)pgs * p.scl_page + (int64_t)skey * p.scl_row +
+                                              4 * (t & 3));
+      pv[(s + 2) % kRing] = page_pair(kb + 2 * kStageKeys);
+    };
+    auto stage_in = [&](const RawPiece& r, uint8_t* st) {
+      uint8_t* krow = st + kStageK + (t >> 4) * kKRowBytes;
+      *reinterpret_cast<bf16x8*>(krow + 64 * (t & 15)) = e4m3x8_to_bf16(uint2{r.lat[0].x, r.lat[0].y});
+      *reinterpret_cast<bf16x8*>(krow + 64 * (t & 15) + 16) = e4m3x8_to_bf16(uint2{r.lat[0].z, r.lat[0].w});
+      *reinterpret_cast<bf16x8*>(krow + 64 * (t & 15) + 32) = e4m3x8_to_bf16(uint2{r.lat[1].x, r.lat[1].y});
+      *reinterpret_cast<bf16x8*>(krow + 64 * (t & 15) + 48) = e4m3x8_to_bf16(uint2{r.lat[1].z, r.lat[1].w});
+      *reinterpret_cast<uint2*>(krow + 2 * kLatent + 8 * (t & 15)) = r.rope;
+      if (t < 128) *reinterpret_cast<float*>(st + kStageScl + 4 * t) = r.scl;
+    };
+    auto barrier = [&]() {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+
+    auto compute = [&](const uint8_t* st, int kb) {
+      // ---- S = K Q^T per 16-key tile tt: one accumulator per 128-value block + rope
+      float sv[2][4];
+      float sp[2][2][4];  // [gg][tt][i]: scale of this wave's d_v block 2 half + gg for key 16 tt + 4 g4 + i
+      for (int tt = 0; tt < 2; ++tt) {
+        const uint8_t* krow = st + kStageK + (16 * tt + r16) * kKRowBytes + 16 * g4;
+        f32x4 acc[4], accr = {0.f, 0.f, 0.f, 0.f};
+        for (int blk = 0; blk < 4; ++blk) {
+          acc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int s = 0; s < 4; ++s) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 2 * (128 * blk + 32 * s));
+            acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qv[4 * blk + s], acc[blk], 0, 0, 0);
+          }
+        }
+        for (int r = 0; r < 2; ++r) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 2 * (kLatent + 32 * r));
+          accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qv[16 + r], accr, 0, 0, 0);
+        }
+        // lane holds S[key kb + 16 tt + 4 g4 + i][row n]
+        for (int i = 0; i < 4; ++i) {
+          const float4 sc = *reinterpret_cast<const float4*>(st + kStageScl + 16 * (16 * tt + 4 * g4 + i));
+          sv[tt][i] = accr[i] + sc.x * acc[0][i] + sc.y * acc[1][i] + sc.z * acc[2][i] + sc.w * acc[3][i];
+          sp[0][tt][i] = half ? sc.z : sc.x;
+          sp[1][tt][i] = half ? sc.w : sc.y;
+        }
+      }
+      if (kb + kStageKeys - 1 > lim_min) {
+        for (int tt = 0; tt < 2; ++tt)
+          for (int i = 0; i < 4; ++i)
+            if (kb + 16 * tt + 4 * g4 + i > lim) sv[tt][i] = -INFINITY;
+      }
+      // ---- online softmax (bf16 P: the reference max may lag) -----------------
+      float mx = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
+                       fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
+      mx = pair32(pair16(mx, true), true);
+      const float m_max = fmaxf(m_run, mx);
+      const bool move = m_run == -INFINITY ? m_max != -INFINITY : (m_max - m_run) * c2 > kLazyLog2;
+      const float m_new = move ? m_max : m_run;
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float corr = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
+      float pr[2][4], psum = 0.f;
+      for (int tt = 0; tt < 2; ++tt)
+        for (int i = 0; i < 4; ++i) {
+          pr[tt][i] = __builtin_amdgcn_exp2f((sv[tt][i] - m_use) * c2);
+          psum += pr[tt][i];
+        }
+      l_part = l_part * corr + psum;
+      if (__builtin_amdgcn_ballot_w64(move)) {
+        for (int gg = 0; gg < 2; ++gg)
+          for (int mt = 0; mt < 8; ++mt) oacc[gg][mt] *= corr;
+      }
+      m_run = m_new;
+      // ---- O^T += V^T (P * scale)^T for this wave's 256 d_v ------------------
+      // k-slot e of lane group g4: key 4 g4 + e (e < 4) or 16 + 4 g4 + e - 4
+      const uint8_t* vrow = st + kStageK + (4 * g4 + (r16 >> 2)) * kKRowBytes + 8 * (r16 & 3) + 512 * half;
+      for (int gg = 0; gg < 2; ++gg) {
+        bf16x8 pb;  // P scaled by the block scale of d_v block 2 half + gg
+        for (int tt = 0; tt < 2; ++tt)
+          for (int i = 0; i < 4; ++i) pb[4 * tt + i] = (__bf16)(pr[tt][i] * sp[gg][tt][i]);
+        for (int mt = 0; mt < 8; ++mt) {
+          const s16x4 lo = lds_read_tr16(vrow + 256 * gg + 32 * mt);
+          const s16x4 hi = lds_read_tr16(vrow + 16 * kKRowBytes + 256 * gg + 32 * mt);
+          const s16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          bf16x8 a;
+          __builtin_memcpy(&a, &a16, 16);
+          oacc[gg][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, oacc[gg][mt], 0, 0, 0);
+        }
+      }
+    };
+
+    // Block j: fetched at step j - (kRing - 1), staged into LDS stage j % 2 at
+    // step j - 1, processed at step j. Rounds of 2 kRing steps keep the ring
+    // and stage indices compile-time; steps past the last block fetch clamped
+    // rows, stage them and skip the math, so every wave runs the same loads
+    // and barriers.
+    constexpr int kRound = 2 * kRing;
+    const int nblocks = (k_end - k_begin + kStageKeys - 1) / kStageKeys;
+    RawPiece ring[kRing];
+#pragma unroll
+    for (int u = 0; u < kRing - 1; ++u) fetch(ring[u], k_begin + u * kStageKeys, u);
+    stage_in(ring[0], lds);
+    barrier();
+    const int rounds = (nblocks + kRound - 1) / kRound;
+    for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+      for (int s = 0; s < kRound; ++s) {
+        const int j = r * kRound + s;
+        const int kb = k_begin + j * kStageKeys;
+        fetch(ring[(s + kRing - 1) % kRing], kb + (kRing - 1) * kStageKeys, (s + kRing - 1) % kRing);
+        stage_in(ring[(s + 1) % kRing], lds + ((s + 1) & 1) * kStageBytes);
+        if (wave_rows && j < nblocks) compute(lds + (s & 1) * kStageBytes, kb);
+        barrier();
+      }
+    }
+  }
+
+  // ---- epilogue: this wave's d_v half; LSE / (max, sum) from the first half -------
+  const float l = pair32(pair16(l_part, false), false);
+  if (!row_ok) return;
+  const int64_t stat_row = (int64_t)b * p.rows + n;
+  const float m_nat = m_run == -INFINITY ? -INFINITY : m_run * p.scale;
+  const int d0 = 256 * half + 4 * g4;
+  if (direct) {
+    const float inv = l > 0.f ? p.o_scale / l : 0.f;
+    uint8_t* orow = p.o + (int64_t)qtok * p.o_tok + (int64_t)qhead * p.o_head;
+    for (int gg = 0; gg < 2; ++gg)
+      for (int mt = 0; mt < 8; ++mt) {
+        bf16x4 out;
+        for (int i = 0; i < 4; ++i) out[i] = (__bf16)(oacc[gg][mt][i] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 2 * (d0 + 128 * gg + 16 * mt)) = out;
+      }
+    if (half == 0 && g4 == 0) p.lse[stat_row] = l > 0.f ? m_nat + logf(l) : -INFINITY;
+  } else {
+    const int64_t prow = (int64_t)slot * p.num_seqs * p.rows + stat_row;
+    float* dst = p.ws_o + prow * kDv + d0;
+    for (int gg = 0; gg < 2; ++gg)
+      for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(dst + 128 * gg + 16 * mt) = oacc[gg][mt];
+    if (half == 0 && g4 == 0) p.ws_ml[prow] = float2{m_nat, l};
+  }
+}
+
+// XCD-aware grid: the workgroups of one work item's q-row tiles read the same
+// records, so they are placed on one XCD (sharing its L2) at about the same
+// time. Workgroups are dispatched to the 8 XCDs round robin, so ids i, i + 8,
+// i + 16, ... share an XCD: a chunk of 8 * tiles consecutive ids holds 8
+// items x tiles, with the item varying fastest (the last chunk holds what is
+// left).
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ void xcd_item_tile(int id, int units, int tiles, int& unit, int& tile) {
+  const int chunk = id / (kXcds * tiles);
+  const int local = id - chunk * kXcds * tiles;
+  const int left = min(kXcds, units - chunk * kXcds);
+  unit = chunk * kXcds + local % left;
+  tile = local / left;
+}
+
+template <bool CAUSAL_TAIL>
+__global__ __launch_bounds__(64 * kLdsWaves) void mla_lds_kernel(MlaParams p, int units, int tiles) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t mla_stage_lds[];
+  int unit, tile;
+  xcd_item_tile(blockIdx.x, units, tiles, unit, tile);
+  int it = unit, it_end = unit + 1;
+  if (p.bin_offsets) {
+    it = p.bin_offsets[unit];
+    it_end = p.bin_offsets[unit + 1];
+  }
+  for (; it < it_end; ++it) {
+    mla_lds_item<CAUSAL_TAIL>(p, it, tile, mla_stage_lds);
+    __syncthreads();  // the next item's first stage overwrites LDS
+  }
+}
+
+// rows >= 64: the staged form; fewer rows: one 16-row wave per record stream
+bool staged(const pkv_decode_args& a) { return a.q_len * a.h_q >= kLdsRows; }
+
+const void* select_kernel(const pkv_decode_args& a) {
+  const bool ct = a.causal && a.q_len > 1;
+  if (staged(a))
+    return ct ? reinterpret_cast<const void*>(&mla_lds_kernel<true>)
+              : reinterpret_cast<const void*>(&mla_lds_kernel<false>);
+  return ct ? reinterpret_cast<const void*>(&mla_decode_kernel<true>)
+            : reinterpret_cast<const void*>(&mla_decode_kernel<false>);
 }
 
 int waves_per_wg(const pkv_decode_args& a) {
+  if (staged(a)) return kLdsWaves;
   const int blocks = (a.q_len * a.h_q + 15) / 16;
   return blocks < kMaxWaves ? blocks : kMaxWaves;
+}
+
+size_t dyn_lds_bytes(const pkv_decode_args& a) {
+  return staged(a) ? (size_t)2 * kStageBytes : (size_t)waves_per_wg(a) * kQSteps * 64 * 16;
 }
 
 int log2_exact(int x) {
@@ -362,13 +680,12 @@ int log2_exact(int x) {
 
 }  // namespace
 
-int mla_rows_per_tile(const pkv_decode_args& a) { return 16 * waves_per_wg(a); }
+int mla_rows_per_tile(const pkv_decode_args& a) { return staged(a) ? kLdsRows : 16 * waves_per_wg(a); }
 
 hipError_t mla_occupancy(const pkv_decode_args& a, int* units_per_cu) {
   // one unit = one workgroup (all rows of one q-row tile of a work item)
-  const int wpw = waves_per_wg(a);
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(units_per_cu, select_kernel(a.causal && a.q_len > 1), 64 * wpw,
-                                                      (size_t)wpw * kQSteps * 64 * 16);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(units_per_cu, select_kernel(a), 64 * waves_per_wg(a),
+                                                      dyn_lds_bytes(a));
 }
 
 hipError_t mla_launch(const pkv_decode_args& a, hipStream_t stream) {
@@ -410,11 +727,16 @@ hipError_t mla_launch(const pkv_decode_args& a, hipStream_t stream) {
   p.max_blocks = a.max_blocks;
   p.max_splits = a.max_splits;
   const int wpw = waves_per_wg(a);
-  const int tiles = (p.rows + 16 * wpw - 1) / (16 * wpw);
-  dim3 grid(a.bin_offsets ? a.num_bins : a.num_work, tiles, 1);
+  int tiles = (p.rows + mla_rows_per_tile(a) - 1) / mla_rows_per_tile(a);
+  int units = a.bin_offsets ? a.num_bins : a.num_work;
+  if (staged(a)) {
+    void* args[] = {&p, &units, &tiles};
+    return hipLaunchKernel(select_kernel(a), dim3((unsigned)(units * tiles)), dim3(64 * wpw), args,
+                           dyn_lds_bytes(a), stream);
+  }
   void* args[] = {&p};
-  return hipLaunchKernel(select_kernel(a.causal && a.q_len > 1), grid, dim3(64 * wpw), args,
-                         (size_t)wpw * kQSteps * 64 * 16, stream);
+  return hipLaunchKernel(select_kernel(a), dim3((unsigned)units, (unsigned)tiles), dim3(64 * wpw), args,
+                         dyn_lds_bytes(a), stream);
 }
 
 }  // namespace pkv

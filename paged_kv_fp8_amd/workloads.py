@@ -93,7 +93,7 @@ WORKLOADS = {
     4: Workload("fp8_b128_hq64_hk4_d128_ps128_mix1k-4k_32k-64k", 128, 1, 64, 4, 128, 128, 128,
                 ("mix", 0.1, (32768, 65536), (1024, 4096)), max_splits=64, q_format="e4m3", seed=1115),
     5: Workload("mla_b32_hq16_hk1_d576-512_ps64_L2k-16k", 32, 1, 16, 1, 576, 512, 64,
-                ("uniform", 2048, 16384), max_splits=16, kv_format="mla", seed=1116),
+                ("uniform", 2048, 16384), max_splits=64, kv_format="mla", seed=1116),
 }
 
 

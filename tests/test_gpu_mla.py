@@ -36,7 +36,8 @@ def compare(batch, dec, seqs=None, what=""):
     return assert_matches(o_g, lse_g, o_ref, lse_ref, max_abs_v(nb, spec, seqs), what=what)
 
 
-@pytest.mark.parametrize("T,causal", [(1, True), (2, True), (4, True), (4, False), (8, True), (16, True)])
+@pytest.mark.parametrize("T,causal", [(1, True), (2, True), (3, True), (4, True), (4, False), (5, True), (5, False),
+                                      (8, True), (16, True)])
 def test_small_latent_every_output(T, causal):
     w = workload(5, q_len=T, causal=causal, num_seqs=4, seq_len_dist=("uniform", 40, 700))
     batch = make_batch(w, device="cuda")
@@ -61,7 +62,7 @@ def test_full_latent_sampled(T):
 EDGE = [0, 1, 2, 15, 16, 17, 63, 64, 65, 127, 128, 129, 1000]
 
 
-@pytest.mark.parametrize("T,force", [(1, 0), (2, 3), (4, 2)])
+@pytest.mark.parametrize("T,force", [(1, 0), (2, 3), (4, 2), (8, 0), (8, 5)])
 def test_latent_edge_lengths(T, force):
     w = workload(5, q_len=T, num_seqs=len(EDGE), seq_len_dist=("fixed", EDGE), max_splits=8)
     batch = make_batch(w, device="cuda")
@@ -69,8 +70,10 @@ def test_latent_edge_lengths(T, force):
     compare(batch, dec, what=f"latent edge T={T} force={force}")
 
 
-def test_latent_repeat_bitwise():
-    w = workload(5, q_len=2, num_seqs=6, seq_len_dist=("uniform", 100, 3000))
+@pytest.mark.parametrize("T", [2, 8])
+def test_latent_repeat_bitwise(T):
+    # T = 2: one 16-row wave per record stream; T = 8: records staged in LDS for four waves
+    w = workload(5, q_len=T, num_seqs=6, seq_len_dist=("uniform", 100, 3000))
     batch = make_batch(w, device="cuda")
     dec = run_batch(batch)
     o1, l1 = dec.o.clone(), dec.lse.clone()
@@ -88,3 +91,30 @@ def test_latent_balanced_plan(T):
     batch = make_batch(w, device="cuda")
     dec = run_batch(batch, plan="balanced")
     compare(batch, dec, what=f"latent balanced T={T}")
+
+
+@pytest.mark.parametrize("h_q,T", [(8, 8), (8, 12), (32, 2), (32, 3)])
+def test_latent_other_head_counts(h_q, T):
+    # rows = T * h_q: 64, 96 (a part-filled second tile), 64, 96 with the staged form
+    w = workload(5, q_len=T, h_q=h_q, num_seqs=5, seq_len_dist=("uniform", 30, 2500))
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch)
+    compare(batch, dec, what=f"latent h_q={h_q} T={T}")
+
+
+def test_latent_staged_graph_replay():
+    w = workload(5, q_len=8, num_seqs=6, seq_len_dist=("uniform", 200, 5000))
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch)
+    eager_o, eager_l = dec.o.clone(), dec.lse.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dec.run()
+    for rep in range(3):
+        dec.o.zero_()
+        dec.lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dec.o.view(torch.int16), eager_o.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(dec.lse.view(torch.int32), eager_l.view(torch.int32)), f"replay {rep}"
