@@ -374,17 +374,28 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mla_decode_kernel(MlaParams p)
 constexpr int kLdsWaves = 8;
 constexpr int kLdsRows = 64;                            // query rows per workgroup
 constexpr int kStageKeys = 32;                          // keys per step
-constexpr int kKRowBytes = 2 * (kLatent + kRope) + 16;  // bf16 key row + 16 B, so rows sit 4 banks apart
+// bf16 key row + 32 B: rows sit 8 banks apart, and the 16-byte pieces of rows
+// 4..7 (mod 8) are swapped in pairs (piece q -> q ^ 1), so 8 rows read at one
+// column (the QK^T pieces) and 4 rows read 32 contiguous bytes each (the
+// transpose loads) both hit distinct banks
+constexpr int kKRowBytes = 2 * (kLatent + kRope) + 32;
 constexpr int kStageK = 0;
 constexpr int kStageScl = kStageKeys * kKRowBytes;
 constexpr int kStageBytes = kStageScl + kStageKeys * 16;
 constexpr int kRing = 3;  // raw blocks per thread: block j+2 is loaded while block j is processed
 
 struct RawPiece {
-  uint4 lat[2];  // key t >> 4: latent bytes 32 (t & 15) .. +31
+  uint2 lat[4];  // key t >> 4: latent bytes 128 i + 8 (t & 15) .. +7
   uint2 rope;    // key t >> 4: rope bytes 8 (t & 15) .. +7
   float scl;     // key (t & 127) >> 2: scale t & 3
 };
+
+// Byte offset of byte `lane_off + c` of key row `row` in a stage (see
+// kKRowBytes) is krow_base(row, lane_off) + c for every c whose bit 4 is
+// clear (all the constant parts of the offsets below are multiples of 32).
+__device__ __forceinline__ int krow_base(int row, int lane_off) {
+  return row * kKRowBytes + (lane_off ^ (((row >> 2) & 1) << 4));
+}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -471,9 +482,8 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
       const int pg1 = clamp_page(__builtin_amdgcn_readlane(pv[s], 1));
       const int pgk = (w >> 2) ? pg1 : pg0;
       const int key = min(kb + (t >> 4), last_key) & pmask;
-      const uint8_t* lat = p.lat + (int64_t)pgk * p.lat_page + (int64_t)key * p.lat_row + 32 * (t & 15);
-      r.lat[0] = *reinterpret_cast<const uint4*>(lat);
-      r.lat[1] = *reinterpret_cast<const uint4*>(lat + 16);
+      const uint8_t* lat = p.lat + (int64_t)pgk * p.lat_page + (int64_t)key * p.lat_row + 8 * (t & 15);
+      for (int i = 0; i < 4; ++i) r.lat[i] = *reinterpret_cast<const uint2*>(lat + 128 * i);
       r.rope = *reinterpret_cast<const uint2*>(p.rope + (int64_t)pgk * p.rope_page + (int64_t)key * p.rope_row +
                                                8 * (t & 15));
       const int pgs = (w & 1) ? pg1 : pg0;
@@ -482,13 +492,12 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
                                               4 * (t & 3));
       pv[(s + 2) % kRing] = page_pair(kb + 2 * kStageKeys);
     };
+    // each store of a 16-lane group covers 256 contiguous bytes of one row
+    const int st_lat = kStageK + krow_base(t >> 4, 16 * (t & 15));
+    const int st_rope = kStageK + krow_base(t >> 4, 8 * (t & 15)) + 2 * kLatent;
     auto stage_in = [&](const RawPiece& r, uint8_t* st) {
-      uint8_t* krow = st + kStageK + (t >> 4) * kKRowBytes;
-      *reinterpret_cast<bf16x8*>(krow + 64 * (t & 15)) = e4m3x8_to_bf16(uint2{r.lat[0].x, r.lat[0].y});
-      *reinterpret_cast<bf16x8*>(krow + 64 * (t & 15) + 16) = e4m3x8_to_bf16(uint2{r.lat[0].z, r.lat[0].w});
-      *reinterpret_cast<bf16x8*>(krow + 64 * (t & 15) + 32) = e4m3x8_to_bf16(uint2{r.lat[1].x, r.lat[1].y});
-      *reinterpret_cast<bf16x8*>(krow + 64 * (t & 15) + 48) = e4m3x8_to_bf16(uint2{r.lat[1].z, r.lat[1].w});
-      *reinterpret_cast<uint2*>(krow + 2 * kLatent + 8 * (t & 15)) = r.rope;
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<bf16x8*>(st + st_lat + 256 * i) = e4m3x8_to_bf16(r.lat[i]);
+      *reinterpret_cast<uint2*>(st + st_rope) = r.rope;
       if (t < 128) *reinterpret_cast<float*>(st + kStageScl + 4 * t) = r.scl;
     };
     auto barrier = [&]() {
@@ -497,12 +506,17 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     };
 
+    // this lane's QK^T piece (key row r16 of a tile, bytes 16 g4 ..) and
+    // transpose-read piece (key row 4 g4 + r16 / 4, bytes 8 (r16 % 4) ..);
+    // rows 16 apart share the swizzle
+    const int qk_base = krow_base(r16, 16 * g4);
+    const int tr_base = krow_base(4 * g4 + (r16 >> 2), 8 * (r16 & 3));
     auto compute = [&](const uint8_t* st, int kb) {
       // ---- S = K Q^T per 16-key tile tt: one accumulator per 128-value block + rope
       float sv[2][4];
       float sp[2][2][4];  // [gg][tt][i]: scale of this wave's d_v block 2 half + gg for key 16 tt + 4 g4 + i
       for (int tt = 0; tt < 2; ++tt) {
-        const uint8_t* krow = st + kStageK + (16 * tt + r16) * kKRowBytes + 16 * g4;
+        const uint8_t* krow = st + kStageK + qk_base + tt * 16 * kKRowBytes;
         f32x4 acc[4], accr = {0.f, 0.f, 0.f, 0.f};
         for (int blk = 0; blk < 4; ++blk) {
           acc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -551,14 +565,14 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
       m_run = m_new;
       // ---- O^T += V^T (P * scale)^T for this wave's 256 d_v ------------------
       // k-slot e of lane group g4: key 4 g4 + e (e < 4) or 16 + 4 g4 + e - 4
-      const uint8_t* vrow = st + kStageK + (4 * g4 + (r16 >> 2)) * kKRowBytes + 8 * (r16 & 3) + 512 * half;
       for (int gg = 0; gg < 2; ++gg) {
         bf16x8 pb;  // P scaled by the block scale of d_v block 2 half + gg
         for (int tt = 0; tt < 2; ++tt)
           for (int i = 0; i < 4; ++i) pb[4 * tt + i] = (__bf16)(pr[tt][i] * sp[gg][tt][i]);
         for (int mt = 0; mt < 8; ++mt) {
-          const s16x4 lo = lds_read_tr16(vrow + 256 * gg + 32 * mt);
-          const s16x4 hi = lds_read_tr16(vrow + 16 * kKRowBytes + 256 * gg + 32 * mt);
+          const uint8_t* v = st + kStageK + tr_base + 512 * half + 256 * gg + 32 * mt;
+          const s16x4 lo = lds_read_tr16(v);
+          const s16x4 hi = lds_read_tr16(v + 16 * kKRowBytes);
           const s16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           bf16x8 a;
           __builtin_memcpy(&a, &a16, 16);
