@@ -25,6 +25,8 @@ Modules
   merge     LSE merge of split partials (the split-KV combine rule).
   plan      the occupancy-pinned split-KV planner (integer algorithm).
   brute     pure-Python loop version of the attention for tiny inputs.
+  producers e4m3 encoding (round to nearest even, saturating), the query
+            quantisation and the paged KV-cache write (e4m3 and latent).
 
 Pin status of each function is recorded in its docstring; every function
 here is pinned by a ``-m "not gpu"`` test in ``tests/test_oracle.py`` or
