@@ -287,6 +287,99 @@ pkv_status pkv_paged_decode_attn(const pkv_decode_args* a, void* stream);
  */
 pkv_status pkv_merge_splits(const pkv_decode_args* a, void* stream);
 
+/* ---- producers either side of the decode ---------------------------------- */
+
+/*
+ * Query quantisation for the fully-fp8 path ("mjolnir-kernel 0.1.0 wheel:
+ * mjolnir/t5_decode.py", quantize_q_fp8). Per sequence b and kv head g:
+ *   amax = max(|q|) over the sequence's q_len tokens, the h_r = h_q / h_k
+ *          query heads g*h_r .. g*h_r + h_r - 1 and the d values (at least 1e-6)
+ *   q_descale[b][g] = amax / 448                                  (fp32)
+ *   q8 = e4m3 code of q / q_descale[b][g], round to nearest even  (fp32 division)
+ * so the largest |q| of each group maps to +-448. One launch, no workspace,
+ * no synchronisation (capturable).
+ *
+ * q          device bf16 [num_seqs * q_len][h_q][d]; strides in elements, d
+ *            contiguous; 16-B aligned, strides multiples of 8 elements
+ * q8         device uint8 (e4m3) of the same logical shape; strides in bytes,
+ *            multiples of 8, 8-B aligned; may not overlap q
+ * q_descale  device fp32 [num_seqs][h_k] with element strides (>= 0)
+ * Errors: INVALID_ARG for sizes < 1, h_q % h_k != 0, d not a multiple of 8,
+ * NULL or misaligned pointers, bad strides; HIP if the launch fails.
+ */
+typedef struct pkv_quant_q_args {
+  int32_t num_seqs, q_len, h_q, h_k, d;
+  const void* q;
+  int64_t q_tok_stride, q_head_stride;
+  uint8_t* q8;
+  int64_t q8_tok_stride, q8_head_stride;
+  float* q_descale;
+  int64_t qd_seq_stride, qd_head_stride;
+} pkv_quant_q_args;
+
+pkv_status pkv_quantize_q(const pkv_quant_q_args* a, void* stream);
+
+/* sizeof(pkv_quant_q_args) in this build (a binding's layout check) */
+size_t pkv_quant_q_args_size(void);
+
+/*
+ * Paged KV-cache write of the newest tokens (the "KV-cache write" that the
+ * t5_decode page names among the kernels before the decode, with the
+ * per-(sequence, kv head) e4m3 storage of its module docstring and harness;
+ * the latent record of "vLLM PR #62633", Kernel design). Token t (0 <= t <
+ * n_new) of sequence b is position pos = seq_lens[b] - n_new + t (seq_lens
+ * already count the new tokens); it is written to row pos % page_size of page
+ * block_table[b][pos / page_size]. Tokens with pos < 0, or whose block-table
+ * entry lies outside [0, num_pages), are skipped.
+ *   PKV_KV_E4M3: k[page][row][g][:] = e4m3(k_new[b*n_new + t][g][:] / k_descale[b][g]),
+ *                likewise v; round to nearest even, |x| beyond 448 saturates to
+ *                +-448, NaN gives 0x7F.
+ *   PKV_KV_MLA:  h_k = 1 and d = 576; per token and 128-value latent block j:
+ *                scale_j = max(amax_j, 1e-6) / 448, k_blk_scale[page][row][j] = scale_j,
+ *                k[page][row][128j + i] = e4m3(x[128j + i] / scale_j); the 64
+ *                rope values are copied bit for bit into k_rope. v_* unused.
+ * One launch, no workspace, no synchronisation (capturable). Tokens written
+ * by one call must map to distinct cache rows.
+ *
+ * k_new, v_new   device bf16 [num_seqs * n_new][h_k][d] (latent: [..][576],
+ *                head stride unused); element strides; 16-B aligned, strides
+ *                multiples of 8 elements, d contiguous
+ * k, v           device uint8 caches with byte strides (page, row, head),
+ *                8-B aligned, strides multiples of 8
+ * k_rope, k_blk_scale  (latent) element strides (page, row), 16-B aligned
+ * Errors: INVALID_ARG for sizes < 1, NULL or misaligned pointers, bad
+ * strides, d not a multiple of 8 (e4m3) or not 576 (latent); UNSUPPORTED for
+ * a page size outside {16, 32, 64, 128}; HIP if the launch fails.
+ */
+typedef struct pkv_kv_write_args {
+  int32_t num_seqs, n_new, h_k, d, page_size, num_pages, max_blocks;
+  int32_t kv_format; /* PKV_KV_* */
+  const void* k_new;
+  int64_t kn_tok_stride, kn_head_stride;
+  const void* v_new;
+  int64_t vn_tok_stride, vn_head_stride;
+  const int32_t* block_table;
+  int64_t bt_row_stride;
+  const int32_t* seq_lens;
+  const float* k_descale;
+  int64_t kd_seq_stride, kd_head_stride;
+  const float* v_descale;
+  int64_t vd_seq_stride, vd_head_stride;
+  uint8_t* k;
+  int64_t k_page_stride, k_row_stride, k_head_stride;
+  uint8_t* v;
+  int64_t v_page_stride, v_row_stride, v_head_stride;
+  uint16_t* k_rope;
+  int64_t rope_page_stride, rope_row_stride;
+  float* k_blk_scale;
+  int64_t scale_page_stride, scale_row_stride;
+} pkv_kv_write_args;
+
+pkv_status pkv_write_kv(const pkv_kv_write_args* a, void* stream);
+
+/* sizeof(pkv_kv_write_args) in this build (a binding's layout check) */
+size_t pkv_kv_write_args_size(void);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

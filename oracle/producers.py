@@ -16,7 +16,8 @@ decode but prints none.
 Readings (where the pages are silent): the write puts the n_new newest tokens
 of sequence b at positions L_b - n_new .. L_b - 1 (L_b = seq_lens[b], new
 tokens included), row pos % page_size of page block_table[b][pos /
-page_size]; the descales are inputs; a value beyond the e4m3 range saturates
+page_size], skipping a token whose position is negative or whose block-table
+entry is missing or outside the pool; the descales are inputs; a value beyond the e4m3 range saturates
 to +-448 and NaN stays NaN (0x7F). The latent-record write computes one scale
 per token and 128-value block (largest |x| of the block, at least 1e-6, over
 448), stores the codes of x / scale, copies the 64 bf16 rope values bitwise
@@ -73,13 +74,19 @@ def quantize_q(q, num_seqs, q_len, h_k):
     return encode_e4m3(y).reshape(q.shape), descale
 
 
-def write_positions(seq_lens, n_new, block_table, page_size):
-    """(page, row) of each new token, [num_seqs, n_new] each."""
+def write_positions(seq_lens, n_new, block_table, page_size, num_pages=None):
+    """(page, row) of each new token, [num_seqs, n_new] each; page -1 marks a
+    token with no slot (position < 0, past the block table, or an entry outside
+    [0, num_pages)), which the write skips."""
     lens = np.asarray(seq_lens, dtype=np.int64)
-    pos = lens[:, None] - n_new + np.arange(n_new)[None, :]
     bt = np.asarray(block_table)
-    pages = np.take_along_axis(bt, pos // page_size, axis=1)
-    return pages, pos % page_size
+    pos = lens[:, None] - n_new + np.arange(n_new)[None, :]
+    blk = pos // page_size
+    ok = (pos >= 0) & (blk < bt.shape[1])
+    pages = np.take_along_axis(bt, np.where(ok, blk, 0), axis=1).astype(np.int64)
+    if num_pages is not None:
+        ok &= (pages >= 0) & (pages < num_pages)
+    return np.where(ok, pages, -1), np.where(ok, pos % page_size, 0)
 
 
 def write_kv_e4m3(cache, x_new, seq_lens, n_new, block_table, descale):
@@ -91,9 +98,11 @@ def write_kv_e4m3(cache, x_new, seq_lens, n_new, block_table, descale):
     num_seqs = len(seq_lens)
     x = np.asarray(x_new, dtype=np.float32).reshape(num_seqs, n_new, *out.shape[2:])
     ds = np.asarray(descale, dtype=np.float32)
-    pages, rows = write_positions(seq_lens, n_new, block_table, page_size)
+    pages, rows = write_positions(seq_lens, n_new, block_table, page_size, out.shape[0])
     for b in range(num_seqs):
         for t in range(n_new):
+            if pages[b, t] < 0:
+                continue
             y = (x[b, t] / ds[b][:, None]).astype(np.float32)
             out[pages[b, t], rows[b, t]] = encode_e4m3(y)
     return out
@@ -109,9 +118,11 @@ def write_kv_latent(lat, rope, scl, x_new, rope_new, seq_lens, n_new, block_tabl
     num_seqs = len(seq_lens)
     x = np.asarray(x_new, dtype=np.float32).reshape(num_seqs, n_new, 4, 128)
     r = np.asarray(rope_new, dtype=np.uint16).reshape(num_seqs, n_new, -1)
-    pages, rows = write_positions(seq_lens, n_new, block_table, page_size)
+    pages, rows = write_positions(seq_lens, n_new, block_table, page_size, lat.shape[0])
     for b in range(num_seqs):
         for t in range(n_new):
+            if pages[b, t] < 0:
+                continue
             amax = np.maximum(np.abs(x[b, t]).max(axis=1).astype(np.float32), np.float32(1e-6))
             s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
             lat[pages[b, t], rows[b, t]] = encode_e4m3((x[b, t] / s[:, None]).astype(np.float32)).reshape(-1)

@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libpkvfp8.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "plan.cpp", "decode_gqa.hip", "decode_mla.hip", "merge.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "decode_gqa.hip", "decode_mla.hip", "merge.hip", "producers.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops
 # (v_pk_*_f32); the host pass warns that it does not know the feature.

@@ -199,3 +199,65 @@ extern "C" pkv_status pkv_merge_splits(const pkv_decode_args* a, void* stream) {
   if (a->max_splits == 1 || (a->merge_counters && a->kv_format == PKV_KV_E4M3)) return PKV_OK;
   return hip_status(merge_launch(*a, static_cast<hipStream_t>(stream)), "merge launch");
 }
+
+namespace {
+bool bad_elem_stride(int64_t s, int64_t mult) { return s < 0 || s % mult != 0; }
+}  // namespace
+
+extern "C" pkv_status pkv_quantize_q(const pkv_quant_q_args* a, void* stream) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "args is NULL");
+  if (a->num_seqs < 1 || a->q_len < 1 || a->h_q < 1 || a->h_k < 1 || a->d < 8)
+    return fail(PKV_ERR_INVALID_ARG, "num_seqs=%d q_len=%d h_q=%d h_k=%d d=%d: sizes must be >= 1 (d >= 8)", a->num_seqs,
+                a->q_len, a->h_q, a->h_k, a->d);
+  if (a->h_q % a->h_k) return fail(PKV_ERR_INVALID_ARG, "h_q=%d is not a multiple of h_k=%d", a->h_q, a->h_k);
+  if (a->d % 8) return fail(PKV_ERR_INVALID_ARG, "d=%d is not a multiple of 8", a->d);
+  if (!a->q || !a->q8 || !a->q_descale) return fail(PKV_ERR_INVALID_ARG, "q, q8 and q_descale must be non-NULL");
+  if (!aligned(a->q, 16) || bad_elem_stride(a->q_tok_stride, 8) || bad_elem_stride(a->q_head_stride, 8))
+    return fail(PKV_ERR_INVALID_ARG, "q must be 16-B aligned with strides that are multiples of 8 elements");
+  if (!aligned(a->q8, 8) || bad_elem_stride(a->q8_tok_stride, 8) || bad_elem_stride(a->q8_head_stride, 8))
+    return fail(PKV_ERR_INVALID_ARG, "q8 must be 8-B aligned with strides that are multiples of 8 bytes");
+  if (!aligned(a->q_descale, 4) || a->qd_seq_stride < 0 || a->qd_head_stride < 0)
+    return fail(PKV_ERR_INVALID_ARG, "q_descale must be 4-B aligned with strides >= 0");
+  return hip_status(quantize_q_launch(*a, static_cast<hipStream_t>(stream)), "query quantisation launch");
+}
+
+extern "C" pkv_status pkv_write_kv(const pkv_kv_write_args* a, void* stream) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "args is NULL");
+  if (a->num_seqs < 1 || a->n_new < 1 || a->h_k < 1 || a->d < 8 || a->num_pages < 1 || a->max_blocks < 1)
+    return fail(PKV_ERR_INVALID_ARG, "num_seqs, n_new, h_k, num_pages, max_blocks must be >= 1 and d >= 8");
+  if (!pow2_page(a->page_size)) return fail(PKV_ERR_UNSUPPORTED, "page_size=%d not in {16,32,64,128}", a->page_size);
+  if (!a->k_new || !a->block_table || !a->seq_lens || !a->k)
+    return fail(PKV_ERR_INVALID_ARG, "k_new, block_table, seq_lens and k must be non-NULL");
+  if (a->bt_row_stride < a->max_blocks) return fail(PKV_ERR_INVALID_ARG, "bt_row_stride < max_blocks");
+  if (!aligned(a->k_new, 16) || bad_elem_stride(a->kn_tok_stride, 8) || bad_elem_stride(a->kn_head_stride, 8))
+    return fail(PKV_ERR_INVALID_ARG, "k_new must be 16-B aligned with strides that are multiples of 8 elements");
+  if (!aligned(a->k, 8) || bad_elem_stride(a->k_page_stride, 8) || bad_elem_stride(a->k_row_stride, 8) ||
+      bad_elem_stride(a->k_head_stride, 8))
+    return fail(PKV_ERR_INVALID_ARG, "k must be 8-B aligned with strides that are multiples of 8 bytes");
+  if (a->kv_format == PKV_KV_MLA) {
+    if (a->h_k != 1 || a->d != 576) return fail(PKV_ERR_INVALID_ARG, "latent write needs h_k = 1 and d = 576");
+    if (!a->k_rope || !a->k_blk_scale) return fail(PKV_ERR_INVALID_ARG, "latent write: k_rope, k_blk_scale NULL");
+    if (!aligned(a->k_rope, 16) || bad_elem_stride(a->rope_page_stride, 8) || bad_elem_stride(a->rope_row_stride, 8))
+      return fail(PKV_ERR_INVALID_ARG, "k_rope must be 16-B aligned with strides that are multiples of 8 elements");
+    if (!aligned(a->k_blk_scale, 4) || a->scale_page_stride < 0 || a->scale_row_stride < 0)
+      return fail(PKV_ERR_INVALID_ARG, "k_blk_scale must be 4-B aligned with strides >= 0");
+  } else if (a->kv_format == PKV_KV_E4M3) {
+    if (a->d % 8) return fail(PKV_ERR_INVALID_ARG, "d=%d is not a multiple of 8", a->d);
+    if (!a->v_new || !a->v || !a->k_descale || !a->v_descale)
+      return fail(PKV_ERR_INVALID_ARG, "v_new, v, k_descale and v_descale must be non-NULL");
+    if (!aligned(a->v_new, 16) || bad_elem_stride(a->vn_tok_stride, 8) || bad_elem_stride(a->vn_head_stride, 8))
+      return fail(PKV_ERR_INVALID_ARG, "v_new must be 16-B aligned with strides that are multiples of 8 elements");
+    if (!aligned(a->v, 8) || bad_elem_stride(a->v_page_stride, 8) || bad_elem_stride(a->v_row_stride, 8) ||
+        bad_elem_stride(a->v_head_stride, 8))
+      return fail(PKV_ERR_INVALID_ARG, "v must be 8-B aligned with strides that are multiples of 8 bytes");
+    if (a->kd_seq_stride < 0 || a->kd_head_stride < 0 || a->vd_seq_stride < 0 || a->vd_head_stride < 0)
+      return fail(PKV_ERR_INVALID_ARG, "descale strides must be >= 0");
+  } else {
+    return fail(PKV_ERR_UNSUPPORTED, "kv_format=%d", a->kv_format);
+  }
+  return hip_status(write_kv_launch(*a, static_cast<hipStream_t>(stream)), "KV-cache write launch");
+}
+
+extern "C" size_t pkv_quant_q_args_size(void) { return sizeof(pkv_quant_q_args); }
+
+extern "C" size_t pkv_kv_write_args_size(void) { return sizeof(pkv_kv_write_args); }

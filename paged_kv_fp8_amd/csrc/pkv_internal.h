@@ -35,6 +35,8 @@ hipError_t mla_launch(const pkv_decode_args& a, hipStream_t stream);
 
 // Combine of split partials.
 hipError_t merge_launch(const pkv_decode_args& a, hipStream_t stream);
+hipError_t quantize_q_launch(const pkv_quant_q_args& a, hipStream_t stream);
+hipError_t write_kv_launch(const pkv_kv_write_args& a, hipStream_t stream);
 
 // Workspace partition, in floats: partial O of every (split, seq, head,
 // row) first, then its (max, sum) pair.

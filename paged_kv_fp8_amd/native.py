@@ -21,7 +21,7 @@ PKV_MAX_SPLITS = 256
 # Every function the header declares, in declaration order.
 EXPORTS = ("pkv_status_string", "pkv_last_error", "pkv_version", "pkv_decode_args_size", "pkv_plan_split_kv",
            "pkv_plan_balanced", "pkv_workspace_bytes", "pkv_decode_slots", "pkv_paged_decode_attn",
-           "pkv_merge_splits")
+           "pkv_merge_splits", "pkv_quantize_q", "pkv_quant_q_args_size", "pkv_write_kv", "pkv_kv_write_args_size")
 
 
 class PkvError(RuntimeError):
@@ -65,6 +65,35 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class QuantQArgs(ctypes.Structure):
+    """pkv_quant_q_args"""
+    _fields_ = [("num_seqs", ctypes.c_int32), ("q_len", ctypes.c_int32), ("h_q", ctypes.c_int32),
+                ("h_k", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("q", ctypes.c_void_p), ("q_tok_stride", ctypes.c_int64), ("q_head_stride", ctypes.c_int64),
+                ("q8", ctypes.c_void_p), ("q8_tok_stride", ctypes.c_int64), ("q8_head_stride", ctypes.c_int64),
+                ("q_descale", ctypes.c_void_p), ("qd_seq_stride", ctypes.c_int64), ("qd_head_stride", ctypes.c_int64)]
+
+
+class KvWriteArgs(ctypes.Structure):
+    """pkv_kv_write_args"""
+    _fields_ = [("num_seqs", ctypes.c_int32), ("n_new", ctypes.c_int32), ("h_k", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("max_blocks", ctypes.c_int32), ("kv_format", ctypes.c_int32),
+                ("k_new", ctypes.c_void_p), ("kn_tok_stride", ctypes.c_int64), ("kn_head_stride", ctypes.c_int64),
+                ("v_new", ctypes.c_void_p), ("vn_tok_stride", ctypes.c_int64), ("vn_head_stride", ctypes.c_int64),
+                ("block_table", ctypes.c_void_p), ("bt_row_stride", ctypes.c_int64),
+                ("seq_lens", ctypes.c_void_p),
+                ("k_descale", ctypes.c_void_p), ("kd_seq_stride", ctypes.c_int64), ("kd_head_stride", ctypes.c_int64),
+                ("v_descale", ctypes.c_void_p), ("vd_seq_stride", ctypes.c_int64), ("vd_head_stride", ctypes.c_int64),
+                ("k", ctypes.c_void_p), ("k_page_stride", ctypes.c_int64), ("k_row_stride", ctypes.c_int64),
+                ("k_head_stride", ctypes.c_int64),
+                ("v", ctypes.c_void_p), ("v_page_stride", ctypes.c_int64), ("v_row_stride", ctypes.c_int64),
+                ("v_head_stride", ctypes.c_int64),
+                ("k_rope", ctypes.c_void_p), ("rope_page_stride", ctypes.c_int64), ("rope_row_stride", ctypes.c_int64),
+                ("k_blk_scale", ctypes.c_void_p), ("scale_page_stride", ctypes.c_int64),
+                ("scale_row_stride", ctypes.c_int64)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run `python -m paged_kv_fp8_amd.build`")
@@ -90,6 +119,16 @@ def _load():
     lib.pkv_paged_decode_attn.argtypes = [P(DecodeArgs), _vp]
     lib.pkv_merge_splits.restype = _i32
     lib.pkv_merge_splits.argtypes = [P(DecodeArgs), _vp]
+    lib.pkv_quantize_q.restype = _i32
+    lib.pkv_quantize_q.argtypes = [P(QuantQArgs), _vp]
+    lib.pkv_quant_q_args_size.restype = ctypes.c_size_t
+    lib.pkv_write_kv.restype = _i32
+    lib.pkv_write_kv.argtypes = [P(KvWriteArgs), _vp]
+    lib.pkv_kv_write_args_size.restype = ctypes.c_size_t
+    for name, st in (("pkv_quant_q_args_size", QuantQArgs), ("pkv_kv_write_args_size", KvWriteArgs)):
+        if getattr(lib, name)() != ctypes.sizeof(st):
+            raise ImportError(f"{st.__doc__} layout mismatch: library {getattr(lib, name)()} B, "
+                              f"binding {ctypes.sizeof(st)} B")
     if lib.pkv_decode_args_size() != ctypes.sizeof(DecodeArgs):
         raise ImportError(f"pkv_decode_args layout mismatch: library {lib.pkv_decode_args_size()} B, "
                           f"binding {ctypes.sizeof(DecodeArgs)} B")
@@ -170,3 +209,11 @@ def paged_decode_attn(args, stream=None):
 
 def merge_splits(args, stream=None):
     _check(lib.pkv_merge_splits(ctypes.byref(args), stream), "pkv_merge_splits")
+
+
+def quantize_q(args, stream=None):
+    _check(lib.pkv_quantize_q(ctypes.byref(args), stream), "pkv_quantize_q")
+
+
+def write_kv(args, stream=None):
+    _check(lib.pkv_write_kv(ctypes.byref(args), stream), "pkv_write_kv")

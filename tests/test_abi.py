@@ -190,3 +190,71 @@ def test_library_balanced_planner_equals_oracle(native, seed):
     assert w2.tolist() == [list(x) for x in work]
     assert ns2.tolist() == ns and offs2.tolist() == offs
     assert (info.num_bins, info.num_work, info.max_n_splits) == (bins, len(work), max(ns))
+
+
+# ---------------------------------------------------------------------------
+# producers: argument checks run before any HIP call
+# ---------------------------------------------------------------------------
+def _quant_args(native, **over):
+    base = 1 << 40
+    a = native.QuantQArgs(num_seqs=2, q_len=1, h_q=8, h_k=2, d=128, q=base, q_tok_stride=8 * 128,
+                          q_head_stride=128, q8=base + (1 << 30), q8_tok_stride=8 * 128, q8_head_stride=128,
+                          q_descale=base + (2 << 30), qd_seq_stride=2, qd_head_stride=1)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def _write_args(native, **over):
+    base = 1 << 40
+    a = native.KvWriteArgs(num_seqs=2, n_new=1, h_k=2, d=128, page_size=16, num_pages=8, max_blocks=4,
+                           kv_format=native.PKV_KV_E4M3, k_new=base, kn_tok_stride=256, kn_head_stride=128,
+                           v_new=base + (1 << 30), vn_tok_stride=256, vn_head_stride=128,
+                           block_table=base + (2 << 30), bt_row_stride=4, seq_lens=base + (2 << 30) + 4096,
+                           k_descale=base + (3 << 30), kd_seq_stride=2, kd_head_stride=1,
+                           v_descale=base + (3 << 30) + 256, vd_seq_stride=2, vd_head_stride=1,
+                           k=base + (4 << 30), k_page_stride=16 * 256, k_row_stride=256, k_head_stride=128,
+                           v=base + (5 << 30), v_page_stride=16 * 256, v_row_stride=256, v_head_stride=128)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+LAT = dict(kv_format=1, h_k=1, d=576, kn_tok_stride=576, kn_head_stride=0, v_new=None, v=None, k_descale=None,
+           v_descale=None, k_page_stride=16 * 512, k_row_stride=512, k_head_stride=0, k_rope=(1 << 40) + (6 << 30),
+           rope_page_stride=16 * 64, rope_row_stride=64, k_blk_scale=(1 << 40) + (7 << 30), scale_page_stride=64,
+           scale_row_stride=4)
+
+BAD_QUANT = [
+    (dict(num_seqs=0), -1), (dict(h_q=6, h_k=4), -1), (dict(d=100), -1), (dict(d=4), -1), (dict(q=None), -1),
+    (dict(q8=None), -1), (dict(q_descale=None), -1), (dict(q=(1 << 40) + 8), -1), (dict(q_tok_stride=100), -1),
+    (dict(q8=(1 << 40) + (1 << 30) + 4), -1), (dict(q8_head_stride=12), -1), (dict(qd_seq_stride=-1), -1),
+]
+
+BAD_WRITE = [
+    (dict(num_seqs=0), -1), (dict(n_new=0), -1), (dict(page_size=24), -2), (dict(kv_format=4), -2),
+    (dict(k_new=None), -1), (dict(block_table=None), -1), (dict(seq_lens=None), -1), (dict(bt_row_stride=2), -1),
+    (dict(k_new=(1 << 40) + 8), -1), (dict(kn_head_stride=100), -1), (dict(k_row_stride=100), -1),
+    (dict(v=None), -1), (dict(v_descale=None), -1), (dict(vd_head_stride=-2), -1), (dict(d=100), -1),
+    (dict(LAT, h_k=2), -1), (dict(LAT, d=512), -1), (dict(LAT, k_rope=None), -1), (dict(LAT, k_blk_scale=None), -1),
+    (dict(LAT, k_rope=(1 << 40) + (6 << 30) + 2), -1),
+]
+
+
+@pytest.mark.parametrize("over,code", BAD_QUANT)
+def test_quantize_q_rejects_invalid_arguments(native, over, code):
+    st = native.lib.pkv_quantize_q(ctypes.byref(_quant_args(native, **over)), None)
+    assert st == code, (over, native.status_string(st), native.last_error())
+    assert native.last_error()
+
+
+@pytest.mark.parametrize("over,code", BAD_WRITE)
+def test_write_kv_rejects_invalid_arguments(native, over, code):
+    st = native.lib.pkv_write_kv(ctypes.byref(_write_args(native, **over)), None)
+    assert st == code, (over, native.status_string(st), native.last_error())
+    assert native.last_error()
+
+
+def test_producers_reject_null_args(native):
+    assert native.lib.pkv_quantize_q(None, None) == -1
+    assert native.lib.pkv_write_kv(None, None) == -1

@@ -125,3 +125,17 @@ def test_write_kv_latent_scales_and_rope():
                 else:
                     assert np.abs(vals[blk]).max() == 448
             assert np.array_equal(rope2[pg[b, t], rw[b, t]], rn[i])
+
+
+def test_write_skips_tokens_without_a_slot():
+    # seq 0: L=1 < n_new=3, so positions -2, -1 have no slot and position 0 goes to
+    # page 2 row 0; seq 1: L=6, positions 3, 4, 5 are blocks 0, 1, 1 -> page 1 row 3,
+    # then block-table entry 9, outside a pool of 4 pages (skipped)
+    bt = np.array([[2, 0], [1, 9]])
+    pages, rows = write_positions([1, 6], 3, bt, 4, num_pages=4)
+    assert pages.tolist() == [[-1, -1, 2], [1, -1, -1]] and rows[0, 2] == 0 and rows[1, 0] == 3
+    cache = np.zeros((4, 4, 1, 8), np.uint8)
+    x = np.ones((6, 1, 8), np.float32)
+    out = write_kv_e4m3(cache, x, [1, 6], 3, bt, np.ones((2, 1), np.float32))
+    written = {(int(p), int(r)) for p, r in zip(*np.nonzero(out.any(axis=(2, 3))))}
+    assert written == {(2, 0), (1, 3)}
