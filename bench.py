@@ -132,6 +132,83 @@ def cpu_oracle_baseline(batch, budget_s):
                       f"numpy fp64, one BLAS thread"}
 
 
+def bench_producers(steps):
+    """Time the producers on the workloads' per-step shapes and on a
+    prefill-sized write: us per call (HIP events on the launch stream) and
+    algorithmic bytes / time."""
+    import torch
+
+    from paged_kv_fp8_amd import producers
+
+    dev = "cuda"
+    g = torch.Generator(device=dev).manual_seed(4242)
+    cases = []
+
+    def timed(name, fn, nbytes, shape):
+        # `steps` calls captured in one graph and replayed, so the host's launch
+        # cost does not sit between the kernels
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(steps):
+                fn()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        cases.append({"case": name, "shape": shape, "us_per_call": round(us, 2), "bytes": nbytes,
+                      "GB_per_s": round(nbytes / us / 1e3, 1), "frac_of_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)})
+        log(f"{name}: {us:.2f} us, {nbytes / us / 1e3:.0f} GB/s")
+
+    for name, (b, t, hq, hk, d) in {"quantize_q, fully-fp8 decode step": (128, 1, 64, 4, 128),
+                                    "quantize_q, speculative verify step": (32, 4, 64, 8, 128),
+                                    "quantize_q, 512 sequences x 8 tokens": (512, 8, 64, 8, 128)}.items():
+        q = torch.randn(b * t, hq, d, device=dev, generator=g).to(torch.bfloat16)
+        q8 = torch.empty(q.shape, dtype=torch.uint8, device=dev)
+        qd = torch.empty(b, hk, dtype=torch.float32, device=dev)
+        nbytes = q.numel() * 2 * 2 + q.numel() + qd.numel() * 4  # q read twice (amax, codes), codes written
+        timed(name, lambda: producers.quantize_q(q, b, t, hk, q8=q8, q_descale=qd), nbytes,
+              {"num_seqs": b, "q_len": t, "h_q": hq, "h_k": hk, "d": d})
+
+    for name, (b, n, hk, ps) in {"write_kv e4m3, decode step (64 x 1 token)": (64, 1, 8, 16),
+                                 "write_kv e4m3, prefill (32 x 1024 tokens)": (32, 1024, 8, 16)}.items():
+        d = 128
+        blocks = (n + 2048) // ps + 1
+        pages = b * blocks
+        kc = torch.zeros(pages, ps, hk, d, dtype=torch.uint8, device=dev)
+        vc = torch.zeros_like(kc)
+        bt = torch.randperm(pages, device=dev, generator=g).to(torch.int32).view(b, blocks)
+        lens = torch.full((b,), 2048 + n, dtype=torch.int32, device=dev)
+        kn = torch.randn(b * n, hk, d, device=dev, generator=g).to(torch.bfloat16)
+        vn = torch.randn(b * n, hk, d, device=dev, generator=g).to(torch.bfloat16)
+        kd = torch.full((b, hk), 0.01, device=dev)
+        nbytes = 2 * kn.numel() * 2 + 2 * kn.numel() + b * n * 4
+        timed(name, lambda: producers.write_kv(kn, vn, bt, lens, n, kc, vc, kd, kd), nbytes,
+              {"num_seqs": b, "n_new": n, "h_k": hk, "d": d, "page_size": ps})
+
+    for name, (b, n, ps) in {"write_kv latent, decode step (32 x 1 token)": (32, 1, 64),
+                             "write_kv latent, prefill (32 x 1024 tokens)": (32, 1024, 64)}.items():
+        blocks = (n + 2048) // ps + 1
+        pages = b * blocks
+        lat = torch.zeros(pages, ps, 512, dtype=torch.uint8, device=dev)
+        rope = torch.zeros(pages, ps, 64, dtype=torch.int16, device=dev)
+        scl = torch.zeros(pages, ps, 4, dtype=torch.float32, device=dev)
+        bt = torch.randperm(pages, device=dev, generator=g).to(torch.int32).view(b, blocks)
+        lens = torch.full((b,), 2048 + n, dtype=torch.int32, device=dev)
+        x = torch.randn(b * n, 576, device=dev, generator=g).to(torch.bfloat16)
+        nbytes = b * n * (576 * 2 + 656 + 4)
+        timed(name, lambda: producers.write_latent(x, bt, lens, n, lat, rope, scl), nbytes,
+              {"num_seqs": b, "n_new": n, "page_size": ps})
+    print(json.dumps({"metric": "producer kernels: us per call and algorithmic GB/s", "n_gpus": 1, "steps": steps,
+                      "data": "synthetic", "cases": cases}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,6 +232,8 @@ def main():
                          "equal shares of all keys, one per workgroup")
     ap.add_argument("--fused-merge", action="store_true",
                     help="merge split sequences inside the decode kernel (last split merges) instead of a second launch")
+    ap.add_argument("--producers", action="store_true",
+                    help="only time the query quantisation and KV-cache write kernels (a separate JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 8 plain 256 MiB device-to-device copies (scale reference for HBM byte counters)")
     args = ap.parse_args()
@@ -165,6 +244,11 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.producers:
+        torch.cuda.set_device(0)
+        bench_producers(args.steps)
+        return
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
