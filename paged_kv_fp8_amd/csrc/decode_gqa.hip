@@ -476,8 +476,8 @@ __device__ __forceinline__ int clamp_page(const GqaParams& p, int pg) { return m
 
 // One work item (a chunk of 128-key tiles of one sequence) for kv head g:
 // the one-item-per-workgroup plan.
-template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES>
-__device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, int lane, int g) {
+template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES, int HW>
+__device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, int lane, int g, int* progress) {
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
 
@@ -549,6 +549,7 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s) fetch(ring[s], k_begin + kBlockKeys * s, s);
     const int rounds = (k_end - k_begin + kBlockKeys * STAGES - 1) / (kBlockKeys * STAGES);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     for (int r = 0; r < rounds; ++r) {
       const int kb0 = k_begin + r * kBlockKeys * STAGES;
 #pragma unroll
@@ -556,6 +557,17 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
         const int kb = kb0 + kBlockKeys * s;
         fetch(ring[(s + STAGES - 1) % STAGES], kb + kBlockKeys * (STAGES - 1), (s + STAGES - 1) % STAGES);
         process_block<FP8Q, NB>(ring[s], kb, q, st, lim, lim_min, c2, g4);
+      }
+      if (HW == 8) {
+        // Eight waves share four SIMDs: wave w and w ^ 4 sit on one SIMD, and
+        // the older wins issue by default. A wave that is not ahead of its
+        // sibling runs at raised priority, so the two keep pace.
+        if (lane == 0) __hip_atomic_store(progress + wave, r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const int sib = __hip_atomic_load(progress + (wave ^ 4), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (__builtin_amdgcn_readfirstlane(sib) >= r)
+          __builtin_amdgcn_s_setprio(1);
+        else
+          __builtin_amdgcn_s_setprio(0);
       }
     }
   }
@@ -728,12 +740,17 @@ template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES, int HW, bool STREAM>
 __global__ __launch_bounds__(64 * HW) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 2 : 1)))
 void gqa_decode_kernel(GqaParams p) {
   const int lane = threadIdx.x & 63;
+  __shared__ int progress[HW];  // rounds done per wave (one-item form, eight waves)
+  if (!STREAM && HW == 8) {
+    if (lane == 0) progress[threadIdx.x >> 6] = 0;
+    __syncthreads();
+  }
   const int g = __builtin_amdgcn_readfirstlane(blockIdx.y * HW + (threadIdx.x >> 6));  // wave-uniform
   if (g >= p.h_k) return;
   if (STREAM)
     gqa_decode_stream<FP8Q, NB, CAUSAL_TAIL, STAGES>(p, lane, g);
   else
-    gqa_decode_item<FP8Q, NB, CAUSAL_TAIL, STAGES>(p, blockIdx.x, lane, g);
+    gqa_decode_item<FP8Q, NB, CAUSAL_TAIL, STAGES, HW>(p, blockIdx.x, lane, g, progress);
 }
 
 // Ring depth in 32-key blocks. Three blocks (two in flight while one is
