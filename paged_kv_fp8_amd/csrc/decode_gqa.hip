@@ -276,9 +276,27 @@ __device__ __forceinline__ RawBlock load_block(const GqaParams& p, int g, int kb
 
 // One 32-key block: S = K Q^T, online softmax, O^T += V^T P^T. lim[nb] is
 // the last key row r16 of block nb may see; keys past lim_min need the mask.
+// Query operand parked in LDS (two row blocks: saves the registers that would
+// otherwise push the O accumulators into AGPRs): entry (nb, s) of lane l at
+// qlds + ((4 nb + s) * 64 + l) * size, one conflict-free read per k-step.
 template <bool FP8Q, int NB>
-__device__ __forceinline__ void process_block(const RawBlock& cur, int kb, const QOperand<NB>& q, RowState<NB>& st,
-                                              const int* lim, int lim_min, float c2, int g4) {
+__device__ __forceinline__ void park_q(const QOperand<NB>& q, uint8_t* qlds, int lane) {
+  for (int nb = 0; nb < NB; ++nb)
+    for (int s = 0; s < 4; ++s) {
+      if (FP8Q)
+        *reinterpret_cast<long*>(qlds + ((4 * nb + s) * 64 + lane) * 8) = q.q8[nb][s];
+      else
+        *reinterpret_cast<bf16x8*>(qlds + ((4 * nb + s) * 64 + lane) * 16) = q.qb[nb][s];
+    }
+}
+
+template <bool FP8Q, int NB, bool QLDS>
+__device__ __forceinline__ void process_block(const RawBlock& cur, int kb, const QOperand<NB>& q, const uint8_t* qlds,
+                                              RowState<NB>& st, const int* lim, int lim_min, float c2, int g4) {
+  const int lane = threadIdx.x & 63;
+  // keep the LDS query reads inside the loop (hoisted, they would occupy the
+  // registers this form saves)
+  if (QLDS) asm volatile("" ::: "memory");
   // ---- S = K Q^T (keys on M) -----------------------------------------------
   f32x4 sacc[NB][2];
   for (int nb = 0; nb < NB; ++nb)
@@ -288,12 +306,17 @@ __device__ __forceinline__ void process_block(const RawBlock& cur, int kb, const
       const uint2 kraw = half_of(cur.k[t][s >> 1], s & 1);
       if (FP8Q) {
         const long a = as_long(kraw);
-        for (int nb = 0; nb < NB; ++nb)
-          sacc[nb][t] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, q.q8[nb][s], sacc[nb][t], 0, 0, 0);
+        for (int nb = 0; nb < NB; ++nb) {
+          const long b = QLDS ? *reinterpret_cast<const long*>(qlds + ((4 * nb + s) * 64 + lane) * 8) : q.q8[nb][s];
+          sacc[nb][t] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, sacc[nb][t], 0, 0, 0);
+        }
       } else {
         const bf16x8 a = e4m3x8_to_bf16(kraw);
-        for (int nb = 0; nb < NB; ++nb)
-          sacc[nb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, q.qb[nb][s], sacc[nb][t], 0, 0, 0);
+        for (int nb = 0; nb < NB; ++nb) {
+          const bf16x8 b =
+              QLDS ? *reinterpret_cast<const bf16x8*>(qlds + ((4 * nb + s) * 64 + lane) * 16) : q.qb[nb][s];
+          sacc[nb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, sacc[nb][t], 0, 0, 0);
+        }
       }
     }
   }
@@ -506,8 +529,12 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
   const float c2 = p.scale_log2e * qd * kdv;  // exponent scale (base 2) on raw scores
   const float cs = p.scale * qd * kdv;        // natural-log scale of the running max
 
+  constexpr bool kQLds = NB == 2;
+  extern __shared__ __attribute__((aligned(16))) uint8_t gqa_q_lds[];
+  uint8_t* qlds = gqa_q_lds + (threadIdx.x >> 6) * (NB * 4 * 64 * (FP8Q ? 8 : 16));
   QOperand<NB> q;
   load_q<FP8Q, NB>(p, q, rm, b, g, g4);
+  if (kQLds) park_q<FP8Q, NB>(q, qlds, lane);
   RowState<NB> st;
   reset_rows<NB>(st);
 
@@ -556,7 +583,7 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
       for (int s = 0; s < STAGES; ++s) {
         const int kb = kb0 + kBlockKeys * s;
         fetch(ring[(s + STAGES - 1) % STAGES], kb + kBlockKeys * (STAGES - 1), (s + STAGES - 1) % STAGES);
-        process_block<FP8Q, NB>(ring[s], kb, q, st, lim, lim_min, c2, g4);
+        process_block<FP8Q, NB, kQLds>(ring[s], kb, q, qlds, st, lim, lim_min, c2, g4);
       }
       if (HW == 8) {
         // Eight waves share four SIMDs: wave w and w ^ 4 sit on one SIMD, and
@@ -718,7 +745,7 @@ __device__ __forceinline__ void gqa_decode_stream(const GqaParams& p, int lane, 
             if (i != cur) advance_to(i);
             const int kb = __builtin_amdgcn_readlane(t_kbase, i) + kBlockKeys * j;
             // a block with no key below the item's end (past L) is skipped
-            if (kb <= lim_max) process_block<FP8Q, NB>(ring[s], kb, qc, st, lim, lim_min, c2, g4);
+            if (kb <= lim_max) process_block<FP8Q, NB, false>(ring[s], kb, qc, nullptr, st, lim, lim_min, c2, g4);
           }
         }
       }
@@ -733,11 +760,12 @@ __device__ __forceinline__ void gqa_decode_stream(const GqaParams& p, int lane, 
 // the number of concurrent DRAM streams per key range at two (K, V). A
 // workgroup runs one work item, or with a balanced plan the items of its
 // bin (a contiguous share of all sequences' keys) as one stream.
-// One row block fits in 256 registers; capping it at two waves per SIMD keeps
-// the compiler from spilling into AGPRs when the workgroup is small enough
-// to allow one wave per SIMD. Two row blocks get the whole register file.
+// Capped at two waves per SIMD (256 registers), which keeps the compiler from
+// parking values in AGPRs when the workgroup would allow one wave per SIMD:
+// one row block fits as is, two row blocks of the one-item form fit with the
+// query in LDS. The streaming form of two row blocks gets the whole file.
 template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES, int HW, bool STREAM>
-__global__ __launch_bounds__(64 * HW) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 2 : 1)))
+__global__ __launch_bounds__(64 * HW) __attribute__((amdgpu_waves_per_eu(NB == 1 || !STREAM ? 2 : 1)))
 void gqa_decode_kernel(GqaParams p) {
   const int lane = threadIdx.x & 63;
   __shared__ int progress[HW];  // rounds done per wave (one-item form, eight waves)
@@ -754,12 +782,14 @@ void gqa_decode_kernel(GqaParams p) {
 }
 
 // Ring depth in 32-key blocks. Three blocks (two in flight while one is
-// processed) for either row-block count: a deeper ring for two row blocks
-// needs more than the 256 VGPRs, and the compiler then shuttles values
-// through AGPRs, which costs more than the extra depth gains.
+// processed), except for the one-item form of two row blocks: with three
+// blocks it needs more than 256 VGPRs, and the compiler then shuttles the O
+// accumulators through AGPRs on every block. Two blocks plus the query in
+// LDS fit in 256 registers, so two waves can share a SIMD (measured on
+// the speculative-verify workload: 99.2 -> 96.3 us).
 template <int NB, bool STREAM>
 constexpr int ring_stages() {
-  return 3;
+  return (NB == 2 && !STREAM) ? 2 : 3;
 }
 
 template <bool FP8Q, int NB, bool CT, int HW>
@@ -803,7 +833,7 @@ GqaVariant gqa_variant(const pkv_decode_args& a) {
   v.n_blocks = rows <= 16 ? 1 : 2;
   v.causal_tail = a.causal && a.q_len > 1;
   v.stream = a.bin_offsets != nullptr;
-  v.stages = 3;
+  v.stages = (v.n_blocks == 2 && !v.stream) ? 2 : 3;
   // kv heads per workgroup: the largest power of two dividing h_k, up to 8
   // (4 for two row blocks, whose waves need more than half the registers)
   const int cap = v.n_blocks == 1 ? 8 : 4;
@@ -814,6 +844,11 @@ GqaVariant gqa_variant(const pkv_decode_args& a) {
 
 int gqa_rows_per_tile(const GqaVariant& v) { return 16 * v.n_blocks; }
 
+// dynamic LDS of a variant: the parked query of two row blocks (one-item form)
+size_t gqa_dyn_lds(const GqaVariant& v) {
+  return (v.n_blocks == 2 && !v.stream) ? (size_t)v.heads_per_wg * 2 * 4 * 64 * (v.fp8_q ? 8 : 16) : 0;
+}
+
 hipError_t gqa_occupancy(const GqaVariant& v, int* units_per_cu) {
   // Units (work item, kv head, q tile) = waves. The plan is sized for about
   // four streaming waves per CU (at least one workgroup), not for the
@@ -822,7 +857,8 @@ hipError_t gqa_occupancy(const GqaVariant& v, int* units_per_cu) {
   // those CUs with twice the bytes (measured on the fully-fp8 workload:
   // 0.61 -> 0.68 of peak).
   int wgs = 0;
-  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&wgs, select_kernel(v), 64 * v.heads_per_wg, 0);
+  const hipError_t e =
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&wgs, select_kernel(v), 64 * v.heads_per_wg, gqa_dyn_lds(v));
   const int resident = wgs * v.heads_per_wg;
   const int target = v.heads_per_wg > 4 ? v.heads_per_wg : 4;
   *units_per_cu = resident < target ? resident : target;
@@ -882,7 +918,7 @@ hipError_t gqa_launch(const pkv_decode_args& a, const GqaVariant& v, hipStream_t
   const int hw = v.heads_per_wg;
   dim3 grid(a.bin_offsets ? a.num_bins : a.num_work, (a.h_k + hw - 1) / hw, tiles);
   void* args[] = {&p};
-  return hipLaunchKernel(select_kernel(v), grid, dim3(64 * hw), args, 0, stream);
+  return hipLaunchKernel(select_kernel(v), grid, dim3(64 * hw), args, gqa_dyn_lds(v), stream);
 }
 
 }  // namespace pkv
