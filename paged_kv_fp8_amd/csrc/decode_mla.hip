@@ -24,9 +24,11 @@
 //  * QK^T on v_mfma_f32_16x16x32_bf16 with keys on M (16 latent + 2 rope
 //    k-steps per 16-key tile); PV on v_mfma_f32_16x16x16_bf16 (16 keys per
 //    step), O^T[d_v][rows] with dv-tile (g, mt) row m = d_v 128 g + 8 m + mt,
-//    so a lane ends with 32 contiguous d_v values per 128-block. V^T is
-//    transposed in registers with v_perm_b32; P stays in the lanes that
-//    computed it.
+//    so a lane ends with 32 contiguous d_v values per 128-block. Each record
+//    byte is loaded once, in the QK^T layout (lane r16 + 16 g4: key r16); the
+//    wave copies the block's latent codes and scales to its own LDS rows and
+//    reads them back as 4 keys x 8 values per lane, which v_perm_b32
+//    transposes into the V^T operand; P stays in the lanes that computed it.
 //  * Same load discipline as the GQA kernel: every fetch issues the same
 //    loads (keys clamped to the chunk's last key), the page of a block comes
 //    from a one-dword vector load two blocks ahead, the loop runs whole
@@ -106,13 +108,20 @@ __device__ __forceinline__ float pair32(float x, bool take_max) {
   return take_max ? fmaxf(a, b) : a + b;
 }
 
-// Raw bytes of one 16-key block as this lane loads them.
+// Raw bytes of one 16-key block as this lane loads them: each byte once, in
+// the layout of the QK^T operand (lane r16 + 16 g4 holds key kb + r16).
 struct RawRec {
-  uint4 kl[4][2];  // key kb + r16: latent bytes 128 blk + 64 h + 16 g4 .. +15
-  uint4 kr[2];     // key kb + r16: rope values 32 t + 8 g4 .. +7
-  float4 sc[4];    // key kb + 4 g4 + i: the four block scales
-  uint2 v[4][4];   // key kb + 4 g4 + i, latent bytes 128 gr + 8 r16 .. +7
+  uint4 kl[4][2];  // latent bytes 128 blk + 64 h + 16 g4 .. +15
+  uint4 kr[2];     // rope values 32 t + 8 g4 .. +7
+  float sc;        // block scale g4
 };
+
+// Per-wave LDS: the parked query operand, then the latent codes and scales of
+// the block being processed, from which the V^T operand is read back.
+constexpr int kQLdsBytes = kQSteps * 64 * 16;
+constexpr int kVRowBytes = kLatent + 16;  // rows 4 banks apart: the 16-byte stores of 8 rows hit distinct banks
+constexpr int kVScl = kBlockKeys * kVRowBytes;
+constexpr int kWaveLds = kQLdsBytes + kVScl + kBlockKeys * 16;
 
 // One work item (sequence chunk) for this wave's 16 query rows.
 template <bool CAUSAL_TAIL>
@@ -151,9 +160,11 @@ __device__ __forceinline__ void mla_decode_item(const MlaParams& p, int item, in
   // parked in this wave's LDS region (k-step major, one 16-byte slot per
   // lane, so each k-step is one conflict-free 16-byte read per lane). Only
   // this wave reads its region, and LDS operations of a wave are ordered.
-  // dynamic LDS: blockDim.x / 64 waves x kQSteps x 64 lanes x 16 bytes
-  extern __shared__ bf16x8 q_lds[];
-  bf16x8(*qw)[64] = reinterpret_cast<bf16x8(*)[64]>(q_lds + (threadIdx.x >> 6) * kQSteps * 64);
+  // dynamic LDS: blockDim.x / 64 waves x kWaveLds bytes
+  extern __shared__ __attribute__((aligned(16))) uint8_t wave_lds[];
+  uint8_t* const my_lds = wave_lds + (threadIdx.x >> 6) * kWaveLds;
+  bf16x8(*qw)[64] = reinterpret_cast<bf16x8(*)[64]>(my_lds);
+  uint8_t* const vlds = my_lds + kQLdsBytes;
   {
     const uint8_t* qrow = p.q + (int64_t)qtok * p.q_tok + (int64_t)qhead * p.q_head;
     for (int k = 0; k < kQSteps; ++k) {
@@ -186,20 +197,13 @@ __device__ __forceinline__ void mla_decode_item(const MlaParams& p, int item, in
       const uint8_t* lat0 = p.lat + (int64_t)pg * p.lat_page;
       const uint8_t* rope0 = p.rope + (int64_t)pg * p.rope_page;
       const uint8_t* scl0 = p.scl + (int64_t)pg * p.scl_page;
-      {
-        const int row = min(kb + r16, last_key) & pmask;
-        const uint8_t* lr = lat0 + (int64_t)row * p.lat_row;
-        for (int blk = 0; blk < 4; ++blk)
-          for (int h = 0; h < 2; ++h) r.kl[blk][h] = *reinterpret_cast<const uint4*>(lr + 128 * blk + 64 * h + 16 * g4);
-        const uint8_t* rr = rope0 + (int64_t)row * p.rope_row;
-        for (int t = 0; t < 2; ++t) r.kr[t] = *reinterpret_cast<const uint4*>(rr + 2 * (32 * t + 8 * g4));
-      }
-      for (int i = 0; i < 4; ++i) {
-        const int row = min(kb + 4 * g4 + i, last_key) & pmask;
-        r.sc[i] = *reinterpret_cast<const float4*>(scl0 + (int64_t)row * p.scl_row);
-        const uint8_t* lr = lat0 + (int64_t)row * p.lat_row;
-        for (int gr = 0; gr < 4; ++gr) r.v[i][gr] = *reinterpret_cast<const uint2*>(lr + 128 * gr + 8 * r16);
-      }
+      const int row = min(kb + r16, last_key) & pmask;
+      const uint8_t* lr = lat0 + (int64_t)row * p.lat_row;
+      for (int blk = 0; blk < 4; ++blk)
+        for (int h = 0; h < 2; ++h) r.kl[blk][h] = *reinterpret_cast<const uint4*>(lr + 128 * blk + 64 * h + 16 * g4);
+      const uint8_t* rr = rope0 + (int64_t)row * p.rope_row;
+      for (int t = 0; t < 2; ++t) r.kr[t] = *reinterpret_cast<const uint4*>(rr + 2 * (32 * t + 8 * g4));
+      r.sc = *reinterpret_cast<const float*>(scl0 + (int64_t)row * p.scl_row + 4 * g4);
       return r;
     };
 
@@ -218,6 +222,12 @@ __device__ __forceinline__ void mla_decode_item(const MlaParams& p, int item, in
       // keep the q reads from LDS inside the loop (hoisting them would hold
       // all 18 k-steps of q in registers again)
       asm volatile("" ::: "memory");
+      // the block's latent codes and scales into this wave's LDS rows (the
+      // previous block's reads come first in the wave's in-order LDS queue)
+      for (int blk = 0; blk < 4; ++blk)
+        for (int h = 0; h < 2; ++h)
+          *reinterpret_cast<uint4*>(vlds + r16 * kVRowBytes + 128 * blk + 64 * h + 16 * g4) = cur.kl[blk][h];
+      *reinterpret_cast<float*>(vlds + kVScl + 16 * r16 + 4 * g4) = cur.sc;
       // ---- S = K Q^T: one accumulator per 128-value block + rope -----------
       f32x4 acc[4], accr = {0.f, 0.f, 0.f, 0.f};
       for (int blk = 0; blk < 4; ++blk) {
@@ -229,10 +239,14 @@ __device__ __forceinline__ void mla_decode_item(const MlaParams& p, int item, in
       }
       for (int t = 0; t < 2; ++t)
         accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.kr[t]), qw[16 + t][lane], accr, 0, 0, 0);
-      // lane holds S[key kb + 4 g4 + i][row n]
+      // lane holds S[key kb + 4 g4 + i][row n]; other lanes' stores are read
+      // back from here on
+      asm volatile("" ::: "memory");
+      float4 scl[4];
+      for (int i = 0; i < 4; ++i) scl[i] = *reinterpret_cast<const float4*>(vlds + kVScl + 16 * (4 * g4 + i));
       float sv[4];
       for (int i = 0; i < 4; ++i) {
-        const float4 sc = cur.sc[i];
+        const float4 sc = scl[i];
         sv[i] = accr[i] + sc.x * acc[0][i] + sc.y * acc[1][i] + sc.z * acc[2][i] + sc.w * acc[3][i];
       }
       if (kb + kBlockKeys - 1 > lim_min) {
@@ -256,22 +270,37 @@ __device__ __forceinline__ void mla_decode_item(const MlaParams& p, int item, in
       }
       l_part = l_part * corr + psum;
       if (__builtin_amdgcn_ballot_w64(move)) {
+        // O lives in AGPRs; written as plain C, the compiler copies all of it
+        // to VGPRs ahead of this rarely taken branch on every block. In place,
+        // each value goes AGPR -> VGPR -> AGPR only when a reference moves.
         for (int gr = 0; gr < 4; ++gr)
-          for (int mt = 0; mt < 8; ++mt) oacc[gr][mt] *= corr;
+          for (int mt = 0; mt < 8; ++mt)
+            for (int i = 0; i < 4; ++i) {
+              float x = oacc[gr][mt][i], t;
+              asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                           : "+a"(x), "=&v"(t)
+                           : "v"(corr));
+              oacc[gr][mt][i] = x;
+            }
       }
       m_run = m_new;
       // ---- O^T += V^T (P * scale)^T per 128-value block of d_v --------------
       for (int gr = 0; gr < 4; ++gr) {
-        const float s0 = gr == 0 ? cur.sc[0].x : gr == 1 ? cur.sc[0].y : gr == 2 ? cur.sc[0].z : cur.sc[0].w;
-        const float s1 = gr == 0 ? cur.sc[1].x : gr == 1 ? cur.sc[1].y : gr == 2 ? cur.sc[1].z : cur.sc[1].w;
-        const float s2 = gr == 0 ? cur.sc[2].x : gr == 1 ? cur.sc[2].y : gr == 2 ? cur.sc[2].z : cur.sc[2].w;
-        const float s3 = gr == 0 ? cur.sc[3].x : gr == 1 ? cur.sc[3].y : gr == 2 ? cur.sc[3].z : cur.sc[3].w;
+        const float s0 = gr == 0 ? scl[0].x : gr == 1 ? scl[0].y : gr == 2 ? scl[0].z : scl[0].w;
+        const float s1 = gr == 0 ? scl[1].x : gr == 1 ? scl[1].y : gr == 2 ? scl[1].z : scl[1].w;
+        const float s2 = gr == 0 ? scl[2].x : gr == 1 ? scl[2].y : gr == 2 ? scl[2].z : scl[2].w;
+        const float s3 = gr == 0 ? scl[3].x : gr == 1 ? scl[3].y : gr == 2 ? scl[3].z : scl[3].w;
         const bf16x4 pb = {(__bf16)(pr[0] * s0), (__bf16)(pr[1] * s1), (__bf16)(pr[2] * s2), (__bf16)(pr[3] * s3)};
+        // key 4 g4 + i, latent bytes 128 gr + 8 r16 .. +7 (one row's 128
+        // contiguous bytes per 16-lane group)
+        uint2 v[4];
+        for (int i = 0; i < 4; ++i)
+          v[i] = *reinterpret_cast<const uint2*>(vlds + (4 * g4 + i) * kVRowBytes + 128 * gr + 8 * r16);
         for (int w2 = 0; w2 < 2; ++w2) {
-          const unsigned a0 = w2 ? cur.v[0][gr].y : cur.v[0][gr].x;
-          const unsigned a1 = w2 ? cur.v[1][gr].y : cur.v[1][gr].x;
-          const unsigned a2 = w2 ? cur.v[2][gr].y : cur.v[2][gr].x;
-          const unsigned a3 = w2 ? cur.v[3][gr].y : cur.v[3][gr].x;
+          const unsigned a0 = w2 ? v[0].y : v[0].x;
+          const unsigned a1 = w2 ? v[1].y : v[1].x;
+          const unsigned a2 = w2 ? v[2].y : v[2].x;
+          const unsigned a3 = w2 ? v[3].y : v[3].x;
           const unsigned x01 = __builtin_amdgcn_perm(a0, a1, 0x01050004u);
           const unsigned y01 = __builtin_amdgcn_perm(a0, a1, 0x03070206u);
           const unsigned x23 = __builtin_amdgcn_perm(a2, a3, 0x01050004u);
@@ -683,7 +712,7 @@ int waves_per_wg(const pkv_decode_args& a) {
 }
 
 size_t dyn_lds_bytes(const pkv_decode_args& a) {
-  return staged(a) ? (size_t)2 * kStageBytes : (size_t)waves_per_wg(a) * kQSteps * 64 * 16;
+  return staged(a) ? (size_t)2 * kStageBytes : (size_t)waves_per_wg(a) * kWaveLds;
 }
 
 int log2_exact(int x) {
