@@ -80,7 +80,7 @@ def measured_traffic(kernel, key):
     since it was taken."""
     import hashlib
 
-    source = {"gqa_decode_kernel": "decode_gqa.hip", "mla_decode_kernel": "decode_mla.hip"}[kernel]
+    source = "decode_mla.hip" if kernel.startswith("mla_") else "decode_gqa.hip"
     path = os.path.join(ROOT, "profiles", f"{kernel.replace('_kernel', '')}_{key}_hbm_bytes.md")
     src = os.path.join(ROOT, "paged_kv_fp8_amd", "csrc", source)
     if not os.path.exists(path):
@@ -368,7 +368,7 @@ def main():
         cpu = cpu_oracle_baseline(first, args.cpu_seconds)
         log(f"cpu oracle: {cpu}")
 
-    kernel = "mla_decode_kernel" if w.kv_format == "mla" else "gqa_decode_kernel"
+    kernel = decs[0].kernel_name
     if t_mfma > t_hbm:
         roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS[dtype], "unit": "TFLOP/s",
                     "frac": round(tflops / MFMA_PEAK_TFLOPS[dtype], 4), "traffic": None}

@@ -264,6 +264,15 @@ pkv_status pkv_decode_slots(const pkv_decode_args* a, int32_t* cu_count, int32_t
                             int32_t* n_q_tiles);
 
 /*
+ * Name of the device kernel that pkv_paged_decode_attn launches for these
+ * arguments ("gqa_decode_kernel", "mla_pair_kernel" or "mla_lds_kernel"), so
+ * that profiler output can be matched to a call. Host only, launches nothing.
+ * Returns a static string, or NULL when the shapes fail validation
+ * (pkv_last_error() says why).
+ */
+const char* pkv_decode_kernel_name(const pkv_decode_args* a);
+
+/*
  * Split-KV decode ("mjolnir-kernel 0.1.0 wheel: mjolnir/t5_decode.py",
  * decode kernel: online softmax over the work item's contiguous key range,
  * then its epilogue). One workgroup per (work item, kv head, q-row tile).

@@ -182,6 +182,11 @@ extern "C" pkv_status pkv_decode_slots(const pkv_decode_args* a, int32_t* cu_cou
   return PKV_OK;
 }
 
+extern "C" const char* pkv_decode_kernel_name(const pkv_decode_args* a) {
+  if (check_shapes(a) != PKV_OK) return nullptr;
+  return a->kv_format == PKV_KV_MLA ? mla_kernel_name(*a) : "gqa_decode_kernel";
+}
+
 extern "C" pkv_status pkv_paged_decode_attn(const pkv_decode_args* a, void* stream) {
   pkv_status st = check_shapes(a);
   if (st != PKV_OK) return st;

@@ -8,31 +8,25 @@
 // values, and whose value is the scaled latent part. Row n = qi * h_q + h
 // (qi-major) sees keys 0 .. lim(n) as in the GQA path.
 //
-// gfx950 design:
-//  * One wave per 16 query rows (= the 16 heads of one query token); up to 4
-//    waves (64 rows) per workgroup; more rows use more q-row tiles. Each wave
-//    streams the chunk's records 16 keys at a time into registers; the waves
-//    of a workgroup read the same records, which the L1/L2 serve after the
-//    first.
+// gfx950 design (two forms, by query rows per sequence):
 //  * The per-128 block scales are not multiplied into the e4m3 codes (the
 //    product is not a bf16 value in general): QK^T keeps one fp32
-//    accumulator per 128-value block and combines them with each key's four
+//    accumulator per 128-value block and combines them with each key's
 //    scales, s = sum_blk scale_blk * <q_blk, code_blk> + <q_rope, rope>; PV
 //    multiplies P by the key's block scale (one bf16 P operand per 128-value
 //    block of d_v), so V stays the exact codes. The codes convert to bf16
 //    exactly (v_cvt_scalef32_pk_bf16_fp8 with scale 1).
-//  * QK^T on v_mfma_f32_16x16x32_bf16 with keys on M (16 latent + 2 rope
-//    k-steps per 16-key tile); PV on v_mfma_f32_16x16x16_bf16 (16 keys per
-//    step), O^T[d_v][rows] with dv-tile (g, mt) row m = d_v 128 g + 8 m + mt,
-//    so a lane ends with 32 contiguous d_v values per 128-block. Each record
-//    byte is loaded once, in the QK^T layout (lane r16 + 16 g4: key r16); the
-//    wave copies the block's latent codes and scales to its own LDS rows and
-//    reads them back as 4 keys x 8 values per lane, which v_perm_b32
-//    transposes into the V^T operand; P stays in the lanes that computed it.
-//  * Same load discipline as the GQA kernel: every fetch issues the same
-//    loads (keys clamped to the chunk's last key), the page of a block comes
-//    from a one-dword vector load two blocks ahead, the loop runs whole
-//    rounds, so waits cover only the block being consumed.
+//  * QK^T on v_mfma_f32_16x16x32_bf16 with keys on M; the V^T operand comes
+//    from bf16 key rows in LDS through the transpose load, so P stays in the
+//    lanes that computed it.
+//  * Fewer than 64 rows (one to three query tokens): the pair form, two waves
+//    per 16 rows that split each record by d_v half and exchange partial S.
+//  * 64 rows and more: the staged form, eight waves that share one bf16 copy
+//    of each 32-key block in LDS.
+//  * Load discipline as in the GQA kernel: every fetch issues the same loads
+//    (keys clamped to the chunk's last key), the page of a block comes from a
+//    one-dword vector load issued early enough that its wait covers only the
+//    block being consumed, the loop runs whole rounds.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -51,9 +45,7 @@ constexpr int kLatent = 512;
 constexpr int kRope = 64;
 constexpr int kDv = 512;
 constexpr int kTileKeys = 128;  // planner tile
-constexpr int kBlockKeys = 16;  // keys per main-loop step
-constexpr int kStages = 2;
-constexpr int kMaxWaves = 4;    // 16-row waves per workgroup
+constexpr int kBlockKeys = 16;  // keys per pair-form step
 constexpr int kQSteps = 18;     // 16 latent + 2 rope k-steps of 32
 constexpr float kLazyLog2 = 8.0f;  // bf16 P: reference max may lag until p would exceed 2^8
 
@@ -107,277 +99,6 @@ __device__ __forceinline__ float pair32(float x, bool take_max) {
   const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
   return take_max ? fmaxf(a, b) : a + b;
 }
-
-// Raw bytes of one 16-key block as this lane loads them: each byte once, in
-// the layout of the QK^T operand (lane r16 + 16 g4 holds key kb + r16).
-struct RawRec {
-  uint4 kl[4][2];  // latent bytes 128 blk + 64 h + 16 g4 .. +15
-  uint4 kr[2];     // rope values 32 t + 8 g4 .. +7
-  float sc;        // block scale g4
-};
-
-// Per-wave LDS: the parked query operand, then the latent codes and scales of
-// the block being processed, from which the V^T operand is read back.
-constexpr int kQLdsBytes = kQSteps * 64 * 16;
-constexpr int kVRowBytes = kLatent + 16;  // rows 4 banks apart: the 16-byte stores of 8 rows hit distinct banks
-constexpr int kVScl = kBlockKeys * kVRowBytes;
-constexpr int kWaveLds = kQLdsBytes + kVScl + kBlockKeys * 16;
-
-// One work item (sequence chunk) for this wave's 16 query rows.
-template <bool CAUSAL_TAIL>
-__device__ __forceinline__ void mla_decode_item(const MlaParams& p, int item, int lane, int row0) {
-  const int r16 = lane & 15;
-  const int g4 = lane >> 4;
-
-  const int4 w = p.work[item];
-  const int b = w.x;
-  if (w.z <= w.y || b < 0 || b >= p.num_seqs) return;
-  const int ns = p.n_splits[b];
-  const bool direct = ns <= 1;
-  const int slot = w.w;
-  if (!direct && (slot < 0 || slot >= p.max_splits)) return;
-  if (row0 >= p.rows) return;
-
-  const int page_size = 1 << p.page_shift;
-  int L = p.seq_lens[b];
-  L = max(0, min(L, p.max_blocks * page_size));
-  // balanced plan items are key ranges, the one-item-per-workgroup plan's tile ranges
-  const int k_begin = p.bin_offsets ? w.y : w.y * kTileKeys;
-  const int k_end = min(p.bin_offsets ? w.z : w.z * kTileKeys, L);
-
-  // rows of this wave: n = row0 + r16 (token qi = n / h_q, head n % h_q)
-  const int n = row0 + r16;
-  const bool row_ok = n < p.rows;
-  const int qi = n / p.h_q;
-  const int qtok = b * p.q_len + qi;
-  const int qhead = n - qi * p.h_q;
-  const int lim = min(CAUSAL_TAIL ? L - p.q_len + qi : L - 1, k_end - 1);
-  const int qi_min = row0 / p.h_q;
-  const int lim_min = min(CAUSAL_TAIL ? L - p.q_len + qi_min : L - 1, k_end - 1);
-  const float c2 = p.scale_log2e;
-
-  // Q as the B operand of QK^T, same head-dim permutation as the K loads,
-  // parked in this wave's LDS region (k-step major, one 16-byte slot per
-  // lane, so each k-step is one conflict-free 16-byte read per lane). Only
-  // this wave reads its region, and LDS operations of a wave are ordered.
-  // dynamic LDS: blockDim.x / 64 waves x kWaveLds bytes
-  extern __shared__ __attribute__((aligned(16))) uint8_t wave_lds[];
-  uint8_t* const my_lds = wave_lds + (threadIdx.x >> 6) * kWaveLds;
-  bf16x8(*qw)[64] = reinterpret_cast<bf16x8(*)[64]>(my_lds);
-  uint8_t* const vlds = my_lds + kQLdsBytes;
-  {
-    const uint8_t* qrow = p.q + (int64_t)qtok * p.q_tok + (int64_t)qhead * p.q_head;
-    for (int k = 0; k < kQSteps; ++k) {
-      // k < 16: latent block k / 4, k-step k % 4; k >= 16: rope k-step k - 16
-      const int blk = k >> 2, s = k & 3;
-      const int d = k < 16 ? 128 * blk + 64 * (s >> 1) + 16 * g4 + 8 * (s & 1) : kLatent + 32 * (k - 16) + 8 * g4;
-      bf16x8 v;
-      if (row_ok) {
-        v = *reinterpret_cast<const bf16x8*>(qrow + 2 * d);
-      } else {
-        for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
-      }
-      qw[k][lane] = v;
-    }
-  }
-
-  f32x4 oacc[4][8];  // [d_v block gr][mt]: O^T[128 gr + 8 (4 g4 + i) + mt][n]
-  for (int gr = 0; gr < 4; ++gr)
-    for (int mt = 0; mt < 8; ++mt) oacc[gr][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_part = 0.f;
-
-  if (k_end > k_begin) {
-    const int32_t* bt = p.block_table + (int64_t)b * p.bt_row;
-    const int last_key = k_end - 1;
-    const int pmask = page_size - 1;
-    auto page_of = [&](int kb) -> int { return bt[min(kb, last_key) >> p.page_shift]; };
-    auto clamp_page = [&](int pg) -> int { return min(max(pg, 0), p.num_pages - 1); };
-    auto load_block = [&](int kb, int pg) {
-      RawRec r;
-      const uint8_t* lat0 = p.lat + (int64_t)pg * p.lat_page;
-      const uint8_t* rope0 = p.rope + (int64_t)pg * p.rope_page;
-      const uint8_t* scl0 = p.scl + (int64_t)pg * p.scl_page;
-      const int row = min(kb + r16, last_key) & pmask;
-      const uint8_t* lr = lat0 + (int64_t)row * p.lat_row;
-      for (int blk = 0; blk < 4; ++blk)
-        for (int h = 0; h < 2; ++h) r.kl[blk][h] = *reinterpret_cast<const uint4*>(lr + 128 * blk + 64 * h + 16 * g4);
-      const uint8_t* rr = rope0 + (int64_t)row * p.rope_row;
-      for (int t = 0; t < 2; ++t) r.kr[t] = *reinterpret_cast<const uint4*>(rr + 2 * (32 * t + 8 * g4));
-      r.sc = *reinterpret_cast<const float*>(scl0 + (int64_t)row * p.scl_row + 4 * g4);
-      return r;
-    };
-
-    // page ring: fetch u reads slot u % kStages and loads the page of fetch
-    // u + 2 into slot (u + 2) % kStages (slot indices are compile-time)
-    int pv[kStages];
-    pv[0] = page_of(k_begin);
-    pv[1 % kStages] = page_of(k_begin + kBlockKeys);
-    auto fetch = [&](RawRec& r, int kb, const int s) {
-      const int pg = clamp_page(__builtin_amdgcn_readlane(pv[s], 0));
-      r = load_block(kb, pg);
-      pv[(s + 2) % kStages] = page_of(kb + 2 * kBlockKeys);
-    };
-
-    auto process = [&](const RawRec& cur, int kb) {
-      // keep the q reads from LDS inside the loop (hoisting them would hold
-      // all 18 k-steps of q in registers again)
-      asm volatile("" ::: "memory");
-      // the block's latent codes and scales into this wave's LDS rows (the
-      // previous block's reads come first in the wave's in-order LDS queue)
-      for (int blk = 0; blk < 4; ++blk)
-        for (int h = 0; h < 2; ++h)
-          *reinterpret_cast<uint4*>(vlds + r16 * kVRowBytes + 128 * blk + 64 * h + 16 * g4) = cur.kl[blk][h];
-      *reinterpret_cast<float*>(vlds + kVScl + 16 * r16 + 4 * g4) = cur.sc;
-      // ---- S = K Q^T: one accumulator per 128-value block + rope -----------
-      f32x4 acc[4], accr = {0.f, 0.f, 0.f, 0.f};
-      for (int blk = 0; blk < 4; ++blk) {
-        acc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 a = e4m3x8_to_bf16(half_of(cur.kl[blk][s >> 1], s & 1));
-          acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qw[4 * blk + s][lane], acc[blk], 0, 0, 0);
-        }
-      }
-      for (int t = 0; t < 2; ++t)
-        accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.kr[t]), qw[16 + t][lane], accr, 0, 0, 0);
-      // lane holds S[key kb + 4 g4 + i][row n]; other lanes' stores are read
-      // back from here on
-      asm volatile("" ::: "memory");
-      float4 scl[4];
-      for (int i = 0; i < 4; ++i) scl[i] = *reinterpret_cast<const float4*>(vlds + kVScl + 16 * (4 * g4 + i));
-      float sv[4];
-      for (int i = 0; i < 4; ++i) {
-        const float4 sc = scl[i];
-        sv[i] = accr[i] + sc.x * acc[0][i] + sc.y * acc[1][i] + sc.z * acc[2][i] + sc.w * acc[3][i];
-      }
-      if (kb + kBlockKeys - 1 > lim_min) {
-        for (int i = 0; i < 4; ++i)
-          if (kb + 4 * g4 + i > lim) sv[i] = -INFINITY;
-      }
-      // ---- online softmax ---------------------------------------------------
-      // bf16 P: the reference max may lag until p would exceed 2^kLazyLog2
-      // (O lives in AGPRs, so a rescale is a full read-multiply-write pass)
-      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      mx = pair32(pair16(mx, true), true);
-      const float m_max = fmaxf(m_run, mx);
-      const bool move = m_run == -INFINITY ? m_max != -INFINITY : (m_max - m_run) * c2 > kLazyLog2;
-      const float m_new = move ? m_max : m_run;
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float corr = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
-      float pr[4], psum = 0.f;
-      for (int i = 0; i < 4; ++i) {
-        pr[i] = __builtin_amdgcn_exp2f((sv[i] - m_use) * c2);
-        psum += pr[i];
-      }
-      l_part = l_part * corr + psum;
-      if (__builtin_amdgcn_ballot_w64(move)) {
-        // O lives in AGPRs; written as plain C, the compiler copies all of it
-        // to VGPRs ahead of this rarely taken branch on every block. In place,
-        // each value goes AGPR -> VGPR -> AGPR only when a reference moves.
-        for (int gr = 0; gr < 4; ++gr)
-          for (int mt = 0; mt < 8; ++mt)
-            for (int i = 0; i < 4; ++i) {
-              float x = oacc[gr][mt][i], t;
-              asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                           : "+a"(x), "=&v"(t)
-                           : "v"(corr));
-              oacc[gr][mt][i] = x;
-            }
-      }
-      m_run = m_new;
-      // ---- O^T += V^T (P * scale)^T per 128-value block of d_v --------------
-      for (int gr = 0; gr < 4; ++gr) {
-        const float s0 = gr == 0 ? scl[0].x : gr == 1 ? scl[0].y : gr == 2 ? scl[0].z : scl[0].w;
-        const float s1 = gr == 0 ? scl[1].x : gr == 1 ? scl[1].y : gr == 2 ? scl[1].z : scl[1].w;
-        const float s2 = gr == 0 ? scl[2].x : gr == 1 ? scl[2].y : gr == 2 ? scl[2].z : scl[2].w;
-        const float s3 = gr == 0 ? scl[3].x : gr == 1 ? scl[3].y : gr == 2 ? scl[3].z : scl[3].w;
-        const bf16x4 pb = {(__bf16)(pr[0] * s0), (__bf16)(pr[1] * s1), (__bf16)(pr[2] * s2), (__bf16)(pr[3] * s3)};
-        // key 4 g4 + i, latent bytes 128 gr + 8 r16 .. +7 (one row's 128
-        // contiguous bytes per 16-lane group)
-        uint2 v[4];
-        for (int i = 0; i < 4; ++i)
-          v[i] = *reinterpret_cast<const uint2*>(vlds + (4 * g4 + i) * kVRowBytes + 128 * gr + 8 * r16);
-        for (int w2 = 0; w2 < 2; ++w2) {
-          const unsigned a0 = w2 ? v[0].y : v[0].x;
-          const unsigned a1 = w2 ? v[1].y : v[1].x;
-          const unsigned a2 = w2 ? v[2].y : v[2].x;
-          const unsigned a3 = w2 ? v[3].y : v[3].x;
-          const unsigned x01 = __builtin_amdgcn_perm(a0, a1, 0x01050004u);
-          const unsigned y01 = __builtin_amdgcn_perm(a0, a1, 0x03070206u);
-          const unsigned x23 = __builtin_amdgcn_perm(a2, a3, 0x01050004u);
-          const unsigned y23 = __builtin_amdgcn_perm(a2, a3, 0x03070206u);
-          for (int e = 0; e < 4; ++e) {
-            const unsigned s01 = (e >> 1) ? y01 : x01;
-            const unsigned s23 = (e >> 1) ? y23 : x23;
-            const bf16x2 lo = (e & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(s01, 1.0f, true)
-                                      : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(s01, 1.0f, false);
-            const bf16x2 hi = (e & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(s23, 1.0f, true)
-                                      : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(s23, 1.0f, false);
-            const bf16x4 a = {lo[0], lo[1], hi[0], hi[1]};
-            const int mt = 4 * w2 + e;
-            oacc[gr][mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, oacc[gr][mt], 0, 0, 0);
-          }
-        }
-      }
-    };
-
-    RawRec ring[kStages];
-#pragma unroll
-    for (int s = 0; s < kStages - 1; ++s) fetch(ring[s], k_begin + kBlockKeys * s, s);
-    const int rounds = (k_end - k_begin + kBlockKeys * kStages - 1) / (kBlockKeys * kStages);
-    for (int r = 0; r < rounds; ++r) {
-      const int kb0 = k_begin + r * kBlockKeys * kStages;
-#pragma unroll
-      for (int s = 0; s < kStages; ++s) {
-        const int kb = kb0 + kBlockKeys * s;
-        fetch(ring[(s + kStages - 1) % kStages], kb + kBlockKeys * (kStages - 1), (s + kStages - 1) % kStages);
-        process(ring[s], kb);
-      }
-    }
-  }
-
-  // ---- epilogue ---------------------------------------------------------------
-  const float l = pair32(pair16(l_part, false), false);
-  if (!row_ok) return;
-  const int64_t stat_row = (int64_t)b * p.rows + n;
-  const float m_nat = m_run == -INFINITY ? -INFINITY : m_run * p.scale;
-  if (direct) {
-    const float inv = l > 0.f ? p.o_scale / l : 0.f;
-    uint8_t* orow = p.o + (int64_t)qtok * p.o_tok + (int64_t)qhead * p.o_head;
-    for (int gr = 0; gr < 4; ++gr)
-      for (int i = 0; i < 4; ++i) {
-        bf16x8 out;
-        for (int mt = 0; mt < 8; ++mt) out[mt] = (__bf16)(oacc[gr][mt][i] * inv);
-        *reinterpret_cast<bf16x8*>(orow + 2 * (128 * gr + 32 * g4 + 8 * i)) = out;
-      }
-    if (g4 == 0) p.lse[stat_row] = l > 0.f ? m_nat + logf(l) : -INFINITY;
-  } else {
-    const int64_t prow = (int64_t)slot * p.num_seqs * p.rows + stat_row;
-    float* dst = p.ws_o + prow * kDv + 32 * g4;
-    for (int gr = 0; gr < 4; ++gr)
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 lo4 = {oacc[gr][0][i], oacc[gr][1][i], oacc[gr][2][i], oacc[gr][3][i]};
-        const f32x4 hi4 = {oacc[gr][4][i], oacc[gr][5][i], oacc[gr][6][i], oacc[gr][7][i]};
-        *reinterpret_cast<f32x4*>(dst + 128 * gr + 8 * i) = lo4;
-        *reinterpret_cast<f32x4*>(dst + 128 * gr + 8 * i + 4) = hi4;
-      }
-    if (g4 == 0) p.ws_ml[prow] = float2{m_nat, l};
-  }
-}
-
-// One wave per 16 query rows; a workgroup runs one work item, or with a
-// balanced plan the items of its bin one after the other.
-template <bool CAUSAL_TAIL>
-__global__ __launch_bounds__(64 * kMaxWaves) void mla_decode_kernel(MlaParams p) {
-  const int lane = threadIdx.x & 63;
-  const int row0 = 16 * (blockIdx.y * (blockDim.x >> 6) + (threadIdx.x >> 6));
-  int it = blockIdx.x, it_end = blockIdx.x + 1;
-  if (p.bin_offsets) {
-    it = p.bin_offsets[blockIdx.x];
-    it_end = p.bin_offsets[blockIdx.x + 1];
-  }
-  for (; it < it_end; ++it) mla_decode_item<CAUSAL_TAIL>(p, it, lane, row0);
-}
-
 
 // ---- multi-token form: records staged once per workgroup ---------------------
 // From 64 query rows on, the latent records of each 32-key block are
@@ -693,26 +414,289 @@ __global__ __launch_bounds__(64 * kLdsWaves) void mla_lds_kernel(MlaParams p, in
   }
 }
 
-// rows >= 64: the staged form; fewer rows: one 16-row wave per record stream
+// ---- pair form: fewer than 64 query rows -------------------------------------
+// Two waves per 16-row group split every record: wave h (HALF) takes latent
+// blocks 2h and 2h + 1 (d_v 256 h .. 256 h + 255) and rope k-step h. It loads
+// only those bytes, converts its latent codes to bf16 once (the QK^T operand,
+// also stored to its LDS rows, from which the V^T operand is read back with
+// the transpose load, see the staged form) and computes the partial S over
+// its part of d_qk. The pair swaps partial S through LDS (one barrier per
+// block); both add the two parts in the same order, so they hold identical S
+// and softmax statistics. O: 256 d_v x 16 rows = 64 VGPRs per lane, so two
+// waves fit on a SIMD. One or two row groups per workgroup.
+constexpr int kPairMaxGroups = 2;
+constexpr int kPairStages = 4;  // ring of 16-key blocks: three in flight while one is processed
+constexpr int kPairQSteps = 9;  // 8 latent k-steps + 1 rope k-step
+constexpr int kHalfRowBytes = 2 * (kDv / 2) + 32;  // bf16 half row + 32 B, swizzled as the staged rows
+constexpr int kPairV = kPairQSteps * 64 * 16;      // after the parked query
+constexpr int kPairScl = kPairV + kBlockKeys * kHalfRowBytes;
+constexpr int kPairX = kPairScl + kBlockKeys * 8;  // partial S, two slots (block parity)
+constexpr int kPairWaveBytes = kPairX + 2 * 64 * 16;
+
+struct HalfRec {
+  uint4 kl[2][2];  // key kb + r16: latent bytes 128 (2 HALF + j) + 64 h + 16 g4 .. +15
+  uint4 kr;        // key kb + r16: rope values 32 HALF + 8 g4 .. +7
+  float2 sc;       // key kb + r16: block scales 2 HALF, 2 HALF + 1
+};
+
+__device__ __forceinline__ int hrow_base(int row, int lane_off) {
+  return row * kHalfRowBytes + (lane_off ^ (((row >> 2) & 1) << 4));
+}
+
+template <bool CAUSAL_TAIL, int HALF>
+__device__ __forceinline__ void mla_pair_item(const MlaParams& p, int item, int tile, int groups, uint8_t* lds) {
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+  const int grp = w >> 1;
+
+  const int4 wk = p.work[item];
+  const int b = wk.x;
+  if (wk.z <= wk.y || b < 0 || b >= p.num_seqs) return;  // the whole workgroup returns
+  const int ns = p.n_splits[b];
+  const bool direct = ns <= 1;
+  const int slot = wk.w;
+  if (!direct && (slot < 0 || slot >= p.max_splits)) return;
+
+  const int page_size = 1 << p.page_shift;
+  int L = p.seq_lens[b];
+  L = max(0, min(L, p.max_blocks * page_size));
+  const int k_begin = p.bin_offsets ? wk.y : wk.y * kTileKeys;
+  const int k_end = min(p.bin_offsets ? wk.z : wk.z * kTileKeys, L);
+
+  // rows of this wave's group; a group past the last row still runs the loop
+  // (on a zero query) and meets every barrier
+  const int row0 = (tile * groups + grp) * 16;
+  const int n = row0 + r16;
+  const bool row_ok = n < p.rows;
+  const int qi = n / p.h_q;
+  const int qtok = b * p.q_len + qi;
+  const int qhead = n - qi * p.h_q;
+  const int lim = min(CAUSAL_TAIL ? L - p.q_len + qi : L - 1, k_end - 1);
+  const int qi_min = min(row0, p.rows - 1) / p.h_q;
+  const int lim_min = min(CAUSAL_TAIL ? L - p.q_len + qi_min : L - 1, k_end - 1);
+  const float c2 = p.scale_log2e;
+
+  uint8_t* const wl = lds + w * kPairWaveBytes;
+  uint8_t* const xl = lds + (w ^ 1) * kPairWaveBytes + kPairX;  // the partner's partial S
+  // this wave's part of the query as the QK^T B operand (k-steps of its two
+  // latent blocks, same head-dim permutation as the K loads, then its rope
+  // k-step); only this wave reads it
+  bf16x8(*qw)[64] = reinterpret_cast<bf16x8(*)[64]>(wl);
+  {
+    const uint8_t* qrow = p.q + (int64_t)qtok * p.q_tok + (int64_t)qhead * p.q_head;
+    for (int k = 0; k < kPairQSteps; ++k) {
+      const int blk = 2 * HALF + (k >> 2), s = k & 3;
+      const int d = k < 8 ? 128 * blk + 64 * (s >> 1) + 16 * g4 + 8 * (s & 1) : kLatent + 32 * HALF + 8 * g4;
+      bf16x8 v;
+      if (row_ok) {
+        v = *reinterpret_cast<const bf16x8*>(qrow + 2 * d);
+      } else {
+        for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
+      }
+      qw[k][lane] = v;
+    }
+  }
+
+  f32x4 oacc[2][8];  // [block j][16-row tile mt]: O^T[256 HALF + 128 j + 16 mt + 4 g4 + i][n]
+  for (int j = 0; j < 2; ++j)
+    for (int mt = 0; mt < 8; ++mt) oacc[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
+
+  if (k_end > k_begin) {
+    const int32_t* bt = p.block_table + (int64_t)b * p.bt_row;
+    const int last_key = k_end - 1;
+    const int pmask = page_size - 1;
+    auto page_of = [&](int kb) -> int { return bt[min(kb, last_key) >> p.page_shift]; };
+    auto clamp_page = [&](int pg) -> int { return min(max(pg, 0), p.num_pages - 1); };
+    auto load_block = [&](int kb, int pg) {
+      HalfRec r;
+      const int row = min(kb + r16, last_key) & pmask;
+      const uint8_t* lr = p.lat + (int64_t)pg * p.lat_page + (int64_t)row * p.lat_row + 256 * HALF;
+      for (int j = 0; j < 2; ++j)
+        for (int h = 0; h < 2; ++h) r.kl[j][h] = *reinterpret_cast<const uint4*>(lr + 128 * j + 64 * h + 16 * g4);
+      r.kr = *reinterpret_cast<const uint4*>(p.rope + (int64_t)pg * p.rope_page + (int64_t)row * p.rope_row +
+                                             2 * (32 * HALF + 8 * g4));
+      r.sc = *reinterpret_cast<const float2*>(p.scl + (int64_t)pg * p.scl_page + (int64_t)row * p.scl_row +
+                                              8 * HALF);
+      return r;
+    };
+    // page ring: fetch u reads slot u % kPairStages and loads the page of
+    // fetch u + kPairStages - 1 into the slot fetch u - 1 used. Loads complete
+    // in order, so the wait for that page must not come before the data of
+    // fetch u - 1 is due anyway: a shorter page distance would cut the ring.
+    constexpr int kPageAhead = kPairStages - 1;
+    int pv[kPairStages];
+    for (int u = 0; u < kPageAhead; ++u) pv[u] = page_of(k_begin + kBlockKeys * u);
+    auto fetch = [&](HalfRec& r, int kb, const int s) {
+      const int pg = clamp_page(__builtin_amdgcn_readlane(pv[s], 0));
+      r = load_block(kb, pg);
+      pv[(s + kPageAhead) % kPairStages] = page_of(kb + kPageAhead * kBlockKeys);
+    };
+
+    // this lane's transpose-read piece: key row 4 g4 + r16 / 4, bytes 8 (r16 % 4) ..
+    const int tr_base = hrow_base(4 * g4 + (r16 >> 2), 8 * (r16 & 3));
+    auto process = [&](const HalfRec& cur, int kb, const int xs) {
+      asm volatile("" ::: "memory");
+      // the four lanes of a key store the same scales (no branch: a divergent
+      // store here costs the loop its load-wait precision)
+      *reinterpret_cast<float2*>(wl + kPairScl + 8 * r16) = cur.sc;
+      // ---- partial S over this wave's latent blocks and rope k-step ------------
+      f32x4 acc[2];
+      for (int j = 0; j < 2; ++j) {
+        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 a = e4m3x8_to_bf16(half_of(cur.kl[j][s >> 1], s & 1));
+          *reinterpret_cast<bf16x8*>(wl + kPairV + hrow_base(r16, 32 * g4 + 16 * (s & 1)) + 256 * j +
+                                     128 * (s >> 1)) = a;
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qw[4 * j + s][lane], acc[j], 0, 0, 0);
+        }
+      }
+      const f32x4 accr =
+          __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.kr), qw[8][lane], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      // lane holds partial S[key kb + 4 g4 + i][row n]; other lanes' stores are
+      // read back from here on
+      asm volatile("" ::: "memory");
+      float2 scl[4];
+      for (int i = 0; i < 4; ++i) scl[i] = *reinterpret_cast<const float2*>(wl + kPairScl + 8 * (4 * g4 + i));
+      f32x4 part;
+      for (int i = 0; i < 4; ++i) part[i] = accr[i] + scl[i].x * acc[0][i] + scl[i].y * acc[1][i];
+      *reinterpret_cast<f32x4*>(wl + kPairX + xs * 1024 + 16 * lane) = part;
+      __syncthreads();
+      const f32x4 other = *reinterpret_cast<const f32x4*>(xl + xs * 1024 + 16 * lane);
+      float sv[4];
+      for (int i = 0; i < 4; ++i) sv[i] = part[i] + other[i];  // the same sum in both waves
+      if (kb + kBlockKeys - 1 > lim_min) {
+        for (int i = 0; i < 4; ++i)
+          if (kb + 4 * g4 + i > lim) sv[i] = -INFINITY;
+      }
+      // ---- online softmax (bf16 P: the reference max may lag) -----------------
+      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      mx = pair32(pair16(mx, true), true);
+      const float m_max = fmaxf(m_run, mx);
+      const bool move = m_run == -INFINITY ? m_max != -INFINITY : (m_max - m_run) * c2 > kLazyLog2;
+      const float m_new = move ? m_max : m_run;
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float corr = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
+      float pr[4], psum = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f((sv[i] - m_use) * c2);
+        psum += pr[i];
+      }
+      l_part = l_part * corr + psum;
+      if (__builtin_amdgcn_ballot_w64(move)) {
+        for (int j = 0; j < 2; ++j)
+          for (int mt = 0; mt < 8; ++mt) oacc[j][mt] *= corr;
+      }
+      m_run = m_new;
+      // ---- O^T += V^T (P * scale)^T for this wave's 256 d_v -------------------
+      for (int j = 0; j < 2; ++j) {
+        bf16x4 pb;  // P scaled by the block scale of latent block 2 HALF + j
+        for (int i = 0; i < 4; ++i) pb[i] = (__bf16)(pr[i] * (j ? scl[i].y : scl[i].x));
+        for (int mt = 0; mt < 8; ++mt) {
+          const s16x4 t4 = lds_read_tr16(wl + kPairV + tr_base + 256 * j + 32 * mt);
+          bf16x4 a;
+          __builtin_memcpy(&a, &t4, 8);
+          oacc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, oacc[j][mt], 0, 0, 0);
+        }
+      }
+    };
+
+    // Rounds of kPairStages blocks keep ring slots and exchange slots (block
+    // parity) compile-time; blocks past the chunk load clamped rows and are
+    // masked, so both waves of a pair run the same barriers.
+    // The prologue issues its loads in loop order (no reordering across the
+    // fences): the waits at the loop head serve both entry paths, so a
+    // reshuffled prologue would make them wait for more than the oldest block.
+    HalfRec ring[kPairStages];
+#pragma unroll
+    for (int s = 0; s < kPairStages - 1; ++s) {
+      fetch(ring[s], k_begin + kBlockKeys * s, s);
+      asm volatile("" ::: "memory");
+    }
+    const int rounds = (k_end - k_begin + kBlockKeys * kPairStages - 1) / (kBlockKeys * kPairStages);
+    for (int r = 0; r < rounds; ++r) {
+      const int kb0 = k_begin + r * kBlockKeys * kPairStages;
+#pragma unroll
+      for (int s = 0; s < kPairStages; ++s) {
+        const int kb = kb0 + kBlockKeys * s;
+        fetch(ring[(s + kPairStages - 1) % kPairStages], kb + kBlockKeys * (kPairStages - 1),
+              (s + kPairStages - 1) % kPairStages);
+        process(ring[s], kb, s & 1);
+      }
+    }
+  }
+
+  // ---- epilogue: this wave's d_v half; LSE / (max, sum) from the first half -------
+  const float l = pair32(pair16(l_part, false), false);
+  if (!row_ok) return;
+  const int64_t stat_row = (int64_t)b * p.rows + n;
+  const float m_nat = m_run == -INFINITY ? -INFINITY : m_run * p.scale;
+  const int d0 = 256 * HALF + 4 * g4;
+  if (direct) {
+    const float inv = l > 0.f ? p.o_scale / l : 0.f;
+    uint8_t* orow = p.o + (int64_t)qtok * p.o_tok + (int64_t)qhead * p.o_head;
+    for (int j = 0; j < 2; ++j)
+      for (int mt = 0; mt < 8; ++mt) {
+        bf16x4 out;
+        for (int i = 0; i < 4; ++i) out[i] = (__bf16)(oacc[j][mt][i] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 2 * (d0 + 128 * j + 16 * mt)) = out;
+      }
+    if (HALF == 0 && g4 == 0) p.lse[stat_row] = l > 0.f ? m_nat + logf(l) : -INFINITY;
+  } else {
+    const int64_t prow = (int64_t)slot * p.num_seqs * p.rows + stat_row;
+    float* dst = p.ws_o + prow * kDv + d0;
+    for (int j = 0; j < 2; ++j)
+      for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(dst + 128 * j + 16 * mt) = oacc[j][mt];
+    if (HALF == 0 && g4 == 0) p.ws_ml[prow] = float2{m_nat, l};
+  }
+}
+
+// Grid (work items or bins, q-row tiles of 16 * groups rows); block 128 *
+// groups threads; the half is a template parameter of the item, chosen once
+// per wave.
+template <bool CAUSAL_TAIL>
+__global__ __launch_bounds__(128 * kPairMaxGroups) __attribute__((amdgpu_waves_per_eu(2)))
+void mla_pair_kernel(MlaParams p, int groups) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t mla_pair_lds[];
+  int it = blockIdx.x, it_end = blockIdx.x + 1;
+  if (p.bin_offsets) {
+    it = p.bin_offsets[blockIdx.x];
+    it_end = p.bin_offsets[blockIdx.x + 1];
+  }
+  const bool odd = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1;
+  for (; it < it_end; ++it) {
+    if (odd)
+      mla_pair_item<CAUSAL_TAIL, 1>(p, it, blockIdx.y, groups, mla_pair_lds);
+    else
+      mla_pair_item<CAUSAL_TAIL, 0>(p, it, blockIdx.y, groups, mla_pair_lds);
+    __syncthreads();  // the next item's query overwrites LDS
+  }
+}
+
+// rows >= 64: the staged form; fewer rows: the pair form
 bool staged(const pkv_decode_args& a) { return a.q_len * a.h_q >= kLdsRows; }
+
+int pair_groups(const pkv_decode_args& a) {
+  const int g = (a.q_len * a.h_q + 15) / 16;
+  return g < kPairMaxGroups ? g : kPairMaxGroups;
+}
 
 const void* select_kernel(const pkv_decode_args& a) {
   const bool ct = a.causal && a.q_len > 1;
   if (staged(a))
     return ct ? reinterpret_cast<const void*>(&mla_lds_kernel<true>)
               : reinterpret_cast<const void*>(&mla_lds_kernel<false>);
-  return ct ? reinterpret_cast<const void*>(&mla_decode_kernel<true>)
-            : reinterpret_cast<const void*>(&mla_decode_kernel<false>);
+  return ct ? reinterpret_cast<const void*>(&mla_pair_kernel<true>)
+            : reinterpret_cast<const void*>(&mla_pair_kernel<false>);
 }
 
-int waves_per_wg(const pkv_decode_args& a) {
-  if (staged(a)) return kLdsWaves;
-  const int blocks = (a.q_len * a.h_q + 15) / 16;
-  return blocks < kMaxWaves ? blocks : kMaxWaves;
-}
+int waves_per_wg(const pkv_decode_args& a) { return staged(a) ? kLdsWaves : 2 * pair_groups(a); }
 
 size_t dyn_lds_bytes(const pkv_decode_args& a) {
-  return staged(a) ? (size_t)2 * kStageBytes : (size_t)waves_per_wg(a) * kWaveLds;
+  if (staged(a)) return (size_t)2 * kStageBytes;
+  return (size_t)2 * pair_groups(a) * kPairWaveBytes;
 }
 
 int log2_exact(int x) {
@@ -723,7 +707,9 @@ int log2_exact(int x) {
 
 }  // namespace
 
-int mla_rows_per_tile(const pkv_decode_args& a) { return staged(a) ? kLdsRows : 16 * waves_per_wg(a); }
+const char* mla_kernel_name(const pkv_decode_args& a) { return staged(a) ? "mla_lds_kernel" : "mla_pair_kernel"; }
+
+int mla_rows_per_tile(const pkv_decode_args& a) { return staged(a) ? kLdsRows : 16 * pair_groups(a); }
 
 hipError_t mla_occupancy(const pkv_decode_args& a, int* units_per_cu) {
   // one unit = one workgroup (all rows of one q-row tile of a work item)
@@ -777,7 +763,8 @@ hipError_t mla_launch(const pkv_decode_args& a, hipStream_t stream) {
     return hipLaunchKernel(select_kernel(a), dim3((unsigned)(units * tiles)), dim3(64 * wpw), args,
                            dyn_lds_bytes(a), stream);
   }
-  void* args[] = {&p};
+  int groups = pair_groups(a);
+  void* args[] = {&p, &groups};
   return hipLaunchKernel(select_kernel(a), dim3((unsigned)units, (unsigned)tiles), dim3(64 * wpw), args,
                          dyn_lds_bytes(a), stream);
 }

@@ -30,6 +30,7 @@ hipError_t gqa_launch(const pkv_decode_args& a, const GqaVariant& v, hipStream_t
 
 // Latent-record (MLA) family.
 int mla_rows_per_tile(const pkv_decode_args& a);
+const char* mla_kernel_name(const pkv_decode_args& a);  // "mla_pair_kernel" or "mla_lds_kernel"
 hipError_t mla_occupancy(const pkv_decode_args& a, int* wg_per_cu);
 hipError_t mla_launch(const pkv_decode_args& a, hipStream_t stream);
 

@@ -130,6 +130,11 @@ class PagedDecode:
         self.plan = plan
 
     @property
+    def kernel_name(self):
+        """The device kernel run() launches for these arguments."""
+        return native.decode_kernel_name(self.args)
+
+    @property
     def has_splits(self):
         return self.plan_info.max_n_splits > 1
 

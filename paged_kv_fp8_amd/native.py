@@ -21,7 +21,8 @@ PKV_MAX_SPLITS = 256
 # Every function the header declares, in declaration order.
 EXPORTS = ("pkv_status_string", "pkv_last_error", "pkv_version", "pkv_decode_args_size", "pkv_plan_split_kv",
            "pkv_plan_balanced", "pkv_workspace_bytes", "pkv_decode_slots", "pkv_paged_decode_attn",
-           "pkv_merge_splits", "pkv_quantize_q", "pkv_quant_q_args_size", "pkv_write_kv", "pkv_kv_write_args_size")
+           "pkv_merge_splits", "pkv_quantize_q", "pkv_quant_q_args_size", "pkv_write_kv", "pkv_kv_write_args_size",
+           "pkv_decode_kernel_name")
 
 
 class PkvError(RuntimeError):
@@ -113,6 +114,8 @@ def _load():
                                       _i32, P(PlanInfo)]
     lib.pkv_workspace_bytes.restype = ctypes.c_size_t
     lib.pkv_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
+    lib.pkv_decode_kernel_name.restype = ctypes.c_char_p
+    lib.pkv_decode_kernel_name.argtypes = [P(DecodeArgs)]
     lib.pkv_decode_slots.restype = _i32
     lib.pkv_decode_slots.argtypes = [P(DecodeArgs), P(_i32), P(_i32), P(_i32)]
     lib.pkv_paged_decode_attn.restype = _i32
@@ -201,6 +204,14 @@ def decode_slots(args):
     _check(lib.pkv_decode_slots(ctypes.byref(args), ctypes.byref(cu), ctypes.byref(wg), ctypes.byref(nt)),
            "pkv_decode_slots")
     return cu.value, wg.value, nt.value
+
+
+def decode_kernel_name(args):
+    """Name of the kernel pkv_paged_decode_attn launches for `args`."""
+    name = lib.pkv_decode_kernel_name(ctypes.byref(args))
+    if name is None:
+        raise PkvError(PKV_ERR_INVALID_ARG, "pkv_decode_kernel_name", lib.pkv_last_error().decode())
+    return name.decode()
 
 
 def paged_decode_attn(args, stream=None):

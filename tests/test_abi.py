@@ -162,6 +162,19 @@ def test_decode_rejects_invalid_arguments_without_touching_the_gpu(native, over,
         assert native.last_error()
 
 
+def test_decode_kernel_name_follows_the_shapes(native):
+    assert native.decode_kernel_name(_valid_args(native)) == "gqa_decode_kernel"
+    mla = dict(kv_format=1, h_k=1, h_q=16, d_qk=576, d_v=512)
+    # fewer than 64 query rows per sequence: the pair form; 64 and more: the staged form
+    for q_len, name in ((1, "mla_pair_kernel"), (3, "mla_pair_kernel"), (4, "mla_lds_kernel"), (16, "mla_lds_kernel")):
+        assert native.decode_kernel_name(_valid_args(native, q_len=q_len, **mla)) == name, q_len
+    assert native.decode_kernel_name(_valid_args(native, q_len=8, **{**mla, "h_q": 8})) == "mla_lds_kernel"
+    assert native.decode_kernel_name(_valid_args(native, q_len=4, **{**mla, "h_q": 8})) == "mla_pair_kernel"
+    with pytest.raises(native.PkvError):
+        native.decode_kernel_name(_valid_args(native, h_q=6, h_k=4))
+    assert native.lib.pkv_decode_kernel_name(None) is None
+
+
 def test_merge_validates_and_is_a_noop_without_splits(native):
     a = _valid_args(native)
     assert native.lib.pkv_merge_splits(ctypes.byref(a), None) == 0  # max_splits == 1: nothing launched

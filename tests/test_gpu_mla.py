@@ -72,7 +72,7 @@ def test_latent_edge_lengths(T, force):
 
 @pytest.mark.parametrize("T", [2, 8])
 def test_latent_repeat_bitwise(T):
-    # T = 2: one 16-row wave per record stream; T = 8: records staged in LDS for four waves
+    # T = 2: the pair form (two row groups, record split by d_v half); T = 8: records staged in LDS
     w = workload(5, q_len=T, num_seqs=6, seq_len_dist=("uniform", 100, 3000))
     batch = make_batch(w, device="cuda")
     dec = run_batch(batch)
