@@ -454,16 +454,19 @@ __device__ __forceinline__ void mla_pair_item(const MlaParams& p, int item, int 
   const int4 wk = p.work[item];
   const int b = wk.x;
   if (wk.z <= wk.y || b < 0 || b >= p.num_seqs) return;  // the whole workgroup returns
-  const int ns = p.n_splits[b];
-  const bool direct = ns <= 1;
-  const int slot = wk.w;
-  if (!direct && (slot < 0 || slot >= p.max_splits)) return;
-
-  const int page_size = 1 << p.page_shift;
-  int L = p.seq_lens[b];
-  L = max(0, min(L, p.max_blocks * page_size));
   const int k_begin = p.bin_offsets ? wk.y : wk.y * kTileKeys;
-  const int k_end = min(p.bin_offsets ? wk.z : wk.z * kTileKeys, L);
+  const int k_plan = p.bin_offsets ? wk.z : wk.z * kTileKeys;  // planned end: lengths of the plan are upper bounds
+  const int32_t* bt = p.block_table + (int64_t)b * p.bt_row;
+
+  // Start-up: the block-table entries of the first fetches, the query, the
+  // split count and the sequence length are independent loads, issued
+  // together (one round trip where a dependent chain takes three). The
+  // entries are those of the planned chunk; when the runtime length ends the
+  // chunk before the last of them, they are loaded again below.
+  constexpr int kPageAhead = kPairStages - 1;
+  int pv[kPairStages];
+  for (int u = 0; u < kPageAhead; ++u)
+    pv[u] = bt[min(min(k_begin + kBlockKeys * u, k_plan - 1) >> p.page_shift, p.max_blocks - 1)];
 
   // rows of this wave's group; a group past the last row still runs the loop
   // (on a zero query) and meets every barrier
@@ -473,6 +476,33 @@ __device__ __forceinline__ void mla_pair_item(const MlaParams& p, int item, int 
   const int qi = n / p.h_q;
   const int qtok = b * p.q_len + qi;
   const int qhead = n - qi * p.h_q;
+  // this wave's part of the query as the QK^T B operand (k-steps of its two
+  // latent blocks, same head-dim permutation as the K loads, then its rope
+  // k-step), parked in LDS below; only this wave reads it. Rows past the last
+  // load the last row (no branch) and are zeroed.
+  bf16x8 qreg[kPairQSteps];
+  {
+    const int nq = row_ok ? n : p.rows - 1;
+    const int qiq = nq / p.h_q;
+    const uint8_t* qrow = p.q + (int64_t)(b * p.q_len + qiq) * p.q_tok + (int64_t)(nq - qiq * p.h_q) * p.q_head;
+    for (int k = 0; k < kPairQSteps; ++k) {
+      const int blk = 2 * HALF + (k >> 2), s = k & 3;
+      const int d = k < 8 ? 128 * blk + 64 * (s >> 1) + 16 * g4 + 8 * (s & 1) : kLatent + 32 * HALF + 8 * g4;
+      qreg[k] = *reinterpret_cast<const bf16x8*>(qrow + 2 * d);
+    }
+  }
+  const int ns = p.n_splits[b];
+  int L = p.seq_lens[b];
+  if (!row_ok)
+    for (int k = 0; k < kPairQSteps; ++k)
+      for (int e = 0; e < 8; ++e) qreg[k][e] = (__bf16)0.0f;
+
+  const bool direct = ns <= 1;
+  const int slot = wk.w;
+  if (!direct && (slot < 0 || slot >= p.max_splits)) return;
+  const int page_size = 1 << p.page_shift;
+  L = max(0, min(L, p.max_blocks * page_size));
+  const int k_end = min(k_plan, L);
   const int lim = min(CAUSAL_TAIL ? L - p.q_len + qi : L - 1, k_end - 1);
   const int qi_min = min(row0, p.rows - 1) / p.h_q;
   const int lim_min = min(CAUSAL_TAIL ? L - p.q_len + qi_min : L - 1, k_end - 1);
@@ -480,24 +510,8 @@ __device__ __forceinline__ void mla_pair_item(const MlaParams& p, int item, int 
 
   uint8_t* const wl = lds + w * kPairWaveBytes;
   uint8_t* const xl = lds + (w ^ 1) * kPairWaveBytes + kPairX;  // the partner's partial S
-  // this wave's part of the query as the QK^T B operand (k-steps of its two
-  // latent blocks, same head-dim permutation as the K loads, then its rope
-  // k-step); only this wave reads it
   bf16x8(*qw)[64] = reinterpret_cast<bf16x8(*)[64]>(wl);
-  {
-    const uint8_t* qrow = p.q + (int64_t)qtok * p.q_tok + (int64_t)qhead * p.q_head;
-    for (int k = 0; k < kPairQSteps; ++k) {
-      const int blk = 2 * HALF + (k >> 2), s = k & 3;
-      const int d = k < 8 ? 128 * blk + 64 * (s >> 1) + 16 * g4 + 8 * (s & 1) : kLatent + 32 * HALF + 8 * g4;
-      bf16x8 v;
-      if (row_ok) {
-        v = *reinterpret_cast<const bf16x8*>(qrow + 2 * d);
-      } else {
-        for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
-      }
-      qw[k][lane] = v;
-    }
-  }
+  for (int k = 0; k < kPairQSteps; ++k) qw[k][lane] = qreg[k];
 
   f32x4 oacc[2][8];  // [block j][16-row tile mt]: O^T[256 HALF + 128 j + 16 mt + 4 g4 + i][n]
   for (int j = 0; j < 2; ++j)
@@ -505,11 +519,13 @@ __device__ __forceinline__ void mla_pair_item(const MlaParams& p, int item, int 
   float m_run = -INFINITY, l_part = 0.f;
 
   if (k_end > k_begin) {
-    const int32_t* bt = p.block_table + (int64_t)b * p.bt_row;
     const int last_key = k_end - 1;
     const int pmask = page_size - 1;
     auto page_of = [&](int kb) -> int { return bt[min(kb, last_key) >> p.page_shift]; };
     auto clamp_page = [&](int pg) -> int { return min(max(pg, 0), p.num_pages - 1); };
+    // the early entries are right unless the chunk ends before the last of them
+    if (k_begin + kBlockKeys * (kPageAhead - 1) > last_key)
+      for (int u = 0; u < kPageAhead; ++u) pv[u] = page_of(k_begin + kBlockKeys * u);
     auto load_block = [&](int kb, int pg) {
       HalfRec r;
       const int row = min(kb + r16, last_key) & pmask;
@@ -523,12 +539,9 @@ __device__ __forceinline__ void mla_pair_item(const MlaParams& p, int item, int 
       return r;
     };
     // page ring: fetch u reads slot u % kPairStages and loads the page of
-    // fetch u + kPairStages - 1 into the slot fetch u - 1 used. Loads complete
-    // in order, so the wait for that page must not come before the data of
+    // fetch u + kPageAhead into the slot fetch u - 1 used. Loads complete in
+    // order, so the wait for that page must not come before the data of
     // fetch u - 1 is due anyway: a shorter page distance would cut the ring.
-    constexpr int kPageAhead = kPairStages - 1;
-    int pv[kPairStages];
-    for (int u = 0; u < kPageAhead; ++u) pv[u] = page_of(k_begin + kBlockKeys * u);
     auto fetch = [&](HalfRec& r, int kb, const int s) {
       const int pg = clamp_page(__builtin_amdgcn_readlane(pv[s], 0));
       r = load_block(kb, pg);
