@@ -228,9 +228,12 @@ def main():
     ap.add_argument("--page-size", type=int, default=None, help="override the workload's page size")
     ap.add_argument("--contiguous-pages", action="store_true", help="hand out pages in order instead of shuffled")
     ap.add_argument("--seq-len", type=int, default=None, help="give every sequence this length")
-    ap.add_argument("--plan", default="wave", choices=["wave", "balanced"],
+    ap.add_argument("--plan", default="wave", choices=["wave", "balanced", "queued"],
                     help="wave: one work item per workgroup (occupancy-pinned split plan); balanced: contiguous "
-                         "equal shares of all keys, one per workgroup")
+                         "equal shares of all keys, one per workgroup; queued: persistent workgroups, packed "
+                         "static bins then a shared queue")
+    ap.add_argument("--dyn-percent", type=int, default=10, help="queued plan: share of the work left to the queue")
+    ap.add_argument("--pieces-per-bin", type=int, default=3, help="queued plan: pieces a bin's share is cut into")
     ap.add_argument("--fused-merge", action="store_true",
                     help="merge split sequences inside the decode kernel (last split merges) instead of a second launch")
     ap.add_argument("--step-mode", default="graph", choices=["graph", "eager"],
@@ -290,7 +293,9 @@ def main():
     lens = first.seq_lens.cpu().numpy()
     batches = [first] + [make_batch(dataclasses.replace(w, seed=w.seed + 1000 * i), device="cuda", seq_lens=lens)
                          for i in range(1, pools)]
-    decs = [decode.for_batch(b, wg_per_cu=args.wg_per_cu, fused_merge=args.fused_merge, plan=args.plan) for b in batches]
+    decs = [decode.for_batch(b, wg_per_cu=args.wg_per_cu, fused_merge=args.fused_merge, plan=args.plan,
+                             **({"dyn_percent": args.dyn_percent, "pieces_per_bin": args.pieces_per_bin}
+                                if args.plan == "queued" else {})) for b in batches]
     info = decs[0].plan_info
     ab = algorithmic_bytes(first, decs[0])
     log(f"workload {w.name}: {w.num_seqs} seqs, {int(lens.sum())} tokens, KV {ab['kv'] / 1e6:.1f} MB, "

@@ -23,8 +23,8 @@
  * "Workspace"; "MiniMax MSA fmha_sm100/cute README", Paged FP8 Decode,
  * plan() then run()):
  *   1. pkv_decode_slots()   -> CU count, resident workgroups per CU, q-row tiles
- *   2. pkv_plan_split_kv() or pkv_plan_balanced() -> host work list +
- *      n_splits (+ bin offsets) (pure host code)
+ *   2. pkv_plan_split_kv(), pkv_plan_balanced() or pkv_plan_queued() -> host
+ *      work list + n_splits (+ bin offsets) (pure host code)
  *   3. copy work / n_splits to the device once (the caller's job)
  *   4. pkv_paged_decode_attn(); then pkv_merge_splits() when any sequence
  *      was split (info.max_n_splits > 1). Both only enqueue on `stream`:
@@ -91,7 +91,8 @@ typedef struct pkv_plan_info {
   int32_t chunk_tiles;  /* 128-key tiles per chunk (a sequence's last chunk may be shorter) */
   int32_t slots;        /* work items that fit one wave of the grid */
   int32_t max_n_splits; /* largest n_splits over the batch */
-  int32_t num_bins;     /* balanced plan: workgroups (bins) of the grid; 0 for pkv_plan_split_kv */
+  int32_t num_bins;     /* balanced / queued plan: workgroups (bins) of the grid; 0 for pkv_plan_split_kv */
+  int32_t num_dynamic;  /* queued plan: items in the shared queue (after the bins' items); 0 otherwise */
 } pkv_plan_info;
 
 /*
@@ -151,6 +152,48 @@ pkv_status pkv_plan_balanced(const int32_t* seq_lens, int32_t num_seqs, int32_t 
                              int32_t cu_count, int32_t wg_per_cu, int32_t max_splits, int32_t* work_out,
                              int32_t work_cap, int32_t* n_splits_out, int32_t* bin_offsets_out, int32_t bins_cap,
                              pkv_plan_info* info);
+
+/*
+ * Queued plan (this library's own planner; not from the pages). Its aim is
+ * that the workgroups finish together, even when sequence lengths differ
+ * and compute units or XCDs stream at different rates. With 32-key blocks
+ * (max(1, ceil(L / 32)) per sequence), total = their sum and
+ * bins = max(1, min(total, cu_count * wg_per_cu / (h_k * n_q_tiles))):
+ *   piece  = max(1, floor(total / (bins * pieces_per_bin)))   piece cap, blocks
+ *   budget = floor(total * (100 - dyn_percent) / (100 * bins)) static load of a bin
+ *   c_b    = max(piece, ceil(blocks_b / max_splits))
+ *   n_b    = ceil(blocks_b / c_b) pieces of sequence b; piece j covers blocks
+ *            [floor(j * blocks_b / n_b), floor((j + 1) * blocks_b / n_b)) and
+ *            uses split slot j (n_splits[b] = n_b).
+ * Pieces are taken longest first (ties: sequence, then piece order). Each
+ * goes to the bin with the smallest load (lowest index among equals). Bins
+ * are then visited in order. While a bin holds more than one piece and its
+ * load exceeds the budget, it moves its most recently assigned piece to the
+ * queue. The queue runs in the same longest-first order. Work items are
+ * (seq, key_begin, key_end, split_slot) in KEYS: key_begin = 32 * first
+ * block, key_end = 32 * end block. key_end may pass L; the decode clamps to
+ * the runtime length. Bin i's items are [bin_offsets[i], bin_offsets[i+1]).
+ * The queue's items follow, [bin_offsets[bins], num_work).
+ * The decode runs one persistent workgroup per bin, per kv-head group and
+ * q-row tile. Each workgroup runs its bin's items, then takes queue items
+ * until the queue is empty. Piece boundaries are fixed by the plan, so the
+ * result does not depend on which workgroup ran which piece.
+ *
+ * seq_lens        host int32[num_seqs], each >= 0
+ * pieces_per_bin  >= 1: pieces a bin's share is cut into (finer balance,
+ *                 more split partials)
+ * dyn_percent     share of the work kept for the queue, 0 .. 90
+ * work_out        host int32[work_cap][4]
+ * n_splits_out    host int32[num_seqs]
+ * bin_offsets_out host int32[bins_cap]; bins + 1 entries are written
+ * info            host, may be NULL (num_bins = bins, num_dynamic = queue length)
+ * Errors: as pkv_plan_balanced; INVALID_ARG for pieces_per_bin < 1 or
+ * dyn_percent outside [0, 90].
+ */
+pkv_status pkv_plan_queued(const int32_t* seq_lens, int32_t num_seqs, int32_t h_k, int32_t n_q_tiles,
+                           int32_t cu_count, int32_t wg_per_cu, int32_t max_splits, int32_t pieces_per_bin,
+                           int32_t dyn_percent, int32_t* work_out, int32_t work_cap, int32_t* n_splits_out,
+                           int32_t* bin_offsets_out, int32_t bins_cap, pkv_plan_info* info);
 
 /* ------------------------------------------------------------------------ */
 /* Decode launch arguments                                                   */
@@ -243,6 +286,16 @@ typedef struct pkv_decode_args {
    * holds 128-key TILE ranges (pkv_plan_split_kv). */
   const int32_t* bin_offsets;
   int32_t num_bins;
+  /* Optional, device int32[2 * h_k * n_q_tiles] (e4m3 K/V cache only), for a
+   * plan from pkv_plan_queued: when non-NULL (bin_offsets required), the
+   * grid has num_bins persistent workgroups per (kv-head group, q-row tile).
+   * Each runs the items of its bin one after another, then takes queue
+   * items [bin_offsets[num_bins], num_work) from a shared counter until none
+   * is left. The counters must be zero before the first call. Every
+   * completed call leaves them zero (the last workgroup to finish resets
+   * them), so no per-call clearing is needed and the launch can be replayed
+   * in a HIP graph. Calls that overlap on one counter array race. */
+  int32_t* queue;
 } pkv_decode_args;
 
 /* Bytes of split workspace: max_splits * num_seqs * h_k * n_rows * (d_v + 2)

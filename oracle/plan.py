@@ -143,3 +143,69 @@ def plan_balanced(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16
                 seen[b] += 1
         offsets.append(len(work))
     return work, pieces, offsets, bins
+
+
+def plan_queued(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16, pieces_per_bin=3, dyn_percent=10):
+    """Queued plan (this build's own planner, not the pages'), written out step
+    by step:
+      1. blocks_b = max(1, ceil(L_b / 32)); total = sum; bins = the slots of
+         the rule above, at most total;
+      2. piece = max(1, total // (bins * pieces_per_bin)),
+         budget = total * (100 - dyn_percent) // (100 * bins);
+      3. sequence b is cut into n_b = ceil(blocks_b / max(piece,
+         ceil(blocks_b / max_splits))) pieces, piece j covering blocks
+         [j * blocks_b // n_b, (j + 1) * blocks_b // n_b), split slot j;
+      4. pieces, longest first (ties: sequence, then piece), each go to the
+         least loaded bin (lowest index among equals);
+      5. bins in order hand their most recently assigned piece to the queue
+         while they hold more than one piece and their load exceeds budget;
+      6. the queue keeps the order of step 4.
+    Work items (seq, 32 * first block, 32 * end block, slot) are listed bin
+    by bin, then the queue. Returns (work, n_splits, bin_offsets[bins + 1],
+    bins, queue length)."""
+    seq_lens = [int(x) for x in seq_lens]
+    if not seq_lens:
+        raise ValueError("empty batch")
+    if any(x < 0 for x in seq_lens):
+        raise ValueError("negative sequence length")
+    if min(h_k, n_q_tiles, cu_count, wg_per_cu, max_splits, pieces_per_bin) < 1:
+        raise ValueError("sizes must be positive")
+    if not 0 <= dyn_percent <= 90:
+        raise ValueError("dyn_percent outside [0, 90]")
+    blocks = [max(1, _ceil_div(L, BALANCE_BLOCK_KEYS)) for L in seq_lens]
+    total = sum(blocks)
+    bins = max(1, min(total, (cu_count * wg_per_cu) // (h_k * n_q_tiles)))
+    piece = max(1, total // (bins * pieces_per_bin))
+    budget = total * (100 - dyn_percent) // (100 * bins)
+
+    pieces, n_splits = [], []
+    for b, bl in enumerate(blocks):
+        n = _ceil_div(bl, max(piece, _ceil_div(bl, max_splits)))
+        n_splits.append(n)
+        pieces.extend((b, j * bl // n, (j + 1) * bl // n, j) for j in range(n))
+    order = sorted(range(len(pieces)), key=lambda i: (-(pieces[i][2] - pieces[i][1]), i))
+    loads = [0] * bins
+    members = [[] for _ in range(bins)]
+    for i in order:
+        k = min(range(bins), key=lambda x: (loads[x], x))
+        loads[k] += pieces[i][2] - pieces[i][1]
+        members[k].append(i)
+    rank = {i: r for r, i in enumerate(order)}
+    queue = []
+    for k in range(bins):
+        while len(members[k]) > 1 and loads[k] > budget:
+            i = members[k].pop()
+            loads[k] -= pieces[i][2] - pieces[i][1]
+            queue.append(i)
+    queue.sort(key=lambda i: rank[i])
+
+    def item(i):
+        b, first, end, slot = pieces[i]
+        return (b, BALANCE_BLOCK_KEYS * first, BALANCE_BLOCK_KEYS * end, slot)
+
+    work, offsets = [], [0]
+    for k in range(bins):
+        work.extend(item(i) for i in members[k])
+        offsets.append(len(work))
+    work.extend(item(i) for i in queue)
+    return work, n_splits, offsets, bins, len(queue)

@@ -21,8 +21,12 @@ SOURCES = ["api.cpp", "plan.cpp", "decode_gqa.hip", "decode_mla.hip", "merge.hip
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops
 # (v_pk_*_f32); the host pass warns that it does not know the feature.
+# -amdgpu-atomic-optimizer-strategy=None: a lane-0 atomic stays one atomic; the
+# optimizer's wave-wide rewrite reads its result back at once, which waits
+# for every load issued before it.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
-         "-packed-fp32-ops", "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas"]
+         "-packed-fp32-ops", "-mllvm", "-amdgpu-atomic-optimizer-strategy=None", "-Wall", "-Wno-unused-function",
+         "-Wno-unknown-pragmas"]
 
 
 def build(verbose=False, extra_flags=()):

@@ -92,6 +92,11 @@ pkv_status check_pointers(const pkv_decode_args* a, bool for_merge) {
   if (!aligned(a->work, 16)) return fail(PKV_ERR_INVALID_ARG, "work must be 16-B aligned");
   if (a->bin_offsets && (a->num_bins < 1 || !aligned(a->bin_offsets, 4)))
     return fail(PKV_ERR_INVALID_ARG, "bin_offsets needs num_bins >= 1 and 4-B alignment");
+  if (a->queue) {
+    if (!a->bin_offsets) return fail(PKV_ERR_INVALID_ARG, "queue needs bin_offsets (a plan from pkv_plan_queued)");
+    if (!aligned(a->queue, 4)) return fail(PKV_ERR_INVALID_ARG, "queue must be 4-B aligned");
+    if (mla) return fail(PKV_ERR_UNSUPPORTED, "latent cache: the queued plan is built for the e4m3 cache only");
+  }
   if (a->bt_row_stride < a->max_blocks)
     return fail(PKV_ERR_INVALID_ARG, "bt_row_stride=%lld < max_blocks=%d", (long long)a->bt_row_stride,
                 a->max_blocks);

@@ -85,8 +85,11 @@ struct GqaParams {
   float2* ws_ml; // [max_splits][num_seqs][h_k][rows]
   int32_t* counters;  // [num_seqs][h_k][q-row tiles] or null: merge in a separate launch
   const int32_t* bin_offsets;  // [bins + 1] or null: one work item per workgroup
+  int32_t* queue;              // [2][h_k * q tiles] or null: no shared queue (persistent form)
   float scale_log2e, scale, o_scale;
   int num_seqs, q_len, h_k, h_r, rows, page_shift, num_pages, max_blocks, max_splits;
+  int key_mult;  // keys per unit of a work item's range: 128 (tile plans) or 1 (key plans)
+  int num_work;
 };
 
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint2 x) {
@@ -495,28 +498,67 @@ __device__ __forceinline__ void finish_item(const GqaParams& p, const RowState<N
   }
 }
 
+// Load through the constant address space: with a wave-uniform address this
+// is a scalar load, which completes out of order on its own counter, so
+// waiting for it never waits for the KV loads in flight (a vector load
+// would: those complete in order). For memory the kernel never writes.
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T* ptr) {
+  return *(const __attribute__((address_space(4))) T*)(ptr);
+}
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ int clamp_page(const GqaParams& p, int pg) { return min(max(pg, 0), p.num_pages - 1); }
+
+// Eight waves share four SIMDs: wave w and w ^ 4 sit on one SIMD, and the
+// older wins issue by default. After each round a wave publishes how far it
+// got (`done`, increasing) and runs at raised priority while it is not ahead
+// of its sibling, so the two keep pace.
+__device__ __forceinline__ void keep_pace(int* progress, int wave, int done, int lane) {
+  if (lane == 0) __hip_atomic_store(progress + wave, done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  const int sib = __hip_atomic_load(progress + (wave ^ 4), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if (__builtin_amdgcn_readfirstlane(sib) >= done)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+}
 
 // One work item (a chunk of 128-key tiles of one sequence) for kv head g:
 // the one-item-per-workgroup plan.
 template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES, int HW>
-__device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, int lane, int g, int* progress) {
+__device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, int lane, int g, int* progress,
+                                                int& round_base) {
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
 
   const int4 w = p.work[item];
   const int b = w.x;
   if (w.z <= w.y || b < 0 || b >= p.num_seqs) return;  // padding item / bad entry
+  const int page_size = 1 << p.page_shift;
+  const int k_begin = w.y * p.key_mult;
+  // planned end of the chunk (the plan's lengths are upper bounds of the runtime ones)
+  const int plan_last = min(w.z * p.key_mult, p.max_blocks * page_size) - 1;
+  const int32_t* bt = p.block_table + (int64_t)b * p.bt_row;
+  // Start-up: the page pairs of the first two fetches are read for the
+  // planned chunk right away, so they travel with the sequence length, split
+  // count, descales and query (one round trip where waiting for the length
+  // first takes two). They are read again with the runtime bound below when
+  // the length ends the chunk before the last of them. Entry indices stay in
+  // [0, max_blocks) either way.
+  auto plan_pair = [&](int kb) -> int {
+    return bt[max(min(kb + 16 * (lane & 1), plan_last), 0) >> p.page_shift];
+  };
+  int pv[STAGES];
+  pv[0] = plan_pair(k_begin);
+  pv[1 % STAGES] = plan_pair(k_begin + kBlockKeys);
   const int ns = p.n_splits[b];
   const int slot = w.w;
+  int L = p.seq_lens[b];
   if (ns > 1 && (slot < 0 || slot >= p.max_splits)) return;
   const int row0 = blockIdx.z * (16 * NB);
 
-  const int page_size = 1 << p.page_shift;
-  int L = p.seq_lens[b];
   L = max(0, min(L, p.max_blocks * page_size));
-  const int k_begin = w.y * kTileKeys;
-  const int k_end = min(w.z * kTileKeys, L);
+  const int k_end = min(plan_last + 1, L);
 
   const RowMap<NB> rm = row_map<NB>(p, row0, r16);
   int lim[NB];  // last key each row may see inside this work item's chunk
@@ -539,7 +581,6 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
   reset_rows<NB>(st);
 
   if (k_end > k_begin) {
-    const int32_t* bt = p.block_table + (int64_t)b * p.bt_row;
     const int last_key = k_end - 1;  // loads never go past the chunk (and so never past L)
     const int pmask = page_size - 1;
     // Pages of one 32-key block (page_size >= 16, so each 16-key group lies
@@ -556,9 +597,12 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
     // slot u % STAGES (loaded two fetches earlier) and loads the pages of
     // fetch u + 2 into slot (u + 2) % STAGES; slot indices are compile-time
     // constants of the unrolled stage loop.
-    int pv[STAGES];
-    pv[0] = page_pair(k_begin);
-    pv[1 % STAGES] = page_pair(k_begin + kBlockKeys);
+    // the early pairs are right unless the length ends the chunk before the
+    // last key they cover
+    if (last_key < plan_last && last_key < k_begin + kBlockKeys + 16) {
+      pv[0] = page_pair(k_begin);
+      pv[1 % STAGES] = page_pair(k_begin + kBlockKeys);
+    }
     auto fetch = [&](RawBlock& r, int kb, const int slot) {
       const int pg0 = clamp_page(p, __builtin_amdgcn_readlane(pv[slot], 0));
       const int pg1 = clamp_page(p, __builtin_amdgcn_readlane(pv[slot], 1));
@@ -585,20 +629,216 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
         fetch(ring[(s + STAGES - 1) % STAGES], kb + kBlockKeys * (STAGES - 1), (s + STAGES - 1) % STAGES);
         process_block<FP8Q, NB, kQLds>(ring[s], kb, q, qlds, st, lim, lim_min, c2, g4);
       }
-      if (HW == 8) {
-        // Eight waves share four SIMDs: wave w and w ^ 4 sit on one SIMD, and
-        // the older wins issue by default. A wave that is not ahead of its
-        // sibling runs at raised priority, so the two keep pace.
-        if (lane == 0) __hip_atomic_store(progress + wave, r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        const int sib = __hip_atomic_load(progress + (wave ^ 4), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (__builtin_amdgcn_readfirstlane(sib) >= r)
-          __builtin_amdgcn_s_setprio(1);
-        else
-          __builtin_amdgcn_s_setprio(0);
-      }
+      if (HW == 8) keep_pace(progress, wave, round_base + r, lane);
     }
+    round_base += rounds;
   }
   finish_item<FP8Q, NB>(p, st, rm, b, g, row0, r16, g4, ns, slot, cs, vdv);
+}
+
+// V rows of keys past `vlast` (loaded through planned block-table entries
+// that may lie past the sequence) are zeroed, so that P = 0 never meets a
+// non-finite value in PV. Lane (r16, g4) holds in v[j] the key
+// kb + 16 (j >> 2) + 4 g4 + (j & 3).
+__device__ __forceinline__ void zero_tail_v(RawBlock& r, int kb, int vlast, int g4) {
+  for (int j = 0; j < 8; ++j)
+    if (kb + 16 * (j >> 2) + 4 * g4 + (j & 3) > vlast) r.v[j] = uint2{0u, 0u};
+}
+
+// Persistent form of the queued plan, one row block: wave (workgroup x, kv
+// head g) runs the items of bin x, then items of kv head g's queue until it
+// is empty. The items form ONE load stream. Each item runs whole rounds of
+// STAGES 32-key blocks (at least two), as the one-item form does. The last
+// round already fetches the next item N's first blocks, so an item boundary
+// costs its epilogue and no round trip. N is prepared while the current item
+// runs, with scalar loads only:
+//   - at the item's start, take a queue item (once the bin is done);
+//   - at the end of the third-to-last round, read N's work entry;
+//   - at the end of the second-to-last round, its length, split count and
+//     descales;
+//   - in the last round, its query and first blocks.
+// Every round therefore issues the same vector loads, and the compiler's
+// waits stay exact. Block-table entries are loaded two fetches ahead, as in
+// the one-item form, from the planned key range, which needs no sequence
+// length. Rows past the runtime length are clamped to its last key, and
+// their V is zeroed before use.
+template <bool FP8Q, bool CAUSAL_TAIL, int STAGES, int HW>
+__device__ __forceinline__ void gqa_decode_persistent(const GqaParams& p, int lane, int g, int* progress) {
+  constexpr int NB = 1;
+  constexpr int S = STAGES;
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+  const int row0 = blockIdx.z * 16;
+  const RowMap<NB> rm = row_map<NB>(p, row0, r16);
+  const int page_size = 1 << p.page_shift;
+  const int pmask = page_size - 1;
+  const int key_cap = p.max_blocks * page_size;
+  const int bin_hi = p.bin_offsets[blockIdx.x + 1];
+  const int q0 = p.bin_offsets[gridDim.x];
+  const int col = blockIdx.z * p.h_k + g;
+  int* const taken = p.queue + col;                          // queue items handed out for this column
+  int* const retired = p.queue + p.h_k * gridDim.z + col;    // waves of this column done taking
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  struct Meta {
+    int idx, b, k_begin, plan_last, slot, ns, L;
+    bool entry_ok;
+    float qd, kd, vd;
+  };
+  auto load_entry = [&](Meta& m) {  // work entry of m.idx (any idx: the load is clamped)
+    const i32x4 w = load_uniform(reinterpret_cast<const i32x4*>(p.work) + min(max(m.idx, 0), p.num_work - 1));
+    m.entry_ok = m.idx < p.num_work && w.x >= 0 && w.x < p.num_seqs && w.y >= 0 && w.z > w.y;
+    m.b = min(max(w.x, 0), p.num_seqs - 1);
+    m.k_begin = max(w.y, 0);
+    m.plan_last = max(min(w.z, key_cap) - 1, m.k_begin);  // planned last key (>= k_begin: an entry exists)
+    m.slot = w.w;
+  };
+  auto load_seq = [&](Meta& m) {
+    m.ns = load_uniform(p.n_splits + m.b);
+    m.L = max(0, min(load_uniform(p.seq_lens + m.b), key_cap));
+    m.qd = FP8Q ? load_uniform(p.qd + m.b * p.qd_seq + g * p.qd_head) : 1.0f;
+    m.kd = load_uniform(p.kd + m.b * p.kd_seq + g * p.kd_head);
+    m.vd = load_uniform(p.vd + m.b * p.vd_seq + g * p.vd_head);
+  };
+  auto last_key_of = [&](const Meta& m) {  // last key a load may touch (< k_begin: none)
+    return m.entry_ok ? min(m.plan_last + 1, m.L) - 1 : m.k_begin - 1;
+  };
+  // At least two rounds per item (masked ones past its keys): the next item
+  // is then always known before the round whose block-table entries reach
+  // into it is loaded, and every round issues the same loads.
+  auto rounds_of = [&](const Meta& m) {
+    const int keys = last_key_of(m) + 1 - m.k_begin;
+    return max(2, (keys + kBlockKeys * S - 1) / (kBlockKeys * S));
+  };
+
+  // current item C and the next item N
+  Meta C, N;
+  int grab = 0;  // lane 0: result of the last queue take
+  auto take = [&]() {
+    if (lane == 0) grab = __hip_atomic_fetch_add(taken, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+
+  const int bin_lo = p.bin_offsets[blockIdx.x];
+  if (bin_lo < bin_hi) {
+    C.idx = bin_lo;
+  } else {
+    take();
+    C.idx = q0 + __builtin_amdgcn_readlane(grab, 0);
+  }
+  if (C.idx < p.num_work) {
+    load_entry(C);
+    load_seq(C);
+    QOperand<NB> q, qn;
+    load_q<FP8Q, NB>(p, q, rm, C.b, g, g4);
+    bool n_valid = false;  // N exists and its entry has been read
+    N.idx = p.num_work;
+
+    int c_last = last_key_of(C), n_last = -1;
+    // Page pair of fetch slot u (lanes 0 / 1: the pages of its two 16-key
+    // groups) from the planned key range: C's slots below c_slots, N's at or
+    // past it once N is known (nx_ok), else C's last block again.
+    auto pair_of = [&](int u, int c_slots, bool nx_ok) -> int {
+      const bool nx = nx_ok && u >= c_slots;
+      const int bb = nx ? N.b : C.b;
+      const int key = nx ? N.k_begin + kBlockKeys * (u - c_slots) : C.k_begin + kBlockKeys * u;
+      const int kk = min(min(key + 16 * (lane & 1), nx ? N.plan_last : C.plan_last), key_cap - 1);
+      return p.block_table[(int64_t)bb * p.bt_row + (max(kk, 0) >> p.page_shift)];
+    };
+    // Fetch slot u into `r` with the pair in pv[slot], and load the pair of
+    // slot u + 2 into pv[(slot + 2) % S] (slot indices are compile-time
+    // constants of the unrolled stage loop). fetch_n: slot u may be N's (N's
+    // last key known); pair_n: slot u + 2 may be N's (N's entry known).
+    int pv[S];
+    auto fetch = [&](RawBlock& r, int u, int c_slots, bool fetch_n, bool pair_n, const int slot) {
+      const bool nx = fetch_n && u >= c_slots;
+      const int kb = nx ? N.k_begin + kBlockKeys * (u - c_slots) : C.k_begin + kBlockKeys * u;
+      const int pg0 = clamp_page(p, __builtin_amdgcn_readlane(pv[slot], 0));
+      const int pg1 = clamp_page(p, __builtin_amdgcn_readlane(pv[slot], 1));
+      r = load_block(p, g, kb, pg0, pg1, nx ? n_last : c_last, pmask, r16, g4);
+      pv[(slot + 2) % S] = pair_of(u + 2, c_slots, pair_n);
+    };
+
+    int R = rounds_of(C);
+    RawBlock ring[S];
+    // first item: its first S - 1 blocks
+    pv[0] = pair_of(0, R * S, false);
+    pv[1 % S] = pair_of(1, R * S, false);
+#pragma unroll
+    for (int d = 0; d < S - 1; ++d) fetch(ring[d], d, R * S, false, false, d);
+    int round_base = 0;
+    for (;;) {
+      // ---- current item C --------------------------------------------------
+      const bool c_ok = C.entry_ok && (C.ns <= 1 || (C.slot >= 0 && C.slot < p.max_splits));
+      int lim[NB];
+      for (int nb = 0; nb < NB; ++nb) lim[nb] = min(CAUSAL_TAIL ? C.L - p.q_len + rm.qi[nb] : C.L - 1, c_last);
+      const int lim_min = min(CAUSAL_TAIL ? C.L - p.q_len : C.L - 1, c_last);
+      const float c2 = p.scale_log2e * C.qd * C.kd;
+      const float cs = p.scale * C.qd * C.kd;
+      const int c_slots = R * S;
+      const bool n_static = C.idx + 1 < bin_hi;  // else N comes from the queue
+      // a queue item for N is taken as C starts; its result is read, and N's
+      // entry loaded, at the end of round R - 3 (at once for two-round items:
+      // round 0 then already fetches N's first page pair)
+      if (!n_static) take();
+      auto prepare_n = [&]() {
+        N.idx = n_static ? C.idx + 1 : q0 + __builtin_amdgcn_readlane(grab, 0);
+        load_entry(N);
+        n_valid = N.idx < p.num_work;
+      };
+      if (R == 2) prepare_n();
+      RowState<NB> st;
+      reset_rows<NB>(st);
+
+      // rounds 0 .. R-2: C's blocks; N is prepared with scalar loads (its
+      // entry 3 rounds before the end, its sequence 2 rounds before), so every
+      // round issues the same vector loads
+      for (int r = 0; r < R - 1; ++r) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          fetch(ring[(s + S - 1) % S], r * S + s + S - 1, c_slots, false, n_valid, (s + S - 1) % S);
+          const int kb = C.k_begin + kBlockKeys * (r * S + s);
+          if (kb + kBlockKeys - 1 > c_last) zero_tail_v(ring[s], kb, c_last, g4);
+          process_block<FP8Q, NB, false>(ring[s], kb, q, nullptr, st, lim, lim_min, c2, g4);
+        }
+        if (HW == 8) keep_pace(progress, wave, round_base + r, lane);
+        // at a round's end, so that many loads have been issued since the take
+        if (r == R - 3) prepare_n();
+        if (r == R - 2 && n_valid) load_seq(N);
+      }
+      {  // last round: N's query, and its first S - 1 blocks into the ring
+        const int r = R - 1;
+        if (n_valid) n_last = last_key_of(N);
+        load_q<FP8Q, NB>(p, qn, rm, n_valid ? N.b : C.b, g, g4);
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          fetch(ring[(s + S - 1) % S], r * S + s + S - 1, c_slots, n_valid, n_valid, (s + S - 1) % S);
+          const int kb = C.k_begin + kBlockKeys * (r * S + s);
+          if (kb + kBlockKeys - 1 > c_last) zero_tail_v(ring[s], kb, c_last, g4);
+          process_block<FP8Q, NB, false>(ring[s], kb, q, nullptr, st, lim, lim_min, c2, g4);
+        }
+        if (HW == 8) keep_pace(progress, wave, round_base + r, lane);
+      }
+      round_base += R;
+      if (c_ok) finish_item<FP8Q, NB>(p, st, rm, C.b, g, row0, r16, g4, C.ns, C.slot, cs, C.vd);
+      if (!n_valid) break;
+      // ---- N becomes current: its first S - 1 blocks are in the ring and the
+      // pairs of its next fetches in pv
+      C = N;
+      q = qn;
+      c_last = n_last;
+      R = rounds_of(C);
+      n_valid = false;
+      N.idx = p.num_work;
+    }
+  }
+  // The wave of this column that retires last has seen every other one
+  // finish taking, so nobody reads the counters again in this launch: it
+  // clears both for the next launch.
+  if (lane == 0 &&
+      __hip_atomic_fetch_add(retired, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1) {
+    __hip_atomic_store(taken, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(retired, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // The work items of one bin of the balanced plan (key ranges of one or more
@@ -613,8 +853,8 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
 // first exceeds j, found with one ballot and a popcount, and item fields are
 // read with readlane -- no LDS, no scalar loads in the loop. Each item's
 // query rows are loaded while the item before it runs.
-template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES>
-__device__ __forceinline__ void gqa_decode_stream(const GqaParams& p, int lane, int g) {
+template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES, int HW>
+__device__ __forceinline__ void gqa_decode_stream(const GqaParams& p, int lane, int g, int* progress) {
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
   const int row0 = blockIdx.z * (16 * NB);
@@ -735,6 +975,7 @@ __device__ __forceinline__ void gqa_decode_stream(const GqaParams& p, int lane, 
 #pragma unroll
       for (int s = 0; s < STAGES - 1; ++s) fetch(ring[s], s, s);
       const int rounds = (nblocks + STAGES - 1) / STAGES;
+      const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
       for (int r = 0; r < rounds; ++r) {
 #pragma unroll
         for (int s = 0; s < STAGES; ++s) {
@@ -748,10 +989,46 @@ __device__ __forceinline__ void gqa_decode_stream(const GqaParams& p, int lane, 
             if (kb <= lim_max) process_block<FP8Q, NB, false>(ring[s], kb, qc, nullptr, st, lim, lim_min, c2, g4);
           }
         }
+        if (HW == 8) keep_pace(progress, wave, seg * 65536 + r, lane);
       }
     }
     advance_to(np - 1);  // items after the last block (empty ones)
     end_item();
+  }
+}
+
+// Persistent form of two row blocks (queued plan): the items of this
+// workgroup's bin, then items of the shared queue of its (kv-head group,
+// q-row tile) until it is empty, each started afresh with the one-item
+// loop. Every wave of the workgroup runs the same items (one kv head each)
+// and meets the same barriers.
+template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES, int HW>
+__device__ __forceinline__ void gqa_decode_bin_then_queue(const GqaParams& p, int lane, int g, int* progress) {
+  int round_base = 0;
+  const int it_end = p.bin_offsets[blockIdx.x + 1];
+  for (int it = p.bin_offsets[blockIdx.x]; it < it_end; ++it)
+    if (g < p.h_k) gqa_decode_item<FP8Q, NB, CAUSAL_TAIL, STAGES, HW>(p, it, lane, g, progress, round_base);
+  const int q0 = p.bin_offsets[gridDim.x];
+  const int col = blockIdx.z * gridDim.y + blockIdx.y;         // < h_k * q tiles
+  int* const taken = p.queue + col;                            // queue items handed out (+ one per final take)
+  int* const retired = p.queue + gridDim.y * gridDim.z + col;  // workgroups done taking
+  __shared__ int next_item;
+  for (;;) {
+    if (threadIdx.x == 0)
+      next_item = q0 + __hip_atomic_fetch_add(taken, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int it = __builtin_amdgcn_readfirstlane(next_item);
+    __syncthreads();  // everyone has read next_item before it is written again
+    if (it >= p.num_work) break;
+    if (g < p.h_k) gqa_decode_item<FP8Q, NB, CAUSAL_TAIL, STAGES, HW>(p, it, lane, g, progress, round_base);
+  }
+  // The workgroup that retires last has seen every other one finish taking,
+  // so nobody reads the counters again in this launch: it clears both for the
+  // next launch.
+  if (threadIdx.x == 0 &&
+      __hip_atomic_fetch_add(retired, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1) {
+    __hip_atomic_store(taken, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(retired, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -768,17 +1045,27 @@ template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES, int HW, bool STREAM>
 __global__ __launch_bounds__(64 * HW) __attribute__((amdgpu_waves_per_eu(NB == 1 || !STREAM ? 2 : 1)))
 void gqa_decode_kernel(GqaParams p) {
   const int lane = threadIdx.x & 63;
-  __shared__ int progress[HW];  // rounds done per wave (one-item form, eight waves)
-  if (!STREAM && HW == 8) {
-    if (lane == 0) progress[threadIdx.x >> 6] = 0;
+  __shared__ int progress[HW];  // rounds done per wave (eight waves)
+  if (HW == 8) {
+    if (lane == 0) progress[threadIdx.x >> 6] = -1;
     __syncthreads();
   }
   const int g = __builtin_amdgcn_readfirstlane(blockIdx.y * HW + (threadIdx.x >> 6));  // wave-uniform
-  if (g >= p.h_k) return;
-  if (STREAM)
-    gqa_decode_stream<FP8Q, NB, CAUSAL_TAIL, STAGES>(p, lane, g);
-  else
-    gqa_decode_item<FP8Q, NB, CAUSAL_TAIL, STAGES, HW>(p, blockIdx.x, lane, g, progress);
+  if (STREAM) {
+    if (g < p.h_k) gqa_decode_stream<FP8Q, NB, CAUSAL_TAIL, STAGES, HW>(p, lane, g, progress);
+    return;
+  }
+  if (!p.queue) {
+    int round_base = 0;
+    if (g < p.h_k) gqa_decode_item<FP8Q, NB, CAUSAL_TAIL, STAGES, HW>(p, blockIdx.x, lane, g, progress, round_base);
+    return;
+  }
+  // queued plan: persistent workgroups
+  if constexpr (NB == 1) {
+    if (g < p.h_k) gqa_decode_persistent<FP8Q, CAUSAL_TAIL, STAGES, HW>(p, lane, g, progress);
+  } else {
+    gqa_decode_bin_then_queue<FP8Q, NB, CAUSAL_TAIL, STAGES, HW>(p, lane, g, progress);
+  }
 }
 
 // Ring depth in 32-key blocks. Three blocks (two in flight while one is
@@ -832,10 +1119,11 @@ GqaVariant gqa_variant(const pkv_decode_args& a) {
   const int rows = a.q_len * (a.h_q / a.h_k);
   v.n_blocks = rows <= 16 ? 1 : 2;
   v.causal_tail = a.causal && a.q_len > 1;
-  v.stream = a.bin_offsets != nullptr;
+  v.stream = a.bin_offsets != nullptr && a.queue == nullptr;
   v.stages = (v.n_blocks == 2 && !v.stream) ? 2 : 3;
   // kv heads per workgroup: the largest power of two dividing h_k, up to 8
-  // (4 for two row blocks, whose waves need more than half the registers)
+  // (4 for two row blocks: eight waves of 32 rows per workgroup measured
+  // slower on the speculative-verify workload, 100 vs 95 us)
   const int cap = v.n_blocks == 1 ? 8 : 4;
   v.heads_per_wg = 1;
   while (v.heads_per_wg * 2 <= cap && a.h_k % (v.heads_per_wg * 2) == 0) v.heads_per_wg *= 2;
@@ -902,6 +1190,9 @@ hipError_t gqa_launch(const pkv_decode_args& a, const GqaVariant& v, hipStream_t
   p.ws_ml = a.workspace ? reinterpret_cast<float2*>(p.ws_o + (int64_t)a.max_splits * rows_all * kD) : nullptr;
   p.counters = a.max_splits > 1 ? a.merge_counters : nullptr;
   p.bin_offsets = a.bin_offsets;
+  p.queue = a.queue;
+  p.key_mult = (a.bin_offsets && a.queue) ? 1 : kTileKeys;
+  p.num_work = a.num_work;
   p.scale_log2e = (float)((double)a.softmax_scale * 1.4426950408889634);
   p.scale = a.softmax_scale;
   p.o_scale = a.o_scale;
@@ -916,7 +1207,7 @@ hipError_t gqa_launch(const pkv_decode_args& a, const GqaVariant& v, hipStream_t
   p.max_splits = a.max_splits;
   const int tiles = (p.rows + gqa_rows_per_tile(v) - 1) / gqa_rows_per_tile(v);
   const int hw = v.heads_per_wg;
-  dim3 grid(a.bin_offsets ? a.num_bins : a.num_work, (a.h_k + hw - 1) / hw, tiles);
+  dim3 grid(a.bin_offsets ? a.num_bins : a.num_work, (a.h_k + hw - 1) / hw, tiles);  // bins: balanced or queued plan
   void* args[] = {&p};
   return hipLaunchKernel(select_kernel(v), grid, dim3(64 * hw), args, gqa_dyn_lds(v), stream);
 }

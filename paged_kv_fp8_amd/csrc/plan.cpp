@@ -108,6 +108,7 @@ extern "C" pkv_status pkv_plan_split_kv(const int32_t* seq_lens, int32_t num_seq
     info->slots = (int32_t)std::min<int64_t>(slots, INT32_MAX);
     info->max_n_splits = max_ns;
     info->num_bins = 0;
+    info->num_dynamic = 0;
   }
   return PKV_OK;
 }
@@ -184,6 +185,109 @@ extern "C" pkv_status pkv_plan_balanced(const int32_t* seq_lens, int32_t num_seq
     info->slots = (int32_t)bins;
     info->max_n_splits = max_ns;
     info->num_bins = (int32_t)bins;
+    info->num_dynamic = 0;
+  }
+  return PKV_OK;
+}
+
+// Queued plan (this library's own; see pkv_fp8.h): sequences cut into even
+// pieces of 32-key blocks, packed longest first onto the least loaded of
+// `bins` persistent workgroups; each bin then hands its last (smallest)
+// pieces to a shared queue until its load fits the static budget, and the
+// workgroups drain the queue as they finish.
+extern "C" pkv_status pkv_plan_queued(const int32_t* seq_lens, int32_t num_seqs, int32_t h_k, int32_t n_q_tiles,
+                                      int32_t cu_count, int32_t wg_per_cu, int32_t max_splits,
+                                      int32_t pieces_per_bin, int32_t dyn_percent, int32_t* work_out,
+                                      int32_t work_cap, int32_t* n_splits_out, int32_t* bin_offsets_out,
+                                      int32_t bins_cap, pkv_plan_info* info) {
+  using pkv::fail;
+  if (!seq_lens || !work_out || !n_splits_out || !bin_offsets_out)
+    return fail(PKV_ERR_INVALID_ARG, "plan: NULL array");
+  if (num_seqs < 1) return fail(PKV_ERR_INVALID_ARG, "plan: num_seqs=%d < 1", num_seqs);
+  if (h_k < 1 || n_q_tiles < 1 || cu_count < 1 || wg_per_cu < 1 || max_splits < 1 || pieces_per_bin < 1)
+    return fail(PKV_ERR_INVALID_ARG, "plan: sizes must be >= 1");
+  if (dyn_percent < 0 || dyn_percent > 90)
+    return fail(PKV_ERR_INVALID_ARG, "plan: dyn_percent=%d not in [0, 90]", dyn_percent);
+  if (work_cap < 0 || bins_cap < 0) return fail(PKV_ERR_INVALID_ARG, "plan: capacities must be >= 0");
+  if (max_splits > PKV_MAX_SPLITS)
+    return fail(PKV_ERR_UNSUPPORTED, "plan: max_splits=%d > %d", max_splits, PKV_MAX_SPLITS);
+  std::vector<int64_t> blocks(num_seqs);
+  int64_t total = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    if (seq_lens[b] < 0) return fail(PKV_ERR_INVALID_ARG, "plan: seq_lens[%d]=%d < 0", b, seq_lens[b]);
+    blocks[b] = std::max<int64_t>(1, ceil_div(seq_lens[b], kBalanceBlockKeys));
+    total += blocks[b];
+  }
+  int64_t bins = ((int64_t)cu_count * wg_per_cu) / ((int64_t)h_k * n_q_tiles);
+  bins = std::max<int64_t>(1, std::min(bins, total));
+  if (bins + 1 > bins_cap) return fail(PKV_ERR_CAPACITY, "plan: %lld bins > bins_cap - 1", (long long)bins);
+  const int64_t piece = std::max<int64_t>(1, total / (bins * pieces_per_bin));  // piece cap, in blocks
+  const int64_t budget = (total * (100 - dyn_percent)) / (100 * bins);         // static load of a bin
+
+  // pieces: sequence b in n_b even pieces of at most max(piece, ceil(blocks_b / max_splits)) blocks
+  struct Piece {
+    int32_t seq, first, end, slot;  // blocks [first, end) of sequence seq, split slot
+  };
+  std::vector<Piece> pieces;
+  int32_t max_ns = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t c = std::max(piece, ceil_div(blocks[b], max_splits));
+    const int64_t n = ceil_div(blocks[b], c);
+    for (int64_t j = 0; j < n; ++j)
+      pieces.push_back({b, (int32_t)((j * blocks[b]) / n), (int32_t)(((j + 1) * blocks[b]) / n), (int32_t)j});
+    n_splits_out[b] = (int32_t)n;
+    max_ns = std::max(max_ns, (int32_t)n);
+  }
+  if ((int64_t)pieces.size() > work_cap)
+    return fail(PKV_ERR_CAPACITY, "plan: %lld work items > work_cap=%d", (long long)pieces.size(), work_cap);
+  // longest first; ties keep sequence, then piece order
+  std::stable_sort(pieces.begin(), pieces.end(),
+                   [](const Piece& x, const Piece& y) { return (x.end - x.first) > (y.end - y.first); });
+  // every piece to the least loaded bin (lowest index among equals)
+  std::vector<int64_t> load(bins, 0);
+  std::vector<std::vector<int32_t>> in_bin(bins);
+  for (int32_t i = 0; i < (int32_t)pieces.size(); ++i) {
+    int64_t best = 0;
+    for (int64_t k = 1; k < bins; ++k)
+      if (load[k] < load[best]) best = k;
+    load[best] += pieces[i].end - pieces[i].first;
+    in_bin[best].push_back(i);
+  }
+  // bins give their last pieces (the smallest they got) to the queue while
+  // over budget, keeping at least one; the queue runs longest first
+  std::vector<int32_t> queue;
+  for (int64_t k = 0; k < bins; ++k)
+    while (in_bin[k].size() > 1 && load[k] > budget) {
+      const int32_t i = in_bin[k].back();
+      in_bin[k].pop_back();
+      load[k] -= pieces[i].end - pieces[i].first;
+      queue.push_back(i);
+    }
+  std::sort(queue.begin(), queue.end());  // sorted-piece index order = longest first, ties as above
+
+  int64_t n = 0;
+  auto emit = [&](int32_t i) {
+    const Piece& pc = pieces[i];
+    work_out[4 * n + 0] = pc.seq;
+    work_out[4 * n + 1] = (int32_t)(kBalanceBlockKeys * pc.first);
+    work_out[4 * n + 2] = (int32_t)(kBalanceBlockKeys * pc.end);
+    work_out[4 * n + 3] = pc.slot;
+    ++n;
+  };
+  bin_offsets_out[0] = 0;
+  for (int64_t k = 0; k < bins; ++k) {
+    for (int32_t i : in_bin[k]) emit(i);
+    bin_offsets_out[k + 1] = (int32_t)n;
+  }
+  for (int32_t i : queue) emit(i);
+  if (info) {
+    info->num_work = (int32_t)n;
+    info->num_real = (int32_t)n;
+    info->chunk_tiles = (int32_t)ceil_div(piece, kTileKeys / kBalanceBlockKeys);
+    info->slots = (int32_t)bins;
+    info->max_n_splits = max_ns;
+    info->num_bins = (int32_t)bins;
+    info->num_dynamic = (int32_t)queue.size();
   }
   return PKV_OK;
 }

@@ -49,7 +49,8 @@ class PagedDecode:
     def __init__(self, *, q, block_table, seq_lens, o, lse, q_len, softmax_scale, k_cache=None, v_cache=None,
                  q_descale=None, k_descale=None, v_descale=None, latent=None, rope=None, blk_scale=None,
                  num_pages=None, causal=True, o_scale=1.0, max_splits=16, force_splits=0, min_chunk_tiles=1,
-                 pad_to=0, wg_per_cu=None, plan_seq_lens=None, fused_merge=False, plan="wave"):
+                 pad_to=0, wg_per_cu=None, plan_seq_lens=None, fused_merge=False, plan="wave", pieces_per_bin=3,
+                 dyn_percent=10, plan_cu_count=None):
         mla = latent is not None
         a = native.DecodeArgs()
         num_seqs = seq_lens.shape[0]
@@ -93,14 +94,26 @@ class PagedDecode:
         a.max_splits = max_splits
 
         cu, wg, n_q_tiles = native.decode_slots(a)
+        cu = plan_cu_count or cu  # a smaller count plans fewer, fuller workgroups (tests)
         self.cu_count, self.wg_per_cu, self.n_q_tiles = cu, wg_per_cu or wg, n_q_tiles
         lens = seq_lens.cpu().numpy() if plan_seq_lens is None else np.asarray(plan_seq_lens)
         dev = q.device
         self.bin_offsets = None
+        self.queue = None
         if plan == "balanced":  # contiguous equal shares, one per resident workgroup
             work, n_splits, offs, info = native.plan_balanced(lens, h_k, n_q_tiles, cu, self.wg_per_cu, max_splits)
             self.bin_offsets = torch.from_numpy(offs).to(dev)
             a.bin_offsets, a.num_bins = _ptr(self.bin_offsets), int(info.num_bins)
+        elif plan == "queued":  # persistent workgroups: packed static bins, then a shared queue
+            if mla:
+                raise ValueError("the queued plan is built for the e4m3 cache only")
+            work, n_splits, offs, info = native.plan_queued(lens, h_k, n_q_tiles, cu, self.wg_per_cu, max_splits,
+                                                            pieces_per_bin, dyn_percent)
+            self.bin_offsets = torch.from_numpy(offs).to(dev)
+            a.bin_offsets, a.num_bins = _ptr(self.bin_offsets), int(info.num_bins)
+            # taken / retired counters per (kv-head group, q tile): zeroed once, left zero by every call
+            self.queue = torch.zeros(2 * h_k * n_q_tiles, dtype=torch.int32, device=dev)
+            a.queue = _ptr(self.queue)
         elif plan == "wave":  # the occupancy-pinned one-wave plan
             work, n_splits, info = native.plan_split_kv(lens, h_k, n_q_tiles, cu, self.wg_per_cu, max_splits,
                                                         force_splits, min_chunk_tiles, pad_to)

@@ -20,7 +20,7 @@ PKV_MAX_SPLITS = 256
 
 # Every function the header declares, in declaration order.
 EXPORTS = ("pkv_status_string", "pkv_last_error", "pkv_version", "pkv_decode_args_size", "pkv_plan_split_kv",
-           "pkv_plan_balanced", "pkv_workspace_bytes", "pkv_decode_slots", "pkv_paged_decode_attn",
+           "pkv_plan_balanced", "pkv_plan_queued", "pkv_workspace_bytes", "pkv_decode_slots", "pkv_paged_decode_attn",
            "pkv_merge_splits", "pkv_quantize_q", "pkv_quant_q_args_size", "pkv_write_kv", "pkv_kv_write_args_size",
            "pkv_decode_kernel_name")
 
@@ -33,7 +33,8 @@ class PkvError(RuntimeError):
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [("num_work", ctypes.c_int32), ("num_real", ctypes.c_int32), ("chunk_tiles", ctypes.c_int32),
-                ("slots", ctypes.c_int32), ("max_n_splits", ctypes.c_int32), ("num_bins", ctypes.c_int32)]
+                ("slots", ctypes.c_int32), ("max_n_splits", ctypes.c_int32), ("num_bins", ctypes.c_int32),
+                ("num_dynamic", ctypes.c_int32)]
 
 
 _i32, _i64, _f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
@@ -63,6 +64,7 @@ class DecodeArgs(ctypes.Structure):
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
         ("merge_counters", _vp),
         ("bin_offsets", _vp), ("num_bins", _i32),
+        ("queue", _vp),
     ]
 
 
@@ -112,6 +114,9 @@ def _load():
     lib.pkv_plan_balanced.restype = _i32
     lib.pkv_plan_balanced.argtypes = [P(_i32), _i32, _i32, _i32, _i32, _i32, _i32, P(_i32), _i32, P(_i32), P(_i32),
                                       _i32, P(PlanInfo)]
+    lib.pkv_plan_queued.restype = _i32
+    lib.pkv_plan_queued.argtypes = [P(_i32), _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, P(_i32), _i32, P(_i32),
+                                    P(_i32), _i32, P(PlanInfo)]
     lib.pkv_workspace_bytes.restype = ctypes.c_size_t
     lib.pkv_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
     lib.pkv_decode_kernel_name.restype = ctypes.c_char_p
@@ -192,6 +197,25 @@ def plan_balanced(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16
                                work.ctypes.data_as(P), work_cap, ns.ctypes.data_as(P), offs.ctypes.data_as(P),
                                bins_cap, ctypes.byref(info))
     _check(st, "pkv_plan_balanced")
+    return work[:info.num_work].copy(), ns[:nseq].copy(), offs[:info.num_bins + 1].copy(), info
+
+
+def plan_queued(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16, pieces_per_bin=3, dyn_percent=10):
+    """Queued plan (static bins + shared queue). Returns (work int32[num_work, 4],
+    n_splits, bin_offsets int32[num_bins + 1], PlanInfo)."""
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    nseq = lens.shape[0]
+    bins_cap = max(2, int(cu_count) * int(wg_per_cu) + 1)
+    work_cap = int(max(1, nseq) * max(1, max_splits))
+    work = np.zeros((max(work_cap, 1), 4), dtype=np.int32)
+    ns = np.zeros(max(nseq, 1), dtype=np.int32)
+    offs = np.zeros(bins_cap, dtype=np.int32)
+    info = PlanInfo()
+    P = ctypes.POINTER(_i32)
+    st = lib.pkv_plan_queued(lens.ctypes.data_as(P), nseq, h_k, n_q_tiles, cu_count, wg_per_cu, max_splits,
+                             pieces_per_bin, dyn_percent, work.ctypes.data_as(P), work_cap, ns.ctypes.data_as(P),
+                             offs.ctypes.data_as(P), bins_cap, ctypes.byref(info))
+    _check(st, "pkv_plan_queued")
     return work[:info.num_work].copy(), ns[:nseq].copy(), offs[:info.num_bins + 1].copy(), info
 
 

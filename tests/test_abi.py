@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 from oracle.plan import plan_balanced as oracle_balanced
+from oracle.plan import plan_queued as oracle_queued
 from oracle.plan import plan_split_kv as oracle_plan
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -203,6 +204,41 @@ def test_library_balanced_planner_equals_oracle(native, seed):
     assert w2.tolist() == [list(x) for x in work]
     assert ns2.tolist() == ns and offs2.tolist() == offs
     assert (info.num_bins, info.num_work, info.max_n_splits) == (bins, len(work), max(ns))
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_library_queued_planner_equals_oracle(native, seed):
+    rng = np.random.default_rng(4000 + seed)
+    b = int(rng.integers(1, 130))
+    lens = np.where(rng.random(b) < 0.15, rng.integers(8192, 70000, size=b), rng.integers(0, 5000, size=b))
+    kw = dict(h_k=int(rng.choice([1, 2, 4, 8])), n_q_tiles=int(rng.integers(1, 3)), cu_count=256,
+              wg_per_cu=int(rng.integers(1, 9)), max_splits=int(rng.choice([2, 8, 16, 64, 256])),
+              pieces_per_bin=int(rng.integers(1, 5)), dyn_percent=int(rng.integers(0, 60)))
+    work, ns, offs, bins, nq = oracle_queued(lens.tolist(), **kw)
+    w2, ns2, offs2, info = native.plan_queued(lens, kw["h_k"], kw["n_q_tiles"], kw["cu_count"], kw["wg_per_cu"],
+                                              kw["max_splits"], kw["pieces_per_bin"], kw["dyn_percent"])
+    assert w2.tolist() == [list(x) for x in work]
+    assert ns2.tolist() == ns and offs2.tolist() == offs
+    assert (info.num_bins, info.num_work, info.max_n_splits, info.num_dynamic) == (bins, len(work), max(ns), nq)
+
+
+def test_queued_planner_errors(native):
+    lens = np.array([100, 200], dtype=np.int32)
+    for over, code in (({"pieces_per_bin": 0}, native.PKV_ERR_INVALID_ARG),
+                       ({"dyn_percent": -1}, native.PKV_ERR_INVALID_ARG),
+                       ({"dyn_percent": 91}, native.PKV_ERR_INVALID_ARG),
+                       ({"max_splits": native.PKV_MAX_SPLITS + 1}, native.PKV_ERR_UNSUPPORTED)):
+        args = dict(h_k=1, n_q_tiles=1, cu_count=4, wg_per_cu=1, max_splits=4, pieces_per_bin=2, dyn_percent=10)
+        args.update(over)
+        with pytest.raises(native.PkvError) as e:
+            native.plan_queued(lens, **args)
+        assert e.value.status == code
+
+
+def test_queued_plan_needs_bin_offsets_and_the_e4m3_cache(native):
+    a = _valid_args(native)
+    a.queue = 1 << 41
+    assert native.lib.pkv_paged_decode_attn(ctypes.byref(a), None) == native.PKV_ERR_INVALID_ARG
 
 
 # ---------------------------------------------------------------------------

@@ -368,3 +368,79 @@ def test_balanced_plan_fused_merge_and_graph():
         torch.cuda.synchronize()
         assert torch.equal(dec.o.view(torch.int16), eager_o.view(torch.int16)), f"replay {rep}"
     assert int(dec.merge_counters.abs().sum()) == 0
+
+
+# ---------------------------------------------------------------------------
+# queued plan: persistent workgroups run their packed bin, then drain a
+# shared queue (which workgroup runs which piece changes from call to call;
+# the pieces and so the results do not)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", list(SMALL))
+def test_queued_plan_small_workloads(name):
+    kw = dict(SMALL[name])
+    w = workload(kw.pop("index"), **kw)
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch, plan="queued", max_splits=64, wg_per_cu=1, dyn_percent=30)
+    assert dec.plan_info.num_bins >= 1
+    compare(batch, dec, what=f"queued {name}")
+    assert int(dec.queue.abs().sum()) == 0
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_queued_plan_full_workloads_sampled(name):
+    idx, over = FULL[name]
+    w = workload(idx, **over)
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch, plan="queued", max_splits=max(w.max_splits, 64))
+    lens = batch.seq_lens.cpu().numpy()
+    seqs = _sample(lens, np.random.default_rng(idx + 70))
+    err_o, err_l, _ = compare(batch, dec, seqs=seqs, what=f"queued {name}")
+    assert int(dec.queue.abs().sum()) == 0
+    print(f"queued {name}: bins={dec.plan_info.num_bins} items={dec.plan_info.num_work} "
+          f"queue={dec.plan_info.num_dynamic} max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
+
+
+@pytest.mark.parametrize("q_format,q_len,causal,ps", [("bf16", 1, True, 16), ("bf16", 4, True, 64),
+                                                      ("e4m3", 2, False, 128)])
+def test_queued_plan_edge_lengths(q_format, q_len, causal, ps):
+    idx = 4 if q_format == "e4m3" else 2
+    h_q, h_k = (64, 4) if q_format == "e4m3" else (16, 2)
+    w = workload(idx, num_seqs=len(EDGE_LENS), q_len=q_len, h_q=h_q, h_k=h_k, page_size=ps, causal=causal,
+                 seq_len_dist=("fixed", EDGE_LENS), max_splits=8)
+    batch = make_batch(w, device="cuda")
+    # four bins: several pieces per workgroup, most of them queued
+    dec = run_batch(batch, plan="queued", wg_per_cu=1, plan_cu_count=4 * h_k, dyn_percent=50)
+    assert dec.plan_info.num_bins == 4 and dec.plan_info.num_dynamic >= 1
+    tol = FP8_SHORT_TOL if q_format == "e4m3" else O_TOL
+    compare(batch, dec, o_tol=tol, what=f"queued edge {q_format} q_len={q_len}")
+    assert int(dec.queue.abs().sum()) == 0
+
+
+def test_queued_plan_bitwise_repeats_and_graph_replay():
+    w = workload(4, num_seqs=24, seq_len_dist=("mix", 0.2, (6000, 20000), (1024, 4096)))
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch, plan="queued", max_splits=64, wg_per_cu=1, dyn_percent=40)
+    assert dec.plan_info.num_dynamic >= 1 and dec.has_splits
+    compare(batch, dec, what="queued fp8")
+    ref_o, ref_l = dec.o.clone(), dec.lse.clone()
+    for rep in range(3):  # counters come back to zero after every call
+        nan_fill_(dec.workspace)
+        dec.o.zero_()
+        dec.lse.zero_()
+        dec.run()
+        torch.cuda.synchronize()
+        assert torch.equal(dec.o.view(torch.int16), ref_o.view(torch.int16)), f"call {rep}"
+        assert torch.equal(dec.lse.view(torch.int32), ref_l.view(torch.int32)), f"call {rep}"
+        assert int(dec.queue.abs().sum()) == 0
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dec.run()
+    for rep in range(3):
+        dec.o.zero_()
+        dec.lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dec.o.view(torch.int16), ref_o.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(dec.lse.view(torch.int32), ref_l.view(torch.int32)), f"replay {rep}"
+        assert int(dec.queue.abs().sum()) == 0

@@ -168,3 +168,72 @@ def test_balanced_invariants(seed):
     assert [(w[0], w[1]) for w in work] == sorted((w[0], w[1]) for w in work)
     assert max(ns) <= kw["max_splits"]
     assert bins <= max(1, 256 * kw["wg_per_cu"] // (kw["h_k"] * kw["n_q_tiles"]))
+
+
+# ---------------------------------------------------------------------------
+# queued plan (the build's own planner): packed bins, then a shared queue
+# ---------------------------------------------------------------------------
+from oracle.plan import plan_queued  # noqa: E402
+
+
+def test_queued_hand_worked():
+    # blocks [10, 4, 1] (15), bins = 3, piece = 15 // (3 * 2) = 2, budget = 15 * 80 // 300 = 4.
+    # pieces: seq 0 -> five of 2 blocks, seq 1 -> two of 2, seq 2 -> one of 1; longest first in input order.
+    # least loaded bin: s0p0 b0, s0p1 b1, s0p2 b2, s0p3 b0, s0p4 b1, s1p0 b2, s1p1 b0 (6), s2p0 b1 (5).
+    # over budget: bin 0 gives s1p1, bin 1 gives s2p0; the queue keeps longest-first order.
+    work, ns, off, bins, nq = plan_queued([300, 100, 0], h_k=1, n_q_tiles=1, cu_count=3, pieces_per_bin=2,
+                                          dyn_percent=20)
+    assert (bins, ns, off, nq) == (3, [5, 2, 1], [0, 2, 4, 6], 2)
+    assert work == [(0, 0, 64, 0), (0, 192, 256, 3),      # bin 0
+                    (0, 64, 128, 1), (0, 256, 320, 4),    # bin 1
+                    (0, 128, 192, 2), (1, 0, 64, 0),      # bin 2
+                    (1, 64, 128, 1), (2, 0, 32, 0)]       # queue
+
+
+def test_queued_small_exact():
+    # two sequences, blocks [4, 2], bins = 2, piece = 6 // 2 = 3, budget = 6*50 // 200 = 1:
+    # seq 0 -> 2 pieces [0,2) [2,4), seq 1 -> 1 piece [0,2); all of size 2, longest-first keeps input order.
+    # bins: (0,0,2)->0, (0,2,4)->1, (1,0,2)->0; bin 0 is over budget with 2 pieces -> (1,0,2) queued.
+    work, ns, off, bins, nq = plan_queued([128, 64], h_k=1, n_q_tiles=1, cu_count=2, pieces_per_bin=1,
+                                          dyn_percent=50)
+    assert (bins, ns, off, nq) == (2, [2, 1], [0, 1, 2], 1)
+    assert work == [(0, 0, 64, 0), (0, 64, 128, 1), (1, 0, 64, 0)]
+
+
+def test_queued_errors():
+    with pytest.raises(ValueError):
+        plan_queued([10], h_k=1, n_q_tiles=1, cu_count=1, pieces_per_bin=0)
+    with pytest.raises(ValueError):
+        plan_queued([10], h_k=1, n_q_tiles=1, cu_count=1, dyn_percent=95)
+    with pytest.raises(ValueError):
+        plan_queued([], h_k=1, n_q_tiles=1, cu_count=1)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_queued_invariants(seed):
+    rng = np.random.default_rng(7000 + seed)
+    b = int(rng.integers(1, 90))
+    lens = rng.integers(0, 70000, size=b)
+    lens[rng.random(b) < 0.1] = 0
+    lens = lens.tolist()
+    kw = dict(h_k=int(rng.choice([1, 2, 4, 8])), n_q_tiles=int(rng.integers(1, 3)), cu_count=int(rng.choice([8, 64, 256])),
+              wg_per_cu=int(rng.integers(1, 9)), max_splits=int(rng.choice([4, 16, 64, 256])),
+              pieces_per_bin=int(rng.integers(1, 5)), dyn_percent=int(rng.integers(0, 60)))
+    work, ns, off, bins, nq = plan_queued(lens, **kw)
+    blocks = [max(1, math.ceil(L / 32)) for L in lens]
+    total = sum(blocks)
+    budget = total * (100 - kw["dyn_percent"]) // (100 * bins)
+    assert len(off) == bins + 1 and off[0] == 0 and off[-1] + nq == len(work)
+    size = lambda w: (w[2] - w[1]) // 32  # noqa: E731
+    for i in range(bins):
+        members = work[off[i]:off[i + 1]]  # may be empty when max_splits makes pieces few and large
+        assert sum(size(w) for w in members) <= budget or len(members) == 1
+    queue = work[off[-1]:]
+    assert [size(w) for w in queue] == sorted((size(w) for w in queue), reverse=True)
+    for s in range(len(lens)):
+        items = sorted(w for w in work if w[0] == s)
+        assert items[0][1] == 0 and items[-1][2] == 32 * blocks[s]
+        assert all(a[2] == c[1] for a, c in zip(items, items[1:]))
+        assert [w[3] for w in items] == list(range(len(items))) and ns[s] == len(items)
+        assert max(size(w) for w in items) - min(size(w) for w in items) <= 1  # even cut
+    assert max(ns) <= kw["max_splits"]
