@@ -250,29 +250,46 @@ __device__ __forceinline__ void load_q(const GqaParams& p, QOperand<NB>& q, cons
   }
 }
 
+// Lane-constant parts of the KV load offsets inside a 16-key group of a page
+// (row r16 / rows 4*g4 + i of the group), and of the clamp bound added to
+// a group's last-row offset.
+struct LaneOffsets {
+  uint32_t k, kb;     // K: r16 * k_row + 16 g4; 16 g4
+  uint32_t v[4], vb;  // V: (4 g4 + i) * v_row + 8 r16; 8 r16
+};
+
+__device__ __forceinline__ LaneOffsets lane_offsets(const GqaParams& p, int r16, int g4) {
+  LaneOffsets o;
+  o.k = (uint32_t)r16 * (uint32_t)p.k_row + 16u * (uint32_t)g4;
+  o.kb = 16u * (uint32_t)g4;
+  for (int i = 0; i < 4; ++i) o.v[i] = (uint32_t)(4 * g4 + i) * (uint32_t)p.v_row + 8u * (uint32_t)r16;
+  o.vb = 8u * (uint32_t)r16;
+  return o;
+}
+
 // The 13 loads of one 32-key block (keys kb.. clamped to last_key) of kv
 // head g from the two pages pg0 (keys kb..kb+15) and pg1 (kb+16..kb+31).
+// Group t starts at key s_t = min(kb + 16 t, last_key), row s_t & pmask of
+// its page (a 16-key group never straddles pages); that part of the address
+// is wave-uniform and goes into the scalar base of each load. A lane's row
+// inside the group is clamped to last_key - s_t, done on byte offsets
+// (min(row, lim) * stride = min(row * stride, lim * stride)), so a block
+// costs one add per group and one min per load of per-lane arithmetic.
 __device__ __forceinline__ RawBlock load_block(const GqaParams& p, int g, int kb, int pg0, int pg1, int last_key,
-                                               int pmask, int r16, int g4) {
-  // Page bases are wave-uniform (scalar registers); lanes add a 32-bit
-  // offset inside the page (page_size * row stride < 2^30, checked by the
-  // library), which the global loads take in their scalar-base form.
+                                               int pmask, const LaneOffsets& lo) {
   RawBlock r;
-  const uint8_t* kbase0 = p.k + (int64_t)pg0 * p.k_page + (int64_t)g * p.k_head;
-  const uint8_t* kbase1 = p.k + (int64_t)pg1 * p.k_page + (int64_t)g * p.k_head;
-  const uint8_t* vbase0 = p.v + (int64_t)pg0 * p.v_page + (int64_t)g * p.v_head;
-  const uint8_t* vbase1 = p.v + (int64_t)pg1 * p.v_page + (int64_t)g * p.v_head;
-  const uint32_t k_row = (uint32_t)p.k_row, v_row = (uint32_t)p.v_row;
   for (int t = 0; t < 2; ++t) {
-    const uint32_t row = (uint32_t)(min(kb + 16 * t + r16, last_key) & pmask);
-    const uint32_t off = row * k_row + 16u * (uint32_t)g4;
-    r.k[t][0] = *reinterpret_cast<const uint4*>((t ? kbase1 : kbase0) + off);
-    r.k[t][1] = *reinterpret_cast<const uint4*>((t ? kbase1 : kbase0) + (off + 64u));
-  }
-  for (int j = 0; j < 8; ++j) {
-    const int t = j >> 2;
-    const uint32_t row = (uint32_t)(min(kb + 16 * t + 4 * g4 + (j & 3), last_key) & pmask);
-    r.v[j] = *reinterpret_cast<const uint2*>((t ? vbase1 : vbase0) + (row * v_row + 8u * (uint32_t)r16));
+    const int st = min(kb + 16 * t, last_key);
+    const uint32_t lim = (uint32_t)max(last_key - st, 0);
+    const int64_t pg = t ? pg1 : pg0;
+    const uint32_t row = (uint32_t)(st & pmask);
+    const uint8_t* kbase = p.k + pg * p.k_page + (int64_t)g * p.k_head + row * (uint32_t)p.k_row;
+    const uint8_t* vbase = p.v + pg * p.v_page + (int64_t)g * p.v_head + row * (uint32_t)p.v_row;
+    const uint32_t koff = min(lo.k, lim * (uint32_t)p.k_row + lo.kb);
+    r.k[t][0] = *reinterpret_cast<const uint4*>(kbase + koff);
+    r.k[t][1] = *reinterpret_cast<const uint4*>(kbase + (koff + 64u));
+    const uint32_t vlim = lim * (uint32_t)p.v_row + lo.vb;
+    for (int i = 0; i < 4; ++i) r.v[4 * t + i] = *reinterpret_cast<const uint2*>(vbase + min(lo.v[i], vlim));
   }
   return r;
 }
@@ -603,10 +620,11 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
       pv[0] = page_pair(k_begin);
       pv[1 % STAGES] = page_pair(k_begin + kBlockKeys);
     }
+    const LaneOffsets lo = lane_offsets(p, r16, g4);
     auto fetch = [&](RawBlock& r, int kb, const int slot) {
       const int pg0 = clamp_page(p, __builtin_amdgcn_readlane(pv[slot], 0));
       const int pg1 = clamp_page(p, __builtin_amdgcn_readlane(pv[slot], 1));
-      r = load_block(p, g, kb, pg0, pg1, last_key, pmask, r16, g4);
+      r = load_block(p, g, kb, pg0, pg1, last_key, pmask, lo);
       pv[(slot + 2) % STAGES] = page_pair(kb + 2 * kBlockKeys);
     };
 
@@ -673,6 +691,7 @@ __device__ __forceinline__ void gqa_decode_persistent(const GqaParams& p, int la
   const int page_size = 1 << p.page_shift;
   const int pmask = page_size - 1;
   const int key_cap = p.max_blocks * page_size;
+  const LaneOffsets lo = lane_offsets(p, r16, g4);
   const int bin_hi = p.bin_offsets[blockIdx.x + 1];
   const int q0 = p.bin_offsets[gridDim.x];
   const int col = blockIdx.z * p.h_k + g;
@@ -754,7 +773,7 @@ __device__ __forceinline__ void gqa_decode_persistent(const GqaParams& p, int la
       const int kb = nx ? N.k_begin + kBlockKeys * (u - c_slots) : C.k_begin + kBlockKeys * u;
       const int pg0 = clamp_page(p, __builtin_amdgcn_readlane(pv[slot], 0));
       const int pg1 = clamp_page(p, __builtin_amdgcn_readlane(pv[slot], 1));
-      r = load_block(p, g, kb, pg0, pg1, nx ? n_last : c_last, pmask, r16, g4);
+      r = load_block(p, g, kb, pg0, pg1, nx ? n_last : c_last, pmask, lo);
       pv[(slot + 2) % S] = pair_of(u + 2, c_slots, pair_n);
     };
 
@@ -862,6 +881,7 @@ __device__ __forceinline__ void gqa_decode_stream(const GqaParams& p, int lane, 
   const int pmask = page_size - 1;
   const int key_cap = p.max_blocks * page_size;
   const RowMap<NB> rm = row_map<NB>(p, row0, r16);
+  const LaneOffsets lo = lane_offsets(p, r16, g4);
   const int it_lo = p.bin_offsets[blockIdx.x];
   const int it_hi = p.bin_offsets[blockIdx.x + 1];
 
@@ -968,7 +988,7 @@ __device__ __forceinline__ void gqa_decode_stream(const GqaParams& p, int lane, 
         block_at(j, b, kb, last);
         const int pg0 = clamp_page(p, __builtin_amdgcn_readlane(pv[slot], 0));
         const int pg1 = clamp_page(p, __builtin_amdgcn_readlane(pv[slot], 1));
-        r = load_block(p, g, kb, pg0, pg1, last, pmask, r16, g4);
+        r = load_block(p, g, kb, pg0, pg1, last, pmask, lo);
         pv[(slot + 2) % STAGES] = page_pair(j + 2);
       };
       RawBlock ring[STAGES];

@@ -37,9 +37,8 @@ struct MergeParams {
   int h_k, rows, h_r, q_len, d_v, max_splits;
 };
 
-// kSplitsPerRound splits are read per round with independent loads (the
-// (max, sum) pairs first, then the partial rows), so a row costs two memory
-// latencies per round instead of one per split.
+// kSplitsPerRound splits are read per round with independent loads, so a
+// row of up to that many splits costs one memory latency.
 constexpr int kSplitsPerRound = 16;
 
 template <int DV>
@@ -58,27 +57,39 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   if (ns <= 1) return;  // written by the decode
   ns = min(ns, p.max_splits);
 
+  // One round trip for up to kSplitsPerRound splits: the (max, sum) pairs and
+  // the partial rows are independent loads, issued together; the weights
+  // need the overall max, so a longer split list takes the max first.
   float m_star = -INFINITY;
-  for (int j0 = 0; j0 < ns; j0 += kSplitsPerRound) {
-    float mj[kSplitsPerRound];
-#pragma unroll
-    for (int u = 0; u < kSplitsPerRound; ++u)
-      mj[u] = j0 + u < ns ? p.ws_ml[(j0 + u) * p.split_stride + row].x : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < kSplitsPerRound; ++u) m_star = fmaxf(m_star, mj[u]);
-  }
-
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-  for (int j0 = 0; j0 < ns; j0 += kSplitsPerRound) {
-    float2 ml[kSplitsPerRound];
-    f32x4 oj[kSplitsPerRound];
+  float2 ml[kSplitsPerRound];
+  f32x4 oj[kSplitsPerRound];
+  auto load_round = [&](int j0) {
 #pragma unroll
     for (int u = 0; u < kSplitsPerRound; ++u) {
       const bool ok = j0 + u < ns;
       const int64_t pr = (int64_t)(j0 + u) * p.split_stride + row;
       ml[u] = ok ? p.ws_ml[pr] : float2{-INFINITY, 0.f};
       oj[u] = ok ? *reinterpret_cast<const f32x4*>(p.ws_o + pr * DV + 4 * tc) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  if (ns > kSplitsPerRound) {
+    for (int j0 = 0; j0 < ns; j0 += kSplitsPerRound) {
+      float mj[kSplitsPerRound];
+#pragma unroll
+      for (int u = 0; u < kSplitsPerRound; ++u)
+        mj[u] = j0 + u < ns ? p.ws_ml[(j0 + u) * p.split_stride + row].x : -INFINITY;
+#pragma unroll
+      for (int u = 0; u < kSplitsPerRound; ++u) m_star = fmaxf(m_star, mj[u]);
+    }
+  }
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  for (int j0 = 0; j0 < ns; j0 += kSplitsPerRound) {
+    load_round(j0);
+    if (ns <= kSplitsPerRound) {
+#pragma unroll
+      for (int u = 0; u < kSplitsPerRound; ++u) m_star = fmaxf(m_star, ml[u].x);
     }
 #pragma unroll
     for (int u = 0; u < kSplitsPerRound; ++u) {
