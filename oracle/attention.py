@@ -24,7 +24,8 @@ this result up to rounding order and its documented roundings of P.
 
 Layouts ([T5] module docstring):
   q           (num_seqs * q_len, h_q, d)   bf16 bit patterns (uint16) or e4m3 (uint8)
-  k/v cache   (num_pages, page_size, h_k, d) uint8 e4m3, any strides (logical view)
+  k/v cache   (num_pages, page_size, h_k, d) uint8 e4m3, any strides (logical view);
+              kv_format "e2m1": (num_pages, page_size, h_k, d/2) packed fp4 bytes
   block_table (num_seqs, max_blocks)        int32
   seq_lens    (num_seqs,)                   int32
   descales    broadcastable to (num_seqs, h_k), float32
@@ -46,7 +47,7 @@ variant against the generic core on the explicitly assembled 576-wide keys.
 
 import numpy as np
 
-from .formats import decode_bf16, decode_e4m3
+from .formats import KV_DECODERS, decode_bf16, decode_e4m3
 
 
 def _decode_q(q):
@@ -105,8 +106,11 @@ def attend(qrows, K, V, limits, softmax_scale, o_scale):
 
 
 def decode_attention(q, k_cache, v_cache, block_table, seq_lens, q_descale, k_descale, v_descale,
-                     *, q_len, h_k, softmax_scale, o_scale=1.0, causal=True):
-    """Decode attention of every sequence, KV head and packed row (steps 1-6)."""
+                     *, q_len, h_k, softmax_scale, o_scale=1.0, causal=True, kv_format="e4m3"):
+    """Decode attention of every sequence, KV head and packed row (steps 1-6).
+    kv_format names the K/V code format (step 3's dec): "e4m3", or "e2m1"
+    (packed fp4 rows, [T5] narrow KV formats)."""
+    dec_kv = KV_DECODERS[kv_format]
     q = np.asarray(q)
     seq_lens = np.asarray(seq_lens)
     num_seqs = seq_lens.shape[0]
@@ -119,15 +123,15 @@ def decode_attention(q, k_cache, v_cache, block_table, seq_lens, q_descale, k_de
     qd = _per_seq_head(q_descale, num_seqs, h_k) if q.dtype == np.uint8 else np.ones((num_seqs, h_k))
     kd = _per_seq_head(k_descale, num_seqs, h_k)
     vd = _per_seq_head(v_descale, num_seqs, h_k)
-    d_v = v_cache.shape[-1]
+    d_v = v_cache.shape[-1] * (2 if kv_format == "e2m1" else 1)
     o = np.zeros((num_seqs * q_len, h_q, d_v))
     lse = np.full((num_seqs, h_k, n_rows), -np.inf)
     for b in range(num_seqs):
         L = int(seq_lens[b])
         lim = row_limits(L, q_len, h_r, causal)
         for g in range(h_k):
-            K = decode_e4m3(gather_tokens(k_cache, block_table[b], L, g)) * kd[b, g]
-            V = decode_e4m3(gather_tokens(v_cache, block_table[b], L, g)) * vd[b, g]
+            K = dec_kv(gather_tokens(k_cache, block_table[b], L, g)) * kd[b, g]
+            V = dec_kv(gather_tokens(v_cache, block_table[b], L, g)) * vd[b, g]
             # packed row n = qi * h_r + hr  <-  token b*q_len + qi, head g*h_r + hr
             rows = qf[b * q_len:(b + 1) * q_len, g * h_r:(g + 1) * h_r].reshape(n_rows, d) * qd[b, g]
             ob, lb = attend(rows, K, V, lim, softmax_scale, o_scale)

@@ -38,19 +38,41 @@ def bf16_bits_to_float(bits):
     return s * math.ldexp(128 + m, e - 134)  # (1 + m/128) * 2^(e-127)
 
 
+def e2m1_nibble_to_float(code):
+    """One e2m1 code from its bit fields: sign | 2-bit exponent (bias 1) | 1-bit mantissa."""
+    code = int(code)
+    s = -1.0 if code & 8 else 1.0
+    e = (code >> 1) & 3
+    m = code & 1
+    if e == 0:
+        return s * math.ldexp(m, -1)  # m/2 * 2^0
+    return s * math.ldexp(2 + m, e - 2)  # (1 + m/2) * 2^(e-1)
+
+
+def fp4_row_to_floats(row):
+    """A packed fp4 row (d/2 bytes) -> d floats: the low nibble of byte i is
+    element 2i, the high nibble element 2i+1."""
+    out = []
+    for byte in row:
+        byte = int(byte)
+        out.append(e2m1_nibble_to_float(byte & 15))
+        out.append(e2m1_nibble_to_float(byte >> 4))
+    return out
+
+
 def _dec(x, fmt):
     return e4m3_bits_to_float(x) if fmt == "e4m3" else bf16_bits_to_float(x)
 
 
 def brute_decode_attention(q, q_fmt, k_cache, v_cache, block_table, seq_lens, qd, kd, vd,
-                           q_len, h_k, softmax_scale, o_scale, causal):
+                           q_len, h_k, softmax_scale, o_scale, causal, kv_fmt="e4m3"):
     """All arguments are nested Python lists (or array-likes indexed one
     element at a time). qd/kd/vd are (num_seqs, h_k) nested lists; qd is
     ignored for bf16 q. Returns (o[token][head][dim], lse[seq][g][n])."""
     num_seqs = len(seq_lens)
     h_q = len(q[0])
     d = len(q[0][0])
-    d_v = len(v_cache[0][0][0])
+    d_v = len(v_cache[0][0][0]) * (2 if kv_fmt == "e2m1" else 1)
     ps = len(k_cache[0])
     h_r = h_q // h_k
     o = [[[0.0] * d_v for _ in range(h_q)] for _ in range(num_seqs * q_len)]
@@ -70,8 +92,12 @@ def brute_decode_attention(q, q_fmt, k_cache, v_cache, block_table, seq_lens, qd
                     for j in range(last + 1):
                         page = int(block_table[b][j // ps])
                         row = j % ps
-                        kv = [e4m3_bits_to_float(k_cache[page][row][g][i]) * float(kd[b][g]) for i in range(d)]
-                        vv = [e4m3_bits_to_float(v_cache[page][row][g][i]) * float(vd[b][g]) for i in range(d_v)]
+                        if kv_fmt == "e2m1":
+                            kv = [x * float(kd[b][g]) for x in fp4_row_to_floats(k_cache[page][row][g])]
+                            vv = [x * float(vd[b][g]) for x in fp4_row_to_floats(v_cache[page][row][g])]
+                        else:
+                            kv = [e4m3_bits_to_float(k_cache[page][row][g][i]) * float(kd[b][g]) for i in range(d)]
+                            vv = [e4m3_bits_to_float(v_cache[page][row][g][i]) * float(vd[b][g]) for i in range(d_v)]
                         scores.append(softmax_scale * math.fsum(a * c for a, c in zip(qv, kv)))
                         values.append(vv)
                     top = max(scores)

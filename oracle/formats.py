@@ -1,4 +1,5 @@
-"""Element formats read by the decode path: OCP e4m3 (fp8) and bf16.
+"""Element formats read by the decode path: OCP e4m3 (fp8), bf16, and the
+packed 4-bit e2m1 (fp4) KV format.
 
 Test infrastructure only (see ``oracle/__init__``).
 
@@ -8,9 +9,19 @@ with bias 7, 3 mantissa bits, no infinities, a single NaN mantissa pattern,
 largest finite value 448). The page's harness poisons unused pages with the
 byte 0x7F and calls it the e4m3fn NaN; it names 448 as the e4m3 maximum.
 
+The narrow KV formats of [T5] (module docstring "KV cache formats" and
+"Narrow KV formats: value tables, quantization and bit packing"): e2m1 has
+1 sign bit, 2 exponent bits with bias 1 and 1 mantissa bit, no infinities
+and no NaN; exponent 0 is subnormal (m/2 * 2^(1-bias)). A row of d codes is
+stored as a little-endian bitstream of d/2 bytes: element 2i in the low
+nibble of byte i, element 2i+1 in its high nibble.
+
 Pinned by tests/test_oracle.py: known codes (0x7E = 448, 0x08 = 2^-6,
 0x01 = 2^-9, 0x38 = 1, 0x7F/0xFF = NaN, sign symmetry), strict monotonicity
-of the finite positive codes, and agreement with torch's float8_e4m3fn cast.
+of the finite positive codes, and agreement with torch's float8_e4m3fn cast;
+the e2m1 value set (golden file of the OCP MX fp4 values), the nibble order
+on hand-packed bytes, and the packed decode against a bit-field decode in
+``oracle.brute``.
 """
 
 import numpy as np
@@ -47,3 +58,37 @@ def decode_bf16(bits) -> np.ndarray:
     if b.dtype != np.uint16:
         raise TypeError(f"bf16 bits must be uint16, got {b.dtype}")
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _e2m1_value(code: int) -> float:
+    """Value of one e2m1 code (4 bits), straight from the format definition."""
+    sign = -1.0 if code & 0x8 else 1.0
+    exp = (code >> 1) & 0x3
+    man = code & 0x1
+    if exp == 0:  # subnormal: 2^(1 - bias) * (m / 2)
+        return sign * (man / 2.0)
+    return sign * (2.0 ** (exp - 1)) * (1.0 + man / 2.0)
+
+
+E2M1_TABLE = np.array([_e2m1_value(c) for c in range(16)], dtype=np.float64)
+E2M1_TABLE.setflags(write=False)
+
+
+def unpack_fp4(packed) -> np.ndarray:
+    """uint8 bytes (..., d/2) -> uint8 codes (..., d): element 2i is the low
+    nibble of byte i, element 2i+1 its high nibble."""
+    b = np.asarray(packed)
+    if b.dtype != np.uint8:
+        raise TypeError(f"packed fp4 rows must be uint8, got {b.dtype}")
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b & 0xF
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def decode_e2m1_packed(packed) -> np.ndarray:
+    """Packed e2m1 rows (..., d/2) uint8 -> float64 values (..., d)."""
+    return E2M1_TABLE[unpack_fp4(packed)]
+
+
+KV_DECODERS = {"e4m3": decode_e4m3, "e2m1": decode_e2m1_packed}

@@ -30,7 +30,12 @@ Data recipe (following the t5_decode page's harness, ``run``):
     that sequence's L tokens and d, 1e-6) / 448, codes = e4m3(x / descale)
     (round to nearest even, |x / descale| <= 448 by construction);
   * latent records: 512 latent values ~ N(0, 1) with one descale per token
-    and 128-value block (amax / 448), 64 rope values ~ N(0, 1) in bf16.
+    and 128-value block (amax / 448), 64 rope values ~ N(0, 1) in bf16;
+  * packed e2m1 (fp4) K/V (the page's narrow KV formats): x ~ N(0, 1) per
+    (sequence, kv head) with descale = max(amax, 1e-6) / 6 and the code of
+    the nearest e2m1 magnitude (ties to the smaller, as the page's
+    ``minifloat_quantize``), packed two per byte, element 2i in the low
+    nibble; unused pages and tail rows hold 0x77 (there is no fp4 NaN).
 Random tensors come from a torch generator on the target device, seeded per
 workload, so a GPU batch is generated on the GPU.
 """
@@ -43,6 +48,8 @@ import torch
 
 E4M3_MAX = 448.0
 E4M3_NAN = 0x7F
+E2M1_MAGNITUDES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)  # codes 0..7
+E2M1_FILL = 0x77
 MLA_LATENT, MLA_ROPE, MLA_BLOCK = 512, 64, 128
 MLA_RECORD_BYTES = MLA_LATENT + 2 * MLA_ROPE + 4 * (MLA_LATENT // MLA_BLOCK)  # 656
 
@@ -60,7 +67,7 @@ class Workload:
     seq_len_dist: tuple  # ("fixed", [..]) | ("uniform", lo, hi) | ("lognormal", median, sigma, lo, hi) | ("mix", ...)
     max_splits: int = 16
     q_format: str = "bf16"  # "bf16" | "e4m3"
-    kv_format: str = "e4m3"  # "e4m3" | "mla"
+    kv_format: str = "e4m3"  # "e4m3" | "mla" | "e2m1" (packed fp4)
     causal: bool = True
     seed: int = 1111
     num_pages: int = 0  # 0: used + max(4, used // 4)
@@ -94,6 +101,10 @@ WORKLOADS = {
                 ("mix", 0.1, (32768, 65536), (1024, 4096)), max_splits=64, q_format="e4m3", seed=1115),
     5: Workload("mla_b32_hq16_hk1_d576-512_ps64_L2k-16k", 32, 1, 16, 1, 576, 512, 64,
                 ("uniform", 2048, 16384), max_splits=64, kv_format="mla", seed=1116),
+    # the fully-fp8 workload with packed fp4 (e2m1) K/V: the page's narrow KV formats
+    6: Workload("fp4kv_b128_hq64_hk4_d128_ps128_mix1k-4k_32k-64k", 128, 1, 64, 4, 128, 128, 128,
+                ("mix", 0.1, (32768, 65536), (1024, 4096)), max_splits=64, q_format="e4m3", kv_format="e2m1",
+                seed=1115),
 }
 
 
@@ -153,6 +164,8 @@ class Batch:
         w = self.spec
         if w.kv_format == "mla":
             return toks * MLA_RECORD_BYTES
+        if w.kv_format == "e2m1":
+            return toks * w.h_k * (w.d_qk + w.d_v) // 2
         return toks * w.h_k * (w.d_qk + w.d_v)
 
     def to_numpy(self):
@@ -213,6 +226,23 @@ def _quantise_per_seq_head(x, seg, num_seqs):
     return y.to(torch.float8_e4m3fn).view(torch.uint8), desc.contiguous()
 
 
+def _quantise_fp4_per_seq_head(x, seg, num_seqs):
+    """x (tokens, h_k, d) float32 -> (packed codes uint8 (tokens, h_k, d/2), descale (b, h_k))."""
+    h_k = x.shape[1]
+    amax = torch.zeros(num_seqs, h_k, device=x.device)
+    amax.scatter_reduce_(0, seg[:, None].expand(-1, h_k), x.abs().amax(dim=-1), "amax")
+    desc = amax.clamp(min=1e-6) / E2M1_MAGNITUDES[-1]
+    y = (x / desc[seg][:, :, None]).clamp(-E2M1_MAGNITUDES[-1], E2M1_MAGNITUDES[-1])
+    mags = torch.tensor(E2M1_MAGNITUDES, device=x.device)
+    ay = y.abs()
+    hi = torch.bucketize(ay, mags).clamp(max=len(E2M1_MAGNITUDES) - 1)  # first magnitude >= |y|
+    lo = (hi - 1).clamp(min=0)
+    code = torch.where((ay - mags[lo]) <= (mags[hi] - ay), lo, hi)
+    code = code | ((y < 0) & (mags[code] > 0)).to(code.dtype) << 3
+    code = code.to(torch.uint8)
+    return (code[..., 0::2] | (code[..., 1::2] << 4)).contiguous(), desc.contiguous()
+
+
 def make_batch(w: Workload, device="cpu", seq_lens=None) -> Batch:
     """Generate the batch of workload ``w`` on ``device``."""
     rng = np.random.Generator(np.random.PCG64(w.seed + 7))
@@ -254,17 +284,20 @@ def make_batch(w: Workload, device="cpu", seq_lens=None) -> Batch:
         return batch
 
     d = w.d_qk
+    fp4 = w.kv_format == "e2m1"
+    row_bytes = d // 2 if fp4 else d
+    fill = E2M1_FILL if fp4 else E4M3_NAN
     if w.kv_layout == "nhd":
-        kbuf = torch.full((2, num_pages, ps, h_k, d), E4M3_NAN, dtype=torch.uint8, device=device)
+        kbuf = torch.full((2, num_pages, ps, h_k, row_bytes), fill, dtype=torch.uint8, device=device)
         k_view, v_view = kbuf[0], kbuf[1]
     elif w.kv_layout == "hnd":
-        kbuf = torch.full((num_pages, 2, h_k, ps, d), E4M3_NAN, dtype=torch.uint8, device=device)
+        kbuf = torch.full((num_pages, 2, h_k, ps, row_bytes), fill, dtype=torch.uint8, device=device)
         k_view, v_view = kbuf[:, 0].transpose(1, 2), kbuf[:, 1].transpose(1, 2)
     else:
         raise ValueError(f"unknown kv_layout {w.kv_layout}")
     for view, name in ((k_view, "k"), (v_view, "v")):
         x = torch.randn(n_tok, h_k, d, generator=gen, device=device)
-        codes, desc = _quantise_per_seq_head(x, seg, b)
+        codes, desc = (_quantise_fp4_per_seq_head if fp4 else _quantise_per_seq_head)(x, seg, b)
         del x
         pages, rows = slot // ps, slot % ps
         view[pages, rows] = codes

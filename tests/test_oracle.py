@@ -126,6 +126,78 @@ def test_bf16_decode_matches_torch():
     assert np.array_equal(formats.decode_bf16(bits), ref)
 
 
+def test_e2m1_golden_codes():
+    rows = [ln.split() for ln in open(os.path.join(GOLDEN, "e2m1_codes.txt")) if ln.strip() and ln[0] != "#"]
+    assert len(rows) == 16
+    for code, val in rows:
+        got = formats.E2M1_TABLE[int(code, 16)]
+        assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val)), (code, got, val)
+
+
+def test_fp4_nibble_order_and_packed_decode():
+    # byte i holds element 2i in its low nibble and element 2i+1 in its high nibble
+    packed = np.array([[0x21, 0xF7, 0x80]], dtype=np.uint8)
+    assert formats.unpack_fp4(packed).tolist() == [[1, 2, 7, 15, 0, 8]]
+    assert formats.decode_e2m1_packed(packed).tolist() == [[0.5, 1.0, 6.0, -6.0, 0.0, -0.0]]
+    rng = np.random.default_rng(3)
+    rows = rng.integers(0, 256, size=(5, 8), dtype=np.uint8)
+    ref = [brute.fp4_row_to_floats(r) for r in rows.tolist()]
+    assert formats.decode_e2m1_packed(rows).tolist() == ref
+
+
+def fp4_case(rng, **kw):
+    """tiny_case with packed e2m1 K/V (random bytes: every code is finite)."""
+    c = tiny_case(rng, **kw)
+    for name in ("k_cache", "v_cache"):
+        shp = c[name].shape
+        c[name] = rng.integers(0, 256, size=shp[:-1] + (shp[-1] // 2,), dtype=np.uint8)
+    return c
+
+
+FP4_CASES = [
+    dict(num_seqs=2, q_len=1, h_q=4, h_k=2, d=8, ps=4, lens=(5, 11), q_fmt="e4m3", causal=True),
+    dict(num_seqs=2, q_len=3, h_q=4, h_k=2, d=8, ps=8, lens=(9, 3), q_fmt="e4m3", causal=False),
+    dict(num_seqs=3, q_len=2, h_q=6, h_k=3, d=16, ps=4, lens=(0, 1, 13), q_fmt="e4m3", causal=True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(FP4_CASES)))
+def test_fp4_oracle_matches_brute_force(case):
+    cfg = dict(FP4_CASES[case])
+    causal = cfg.pop("causal")
+    c = fp4_case(np.random.default_rng(900 + case), **cfg)
+    kw = dict(softmax_scale=0.37, o_scale=1.25, causal=causal)
+    o, lse = run_oracle(c, kv_format="e2m1", **kw)
+    ob, lb = brute.brute_decode_attention(
+        c["q"].tolist(), "e4m3", c["k_cache"].tolist(), c["v_cache"].tolist(), c["block_table"].tolist(),
+        c["seq_lens"].tolist(), c["q_descale"].tolist(), c["k_descale"].tolist(), c["v_descale"].tolist(),
+        c["q_len"], c["h_k"], kw["softmax_scale"], kw["o_scale"], kw["causal"], kv_fmt="e2m1")
+    assert o.shape[-1] == cfg["d"] and np.all(np.isfinite(o))
+    np.testing.assert_allclose(o, np.array(ob), rtol=0, atol=1e-12)
+    fin = np.isfinite(lse)
+    np.testing.assert_array_equal(fin, np.isfinite(np.array(lb)))
+    np.testing.assert_allclose(lse[fin], np.array(lb)[fin], rtol=0, atol=1e-12)
+
+
+def test_fp4_equals_e4m3_on_the_same_values():
+    # every e2m1 value is an e4m3 value: re-encoding the unpacked codes as the
+    # e4m3 bytes of the same values (found by lookup in the e4m3 table) must
+    # give the identical result through the e4m3 path
+    c = fp4_case(np.random.default_rng(77), num_seqs=2, q_len=2, h_q=4, h_k=2, d=16, ps=4, lens=(6, 13),
+                 q_fmt="e4m3")
+    mag = {float(formats.E4M3_TABLE[m]): m for m in range(0x7F)}  # finite non-negative e4m3 codes
+    lut = np.array([mag[abs(float(formats.E2M1_TABLE[c]))] | (0x80 if c & 8 else 0) for c in range(16)],
+                   dtype=np.uint8)
+    c8 = dict(c)
+    c8["k_cache"] = lut[formats.unpack_fp4(c["k_cache"])]
+    c8["v_cache"] = lut[formats.unpack_fp4(c["v_cache"])]
+    assert np.array_equal(formats.decode_e4m3(c8["k_cache"]), formats.decode_e2m1_packed(c["k_cache"]))
+    kw = dict(softmax_scale=0.29, causal=True)
+    o4, l4 = run_oracle(c, kv_format="e2m1", **kw)
+    o8, l8 = run_oracle(c8, **kw)
+    assert np.array_equal(o4, o8) and np.array_equal(l4, l8)
+
+
 # ----------------------------------------------------------------------------
 # attention: brute force, special cases, textbook routine
 # ----------------------------------------------------------------------------
