@@ -18,7 +18,8 @@ sample of the same batch on the host cores. Diagnostics go to stderr.
 
 Default workload: 64 sequences, q_len 1, 32 query heads on 8 e4m3 KV heads,
 d = 128, 16-key pages, lengths uniform in [512, 8192], split-KV up to 16
-chunks (``--config 2``). ``--config 1..4`` selects the other workloads.
+chunks (``--config 2``). ``--config 1..5`` selects the other workloads; 6 is
+workload 4 with packed fp4 (e2m1) K/V.
 """
 
 import argparse
@@ -215,7 +216,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6],
+                    help="workload: 1-5 as specified, 6 = workload 4 with packed fp4 (e2m1) K/V")
     ap.add_argument("--q-len", type=int, default=None, help="query tokens per sequence (latent workload: 1..16)")
     ap.add_argument("--causal", type=int, default=None, help="override the workload's causal flag (0/1)")
     ap.add_argument("--pools", type=int, default=0, help="KV pools to rotate (0: enough for >= 1 GiB, min 3)")

@@ -203,6 +203,13 @@ pkv_status pkv_plan_queued(const int32_t* seq_lens, int32_t num_seqs, int32_t h_
 
 #define PKV_KV_E4M3 0 /* K and V caches of e4m3 codes, d_qk = d_v = 128 */
 #define PKV_KV_MLA 1  /* latent records: h_k = 1, d_qk = 576 (512 latent + 64 rope), d_v = 512 */
+/* Packed fp4 K and V caches ("mjolnir-kernel 0.1.0 wheel: mjolnir/t5_decode.py",
+ * narrow KV formats): e2m1 codes (1 sign, 2 exponent bits with bias 1, 1
+ * mantissa bit; no inf/NaN), a row of d = 128 codes in 64 bytes with element
+ * 2i in the low nibble of byte i; the usual per-(sequence, kv-head) descales;
+ * d_qk = d_v = 128 and an e4m3 query (PKV_Q_E4M3); one-wave plan only (no
+ * bin_offsets / queue). */
+#define PKV_KV_E2M1 2
 
 /*
  * All strides are in ELEMENTS of the pointed-to type, >= 0; a descale
@@ -212,6 +219,7 @@ pkv_status pkv_plan_queued(const int32_t* seq_lens, int32_t num_seqs, int32_t h_
  * the last dimension contiguous):
  *   q      [num_seqs * q_len][h_q][d_qk]     bf16 or e4m3  (q_tok_stride, q_head_stride)
  *   k, v   [num_pages][page_size][h_k][d]    e4m3 codes    (page, row, head strides, bytes)
+ *          PKV_KV_E2M1: [num_pages][page_size][h_k][d/2] packed fp4 bytes (byte strides)
  *          MLA: k = v = latent [pages][PS][1][512] e4m3 (v may be NULL or equal k)
  *   k_rope MLA only: [pages][PS][1][64] bf16 (page, row strides)
  *   k_blk_scale MLA only: [pages][PS][1][4] fp32, one scale per 128 latent values
@@ -269,8 +277,8 @@ typedef struct pkv_decode_args {
   int32_t max_splits;
   void* workspace;
   size_t workspace_bytes;
-  /* Optional, device int32[num_seqs * h_k * n_q_tiles] (e4m3 K/V cache only;
-   * ignored for the latent cache): when non-NULL the decode merges split
+  /* Optional, device int32[num_seqs * h_k * n_q_tiles] (e4m3 or fp4 K/V
+   * cache; ignored for the latent cache): when non-NULL the decode merges split
    * sequences itself (the last split of each (sequence,
    * kv head, q-row tile) to finish combines the partials, same rule and
    * order as pkv_merge_splits) and pkv_merge_splits does nothing. The

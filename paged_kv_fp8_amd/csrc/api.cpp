@@ -49,6 +49,11 @@ pkv_status check_shapes(const pkv_decode_args* a) {
     if (a->d_qk != 128 || a->d_v != 128)
       return fail(PKV_ERR_UNSUPPORTED, "e4m3 cache: d_qk=%d d_v=%d, only 128/128 is built", a->d_qk, a->d_v);
     if (rows > 4096) return fail(PKV_ERR_UNSUPPORTED, "q_len * h_r = %lld rows > 4096", (long long)rows);
+  } else if (a->kv_format == PKV_KV_E2M1) {
+    if (a->d_qk != 128 || a->d_v != 128)
+      return fail(PKV_ERR_UNSUPPORTED, "fp4 cache: d_qk=%d d_v=%d, only 128/128 is built", a->d_qk, a->d_v);
+    if (a->q_format != PKV_Q_E4M3) return fail(PKV_ERR_UNSUPPORTED, "fp4 cache: the query must be e4m3");
+    if (rows > 4096) return fail(PKV_ERR_UNSUPPORTED, "q_len * h_r = %lld rows > 4096", (long long)rows);
   } else if (a->kv_format == PKV_KV_MLA) {
     if (a->d_qk != 576 || a->d_v != 512 || a->h_k != 1)
       return fail(PKV_ERR_UNSUPPORTED, "latent cache needs h_k=1, d_qk=576, d_v=512 (got %d, %d, %d)", a->h_k,
@@ -92,6 +97,8 @@ pkv_status check_pointers(const pkv_decode_args* a, bool for_merge) {
   if (!aligned(a->work, 16)) return fail(PKV_ERR_INVALID_ARG, "work must be 16-B aligned");
   if (a->bin_offsets && (a->num_bins < 1 || !aligned(a->bin_offsets, 4)))
     return fail(PKV_ERR_INVALID_ARG, "bin_offsets needs num_bins >= 1 and 4-B alignment");
+  if (a->kv_format == PKV_KV_E2M1 && (a->bin_offsets || a->queue))
+    return fail(PKV_ERR_UNSUPPORTED, "fp4 cache: only the one-wave plan (pkv_plan_split_kv) is built");
   if (a->queue) {
     if (!a->bin_offsets) return fail(PKV_ERR_INVALID_ARG, "queue needs bin_offsets (a plan from pkv_plan_queued)");
     if (!aligned(a->queue, 4)) return fail(PKV_ERR_INVALID_ARG, "queue must be 4-B aligned");
@@ -206,7 +213,7 @@ extern "C" pkv_status pkv_merge_splits(const pkv_decode_args* a, void* stream) {
   if (st != PKV_OK) return st;
   if ((st = check_pointers(a, true)) != PKV_OK) return st;
   // the e4m3-cache decode merges in place when given counters
-  if (a->max_splits == 1 || (a->merge_counters && a->kv_format == PKV_KV_E4M3)) return PKV_OK;
+  if (a->max_splits == 1 || (a->merge_counters && a->kv_format != PKV_KV_MLA)) return PKV_OK;
   return hip_status(merge_launch(*a, static_cast<hipStream_t>(stream)), "merge launch");
 }
 

@@ -42,6 +42,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "pkv_internal.h"
 
@@ -294,6 +295,74 @@ __device__ __forceinline__ RawBlock load_block(const GqaParams& p, int g, int kb
   return r;
 }
 
+// ---- packed fp4 (e2m1) K/V --------------------------------------------------
+// A cache row holds d = 128 codes in 64 bytes, element 2i in the low nibble
+// of byte i ("mjolnir-kernel 0.1.0 wheel: mjolnir/t5_decode.py", narrow KV
+// formats and pack_subbyte).
+//
+// Raw bytes of one 32-key block as this lane loads them: K for the QK^T
+// operand of v_mfma_scale_f32_16x16x128_f8f6f4 (the 32 codes d = 32*g4 ..
+// 32*g4+31 of key kb+16t+r16, one 16-byte run), V as 8 codes (d_v 8*r16 ..)
+// of each of the lane's 8 keys. With an fp4 A and an e4m3 B operand the
+// instruction pairs the A nibbles of lane group g with the B bytes of lane
+// groups {0, 2} (g even) or {1, 3} (g odd) in 16-element chunks; measured
+// slot by slot, that puts d = 32*g4.. here against exactly the head dims the
+// e4m3 query operand (d = 64*(s>>1) + 16*g4 + 8*(s&1) ..) holds.
+struct RawBlock4 {
+  uint4 k[2];
+  uint32_t v[8];
+};
+
+struct LaneOffsets4 {
+  uint32_t k, kb;     // K: r16 * k_row + 16 g4; 16 g4
+  uint32_t v[4], vb;  // V: (4 g4 + i) * v_row + 4 r16; 4 r16
+};
+
+__device__ __forceinline__ LaneOffsets4 lane_offsets4(const GqaParams& p, int r16, int g4) {
+  LaneOffsets4 o;
+  o.k = (uint32_t)r16 * (uint32_t)p.k_row + 16u * (uint32_t)g4;
+  o.kb = 16u * (uint32_t)g4;
+  for (int i = 0; i < 4; ++i) o.v[i] = (uint32_t)(4 * g4 + i) * (uint32_t)p.v_row + 4u * (uint32_t)r16;
+  o.vb = 4u * (uint32_t)r16;
+  return o;
+}
+
+// load_block for packed fp4 rows: 2 + 8 loads, same row clamping.
+__device__ __forceinline__ RawBlock4 load_block4(const GqaParams& p, int g, int kb, int pg0, int pg1, int last_key,
+                                                 int pmask, const LaneOffsets4& lo) {
+  RawBlock4 r;
+  for (int t = 0; t < 2; ++t) {
+    const int st = min(kb + 16 * t, last_key);
+    const uint32_t lim = (uint32_t)max(last_key - st, 0);
+    const int64_t pg = t ? pg1 : pg0;
+    const uint32_t row = (uint32_t)(st & pmask);
+    const uint8_t* kbase = p.k + pg * p.k_page + (int64_t)g * p.k_head + row * (uint32_t)p.k_row;
+    const uint8_t* vbase = p.v + pg * p.v_page + (int64_t)g * p.v_head + row * (uint32_t)p.v_row;
+    const uint32_t koff = min(lo.k, lim * (uint32_t)p.k_row + lo.kb);
+    r.k[t] = *reinterpret_cast<const uint4*>(kbase + koff);
+    const uint32_t vlim = lim * (uint32_t)p.v_row + lo.vb;
+    for (int i = 0; i < 4; ++i) r.v[4 * t + i] = *reinterpret_cast<const uint32_t*>(vbase + min(lo.v[i], vlim));
+  }
+  return r;
+}
+
+// Eight e2m1 codes (element 2i in the low nibble of byte i) -> their e4m3
+// bytes, exact (every e2m1 value is an e4m3 value): the magnitude (3 bits)
+// picks one of 8 bytes with v_perm_b32 (0, 0.5, 1, 1.5, 2, 3, 4, 6 as
+// 0x00 0x30 0x38 0x3C 0x40 0x44 0x48 0x4C), the sign moves from bit 3 to 7.
+__device__ __forceinline__ uint32_t e2m1x4_to_e4m3(uint32_t spread) {
+  // spread = [b, b, c, c] -> nibbles [b & 15, b >> 4, c & 15, c >> 4], one per byte
+  const uint32_t n = (spread & 0x000F000Fu) | ((spread >> 4) & 0x0F000F00u);
+  const uint32_t mag = __builtin_amdgcn_perm(0x4C484440u, 0x3C383000u, n & 0x07070707u);
+  return mag | ((n & 0x08080808u) << 4);
+}
+__device__ __forceinline__ uint2 e2m1x8_to_e4m3(uint32_t x) {
+  return uint2{e2m1x4_to_e4m3(__builtin_amdgcn_perm(x, x, 0x01010000u)),
+               e2m1x4_to_e4m3(__builtin_amdgcn_perm(x, x, 0x03030202u))};
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
 // One 32-key block: S = K Q^T, online softmax, O^T += V^T P^T. lim[nb] is
 // the last key row r16 of block nb may see; keys past lim_min need the mask.
 // Query operand parked in LDS (two row blocks: saves the registers that would
@@ -310,37 +379,13 @@ __device__ __forceinline__ void park_q(const QOperand<NB>& q, uint8_t* qlds, int
     }
 }
 
-template <bool FP8Q, int NB, bool QLDS>
-__device__ __forceinline__ void process_block(const RawBlock& cur, int kb, const QOperand<NB>& q, const uint8_t* qlds,
-                                              RowState<NB>& st, const int* lim, int lim_min, float c2, int g4) {
-  const int lane = threadIdx.x & 63;
-  // keep the LDS query reads inside the loop (hoisted, they would occupy the
-  // registers this form saves)
-  if (QLDS) asm volatile("" ::: "memory");
-  // ---- S = K Q^T (keys on M) -----------------------------------------------
-  f32x4 sacc[NB][2];
-  for (int nb = 0; nb < NB; ++nb)
-    for (int t = 0; t < 2; ++t) sacc[nb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int t = 0; t < 2; ++t) {
-    for (int s = 0; s < 4; ++s) {
-      const uint2 kraw = half_of(cur.k[t][s >> 1], s & 1);
-      if (FP8Q) {
-        const long a = as_long(kraw);
-        for (int nb = 0; nb < NB; ++nb) {
-          const long b = QLDS ? *reinterpret_cast<const long*>(qlds + ((4 * nb + s) * 64 + lane) * 8) : q.q8[nb][s];
-          sacc[nb][t] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, sacc[nb][t], 0, 0, 0);
-        }
-      } else {
-        const bf16x8 a = e4m3x8_to_bf16(kraw);
-        for (int nb = 0; nb < NB; ++nb) {
-          const bf16x8 b =
-              QLDS ? *reinterpret_cast<const bf16x8*>(qlds + ((4 * nb + s) * 64 + lane) * 16) : q.qb[nb][s];
-          sacc[nb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, sacc[nb][t], 0, 0, 0);
-        }
-      }
-    }
-  }
-
+// Online softmax of one 32-key block's scores and O^T += V^T P^T, with the
+// block's V as e4m3 (fp8 path) codes or as the bytes the bf16 path converts
+// exactly: vraw[j] holds key kb + 16 (j >> 2) + 4 g4 + (j & 3), d_v bytes
+// 8 r16 .. 8 r16 + 7 of this lane.
+template <bool FP8Q, int NB>
+__device__ __forceinline__ void softmax_pv(f32x4 (&sacc)[NB][2], const uint2 (&vraw)[8], int kb, RowState<NB>& st,
+                                           const int* lim, int lim_min, float c2, int g4) {
   // ---- online softmax (per query row = lane column r16) --------------------
   bf16x8 pb[NB];
   long p8[NB];
@@ -397,10 +442,10 @@ __device__ __forceinline__ void process_block(const RawBlock& cur, int kb, const
     for (int w2 = 0; w2 < 2; ++w2) {
       unsigned col[2][4];  // [kq][e]: keys 4kq..4kq+3 at d_v 8*r16 + 4*w2 + e
       for (int kq = 0; kq < 2; ++kq) {
-        const unsigned r0 = w2 ? cur.v[4 * kq + 0].y : cur.v[4 * kq + 0].x;
-        const unsigned r1 = w2 ? cur.v[4 * kq + 1].y : cur.v[4 * kq + 1].x;
-        const unsigned r2 = w2 ? cur.v[4 * kq + 2].y : cur.v[4 * kq + 2].x;
-        const unsigned r3 = w2 ? cur.v[4 * kq + 3].y : cur.v[4 * kq + 3].x;
+        const unsigned r0 = w2 ? vraw[4 * kq + 0].y : vraw[4 * kq + 0].x;
+        const unsigned r1 = w2 ? vraw[4 * kq + 1].y : vraw[4 * kq + 1].x;
+        const unsigned r2 = w2 ? vraw[4 * kq + 2].y : vraw[4 * kq + 2].x;
+        const unsigned r3 = w2 ? vraw[4 * kq + 3].y : vraw[4 * kq + 3].x;
         const unsigned t0 = __builtin_amdgcn_perm(r0, r1, 0x01050004u);
         const unsigned t1 = __builtin_amdgcn_perm(r0, r1, 0x03070206u);
         const unsigned t2 = __builtin_amdgcn_perm(r2, r3, 0x01050004u);
@@ -421,8 +466,8 @@ __device__ __forceinline__ void process_block(const RawBlock& cur, int kb, const
     for (int w2 = 0; w2 < 2; ++w2) {
       unsigned xy[4][2];  // [key pair pp][0: d_v bytes 0,1 / 1: bytes 2,3 of the word], interleaved by key
       for (int pp = 0; pp < 4; ++pp) {
-        const unsigned a0 = w2 ? cur.v[2 * pp].y : cur.v[2 * pp].x;
-        const unsigned a1 = w2 ? cur.v[2 * pp + 1].y : cur.v[2 * pp + 1].x;
+        const unsigned a0 = w2 ? vraw[2 * pp].y : vraw[2 * pp].x;
+        const unsigned a1 = w2 ? vraw[2 * pp + 1].y : vraw[2 * pp + 1].x;
         xy[pp][0] = __builtin_amdgcn_perm(a0, a1, 0x01050004u);
         xy[pp][1] = __builtin_amdgcn_perm(a0, a1, 0x03070206u);
       }
@@ -440,6 +485,68 @@ __device__ __forceinline__ void process_block(const RawBlock& cur, int kb, const
       }
     }
   }
+}
+
+template <bool FP8Q, int NB, bool QLDS>
+__device__ __forceinline__ void process_block(const RawBlock& cur, int kb, const QOperand<NB>& q, const uint8_t* qlds,
+                                              RowState<NB>& st, const int* lim, int lim_min, float c2, int g4) {
+  const int lane = threadIdx.x & 63;
+  // keep the LDS query reads inside the loop (hoisted, they would occupy the
+  // registers this form saves)
+  if (QLDS) asm volatile("" ::: "memory");
+  // ---- S = K Q^T (keys on M) -----------------------------------------------
+  f32x4 sacc[NB][2];
+  for (int nb = 0; nb < NB; ++nb)
+    for (int t = 0; t < 2; ++t) sacc[nb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < 2; ++t) {
+    for (int s = 0; s < 4; ++s) {
+      const uint2 kraw = half_of(cur.k[t][s >> 1], s & 1);
+      if (FP8Q) {
+        const long a = as_long(kraw);
+        for (int nb = 0; nb < NB; ++nb) {
+          const long b = QLDS ? *reinterpret_cast<const long*>(qlds + ((4 * nb + s) * 64 + lane) * 8) : q.q8[nb][s];
+          sacc[nb][t] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, sacc[nb][t], 0, 0, 0);
+        }
+      } else {
+        const bf16x8 a = e4m3x8_to_bf16(kraw);
+        for (int nb = 0; nb < NB; ++nb) {
+          const bf16x8 b =
+              QLDS ? *reinterpret_cast<const bf16x8*>(qlds + ((4 * nb + s) * 64 + lane) * 16) : q.qb[nb][s];
+          sacc[nb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, sacc[nb][t], 0, 0, 0);
+        }
+      }
+    }
+  }
+  softmax_pv<FP8Q, NB>(sacc, cur.v, kb, st, lim, lim_min, c2, g4);
+}
+
+// One 32-key block of packed fp4 K/V with an e4m3 query: S = K Q^T on
+// v_mfma_scale_f32_16x16x128_f8f6f4 (A = 16 keys x 128 head-dim fp4 codes,
+// B = the e4m3 query rows, block scales 1.0: one instruction per 16 keys),
+// then V converted to e4m3 and the fp8 softmax / PV.
+template <int NB, bool QLDS>
+__device__ __forceinline__ void process_block_fp4(const RawBlock4& cur, int kb, const QOperand<NB>& q,
+                                                  const uint8_t* qlds, RowState<NB>& st, const int* lim, int lim_min,
+                                                  float c2, int g4) {
+  const int lane = threadIdx.x & 63;
+  if (QLDS) asm volatile("" ::: "memory");
+  f32x4 sacc[NB][2];
+  for (int t = 0; t < 2; ++t) {
+    const i32x8 a = {(int)cur.k[t].x, (int)cur.k[t].y, (int)cur.k[t].z, (int)cur.k[t].w, 0, 0, 0, 0};
+    for (int nb = 0; nb < NB; ++nb) {
+      long qv[4];
+      for (int s = 0; s < 4; ++s)
+        qv[s] = QLDS ? *reinterpret_cast<const long*>(qlds + ((4 * nb + s) * 64 + lane) * 8) : q.q8[nb][s];
+      const i32x8 b = {(int)qv[0], (int)(qv[0] >> 32), (int)qv[1], (int)(qv[1] >> 32),
+                       (int)qv[2], (int)(qv[2] >> 32), (int)qv[3], (int)(qv[3] >> 32)};
+      // A format 4 = fp4 e2m1, B format 0 = fp8 e4m3; E8M0 scales 127 = 2^0
+      sacc[nb][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, f32x4{0.f, 0.f, 0.f, 0.f}, 4, 0, 0,
+                                                                      127, 0, 127);
+    }
+  }
+  uint2 v8[8];
+  for (int j = 0; j < 8; ++j) v8[j] = e2m1x8_to_e4m3(cur.v[j]);
+  softmax_pv<true, NB>(sacc, v8, kb, st, lim, lim_min, c2, g4);
 }
 
 // Epilogue of one work item for kv head g of sequence b: a sequence with one
@@ -542,9 +649,15 @@ __device__ __forceinline__ void keep_pace(int* progress, int wave, int done, int
 
 // One work item (a chunk of 128-key tiles of one sequence) for kv head g:
 // the one-item-per-workgroup plan.
-template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES, int HW>
+// KVF: 0 = e4m3 K/V, 2 = packed fp4 (e2m1) K/V (e4m3 query only). The page
+// pairs of a fetch are loaded LA fetches ahead: two for the e4m3 ring, one
+// fewer than the ring depth for the deeper fp4 ring (a pair loaded sooner
+// would make its wait cover KV loads still in the ring).
+template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES, int HW, int KVF = 0>
 __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, int lane, int g, int* progress,
                                                 int& round_base) {
+  static_assert(KVF == 0 || (KVF == 2 && FP8Q), "fp4 K/V needs the e4m3 query");
+  constexpr int LA = KVF == 2 ? STAGES - 1 : 2;
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
 
@@ -566,8 +679,8 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
     return bt[max(min(kb + 16 * (lane & 1), plan_last), 0) >> p.page_shift];
   };
   int pv[STAGES];
-  pv[0] = plan_pair(k_begin);
-  pv[1 % STAGES] = plan_pair(k_begin + kBlockKeys);
+#pragma unroll
+  for (int u = 0; u < LA; ++u) pv[u % STAGES] = plan_pair(k_begin + kBlockKeys * u);
   const int ns = p.n_splits[b];
   const int slot = w.w;
   int L = p.seq_lens[b];
@@ -616,16 +729,25 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
     // constants of the unrolled stage loop.
     // the early pairs are right unless the length ends the chunk before the
     // last key they cover
-    if (last_key < plan_last && last_key < k_begin + kBlockKeys + 16) {
-      pv[0] = page_pair(k_begin);
-      pv[1 % STAGES] = page_pair(k_begin + kBlockKeys);
+    if (last_key < plan_last && last_key < k_begin + kBlockKeys * (LA - 1) + 16) {
+#pragma unroll
+      for (int u = 0; u < LA; ++u) pv[u % STAGES] = page_pair(k_begin + kBlockKeys * u);
     }
-    const LaneOffsets lo = lane_offsets(p, r16, g4);
-    auto fetch = [&](RawBlock& r, int kb, const int slot) {
+    using Raw = typename std::conditional<KVF == 2, RawBlock4, RawBlock>::type;
+    const auto lo = [&] {
+      if constexpr (KVF == 2)
+        return lane_offsets4(p, r16, g4);
+      else
+        return lane_offsets(p, r16, g4);
+    }();
+    auto fetch = [&](Raw& r, int kb, const int slot) {
       const int pg0 = clamp_page(p, __builtin_amdgcn_readlane(pv[slot], 0));
       const int pg1 = clamp_page(p, __builtin_amdgcn_readlane(pv[slot], 1));
-      r = load_block(p, g, kb, pg0, pg1, last_key, pmask, lo);
-      pv[(slot + 2) % STAGES] = page_pair(kb + 2 * kBlockKeys);
+      if constexpr (KVF == 2)
+        r = load_block4(p, g, kb, pg0, pg1, last_key, pmask, lo);
+      else
+        r = load_block(p, g, kb, pg0, pg1, last_key, pmask, lo);
+      pv[(slot + LA) % STAGES] = page_pair(kb + LA * kBlockKeys);
     };
 
     // Ring of STAGES register buffers: while block i is processed, blocks
@@ -634,9 +756,16 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
     // entry and back edge see the same loads in flight. Blocks past the
     // chunk (at most STAGES - 1 per work item) re-read its last row and are
     // masked out entirely (P = 0 on finite data): they change nothing.
-    RawBlock ring[STAGES];
+    // The prologue's fetches stay in issue order (the scheduler would
+    // otherwise hoist the later K loads past the page-pair loads, and the
+    // wait at the loop header, shared by entry and back edge, would drain
+    // the ring on every pass of the loop).
+    Raw ring[STAGES];
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) fetch(ring[s], k_begin + kBlockKeys * s, s);
+    for (int s = 0; s < STAGES - 1; ++s) {
+      fetch(ring[s], k_begin + kBlockKeys * s, s);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     const int rounds = (k_end - k_begin + kBlockKeys * STAGES - 1) / (kBlockKeys * STAGES);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     for (int r = 0; r < rounds; ++r) {
@@ -645,7 +774,10 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
       for (int s = 0; s < STAGES; ++s) {
         const int kb = kb0 + kBlockKeys * s;
         fetch(ring[(s + STAGES - 1) % STAGES], kb + kBlockKeys * (STAGES - 1), (s + STAGES - 1) % STAGES);
-        process_block<FP8Q, NB, kQLds>(ring[s], kb, q, qlds, st, lim, lim_min, c2, g4);
+        if constexpr (KVF == 2)
+          process_block_fp4<NB, kQLds>(ring[s], kb, q, qlds, st, lim, lim_min, c2, g4);
+        else
+          process_block<FP8Q, NB, kQLds>(ring[s], kb, q, qlds, st, lim, lim_min, c2, g4);
       }
       if (HW == 8) keep_pace(progress, wave, round_base + r, lane);
     }
@@ -1061,7 +1193,7 @@ __device__ __forceinline__ void gqa_decode_bin_then_queue(const GqaParams& p, in
 // parking values in AGPRs when the workgroup would allow one wave per SIMD:
 // one row block fits as is, two row blocks of the one-item form fit with the
 // query in LDS. The streaming form of two row blocks gets the whole file.
-template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES, int HW, bool STREAM>
+template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES, int HW, bool STREAM, int KVF = 0>
 __global__ __launch_bounds__(64 * HW) __attribute__((amdgpu_waves_per_eu(NB == 1 || !STREAM ? 2 : 1)))
 void gqa_decode_kernel(GqaParams p) {
   const int lane = threadIdx.x & 63;
@@ -1071,6 +1203,12 @@ void gqa_decode_kernel(GqaParams p) {
     __syncthreads();
   }
   const int g = __builtin_amdgcn_readfirstlane(blockIdx.y * HW + (threadIdx.x >> 6));  // wave-uniform
+  if constexpr (KVF != 0) {  // packed narrow K/V: the one-item form
+    int round_base = 0;
+    if (g < p.h_k)
+      gqa_decode_item<FP8Q, NB, CAUSAL_TAIL, STAGES, HW, KVF>(p, blockIdx.x, lane, g, progress, round_base);
+    return;
+  }
   if (STREAM) {
     if (g < p.h_k) gqa_decode_stream<FP8Q, NB, CAUSAL_TAIL, STAGES, HW>(p, lane, g, progress);
     return;
@@ -1105,6 +1243,28 @@ const void* kernel_ptr(bool stream) {
                 : reinterpret_cast<const void*>(&gqa_decode_kernel<FP8Q, NB, CT, ring_stages<NB, false>(), HW, false>);
 }
 
+// fp4 K/V: one-item form, a ring of five blocks (one row block) or three
+// (two row blocks): 4 KB blocks, so a deeper ring keeps the bytes in flight.
+template <int NB>
+constexpr int fp4_stages() {
+  return NB == 1 ? 5 : 3;
+}
+
+template <int NB, bool CT, int HW>
+const void* fp4_ptr() {
+  return reinterpret_cast<const void*>(&gqa_decode_kernel<true, NB, CT, fp4_stages<NB>(), HW, false, 2>);
+}
+
+template <int NB, bool CT>
+const void* select_fp4_heads(const GqaVariant& v) {
+  switch (v.heads_per_wg) {
+    case 1: return fp4_ptr<NB, CT, 1>();
+    case 2: return fp4_ptr<NB, CT, 2>();
+    case 4: return fp4_ptr<NB, CT, 4>();
+    default: return fp4_ptr<NB, CT, NB == 1 ? 8 : 4>();
+  }
+}
+
 template <bool FP8Q, int NB, bool CT>
 const void* select_heads(const GqaVariant& v) {
   switch (v.heads_per_wg) {
@@ -1121,6 +1281,10 @@ const void* select_tail(const GqaVariant& v) {
 }
 
 const void* select_kernel(const GqaVariant& v) {
+  if (v.kv_fp4) {
+    if (v.n_blocks == 1) return v.causal_tail ? select_fp4_heads<1, true>(v) : select_fp4_heads<1, false>(v);
+    return v.causal_tail ? select_fp4_heads<2, true>(v) : select_fp4_heads<2, false>(v);
+  }
   if (v.fp8_q) return v.n_blocks == 1 ? select_tail<true, 1>(v) : select_tail<true, 2>(v);
   return v.n_blocks == 1 ? select_tail<false, 1>(v) : select_tail<false, 2>(v);
 }
@@ -1136,11 +1300,12 @@ int log2_exact(int x) {
 GqaVariant gqa_variant(const pkv_decode_args& a) {
   GqaVariant v;
   v.fp8_q = a.q_format == PKV_Q_E4M3;
+  v.kv_fp4 = a.kv_format == PKV_KV_E2M1;
   const int rows = a.q_len * (a.h_q / a.h_k);
   v.n_blocks = rows <= 16 ? 1 : 2;
   v.causal_tail = a.causal && a.q_len > 1;
   v.stream = a.bin_offsets != nullptr && a.queue == nullptr;
-  v.stages = (v.n_blocks == 2 && !v.stream) ? 2 : 3;
+  v.stages = v.kv_fp4 ? (v.n_blocks == 1 ? 5 : 3) : (v.n_blocks == 2 && !v.stream) ? 2 : 3;
   // kv heads per workgroup: the largest power of two dividing h_k, up to 8
   // (4 for two row blocks: eight waves of 32 rows per workgroup measured
   // slower on the speculative-verify workload, 100 vs 95 us)

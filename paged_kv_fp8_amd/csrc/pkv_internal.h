@@ -22,6 +22,7 @@ struct GqaVariant {
   int stages;       // register ring depth of the KV stream (blocks of 32 keys)
   int heads_per_wg; // kv heads (one wave each) per workgroup
   bool stream;      // balanced plan: each workgroup streams the items of its bin
+  bool kv_fp4;      // packed fp4 (e2m1) K/V: one-item form only
 };
 GqaVariant gqa_variant(const pkv_decode_args& a);
 int gqa_rows_per_tile(const GqaVariant& v);

@@ -13,7 +13,7 @@ import numpy as np
 import torch
 
 from . import native
-from .native import PKV_KV_E4M3, PKV_KV_MLA, PKV_Q_BF16, PKV_Q_E4M3
+from .native import PKV_KV_E2M1, PKV_KV_E4M3, PKV_KV_MLA, PKV_Q_BF16, PKV_Q_E4M3
 
 
 def _ptr(t):
@@ -50,7 +50,7 @@ class PagedDecode:
                  q_descale=None, k_descale=None, v_descale=None, latent=None, rope=None, blk_scale=None,
                  num_pages=None, causal=True, o_scale=1.0, max_splits=16, force_splits=0, min_chunk_tiles=1,
                  pad_to=0, wg_per_cu=None, plan_seq_lens=None, fused_merge=False, plan="wave", pieces_per_bin=3,
-                 dyn_percent=10, plan_cu_count=None):
+                 dyn_percent=10, plan_cu_count=None, kv_format="e4m3"):
         mla = latent is not None
         a = native.DecodeArgs()
         num_seqs = seq_lens.shape[0]
@@ -58,14 +58,15 @@ class PagedDecode:
         if mla:
             h_k, d_qk, d_v, ps = 1, q.shape[2], 512, latent.shape[1]
             num_pages = num_pages or latent.shape[0]
-        else:
-            h_k, d_qk, d_v, ps = k_cache.shape[2], q.shape[2], v_cache.shape[3], k_cache.shape[1]
+        else:  # e4m3 codes, or packed fp4 rows of d/2 bytes
+            per_byte = 2 if kv_format == "e2m1" else 1
+            h_k, d_qk, d_v, ps = k_cache.shape[2], q.shape[2], v_cache.shape[3] * per_byte, k_cache.shape[1]
             num_pages = num_pages or k_cache.shape[0]
         a.num_seqs, a.q_len, a.h_q, a.h_k, a.d_qk, a.d_v = num_seqs, q_len, h_q, h_k, d_qk, d_v
         a.page_size, a.num_pages, a.max_blocks = ps, num_pages, block_table.shape[1]
         a.causal = 1 if causal else 0
         a.q_format = PKV_Q_BF16 if q.dtype == torch.bfloat16 else PKV_Q_E4M3
-        a.kv_format = PKV_KV_MLA if mla else PKV_KV_E4M3
+        a.kv_format = PKV_KV_MLA if mla else (PKV_KV_E2M1 if kv_format == "e2m1" else PKV_KV_E4M3)
         a.softmax_scale, a.o_scale = float(softmax_scale), float(o_scale)
         a.q, a.q_tok_stride, a.q_head_stride = _ptr(q), q.stride(0), q.stride(1)
         if mla:
@@ -182,5 +183,6 @@ def for_batch(batch, *, o=None, lse=None, **kw):
     if w.kv_format == "mla":
         return PagedDecode(latent=batch.mla_latent, rope=batch.mla_rope, blk_scale=batch.mla_scales, **common, **kw)
     q_descale = batch.q_descale if w.q_format == "e4m3" else None
+    kw.setdefault("kv_format", w.kv_format)
     return PagedDecode(k_cache=batch.k_cache, v_cache=batch.v_cache, q_descale=q_descale, k_descale=batch.k_descale,
                        v_descale=batch.v_descale, **common, **kw)

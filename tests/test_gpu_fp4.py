@@ -1,0 +1,111 @@
+"""GPU parity of the packed fp4 (e2m1) K/V decode against the fp64 oracle,
+through the C ABI: the page's narrow KV format with an e4m3 query, on small
+variants of the fp4 workload (one and two 16-row blocks, causal tail and
+block mode, split and unsplit sequences, ragged tails), the full workload on
+sampled sequences, the edge lengths, and bit-identical repeats and graph
+replays. Bars as for the e4m3 cache (e4m3 P): max|dO| <= 1e-2 * max|V| at the
+workload's lengths, and the derived short-sequence bound 0.07 * max|V| for
+the edge lengths (L < 1024)."""
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import O_TOL, assert_matches, gpu_rows, max_abs_v, nan_fill_, oracle_for
+from paged_kv_fp8_amd.workloads import make_batch, workload
+
+pytestmark = pytest.mark.gpu
+
+FP8_SHORT_TOL = 0.07
+EDGE_LENS = [0, 1, 2, 3, 15, 16, 17, 31, 32, 33, 127, 128, 129, 255, 256, 257, 1000, 1025]
+
+
+def _decode():
+    from paged_kv_fp8_amd import decode  # loads the HIP library; fails loudly if missing
+    return decode
+
+
+def run(batch, **kw):
+    dec = _decode().for_batch(batch, **kw)
+    if dec.has_splits:
+        nan_fill_(dec.workspace)
+    dec.run()
+    torch.cuda.synchronize()
+    return dec
+
+
+def check(batch, dec, seqs=None, o_tol=O_TOL, what=""):
+    spec = batch.spec
+    nb = batch.to_numpy()
+    o_ref, lse_ref = oracle_for(nb, spec, seqs)
+    o_g, lse_g = gpu_rows(dec.o, dec.lse, spec, seqs)
+    return assert_matches(o_g, lse_g, o_ref, lse_ref, max_abs_v(nb, spec, seqs), o_tol=o_tol, what=what)
+
+
+SMALL = {
+    "one_block": dict(num_seqs=6, seq_len_dist=("mix", 0.34, (3000, 9000), (1024, 2000))),
+    "two_blocks_causal": dict(num_seqs=5, q_len=2, seq_len_dist=("uniform", 1024, 5000)),
+    "two_blocks_block_mode": dict(num_seqs=5, q_len=2, causal=False, seq_len_dist=("uniform", 1024, 5000)),
+    "ps16_hk8": dict(num_seqs=4, h_q=64, h_k=8, page_size=16, seq_len_dist=("uniform", 1024, 3000)),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_fp4_small_every_output(name):
+    w = workload(6, **SMALL[name])
+    batch = make_batch(w, device="cuda")
+    dec = run(batch)
+    err_o, err_l, _ = check(batch, dec, what=name)
+    print(f"fp4 {name}: kernel={dec.kernel_name} splits={dec.plan_info.max_n_splits} "
+          f"max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
+
+
+def test_fp4_full_workload_sampled():
+    w = workload(6)
+    batch = make_batch(w, device="cuda")
+    dec = run(batch)
+    lens = batch.seq_lens.cpu().numpy()
+    order = np.argsort(lens)
+    rng = np.random.default_rng(61)
+    seqs = sorted({int(order[0]), int(order[-1])} | {int(x) for x in rng.choice(len(lens), 6, replace=False)})
+    err_o, err_l, _ = check(batch, dec, seqs=seqs, what="fp4 full")
+    print(f"fp4 full: work={dec.plan_info.num_real} max_splits_used={dec.plan_info.max_n_splits} "
+          f"max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
+
+
+@pytest.mark.parametrize("q_len,causal,ps,force", [(1, True, 128, 0), (2, True, 16, 3), (2, False, 64, 0),
+                                                   (1, True, 32, 5)])
+def test_fp4_edge_lengths(q_len, causal, ps, force):
+    w = workload(6, num_seqs=len(EDGE_LENS), q_len=q_len, page_size=ps, causal=causal,
+                 seq_len_dist=("fixed", EDGE_LENS), max_splits=8)
+    batch = make_batch(w, device="cuda")
+    dec = run(batch, force_splits=force)
+    _, _, empty = check(batch, dec, o_tol=FP8_SHORT_TOL, what=f"fp4 edge q_len={q_len} ps={ps}")
+    o = dec.o.float().cpu().numpy()
+    assert np.all(o[0:q_len] == 0.0)  # L = 0: O = 0 exactly (LSE = -inf is checked above)
+
+
+def test_fp4_bitwise_repeats_graph_replay_and_fused_merge():
+    w = workload(6, num_seqs=12, seq_len_dist=("mix", 0.25, (6000, 20000), (1024, 4096)))
+    batch = make_batch(w, device="cuda")
+    dec = run(batch)
+    assert dec.has_splits
+    ref_o, ref_l = dec.o.clone(), dec.lse.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dec.run()
+    for rep in range(3):
+        dec.o.zero_()
+        dec.lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dec.o.view(torch.int16), ref_o.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(dec.lse.view(torch.int32), ref_l.view(torch.int32)), f"replay {rep}"
+    fused = _decode().for_batch(batch, fused_merge=True)
+    for rep in range(2):
+        nan_fill_(fused.workspace[: fused.workspace.numel() // 2])
+        fused.run()
+        torch.cuda.synchronize()
+        assert torch.equal(fused.o.view(torch.int16), ref_o.view(torch.int16)), f"fused {rep}"
+        assert int(fused.merge_counters.abs().sum()) == 0
