@@ -347,18 +347,15 @@ __device__ __forceinline__ RawBlock4 load_block4(const GqaParams& p, int g, int 
 }
 
 // Eight e2m1 codes (element 2i in the low nibble of byte i) -> their e4m3
-// bytes, exact (every e2m1 value is an e4m3 value): the magnitude (3 bits)
-// picks one of 8 bytes with v_perm_b32 (0, 0.5, 1, 1.5, 2, 3, 4, 6 as
-// 0x00 0x30 0x38 0x3C 0x40 0x44 0x48 0x4C), the sign moves from bit 3 to 7.
-__device__ __forceinline__ uint32_t e2m1x4_to_e4m3(uint32_t spread) {
-  // spread = [b, b, c, c] -> nibbles [b & 15, b >> 4, c & 15, c >> 4], one per byte
-  const uint32_t n = (spread & 0x000F000Fu) | ((spread >> 4) & 0x0F000F00u);
-  const uint32_t mag = __builtin_amdgcn_perm(0x4C484440u, 0x3C383000u, n & 0x07070707u);
-  return mag | ((n & 0x08080808u) << 4);
-}
+// bytes, exact (every e2m1 value is an e4m3 value), split by parity:
+// .x = elements 0, 2, 4, 6 and .y = elements 1, 3, 5, 7. The magnitude (3
+// bits) picks one of 8 bytes with v_perm_b32 (0, 0.5, 1, 1.5, 2, 3, 4, 6 as
+// 0x00 0x30 0x38 0x3C 0x40 0x44 0x48 0x4C); the sign (bit 3 of the code) goes
+// to bit 7, where a high nibble already has it.
 __device__ __forceinline__ uint2 e2m1x8_to_e4m3(uint32_t x) {
-  return uint2{e2m1x4_to_e4m3(__builtin_amdgcn_perm(x, x, 0x01010000u)),
-               e2m1x4_to_e4m3(__builtin_amdgcn_perm(x, x, 0x03030202u))};
+  const uint32_t lo = __builtin_amdgcn_perm(0x4C484440u, 0x3C383000u, x & 0x07070707u);
+  const uint32_t hi = __builtin_amdgcn_perm(0x4C484440u, 0x3C383000u, (x >> 4) & 0x07070707u);
+  return uint2{lo | ((x << 4) & 0x80808080u), hi | (x & 0x80808080u)};
 }
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -383,7 +380,9 @@ __device__ __forceinline__ void park_q(const QOperand<NB>& q, uint8_t* qlds, int
 // block's V as e4m3 (fp8 path) codes or as the bytes the bf16 path converts
 // exactly: vraw[j] holds key kb + 16 (j >> 2) + 4 g4 + (j & 3), d_v bytes
 // 8 r16 .. 8 r16 + 7 of this lane.
-template <bool FP8Q, int NB>
+// With V_BY_PARITY (converted fp4 codes) .x holds d_v bytes 8 r16 + 0, 2, 4,
+// 6 and .y bytes 8 r16 + 1, 3, 5, 7, and the Oᵀ tiles are indexed to match.
+template <bool FP8Q, int NB, bool V_BY_PARITY = false>
 __device__ __forceinline__ void softmax_pv(f32x4 (&sacc)[NB][2], const uint2 (&vraw)[8], int kb, RowState<NB>& st,
                                            const int* lim, int lim_min, float c2, int g4) {
   // ---- online softmax (per query row = lane column r16) --------------------
@@ -457,7 +456,7 @@ __device__ __forceinline__ void softmax_pv(f32x4 (&sacc)[NB][2], const uint2 (&v
       }
       for (int e = 0; e < 4; ++e) {
         const long a = as_long(uint2{col[0][e], col[1][e]});
-        const int mt = 4 * w2 + e;
+        const int mt = V_BY_PARITY ? 2 * e + w2 : 4 * w2 + e;
         for (int nb = 0; nb < NB; ++nb)
           st.oacc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, p8[nb], st.oacc[nb][mt], 0, 0, 0);
       }
@@ -546,7 +545,7 @@ __device__ __forceinline__ void process_block_fp4(const RawBlock4& cur, int kb, 
   }
   uint2 v8[8];
   for (int j = 0; j < 8; ++j) v8[j] = e2m1x8_to_e4m3(cur.v[j]);
-  softmax_pv<true, NB>(sacc, v8, kb, st, lim, lim_min, c2, g4);
+  softmax_pv<true, NB, true>(sacc, v8, kb, st, lim, lim_min, c2, g4);
 }
 
 // Epilogue of one work item for kv head g of sequence b: a sequence with one
@@ -1245,9 +1244,12 @@ const void* kernel_ptr(bool stream) {
 
 // fp4 K/V: one-item form, a ring of five blocks (one row block) or three
 // (two row blocks): 4 KB blocks, so a deeper ring keeps the bytes in flight.
+#ifndef PKV_FP4_STAGES
+#define PKV_FP4_STAGES 5
+#endif
 template <int NB>
 constexpr int fp4_stages() {
-  return NB == 1 ? 5 : 3;
+  return NB == 1 ? PKV_FP4_STAGES : 3;
 }
 
 template <int NB, bool CT, int HW>
@@ -1305,7 +1307,7 @@ GqaVariant gqa_variant(const pkv_decode_args& a) {
   v.n_blocks = rows <= 16 ? 1 : 2;
   v.causal_tail = a.causal && a.q_len > 1;
   v.stream = a.bin_offsets != nullptr && a.queue == nullptr;
-  v.stages = v.kv_fp4 ? (v.n_blocks == 1 ? 5 : 3) : (v.n_blocks == 2 && !v.stream) ? 2 : 3;
+  v.stages = v.kv_fp4 ? (v.n_blocks == 1 ? fp4_stages<1>() : fp4_stages<2>()) : (v.n_blocks == 2 && !v.stream) ? 2 : 3;
   // kv heads per workgroup: the largest power of two dividing h_k, up to 8
   // (4 for two row blocks: eight waves of 32 rows per workgroup measured
   // slower on the speculative-verify workload, 100 vs 95 us)
