@@ -47,7 +47,7 @@ variant against the generic core on the explicitly assembled 576-wide keys.
 
 import numpy as np
 
-from .formats import KV_DECODERS, decode_bf16, decode_e4m3
+from .formats import KV_DECODERS, decode_bf16, decode_e4m3, kv_row_elems
 
 
 def _decode_q(q):
@@ -108,8 +108,8 @@ def attend(qrows, K, V, limits, softmax_scale, o_scale):
 def decode_attention(q, k_cache, v_cache, block_table, seq_lens, q_descale, k_descale, v_descale,
                      *, q_len, h_k, softmax_scale, o_scale=1.0, causal=True, kv_format="e4m3"):
     """Decode attention of every sequence, KV head and packed row (steps 1-6).
-    kv_format names the K/V code format (step 3's dec): "e4m3", or "e2m1"
-    (packed fp4 rows, [T5] narrow KV formats)."""
+    kv_format names the K/V code format (step 3's dec): "e4m3", or one of
+    the packed narrow formats of [T5] ("e2m1" fp4, "e2m3" / "e3m2" fp6)."""
     dec_kv = KV_DECODERS[kv_format]
     q = np.asarray(q)
     seq_lens = np.asarray(seq_lens)
@@ -123,7 +123,7 @@ def decode_attention(q, k_cache, v_cache, block_table, seq_lens, q_descale, k_de
     qd = _per_seq_head(q_descale, num_seqs, h_k) if q.dtype == np.uint8 else np.ones((num_seqs, h_k))
     kd = _per_seq_head(k_descale, num_seqs, h_k)
     vd = _per_seq_head(v_descale, num_seqs, h_k)
-    d_v = v_cache.shape[-1] * (2 if kv_format == "e2m1" else 1)
+    d_v = kv_row_elems(v_cache.shape[-1], kv_format)
     o = np.zeros((num_seqs * q_len, h_q, d_v))
     lse = np.full((num_seqs, h_k, n_rows), -np.inf)
     for b in range(num_seqs):

@@ -60,6 +60,33 @@ def fp4_row_to_floats(row):
     return out
 
 
+def fp6_code_to_float(code, kv_fmt):
+    """One 6-bit code from its bit fields: e2m3 = sign | 2-bit exponent (bias 1)
+    | 3-bit mantissa; e3m2 = sign | 3-bit exponent (bias 3) | 2-bit mantissa."""
+    code = int(code)
+    s = -1.0 if code & 32 else 1.0
+    if kv_fmt == "e2m3":
+        e, m = (code >> 3) & 3, code & 7
+        return s * (math.ldexp(m, -3) if e == 0 else math.ldexp(8 + m, e - 4))
+    e, m = (code >> 2) & 7, code & 3
+    return s * (math.ldexp(m, -4) if e == 0 else math.ldexp(4 + m, e - 5))
+
+
+def fp6_row_to_floats(row, kv_fmt):
+    """A packed fp6 row (3d/4 bytes) -> d floats: the whole row read as one
+    little-endian integer, element i = bits 6i .. 6i+5."""
+    n = int.from_bytes(bytes(int(x) for x in row), "little")
+    return [fp6_code_to_float((n >> (6 * i)) & 63, kv_fmt) for i in range(len(row) * 8 // 6)]
+
+
+def _row_floats(row, kv_fmt):
+    if kv_fmt == "e2m1":
+        return fp4_row_to_floats(row)
+    if kv_fmt in ("e2m3", "e3m2"):
+        return fp6_row_to_floats(row, kv_fmt)
+    return [e4m3_bits_to_float(x) for x in row]
+
+
 def _dec(x, fmt):
     return e4m3_bits_to_float(x) if fmt == "e4m3" else bf16_bits_to_float(x)
 
@@ -72,7 +99,7 @@ def brute_decode_attention(q, q_fmt, k_cache, v_cache, block_table, seq_lens, qd
     num_seqs = len(seq_lens)
     h_q = len(q[0])
     d = len(q[0][0])
-    d_v = len(v_cache[0][0][0]) * (2 if kv_fmt == "e2m1" else 1)
+    d_v = len(v_cache[0][0][0]) * 8 // {"e2m1": 4, "e2m3": 6, "e3m2": 6}.get(kv_fmt, 8)
     ps = len(k_cache[0])
     h_r = h_q // h_k
     o = [[[0.0] * d_v for _ in range(h_q)] for _ in range(num_seqs * q_len)]
@@ -92,12 +119,8 @@ def brute_decode_attention(q, q_fmt, k_cache, v_cache, block_table, seq_lens, qd
                     for j in range(last + 1):
                         page = int(block_table[b][j // ps])
                         row = j % ps
-                        if kv_fmt == "e2m1":
-                            kv = [x * float(kd[b][g]) for x in fp4_row_to_floats(k_cache[page][row][g])]
-                            vv = [x * float(vd[b][g]) for x in fp4_row_to_floats(v_cache[page][row][g])]
-                        else:
-                            kv = [e4m3_bits_to_float(k_cache[page][row][g][i]) * float(kd[b][g]) for i in range(d)]
-                            vv = [e4m3_bits_to_float(v_cache[page][row][g][i]) * float(vd[b][g]) for i in range(d_v)]
+                        kv = [x * float(kd[b][g]) for x in _row_floats(k_cache[page][row][g], kv_fmt)]
+                        vv = [x * float(vd[b][g]) for x in _row_floats(v_cache[page][row][g], kv_fmt)]
                         scores.append(softmax_scale * math.fsum(a * c for a, c in zip(qv, kv)))
                         values.append(vv)
                     top = max(scores)

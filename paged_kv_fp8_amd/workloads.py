@@ -35,7 +35,11 @@ Data recipe (following the t5_decode page's harness, ``run``):
     (sequence, kv head) with descale = max(amax, 1e-6) / 6 and the code of
     the nearest e2m1 magnitude (ties to the smaller, as the page's
     ``minifloat_quantize``), packed two per byte, element 2i in the low
-    nibble; unused pages and tail rows hold 0x77 (there is no fp4 NaN).
+    nibble; unused pages and tail rows hold 0x77 (there is no fp4 NaN);
+  * packed e2m3 / e3m2 (fp6) K/V, the same list: descale = max(amax, 1e-6) /
+    7.5 (e2m3) or / 28 (e3m2), nearest magnitude with ties to the smaller,
+    four codes per three bytes (element i at bits 6i .. 6i+5 of the row);
+    unused pages and tail rows hold the largest positive code 0x1F.
 Random tensors come from a torch generator on the target device, seeded per
 workload, so a GPU batch is generated on the GPU.
 """
@@ -50,6 +54,26 @@ E4M3_MAX = 448.0
 E4M3_NAN = 0x7F
 E2M1_MAGNITUDES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)  # codes 0..7
 E2M1_FILL = 0x77
+
+
+def _minifloat_magnitudes(exp_bits, man_bits):
+    """Non-negative values of a sign-magnitude minifloat with no inf/NaN
+    (OCP MX style), in code order: bias 2^(E-1) - 1, exponent 0 subnormal."""
+    bias = (1 << (exp_bits - 1)) - 1
+    out = []
+    for code in range(1 << (exp_bits + man_bits)):
+        e, m = code >> man_bits, code & ((1 << man_bits) - 1)
+        frac = m / (1 << man_bits)
+        out.append(math.ldexp(frac, 1 - bias) if e == 0 else math.ldexp(1.0 + frac, e - bias))
+    return tuple(out)
+
+
+# magnitudes in code order, sign bit, bits per code, fill byte pattern of a row
+NARROW_FORMATS = {
+    "e2m1": (E2M1_MAGNITUDES, 0x8, 4, (E2M1_FILL,)),
+    "e2m3": (_minifloat_magnitudes(2, 3), 0x20, 6, (0xDF, 0xF7, 0x7D)),  # 0x1F in all four slots
+    "e3m2": (_minifloat_magnitudes(3, 2), 0x20, 6, (0xDF, 0xF7, 0x7D)),
+}
 MLA_LATENT, MLA_ROPE, MLA_BLOCK = 512, 64, 128
 MLA_RECORD_BYTES = MLA_LATENT + 2 * MLA_ROPE + 4 * (MLA_LATENT // MLA_BLOCK)  # 656
 
@@ -67,7 +91,7 @@ class Workload:
     seq_len_dist: tuple  # ("fixed", [..]) | ("uniform", lo, hi) | ("lognormal", median, sigma, lo, hi) | ("mix", ...)
     max_splits: int = 16
     q_format: str = "bf16"  # "bf16" | "e4m3"
-    kv_format: str = "e4m3"  # "e4m3" | "mla" | "e2m1" (packed fp4)
+    kv_format: str = "e4m3"  # "e4m3" | "mla" | "e2m1" (packed fp4) | "e2m3" / "e3m2" (packed fp6)
     causal: bool = True
     seed: int = 1111
     num_pages: int = 0  # 0: used + max(4, used // 4)
@@ -104,6 +128,13 @@ WORKLOADS = {
     # the fully-fp8 workload with packed fp4 (e2m1) K/V: the page's narrow KV formats
     6: Workload("fp4kv_b128_hq64_hk4_d128_ps128_mix1k-4k_32k-64k", 128, 1, 64, 4, 128, 128, 128,
                 ("mix", 0.1, (32768, 65536), (1024, 4096)), max_splits=64, q_format="e4m3", kv_format="e2m1",
+                seed=1115),
+    # ... and with packed fp6 K/V (e2m3, the page's harness default narrow format; e3m2)
+    7: Workload("fp6e2m3kv_b128_hq64_hk4_d128_ps128_mix1k-4k_32k-64k", 128, 1, 64, 4, 128, 128, 128,
+                ("mix", 0.1, (32768, 65536), (1024, 4096)), max_splits=64, q_format="e4m3", kv_format="e2m3",
+                seed=1115),
+    8: Workload("fp6e3m2kv_b128_hq64_hk4_d128_ps128_mix1k-4k_32k-64k", 128, 1, 64, 4, 128, 128, 128,
+                ("mix", 0.1, (32768, 65536), (1024, 4096)), max_splits=64, q_format="e4m3", kv_format="e3m2",
                 seed=1115),
 }
 
@@ -164,8 +195,8 @@ class Batch:
         w = self.spec
         if w.kv_format == "mla":
             return toks * MLA_RECORD_BYTES
-        if w.kv_format == "e2m1":
-            return toks * w.h_k * (w.d_qk + w.d_v) // 2
+        if w.kv_format in NARROW_FORMATS:
+            return toks * w.h_k * (w.d_qk + w.d_v) * NARROW_FORMATS[w.kv_format][2] // 8
         return toks * w.h_k * (w.d_qk + w.d_v)
 
     def to_numpy(self):
@@ -226,21 +257,27 @@ def _quantise_per_seq_head(x, seg, num_seqs):
     return y.to(torch.float8_e4m3fn).view(torch.uint8), desc.contiguous()
 
 
-def _quantise_fp4_per_seq_head(x, seg, num_seqs):
-    """x (tokens, h_k, d) float32 -> (packed codes uint8 (tokens, h_k, d/2), descale (b, h_k))."""
+def _quantise_narrow_per_seq_head(x, seg, num_seqs, kv_format):
+    """x (tokens, h_k, d) float32 -> (packed codes uint8 (tokens, h_k, d*bits/8), descale (b, h_k))."""
+    mags_t, sign_bit, bits, _ = NARROW_FORMATS[kv_format]
     h_k = x.shape[1]
     amax = torch.zeros(num_seqs, h_k, device=x.device)
     amax.scatter_reduce_(0, seg[:, None].expand(-1, h_k), x.abs().amax(dim=-1), "amax")
-    desc = amax.clamp(min=1e-6) / E2M1_MAGNITUDES[-1]
-    y = (x / desc[seg][:, :, None]).clamp(-E2M1_MAGNITUDES[-1], E2M1_MAGNITUDES[-1])
-    mags = torch.tensor(E2M1_MAGNITUDES, device=x.device)
+    desc = amax.clamp(min=1e-6) / mags_t[-1]
+    y = (x / desc[seg][:, :, None]).clamp(-mags_t[-1], mags_t[-1])
+    mags = torch.tensor(mags_t, device=x.device)
     ay = y.abs()
-    hi = torch.bucketize(ay, mags).clamp(max=len(E2M1_MAGNITUDES) - 1)  # first magnitude >= |y|
+    hi = torch.bucketize(ay, mags).clamp(max=len(mags_t) - 1)  # first magnitude >= |y|
     lo = (hi - 1).clamp(min=0)
     code = torch.where((ay - mags[lo]) <= (mags[hi] - ay), lo, hi)
-    code = code | ((y < 0) & (mags[code] > 0)).to(code.dtype) << 3
-    code = code.to(torch.uint8)
-    return (code[..., 0::2] | (code[..., 1::2] << 4)).contiguous(), desc.contiguous()
+    code = code | ((y < 0) & (mags[code] > 0)).to(code.dtype) * sign_bit
+    if bits == 4:
+        packed = code[..., 0::2] | (code[..., 1::2] << 4)
+    else:  # four 6-bit codes -> 24 bits -> 3 bytes, little-endian
+        c = code.view(*code.shape[:-1], code.shape[-1] // 4, 4)
+        w = c[..., 0] | (c[..., 1] << 6) | (c[..., 2] << 12) | (c[..., 3] << 18)
+        packed = torch.stack([w & 0xFF, (w >> 8) & 0xFF, (w >> 16) & 0xFF], dim=-1).flatten(-2)
+    return packed.to(torch.uint8).contiguous(), desc.contiguous()
 
 
 def make_batch(w: Workload, device="cpu", seq_lens=None) -> Batch:
@@ -284,20 +321,25 @@ def make_batch(w: Workload, device="cpu", seq_lens=None) -> Batch:
         return batch
 
     d = w.d_qk
-    fp4 = w.kv_format == "e2m1"
-    row_bytes = d // 2 if fp4 else d
-    fill = E2M1_FILL if fp4 else E4M3_NAN
+    narrow = w.kv_format in NARROW_FORMATS
+    row_bytes = d * NARROW_FORMATS[w.kv_format][2] // 8 if narrow else d
+    fill = NARROW_FORMATS[w.kv_format][3] if narrow else (E4M3_NAN,)
     if w.kv_layout == "nhd":
-        kbuf = torch.full((2, num_pages, ps, h_k, row_bytes), fill, dtype=torch.uint8, device=device)
+        kbuf = torch.empty((2, num_pages, ps, h_k, row_bytes), dtype=torch.uint8, device=device)
         k_view, v_view = kbuf[0], kbuf[1]
     elif w.kv_layout == "hnd":
-        kbuf = torch.full((num_pages, 2, h_k, ps, row_bytes), fill, dtype=torch.uint8, device=device)
+        kbuf = torch.empty((num_pages, 2, h_k, ps, row_bytes), dtype=torch.uint8, device=device)
         k_view, v_view = kbuf[:, 0].transpose(1, 2), kbuf[:, 1].transpose(1, 2)
     else:
         raise ValueError(f"unknown kv_layout {w.kv_layout}")
+    pat = torch.tensor(fill, dtype=torch.uint8, device=device)
+    kbuf.view(-1, len(fill)).copy_(pat.expand(kbuf.numel() // len(fill), -1))
     for view, name in ((k_view, "k"), (v_view, "v")):
         x = torch.randn(n_tok, h_k, d, generator=gen, device=device)
-        codes, desc = (_quantise_fp4_per_seq_head if fp4 else _quantise_per_seq_head)(x, seg, b)
+        if narrow:
+            codes, desc = _quantise_narrow_per_seq_head(x, seg, b, w.kv_format)
+        else:
+            codes, desc = _quantise_per_seq_head(x, seg, b)
         del x
         pages, rows = slot // ps, slot % ps
         view[pages, rows] = codes

@@ -526,3 +526,83 @@ def test_planted_mistakes_are_caught(monkeypatch):
         mod.__dict__["__package__"] = "oracle"
         exec(compile(msrc, "mutant", "exec"), mod.__dict__)
         assert not _pins_pass(mod.decode_attention), f"planted mistake {name!r} survived every pin"
+
+
+def test_fp6_golden_codes():
+    rows = [ln.split() for ln in open(os.path.join(GOLDEN, "fp6_codes.txt")) if ln.strip() and ln[0] != "#"]
+    assert len(rows) == 33
+    tables = {"e2m3": formats.E2M3_TABLE, "e3m2": formats.E3M2_TABLE}
+    for fmt, code, val in rows:
+        got = tables[fmt][int(code, 16)]
+        assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val)), (fmt, code, got, val)
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+def test_fp6_value_set_properties(fmt):
+    t = {"e2m3": formats.E2M3_TABLE, "e3m2": formats.E3M2_TABLE}[fmt]
+    pos = t[:32]
+    assert np.all(np.isfinite(t)) and np.all(np.diff(pos) > 0)  # no inf/NaN, strictly increasing
+    assert np.array_equal(t[32:], -pos)  # sign-magnitude
+    assert pos[-1] == {"e2m3": 7.5, "e3m2": 28.0}[fmt] and pos[1] == {"e2m3": 0.125, "e3m2": 0.0625}[fmt]
+    # every fp6 value is an e4m3 value (torch's float8_e4m3fn cast returns it unchanged)
+    back = torch.from_numpy(t.copy()).to(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(back, t)
+
+
+def test_fp6_packing_golden_and_decode():
+    for ln in open(os.path.join(GOLDEN, "fp6_pack.txt")):
+        if ln.startswith("#") or not ln.strip():
+            continue
+        b, c = ln.split("|")
+        packed = np.array([[int(x, 16) for x in b.split()]], dtype=np.uint8)
+        assert formats.unpack_fp6(packed).tolist() == [[int(x, 16) for x in c.split()]]
+    rng = np.random.default_rng(4)
+    rows = rng.integers(0, 256, size=(6, 12), dtype=np.uint8)
+    for fmt, dec in (("e2m3", formats.decode_e2m3_packed), ("e3m2", formats.decode_e3m2_packed)):
+        ref = [brute.fp6_row_to_floats(r, fmt) for r in rows.tolist()]
+        assert dec(rows).tolist() == ref
+
+
+def fp6_case(rng, **kw):
+    """tiny_case with packed fp6 K/V (random bytes: every code is finite)."""
+    c = tiny_case(rng, **kw)
+    for name in ("k_cache", "v_cache"):
+        shp = c[name].shape
+        c[name] = rng.integers(0, 256, size=shp[:-1] + (shp[-1] * 3 // 4,), dtype=np.uint8)
+    return c
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+@pytest.mark.parametrize("case", range(len(FP4_CASES)))
+def test_fp6_oracle_matches_brute_force(case, fmt):
+    cfg = dict(FP4_CASES[case])
+    causal = cfg.pop("causal")
+    c = fp6_case(np.random.default_rng(950 + case), **cfg)
+    kw = dict(softmax_scale=0.21, o_scale=0.8, causal=causal)
+    o, lse = run_oracle(c, kv_format=fmt, **kw)
+    ob, lb = brute.brute_decode_attention(
+        c["q"].tolist(), "e4m3", c["k_cache"].tolist(), c["v_cache"].tolist(), c["block_table"].tolist(),
+        c["seq_lens"].tolist(), c["q_descale"].tolist(), c["k_descale"].tolist(), c["v_descale"].tolist(),
+        c["q_len"], c["h_k"], kw["softmax_scale"], kw["o_scale"], kw["causal"], kv_fmt=fmt)
+    assert o.shape[-1] == cfg["d"] and np.all(np.isfinite(o))
+    np.testing.assert_allclose(o, np.array(ob), rtol=0, atol=1e-12)
+    fin = np.isfinite(lse)
+    np.testing.assert_array_equal(fin, np.isfinite(np.array(lb)))
+    np.testing.assert_allclose(lse[fin], np.array(lb)[fin], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+def test_fp6_equals_e4m3_on_the_same_values(fmt):
+    c = fp6_case(np.random.default_rng(78), num_seqs=2, q_len=2, h_q=4, h_k=2, d=16, ps=4, lens=(6, 13),
+                 q_fmt="e4m3")
+    table = {"e2m3": formats.E2M3_TABLE, "e3m2": formats.E3M2_TABLE}[fmt]
+    mag = {float(formats.E4M3_TABLE[m]): m for m in range(0x7F)}
+    lut = np.array([mag[abs(float(table[c]))] | (0x80 if c & 0x20 else 0) for c in range(64)], dtype=np.uint8)
+    c8 = dict(c)
+    c8["k_cache"] = lut[formats.unpack_fp6(c["k_cache"])]
+    c8["v_cache"] = lut[formats.unpack_fp6(c["v_cache"])]
+    kw = dict(softmax_scale=0.29, causal=True)
+    o6, l6 = run_oracle(c, kv_format=fmt, **kw)
+    o8, l8 = run_oracle(c8, **kw)
+    assert np.array_equal(o6, o8) and np.array_equal(l6, l8)
+
