@@ -18,8 +18,8 @@ sample of the same batch on the host cores. Diagnostics go to stderr.
 
 Default workload: 64 sequences, q_len 1, 32 query heads on 8 e4m3 KV heads,
 d = 128, 16-key pages, lengths uniform in [512, 8192], split-KV up to 16
-chunks (``--config 2``). ``--config 1..5`` selects the other workloads; 6 is
-workload 4 with packed fp4 (e2m1) K/V.
+chunks (``--config 2``). ``--config 1..5`` selects the other workloads; 6, 7
+and 8 are workload 4 with packed fp4 (e2m1), fp6 e2m3 and fp6 e3m2 K/V.
 """
 
 import argparse
@@ -123,8 +123,8 @@ def cpu_oracle_baseline(batch, budget_s):
                 decode_attention(nb["q"][sl], nb["k_cache"], nb["v_cache"], nb["block_table"][b:b + 1],
                                  lens[b:b + 1], nb["q_descale"][b:b + 1], nb["k_descale"][b:b + 1],
                                  nb["v_descale"][b:b + 1], q_len=w.q_len, h_k=w.h_k, softmax_scale=w.scale,
-                                 causal=w.causal)
-                kv += int(lens[b]) * w.h_k * (w.d_qk + w.d_v)
+                                 causal=w.causal, kv_format=w.kv_format)
+                kv += int(lens[b]) * w.h_k * (nb["k_cache"].shape[-1] + nb["v_cache"].shape[-1])  # stored row bytes
             done += 1
             if time.perf_counter() - t0 >= budget_s:
                 break
@@ -216,8 +216,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6],
-                    help="workload: 1-5 as specified, 6 = workload 4 with packed fp4 (e2m1) K/V")
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8],
+                    help="workload: 1-5 as specified; 6, 7, 8 = workload 4 with packed fp4 (e2m1), "
+                         "fp6 e2m3, fp6 e3m2 K/V")
     ap.add_argument("--q-len", type=int, default=None, help="query tokens per sequence (latent workload: 1..16)")
     ap.add_argument("--causal", type=int, default=None, help="override the workload's causal flag (0/1)")
     ap.add_argument("--pools", type=int, default=0, help="KV pools to rotate (0: enough for >= 1 GiB, min 3)")

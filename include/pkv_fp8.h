@@ -210,6 +210,15 @@ pkv_status pkv_plan_queued(const int32_t* seq_lens, int32_t num_seqs, int32_t h_
  * d_qk = d_v = 128 and an e4m3 query (PKV_Q_E4M3); one-wave plan only (no
  * bin_offsets / queue). */
 #define PKV_KV_E2M1 2
+/* Packed fp6 K and V caches (the same page's KV cache formats "e2m3" and
+ * "e3m2", and pack_subbyte): e2m3 codes (1 sign, 2 exponent bits with bias 1,
+ * 3 mantissa bits; largest 7.5) or e3m2 codes (1 sign, 3 exponent bits with
+ * bias 3, 2 mantissa bits; largest 28), no inf/NaN; a row of d = 128 codes in
+ * 96 bytes read as one little-endian bitstream, element i at bits 6i..6i+5;
+ * per-(sequence, kv-head) descales; d_qk = d_v = 128, an e4m3 query and the
+ * one-wave plan only, as for PKV_KV_E2M1. */
+#define PKV_KV_E2M3 3
+#define PKV_KV_E3M2 4
 
 /*
  * All strides are in ELEMENTS of the pointed-to type, >= 0; a descale
@@ -220,6 +229,7 @@ pkv_status pkv_plan_queued(const int32_t* seq_lens, int32_t num_seqs, int32_t h_
  *   q      [num_seqs * q_len][h_q][d_qk]     bf16 or e4m3  (q_tok_stride, q_head_stride)
  *   k, v   [num_pages][page_size][h_k][d]    e4m3 codes    (page, row, head strides, bytes)
  *          PKV_KV_E2M1: [num_pages][page_size][h_k][d/2] packed fp4 bytes (byte strides)
+ *          PKV_KV_E2M3 / E3M2: [num_pages][page_size][h_k][3d/4] packed fp6 bytes (byte strides)
  *          MLA: k = v = latent [pages][PS][1][512] e4m3 (v may be NULL or equal k)
  *   k_rope MLA only: [pages][PS][1][64] bf16 (page, row strides)
  *   k_blk_scale MLA only: [pages][PS][1][4] fp32, one scale per 128 latent values
@@ -277,7 +287,7 @@ typedef struct pkv_decode_args {
   int32_t max_splits;
   void* workspace;
   size_t workspace_bytes;
-  /* Optional, device int32[num_seqs * h_k * n_q_tiles] (e4m3 or fp4 K/V
+  /* Optional, device int32[num_seqs * h_k * n_q_tiles] (e4m3, fp4 or fp6 K/V
    * cache; ignored for the latent cache): when non-NULL the decode merges split
    * sequences itself (the last split of each (sequence,
    * kv head, q-row tile) to finish combines the partials, same rule and

@@ -49,10 +49,10 @@ pkv_status check_shapes(const pkv_decode_args* a) {
     if (a->d_qk != 128 || a->d_v != 128)
       return fail(PKV_ERR_UNSUPPORTED, "e4m3 cache: d_qk=%d d_v=%d, only 128/128 is built", a->d_qk, a->d_v);
     if (rows > 4096) return fail(PKV_ERR_UNSUPPORTED, "q_len * h_r = %lld rows > 4096", (long long)rows);
-  } else if (a->kv_format == PKV_KV_E2M1) {
+  } else if (narrow_kv(a->kv_format)) {
     if (a->d_qk != 128 || a->d_v != 128)
-      return fail(PKV_ERR_UNSUPPORTED, "fp4 cache: d_qk=%d d_v=%d, only 128/128 is built", a->d_qk, a->d_v);
-    if (a->q_format != PKV_Q_E4M3) return fail(PKV_ERR_UNSUPPORTED, "fp4 cache: the query must be e4m3");
+      return fail(PKV_ERR_UNSUPPORTED, "fp4/fp6 cache: d_qk=%d d_v=%d, only 128/128 is built", a->d_qk, a->d_v);
+    if (a->q_format != PKV_Q_E4M3) return fail(PKV_ERR_UNSUPPORTED, "fp4/fp6 cache: the query must be e4m3");
     if (rows > 4096) return fail(PKV_ERR_UNSUPPORTED, "q_len * h_r = %lld rows > 4096", (long long)rows);
   } else if (a->kv_format == PKV_KV_MLA) {
     if (a->d_qk != 576 || a->d_v != 512 || a->h_k != 1)
@@ -97,8 +97,8 @@ pkv_status check_pointers(const pkv_decode_args* a, bool for_merge) {
   if (!aligned(a->work, 16)) return fail(PKV_ERR_INVALID_ARG, "work must be 16-B aligned");
   if (a->bin_offsets && (a->num_bins < 1 || !aligned(a->bin_offsets, 4)))
     return fail(PKV_ERR_INVALID_ARG, "bin_offsets needs num_bins >= 1 and 4-B alignment");
-  if (a->kv_format == PKV_KV_E2M1 && (a->bin_offsets || a->queue))
-    return fail(PKV_ERR_UNSUPPORTED, "fp4 cache: only the one-wave plan (pkv_plan_split_kv) is built");
+  if (narrow_kv(a->kv_format) && (a->bin_offsets || a->queue))
+    return fail(PKV_ERR_UNSUPPORTED, "fp4/fp6 cache: only the one-wave plan (pkv_plan_split_kv) is built");
   if (a->queue) {
     if (!a->bin_offsets) return fail(PKV_ERR_INVALID_ARG, "queue needs bin_offsets (a plan from pkv_plan_queued)");
     if (!aligned(a->queue, 4)) return fail(PKV_ERR_INVALID_ARG, "queue must be 4-B aligned");

@@ -358,6 +358,97 @@ __device__ __forceinline__ uint2 e2m1x8_to_e4m3(uint32_t x) {
   return uint2{lo | ((x << 4) & 0x80808080u), hi | (x & 0x80808080u)};
 }
 
+// Packed fp6 rows (e2m3 or e3m2, 96 bytes per row of 128 codes, element i at
+// bits 6i .. 6i+5; "mjolnir-kernel 0.1.0 wheel: mjolnir/t5_decode.py", KV
+// cache formats and pack_subbyte). The scaled MFMA reads an fp6 A operand as
+// that same bitstream, 32 codes in 6 VGPRs, with the fp4 slot map (measured
+// slot by slot), so lane group g4 takes the 24 bytes of head dims 32*g4 ..
+// 32*g4+31. V: the 8 codes d_v 8*r16 .. of a key are 6 bytes at byte 6*r16;
+// each lane loads the 8-byte window at 6*r16 rounded down to 4 bytes (its
+// codes start 0 or 2 bytes in; the window never passes the row's end).
+struct RawBlock6 {
+  uint2 k[2][3];
+  uint2 v[8];
+};
+
+struct LaneOffsets6 {
+  uint32_t k, kb;     // K: r16 * k_row + 24 g4; 24 g4
+  uint32_t v[4], vb;  // V: (4 g4 + i) * v_row + w; w = (6 r16) & ~3
+  uint32_t sel[3];    // v_perm selectors gathering two keys' 12 code bytes from their windows
+};
+
+__device__ __forceinline__ LaneOffsets6 lane_offsets6(const GqaParams& p, int r16, int g4) {
+  LaneOffsets6 o;
+  o.k = (uint32_t)r16 * (uint32_t)p.k_row + 24u * (uint32_t)g4;
+  o.kb = 24u * (uint32_t)g4;
+  const uint32_t w = (6u * (uint32_t)r16) & ~3u;
+  for (int i = 0; i < 4; ++i) o.v[i] = (uint32_t)(4 * g4 + i) * (uint32_t)p.v_row + w;
+  o.vb = w;
+  const bool odd = (6 * r16) & 2;  // codes start 2 bytes into the window
+  o.sel[0] = odd ? 0x05040302u : 0x03020100u;  // key a bytes 0..3
+  o.sel[1] = odd ? 0x07060302u : 0x05040100u;  // key a bytes 4, 5 | key b bytes 0, 1
+  o.sel[2] = odd ? 0x07060504u : 0x05040302u;  // key b bytes 2..5
+  return o;
+}
+
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2))) __attribute__((aligned(4)));
+typedef int i32x6 __attribute__((ext_vector_type(6)));
+typedef _Float16 f16x32 __attribute__((ext_vector_type(32)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// load_block for packed fp6 rows: 6 + 8 loads, same row clamping.
+__device__ __forceinline__ RawBlock6 load_block6(const GqaParams& p, int g, int kb, int pg0, int pg1, int last_key,
+                                                 int pmask, const LaneOffsets6& lo) {
+  RawBlock6 r;
+  for (int t = 0; t < 2; ++t) {
+    const int st = min(kb + 16 * t, last_key);
+    const uint32_t lim = (uint32_t)max(last_key - st, 0);
+    const int64_t pg = t ? pg1 : pg0;
+    const uint32_t row = (uint32_t)(st & pmask);
+    const uint8_t* kbase = p.k + pg * p.k_page + (int64_t)g * p.k_head + row * (uint32_t)p.k_row;
+    const uint8_t* vbase = p.v + pg * p.v_page + (int64_t)g * p.v_head + row * (uint32_t)p.v_row;
+    const uint32_t koff = min(lo.k, lim * (uint32_t)p.k_row + lo.kb);
+    for (int j = 0; j < 3; ++j) r.k[t][j] = *reinterpret_cast<const uint2*>(kbase + (koff + 8u * j));
+    const uint32_t vlim = lim * (uint32_t)p.v_row + lo.vb;
+    for (int i = 0; i < 4; ++i) {
+      const u32x2_a4 x = *reinterpret_cast<const u32x2_a4*>(vbase + min(lo.v[i], vlim));
+      r.v[4 * t + i] = uint2{x[0], x[1]};
+    }
+  }
+  return r;
+}
+
+// Four keys' V codes (windows a0, a1, b0, b1) -> their e4m3 bytes: the 32
+// codes are packed into one 192-bit bitstream, widened to f16 with
+// v_cvt_scalef32_pk32_f16_{fp6,bf6} and narrowed to e4m3 two at a time; all
+// three steps are exact (every e2m3 and e3m2 value is an e4m3 value).
+template <int KVF>
+__device__ __forceinline__ void fp6x32_to_e4m3(const uint2* win, const LaneOffsets6& lo, uint2* out) {
+  i32x6 x;
+  for (int pr = 0; pr < 2; ++pr) {
+    const uint2 a = win[2 * pr], b = win[2 * pr + 1];
+    x[3 * pr + 0] = (int)__builtin_amdgcn_perm(a.y, a.x, lo.sel[0]);
+    x[3 * pr + 1] = (int)__builtin_amdgcn_perm(b.x, a.y, lo.sel[1]);
+    x[3 * pr + 2] = (int)__builtin_amdgcn_perm(b.y, b.x, lo.sel[2]);
+  }
+  f16x32 h;
+  if constexpr (KVF == PKV_KV_E2M3)
+    h = __builtin_amdgcn_cvt_scalef32_pk32_f16_fp6(x, 1.0f);
+  else
+    h = __builtin_amdgcn_cvt_scalef32_pk32_f16_bf6(x, 1.0f);
+  for (int i = 0; i < 4; ++i) {
+    uint32_t w[2];
+    for (int hw = 0; hw < 2; ++hw) {
+      s16x2 v = {0, 0};
+      v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(v, f16x2{h[8 * i + 4 * hw], h[8 * i + 4 * hw + 1]}, 1.0f, false);
+      v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(v, f16x2{h[8 * i + 4 * hw + 2], h[8 * i + 4 * hw + 3]}, 1.0f, true);
+      w[hw] = __builtin_bit_cast(uint32_t, v);
+    }
+    out[i] = uint2{w[0], w[1]};
+  }
+}
+
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // One 32-key block: S = K Q^T, online softmax, O^T += V^T P^T. lim[nb] is
@@ -548,6 +639,37 @@ __device__ __forceinline__ void process_block_fp4(const RawBlock4& cur, int kb, 
   softmax_pv<true, NB, true>(sacc, v8, kb, st, lim, lim_min, c2, g4);
 }
 
+// One 32-key block of packed fp6 K/V with an e4m3 query: S = K Q^T on the
+// scaled MFMA (A format 2 = e2m3 or 3 = e3m2), then V converted to e4m3 and
+// the fp8 softmax / PV.
+template <int NB, bool QLDS, int KVF>
+__device__ __forceinline__ void process_block_fp6(const RawBlock6& cur, int kb, const QOperand<NB>& q,
+                                                  const uint8_t* qlds, const LaneOffsets6& lo, RowState<NB>& st,
+                                                  const int* lim, int lim_min, float c2, int g4) {
+  constexpr int kFmt = KVF == PKV_KV_E2M3 ? 2 : 3;
+  const int lane = threadIdx.x & 63;
+  if (QLDS) asm volatile("" ::: "memory");
+  f32x4 sacc[NB][2];
+  for (int t = 0; t < 2; ++t) {
+    const i32x8 a = {(int)cur.k[t][0].x, (int)cur.k[t][0].y, (int)cur.k[t][1].x, (int)cur.k[t][1].y,
+                     (int)cur.k[t][2].x, (int)cur.k[t][2].y, 0, 0};
+    for (int nb = 0; nb < NB; ++nb) {
+      long qv[4];
+      for (int s = 0; s < 4; ++s)
+        qv[s] = QLDS ? *reinterpret_cast<const long*>(qlds + ((4 * nb + s) * 64 + lane) * 8) : q.q8[nb][s];
+      const i32x8 b = {(int)qv[0], (int)(qv[0] >> 32), (int)qv[1], (int)(qv[1] >> 32),
+                       (int)qv[2], (int)(qv[2] >> 32), (int)qv[3], (int)(qv[3] >> 32)};
+      // B format 0 = fp8 e4m3; E8M0 scales 127 = 2^0
+      sacc[nb][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, f32x4{0.f, 0.f, 0.f, 0.f}, kFmt, 0, 0,
+                                                                      127, 0, 127);
+    }
+  }
+  uint2 v8[8];
+  fp6x32_to_e4m3<KVF>(cur.v, lo, v8);
+  fp6x32_to_e4m3<KVF>(cur.v + 4, lo, v8 + 4);
+  softmax_pv<true, NB, false>(sacc, v8, kb, st, lim, lim_min, c2, g4);
+}
+
 // Epilogue of one work item for kv head g of sequence b: a sequence with one
 // split writes O and LSE itself; otherwise the rows go to split slot `slot`
 // of the workspace, and with merge counters the split that finishes last for
@@ -648,15 +770,16 @@ __device__ __forceinline__ void keep_pace(int* progress, int wave, int done, int
 
 // One work item (a chunk of 128-key tiles of one sequence) for kv head g:
 // the one-item-per-workgroup plan.
-// KVF: 0 = e4m3 K/V, 2 = packed fp4 (e2m1) K/V (e4m3 query only). The page
-// pairs of a fetch are loaded LA fetches ahead: two for the e4m3 ring, one
-// fewer than the ring depth for the deeper fp4 ring (a pair loaded sooner
-// would make its wait cover KV loads still in the ring).
+// KVF: 0 = e4m3 K/V, else the packed narrow format (PKV_KV_E2M1 fp4,
+// PKV_KV_E2M3 / PKV_KV_E3M2 fp6; e4m3 query only). The page pairs of a fetch
+// are loaded LA fetches ahead: two for the e4m3 ring, one fewer than the ring
+// depth for the deeper narrow rings (a pair loaded sooner would make its wait
+// cover KV loads still in the ring).
 template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES, int HW, int KVF = 0>
 __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, int lane, int g, int* progress,
                                                 int& round_base) {
-  static_assert(KVF == 0 || (KVF == 2 && FP8Q), "fp4 K/V needs the e4m3 query");
-  constexpr int LA = KVF == 2 ? STAGES - 1 : 2;
+  static_assert(KVF == 0 || FP8Q, "narrow K/V formats need the e4m3 query");
+  constexpr int LA = KVF != 0 && STAGES > 2 ? STAGES - 1 : 2;
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
 
@@ -732,18 +855,24 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
 #pragma unroll
       for (int u = 0; u < LA; ++u) pv[u % STAGES] = page_pair(k_begin + kBlockKeys * u);
     }
-    using Raw = typename std::conditional<KVF == 2, RawBlock4, RawBlock>::type;
+    constexpr bool kFp4 = KVF == PKV_KV_E2M1, kFp6 = KVF == PKV_KV_E2M3 || KVF == PKV_KV_E3M2;
+    using Raw = typename std::conditional<kFp4, RawBlock4,
+                                          typename std::conditional<kFp6, RawBlock6, RawBlock>::type>::type;
     const auto lo = [&] {
-      if constexpr (KVF == 2)
+      if constexpr (kFp4)
         return lane_offsets4(p, r16, g4);
+      else if constexpr (kFp6)
+        return lane_offsets6(p, r16, g4);
       else
         return lane_offsets(p, r16, g4);
     }();
     auto fetch = [&](Raw& r, int kb, const int slot) {
       const int pg0 = clamp_page(p, __builtin_amdgcn_readlane(pv[slot], 0));
       const int pg1 = clamp_page(p, __builtin_amdgcn_readlane(pv[slot], 1));
-      if constexpr (KVF == 2)
+      if constexpr (kFp4)
         r = load_block4(p, g, kb, pg0, pg1, last_key, pmask, lo);
+      else if constexpr (kFp6)
+        r = load_block6(p, g, kb, pg0, pg1, last_key, pmask, lo);
       else
         r = load_block(p, g, kb, pg0, pg1, last_key, pmask, lo);
       pv[(slot + LA) % STAGES] = page_pair(kb + LA * kBlockKeys);
@@ -773,8 +902,10 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
       for (int s = 0; s < STAGES; ++s) {
         const int kb = kb0 + kBlockKeys * s;
         fetch(ring[(s + STAGES - 1) % STAGES], kb + kBlockKeys * (STAGES - 1), (s + STAGES - 1) % STAGES);
-        if constexpr (KVF == 2)
+        if constexpr (kFp4)
           process_block_fp4<NB, kQLds>(ring[s], kb, q, qlds, st, lim, lim_min, c2, g4);
+        else if constexpr (kFp6)
+          process_block_fp6<NB, kQLds, KVF>(ring[s], kb, q, qlds, lo, st, lim, lim_min, c2, g4);
         else
           process_block<FP8Q, NB, kQLds>(ring[s], kb, q, qlds, st, lim, lim_min, c2, g4);
       }
@@ -1242,29 +1373,39 @@ const void* kernel_ptr(bool stream) {
                 : reinterpret_cast<const void*>(&gqa_decode_kernel<FP8Q, NB, CT, ring_stages<NB, false>(), HW, false>);
 }
 
-// fp4 K/V: one-item form, a ring of five blocks (one row block) or three
-// (two row blocks): 4 KB blocks, so a deeper ring keeps the bytes in flight.
+// Packed narrow K/V: one-item form. One row block: a ring of five 4 KB fp4
+// blocks or four 6 KB fp6 blocks (a deeper ring than e4m3's three 8 KB
+// blocks keeps a similar number of bytes in flight; fp6's 15 loads per fetch
+// also bound its depth); two row blocks: three (fp4) or two (fp6, whose
+// conversion needs the registers a third block would take).
 #ifndef PKV_FP4_STAGES
 #define PKV_FP4_STAGES 5
 #endif
-template <int NB>
-constexpr int fp4_stages() {
-  return NB == 1 ? PKV_FP4_STAGES : 3;
+template <int NB, int KVF>
+constexpr int narrow_stages() {
+  return NB == 2 ? (KVF == PKV_KV_E2M1 ? 3 : 2) : KVF == PKV_KV_E2M1 ? PKV_FP4_STAGES : 4;
 }
 
-template <int NB, bool CT, int HW>
-const void* fp4_ptr() {
-  return reinterpret_cast<const void*>(&gqa_decode_kernel<true, NB, CT, fp4_stages<NB>(), HW, false, 2>);
+template <int NB, bool CT, int HW, int KVF>
+const void* narrow_ptr() {
+  return reinterpret_cast<const void*>(&gqa_decode_kernel<true, NB, CT, narrow_stages<NB, KVF>(), HW, false, KVF>);
 }
 
-template <int NB, bool CT>
-const void* select_fp4_heads(const GqaVariant& v) {
+template <int NB, bool CT, int KVF>
+const void* select_narrow_heads(const GqaVariant& v) {
   switch (v.heads_per_wg) {
-    case 1: return fp4_ptr<NB, CT, 1>();
-    case 2: return fp4_ptr<NB, CT, 2>();
-    case 4: return fp4_ptr<NB, CT, 4>();
-    default: return fp4_ptr<NB, CT, NB == 1 ? 8 : 4>();
+    case 1: return narrow_ptr<NB, CT, 1, KVF>();
+    case 2: return narrow_ptr<NB, CT, 2, KVF>();
+    case 4: return narrow_ptr<NB, CT, 4, KVF>();
+    default: return narrow_ptr<NB, CT, NB == 1 ? 8 : 4, KVF>();
   }
+}
+
+template <int KVF>
+const void* select_narrow(const GqaVariant& v) {
+  if (v.n_blocks == 1)
+    return v.causal_tail ? select_narrow_heads<1, true, KVF>(v) : select_narrow_heads<1, false, KVF>(v);
+  return v.causal_tail ? select_narrow_heads<2, true, KVF>(v) : select_narrow_heads<2, false, KVF>(v);
 }
 
 template <bool FP8Q, int NB, bool CT>
@@ -1283,10 +1424,9 @@ const void* select_tail(const GqaVariant& v) {
 }
 
 const void* select_kernel(const GqaVariant& v) {
-  if (v.kv_fp4) {
-    if (v.n_blocks == 1) return v.causal_tail ? select_fp4_heads<1, true>(v) : select_fp4_heads<1, false>(v);
-    return v.causal_tail ? select_fp4_heads<2, true>(v) : select_fp4_heads<2, false>(v);
-  }
+  if (v.kvf == PKV_KV_E2M1) return select_narrow<PKV_KV_E2M1>(v);
+  if (v.kvf == PKV_KV_E2M3) return select_narrow<PKV_KV_E2M3>(v);
+  if (v.kvf == PKV_KV_E3M2) return select_narrow<PKV_KV_E3M2>(v);
   if (v.fp8_q) return v.n_blocks == 1 ? select_tail<true, 1>(v) : select_tail<true, 2>(v);
   return v.n_blocks == 1 ? select_tail<false, 1>(v) : select_tail<false, 2>(v);
 }
@@ -1302,12 +1442,17 @@ int log2_exact(int x) {
 GqaVariant gqa_variant(const pkv_decode_args& a) {
   GqaVariant v;
   v.fp8_q = a.q_format == PKV_Q_E4M3;
-  v.kv_fp4 = a.kv_format == PKV_KV_E2M1;
+  v.kvf = narrow_kv(a.kv_format) ? a.kv_format : 0;
   const int rows = a.q_len * (a.h_q / a.h_k);
   v.n_blocks = rows <= 16 ? 1 : 2;
   v.causal_tail = a.causal && a.q_len > 1;
   v.stream = a.bin_offsets != nullptr && a.queue == nullptr;
-  v.stages = v.kv_fp4 ? (v.n_blocks == 1 ? fp4_stages<1>() : fp4_stages<2>()) : (v.n_blocks == 2 && !v.stream) ? 2 : 3;
+  if (v.kvf == PKV_KV_E2M1)
+    v.stages = v.n_blocks == 1 ? narrow_stages<1, PKV_KV_E2M1>() : narrow_stages<2, PKV_KV_E2M1>();
+  else if (v.kvf)
+    v.stages = v.n_blocks == 1 ? narrow_stages<1, PKV_KV_E2M3>() : narrow_stages<2, PKV_KV_E2M3>();
+  else
+    v.stages = (v.n_blocks == 2 && !v.stream) ? 2 : 3;
   // kv heads per workgroup: the largest power of two dividing h_k, up to 8
   // (4 for two row blocks: eight waves of 32 rows per workgroup measured
   // slower on the speculative-verify workload, 100 vs 95 us)

@@ -22,8 +22,13 @@ struct GqaVariant {
   int stages;       // register ring depth of the KV stream (blocks of 32 keys)
   int heads_per_wg; // kv heads (one wave each) per workgroup
   bool stream;      // balanced plan: each workgroup streams the items of its bin
-  bool kv_fp4;      // packed fp4 (e2m1) K/V: one-item form only
+  int kvf;          // K/V format: 0 = e4m3, else the packed narrow format's PKV_KV_* value (one-item form only)
 };
+
+// Packed narrow K/V formats (fp4 e2m1, fp6 e2m3 / e3m2).
+inline bool narrow_kv(int kv_format) {
+  return kv_format == PKV_KV_E2M1 || kv_format == PKV_KV_E2M3 || kv_format == PKV_KV_E3M2;
+}
 GqaVariant gqa_variant(const pkv_decode_args& a);
 int gqa_rows_per_tile(const GqaVariant& v);
 hipError_t gqa_occupancy(const GqaVariant& v, int* units_per_cu);

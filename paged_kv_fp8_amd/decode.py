@@ -13,7 +13,11 @@ import numpy as np
 import torch
 
 from . import native
-from .native import PKV_KV_E2M1, PKV_KV_E4M3, PKV_KV_MLA, PKV_Q_BF16, PKV_Q_E4M3
+from .native import PKV_KV_E2M1, PKV_KV_E2M3, PKV_KV_E3M2, PKV_KV_E4M3, PKV_KV_MLA, PKV_Q_BF16, PKV_Q_E4M3
+
+# K/V code formats by name: ABI value and bits per code
+_KV_FORMATS = {"e4m3": PKV_KV_E4M3, "e2m1": PKV_KV_E2M1, "e2m3": PKV_KV_E2M3, "e3m2": PKV_KV_E3M2}
+_KV_BITS = {"e4m3": 8, "e2m1": 4, "e2m3": 6, "e3m2": 6}
 
 
 def _ptr(t):
@@ -58,15 +62,15 @@ class PagedDecode:
         if mla:
             h_k, d_qk, d_v, ps = 1, q.shape[2], 512, latent.shape[1]
             num_pages = num_pages or latent.shape[0]
-        else:  # e4m3 codes, or packed fp4 rows of d/2 bytes
-            per_byte = 2 if kv_format == "e2m1" else 1
-            h_k, d_qk, d_v, ps = k_cache.shape[2], q.shape[2], v_cache.shape[3] * per_byte, k_cache.shape[1]
+        else:  # e4m3 codes, or packed narrow rows (fp4: d/2 bytes, fp6: 3d/4 bytes)
+            bits = _KV_BITS[kv_format]
+            h_k, d_qk, d_v, ps = k_cache.shape[2], q.shape[2], v_cache.shape[3] * 8 // bits, k_cache.shape[1]
             num_pages = num_pages or k_cache.shape[0]
         a.num_seqs, a.q_len, a.h_q, a.h_k, a.d_qk, a.d_v = num_seqs, q_len, h_q, h_k, d_qk, d_v
         a.page_size, a.num_pages, a.max_blocks = ps, num_pages, block_table.shape[1]
         a.causal = 1 if causal else 0
         a.q_format = PKV_Q_BF16 if q.dtype == torch.bfloat16 else PKV_Q_E4M3
-        a.kv_format = PKV_KV_MLA if mla else (PKV_KV_E2M1 if kv_format == "e2m1" else PKV_KV_E4M3)
+        a.kv_format = PKV_KV_MLA if mla else _KV_FORMATS[kv_format]
         a.softmax_scale, a.o_scale = float(softmax_scale), float(o_scale)
         a.q, a.q_tok_stride, a.q_head_stride = _ptr(q), q.stride(0), q.stride(1)
         if mla:

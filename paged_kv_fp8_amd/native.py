@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkvfp8.s
 
 PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_CAPACITY, PKV_ERR_WORKSPACE, PKV_ERR_HIP = 0, -1, -2, -3, -4, -5
 PKV_Q_BF16, PKV_Q_E4M3 = 0, 1
-PKV_KV_E4M3, PKV_KV_MLA, PKV_KV_E2M1 = 0, 1, 2
+PKV_KV_E4M3, PKV_KV_MLA, PKV_KV_E2M1, PKV_KV_E2M3, PKV_KV_E3M2 = 0, 1, 2, 3, 4
 PKV_MAX_SPLITS = 256
 
 # Every function the header declares, in declaration order.

@@ -1,9 +1,9 @@
-"""GPU parity of the packed fp4 (e2m1) K/V decode against the fp64 oracle,
-through the C ABI: the page's narrow KV format with an e4m3 query, on small
-variants of the fp4 workload (one and two 16-row blocks, causal tail and
-block mode, split and unsplit sequences, ragged tails), the full workload on
-sampled sequences, the edge lengths, and bit-identical repeats and graph
-replays. Bars as for the e4m3 cache (e4m3 P): max|dO| <= 1e-2 * max|V| at the
+"""GPU parity of the packed narrow K/V decodes (fp4 e2m1, fp6 e2m3 and e3m2)
+against the fp64 oracle, through the C ABI: the page's narrow KV formats with
+an e4m3 query, on small variants of each format's workload (one and two
+16-row blocks, causal tail and block mode, split and unsplit sequences,
+ragged tails, 16-key pages), the full workload on sampled sequences, the edge
+lengths, and bit-identical repeats, graph replays and the in-kernel merge. Bars as for the e4m3 cache (e4m3 P): max|dO| <= 1e-2 * max|V| at the
 workload's lengths, and the derived short-sequence bound 0.07 * max|V| for
 the edge lengths (L < 1024)."""
 
@@ -18,6 +18,8 @@ pytestmark = pytest.mark.gpu
 
 FP8_SHORT_TOL = 0.07
 EDGE_LENS = [0, 1, 2, 3, 15, 16, 17, 31, 32, 33, 127, 128, 129, 255, 256, 257, 1000, 1025]
+# workload index of each format: the fully-fp8 batch with that K/V format
+FORMATS = {"e2m1": 6, "e2m3": 7, "e3m2": 8}
 
 
 def _decode():
@@ -50,43 +52,47 @@ SMALL = {
 }
 
 
+@pytest.mark.parametrize("fmt", list(FORMATS))
 @pytest.mark.parametrize("name", list(SMALL))
-def test_fp4_small_every_output(name):
-    w = workload(6, **SMALL[name])
+def test_narrow_small_every_output(name, fmt):
+    w = workload(FORMATS[fmt], **SMALL[name])
     batch = make_batch(w, device="cuda")
     dec = run(batch)
-    err_o, err_l, _ = check(batch, dec, what=name)
-    print(f"fp4 {name}: kernel={dec.kernel_name} splits={dec.plan_info.max_n_splits} "
+    err_o, err_l, _ = check(batch, dec, what=f"{fmt} {name}")
+    print(f"{fmt} {name}: kernel={dec.kernel_name} splits={dec.plan_info.max_n_splits} "
           f"max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
 
 
-def test_fp4_full_workload_sampled():
-    w = workload(6)
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_narrow_full_workload_sampled(fmt):
+    w = workload(FORMATS[fmt])
     batch = make_batch(w, device="cuda")
     dec = run(batch)
     lens = batch.seq_lens.cpu().numpy()
     order = np.argsort(lens)
     rng = np.random.default_rng(61)
     seqs = sorted({int(order[0]), int(order[-1])} | {int(x) for x in rng.choice(len(lens), 6, replace=False)})
-    err_o, err_l, _ = check(batch, dec, seqs=seqs, what="fp4 full")
-    print(f"fp4 full: work={dec.plan_info.num_real} max_splits_used={dec.plan_info.max_n_splits} "
+    err_o, err_l, _ = check(batch, dec, seqs=seqs, what=f"{fmt} full")
+    print(f"{fmt} full: work={dec.plan_info.num_real} max_splits_used={dec.plan_info.max_n_splits} "
           f"max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
 
 
+@pytest.mark.parametrize("fmt", list(FORMATS))
 @pytest.mark.parametrize("q_len,causal,ps,force", [(1, True, 128, 0), (2, True, 16, 3), (2, False, 64, 0),
                                                    (1, True, 32, 5)])
-def test_fp4_edge_lengths(q_len, causal, ps, force):
-    w = workload(6, num_seqs=len(EDGE_LENS), q_len=q_len, page_size=ps, causal=causal,
+def test_narrow_edge_lengths(q_len, causal, ps, force, fmt):
+    w = workload(FORMATS[fmt], num_seqs=len(EDGE_LENS), q_len=q_len, page_size=ps, causal=causal,
                  seq_len_dist=("fixed", EDGE_LENS), max_splits=8)
     batch = make_batch(w, device="cuda")
     dec = run(batch, force_splits=force)
-    _, _, empty = check(batch, dec, o_tol=FP8_SHORT_TOL, what=f"fp4 edge q_len={q_len} ps={ps}")
+    _, _, empty = check(batch, dec, o_tol=FP8_SHORT_TOL, what=f"{fmt} edge q_len={q_len} ps={ps}")
     o = dec.o.float().cpu().numpy()
     assert np.all(o[0:q_len] == 0.0)  # L = 0: O = 0 exactly (LSE = -inf is checked above)
 
 
-def test_fp4_bitwise_repeats_graph_replay_and_fused_merge():
-    w = workload(6, num_seqs=12, seq_len_dist=("mix", 0.25, (6000, 20000), (1024, 4096)))
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_narrow_bitwise_repeats_graph_replay_and_fused_merge(fmt):
+    w = workload(FORMATS[fmt], num_seqs=12, seq_len_dist=("mix", 0.25, (6000, 20000), (1024, 4096)))
     batch = make_batch(w, device="cuda")
     dec = run(batch)
     assert dec.has_splits
