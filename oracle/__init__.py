@@ -25,6 +25,7 @@ Modules
   merge     LSE merge of split partials (the split-KV combine rule).
   plan      the occupancy-pinned split-KV planner (integer algorithm).
   brute     pure-Python loop version of the attention for tiny inputs.
+  sparse    decode over per-token slot lists (window + top-k) with a sink.
   producers e4m3 encoding (round to nearest even, saturating), the query
             quantisation and the paged KV-cache write (e4m3 and latent).
 

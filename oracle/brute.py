@@ -131,3 +131,41 @@ def brute_decode_attention(q, q_fmt, k_cache, v_cache, block_table, seq_lens, qd
                             wj * vj[i] for wj, vj in zip(w, values)) / den
                     lse[b][g][n] = top + math.log(den)
     return o, lse
+
+
+def brute_sparse_decode(q, sources, softmax_scale, o_scale, sink):
+    """Slot-list decode over latent records with nested loops: q[t][h][576]
+    bf16 bits; each source a dict of nested lists "latent" [page][row][0][512]
+    e4m3 codes, "rope" [page][row][0][64] bf16 bits, "scales" [page][row][0][4]
+    floats and "slots" [t][width]; sink [h] or None. A slot s is row s % PS of
+    page s // PS; negative entries are skipped. Returns (o[t][h][512],
+    lse[t][h])."""
+    T, h_q = len(q), len(q[0])
+    o = [[[0.0] * 512 for _ in range(h_q)] for _ in range(T)]
+    lse = [[-math.inf] * h_q for _ in range(T)]
+    for t in range(T):
+        recs = []  # (key 576 floats, value 512 floats)
+        for src in sources:
+            ps = len(src["latent"][0])
+            for s in src["slots"][t]:
+                s = int(s)
+                if s < 0:
+                    continue
+                page, row = s // ps, s % ps
+                sc = [float(x) for x in src["scales"][page][row][0]]
+                lat = [e4m3_bits_to_float(src["latent"][page][row][0][i]) * sc[i // 128] for i in range(512)]
+                rope = [bf16_bits_to_float(x) for x in src["rope"][page][row][0]]
+                recs.append((lat + rope, lat))
+        for h in range(h_q):
+            qv = [bf16_bits_to_float(x) for x in q[t][h]]
+            z = [softmax_scale * math.fsum(a * b for a, b in zip(k, qv)) for k, _ in recs]
+            terms = z + ([float(sink[h])] if sink is not None else [])
+            if not terms:
+                continue
+            m = max(terms)
+            w = [math.exp(x - m) for x in z]
+            Z = math.fsum(w + ([math.exp(float(sink[h]) - m)] if sink is not None else []))
+            for d in range(512):
+                o[t][h][d] = o_scale * math.fsum(w[j] * recs[j][1][d] for j in range(len(recs))) / Z
+            lse[t][h] = m + math.log(Z)
+    return o, lse

@@ -347,3 +347,132 @@ def make_batch(w: Workload, device="cpu", seq_lens=None) -> Batch:
         setattr(batch, f"{name}_descale", desc)
     batch.kv_buffer = kbuf
     return batch
+
+
+# ---- sparse slot-list decode ---------------------------------------------------
+# Each decode token (one per sequence) attends to the records named by two
+# slot lists over two latent-record pools ("vLLM PR #62633", Kernel design):
+# the sliding window (the last `window` positions of its sequence, in a pool
+# of `page_size[0]`-slot pages) and `topk` compressed records (one per
+# `compress_ratio` positions, distinct, drawn at random: a synthetic stand-in
+# for the indexer's choice, in a pool of `page_size[1]` = 128 // ratio-slot
+# pages). Lists are padded with -1; pages are handed out from a seeded
+# permutation, spare pages stay poisoned (e4m3 NaN bytes). Records as for the
+# latent workload: 512 values ~ N(0, 1) quantised per 128-value block
+# (amax / 448), 64 rope values ~ N(0, 1) in bf16. Sink logits ~ N(0, 1) per
+# head. Query ~ N(0, 1) in bf16, one token per sequence.
+@dataclass(frozen=True)
+class SparseWorkload:
+    name: str
+    num_tokens: int
+    h_q: int
+    window: int
+    topk: int
+    compress_ratio: int
+    page_size: tuple
+    seq_len_dist: tuple
+    sink: bool = True
+    seed: int = 1120
+
+    @property
+    def scale(self):
+        return 1.0 / math.sqrt(MLA_LATENT + MLA_ROPE)
+
+
+SPARSE_WORKLOADS = {
+    # a small decode step of the page's flash configuration: 16 tokens, 16 live
+    # heads, a 128-slot window plus 512 compressed slots (6 tiles per token)
+    9: SparseWorkload("sparse_t16_hq16_win128_top512_ratio4_L4k-64k", 16, 16, 128, 512, 4, (64, 32),
+                      ("uniform", 4096, 65536)),
+}
+
+
+def sparse_workload(index, **overrides):
+    return replace(SPARSE_WORKLOADS[index], **overrides)
+
+
+@dataclass
+class SparseBatch:
+    spec: SparseWorkload
+    seq_lens: np.ndarray
+    q: torch.Tensor                 # (T, h_q, 576) bf16
+    sources: list                   # per list: dict(latent, rope, scales views, slots (T, width) int32, page_size, num_pages)
+    sink: torch.Tensor = None       # (h_q,) float32 or None
+    kv_buffers: list = field(default_factory=list)
+
+    @property
+    def kv_bytes(self):
+        """Record bytes the decode must read: every listed (non-negative) slot."""
+        return sum(int((s["slots"] >= 0).sum().item()) for s in self.sources) * MLA_RECORD_BYTES
+
+    def to_numpy(self):
+        def u16(t):
+            return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        out = {"q": u16(self.q), "sink": None if self.sink is None else self.sink.cpu().numpy().astype(np.float64),
+               "sources": []}
+        for s in self.sources:
+            out["sources"].append({"latent": s["latent"].contiguous().cpu().numpy(), "rope": u16(s["rope"]),
+                                   "scales": s["scales"].contiguous().cpu().numpy(),
+                                   "slots": s["slots"].cpu().numpy()})
+        return out
+
+
+def _latent_pool(gen, pages, ps, device):
+    """A record pool of `pages` pages of `ps` slots, every slot filled."""
+    n = pages * ps
+    rec = torch.empty((n, MLA_RECORD_BYTES), dtype=torch.uint8, device=device)
+    lat = torch.randn(n, MLA_LATENT // MLA_BLOCK, MLA_BLOCK, generator=gen, device=device)
+    desc = lat.abs().amax(dim=-1).clamp(min=1e-6) / E4M3_MAX
+    codes = (lat / desc[:, :, None]).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+    rope = torch.randn(n, MLA_ROPE, generator=gen, device=device).to(torch.bfloat16)
+    rec[:, :MLA_LATENT] = codes.view(torch.uint8).view(n, MLA_LATENT)
+    rec[:, MLA_LATENT:MLA_LATENT + 2 * MLA_ROPE] = rope.view(torch.uint8).view(n, 2 * MLA_ROPE)
+    rec[:, MLA_LATENT + 2 * MLA_ROPE:] = desc.float().contiguous().view(torch.uint8).view(n, 16)
+    return rec.view(pages, ps, 1, MLA_RECORD_BYTES)
+
+
+def make_sparse_batch(w: SparseWorkload, device="cpu", seq_lens=None) -> SparseBatch:
+    rng = np.random.Generator(np.random.PCG64(w.seed + 7))
+    if seq_lens is None:
+        lens = draw_seq_lens(replace(WORKLOADS[2], num_seqs=w.num_tokens, seq_len_dist=w.seq_len_dist, seed=w.seed))
+    else:
+        lens = np.asarray(seq_lens, dtype=np.int32)
+    assert lens.shape == (w.num_tokens,)
+    gen = torch.Generator(device=device).manual_seed(w.seed)
+    T = w.num_tokens
+    q = torch.randn(T, w.h_q, MLA_LATENT + MLA_ROPE, generator=gen, device=device).to(torch.bfloat16)
+    sources, buffers = [], []
+    for which in (0, 1):
+        ps = w.page_size[which]
+        width = w.window if which == 0 else w.topk
+        # positions each token lists: the window's last positions, or distinct compressed records
+        picks = []
+        for L in lens:
+            L = int(L)
+            if which == 0:
+                picks.append(np.arange(max(0, L - w.window), L))
+            else:
+                n_c = L // w.compress_ratio
+                picks.append(np.sort(rng.choice(n_c, size=min(w.topk, n_c), replace=False)) if n_c else
+                             np.zeros(0, np.int64))
+        # pages touched per token, handed out from one permutation of the pool
+        touched = [np.unique(p // ps) for p in picks]
+        used = sum(len(t) for t in touched)
+        num_pages = used + max(4, used // 4)
+        perm = rng.permutation(num_pages)
+        slots = np.full((T, width), -1, dtype=np.int32)
+        cursor = 0
+        for t, (p, tp) in enumerate(zip(picks, touched)):
+            page_of = dict(zip(tp.tolist(), perm[cursor:cursor + len(tp)].tolist()))
+            cursor += len(tp)
+            slots[t, :len(p)] = [page_of[int(x) // ps] * ps + int(x) % ps for x in p]
+        rec = _latent_pool(gen, num_pages, ps, device)
+        spare = torch.from_numpy(perm[used:].copy()).to(device)
+        rec[spare] = E4M3_NAN  # poisoned, never listed
+        buffers.append(rec)
+        sources.append({"latent": rec[..., :MLA_LATENT],
+                        "rope": rec[..., MLA_LATENT:MLA_LATENT + 2 * MLA_ROPE].view(torch.bfloat16),
+                        "scales": rec[..., MLA_LATENT + 2 * MLA_ROPE:].view(torch.float32),
+                        "slots": torch.from_numpy(slots).to(device), "page_size": ps, "num_pages": num_pages})
+    sink = torch.randn(w.h_q, generator=gen, device=device) if w.sink else None
+    return SparseBatch(spec=w, seq_lens=lens, q=q, sources=sources, sink=sink, kv_buffers=buffers)
