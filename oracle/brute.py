@@ -138,7 +138,8 @@ def brute_sparse_decode(q, sources, softmax_scale, o_scale, sink):
     bf16 bits; each source a dict of nested lists "latent" [page][row][0][512]
     e4m3 codes, "rope" [page][row][0][64] bf16 bits, "scales" [page][row][0][4]
     floats and "slots" [t][width]; sink [h] or None. A slot s is row s % PS of
-    page s // PS; negative entries are skipped. Returns (o[t][h][512],
+    page s // PS; negative entries and entries past the pool are skipped.
+    Returns (o[t][h][512],
     lse[t][h])."""
     T, h_q = len(q), len(q[0])
     o = [[[0.0] * 512 for _ in range(h_q)] for _ in range(T)]
@@ -149,7 +150,7 @@ def brute_sparse_decode(q, sources, softmax_scale, o_scale, sink):
             ps = len(src["latent"][0])
             for s in src["slots"][t]:
                 s = int(s)
-                if s < 0:
+                if s < 0 or s >= len(src["latent"]) * ps:
                     continue
                 page, row = s // ps, s % ps
                 sc = [float(x) for x in src["scales"][page][row][0]]

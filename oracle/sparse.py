@@ -10,8 +10,9 @@ record is both key and value); the token's partials are merged together with
 the attention sink. Readings taken here (the page leaves them open):
 
   * A slot is a flat index into a pool of pages, page * page_size + row
-    (the usual paged-cache slot mapping); a negative list entry names no key.
-    Entries are keys, so a slot listed twice counts twice.
+    (the usual paged-cache slot mapping); a negative entry, or one past the
+    pool, names no key. Entries are keys, so a slot listed twice counts
+    twice.
   * The record is this package's latent record (``attention.mla_keys_values``:
     512 e4m3 codes times one fp32 scale per 128 values, then 64 bf16 rope
     values; the value is the scaled latent part); the model's own record
@@ -29,7 +30,8 @@ Pins (tests/test_sparse_oracle.py): the contiguous latent decode reproduced
 by listing a sequence's own slots; the closed form of the sink
 (LSE' = logaddexp(LSE, sink), O' = O * exp(LSE - LSE')); a pure-Python brute
 force on tiny inputs; order invariance of the lists; split invariance through
-``oracle.merge`` plus one sink term; empty lists with and without a sink.
+``oracle.merge`` plus one sink term; empty lists with and without a sink; an
+entry past the pool equal to a negative one.
 """
 
 import numpy as np
@@ -39,13 +41,11 @@ from .attention import _decode_q, mla_keys_values
 
 def gather_slots(pool, slots):
     """Records of the listed slots: pool (pages, page_size, 1, w) -> (n, w)
-    for the non-negative entries of `slots`, in list order."""
+    for the entries of `slots` inside the pool, in list order."""
     pool = np.asarray(pool)
     flat = pool.reshape(pool.shape[0] * pool.shape[1], pool.shape[-1])
     s = np.asarray(slots)
-    s = s[s >= 0]
-    if s.size and s.max() >= flat.shape[0]:
-        raise IndexError("slot past the pool")
+    s = s[(s >= 0) & (s < flat.shape[0])]
     return flat[s]
 
 

@@ -4,7 +4,6 @@ test_oracle.py), the closed form of the attention sink, a pure-Python brute
 force, order and split invariance, and the empty cases. CPU only."""
 
 import numpy as np
-import pytest
 
 from oracle import attention as A
 from oracle import brute, merge
@@ -124,9 +123,15 @@ def test_empty_lists():
     assert np.all(o == 0) and np.array_equal(lse, np.broadcast_to(sink, (2, 16)))
 
 
-def test_slot_past_the_pool_is_an_error():
+def test_a_slot_past_the_pool_names_no_key():
     rng = np.random.default_rng(11)
     p = pool(rng, 2, 16)
-    with pytest.raises(IndexError):
-        sparse_decode_attention(_bf16_bits(rng, (1, 16, 576)), [dict(p, slots=np.array([[32]], np.int32))],
-                                softmax_scale=0.1)
+    q = _bf16_bits(rng, (1, 16, 576))
+    past = np.array([[3, 32, 7, 5000]], np.int32)
+    neg = np.array([[3, -1, 7, -1]], np.int32)
+    o1, l1 = sparse_decode_attention(q, [dict(p, slots=past)], softmax_scale=0.1)
+    o2, l2 = sparse_decode_attention(q, [dict(p, slots=neg)], softmax_scale=0.1)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    ob, lb = brute.brute_sparse_decode(q.tolist(), [{k: v.tolist() for k, v in dict(p, slots=past).items()}],
+                                       0.1, 1.0, None)
+    np.testing.assert_allclose(o1, np.array(ob), rtol=0, atol=1e-12)
