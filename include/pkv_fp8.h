@@ -31,6 +31,8 @@
  *      they never allocate, never synchronise and are capturable in a HIP
  *      graph; a plan made for upper-bound lengths stays valid for shorter
  *      runtime seq_lens.
+ * The sparse slot-list decode needs no plan: pkv_sparse_decode() with a
+ * workspace of pkv_sparse_workspace_bytes() (declared at the end).
  *
  * Ownership. The caller owns every buffer; the library keeps no state
  * between calls and never frees or retains a pointer. Device pointers are
@@ -459,6 +461,75 @@ pkv_status pkv_write_kv(const pkv_kv_write_args* a, void* stream);
 
 /* sizeof(pkv_kv_write_args) in this build (a binding's layout check) */
 size_t pkv_kv_write_args_size(void);
+
+/* ------------------------------------------------------------------------ */
+/* Sparse slot-list decode over latent records                               */
+/* ------------------------------------------------------------------------ */
+/*
+ * "vLLM PR #62633: swap-AB CuTe DSL decode attention for DeepSeek-V4.1",
+ * Kernel design: each decode token attends to the records named by its slot
+ * lists (a sliding-window list and a top-k list of compressed records), the
+ * record serving as key and value (S = KV Q^T, O = KV^T P, P split into bf16
+ * hi and lo parts), and the token's tile partials are merged together with
+ * a per-head attention sink. The record is the latent record of PKV_KV_MLA
+ * (512 e4m3 codes, one fp32 scale per 128 codes, 64 bf16 rope values); the
+ * model's own record format is not built.
+ *
+ * For token t and head h, over the non-negative entries s of both lists
+ * (a slot is row s % page_size of page s / page_size of that list's pool;
+ * an entry listed twice counts twice):
+ *   z_s = softmax_scale * <q[t][h], key_s>
+ *   Z   = sum_s exp(z_s) + exp(sink[h])            (no sink term if sink == NULL)
+ *   o[t][h]   = o_scale * sum_s exp(z_s) value_s / Z   (bf16)
+ *   lse[t][h] = log Z   (natural log; O = 0 and LSE = -inf when Z = 0)
+ */
+typedef struct pkv_sparse_list {
+  const uint8_t* latent;    /* [num_pages][page_size] records: 512 e4m3 codes (bytes) */
+  int64_t lat_page_stride, lat_row_stride;        /* bytes */
+  const uint16_t* rope;     /* [num_pages][page_size][64] bf16 */
+  int64_t rope_page_stride, rope_row_stride;      /* bf16 elements */
+  const float* blk_scale;   /* [num_pages][page_size][4] fp32 */
+  int64_t scale_page_stride, scale_row_stride;    /* fp32 elements */
+  int32_t page_size;        /* 16, 32, 64 or 128 */
+  int32_t num_pages;
+  const int32_t* slots;     /* device [num_tokens][width] int32, row stride slots_row_stride; < 0: none */
+  int64_t slots_row_stride;
+  int32_t width;            /* entries per token, 0 .. 4096; 0 = list unused (pointers may be NULL) */
+} pkv_sparse_list;
+
+typedef struct pkv_sparse_args {
+  int32_t num_tokens;       /* decode tokens, 1 .. 65535 */
+  int32_t h_q;              /* query heads, a multiple of 16, <= 128 */
+  const uint16_t* q;        /* [num_tokens][h_q][576] bf16 (q_tok_stride, q_head_stride in elements) */
+  int64_t q_tok_stride, q_head_stride;
+  /* list 0: sliding window, processed in tiles of 64 slots; list 1: top-k
+   * compressed records, tiles of 128 slots (the page's tile sizes) */
+  pkv_sparse_list list[2];
+  const float* sink;        /* device [h_q] fp32 logits in scaled-score units, or NULL */
+  float softmax_scale, o_scale;
+  uint16_t* o;              /* [num_tokens][h_q][512] bf16 (o_tok_stride, o_head_stride in elements) */
+  int64_t o_tok_stride, o_head_stride;
+  float* lse;               /* device [num_tokens][h_q] fp32, contiguous */
+  void* workspace;          /* >= pkv_sparse_workspace_bytes(a) bytes, 256-B aligned, never initialised */
+  int64_t workspace_bytes;
+} pkv_sparse_args;
+
+/* Bytes of tile partials one call needs: tiles * num_tokens * h_q * (512 + 2)
+ * fp32, tiles = ceil(width0 / 64) + ceil(width1 / 128); 0 on invalid args. */
+int64_t pkv_sparse_workspace_bytes(const pkv_sparse_args* a);
+
+/* Two launches on `stream` (a hipStream_t; NULL = default stream): the tile
+ * kernel (one workgroup per (token, tile, 16 or 32 heads), tile partials to
+ * the workspace) and the merge (partials in tile order, list 0 first, plus
+ * the sink). Allocates nothing, does not synchronise. Errors before any
+ * launch: PKV_ERR_INVALID_ARG (NULL or misaligned pointers, bad strides or
+ * sizes), PKV_ERR_UNSUPPORTED (page size, h_q, width limits),
+ * PKV_ERR_WORKSPACE (missing or short workspace), PKV_ERR_HIP (a launch
+ * failed). Slots past a pool are treated as absent (never read). */
+pkv_status pkv_sparse_decode(const pkv_sparse_args* a, void* stream);
+
+/* sizeof(pkv_sparse_args) in this build (a binding's layout check) */
+size_t pkv_sparse_args_size(void);
 
 #ifdef __cplusplus
 } /* extern "C" */

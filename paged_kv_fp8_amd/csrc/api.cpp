@@ -278,3 +278,68 @@ extern "C" pkv_status pkv_write_kv(const pkv_kv_write_args* a, void* stream) {
 extern "C" size_t pkv_quant_q_args_size(void) { return sizeof(pkv_quant_q_args); }
 
 extern "C" size_t pkv_kv_write_args_size(void) { return sizeof(pkv_kv_write_args); }
+
+namespace {
+// Checks of one slot list of a sparse decode call (nothing is read when the
+// list is unused).
+pkv_status check_sparse_list(const pkv_sparse_list& l, int idx) {
+  if (l.width < 0) return fail(PKV_ERR_INVALID_ARG, "list[%d].width=%d < 0", idx, l.width);
+  if (l.width == 0) return PKV_OK;
+  if (l.width > 4096) return fail(PKV_ERR_UNSUPPORTED, "list[%d].width=%d > 4096", idx, l.width);
+  if (!pow2_page(l.page_size))
+    return fail(PKV_ERR_UNSUPPORTED, "list[%d].page_size=%d not in {16,32,64,128}", idx, l.page_size);
+  if (l.num_pages < 1 || (int64_t)l.num_pages * l.page_size >= (int64_t{1} << 31))
+    return fail(PKV_ERR_INVALID_ARG, "list[%d].num_pages=%d: need 1 <= num_pages * page_size < 2^31", idx,
+                l.num_pages);
+  if (!l.latent || !l.rope || !l.blk_scale || !l.slots)
+    return fail(PKV_ERR_INVALID_ARG, "list[%d]: latent, rope, blk_scale and slots must be non-NULL", idx);
+  if (!aligned(l.latent, 16) || bad_elem_stride(l.lat_page_stride, 16) || bad_elem_stride(l.lat_row_stride, 16))
+    return fail(PKV_ERR_INVALID_ARG, "list[%d].latent must be 16-B aligned with 16-B multiple strides", idx);
+  if (!aligned(l.rope, 16) || bad_elem_stride(l.rope_page_stride, 8) || bad_elem_stride(l.rope_row_stride, 8))
+    return fail(PKV_ERR_INVALID_ARG, "list[%d].rope must be 16-B aligned with strides of 8 elements", idx);
+  if (!aligned(l.blk_scale, 8) || bad_elem_stride(l.scale_page_stride, 2) || bad_elem_stride(l.scale_row_stride, 2))
+    return fail(PKV_ERR_INVALID_ARG, "list[%d].blk_scale must be 8-B aligned with even strides", idx);
+  if (!aligned(l.slots, 4) || l.slots_row_stride < l.width)
+    return fail(PKV_ERR_INVALID_ARG, "list[%d].slots must be 4-B aligned with row stride >= width", idx);
+  return PKV_OK;
+}
+
+pkv_status check_sparse(const pkv_sparse_args* a) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "args is NULL");
+  if (a->num_tokens < 1 || a->h_q < 1)
+    return fail(PKV_ERR_INVALID_ARG, "num_tokens=%d h_q=%d must be >= 1", a->num_tokens, a->h_q);
+  if (a->h_q % 16 || a->h_q > 128) return fail(PKV_ERR_UNSUPPORTED, "h_q=%d: a multiple of 16 up to 128", a->h_q);
+  if (a->num_tokens > 65535) return fail(PKV_ERR_UNSUPPORTED, "num_tokens=%d > 65535", a->num_tokens);
+  if (!std::isfinite(a->softmax_scale) || !std::isfinite(a->o_scale))
+    return fail(PKV_ERR_INVALID_ARG, "softmax_scale and o_scale must be finite");
+  if (!a->q || !a->o || !a->lse) return fail(PKV_ERR_INVALID_ARG, "q, o and lse must be non-NULL");
+  if (!aligned(a->q, 16) || bad_elem_stride(a->q_tok_stride, 8) || bad_elem_stride(a->q_head_stride, 8))
+    return fail(PKV_ERR_INVALID_ARG, "q must be 16-B aligned with strides that are multiples of 8 elements");
+  if (!aligned(a->o, 8) || bad_elem_stride(a->o_tok_stride, 4) || bad_elem_stride(a->o_head_stride, 4))
+    return fail(PKV_ERR_INVALID_ARG, "o must be 8-B aligned with strides that are multiples of 4 elements");
+  if (!aligned(a->lse, 4)) return fail(PKV_ERR_INVALID_ARG, "lse must be 4-B aligned");
+  if (a->sink && !aligned(a->sink, 4)) return fail(PKV_ERR_INVALID_ARG, "sink must be 4-B aligned");
+  for (int i = 0; i < 2; ++i) {
+    const pkv_status st = check_sparse_list(a->list[i], i);
+    if (st != PKV_OK) return st;
+  }
+  return PKV_OK;
+}
+}  // namespace
+
+extern "C" int64_t pkv_sparse_workspace_bytes(const pkv_sparse_args* a) {
+  if (check_sparse(a) != PKV_OK) return 0;
+  return sparse_ws_bytes(*a);
+}
+
+extern "C" pkv_status pkv_sparse_decode(const pkv_sparse_args* a, void* stream) {
+  pkv_status st = check_sparse(a);
+  if (st != PKV_OK) return st;
+  const int64_t need = sparse_ws_bytes(*a);
+  if (need > 0 && (!a->workspace || !aligned(a->workspace, 256) || a->workspace_bytes < need))
+    return fail(PKV_ERR_WORKSPACE, "workspace: %lld bytes needed, 256-B aligned (got %lld)", (long long)need,
+                (long long)a->workspace_bytes);
+  return hip_status(sparse_launch(*a, static_cast<hipStream_t>(stream)), "sparse decode launch");
+}
+
+extern "C" size_t pkv_sparse_args_size(void) { return sizeof(pkv_sparse_args); }

@@ -688,6 +688,269 @@ void mla_pair_kernel(MlaParams p, int groups) {
   }
 }
 
+// ---- sparse slot-list form ------------------------------------------------------
+// The decode of "vLLM PR #62633" (Kernel design) on these records: every
+// decode token lists the slots it attends to (a sliding-window list and a
+// top-k list, each over its own record pool); one workgroup per (tile of a
+// list, 16 or 32 heads, token) runs the pair form over the tile's slots and
+// writes a partial; the merge below combines a token's partials with the
+// attention sink. Differences from the pair form:
+//  * a key's record address comes from its list entry (a slot = page *
+//    page_size + row): lane r16 of each 16-key block loads entry kb + r16
+//    (a vector load, kPageAhead fetches ahead, as the pair form's page
+//    entries), so every load has a per-lane 64-bit address;
+//  * absent keys (a negative entry, one past the pool, or past the tile) read
+//    slot 0 and are zeroed after the load (codes and scales, so no NaN from a
+//    poisoned slot reaches PV) and masked to -inf;
+//  * P * scale is split into a bf16 hi part and the bf16 rounding of the rest
+//    (lo), and PV runs on both, so P enters the product with ~16 bits;
+//  * no causal limit (every head sees every listed key) and always partials.
+constexpr int kSparseTile0 = 64;   // sliding-window list: slots per tile
+constexpr int kSparseTile1 = 128;  // top-k list
+
+struct SparseList {
+  const uint8_t* lat;
+  int64_t lat_page, lat_row;  // bytes
+  const uint8_t* rope;
+  int64_t rope_page, rope_row;  // bytes
+  const uint8_t* scl;
+  int64_t scl_page, scl_row;  // bytes
+  const int32_t* slots;
+  int64_t slots_row;  // elements
+  int width, page_shift, num_slots;
+};
+
+struct SparseParams {
+  const uint8_t* q;
+  int64_t q_tok, q_head;  // bytes
+  SparseList list[2];
+  const float* sink;
+  uint8_t* o;
+  int64_t o_tok, o_head;  // bytes
+  float* lse;
+  float* ws_o;    // [tiles][num_tokens][h_q][512]
+  float2* ws_ml;  // [tiles][num_tokens][h_q]: (max in natural-log units, sum)
+  float scale_log2e, scale, o_scale;
+  int num_tokens, h_q, tiles0, tiles;
+};
+
+template <int HALF>
+__device__ __forceinline__ void sparse_pair_item(const SparseParams& p, int tile, int rtile, int t, int groups,
+                                                 uint8_t* lds) {
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+  const int grp = w >> 1;
+
+  const bool second = tile >= p.tiles0;
+  const SparseList& L = second ? p.list[1] : p.list[0];
+  const int j_begin = second ? (tile - p.tiles0) * kSparseTile1 : tile * kSparseTile0;
+  const int j_end = min(j_begin + (second ? kSparseTile1 : kSparseTile0), L.width);
+  const int32_t* list = L.slots + (int64_t)t * L.slots_row;
+  const int pmask = (1 << L.page_shift) - 1;
+
+  constexpr int kPageAhead = kPairStages - 1;
+  // list entry of this lane's key in block kb (lanes of one key load the same entry)
+  auto entry = [&](int kb) -> int { return list[min(kb + r16, j_end - 1)]; };
+  int sv_ring[kPairStages];
+  for (int u = 0; u < kPageAhead; ++u) sv_ring[u] = entry(j_begin + kBlockKeys * u);
+
+  const int n = (rtile * groups + grp) * 16 + r16;  // query head; h_q is a multiple of 16
+  bf16x8 qreg[kPairQSteps];
+  {
+    const uint8_t* qrow = p.q + (int64_t)t * p.q_tok + (int64_t)n * p.q_head;
+    for (int k = 0; k < kPairQSteps; ++k) {
+      const int blk = 2 * HALF + (k >> 2), s = k & 3;
+      const int d = k < 8 ? 128 * blk + 64 * (s >> 1) + 16 * g4 + 8 * (s & 1) : kLatent + 32 * HALF + 8 * g4;
+      qreg[k] = *reinterpret_cast<const bf16x8*>(qrow + 2 * d);
+    }
+  }
+  const float c2 = p.scale_log2e;
+
+  uint8_t* const wl = lds + w * kPairWaveBytes;
+  uint8_t* const xl = lds + (w ^ 1) * kPairWaveBytes + kPairX;
+  bf16x8(*qw)[64] = reinterpret_cast<bf16x8(*)[64]>(wl);
+  for (int k = 0; k < kPairQSteps; ++k) qw[k][lane] = qreg[k];
+
+  f32x4 oacc[2][8];
+  for (int j = 0; j < 2; ++j)
+    for (int mt = 0; mt < 8; ++mt) oacc[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
+
+  if (j_end > j_begin) {
+    struct Fetched {
+      HalfRec r;
+      bool ok;
+    };
+    auto load_block = [&](int kb, int sv) {
+      Fetched f;
+      f.ok = kb + r16 < j_end && sv >= 0 && sv < L.num_slots;
+      const int s = f.ok ? sv : 0;
+      const int64_t pg = s >> L.page_shift;
+      const int row = s & pmask;
+      const uint8_t* lr = L.lat + pg * L.lat_page + (int64_t)row * L.lat_row + 256 * HALF;
+      for (int j = 0; j < 2; ++j)
+        for (int h = 0; h < 2; ++h) f.r.kl[j][h] = *reinterpret_cast<const uint4*>(lr + 128 * j + 64 * h + 16 * g4);
+      f.r.kr = *reinterpret_cast<const uint4*>(L.rope + pg * L.rope_page + (int64_t)row * L.rope_row +
+                                               2 * (32 * HALF + 8 * g4));
+      f.r.sc = *reinterpret_cast<const float2*>(L.scl + pg * L.scl_page + (int64_t)row * L.scl_row + 8 * HALF);
+      return f;
+    };
+    auto fetch = [&](Fetched& f, int kb, const int s) {
+      f = load_block(kb, sv_ring[s]);
+      sv_ring[(s + kPageAhead) % kPairStages] = entry(kb + kPageAhead * kBlockKeys);
+    };
+
+    const int tr_base = hrow_base(4 * g4 + (r16 >> 2), 8 * (r16 & 3));
+    auto process = [&](const Fetched& cur, int kb, const int xs) {
+      asm volatile("" ::: "memory");
+      // keys 4 g4 + i of this block that exist (ballot of the lanes r16 = key, g4 = 0)
+      const uint64_t okm = __builtin_amdgcn_ballot_w64(cur.ok);
+      HalfRec r = cur.r;
+      if (!cur.ok) {  // a select on loaded values: no conditional load
+        for (int j = 0; j < 2; ++j)
+          for (int h = 0; h < 2; ++h) r.kl[j][h] = uint4{0u, 0u, 0u, 0u};
+        r.kr = uint4{0u, 0u, 0u, 0u};
+        r.sc = float2{0.f, 0.f};
+      }
+      *reinterpret_cast<float2*>(wl + kPairScl + 8 * r16) = r.sc;
+      f32x4 acc[2];
+      for (int j = 0; j < 2; ++j) {
+        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 a = e4m3x8_to_bf16(half_of(r.kl[j][s >> 1], s & 1));
+          *reinterpret_cast<bf16x8*>(wl + kPairV + hrow_base(r16, 32 * g4 + 16 * (s & 1)) + 256 * j +
+                                     128 * (s >> 1)) = a;
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qw[4 * j + s][lane], acc[j], 0, 0, 0);
+        }
+      }
+      const f32x4 accr =
+          __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.kr), qw[8][lane], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      asm volatile("" ::: "memory");
+      float2 scl[4];
+      for (int i = 0; i < 4; ++i) scl[i] = *reinterpret_cast<const float2*>(wl + kPairScl + 8 * (4 * g4 + i));
+      f32x4 part;
+      for (int i = 0; i < 4; ++i) part[i] = accr[i] + scl[i].x * acc[0][i] + scl[i].y * acc[1][i];
+      *reinterpret_cast<f32x4*>(wl + kPairX + xs * 1024 + 16 * lane) = part;
+      __syncthreads();
+      const f32x4 other = *reinterpret_cast<const f32x4*>(xl + xs * 1024 + 16 * lane);
+      float sv[4];
+      for (int i = 0; i < 4; ++i) sv[i] = ((okm >> (4 * g4 + i)) & 1) ? part[i] + other[i] : -INFINITY;
+      // ---- online softmax (the reference max may lag, as in the pair form) ----
+      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      mx = pair32(pair16(mx, true), true);
+      const float m_max = fmaxf(m_run, mx);
+      const bool move = m_run == -INFINITY ? m_max != -INFINITY : (m_max - m_run) * c2 > kLazyLog2;
+      const float m_new = move ? m_max : m_run;
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float corr = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
+      float pr[4], psum = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f((sv[i] - m_use) * c2);
+        psum += pr[i];
+      }
+      l_part = l_part * corr + psum;
+      if (__builtin_amdgcn_ballot_w64(move)) {
+        for (int j = 0; j < 2; ++j)
+          for (int mt = 0; mt < 8; ++mt) oacc[j][mt] *= corr;
+      }
+      m_run = m_new;
+      // ---- O^T += V^T (P * scale)^T, P * scale = hi + lo in bf16 -----------------
+      for (int j = 0; j < 2; ++j) {
+        bf16x4 ph, pl;
+        for (int i = 0; i < 4; ++i) {
+          const float v = pr[i] * (j ? scl[i].y : scl[i].x);
+          ph[i] = (__bf16)v;
+          pl[i] = (__bf16)(v - (float)ph[i]);
+        }
+        bf16x4 a[8];
+        for (int mt = 0; mt < 8; ++mt) {
+          const s16x4 t4 = lds_read_tr16(wl + kPairV + tr_base + 256 * j + 32 * mt);
+          __builtin_memcpy(&a[mt], &t4, 8);
+        }
+        for (int mt = 0; mt < 8; ++mt)
+          oacc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[mt], ph, oacc[j][mt], 0, 0, 0);
+        for (int mt = 0; mt < 8; ++mt)
+          oacc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[mt], pl, oacc[j][mt], 0, 0, 0);
+      }
+    };
+
+    Fetched ring[kPairStages];
+#pragma unroll
+    for (int s = 0; s < kPairStages - 1; ++s) {
+      fetch(ring[s], j_begin + kBlockKeys * s, s);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int rounds = (j_end - j_begin + kBlockKeys * kPairStages - 1) / (kBlockKeys * kPairStages);
+    for (int r = 0; r < rounds; ++r) {
+      const int kb0 = j_begin + r * kBlockKeys * kPairStages;
+#pragma unroll
+      for (int s = 0; s < kPairStages; ++s) {
+        const int kb = kb0 + kBlockKeys * s;
+        fetch(ring[(s + kPairStages - 1) % kPairStages], kb + kBlockKeys * (kPairStages - 1),
+              (s + kPairStages - 1) % kPairStages);
+        process(ring[s], kb, s & 1);
+      }
+    }
+  }
+
+  // ---- epilogue: the tile's partial (this wave's d_v half) -------------------------
+  const float l = pair32(pair16(l_part, false), false);
+  const int64_t prow = ((int64_t)tile * p.num_tokens + t) * p.h_q + n;
+  const float m_nat = m_run == -INFINITY ? -INFINITY : m_run * p.scale;
+  float* dst = p.ws_o + prow * kDv + 256 * HALF + 4 * g4;
+  for (int j = 0; j < 2; ++j)
+    for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(dst + 128 * j + 16 * mt) = oacc[j][mt];
+  if (HALF == 0 && g4 == 0) p.ws_ml[prow] = float2{m_nat, l};
+}
+
+// Grid (tiles, head tiles of 16 * groups heads, tokens); block 128 * groups.
+__global__ __launch_bounds__(128 * kPairMaxGroups) __attribute__((amdgpu_waves_per_eu(2)))
+void sparse_pair_kernel(SparseParams p, int groups) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t sparse_pair_lds[];
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1)
+    sparse_pair_item<1>(p, blockIdx.x, blockIdx.y, blockIdx.z, groups, sparse_pair_lds);
+  else
+    sparse_pair_item<0>(p, blockIdx.x, blockIdx.y, blockIdx.z, groups, sparse_pair_lds);
+}
+
+// Combine of a token's tile partials, in tile order (list 0, then list 1),
+// with the sink as one more term of the denominator (the LSE merge of the
+// split-KV path plus a partial with O = 0, max = sink, sum = 1). One thread
+// per (token, head, 4 d_v).
+__global__ __launch_bounds__(256) void sparse_merge_kernel(SparseParams p) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rows = (int64_t)p.num_tokens * p.h_q;
+  if (id >= rows * (kDv / 4)) return;
+  const int64_t row = id / (kDv / 4);  // t * h_q + h
+  const int d = (int)(id - row * (kDv / 4)) * 4;
+  const int h = (int)(row % p.h_q);
+  const int t = (int)(row / p.h_q);
+  const float sink = p.sink ? p.sink[h] : -INFINITY;
+  float m_star = sink;
+  for (int i = 0; i < p.tiles; ++i) {
+    const float2 ml = p.ws_ml[(int64_t)i * rows + row];
+    if (ml.y > 0.f) m_star = fmaxf(m_star, ml.x);
+  }
+  float den = 0.f;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < p.tiles; ++i) {
+    const float2 ml = p.ws_ml[(int64_t)i * rows + row];
+    if (!(ml.y > 0.f)) continue;
+    const float wgt = expf(ml.x - m_star);
+    den += wgt * ml.y;
+    num += wgt * *reinterpret_cast<const f32x4*>(p.ws_o + ((int64_t)i * rows + row) * kDv + d);
+  }
+  if (p.sink) den += expf(sink - m_star);
+  const float inv = den > 0.f ? p.o_scale / den : 0.f;
+  bf16x4 out;
+  for (int e = 0; e < 4; ++e) out[e] = (__bf16)(num[e] * inv);
+  *reinterpret_cast<bf16x4*>(p.o + (int64_t)t * p.o_tok + (int64_t)h * p.o_head + 2 * d) = out;
+  if (d == 0) p.lse[row] = den > 0.f ? m_star + logf(den) : -INFINITY;
+}
+
 // rows >= 64: the staged form; fewer rows: the pair form
 bool staged(const pkv_decode_args& a) { return a.q_len * a.h_q >= kLdsRows; }
 
@@ -780,6 +1043,67 @@ hipError_t mla_launch(const pkv_decode_args& a, hipStream_t stream) {
   void* args[] = {&p, &groups};
   return hipLaunchKernel(select_kernel(a), dim3((unsigned)units, (unsigned)tiles), dim3(64 * wpw), args,
                          dyn_lds_bytes(a), stream);
+}
+
+int sparse_tiles(const pkv_sparse_args& a) {
+  return (a.list[0].width + kSparseTile0 - 1) / kSparseTile0 + (a.list[1].width + kSparseTile1 - 1) / kSparseTile1;
+}
+
+int64_t sparse_ws_bytes(const pkv_sparse_args& a) {
+  return (int64_t)sparse_tiles(a) * a.num_tokens * a.h_q * (kDv + 2) * 4;
+}
+
+hipError_t sparse_launch(const pkv_sparse_args& a, hipStream_t stream) {
+  SparseParams p;
+  p.q = reinterpret_cast<const uint8_t*>(a.q);
+  p.q_tok = a.q_tok_stride * 2;
+  p.q_head = a.q_head_stride * 2;
+  for (int i = 0; i < 2; ++i) {
+    const pkv_sparse_list& s = a.list[i];
+    SparseList& d = p.list[i];
+    d.lat = s.latent;
+    d.lat_page = s.lat_page_stride;
+    d.lat_row = s.lat_row_stride;
+    d.rope = reinterpret_cast<const uint8_t*>(s.rope);
+    d.rope_page = s.rope_page_stride * 2;
+    d.rope_row = s.rope_row_stride * 2;
+    d.scl = reinterpret_cast<const uint8_t*>(s.blk_scale);
+    d.scl_page = s.scale_page_stride * 4;
+    d.scl_row = s.scale_row_stride * 4;
+    d.slots = s.slots;
+    d.slots_row = s.slots_row_stride;
+    d.width = s.width;
+    d.page_shift = s.width > 0 ? log2_exact(s.page_size) : 0;
+    d.num_slots = s.width > 0 ? s.num_pages * s.page_size : 0;
+  }
+  p.sink = a.sink;
+  p.o = reinterpret_cast<uint8_t*>(a.o);
+  p.o_tok = a.o_tok_stride * 2;
+  p.o_head = a.o_head_stride * 2;
+  p.lse = a.lse;
+  const int tiles = sparse_tiles(a);
+  const int64_t rows = (int64_t)a.num_tokens * a.h_q;
+  p.ws_o = static_cast<float*>(a.workspace);
+  p.ws_ml = reinterpret_cast<float2*>(p.ws_o + (int64_t)tiles * rows * kDv);
+  p.scale_log2e = (float)((double)a.softmax_scale * 1.4426950408889634);
+  p.scale = a.softmax_scale;
+  p.o_scale = a.o_scale;
+  p.num_tokens = a.num_tokens;
+  p.h_q = a.h_q;
+  p.tiles0 = (a.list[0].width + kSparseTile0 - 1) / kSparseTile0;
+  p.tiles = tiles;
+  if (tiles > 0) {
+    int groups = a.h_q % 32 == 0 ? 2 : 1;
+    void* args[] = {&p, &groups};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&sparse_pair_kernel),
+                                         dim3((unsigned)tiles, (unsigned)(a.h_q / (16 * groups)), (unsigned)a.num_tokens),
+                                         dim3(128 * groups), args, (size_t)2 * groups * kPairWaveBytes, stream);
+    if (e != hipSuccess) return e;
+  }
+  void* margs[] = {&p};
+  const int64_t threads = rows * (kDv / 4);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&sparse_merge_kernel), dim3((unsigned)((threads + 255) / 256)),
+                         dim3(256), margs, 0, stream);
 }
 
 }  // namespace pkv

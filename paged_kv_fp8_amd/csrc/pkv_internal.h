@@ -40,6 +40,11 @@ const char* mla_kernel_name(const pkv_decode_args& a);  // "mla_pair_kernel" or 
 hipError_t mla_occupancy(const pkv_decode_args& a, int* wg_per_cu);
 hipError_t mla_launch(const pkv_decode_args& a, hipStream_t stream);
 
+// Sparse slot-list decode over latent records (tile kernel + merge).
+int sparse_tiles(const pkv_sparse_args& a);
+int64_t sparse_ws_bytes(const pkv_sparse_args& a);
+hipError_t sparse_launch(const pkv_sparse_args& a, hipStream_t stream);
+
 // Combine of split partials.
 hipError_t merge_launch(const pkv_decode_args& a, hipStream_t stream);
 hipError_t quantize_q_launch(const pkv_quant_q_args& a, hipStream_t stream);

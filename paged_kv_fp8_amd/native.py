@@ -22,7 +22,7 @@ PKV_MAX_SPLITS = 256
 EXPORTS = ("pkv_status_string", "pkv_last_error", "pkv_version", "pkv_decode_args_size", "pkv_plan_split_kv",
            "pkv_plan_balanced", "pkv_plan_queued", "pkv_workspace_bytes", "pkv_decode_slots", "pkv_paged_decode_attn",
            "pkv_merge_splits", "pkv_quantize_q", "pkv_quant_q_args_size", "pkv_write_kv", "pkv_kv_write_args_size",
-           "pkv_decode_kernel_name")
+           "pkv_decode_kernel_name", "pkv_sparse_workspace_bytes", "pkv_sparse_decode", "pkv_sparse_args_size")
 
 
 class PkvError(RuntimeError):
@@ -97,6 +97,32 @@ class KvWriteArgs(ctypes.Structure):
                 ("scale_row_stride", ctypes.c_int64)]
 
 
+class SparseList(ctypes.Structure):
+    """Mirror of ``pkv_sparse_list``."""
+    _fields_ = [
+        ("latent", _vp), ("lat_page_stride", _i64), ("lat_row_stride", _i64),
+        ("rope", _vp), ("rope_page_stride", _i64), ("rope_row_stride", _i64),
+        ("blk_scale", _vp), ("scale_page_stride", _i64), ("scale_row_stride", _i64),
+        ("page_size", _i32), ("num_pages", _i32),
+        ("slots", _vp), ("slots_row_stride", _i64),
+        ("width", _i32),
+    ]
+
+
+class SparseArgs(ctypes.Structure):
+    """Mirror of ``pkv_sparse_args``."""
+    _fields_ = [
+        ("num_tokens", _i32), ("h_q", _i32),
+        ("q", _vp), ("q_tok_stride", _i64), ("q_head_stride", _i64),
+        ("list", SparseList * 2),
+        ("sink", _vp),
+        ("softmax_scale", _f32), ("o_scale", _f32),
+        ("o", _vp), ("o_tok_stride", _i64), ("o_head_stride", _i64),
+        ("lse", _vp),
+        ("workspace", _vp), ("workspace_bytes", _i64),
+    ]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run `python -m paged_kv_fp8_amd.build`")
@@ -133,7 +159,13 @@ def _load():
     lib.pkv_write_kv.restype = _i32
     lib.pkv_write_kv.argtypes = [P(KvWriteArgs), _vp]
     lib.pkv_kv_write_args_size.restype = ctypes.c_size_t
-    for name, st in (("pkv_quant_q_args_size", QuantQArgs), ("pkv_kv_write_args_size", KvWriteArgs)):
+    lib.pkv_sparse_workspace_bytes.restype = _i64
+    lib.pkv_sparse_workspace_bytes.argtypes = [P(SparseArgs)]
+    lib.pkv_sparse_decode.restype = _i32
+    lib.pkv_sparse_decode.argtypes = [P(SparseArgs), _vp]
+    lib.pkv_sparse_args_size.restype = ctypes.c_size_t
+    for name, st in (("pkv_quant_q_args_size", QuantQArgs), ("pkv_kv_write_args_size", KvWriteArgs),
+                     ("pkv_sparse_args_size", SparseArgs)):
         if getattr(lib, name)() != ctypes.sizeof(st):
             raise ImportError(f"{st.__doc__} layout mismatch: library {getattr(lib, name)()} B, "
                               f"binding {ctypes.sizeof(st)} B")
@@ -252,3 +284,11 @@ def quantize_q(args, stream=None):
 
 def write_kv(args, stream=None):
     _check(lib.pkv_write_kv(ctypes.byref(args), stream), "pkv_write_kv")
+
+
+def sparse_workspace_bytes(args):
+    return int(lib.pkv_sparse_workspace_bytes(ctypes.byref(args)))
+
+
+def sparse_decode(args, stream=None):
+    _check(lib.pkv_sparse_decode(ctypes.byref(args), stream), "pkv_sparse_decode")

@@ -315,3 +315,64 @@ def test_write_kv_rejects_invalid_arguments(native, over, code):
 def test_producers_reject_null_args(native):
     assert native.lib.pkv_quantize_q(None, None) == -1
     assert native.lib.pkv_write_kv(None, None) == -1
+
+
+def _sparse_args(native, **over):
+    """A well-formed sparse argument block with fake (never dereferenced)
+    aligned addresses; list fields are set with keys "l0_<field>" / "l1_<field>"."""
+    a = native.SparseArgs()
+    base = 1 << 40
+    a.num_tokens, a.h_q = 4, 16
+    a.q, a.q_tok_stride, a.q_head_stride = base, 16 * 576, 576
+    for i, width in ((0, 128), (1, 512)):
+        l = a.list[i]
+        off = base + ((i + 1) << 32)
+        l.latent, l.lat_page_stride, l.lat_row_stride = off, 64 * 656, 656
+        l.rope, l.rope_page_stride, l.rope_row_stride = off + 512, 64 * 328, 328
+        l.blk_scale, l.scale_page_stride, l.scale_row_stride = off + 640, 64 * 164, 164
+        l.page_size, l.num_pages = 64, 100
+        l.slots, l.slots_row_stride, l.width = off + (1 << 31), width, width
+    a.sink = base + (3 << 32)
+    a.softmax_scale, a.o_scale = 0.04, 1.0
+    a.o, a.o_tok_stride, a.o_head_stride = base + (4 << 32), 16 * 512, 512
+    a.lse = base + (5 << 32)
+    a.workspace = base + (6 << 32)
+    for k, v in over.items():
+        if k.startswith("l0_") or k.startswith("l1_"):
+            setattr(a.list[int(k[1])], k[3:], v)
+        else:
+            setattr(a, k, v)
+    a.workspace_bytes = over.get("workspace_bytes", native.sparse_workspace_bytes(a) or 1)
+    return a
+
+
+def test_sparse_workspace_formula(native):
+    a = _sparse_args(native)
+    tiles = 128 // 64 + 512 // 128
+    assert native.sparse_workspace_bytes(a) == tiles * 4 * 16 * (512 + 2) * 4
+    a = _sparse_args(native, l0_width=65, l1_width=0)
+    assert native.sparse_workspace_bytes(a) == 2 * 4 * 16 * 514 * 4
+    assert native.sparse_workspace_bytes(_sparse_args(native, h_q=24)) == 0  # invalid: 0
+
+
+SPARSE_BAD = [
+    (dict(num_tokens=0), -1), (dict(num_tokens=70000), -2), (dict(h_q=24), -2), (dict(h_q=144), -2), (dict(q=None), -1),
+    (dict(q=(1 << 40) + 8), -1), (dict(o_head_stride=510), -1), (dict(lse=None), -1), (dict(sink=(1 << 40) + 2), -1),
+    (dict(softmax_scale=float("nan")), -1), (dict(l0_width=-1), -1), (dict(l1_width=5000), -2),
+    (dict(l0_page_size=48), -2), (dict(l1_num_pages=0), -1), (dict(l0_slots=None), -1),
+    (dict(l1_latent=(1 << 40) + (2 << 32) + 8), -1), (dict(l0_lat_row_stride=650), -1),
+    (dict(l1_scale_row_stride=163), -1), (dict(l0_slots_row_stride=100), -1),
+    (dict(workspace=None), -4), (dict(workspace_bytes=64), -4),
+]
+
+
+@pytest.mark.parametrize("over,code", SPARSE_BAD)
+def test_sparse_decode_rejects_invalid_arguments_without_touching_the_gpu(native, over, code):
+    st = native.lib.pkv_sparse_decode(ctypes.byref(_sparse_args(native, **over)), None)
+    assert st == code, (over, native.status_string(st), native.last_error())
+    assert native.last_error()
+
+
+def test_sparse_null_args(native):
+    assert native.lib.pkv_sparse_decode(None, None) == native.PKV_ERR_INVALID_ARG
+    assert native.lib.pkv_sparse_workspace_bytes(None) == 0
