@@ -19,7 +19,9 @@ sample of the same batch on the host cores. Diagnostics go to stderr.
 Default workload: 64 sequences, q_len 1, 32 query heads on 8 e4m3 KV heads,
 d = 128, 16-key pages, lengths uniform in [512, 8192], split-KV up to 16
 chunks (``--config 2``). ``--config 1..5`` selects the other workloads; 6, 7
-and 8 are workload 4 with packed fp4 (e2m1), fp6 e2m3 and fp6 e3m2 K/V.
+and 8 are workload 4 with packed fp4 (e2m1), fp6 e2m3 and fp6 e3m2 K/V; 9 is
+the sparse slot-list decode step (its metric: listed record bytes per step
+time).
 """
 
 import argparse
@@ -81,7 +83,7 @@ def measured_traffic(kernel, key):
     since it was taken."""
     import hashlib
 
-    source = "decode_mla.hip" if kernel.startswith("mla_") else "decode_gqa.hip"
+    source = "decode_mla.hip" if kernel.startswith(("mla_", "sparse_")) else "decode_gqa.hip"
     path = os.path.join(ROOT, "profiles", f"{kernel.replace('_kernel', '')}_{key}_hbm_bytes.md")
     src = os.path.join(ROOT, "paged_kv_fp8_amd", "csrc", source)
     if not os.path.exists(path):
@@ -132,6 +134,127 @@ def cpu_oracle_baseline(batch, budget_s):
     return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"first {done} of {w.num_seqs} sequences ({kv} KV bytes, all heads and rows) in {dt:.1f} s, "
                       f"numpy fp64, one BLAS thread"}
+
+
+def sparse_cpu_baseline(batch, budget_s):
+    """The sparse oracle on whole tokens of the batch until the budget is
+    spent; GB/s of listed record bytes."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle.sparse import sparse_decode_attention
+
+    nb = batch.to_numpy()
+    done, kv = 0, 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for t in range(batch.spec.num_tokens):
+            srcs = [dict(s, slots=s["slots"][t:t + 1]) for s in nb["sources"]]
+            sparse_decode_attention(nb["q"][t:t + 1], srcs, softmax_scale=batch.spec.scale, sink=nb["sink"])
+            kv += sum(int((s["slots"] >= 0).sum()) for s in srcs) * 656
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} of {batch.spec.num_tokens} tokens ({kv} record bytes, all heads) in {dt:.1f} s, "
+                      f"numpy fp64, one BLAS thread"}
+
+
+def bench_sparse(args):
+    """The sparse slot-list decode step: tile kernel + merge per step, pools
+    rotated so that the records come from HBM."""
+    import numpy as np
+    import torch
+
+    from paged_kv_fp8_amd import sparse
+    from paged_kv_fp8_amd.workloads import make_sparse_batch, sparse_workload
+
+    w = sparse_workload(9)
+    torch.cuda.set_device(0)
+    first = make_sparse_batch(w, device="cuda")
+    pool_bytes = sum(b.numel() for b in first.kv_buffers)
+    pools = args.pools or min(64, max(3, -(-(1 << 30) // max(1, pool_bytes))))
+    batches = [first] + [make_sparse_batch(dataclasses.replace(w, seed=w.seed + 1000 * i), device="cuda",
+                                           seq_lens=first.seq_lens) for i in range(1, pools)]
+    decs = [sparse.for_batch(b) for b in batches]
+    T = w.num_tokens
+    listed = sum(int((s["slots"] >= 0).sum().item()) for s in first.sources)
+    kv = listed * 656
+    widths = [s["slots"].shape[1] for s in first.sources]
+    tiles = decs[0].tiles
+    alg = {"kv": kv, "q": T * w.h_q * 576 * 2, "lists": T * sum(widths) * 4,
+           "partials": tiles * T * w.h_q * (512 + 2) * 4}
+    alg["total"] = sum(alg.values())
+    flops = listed * w.h_q * (2 * 576 + 2 * 512)
+    log(f"workload {w.name}: {T} tokens, {listed} listed records ({kv / 1e6:.2f} MB), tiles/token {tiles}, "
+        f"pools {pools} ({pool_bytes / 1e6:.0f} MB each)")
+    for i in range(args.warmup):
+        decs[i % pools].run()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(K):
+        d = decs[i % pools]
+        ev[i][0].record()
+        d.run_tiles_only()
+        ev[i][1].record()
+        d.run_merge_only()
+        ev[i][2].record()
+    end.record()
+    torch.cuda.synchronize()
+    eager_ms_step = start.elapsed_time(end) / K
+    tile_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    mrg_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    graphs = []
+    for d in decs:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            d.run()
+        graphs.append(g)
+    for i in range(args.warmup):
+        graphs[i % pools].replay()
+    torch.cuda.synchronize()
+    gstart, gend = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gstart.record()
+    for i in range(K):
+        graphs[i % pools].replay()
+    gend.record()
+    torch.cuda.synchronize()
+    graph_ms_step = gstart.elapsed_time(gend) / K
+    ms_step = graph_ms_step if args.step_mode == "graph" else eager_ms_step
+    value = kv / (ms_step * 1e-3) / 1e9
+    achieved = alg["total"] / (tile_ms * 1e-3) / 1e9
+    t_hbm = alg["total"] / (HBM_PEAK_GBS * 1e9)
+    log(f"step {ms_step * 1e3:.1f} us (tiles {tile_ms * 1e3:.1f} us, merge {mrg_ms * 1e3:.1f} us; graph "
+        f"{graph_ms_step * 1e3:.1f}, eager {eager_ms_step * 1e3:.1f}); records {value:.0f} GB/s; tile kernel "
+        f"{achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.3f} of peak; roofline time {t_hbm * 1e6:.2f} us (hbm)")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = sparse_cpu_baseline(first, args.cpu_seconds)
+        log(f"cpu oracle: {cpu}")
+    kernel = "sparse_pair_kernel"
+    roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(kernel, w.name) if not args.pools else None,
+                "kernel": kernel, "kernel_us": round(tile_ms * 1e3, 2), "algorithmic_bytes_per_launch": alg["total"],
+                "algorithmic_flops_per_launch": flops, "merge_us": round(mrg_ms * 1e3, 2)}
+    line = {
+        "metric": "achieved HBM GB/s (listed record bytes / decode-step time), us per decode step",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "us_per_step": round(ms_step * 1e3, 2), "step_mode": args.step_mode,
+        "us_per_step_eager": round(eager_ms_step * 1e3, 2), "us_per_step_graph": round(graph_ms_step * 1e3, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "num_tokens": T, "q_len": 1, "h_q": w.h_q, "window": w.window,
+                   "topk": w.topk, "compress_ratio": w.compress_ratio, "page_size": list(w.page_size),
+                   "sink": w.sink, "listed_records": listed, "kv_bytes": kv, "tiles_per_token": tiles,
+                   "pools": pools},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
 
 
 def bench_producers(steps):
@@ -216,9 +339,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8],
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9],
                     help="workload: 1-5 as specified; 6, 7, 8 = workload 4 with packed fp4 (e2m1), "
-                         "fp6 e2m3, fp6 e3m2 K/V")
+                         "fp6 e2m3, fp6 e3m2 K/V; 9 = the sparse slot-list decode step (16 tokens, 16 heads, "
+                         "128-slot window + 512 top-k slots)")
     ap.add_argument("--q-len", type=int, default=None, help="query tokens per sequence (latent workload: 1..16)")
     ap.add_argument("--causal", type=int, default=None, help="override the workload's causal flag (0/1)")
     ap.add_argument("--pools", type=int, default=0, help="KV pools to rotate (0: enough for >= 1 GiB, min 3)")
@@ -268,6 +392,9 @@ def main():
         torch.cuda.synchronize()
         log("copied 8 x 256 MiB")
         return
+
+    if args.config == 9:
+        return bench_sparse(args)
 
     from paged_kv_fp8_amd import decode
     from paged_kv_fp8_amd.workloads import make_batch, workload

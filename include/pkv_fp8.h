@@ -502,8 +502,8 @@ typedef struct pkv_sparse_args {
   int32_t h_q;              /* query heads, a multiple of 16, <= 128 */
   const uint16_t* q;        /* [num_tokens][h_q][576] bf16 (q_tok_stride, q_head_stride in elements) */
   int64_t q_tok_stride, q_head_stride;
-  /* list 0: sliding window, processed in tiles of 64 slots; list 1: top-k
-   * compressed records, tiles of 128 slots (the page's tile sizes) */
+  /* list 0: sliding window; list 1: top-k compressed records; each list is
+   * processed in tiles of 64 slots (the page cuts the top-k list into 128) */
   pkv_sparse_list list[2];
   const float* sink;        /* device [h_q] fp32 logits in scaled-score units, or NULL */
   float softmax_scale, o_scale;
@@ -515,7 +515,7 @@ typedef struct pkv_sparse_args {
 } pkv_sparse_args;
 
 /* Bytes of tile partials one call needs: tiles * num_tokens * h_q * (512 + 2)
- * fp32, tiles = ceil(width0 / 64) + ceil(width1 / 128); 0 on invalid args. */
+ * fp32, tiles = ceil(width0 / 64) + ceil(width1 / 64); 0 on invalid args. */
 int64_t pkv_sparse_workspace_bytes(const pkv_sparse_args* a);
 
 /* Two launches on `stream` (a hipStream_t; NULL = default stream): the tile
@@ -527,6 +527,13 @@ int64_t pkv_sparse_workspace_bytes(const pkv_sparse_args* a);
  * PKV_ERR_WORKSPACE (missing or short workspace), PKV_ERR_HIP (a launch
  * failed). Slots past a pool are treated as absent (never read). */
 pkv_status pkv_sparse_decode(const pkv_sparse_args* a, void* stream);
+
+/* The two launches of pkv_sparse_decode separately (same checks, same
+ * errors): the tile kernel, which writes the tile partials to the workspace,
+ * and the merge, which reads them; pkv_sparse_merge must follow a
+ * pkv_sparse_tiles call with the same arguments on the same stream. */
+pkv_status pkv_sparse_tiles(const pkv_sparse_args* a, void* stream);
+pkv_status pkv_sparse_merge(const pkv_sparse_args* a, void* stream);
 
 /* sizeof(pkv_sparse_args) in this build (a binding's layout check) */
 size_t pkv_sparse_args_size(void);

@@ -332,14 +332,28 @@ extern "C" int64_t pkv_sparse_workspace_bytes(const pkv_sparse_args* a) {
   return sparse_ws_bytes(*a);
 }
 
-extern "C" pkv_status pkv_sparse_decode(const pkv_sparse_args* a, void* stream) {
+namespace {
+pkv_status sparse_call(const pkv_sparse_args* a, void* stream, bool tiles, bool merge) {
   pkv_status st = check_sparse(a);
   if (st != PKV_OK) return st;
   const int64_t need = sparse_ws_bytes(*a);
   if (need > 0 && (!a->workspace || !aligned(a->workspace, 256) || a->workspace_bytes < need))
     return fail(PKV_ERR_WORKSPACE, "workspace: %lld bytes needed, 256-B aligned (got %lld)", (long long)need,
                 (long long)a->workspace_bytes);
-  return hip_status(sparse_launch(*a, static_cast<hipStream_t>(stream)), "sparse decode launch");
+  return hip_status(sparse_launch(*a, static_cast<hipStream_t>(stream), tiles, merge), "sparse decode launch");
+}
+}  // namespace
+
+extern "C" pkv_status pkv_sparse_decode(const pkv_sparse_args* a, void* stream) {
+  return sparse_call(a, stream, true, true);
+}
+
+extern "C" pkv_status pkv_sparse_tiles(const pkv_sparse_args* a, void* stream) {
+  return sparse_call(a, stream, true, false);
+}
+
+extern "C" pkv_status pkv_sparse_merge(const pkv_sparse_args* a, void* stream) {
+  return sparse_call(a, stream, false, true);
 }
 
 extern "C" size_t pkv_sparse_args_size(void) { return sizeof(pkv_sparse_args); }

@@ -705,8 +705,12 @@ void mla_pair_kernel(MlaParams p, int groups) {
 //  * P * scale is split into a bf16 hi part and the bf16 rounding of the rest
 //    (lo), and PV runs on both, so P enters the product with ~16 bits;
 //  * no causal limit (every head sees every listed key) and always partials.
-constexpr int kSparseTile0 = 64;   // sliding-window list: slots per tile
-constexpr int kSparseTile1 = 128;  // top-k list
+// Slots per tile of each list: one round of the ring (4 blocks of 16 keys).
+// The page cuts the top-k list into 128-slot tiles (its MMA's M); here both
+// lists use 64, twice the workgroups for a small step and half the chain of
+// dependent loads per workgroup.
+constexpr int kSparseTile0 = 64;  // sliding-window list
+constexpr int kSparseTile1 = 64;  // top-k list
 
 struct SparseList {
   const uint8_t* lat;
@@ -921,6 +925,7 @@ void sparse_pair_kernel(SparseParams p, int groups) {
 // split-KV path plus a partial with O = 0, max = sink, sum = 1). One thread
 // per (token, head, 4 d_v).
 __global__ __launch_bounds__(256) void sparse_merge_kernel(SparseParams p) {
+  constexpr int kRound = 16;  // partials whose (max, sum) and rows are loaded together
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t rows = (int64_t)p.num_tokens * p.h_q;
   if (id >= rows * (kDv / 4)) return;
@@ -929,19 +934,33 @@ __global__ __launch_bounds__(256) void sparse_merge_kernel(SparseParams p) {
   const int h = (int)(row % p.h_q);
   const int t = (int)(row / p.h_q);
   const float sink = p.sink ? p.sink[h] : -INFINITY;
-  float m_star = sink;
-  for (int i = 0; i < p.tiles; ++i) {
-    const float2 ml = p.ws_ml[(int64_t)i * rows + row];
-    if (ml.y > 0.f) m_star = fmaxf(m_star, ml.x);
-  }
-  float den = 0.f;
+  // the running maximum m_star may rise from round to round: sums and rows
+  // gathered so far are rescaled to it (one exp per round)
+  float m_star = sink, den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < p.tiles; ++i) {
-    const float2 ml = p.ws_ml[(int64_t)i * rows + row];
-    if (!(ml.y > 0.f)) continue;
-    const float wgt = expf(ml.x - m_star);
-    den += wgt * ml.y;
-    num += wgt * *reinterpret_cast<const f32x4*>(p.ws_o + ((int64_t)i * rows + row) * kDv + d);
+  for (int i0 = 0; i0 < p.tiles; i0 += kRound) {
+    float2 ml[kRound];
+    f32x4 oj[kRound];
+    for (int k = 0; k < kRound; ++k) {
+      const int i = min(i0 + k, p.tiles - 1);
+      ml[k] = p.ws_ml[(int64_t)i * rows + row];
+      oj[k] = *reinterpret_cast<const f32x4*>(p.ws_o + ((int64_t)i * rows + row) * kDv + d);
+    }
+    float m_round = m_star;
+    for (int k = 0; k < kRound; ++k)
+      if (i0 + k < p.tiles && ml[k].y > 0.f) m_round = fmaxf(m_round, ml[k].x);
+    if (m_round > m_star && m_star != -INFINITY) {
+      const float c = expf(m_star - m_round);
+      den *= c;
+      num *= c;
+    }
+    m_star = m_round;
+    for (int k = 0; k < kRound; ++k) {
+      if (i0 + k >= p.tiles || !(ml[k].y > 0.f)) continue;
+      const float wgt = expf(ml[k].x - m_star);
+      den += wgt * ml[k].y;
+      num += wgt * oj[k];
+    }
   }
   if (p.sink) den += expf(sink - m_star);
   const float inv = den > 0.f ? p.o_scale / den : 0.f;
@@ -1053,7 +1072,7 @@ int64_t sparse_ws_bytes(const pkv_sparse_args& a) {
   return (int64_t)sparse_tiles(a) * a.num_tokens * a.h_q * (kDv + 2) * 4;
 }
 
-hipError_t sparse_launch(const pkv_sparse_args& a, hipStream_t stream) {
+hipError_t sparse_launch(const pkv_sparse_args& a, hipStream_t stream, bool tiles_kernel, bool merge_kernel) {
   SparseParams p;
   p.q = reinterpret_cast<const uint8_t*>(a.q);
   p.q_tok = a.q_tok_stride * 2;
@@ -1092,7 +1111,7 @@ hipError_t sparse_launch(const pkv_sparse_args& a, hipStream_t stream) {
   p.h_q = a.h_q;
   p.tiles0 = (a.list[0].width + kSparseTile0 - 1) / kSparseTile0;
   p.tiles = tiles;
-  if (tiles > 0) {
+  if (tiles > 0 && tiles_kernel) {
     int groups = a.h_q % 32 == 0 ? 2 : 1;
     void* args[] = {&p, &groups};
     const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&sparse_pair_kernel),
@@ -1100,6 +1119,7 @@ hipError_t sparse_launch(const pkv_sparse_args& a, hipStream_t stream) {
                                          dim3(128 * groups), args, (size_t)2 * groups * kPairWaveBytes, stream);
     if (e != hipSuccess) return e;
   }
+  if (!merge_kernel) return hipSuccess;
   void* margs[] = {&p};
   const int64_t threads = rows * (kDv / 4);
   return hipLaunchKernel(reinterpret_cast<const void*>(&sparse_merge_kernel), dim3((unsigned)((threads + 255) / 256)),

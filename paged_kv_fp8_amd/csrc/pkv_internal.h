@@ -43,7 +43,7 @@ hipError_t mla_launch(const pkv_decode_args& a, hipStream_t stream);
 // Sparse slot-list decode over latent records (tile kernel + merge).
 int sparse_tiles(const pkv_sparse_args& a);
 int64_t sparse_ws_bytes(const pkv_sparse_args& a);
-hipError_t sparse_launch(const pkv_sparse_args& a, hipStream_t stream);
+hipError_t sparse_launch(const pkv_sparse_args& a, hipStream_t stream, bool tiles, bool merge);
 
 // Combine of split partials.
 hipError_t merge_launch(const pkv_decode_args& a, hipStream_t stream);

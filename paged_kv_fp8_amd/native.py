@@ -22,7 +22,8 @@ PKV_MAX_SPLITS = 256
 EXPORTS = ("pkv_status_string", "pkv_last_error", "pkv_version", "pkv_decode_args_size", "pkv_plan_split_kv",
            "pkv_plan_balanced", "pkv_plan_queued", "pkv_workspace_bytes", "pkv_decode_slots", "pkv_paged_decode_attn",
            "pkv_merge_splits", "pkv_quantize_q", "pkv_quant_q_args_size", "pkv_write_kv", "pkv_kv_write_args_size",
-           "pkv_decode_kernel_name", "pkv_sparse_workspace_bytes", "pkv_sparse_decode", "pkv_sparse_args_size")
+           "pkv_decode_kernel_name", "pkv_sparse_workspace_bytes", "pkv_sparse_decode", "pkv_sparse_tiles", "pkv_sparse_merge",
+           "pkv_sparse_args_size")
 
 
 class PkvError(RuntimeError):
@@ -161,8 +162,9 @@ def _load():
     lib.pkv_kv_write_args_size.restype = ctypes.c_size_t
     lib.pkv_sparse_workspace_bytes.restype = _i64
     lib.pkv_sparse_workspace_bytes.argtypes = [P(SparseArgs)]
-    lib.pkv_sparse_decode.restype = _i32
-    lib.pkv_sparse_decode.argtypes = [P(SparseArgs), _vp]
+    for name in ("pkv_sparse_decode", "pkv_sparse_tiles", "pkv_sparse_merge"):
+        getattr(lib, name).restype = _i32
+        getattr(lib, name).argtypes = [P(SparseArgs), _vp]
     lib.pkv_sparse_args_size.restype = ctypes.c_size_t
     for name, st in (("pkv_quant_q_args_size", QuantQArgs), ("pkv_kv_write_args_size", KvWriteArgs),
                      ("pkv_sparse_args_size", SparseArgs)):
@@ -292,3 +294,11 @@ def sparse_workspace_bytes(args):
 
 def sparse_decode(args, stream=None):
     _check(lib.pkv_sparse_decode(ctypes.byref(args), stream), "pkv_sparse_decode")
+
+
+def sparse_tiles(args, stream=None):
+    _check(lib.pkv_sparse_tiles(ctypes.byref(args), stream), "pkv_sparse_tiles")
+
+
+def sparse_merge(args, stream=None):
+    _check(lib.pkv_sparse_merge(ctypes.byref(args), stream), "pkv_sparse_merge")

@@ -24,8 +24,8 @@ class SparseDecode:
     """q: (T, h_q, 576) bf16; lists: up to two dicts with "latent" (pages, PS,
     1, 512) uint8 e4m3, "rope" (pages, PS, 1, 64) bf16, "scales" (pages, PS,
     1, 4) float32 views, "slots" (T, width) int32 (flat page * PS + row, < 0
-    = none); list 0 is the sliding window (tiles of 64), list 1 the top-k
-    list (tiles of 128); sink: (h_q,) float32 or None. Allocates O (T, h_q,
+    = none); list 0 is the sliding window, list 1 the top-k list (both in
+    tiles of 64 slots); sink: (h_q,) float32 or None. Allocates O (T, h_q,
     512) bf16, LSE (T, h_q) float32 and the workspace once."""
 
     def __init__(self, *, q, lists, softmax_scale, sink=None, o_scale=1.0, o=None, lse=None):
@@ -51,7 +51,7 @@ class SparseDecode:
         a.softmax_scale, a.o_scale = float(softmax_scale), float(o_scale)
         a.o, a.o_tok_stride, a.o_head_stride = _ptr(self.o), self.o.stride(0), self.o.stride(1)
         a.lse = _ptr(self.lse)
-        self.tiles = sum(-(-l["slots"].shape[1] // t) for l, t in zip(self.lists, (64, 128)))
+        self.tiles = sum(-(-l["slots"].shape[1] // 64) for l in self.lists)
         ws = native.sparse_workspace_bytes(a)
         if ws == 0 and self.tiles > 0:
             native.sparse_decode(a)  # invalid arguments: raises with the library's reason
@@ -63,6 +63,12 @@ class SparseDecode:
         """Enqueue the tile kernel and the merge on `stream` (default: torch's
         current stream). No allocation, no sync."""
         native.sparse_decode(self.args, (stream or torch.cuda.current_stream()).cuda_stream)
+
+    def run_tiles_only(self, stream=None):
+        native.sparse_tiles(self.args, (stream or torch.cuda.current_stream()).cuda_stream)
+
+    def run_merge_only(self, stream=None):
+        native.sparse_merge(self.args, (stream or torch.cuda.current_stream()).cuda_stream)
 
 
 def for_batch(batch, **kw):

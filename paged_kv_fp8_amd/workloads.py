@@ -381,7 +381,7 @@ class SparseWorkload:
 
 SPARSE_WORKLOADS = {
     # a small decode step of the page's flash configuration: 16 tokens, 16 live
-    # heads, a 128-slot window plus 512 compressed slots (6 tiles per token)
+    # heads, a 128-slot window plus 512 compressed slots (ten 64-slot tiles per token)
     9: SparseWorkload("sparse_t16_hq16_win128_top512_ratio4_L4k-64k", 16, 16, 128, 512, 4, (64, 32),
                       ("uniform", 4096, 65536)),
 }

@@ -348,7 +348,7 @@ def _sparse_args(native, **over):
 
 def test_sparse_workspace_formula(native):
     a = _sparse_args(native)
-    tiles = 128 // 64 + 512 // 128
+    tiles = 128 // 64 + 512 // 64
     assert native.sparse_workspace_bytes(a) == tiles * 4 * 16 * (512 + 2) * 4
     a = _sparse_args(native, l0_width=65, l1_width=0)
     assert native.sparse_workspace_bytes(a) == 2 * 4 * 16 * 514 * 4
@@ -368,9 +368,10 @@ SPARSE_BAD = [
 
 @pytest.mark.parametrize("over,code", SPARSE_BAD)
 def test_sparse_decode_rejects_invalid_arguments_without_touching_the_gpu(native, over, code):
-    st = native.lib.pkv_sparse_decode(ctypes.byref(_sparse_args(native, **over)), None)
-    assert st == code, (over, native.status_string(st), native.last_error())
-    assert native.last_error()
+    for fn in (native.lib.pkv_sparse_decode, native.lib.pkv_sparse_tiles, native.lib.pkv_sparse_merge):
+        st = fn(ctypes.byref(_sparse_args(native, **over)), None)
+        assert st == code, (over, native.status_string(st), native.last_error())
+        assert native.last_error()
 
 
 def test_sparse_null_args(native):
