@@ -106,11 +106,26 @@ def attend(qrows, K, V, limits, softmax_scale, o_scale):
 
 
 def decode_attention(q, k_cache, v_cache, block_table, seq_lens, q_descale, k_descale, v_descale,
-                     *, q_len, h_k, softmax_scale, o_scale=1.0, causal=True, kv_format="e4m3"):
+                     *, q_len, h_k, softmax_scale, o_scale=1.0, causal=True, kv_format="e4m3", k_scale=None,
+                     v_scale=None):
     """Decode attention of every sequence, KV head and packed row (steps 1-6).
-    kv_format names the K/V code format (step 3's dec): "e4m3", or one of
-    the packed narrow formats of [T5] ("e2m1" fp4, "e2m3" / "e3m2" fp6)."""
-    dec_kv = KV_DECODERS[kv_format]
+    kv_format names the K/V code format (step 3's dec): "e4m3", one of the
+    packed narrow formats of [T5] ("e2m1" fp4, "e2m3" / "e3m2" fp6), or
+    "nvfp4" (packed e2m1 with the e4m3 group scales k_scale / v_scale,
+    (pages, PS, h_k, d/16) bytes, decoded to the kernel values of
+    ``producers.nvfp4_kernel_values``)."""
+    if kv_format == "nvfp4":
+        from .producers import nvfp4_kernel_values
+        d_v = v_cache.shape[-1] * 2
+
+        def gather_kv(cache, scales, bt, L, g):
+            return nvfp4_kernel_values(gather_tokens(cache, bt, L, g), gather_tokens(scales, bt, L, g))
+    else:
+        dec_kv = KV_DECODERS[kv_format]
+        d_v = kv_row_elems(v_cache.shape[-1], kv_format)
+
+        def gather_kv(cache, scales, bt, L, g):
+            return dec_kv(gather_tokens(cache, bt, L, g))
     q = np.asarray(q)
     seq_lens = np.asarray(seq_lens)
     num_seqs = seq_lens.shape[0]
@@ -123,15 +138,14 @@ def decode_attention(q, k_cache, v_cache, block_table, seq_lens, q_descale, k_de
     qd = _per_seq_head(q_descale, num_seqs, h_k) if q.dtype == np.uint8 else np.ones((num_seqs, h_k))
     kd = _per_seq_head(k_descale, num_seqs, h_k)
     vd = _per_seq_head(v_descale, num_seqs, h_k)
-    d_v = kv_row_elems(v_cache.shape[-1], kv_format)
     o = np.zeros((num_seqs * q_len, h_q, d_v))
     lse = np.full((num_seqs, h_k, n_rows), -np.inf)
     for b in range(num_seqs):
         L = int(seq_lens[b])
         lim = row_limits(L, q_len, h_r, causal)
         for g in range(h_k):
-            K = dec_kv(gather_tokens(k_cache, block_table[b], L, g)) * kd[b, g]
-            V = dec_kv(gather_tokens(v_cache, block_table[b], L, g)) * vd[b, g]
+            K = gather_kv(k_cache, k_scale, block_table[b], L, g) * kd[b, g]
+            V = gather_kv(v_cache, v_scale, block_table[b], L, g) * vd[b, g]
             # packed row n = qi * h_r + hr  <-  token b*q_len + qi, head g*h_r + hr
             rows = qf[b * q_len:(b + 1) * q_len, g * h_r:(g + 1) * h_r].reshape(n_rows, d) * qd[b, g]
             ob, lb = attend(rows, K, V, lim, softmax_scale, o_scale)

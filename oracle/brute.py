@@ -79,6 +79,25 @@ def fp6_row_to_floats(row, kv_fmt):
     return [fp6_code_to_float((n >> (6 * i)) & 63, kv_fmt) for i in range(len(row) * 8 // 6)]
 
 
+def e4m3_round_brute(x):
+    """The e4m3 value nearest to x (finite, |x| <= 448), ties to the even
+    code: a search over all 127 non-negative finite codes."""
+    best = None
+    for code in range(0x7F):
+        v = e4m3_bits_to_float(code)
+        d = abs(abs(x) - v)
+        if best is None or d < best[0] or (d == best[0] and code % 2 == 0):
+            best = (d, code, v)
+    return math.copysign(best[2], x)
+
+
+def nvfp4_row_to_floats(row, scales):
+    """A packed NVFP4 row (d/2 bytes) with its e4m3 group scales (d/16 bytes)
+    -> the d kernel values e4m3(code * scale / 8)."""
+    codes = fp4_row_to_floats(row)
+    return [e4m3_round_brute(c * e4m3_bits_to_float(scales[i // 16]) / 8.0) for i, c in enumerate(codes)]
+
+
 def _row_floats(row, kv_fmt):
     if kv_fmt == "e2m1":
         return fp4_row_to_floats(row)
@@ -92,14 +111,14 @@ def _dec(x, fmt):
 
 
 def brute_decode_attention(q, q_fmt, k_cache, v_cache, block_table, seq_lens, qd, kd, vd,
-                           q_len, h_k, softmax_scale, o_scale, causal, kv_fmt="e4m3"):
+                           q_len, h_k, softmax_scale, o_scale, causal, kv_fmt="e4m3", k_scale=None, v_scale=None):
     """All arguments are nested Python lists (or array-likes indexed one
     element at a time). qd/kd/vd are (num_seqs, h_k) nested lists; qd is
     ignored for bf16 q. Returns (o[token][head][dim], lse[seq][g][n])."""
     num_seqs = len(seq_lens)
     h_q = len(q[0])
     d = len(q[0][0])
-    d_v = len(v_cache[0][0][0]) * 8 // {"e2m1": 4, "e2m3": 6, "e3m2": 6}.get(kv_fmt, 8)
+    d_v = len(v_cache[0][0][0]) * 8 // {"e2m1": 4, "nvfp4": 4, "e2m3": 6, "e3m2": 6}.get(kv_fmt, 8)
     ps = len(k_cache[0])
     h_r = h_q // h_k
     o = [[[0.0] * d_v for _ in range(h_q)] for _ in range(num_seqs * q_len)]
@@ -119,8 +138,14 @@ def brute_decode_attention(q, q_fmt, k_cache, v_cache, block_table, seq_lens, qd
                     for j in range(last + 1):
                         page = int(block_table[b][j // ps])
                         row = j % ps
-                        kv = [x * float(kd[b][g]) for x in _row_floats(k_cache[page][row][g], kv_fmt)]
-                        vv = [x * float(vd[b][g]) for x in _row_floats(v_cache[page][row][g], kv_fmt)]
+                        if kv_fmt == "nvfp4":
+                            kr = nvfp4_row_to_floats(k_cache[page][row][g], k_scale[page][row][g])
+                            vr = nvfp4_row_to_floats(v_cache[page][row][g], v_scale[page][row][g])
+                        else:
+                            kr = _row_floats(k_cache[page][row][g], kv_fmt)
+                            vr = _row_floats(v_cache[page][row][g], kv_fmt)
+                        kv = [x * float(kd[b][g]) for x in kr]
+                        vv = [x * float(vd[b][g]) for x in vr]
                         scores.append(softmax_scale * math.fsum(a * c for a, c in zip(qv, kv)))
                         values.append(vv)
                     top = max(scores)

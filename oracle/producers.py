@@ -129,3 +129,19 @@ def write_kv_latent(lat, rope, scl, x_new, rope_new, seq_lens, n_new, block_tabl
             scl[pages[b, t], rows[b, t]] = s
             rope[pages[b, t], rows[b, t]] = r[b, t]
     return lat, rope, scl
+
+
+def nvfp4_kernel_values(packed, scales):
+    """NVFP4 K/V rows -> the values the decode multiplies ([T5] KV cache
+    formats and ``nvfp4_quantize``): packed e2m1 codes (..., d/2) with one
+    e4m3 scale byte per 16 elements (..., d/16); value = e4m3(code * scale *
+    2^-3), rounded to nearest, ties to even (the product is exact in float32:
+    at most 6 significant bits). The host folds the 2^3 back into the
+    descale."""
+    from .formats import E2M1_TABLE, E4M3_TABLE, unpack_fp4
+
+    codes = E2M1_TABLE[unpack_fp4(np.asarray(packed))]
+    sc = np.repeat(E4M3_TABLE[np.asarray(scales)], 16, axis=-1)
+    prod = (codes * sc * 0.125).astype(np.float32)
+    assert np.array_equal(prod.astype(np.float64), codes * sc * 0.125)  # exact
+    return E4M3_TABLE[encode_e4m3(prod)]

@@ -39,7 +39,13 @@ Data recipe (following the t5_decode page's harness, ``run``):
   * packed e2m3 / e3m2 (fp6) K/V, the same list: descale = max(amax, 1e-6) /
     7.5 (e2m3) or / 28 (e3m2), nearest magnitude with ties to the smaller,
     four codes per three bytes (element i at bits 6i .. 6i+5 of the row);
-    unused pages and tail rows hold the largest positive code 0x1F.
+    unused pages and tail rows hold the largest positive code 0x1F;
+  * NVFP4 K/V (the page's "nvfp4" and ``nvfp4_quantize``): per (sequence,
+    kv head) a global scale gs = max(amax, 1e-12) / (6 * 448); per 16
+    head-dim values an e4m3 scale e4m3(min(amax_16 / 6 / gs, 448)); codes =
+    nearest e2m1 of x / (scale * gs) (ties to the smaller), packed as fp4;
+    the descale passed to the kernel is 8 * gs (the page folds the 2^3 of
+    its conversion into it); unused rows hold code 0x77 and scale 0x7E.
 Random tensors come from a torch generator on the target device, seeded per
 workload, so a GPU batch is generated on the GPU.
 """
@@ -91,7 +97,7 @@ class Workload:
     seq_len_dist: tuple  # ("fixed", [..]) | ("uniform", lo, hi) | ("lognormal", median, sigma, lo, hi) | ("mix", ...)
     max_splits: int = 16
     q_format: str = "bf16"  # "bf16" | "e4m3"
-    kv_format: str = "e4m3"  # "e4m3" | "mla" | "e2m1" (packed fp4) | "e2m3" / "e3m2" (packed fp6)
+    kv_format: str = "e4m3"  # "e4m3" | "mla" | "e2m1" (packed fp4) | "e2m3" / "e3m2" (packed fp6) | "nvfp4"
     causal: bool = True
     seed: int = 1111
     num_pages: int = 0  # 0: used + max(4, used // 4)
@@ -136,6 +142,10 @@ WORKLOADS = {
     8: Workload("fp6e3m2kv_b128_hq64_hk4_d128_ps128_mix1k-4k_32k-64k", 128, 1, 64, 4, 128, 128, 128,
                 ("mix", 0.1, (32768, 65536), (1024, 4096)), max_splits=64, q_format="e4m3", kv_format="e3m2",
                 seed=1115),
+    # ... and with NVFP4 K/V (packed e2m1 codes + one e4m3 scale per 16 head-dim values)
+    10: Workload("nvfp4kv_b128_hq64_hk4_d128_ps128_mix1k-4k_32k-64k", 128, 1, 64, 4, 128, 128, 128,
+                 ("mix", 0.1, (32768, 65536), (1024, 4096)), max_splits=64, q_format="e4m3", kv_format="nvfp4",
+                 seed=1115),
 }
 
 
@@ -185,6 +195,8 @@ class Batch:
     mla_latent: torch.Tensor = None  # (pages, PS, 1, 512) uint8 view of the records
     mla_rope: torch.Tensor = None  # (pages, PS, 1, 64) bf16 view
     mla_scales: torch.Tensor = None  # (pages, PS, 1, 4) float32 view
+    k_scale: torch.Tensor = None  # nvfp4: (pages, PS, h_k, d/16) uint8 e4m3 group scales
+    v_scale: torch.Tensor = None
     unused_pages: list = field(default_factory=list)
 
     @property
@@ -197,6 +209,8 @@ class Batch:
             return toks * MLA_RECORD_BYTES
         if w.kv_format in NARROW_FORMATS:
             return toks * w.h_k * (w.d_qk + w.d_v) * NARROW_FORMATS[w.kv_format][2] // 8
+        if w.kv_format == "nvfp4":  # codes + one scale byte per 16 values
+            return toks * w.h_k * ((w.d_qk + w.d_v) // 2 + (w.d_qk + w.d_v) // 16)
         return toks * w.h_k * (w.d_qk + w.d_v)
 
     def to_numpy(self):
@@ -217,6 +231,9 @@ class Batch:
             out["v_cache"] = self.v_cache.contiguous().cpu().numpy()
             out["k_descale"] = self.k_descale.cpu().numpy()
             out["v_descale"] = self.v_descale.cpu().numpy()
+            if self.spec.kv_format == "nvfp4":
+                out["k_scale"] = self.k_scale.contiguous().cpu().numpy()
+                out["v_scale"] = self.v_scale.contiguous().cpu().numpy()
         return out
 
 
@@ -280,6 +297,27 @@ def _quantise_narrow_per_seq_head(x, seg, num_seqs, kv_format):
     return packed.to(torch.uint8).contiguous(), desc.contiguous()
 
 
+def _quantise_nvfp4_per_seq_head(x, seg, num_seqs):
+    """x (tokens, h_k, d) float32 -> (packed codes (tokens, h_k, d/2), e4m3
+    group scales (tokens, h_k, d/16) uint8, descale (b, h_k) = 8 * gs)."""
+    tokens, h_k, d = x.shape
+    amax = torch.zeros(num_seqs, h_k, device=x.device)
+    amax.scatter_reduce_(0, seg[:, None].expand(-1, h_k), x.abs().amax(dim=-1), "amax")
+    gs = amax.clamp(min=1e-12) / (6.0 * E4M3_MAX)
+    xg = x.view(tokens, h_k, d // 16, 16)
+    sc = (xg.abs().amax(dim=-1) / 6.0 / gs[seg][:, :, None]).clamp(max=E4M3_MAX).to(torch.float8_e4m3fn)
+    denom = (sc.float() * gs[seg][:, :, None])[..., None]
+    y = torch.where(denom > 0, xg / denom.clamp(min=1e-30), torch.zeros_like(xg)).view(tokens, h_k, d)
+    mags = torch.tensor(E2M1_MAGNITUDES, device=x.device)
+    ay = y.abs().clamp(max=E2M1_MAGNITUDES[-1])
+    hi = torch.bucketize(ay, mags).clamp(max=len(E2M1_MAGNITUDES) - 1)
+    lo = (hi - 1).clamp(min=0)
+    code = torch.where((ay - mags[lo]) <= (mags[hi] - ay), lo, hi)
+    code = code | ((y < 0) & (mags[code] > 0)).to(code.dtype) << 3
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).to(torch.uint8).contiguous()
+    return packed, sc.view(torch.uint8).contiguous(), (gs * 8.0).contiguous()
+
+
 def make_batch(w: Workload, device="cpu", seq_lens=None) -> Batch:
     """Generate the batch of workload ``w`` on ``device``."""
     rng = np.random.Generator(np.random.PCG64(w.seed + 7))
@@ -321,9 +359,10 @@ def make_batch(w: Workload, device="cpu", seq_lens=None) -> Batch:
         return batch
 
     d = w.d_qk
+    nv = w.kv_format == "nvfp4"
     narrow = w.kv_format in NARROW_FORMATS
-    row_bytes = d * NARROW_FORMATS[w.kv_format][2] // 8 if narrow else d
-    fill = NARROW_FORMATS[w.kv_format][3] if narrow else (E4M3_NAN,)
+    row_bytes = d * NARROW_FORMATS[w.kv_format][2] // 8 if narrow else d // 2 if nv else d
+    fill = NARROW_FORMATS[w.kv_format][3] if narrow else (E2M1_FILL,) if nv else (E4M3_NAN,)
     if w.kv_layout == "nhd":
         kbuf = torch.empty((2, num_pages, ps, h_k, row_bytes), dtype=torch.uint8, device=device)
         k_view, v_view = kbuf[0], kbuf[1]
@@ -334,9 +373,21 @@ def make_batch(w: Workload, device="cpu", seq_lens=None) -> Batch:
         raise ValueError(f"unknown kv_layout {w.kv_layout}")
     pat = torch.tensor(fill, dtype=torch.uint8, device=device)
     kbuf.view(-1, len(fill)).copy_(pat.expand(kbuf.numel() // len(fill), -1))
+    if nv:  # group scales beside the codes, in the same layout; unused rows hold 448 (0x7E)
+        if w.kv_layout == "nhd":
+            sbuf = torch.full((2, num_pages, ps, h_k, d // 16), 0x7E, dtype=torch.uint8, device=device)
+            scale_views = (sbuf[0], sbuf[1])
+        else:
+            sbuf = torch.full((num_pages, 2, h_k, ps, d // 16), 0x7E, dtype=torch.uint8, device=device)
+            scale_views = (sbuf[:, 0].transpose(1, 2), sbuf[:, 1].transpose(1, 2))
     for view, name in ((k_view, "k"), (v_view, "v")):
         x = torch.randn(n_tok, h_k, d, generator=gen, device=device)
-        if narrow:
+        if nv:
+            codes, scl, desc = _quantise_nvfp4_per_seq_head(x, seg, b)
+            sv = scale_views[0 if name == "k" else 1]
+            sv[slot // ps, slot % ps] = scl
+            setattr(batch, f"{name}_scale", sv)
+        elif narrow:
             codes, desc = _quantise_narrow_per_seq_head(x, seg, b, w.kv_format)
         else:
             codes, desc = _quantise_per_seq_head(x, seg, b)

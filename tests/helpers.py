@@ -12,6 +12,7 @@ import torch
 
 from oracle import attention as A
 from oracle.formats import KV_DECODERS, decode_e4m3
+from oracle.producers import nvfp4_kernel_values
 
 O_TOL = 1e-2
 LSE_TOL = 1e-3
@@ -28,7 +29,8 @@ def oracle_for(np_batch, spec, seqs=None, causal=None):
                                       nb["seq_lens"][idx], q_len=spec.q_len, softmax_scale=spec.scale, causal=causal)
     return A.decode_attention(nb["q"][tok], nb["k_cache"], nb["v_cache"], nb["block_table"][idx], nb["seq_lens"][idx],
                               nb["q_descale"][idx], nb["k_descale"][idx], nb["v_descale"][idx], q_len=spec.q_len,
-                              h_k=spec.h_k, softmax_scale=spec.scale, causal=causal, kv_format=spec.kv_format)
+                              h_k=spec.h_k, softmax_scale=spec.scale, causal=causal, kv_format=spec.kv_format,
+                              k_scale=nb.get("k_scale"), v_scale=nb.get("v_scale"))
 
 
 def max_abs_v(np_batch, spec, seqs=None):
@@ -44,6 +46,10 @@ def max_abs_v(np_batch, spec, seqs=None):
                 lat = A.gather_tokens(nb["latent"], nb["block_table"][b], L, 0)
                 sc = A.gather_tokens(nb["scales"], nb["block_table"][b], L, 0).astype(np.float64)
                 v = decode_e4m3(lat) * np.repeat(sc, 128, axis=-1)
+            elif spec.kv_format == "nvfp4":
+                v = nvfp4_kernel_values(A.gather_tokens(nb["v_cache"], nb["block_table"][b], L, g),
+                                        A.gather_tokens(nb["v_scale"], nb["block_table"][b], L, g))
+                v = v * float(nb["v_descale"][b, g])
             else:
                 v = KV_DECODERS[spec.kv_format](A.gather_tokens(nb["v_cache"], nb["block_table"][b], L, g))
                 v = v * float(nb["v_descale"][b, g])

@@ -606,3 +606,74 @@ def test_fp6_equals_e4m3_on_the_same_values(fmt):
     o8, l8 = run_oracle(c8, **kw)
     assert np.array_equal(o6, o8) and np.array_equal(l6, l8)
 
+
+
+def test_nvfp4_kernel_values_closed_forms():
+    from oracle.producers import nvfp4_kernel_values
+    # one row of 16 codes per case, one scale byte each
+    def val(code, scale_byte):
+        packed = np.array([[code | (code << 4)] * 8], dtype=np.uint8)
+        return nvfp4_kernel_values(packed, np.array([[scale_byte]], dtype=np.uint8))[0, 0]
+    # the page's bound: code 6.0 times scale 448 times 2^-3 = 336, not an e4m3
+    # value; halfway between 320 (even code 0x7A) and 352 (0x7B): ties to even
+    assert val(0x7, 0x7E) == 320.0
+    assert val(0xF, 0x7E) == -320.0
+    assert val(0x2, 0x38) == 0.125                   # 1.0 * 1.0 / 8, exact
+    assert val(0x1, 0x08) == 0.0                     # 0.5 * 2^-6 / 8 = 2^-10: half the smallest subnormal, ties to 0
+    assert val(0x3, 0x08) == 2.0 ** -8               # 1.5 * 2^-9: halfway between subnormal codes 1 and 2, ties to 2
+    assert val(0x5, 0x3C) == 0.5625                  # 3 * 1.5 / 8 = 0.5625 = 1.125 * 2^-1, exact
+
+
+def test_nvfp4_rounding_matches_torch_cast():
+    from oracle.producers import nvfp4_kernel_values
+    rng = np.random.default_rng(21)
+    packed = rng.integers(0, 256, size=(64, 64), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, size=(64, 8), dtype=np.uint8)  # finite, non-negative scales
+    got = nvfp4_kernel_values(packed, scales)
+    prod = formats.E2M1_TABLE[formats.unpack_fp4(packed)] * np.repeat(formats.E4M3_TABLE[scales], 16, axis=-1) / 8
+    ref = torch.from_numpy(prod.astype(np.float32)).to(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(got, ref)
+
+
+def nvfp4_case(rng, **kw):
+    c = fp4_case(rng, **kw)
+    for name in ("k_scale", "v_scale"):
+        shp = c["k_cache"].shape
+        c[name] = rng.integers(0x20, 0x60, size=shp[:-1] + (shp[-1] * 2 // 16,), dtype=np.uint8)
+    return c
+
+
+NVFP4_CASES = [
+    dict(num_seqs=2, q_len=1, h_q=4, h_k=2, d=16, ps=4, lens=(5, 11), q_fmt="e4m3", causal=True),
+    dict(num_seqs=2, q_len=3, h_q=4, h_k=2, d=32, ps=8, lens=(9, 3), q_fmt="e4m3", causal=False),
+]
+
+
+@pytest.mark.parametrize("case", range(len(NVFP4_CASES)))
+def test_nvfp4_oracle_matches_brute_force(case):
+    cfg = dict(NVFP4_CASES[case])
+    causal = cfg.pop("causal")
+    c = nvfp4_case(np.random.default_rng(990 + case), **cfg)
+    kw = dict(softmax_scale=0.33, o_scale=1.1, causal=causal)
+    o, lse = run_oracle(c, kv_format="nvfp4", k_scale=c["k_scale"], v_scale=c["v_scale"], **kw)
+    ob, lb = brute.brute_decode_attention(
+        c["q"].tolist(), "e4m3", c["k_cache"].tolist(), c["v_cache"].tolist(), c["block_table"].tolist(),
+        c["seq_lens"].tolist(), c["q_descale"].tolist(), c["k_descale"].tolist(), c["v_descale"].tolist(),
+        c["q_len"], c["h_k"], kw["softmax_scale"], kw["o_scale"], kw["causal"], kv_fmt="nvfp4",
+        k_scale=c["k_scale"].tolist(), v_scale=c["v_scale"].tolist())
+    assert o.shape[-1] == cfg["d"] and np.all(np.isfinite(o))
+    np.testing.assert_allclose(o, np.array(ob), rtol=0, atol=1e-12)
+    fin = np.isfinite(lse)
+    np.testing.assert_allclose(lse[fin], np.array(lb)[fin], rtol=0, atol=1e-12)
+
+
+def test_nvfp4_with_unit_group_scales_is_the_fp4_path():
+    # scale 8.0 (e4m3 0x50) times 2^-3 is 1: every kernel value is the e2m1 value itself
+    c = nvfp4_case(np.random.default_rng(79), num_seqs=2, q_len=2, h_q=4, h_k=2, d=32, ps=4, lens=(6, 13),
+                   q_fmt="e4m3")
+    c["k_scale"][:] = 0x50
+    c["v_scale"][:] = 0x50
+    kw = dict(softmax_scale=0.29, causal=True)
+    on, ln = run_oracle(c, kv_format="nvfp4", k_scale=c["k_scale"], v_scale=c["v_scale"], **kw)
+    o4, l4 = run_oracle(c, kv_format="e2m1", **kw)
+    assert np.array_equal(on, o4) and np.array_equal(ln, l4)
