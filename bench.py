@@ -19,7 +19,7 @@ sample of the same batch on the host cores. Diagnostics go to stderr.
 Default workload: 64 sequences, q_len 1, 32 query heads on 8 e4m3 KV heads,
 d = 128, 16-key pages, lengths uniform in [512, 8192], split-KV up to 16
 chunks (``--config 2``). ``--config 1..5`` selects the other workloads; 6, 7
-and 8 are workload 4 with packed fp4 (e2m1), fp6 e2m3 and fp6 e3m2 K/V; 9 is
+8 and 10 are workload 4 with packed fp4 (e2m1), fp6 e2m3, fp6 e3m2 and NVFP4 K/V; 9 is
 the sparse slot-list decode step (its metric: listed record bytes per step
 time).
 """
@@ -339,9 +339,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9],
-                    help="workload: 1-5 as specified; 6, 7, 8 = workload 4 with packed fp4 (e2m1), "
-                         "fp6 e2m3, fp6 e3m2 K/V; 9 = the sparse slot-list decode step (16 tokens, 16 heads, "
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9, 10],
+                    help="workload: 1-5 as specified; 6, 7, 8, 10 = workload 4 with packed fp4 (e2m1), "
+                         "fp6 e2m3, fp6 e3m2, NVFP4 K/V; 9 = the sparse slot-list decode step (16 tokens, 16 heads, "
                          "128-slot window + 512 top-k slots)")
     ap.add_argument("--q-len", type=int, default=None, help="query tokens per sequence (latent workload: 1..16)")
     ap.add_argument("--causal", type=int, default=None, help="override the workload's causal flag (0/1)")

@@ -221,6 +221,14 @@ pkv_status pkv_plan_queued(const int32_t* seq_lens, int32_t num_seqs, int32_t h_
  * one-wave plan only, as for PKV_KV_E2M1. */
 #define PKV_KV_E2M3 3
 #define PKV_KV_E3M2 4
+/* NVFP4 K and V caches (the same page's "nvfp4" and nvfp4_quantize): rows
+ * packed as for PKV_KV_E2M1 plus one e4m3 scale per 16 head-dim values in
+ * k_group_scale / v_group_scale. The decode multiplies the values
+ * e4m3(code * scale * 2^-3) (rounded to nearest, ties to even; the product
+ * is at most 336, so nothing saturates) times the per-(sequence, kv-head)
+ * descales, which carry the 2^3 back. d_qk = d_v = 128, an e4m3 query and
+ * the one-wave plan only. */
+#define PKV_KV_NVFP4 5
 
 /*
  * All strides are in ELEMENTS of the pointed-to type, >= 0; a descale
@@ -232,6 +240,7 @@ pkv_status pkv_plan_queued(const int32_t* seq_lens, int32_t num_seqs, int32_t h_
  *   k, v   [num_pages][page_size][h_k][d]    e4m3 codes    (page, row, head strides, bytes)
  *          PKV_KV_E2M1: [num_pages][page_size][h_k][d/2] packed fp4 bytes (byte strides)
  *          PKV_KV_E2M3 / E3M2: [num_pages][page_size][h_k][3d/4] packed fp6 bytes (byte strides)
+ *          PKV_KV_NVFP4: as PKV_KV_E2M1, plus the group scales (k/v_group_scale)
  *          MLA: k = v = latent [pages][PS][1][512] e4m3 (v may be NULL or equal k)
  *   k_rope MLA only: [pages][PS][1][64] bf16 (page, row strides)
  *   k_blk_scale MLA only: [pages][PS][1][4] fp32, one scale per 128 latent values
@@ -316,6 +325,13 @@ typedef struct pkv_decode_args {
    * them), so no per-call clearing is needed and the launch can be replayed
    * in a HIP graph. Calls that overlap on one counter array race. */
   int32_t* queue;
+  /* PKV_KV_NVFP4 only (NULL otherwise): the e4m3 group scales of K and V,
+   * one byte per 16 head-dim values, [num_pages][page_size][h_k][d/16] with
+   * byte strides; k_group_scale 8-B aligned with 8-B multiple strides. */
+  const uint8_t* k_group_scale;
+  int64_t kgs_page_stride, kgs_row_stride, kgs_head_stride;
+  const uint8_t* v_group_scale;
+  int64_t vgs_page_stride, vgs_row_stride, vgs_head_stride;
 } pkv_decode_args;
 
 /* Bytes of split workspace: max_splits * num_seqs * h_k * n_rows * (d_v + 2)

@@ -99,6 +99,15 @@ pkv_status check_pointers(const pkv_decode_args* a, bool for_merge) {
     return fail(PKV_ERR_INVALID_ARG, "bin_offsets needs num_bins >= 1 and 4-B alignment");
   if (narrow_kv(a->kv_format) && (a->bin_offsets || a->queue))
     return fail(PKV_ERR_UNSUPPORTED, "fp4/fp6 cache: only the one-wave plan (pkv_plan_split_kv) is built");
+  if (a->kv_format == PKV_KV_NVFP4) {
+    if (!a->k_group_scale || !a->v_group_scale)
+      return fail(PKV_ERR_INVALID_ARG, "NVFP4 cache: k_group_scale and v_group_scale must be non-NULL");
+    if (!aligned(a->k_group_scale, 8) || bad_stride(a->kgs_page_stride, 1, 8) || bad_stride(a->kgs_row_stride, 1, 8) ||
+        bad_stride(a->kgs_head_stride, 1, 8))
+      return fail(PKV_ERR_INVALID_ARG, "k_group_scale must be 8-B aligned with 8-B multiple strides");
+    if (a->vgs_page_stride < 0 || a->vgs_row_stride < 0 || a->vgs_head_stride < 0)
+      return fail(PKV_ERR_INVALID_ARG, "v_group_scale strides must be >= 0");
+  }
   if (a->queue) {
     if (!a->bin_offsets) return fail(PKV_ERR_INVALID_ARG, "queue needs bin_offsets (a plan from pkv_plan_queued)");
     if (!aligned(a->queue, 4)) return fail(PKV_ERR_INVALID_ARG, "queue must be 4-B aligned");

@@ -91,6 +91,10 @@ struct GqaParams {
   int num_seqs, q_len, h_k, h_r, rows, page_shift, num_pages, max_blocks, max_splits;
   int key_mult;  // keys per unit of a work item's range: 128 (tile plans) or 1 (key plans)
   int num_work;
+  const uint8_t* ks;  // NVFP4: e4m3 group scales of K and V (one byte per 16 values)
+  int64_t ks_page, ks_row, ks_head;  // bytes
+  const uint8_t* vs;
+  int64_t vs_page, vs_row, vs_head;
 };
 
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint2 x) {
@@ -639,6 +643,102 @@ __device__ __forceinline__ void process_block_fp4(const RawBlock4& cur, int kb, 
   softmax_pv<true, NB, true>(sacc, v8, kb, st, lim, lim_min, c2, g4);
 }
 
+// NVFP4 rows ("mjolnir-kernel 0.1.0 wheel: mjolnir/t5_decode.py", KV cache
+// formats and nvfp4_quantize): packed e2m1 codes as for fp4 plus one e4m3
+// scale per 16 head-dim values. The decode multiplies the values
+// e4m3(code * scale * 2^-3): the e4m3 scale is not a power of two, so the
+// codes cannot go to the scaled MFMA (its block scales are E8M0 per 32) and
+// the rounding is part of the method. Each block is converted to the e4m3
+// block of the e4m3 cache and runs that path: a lane loads its e4m3 lane
+// layout's head dims (K: 16*g4 .. and 64 + 16*g4 .., 8 bytes each, with the
+// key's 8 group scales; V: 8 codes d_v 8*r16 .. of each of its 8 keys and
+// their group scale byte r16 / 2).
+struct RawBlockN {
+  uint2 k[2][2];   // [t][half] packed codes
+  uint2 ks[2];     // [t] the key's 8 group scales
+  uint32_t v[8];   // packed codes
+  uint32_t vs[8];  // group scale byte
+};
+
+struct LaneOffsetsN {
+  uint32_t k, kb;       // K: r16 * k_row + 8 g4 (second half +32 bytes); 8 g4
+  uint32_t ks;          // K scales: r16 * ks_row
+  uint32_t v[4], vb;    // V: (4 g4 + i) * v_row + 4 r16; 4 r16
+  uint32_t vs[4], vsb;  // V scales: (4 g4 + i) * vs_row + r16 / 2; r16 / 2
+};
+
+__device__ __forceinline__ LaneOffsetsN lane_offsetsN(const GqaParams& p, int r16, int g4) {
+  LaneOffsetsN o;
+  o.k = (uint32_t)r16 * (uint32_t)p.k_row + 8u * (uint32_t)g4;
+  o.kb = 8u * (uint32_t)g4;
+  o.ks = (uint32_t)r16 * (uint32_t)p.ks_row;
+  for (int i = 0; i < 4; ++i) {
+    o.v[i] = (uint32_t)(4 * g4 + i) * (uint32_t)p.v_row + 4u * (uint32_t)r16;
+    o.vs[i] = (uint32_t)(4 * g4 + i) * (uint32_t)p.vs_row + (uint32_t)(r16 >> 1);
+  }
+  o.vb = 4u * (uint32_t)r16;
+  o.vsb = (uint32_t)(r16 >> 1);
+  return o;
+}
+
+// load_block for NVFP4 rows: 4 + 2 + 8 + 8 loads, same row clamping.
+__device__ __forceinline__ RawBlockN load_blockN(const GqaParams& p, int g, int kb, int pg0, int pg1, int last_key,
+                                                 int pmask, const LaneOffsetsN& lo) {
+  RawBlockN r;
+  for (int t = 0; t < 2; ++t) {
+    const int st = min(kb + 16 * t, last_key);
+    const uint32_t lim = (uint32_t)max(last_key - st, 0);
+    const int64_t pg = t ? pg1 : pg0;
+    const uint32_t row = (uint32_t)(st & pmask);
+    const uint8_t* kbase = p.k + pg * p.k_page + (int64_t)g * p.k_head + row * (uint32_t)p.k_row;
+    const uint8_t* vbase = p.v + pg * p.v_page + (int64_t)g * p.v_head + row * (uint32_t)p.v_row;
+    const uint8_t* ksbase = p.ks + pg * p.ks_page + (int64_t)g * p.ks_head + row * (uint32_t)p.ks_row;
+    const uint8_t* vsbase = p.vs + pg * p.vs_page + (int64_t)g * p.vs_head + row * (uint32_t)p.vs_row;
+    const uint32_t koff = min(lo.k, lim * (uint32_t)p.k_row + lo.kb);
+    r.k[t][0] = *reinterpret_cast<const uint2*>(kbase + koff);
+    r.k[t][1] = *reinterpret_cast<const uint2*>(kbase + (koff + 32u));
+    r.ks[t] = *reinterpret_cast<const uint2*>(ksbase + min(lo.ks, lim * (uint32_t)p.ks_row));
+    const uint32_t vlim = lim * (uint32_t)p.v_row + lo.vb;
+    const uint32_t vslim = lim * (uint32_t)p.vs_row + lo.vsb;
+    for (int i = 0; i < 4; ++i) {
+      r.v[4 * t + i] = *reinterpret_cast<const uint32_t*>(vbase + min(lo.v[i], vlim));
+      r.vs[4 * t + i] = vsbase[min(lo.vs[i], vslim)];
+    }
+  }
+  return r;
+}
+
+// Eight NVFP4 codes (element 2i in the low nibble of byte i) with their
+// group scale byte -> the e4m3 bytes of e4m3(code * scale * 2^-3): each code
+// pair widened to f32 (v_cvt_scalef32_pk_f32_fp4, exact), times scale / 8
+// (exact in f32: at most 6 significant bits), rounded to e4m3 two at a time
+// by v_cvt_pk_fp8_f32 (round to nearest even; |value| <= 336, no overflow).
+__device__ __forceinline__ uint2 nvfp4x8_to_e4m3(uint32_t codes, uint32_t scale_byte) {
+  const float s = __builtin_amdgcn_cvt_f32_fp8((int)scale_byte, 0) * 0.125f;
+  const auto e01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+  const auto e23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+  const auto e45 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+  const auto e67 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e01[0] * s, e01[1] * s, 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(e23[0] * s, e23[1] * s, lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(e45[0] * s, e45[1] * s, 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(e67[0] * s, e67[1] * s, hi, true);
+  return uint2{(uint32_t)lo, (uint32_t)hi};
+}
+
+__device__ __forceinline__ RawBlock nvfp4_block_to_e4m3(const RawBlockN& c, int g4) {
+  RawBlock r;
+  for (int t = 0; t < 2; ++t)
+    for (int h = 0; h < 2; ++h) {  // head dims 64 h + 16 g4 ..: group 4 h + g4
+      const uint32_t sb = ((h ? c.ks[t].y : c.ks[t].x) >> (8 * g4)) & 0xFFu;
+      const uint2 lo = nvfp4x8_to_e4m3(c.k[t][h].x, sb);
+      const uint2 hi = nvfp4x8_to_e4m3(c.k[t][h].y, sb);
+      r.k[t][h] = uint4{lo.x, lo.y, hi.x, hi.y};
+    }
+  for (int j = 0; j < 8; ++j) r.v[j] = nvfp4x8_to_e4m3(c.v[j], c.vs[j]);
+  return r;
+}
+
 // One 32-key block of packed fp6 K/V with an e4m3 query: S = K Q^T on the
 // scaled MFMA (A format 2 = e2m3 or 3 = e3m2), then V converted to e4m3 and
 // the fp8 softmax / PV.
@@ -771,7 +871,7 @@ __device__ __forceinline__ void keep_pace(int* progress, int wave, int done, int
 // One work item (a chunk of 128-key tiles of one sequence) for kv head g:
 // the one-item-per-workgroup plan.
 // KVF: 0 = e4m3 K/V, else the packed narrow format (PKV_KV_E2M1 fp4,
-// PKV_KV_E2M3 / PKV_KV_E3M2 fp6; e4m3 query only). The page pairs of a fetch
+// PKV_KV_E2M3 / PKV_KV_E3M2 fp6, PKV_KV_NVFP4; e4m3 query only). The page pairs of a fetch
 // are loaded LA fetches ahead: two for the e4m3 ring, one fewer than the ring
 // depth for the deeper narrow rings (a pair loaded sooner would make its wait
 // cover KV loads still in the ring).
@@ -856,13 +956,18 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
       for (int u = 0; u < LA; ++u) pv[u % STAGES] = page_pair(k_begin + kBlockKeys * u);
     }
     constexpr bool kFp4 = KVF == PKV_KV_E2M1, kFp6 = KVF == PKV_KV_E2M3 || KVF == PKV_KV_E3M2;
-    using Raw = typename std::conditional<kFp4, RawBlock4,
-                                          typename std::conditional<kFp6, RawBlock6, RawBlock>::type>::type;
+    constexpr bool kNv = KVF == PKV_KV_NVFP4;
+    using Raw = typename std::conditional<
+        kFp4, RawBlock4,
+        typename std::conditional<kFp6, RawBlock6,
+                                  typename std::conditional<kNv, RawBlockN, RawBlock>::type>::type>::type;
     const auto lo = [&] {
       if constexpr (kFp4)
         return lane_offsets4(p, r16, g4);
       else if constexpr (kFp6)
         return lane_offsets6(p, r16, g4);
+      else if constexpr (kNv)
+        return lane_offsetsN(p, r16, g4);
       else
         return lane_offsets(p, r16, g4);
     }();
@@ -873,6 +978,8 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
         r = load_block4(p, g, kb, pg0, pg1, last_key, pmask, lo);
       else if constexpr (kFp6)
         r = load_block6(p, g, kb, pg0, pg1, last_key, pmask, lo);
+      else if constexpr (kNv)
+        r = load_blockN(p, g, kb, pg0, pg1, last_key, pmask, lo);
       else
         r = load_block(p, g, kb, pg0, pg1, last_key, pmask, lo);
       pv[(slot + LA) % STAGES] = page_pair(kb + LA * kBlockKeys);
@@ -906,6 +1013,8 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
           process_block_fp4<NB, kQLds>(ring[s], kb, q, qlds, st, lim, lim_min, c2, g4);
         else if constexpr (kFp6)
           process_block_fp6<NB, kQLds, KVF>(ring[s], kb, q, qlds, lo, st, lim, lim_min, c2, g4);
+        else if constexpr (kNv)
+          process_block<true, NB, kQLds>(nvfp4_block_to_e4m3(ring[s], g4), kb, q, qlds, st, lim, lim_min, c2, g4);
         else
           process_block<FP8Q, NB, kQLds>(ring[s], kb, q, qlds, st, lim, lim_min, c2, g4);
       }
@@ -1383,7 +1492,9 @@ const void* kernel_ptr(bool stream) {
 #endif
 template <int NB, int KVF>
 constexpr int narrow_stages() {
-  return NB == 2 ? (KVF == PKV_KV_E2M1 ? 3 : 2) : KVF == PKV_KV_E2M1 ? PKV_FP4_STAGES : 4;
+  // NVFP4: 23 loads per fetch, so at most two fetches ahead (the load counter holds 63)
+  return KVF == PKV_KV_NVFP4 ? (NB == 2 ? 2 : 3)
+                             : NB == 2 ? (KVF == PKV_KV_E2M1 ? 3 : 2) : KVF == PKV_KV_E2M1 ? PKV_FP4_STAGES : 4;
 }
 
 template <int NB, bool CT, int HW, int KVF>
@@ -1427,6 +1538,7 @@ const void* select_kernel(const GqaVariant& v) {
   if (v.kvf == PKV_KV_E2M1) return select_narrow<PKV_KV_E2M1>(v);
   if (v.kvf == PKV_KV_E2M3) return select_narrow<PKV_KV_E2M3>(v);
   if (v.kvf == PKV_KV_E3M2) return select_narrow<PKV_KV_E3M2>(v);
+  if (v.kvf == PKV_KV_NVFP4) return select_narrow<PKV_KV_NVFP4>(v);
   if (v.fp8_q) return v.n_blocks == 1 ? select_tail<true, 1>(v) : select_tail<true, 2>(v);
   return v.n_blocks == 1 ? select_tail<false, 1>(v) : select_tail<false, 2>(v);
 }
@@ -1449,6 +1561,8 @@ GqaVariant gqa_variant(const pkv_decode_args& a) {
   v.stream = a.bin_offsets != nullptr && a.queue == nullptr;
   if (v.kvf == PKV_KV_E2M1)
     v.stages = v.n_blocks == 1 ? narrow_stages<1, PKV_KV_E2M1>() : narrow_stages<2, PKV_KV_E2M1>();
+  else if (v.kvf == PKV_KV_NVFP4)
+    v.stages = v.n_blocks == 1 ? narrow_stages<1, PKV_KV_NVFP4>() : narrow_stages<2, PKV_KV_NVFP4>();
   else if (v.kvf)
     v.stages = v.n_blocks == 1 ? narrow_stages<1, PKV_KV_E2M3>() : narrow_stages<2, PKV_KV_E2M3>();
   else
@@ -1523,6 +1637,14 @@ hipError_t gqa_launch(const pkv_decode_args& a, const GqaVariant& v, hipStream_t
   p.counters = a.max_splits > 1 ? a.merge_counters : nullptr;
   p.bin_offsets = a.bin_offsets;
   p.queue = a.queue;
+  p.ks = a.k_group_scale;
+  p.ks_page = a.kgs_page_stride;
+  p.ks_row = a.kgs_row_stride;
+  p.ks_head = a.kgs_head_stride;
+  p.vs = a.v_group_scale;
+  p.vs_page = a.vgs_page_stride;
+  p.vs_row = a.vgs_row_stride;
+  p.vs_head = a.vgs_head_stride;
   p.key_mult = (a.bin_offsets && a.queue) ? 1 : kTileKeys;
   p.num_work = a.num_work;
   p.scale_log2e = (float)((double)a.softmax_scale * 1.4426950408889634);

@@ -27,7 +27,8 @@ struct GqaVariant {
 
 // Packed narrow K/V formats (fp4 e2m1, fp6 e2m3 / e3m2).
 inline bool narrow_kv(int kv_format) {
-  return kv_format == PKV_KV_E2M1 || kv_format == PKV_KV_E2M3 || kv_format == PKV_KV_E3M2;
+  return kv_format == PKV_KV_E2M1 || kv_format == PKV_KV_E2M3 || kv_format == PKV_KV_E3M2 ||
+         kv_format == PKV_KV_NVFP4;
 }
 GqaVariant gqa_variant(const pkv_decode_args& a);
 int gqa_rows_per_tile(const GqaVariant& v);

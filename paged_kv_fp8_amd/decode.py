@@ -13,11 +13,13 @@ import numpy as np
 import torch
 
 from . import native
-from .native import PKV_KV_E2M1, PKV_KV_E2M3, PKV_KV_E3M2, PKV_KV_E4M3, PKV_KV_MLA, PKV_Q_BF16, PKV_Q_E4M3
+from .native import (PKV_KV_E2M1, PKV_KV_E2M3, PKV_KV_E3M2, PKV_KV_E4M3, PKV_KV_MLA, PKV_KV_NVFP4, PKV_Q_BF16,
+                     PKV_Q_E4M3)
 
 # K/V code formats by name: ABI value and bits per code
-_KV_FORMATS = {"e4m3": PKV_KV_E4M3, "e2m1": PKV_KV_E2M1, "e2m3": PKV_KV_E2M3, "e3m2": PKV_KV_E3M2}
-_KV_BITS = {"e4m3": 8, "e2m1": 4, "e2m3": 6, "e3m2": 6}
+_KV_FORMATS = {"e4m3": PKV_KV_E4M3, "e2m1": PKV_KV_E2M1, "e2m3": PKV_KV_E2M3, "e3m2": PKV_KV_E3M2,
+               "nvfp4": PKV_KV_NVFP4}
+_KV_BITS = {"e4m3": 8, "e2m1": 4, "e2m3": 6, "e3m2": 6, "nvfp4": 4}
 
 
 def _ptr(t):
@@ -54,7 +56,7 @@ class PagedDecode:
                  q_descale=None, k_descale=None, v_descale=None, latent=None, rope=None, blk_scale=None,
                  num_pages=None, causal=True, o_scale=1.0, max_splits=16, force_splits=0, min_chunk_tiles=1,
                  pad_to=0, wg_per_cu=None, plan_seq_lens=None, fused_merge=False, plan="wave", pieces_per_bin=3,
-                 dyn_percent=10, plan_cu_count=None, kv_format="e4m3"):
+                 dyn_percent=10, plan_cu_count=None, kv_format="e4m3", k_group_scale=None, v_group_scale=None):
         mla = latent is not None
         a = native.DecodeArgs()
         num_seqs = seq_lens.shape[0]
@@ -89,6 +91,11 @@ class PagedDecode:
             a.kd_seq_stride, a.kd_head_stride = _descale_strides(k_descale, num_seqs, h_k)
             a.v_descale = _ptr(v_descale)
             a.vd_seq_stride, a.vd_head_stride = _descale_strides(v_descale, num_seqs, h_k)
+            if k_group_scale is not None:  # NVFP4: e4m3 scale per 16 head-dim values
+                a.k_group_scale, a.kgs_page_stride, a.kgs_row_stride, a.kgs_head_stride = (
+                    _ptr(k_group_scale), k_group_scale.stride(0), k_group_scale.stride(1), k_group_scale.stride(2))
+                a.v_group_scale, a.vgs_page_stride, a.vgs_row_stride, a.vgs_head_stride = (
+                    _ptr(v_group_scale), v_group_scale.stride(0), v_group_scale.stride(1), v_group_scale.stride(2))
             if q_descale is not None:
                 a.q_descale = _ptr(q_descale)
                 a.qd_seq_stride, a.qd_head_stride = _descale_strides(q_descale, num_seqs, h_k)
@@ -188,5 +195,8 @@ def for_batch(batch, *, o=None, lse=None, **kw):
         return PagedDecode(latent=batch.mla_latent, rope=batch.mla_rope, blk_scale=batch.mla_scales, **common, **kw)
     q_descale = batch.q_descale if w.q_format == "e4m3" else None
     kw.setdefault("kv_format", w.kv_format)
+    if w.kv_format == "nvfp4":
+        kw.setdefault("k_group_scale", batch.k_scale)
+        kw.setdefault("v_group_scale", batch.v_scale)
     return PagedDecode(k_cache=batch.k_cache, v_cache=batch.v_cache, q_descale=q_descale, k_descale=batch.k_descale,
                        v_descale=batch.v_descale, **common, **kw)

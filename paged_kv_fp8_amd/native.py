@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkvfp8.s
 
 PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_CAPACITY, PKV_ERR_WORKSPACE, PKV_ERR_HIP = 0, -1, -2, -3, -4, -5
 PKV_Q_BF16, PKV_Q_E4M3 = 0, 1
-PKV_KV_E4M3, PKV_KV_MLA, PKV_KV_E2M1, PKV_KV_E2M3, PKV_KV_E3M2 = 0, 1, 2, 3, 4
+PKV_KV_E4M3, PKV_KV_MLA, PKV_KV_E2M1, PKV_KV_E2M3, PKV_KV_E3M2, PKV_KV_NVFP4 = 0, 1, 2, 3, 4, 5
 PKV_MAX_SPLITS = 256
 
 # Every function the header declares, in declaration order.
@@ -66,6 +66,8 @@ class DecodeArgs(ctypes.Structure):
         ("merge_counters", _vp),
         ("bin_offsets", _vp), ("num_bins", _i32),
         ("queue", _vp),
+        ("k_group_scale", _vp), ("kgs_page_stride", _i64), ("kgs_row_stride", _i64), ("kgs_head_stride", _i64),
+        ("v_group_scale", _vp), ("vgs_page_stride", _i64), ("vgs_row_stride", _i64), ("vgs_head_stride", _i64),
     ]
 
 

@@ -155,7 +155,11 @@ BAD = [
     (dict(kv_format=3), -2),
     (dict(kv_format=4, q_format=1, q_descale=1 << 42, d_qk=64, d_v=64), -2),
     (dict(kv_format=3, q_format=1, q_descale=1 << 42, bin_offsets=1 << 43, num_bins=4), -2),  # one-wave plan only
-    (dict(kv_format=5), -1),
+    (dict(kv_format=5), -2),  # NVFP4 needs the e4m3 query
+    (dict(kv_format=5, q_format=1, q_descale=1 << 42), -1),  # ... and its group scales
+    (dict(kv_format=5, q_format=1, q_descale=1 << 42, k_group_scale=1 << 43, v_group_scale=1 << 44,
+          kgs_row_stride=4), -1),
+    (dict(kv_format=6), -1),
 ]
 
 
@@ -179,7 +183,7 @@ def test_decode_kernel_name_follows_the_shapes(native):
     with pytest.raises(native.PkvError):
         native.decode_kernel_name(_valid_args(native, h_q=6, h_k=4))
     assert native.lib.pkv_decode_kernel_name(None) is None
-    for fmt in (native.PKV_KV_E2M1, native.PKV_KV_E2M3, native.PKV_KV_E3M2):
+    for fmt in (native.PKV_KV_E2M1, native.PKV_KV_E2M3, native.PKV_KV_E3M2, native.PKV_KV_NVFP4):
         narrow = _valid_args(native, kv_format=fmt, q_format=native.PKV_Q_E4M3, q_descale=1 << 42)
         assert native.decode_kernel_name(narrow) == "gqa_decode_kernel", fmt
 

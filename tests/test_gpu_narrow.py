@@ -1,4 +1,4 @@
-"""GPU parity of the packed narrow K/V decodes (fp4 e2m1, fp6 e2m3 and e3m2)
+"""GPU parity of the packed narrow K/V decodes (fp4 e2m1, fp6 e2m3 and e3m2, NVFP4)
 against the fp64 oracle, through the C ABI: the page's narrow KV formats with
 an e4m3 query, on small variants of each format's workload (one and two
 16-row blocks, causal tail and block mode, split and unsplit sequences,
@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 FP8_SHORT_TOL = 0.07
 EDGE_LENS = [0, 1, 2, 3, 15, 16, 17, 31, 32, 33, 127, 128, 129, 255, 256, 257, 1000, 1025]
 # workload index of each format: the fully-fp8 batch with that K/V format
-FORMATS = {"e2m1": 6, "e2m3": 7, "e3m2": 8}
+FORMATS = {"e2m1": 6, "e2m3": 7, "e3m2": 8, "nvfp4": 10}
 
 
 def _decode():
