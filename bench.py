@@ -355,8 +355,9 @@ def main():
     ap.add_argument("--page-size", type=int, default=None, help="override the workload's page size")
     ap.add_argument("--contiguous-pages", action="store_true", help="hand out pages in order instead of shuffled")
     ap.add_argument("--seq-len", type=int, default=None, help="give every sequence this length")
-    ap.add_argument("--plan", default="wave", choices=["wave", "balanced", "queued"],
-                    help="wave: one work item per workgroup (occupancy-pinned split plan); balanced: contiguous "
+    ap.add_argument("--plan", default="wave", choices=["wave", "even", "balanced", "queued"],
+                    help="wave: one work item per workgroup (occupancy-pinned split plan); even: the same rule with "
+                         "equal 32-key-block pieces per sequence; balanced: contiguous "
                          "equal shares of all keys, one per workgroup; queued: persistent workgroups, packed "
                          "static bins then a shared queue")
     ap.add_argument("--dyn-percent", type=int, default=10, help="queued plan: share of the work left to the queue")

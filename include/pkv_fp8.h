@@ -23,7 +23,7 @@
  * "Workspace"; "MiniMax MSA fmha_sm100/cute README", Paged FP8 Decode,
  * plan() then run()):
  *   1. pkv_decode_slots()   -> CU count, resident workgroups per CU, q-row tiles
- *   2. pkv_plan_split_kv(), pkv_plan_balanced() or pkv_plan_queued() -> host
+ *   2. pkv_plan_split_kv(), pkv_plan_even(), pkv_plan_balanced() or pkv_plan_queued() -> host
  *      work list + n_splits (+ bin offsets) (pure host code)
  *   3. copy work / n_splits to the device once (the caller's job)
  *   4. pkv_paged_decode_attn(); then pkv_merge_splits() when any sequence
@@ -126,6 +126,21 @@ pkv_status pkv_plan_split_kv(const int32_t* seq_lens, int32_t num_seqs, int32_t 
                              int32_t cu_count, int32_t wg_per_cu, int32_t max_splits, int32_t force_splits,
                              int32_t min_chunk_tiles, int32_t pad_to, int32_t* work_out, int32_t work_cap,
                              int32_t* n_splits_out, pkv_plan_info* info);
+
+/* Even plan (this library's own): the page's occupancy-pinned rule of
+ * pkv_plan_split_kv at 32-key granularity. With blocks_b = max(1,
+ * ceil(L_b / 32)), pick the smallest c >= ceil(max blocks / max_splits) with
+ * sum_b ceil(blocks_b / c) <= slots (slots as in pkv_plan_split_kv; c = the
+ * longest sequence's blocks when num_seqs >= slots), cut sequence b into
+ * k_b = ceil(blocks_b / c) pieces, piece j covering blocks
+ * [j * blocks_b / k_b, (j + 1) * blocks_b / k_b) (floors), and emit the items
+ * (seq, key_begin, key_end, split_slot) in KEYS, longest first (stable).
+ * Pieces of one sequence differ by at most one block, so the longest item is
+ * shorter than with 128-key tiles. Run the decode with work_in_keys = 1.
+ * info->chunk_tiles holds c in 32-key blocks. Errors as pkv_plan_split_kv. */
+pkv_status pkv_plan_even(const int32_t* seq_lens, int32_t num_seqs, int32_t h_k, int32_t n_q_tiles, int32_t cu_count,
+                         int32_t wg_per_cu, int32_t max_splits, int32_t* work_out, int32_t work_cap,
+                         int32_t* n_splits_out, pkv_plan_info* info);
 
 /*
  * Balanced contiguous plan (this library's own planner; not from the pages).
@@ -332,6 +347,11 @@ typedef struct pkv_decode_args {
   int64_t kgs_page_stride, kgs_row_stride, kgs_head_stride;
   const uint8_t* v_group_scale;
   int64_t vgs_page_stride, vgs_row_stride, vgs_head_stride;
+  /* 1: the work items' ranges are in keys (pkv_plan_even; every key_begin a
+   * multiple of 32, else the item is skipped), 0: in 128-key tiles
+   * (pkv_plan_split_kv). The balanced and queued plans are in keys whatever
+   * this says. e4m3 and narrow caches only. */
+  int32_t work_in_keys;
 } pkv_decode_args;
 
 /* Bytes of split workspace: max_splits * num_seqs * h_k * n_rows * (d_v + 2)

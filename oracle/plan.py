@@ -209,3 +209,35 @@ def plan_queued(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16, 
         offsets.append(len(work))
     work.extend(item(i) for i in queue)
     return work, n_splits, offsets, bins, len(queue)
+
+
+def plan_even(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16):
+    """The library's even plan: the occupancy-pinned rule at 32-key
+    granularity (blocks of 32 keys instead of 128-key tiles), each sequence
+    cut into pieces whose block counts differ by at most one. Returns (work
+    list of (seq, key_begin, key_end, split_slot) in keys, longest first,
+    n_splits, c in blocks, slots). A plain scan over c, not a bisection."""
+    seq_lens = [int(x) for x in seq_lens]
+    if not seq_lens:
+        raise ValueError("empty batch")
+    if any(x < 0 for x in seq_lens):
+        raise ValueError("negative sequence length")
+    if min(h_k, n_q_tiles, cu_count, wg_per_cu, max_splits) < 1:
+        raise ValueError("sizes must be positive")
+    blocks = [max(1, _ceil_div(L, BALANCE_BLOCK_KEYS)) for L in seq_lens]
+    slots = max(1, (cu_count * wg_per_cu) // (h_k * n_q_tiles))
+    b_max = max(blocks)
+    c = b_max
+    if len(blocks) < slots and max_splits > 1:
+        for cand in range(_ceil_div(b_max, max_splits), b_max + 1):
+            if sum(_ceil_div(x, cand) for x in blocks) <= slots:
+                c = cand
+                break
+    work, n_splits = [], []
+    for b, x in enumerate(blocks):
+        k = _ceil_div(x, c)
+        n_splits.append(k)
+        cuts = [j * x // k for j in range(k + 1)]
+        work.extend((b, BALANCE_BLOCK_KEYS * cuts[j], BALANCE_BLOCK_KEYS * cuts[j + 1], j) for j in range(k))
+    work.sort(key=lambda w: w[1] - w[2])  # longest first; sort is stable
+    return work, n_splits, c, slots

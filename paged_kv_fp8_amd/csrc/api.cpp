@@ -99,6 +99,9 @@ pkv_status check_pointers(const pkv_decode_args* a, bool for_merge) {
     return fail(PKV_ERR_INVALID_ARG, "bin_offsets needs num_bins >= 1 and 4-B alignment");
   if (narrow_kv(a->kv_format) && (a->bin_offsets || a->queue))
     return fail(PKV_ERR_UNSUPPORTED, "fp4/fp6 cache: only the one-wave plan (pkv_plan_split_kv) is built");
+  if (a->work_in_keys != 0 && a->work_in_keys != 1)
+    return fail(PKV_ERR_INVALID_ARG, "work_in_keys=%d must be 0 or 1", a->work_in_keys);
+  if (a->work_in_keys && mla) return fail(PKV_ERR_UNSUPPORTED, "latent cache: plans in 128-key tiles only");
   if (a->kv_format == PKV_KV_NVFP4) {
     if (!a->k_group_scale || !a->v_group_scale)
       return fail(PKV_ERR_INVALID_ARG, "NVFP4 cache: k_group_scale and v_group_scale must be non-NULL");

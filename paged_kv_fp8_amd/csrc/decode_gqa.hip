@@ -888,6 +888,7 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
   if (w.z <= w.y || b < 0 || b >= p.num_seqs) return;  // padding item / bad entry
   const int page_size = 1 << p.page_shift;
   const int k_begin = w.y * p.key_mult;
+  if (k_begin & (kBlockKeys - 1)) return;  // a key plan's items start on 32-key blocks (16-key groups stay in a page)
   // planned end of the chunk (the plan's lengths are upper bounds of the runtime ones)
   const int plan_last = min(w.z * p.key_mult, p.max_blocks * page_size) - 1;
   const int32_t* bt = p.block_table + (int64_t)b * p.bt_row;
@@ -1645,7 +1646,7 @@ hipError_t gqa_launch(const pkv_decode_args& a, const GqaVariant& v, hipStream_t
   p.vs_page = a.vgs_page_stride;
   p.vs_row = a.vgs_row_stride;
   p.vs_head = a.vgs_head_stride;
-  p.key_mult = (a.bin_offsets && a.queue) ? 1 : kTileKeys;
+  p.key_mult = ((a.bin_offsets && a.queue) || a.work_in_keys) ? 1 : kTileKeys;
   p.num_work = a.num_work;
   p.scale_log2e = (float)((double)a.softmax_scale * 1.4426950408889634);
   p.scale = a.softmax_scale;

@@ -113,6 +113,77 @@ extern "C" pkv_status pkv_plan_split_kv(const int32_t* seq_lens, int32_t num_seq
   return PKV_OK;
 }
 
+// Even plan (this library's own; see pkv_fp8.h): the rule above at 32-key
+// granularity, each sequence cut into pieces as equal as 32-key blocks allow.
+extern "C" pkv_status pkv_plan_even(const int32_t* seq_lens, int32_t num_seqs, int32_t h_k, int32_t n_q_tiles,
+                                    int32_t cu_count, int32_t wg_per_cu, int32_t max_splits, int32_t* work_out,
+                                    int32_t work_cap, int32_t* n_splits_out, pkv_plan_info* info) {
+  using pkv::fail;
+  if (!seq_lens || !work_out || !n_splits_out) return fail(PKV_ERR_INVALID_ARG, "plan: NULL array");
+  if (num_seqs < 1) return fail(PKV_ERR_INVALID_ARG, "plan: num_seqs=%d < 1", num_seqs);
+  if (h_k < 1 || n_q_tiles < 1 || cu_count < 1 || wg_per_cu < 1 || max_splits < 1)
+    return fail(PKV_ERR_INVALID_ARG, "plan: sizes must be >= 1");
+  if (work_cap < 0) return fail(PKV_ERR_INVALID_ARG, "plan: work_cap must be >= 0");
+  if (max_splits > PKV_MAX_SPLITS)
+    return fail(PKV_ERR_UNSUPPORTED, "plan: max_splits=%d > %d", max_splits, PKV_MAX_SPLITS);
+  std::vector<int64_t> blocks(num_seqs);
+  int64_t b_max = 1;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    if (seq_lens[b] < 0) return fail(PKV_ERR_INVALID_ARG, "plan: seq_lens[%d]=%d < 0", b, seq_lens[b]);
+    blocks[b] = std::max<int64_t>(1, ceil_div(seq_lens[b], kBalanceBlockKeys));
+    b_max = std::max(b_max, blocks[b]);
+  }
+  const int64_t slots = std::max<int64_t>(1, ((int64_t)cu_count * wg_per_cu) / ((int64_t)h_k * n_q_tiles));
+  const int64_t lo = ceil_div(b_max, max_splits);
+  auto n_pieces = [&](int64_t c) {
+    int64_t s = 0;
+    for (int64_t x : blocks) s += ceil_div(x, c);
+    return s;
+  };
+  int64_t c = b_max;
+  if (num_seqs < slots && max_splits > 1) {
+    int64_t a = lo, z = b_max;  // n_pieces is non-increasing in c; b_max always fits
+    while (a < z) {
+      const int64_t mid = a + (z - a) / 2;
+      if (n_pieces(mid) <= slots)
+        z = mid;
+      else
+        a = mid + 1;
+    }
+    c = a;
+  }
+  std::vector<Item> items;
+  int32_t max_ns = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t k = ceil_div(blocks[b], c);  // <= max_splits since c >= lo
+    n_splits_out[b] = (int32_t)k;
+    max_ns = std::max<int32_t>(max_ns, (int32_t)k);
+    for (int64_t j = 0; j < k; ++j)  // piece j: blocks [j * n / k, (j + 1) * n / k)
+      items.push_back({b, (int32_t)(kBalanceBlockKeys * ((j * blocks[b]) / k)),
+                       (int32_t)(kBalanceBlockKeys * (((j + 1) * blocks[b]) / k)), (int32_t)j});
+  }
+  std::stable_sort(items.begin(), items.end(),
+                   [](const Item& x, const Item& y) { return (x.end - x.begin) > (y.end - y.begin); });
+  const int64_t n = (int64_t)items.size();
+  if (n > work_cap) return fail(PKV_ERR_CAPACITY, "plan: %lld work items > work_cap=%d", (long long)n, work_cap);
+  for (int64_t i = 0; i < n; ++i) {
+    work_out[4 * i + 0] = items[i].seq;
+    work_out[4 * i + 1] = items[i].begin;
+    work_out[4 * i + 2] = items[i].end;
+    work_out[4 * i + 3] = items[i].slot;
+  }
+  if (info) {
+    info->num_work = (int32_t)n;
+    info->num_real = (int32_t)n;
+    info->chunk_tiles = (int32_t)c;  // here in 32-key blocks
+    info->slots = (int32_t)std::min<int64_t>(slots, INT32_MAX);
+    info->max_n_splits = max_ns;
+    info->num_bins = 0;
+    info->num_dynamic = 0;
+  }
+  return PKV_OK;
+}
+
 // Balanced contiguous plan (this library's own; see pkv_fp8.h): tiles of all
 // sequences end to end, cut into `bins` equal contiguous shares.
 extern "C" pkv_status pkv_plan_balanced(const int32_t* seq_lens, int32_t num_seqs, int32_t h_k, int32_t n_q_tiles,

@@ -126,6 +126,11 @@ class PagedDecode:
             # taken / retired counters per (kv-head group, q tile): zeroed once, left zero by every call
             self.queue = torch.zeros(2 * h_k * n_q_tiles, dtype=torch.int32, device=dev)
             a.queue = _ptr(self.queue)
+        elif plan == "even":  # the same rule at 32-key granularity, equal pieces per sequence (key ranges)
+            if mla:
+                raise ValueError("the even plan is built for the e4m3 and narrow caches")
+            work, n_splits, info = native.plan_even(lens, h_k, n_q_tiles, cu, self.wg_per_cu, max_splits)
+            a.work_in_keys = 1
         elif plan == "wave":  # the occupancy-pinned one-wave plan
             work, n_splits, info = native.plan_split_kv(lens, h_k, n_q_tiles, cu, self.wg_per_cu, max_splits,
                                                         force_splits, min_chunk_tiles, pad_to)

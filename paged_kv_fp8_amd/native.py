@@ -20,7 +20,7 @@ PKV_MAX_SPLITS = 256
 
 # Every function the header declares, in declaration order.
 EXPORTS = ("pkv_status_string", "pkv_last_error", "pkv_version", "pkv_decode_args_size", "pkv_plan_split_kv",
-           "pkv_plan_balanced", "pkv_plan_queued", "pkv_workspace_bytes", "pkv_decode_slots", "pkv_paged_decode_attn",
+           "pkv_plan_even", "pkv_plan_balanced", "pkv_plan_queued", "pkv_workspace_bytes", "pkv_decode_slots", "pkv_paged_decode_attn",
            "pkv_merge_splits", "pkv_quantize_q", "pkv_quant_q_args_size", "pkv_write_kv", "pkv_kv_write_args_size",
            "pkv_decode_kernel_name", "pkv_sparse_workspace_bytes", "pkv_sparse_decode", "pkv_sparse_tiles", "pkv_sparse_merge",
            "pkv_sparse_args_size")
@@ -68,6 +68,7 @@ class DecodeArgs(ctypes.Structure):
         ("queue", _vp),
         ("k_group_scale", _vp), ("kgs_page_stride", _i64), ("kgs_row_stride", _i64), ("kgs_head_stride", _i64),
         ("v_group_scale", _vp), ("vgs_page_stride", _i64), ("vgs_row_stride", _i64), ("vgs_head_stride", _i64),
+        ("work_in_keys", _i32),
     ]
 
 
@@ -140,6 +141,8 @@ def _load():
     lib.pkv_plan_split_kv.restype = _i32
     lib.pkv_plan_split_kv.argtypes = [P(_i32), _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, P(_i32), _i32,
                                       P(_i32), P(PlanInfo)]
+    lib.pkv_plan_even.restype = _i32
+    lib.pkv_plan_even.argtypes = [P(_i32), _i32, _i32, _i32, _i32, _i32, _i32, P(_i32), _i32, P(_i32), P(PlanInfo)]
     lib.pkv_plan_balanced.restype = _i32
     lib.pkv_plan_balanced.argtypes = [P(_i32), _i32, _i32, _i32, _i32, _i32, _i32, P(_i32), _i32, P(_i32), P(_i32),
                                       _i32, P(PlanInfo)]
@@ -215,6 +218,20 @@ def plan_split_kv(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16
                                ns.ctypes.data_as(P), ctypes.byref(info))
     _check(st, "pkv_plan_split_kv")
     return work[:info.num_work].copy(), ns[:nseq].copy(), info
+
+
+def plan_even(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16):
+    """pkv_plan_even: (work (n, 4) int32 in keys, n_splits, PlanInfo)."""
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    cap = int(max(1, -(-int(lens.max(initial=0)) // 32)) * len(lens)) + 1
+    work = np.zeros((cap, 4), dtype=np.int32)
+    n_splits = np.zeros(len(lens), dtype=np.int32)
+    info = PlanInfo()
+    P = ctypes.POINTER(_i32)
+    _check(lib.pkv_plan_even(lens.ctypes.data_as(P), len(lens), h_k, n_q_tiles, cu_count, wg_per_cu, max_splits,
+                             work.ctypes.data_as(P), cap, n_splits.ctypes.data_as(P), ctypes.byref(info)),
+           "pkv_plan_even")
+    return work[:info.num_work].copy(), n_splits, info
 
 
 def plan_balanced(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16):

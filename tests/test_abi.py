@@ -218,6 +218,39 @@ def test_library_balanced_planner_equals_oracle(native, seed):
     assert (info.num_bins, info.num_work, info.max_n_splits) == (bins, len(work), max(ns))
 
 
+@pytest.mark.parametrize("seed", range(40))
+def test_library_even_planner_equals_oracle(native, seed):
+    from oracle.plan import plan_even
+    rng = np.random.default_rng(5000 + seed)
+    b = int(rng.integers(1, 130))
+    lens = np.where(rng.random(b) < 0.15, rng.integers(8192, 70000, size=b), rng.integers(0, 5000, size=b))
+    kw = dict(h_k=int(rng.choice([1, 2, 4, 8])), n_q_tiles=int(rng.integers(1, 3)), cu_count=256,
+              wg_per_cu=int(rng.integers(1, 9)), max_splits=int(rng.choice([1, 2, 8, 16, 64, 256])))
+    work, ns, c, slots = plan_even(lens.tolist(), **kw)
+    w2, ns2, info = native.plan_even(lens, kw["h_k"], kw["n_q_tiles"], kw["cu_count"], kw["wg_per_cu"],
+                                     kw["max_splits"])
+    assert w2.tolist() == [list(x) for x in work]
+    assert ns2.tolist() == ns
+    assert (info.chunk_tiles, info.slots, info.num_work, info.max_n_splits) == (c, slots, len(work), max(ns))
+
+
+def test_even_planner_errors(native):
+    lens = np.array([100, 200], dtype=np.int32)
+    with pytest.raises(native.PkvError):
+        native.plan_even(lens, 0, 1, 256)
+    with pytest.raises(native.PkvError):
+        native.plan_even(np.array([-5], dtype=np.int32), 1, 1, 256)
+    with pytest.raises(native.PkvError):
+        native.plan_even(lens, 1, 1, 256, max_splits=native.PKV_MAX_SPLITS + 1)
+
+
+def test_decode_rejects_bad_work_units(native):
+    for over, code in ((dict(work_in_keys=2), -1), (dict(work_in_keys=1, kv_format=1, h_k=1, h_q=16, d_qk=576,
+                                                             d_v=512, v=None), -2)):
+        st = native.lib.pkv_paged_decode_attn(ctypes.byref(_valid_args(native, **over)), None)
+        assert st == code, (over, native.last_error())
+
+
 @pytest.mark.parametrize("seed", range(30))
 def test_library_queued_planner_equals_oracle(native, seed):
     rng = np.random.default_rng(4000 + seed)

@@ -444,3 +444,63 @@ def test_queued_plan_bitwise_repeats_and_graph_replay():
         assert torch.equal(dec.o.view(torch.int16), ref_o.view(torch.int16)), f"replay {rep}"
         assert torch.equal(dec.lse.view(torch.int32), ref_l.view(torch.int32)), f"replay {rep}"
         assert int(dec.queue.abs().sum()) == 0
+
+
+# ---------------------------------------------------------------------------
+# even plan: one item per workgroup, pieces in 32-key blocks (key ranges)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", list(SMALL))
+def test_even_plan_small_workloads(name):
+    kw = dict(SMALL[name])
+    w = workload(kw.pop("index"), **kw)
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch, plan="even")
+    assert dec.args.work_in_keys == 1
+    compare(batch, dec, what=f"even {name}")
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_even_plan_full_workloads_sampled(name):
+    idx, over = FULL[name]
+    w = workload(idx, **over)
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch, plan="even")
+    lens = batch.seq_lens.cpu().numpy()
+    seqs = _sample(lens, np.random.default_rng(idx + 70))
+    err_o, err_l, _ = compare(batch, dec, seqs=seqs, what=f"even {name}")
+    print(f"even {name}: items={dec.plan_info.num_work} c={dec.plan_info.chunk_tiles} blocks "
+          f"max_splits_used={dec.plan_info.max_n_splits} max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
+
+
+@pytest.mark.parametrize("q_format,q_len,causal,ps", [("bf16", 1, True, 16), ("bf16", 4, True, 64),
+                                                      ("e4m3", 2, False, 128)])
+def test_even_plan_edge_lengths(q_format, q_len, causal, ps):
+    idx = 4 if q_format == "e4m3" else 2
+    h_q, h_k = (64, 4) if q_format == "e4m3" else (16, 2)
+    w = workload(idx, num_seqs=len(EDGE_LENS), q_len=q_len, h_q=h_q, h_k=h_k, page_size=ps, causal=causal,
+                 seq_len_dist=("fixed", EDGE_LENS), max_splits=8)
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch, plan="even", plan_cu_count=8)  # few slots: several pieces per long sequence
+    tol = FP8_SHORT_TOL if q_format == "e4m3" else O_TOL
+    compare(batch, dec, o_tol=tol, what=f"even edge {q_format} q_len={q_len}")
+
+
+def test_even_plan_narrow_format_fused_merge_and_graph():
+    w = workload(6, num_seqs=10, seq_len_dist=("mix", 0.3, (5000, 15000), (1024, 3000)))
+    batch = make_batch(w, device="cuda")
+    dec = _decode().for_batch(batch, plan="even", fused_merge=True)
+    dec.run()
+    torch.cuda.synchronize()
+    assert dec.has_splits
+    compare(batch, dec, what="even fp4 + fused merge")
+    ref_o = dec.o.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dec.run()
+    for rep in range(3):
+        dec.o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dec.o.view(torch.int16), ref_o.view(torch.int16)), f"replay {rep}"
+    assert int(dec.merge_counters.abs().sum()) == 0

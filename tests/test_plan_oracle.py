@@ -237,3 +237,56 @@ def test_queued_invariants(seed):
         assert [w[3] for w in items] == list(range(len(items))) and ns[s] == len(items)
         assert max(size(w) for w in items) - min(size(w) for w in items) <= 1  # even cut
     assert max(ns) <= kw["max_splits"]
+
+
+from oracle.plan import plan_even, plan_split_kv as _tile_plan  # noqa: E402
+
+
+def test_even_hand_worked():
+    # blocks of 32 keys: [10, 4, 1], 4 slots; c = 1..4 give 15, 8, 7, 5 pieces,
+    # c = 5 gives 2 + 1 + 1 = 4
+    work, ns, c, slots = plan_even([300, 100, 0], h_k=1, n_q_tiles=1, cu_count=4)
+    assert (c, slots, ns) == (5, 4, [2, 1, 1])
+    assert work == [(0, 0, 160, 0), (0, 160, 320, 1), (1, 0, 128, 0), (2, 0, 32, 0)]
+
+
+def test_even_unequal_pieces_differ_by_one_block():
+    # 7 blocks in 3 pieces: cuts at 7*1//3 = 2 and 7*2//3 = 4 -> 2, 2, 3 blocks
+    work, ns, c, slots = plan_even([224], h_k=1, n_q_tiles=1, cu_count=3)
+    assert c == 3 and ns == [3]
+    assert work == [(0, 128, 224, 2), (0, 0, 64, 0), (0, 64, 128, 1)]
+
+
+def test_even_errors():
+    with pytest.raises(ValueError):
+        plan_even([], h_k=1, n_q_tiles=1, cu_count=1)
+    with pytest.raises(ValueError):
+        plan_even([-1], h_k=1, n_q_tiles=1, cu_count=1)
+    with pytest.raises(ValueError):
+        plan_even([10], h_k=0, n_q_tiles=1, cu_count=1)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_even_invariants(seed):
+    rng = np.random.default_rng(700 + seed)
+    n = int(rng.integers(1, 90))
+    lens = rng.integers(0, 20000, size=n).tolist()
+    kw = dict(h_k=int(rng.choice([1, 2, 4, 8])), n_q_tiles=int(rng.integers(1, 3)), cu_count=256,
+              wg_per_cu=int(rng.integers(1, 9)), max_splits=int(rng.choice([1, 4, 16, 64])))
+    work, ns, c, slots = plan_even(lens, **kw)
+    if len(lens) < slots and kw["max_splits"] > 1:
+        assert len(work) <= slots
+    lengths = [w[2] - w[1] for w in work]
+    assert lengths == sorted(lengths, reverse=True)
+    for b, L in enumerate(lens):
+        mine = sorted((w for w in work if w[0] == b), key=lambda w: w[1])
+        assert len(mine) == ns[b] <= kw["max_splits"]
+        assert [w[3] for w in mine] == list(range(ns[b]))
+        assert mine[0][1] == 0 and mine[-1][2] == 32 * max(1, -(-L // 32))
+        assert all(x[2] == y[1] for x, y in zip(mine, mine[1:]))  # contiguous cover
+        assert all(w[1] % 32 == 0 and w[2] > w[1] for w in mine)
+        sizes = [(w[2] - w[1]) // 32 for w in mine]
+        assert max(sizes) - min(sizes) <= 1 and max(sizes) <= c
+    # never a longer item than the 128-key tile plan of the same batch
+    twork = _tile_plan(lens, **kw)[0]
+    assert max(lengths) <= max((w[2] - w[1]) * 128 for w in twork)
