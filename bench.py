@@ -115,7 +115,8 @@ def cpu_oracle_baseline(batch, budget_s):
     done, kv = 0, 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        for b in range(w.num_seqs):
+        for i in range(1 << 30):  # whole passes over the batch until the budget is spent
+            b = i % w.num_seqs
             sl = slice(b * w.q_len, (b + 1) * w.q_len)
             if w.kv_format == "mla":
                 mla_decode_attention(nb["q"][sl], nb["latent"], nb["rope"], nb["scales"], nb["block_table"][b:b + 1],
@@ -125,15 +126,19 @@ def cpu_oracle_baseline(batch, budget_s):
                 decode_attention(nb["q"][sl], nb["k_cache"], nb["v_cache"], nb["block_table"][b:b + 1],
                                  lens[b:b + 1], nb["q_descale"][b:b + 1], nb["k_descale"][b:b + 1],
                                  nb["v_descale"][b:b + 1], q_len=w.q_len, h_k=w.h_k, softmax_scale=w.scale,
-                                 causal=w.causal, kv_format=w.kv_format)
-                kv += int(lens[b]) * w.h_k * (nb["k_cache"].shape[-1] + nb["v_cache"].shape[-1])  # stored row bytes
+                                 causal=w.causal, kv_format=w.kv_format, k_scale=nb.get("k_scale"),
+                                 v_scale=nb.get("v_scale"))
+                row_bytes = nb["k_cache"].shape[-1] + nb["v_cache"].shape[-1]  # stored bytes per token and head
+                if "k_scale" in nb:
+                    row_bytes += nb["k_scale"].shape[-1] + nb["v_scale"].shape[-1]
+                kv += int(lens[b]) * w.h_k * row_bytes
             done += 1
             if time.perf_counter() - t0 >= budget_s:
                 break
         dt = time.perf_counter() - t0
     return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {done} of {w.num_seqs} sequences ({kv} KV bytes, all heads and rows) in {dt:.1f} s, "
-                      f"numpy fp64, one BLAS thread"}
+            "sample": f"{done} sequences in order, cycling over the {w.num_seqs} of the batch ({kv} KV bytes, all "
+                      f"heads and rows) in {dt:.1f} s, numpy fp64, one BLAS thread"}
 
 
 def sparse_cpu_baseline(batch, budget_s):
@@ -148,7 +153,8 @@ def sparse_cpu_baseline(batch, budget_s):
     done, kv = 0, 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        for t in range(batch.spec.num_tokens):
+        for i in range(1 << 30):  # whole passes over the tokens until the budget is spent
+            t = i % batch.spec.num_tokens
             srcs = [dict(s, slots=s["slots"][t:t + 1]) for s in nb["sources"]]
             sparse_decode_attention(nb["q"][t:t + 1], srcs, softmax_scale=batch.spec.scale, sink=nb["sink"])
             kv += sum(int((s["slots"] >= 0).sum()) for s in srcs) * 656
@@ -157,8 +163,8 @@ def sparse_cpu_baseline(batch, budget_s):
                 break
         dt = time.perf_counter() - t0
     return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {done} of {batch.spec.num_tokens} tokens ({kv} record bytes, all heads) in {dt:.1f} s, "
-                      f"numpy fp64, one BLAS thread"}
+            "sample": f"{done} tokens in order, cycling over the {batch.spec.num_tokens} of the step ({kv} record "
+                      f"bytes, all heads) in {dt:.1f} s, numpy fp64, one BLAS thread"}
 
 
 def bench_sparse(args):
