@@ -57,7 +57,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int kD = 128;          // head dim (qk and v)
 constexpr int kTileKeys = 128;   // planner tile
 constexpr int kBlockKeys = 32;   // keys per main-loop step
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kP8Scale = 448.0f;  // fp8 P is stored as e4m3(p * 448)
 constexpr float kLazyLog2 = 8.0f;   // bf16 P: reference max may lag until p would exceed 2^8
 
