@@ -115,3 +115,19 @@ def test_narrow_bitwise_repeats_graph_replay_and_fused_merge(fmt):
         torch.cuda.synchronize()
         assert torch.equal(fused.o.view(torch.int16), ref_o.view(torch.int16)), f"fused {rep}"
         assert int(fused.merge_counters.abs().sum()) == 0
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_narrow_layouts_bit_identical(fmt):
+    # the same codes in the head-major (HND) layout give bit-identical outputs
+    lens = ("uniform", 1024, 6000)
+    outs = []
+    for layout in ("nhd", "hnd"):
+        w = workload(FORMATS[fmt], num_seqs=6, seq_len_dist=lens, kv_layout=layout)
+        batch = make_batch(w, device="cuda")
+        dec = run(batch)
+        outs.append((dec.o.clone(), dec.lse.clone(), batch))
+    (o1, l1, b1), (o2, l2, b2) = outs
+    assert torch.equal(b1.k_cache.contiguous(), b2.k_cache.contiguous())  # same codes, other strides
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
