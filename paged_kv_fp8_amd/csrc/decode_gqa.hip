@@ -90,6 +90,8 @@ struct GqaParams {
   int num_seqs, q_len, h_k, h_r, rows, page_shift, num_pages, max_blocks, max_splits;
   int key_mult;  // keys per unit of a work item's range: 128 (tile plans) or 1 (key plans)
   int num_work;
+  int q_tiles;    // q-row tiles per work item
+  int xcd_tiles;  // one-item form with q_tiles > 1: blockIdx.x enumerates (item, tile), tiles of an item on one XCD
   const uint8_t* ks;  // NVFP4: e4m3 group scales of K and V (one byte per 16 values)
   int64_t ks_page, ks_row, ks_head;  // bytes
   const uint8_t* vs;
@@ -775,7 +777,7 @@ __device__ __forceinline__ void process_block_fp6(const RawBlock6& cur, int kb, 
 // this (sequence, head, q tile) combines all of them.
 template <bool FP8Q, int NB>
 __device__ __forceinline__ void finish_item(const GqaParams& p, const RowState<NB>& st, const RowMap<NB>& rm, int b,
-                                            int g, int row0, int r16, int g4, int ns, int slot, float cs, float vdv) {
+                                            int g, int tile, int row0, int r16, int g4, int ns, int slot, float cs, float vdv) {
   const bool direct = ns <= 1;
   const float p_scale = FP8Q ? kP8Scale : 1.0f;
   int qtok[NB], qhead[NB];
@@ -829,7 +831,7 @@ __device__ __forceinline__ void finish_item(const GqaParams& p, const RowState<N
     // partials and the counter are shared, so no cache-wide write-back or
     // invalidate is needed.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    int32_t* ctr = p.counters + ((int64_t)b * p.h_k + g) * gridDim.z + blockIdx.z;
+    int32_t* ctr = p.counters + ((int64_t)b * p.h_k + g) * p.q_tiles + tile;
     int last = 0;
     if ((threadIdx.x & 63) == 0)
       last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == min(ns, p.max_splits) - 1;
@@ -875,7 +877,7 @@ __device__ __forceinline__ void keep_pace(int* progress, int wave, int done, int
 // depth for the deeper narrow rings (a pair loaded sooner would make its wait
 // cover KV loads still in the ring).
 template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES, int HW, int KVF = 0>
-__device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, int lane, int g, int* progress,
+__device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, int tile, int lane, int g, int* progress,
                                                 int& round_base) {
   static_assert(KVF == 0 || FP8Q, "narrow K/V formats need the e4m3 query");
   constexpr int LA = KVF != 0 && STAGES > 2 ? STAGES - 1 : 2;
@@ -907,7 +909,7 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
   const int slot = w.w;
   int L = p.seq_lens[b];
   if (ns > 1 && (slot < 0 || slot >= p.max_splits)) return;
-  const int row0 = blockIdx.z * (16 * NB);
+  const int row0 = tile * (16 * NB);
 
   L = max(0, min(L, p.max_blocks * page_size));
   const int k_end = min(plan_last + 1, L);
@@ -1022,7 +1024,7 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
     }
     round_base += rounds;
   }
-  finish_item<FP8Q, NB>(p, st, rm, b, g, row0, r16, g4, ns, slot, cs, vdv);
+  finish_item<FP8Q, NB>(p, st, rm, b, g, tile, row0, r16, g4, ns, slot, cs, vdv);
 }
 
 // V rows of keys past `vlast` (loaded through planned block-table entries
@@ -1209,7 +1211,7 @@ __device__ __forceinline__ void gqa_decode_persistent(const GqaParams& p, int la
         if (HW == 8) keep_pace(progress, wave, round_base + r, lane);
       }
       round_base += R;
-      if (c_ok) finish_item<FP8Q, NB>(p, st, rm, C.b, g, row0, r16, g4, C.ns, C.slot, cs, C.vd);
+      if (c_ok) finish_item<FP8Q, NB>(p, st, rm, C.b, g, (int)blockIdx.z, row0, r16, g4, C.ns, C.slot, cs, C.vd);
       if (!n_valid) break;
       // ---- N becomes current: its first S - 1 blocks are in the ring and the
       // pairs of its next fetches in pv
@@ -1324,7 +1326,7 @@ __device__ __forceinline__ void gqa_decode_stream(const GqaParams& p, int lane, 
       prefetch_q(i + 1);
     };
     auto end_item = [&]() {
-      if (c_ok) finish_item<FP8Q, NB>(p, st, rm, c_b, g, row0, r16, g4, c_ns, c_slot, cs, c_vd);
+      if (c_ok) finish_item<FP8Q, NB>(p, st, rm, c_b, g, (int)blockIdx.z, row0, r16, g4, c_ns, c_slot, cs, c_vd);
     };
     auto advance_to = [&](int i) {  // finish items before i (empty ones too), begin item i
       while (cur < i) {
@@ -1398,7 +1400,7 @@ __device__ __forceinline__ void gqa_decode_bin_then_queue(const GqaParams& p, in
   int round_base = 0;
   const int it_end = p.bin_offsets[blockIdx.x + 1];
   for (int it = p.bin_offsets[blockIdx.x]; it < it_end; ++it)
-    if (g < p.h_k) gqa_decode_item<FP8Q, NB, CAUSAL_TAIL, STAGES, HW>(p, it, lane, g, progress, round_base);
+    if (g < p.h_k) gqa_decode_item<FP8Q, NB, CAUSAL_TAIL, STAGES, HW>(p, it, blockIdx.z, lane, g, progress, round_base);
   const int q0 = p.bin_offsets[gridDim.x];
   const int col = blockIdx.z * gridDim.y + blockIdx.y;         // < h_k * q tiles
   int* const taken = p.queue + col;                            // queue items handed out (+ one per final take)
@@ -1411,7 +1413,7 @@ __device__ __forceinline__ void gqa_decode_bin_then_queue(const GqaParams& p, in
     const int it = __builtin_amdgcn_readfirstlane(next_item);
     __syncthreads();  // everyone has read next_item before it is written again
     if (it >= p.num_work) break;
-    if (g < p.h_k) gqa_decode_item<FP8Q, NB, CAUSAL_TAIL, STAGES, HW>(p, it, lane, g, progress, round_base);
+    if (g < p.h_k) gqa_decode_item<FP8Q, NB, CAUSAL_TAIL, STAGES, HW>(p, it, blockIdx.z, lane, g, progress, round_base);
   }
   // The workgroup that retires last has seen every other one finish taking,
   // so nobody reads the counters again in this launch: it clears both for the
@@ -1432,6 +1434,19 @@ __device__ __forceinline__ void gqa_decode_bin_then_queue(const GqaParams& p, in
 // parking values in AGPRs when the workgroup would allow one wave per SIMD:
 // one row block fits as is, two row blocks of the one-item form fit with the
 // query in LDS. The streaming form of two row blocks gets the whole file.
+// Workgroup id -> (work item, q-row tile) so that the tiles of one item get
+// ids i, i + 8, i + 16, ...: consecutive ids go to the 8 XCDs in turn, so
+// an item's tiles run at about the same time on one XCD and the later ones
+// read the item's pages from that XCD's L2.
+__device__ __forceinline__ void xcd_item_tile(int id, int units, int tiles, int& unit, int& tile) {
+  constexpr int kXcds = 8;
+  const int chunk = id / (kXcds * tiles);
+  const int local = id - chunk * kXcds * tiles;
+  const int left = min(kXcds, units - chunk * kXcds);
+  unit = chunk * kXcds + local % left;
+  tile = local / left;
+}
+
 template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES, int HW, bool STREAM, int KVF = 0>
 __global__ __launch_bounds__(64 * HW) __attribute__((amdgpu_waves_per_eu(NB == 1 || !STREAM ? 2 : 1)))
 void gqa_decode_kernel(GqaParams p) {
@@ -1442,10 +1457,12 @@ void gqa_decode_kernel(GqaParams p) {
     __syncthreads();
   }
   const int g = __builtin_amdgcn_readfirstlane(blockIdx.y * HW + (threadIdx.x >> 6));  // wave-uniform
+  // one-item form: the work item and q-row tile of this workgroup
+  int item = blockIdx.x, tile = blockIdx.z;
+  if (p.xcd_tiles) xcd_item_tile(blockIdx.x, p.num_work, p.q_tiles, item, tile);
   if constexpr (KVF != 0) {  // packed narrow K/V: the one-item form
     int round_base = 0;
-    if (g < p.h_k)
-      gqa_decode_item<FP8Q, NB, CAUSAL_TAIL, STAGES, HW, KVF>(p, blockIdx.x, lane, g, progress, round_base);
+    if (g < p.h_k) gqa_decode_item<FP8Q, NB, CAUSAL_TAIL, STAGES, HW, KVF>(p, item, tile, lane, g, progress, round_base);
     return;
   }
   if (STREAM) {
@@ -1454,7 +1471,7 @@ void gqa_decode_kernel(GqaParams p) {
   }
   if (!p.queue) {
     int round_base = 0;
-    if (g < p.h_k) gqa_decode_item<FP8Q, NB, CAUSAL_TAIL, STAGES, HW>(p, blockIdx.x, lane, g, progress, round_base);
+    if (g < p.h_k) gqa_decode_item<FP8Q, NB, CAUSAL_TAIL, STAGES, HW>(p, item, tile, lane, g, progress, round_base);
     return;
   }
   // queued plan: persistent workgroups
@@ -1556,6 +1573,9 @@ GqaVariant gqa_variant(const pkv_decode_args& a) {
   v.fp8_q = a.q_format == PKV_Q_E4M3;
   v.kvf = narrow_kv(a.kv_format) ? a.kv_format : 0;
   const int rows = a.q_len * (a.h_q / a.h_k);
+  // two 16-row blocks per wave up to 32 rows: splitting them over two
+  // workgroups (one block per wave) measured 124 vs 96 us on the
+  // speculative-verify workload
   v.n_blocks = rows <= 16 ? 1 : 2;
   v.causal_tail = a.causal && a.q_len > 1;
   v.stream = a.bin_offsets != nullptr && a.queue == nullptr;
@@ -1661,7 +1681,10 @@ hipError_t gqa_launch(const pkv_decode_args& a, const GqaVariant& v, hipStream_t
   p.max_splits = a.max_splits;
   const int tiles = (p.rows + gqa_rows_per_tile(v) - 1) / gqa_rows_per_tile(v);
   const int hw = v.heads_per_wg;
+  p.q_tiles = tiles;
+  p.xcd_tiles = !a.bin_offsets && tiles > 1;
   dim3 grid(a.bin_offsets ? a.num_bins : a.num_work, (a.h_k + hw - 1) / hw, tiles);  // bins: balanced or queued plan
+  if (p.xcd_tiles) grid = dim3(a.num_work * tiles, (a.h_k + hw - 1) / hw, 1);
   void* args[] = {&p};
   return hipLaunchKernel(select_kernel(v), grid, dim3(64 * hw), args, gqa_dyn_lds(v), stream);
 }
