@@ -58,6 +58,7 @@ constexpr int kD = 128;          // head dim (qk and v)
 constexpr int kTileKeys = 128;   // planner tile
 constexpr int kBlockKeys = 32;   // keys per main-loop step
 constexpr float kP8Scale = 448.0f;  // fp8 P is stored as e4m3(p * 448)
+constexpr float kLog2P8Scale = 8.807354922057604f;  // log2(448): p * 448 = exp2(... + log2 448)
 constexpr float kLazyLog2 = 8.0f;   // bf16 P: reference max may lag until p would exceed 2^8
 
 struct GqaParams {
@@ -507,11 +508,14 @@ __device__ __forceinline__ void softmax_pv(f32x4 (&sacc)[NB][2], const uint2 (&v
     const float m_new = move ? m_max : st.m_run[nb];
     const float m_use = m_new == -INFINITY ? 0.f : m_new;  // no visible key yet: exp2(-inf) = 0
     const float corr = __builtin_amdgcn_exp2f((st.m_run[nb] - m_use) * c2);
+    // one fma per score: exp2(s c2 - m c2), times 448 for e4m3 P (then l
+    // sums p * 448 too, and the epilogue divides it out)
+    const float off = (FP8Q ? kLog2P8Scale : 0.f) - m_use * c2;
     float pr[8];
     float psum = 0.f;
     for (int t = 0; t < 2; ++t)
       for (int i = 0; i < 4; ++i) {
-        pr[4 * t + i] = __builtin_amdgcn_exp2f((sacc[nb][t][i] - m_use) * c2);
+        pr[4 * t + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[nb][t][i], c2, off));
         psum += pr[4 * t + i];
       }
     st.l_part[nb] = st.l_part[nb] * corr + psum;
@@ -521,10 +525,10 @@ __device__ __forceinline__ void softmax_pv(f32x4 (&sacc)[NB][2], const uint2 (&v
     }
     st.m_run[nb] = m_new;
     if (FP8Q) {
-      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0] * kP8Scale, pr[1] * kP8Scale, 0, false);
-      lo = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2] * kP8Scale, pr[3] * kP8Scale, lo, true);
-      int hi = __builtin_amdgcn_cvt_pk_fp8_f32(pr[4] * kP8Scale, pr[5] * kP8Scale, 0, false);
-      hi = __builtin_amdgcn_cvt_pk_fp8_f32(pr[6] * kP8Scale, pr[7] * kP8Scale, hi, true);
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], 0, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], lo, true);
+      int hi = __builtin_amdgcn_cvt_pk_fp8_f32(pr[4], pr[5], 0, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(pr[6], pr[7], hi, true);
       p8[nb] = as_long(uint2{(unsigned)lo, (unsigned)hi});
     } else {
       for (int e = 0; e < 8; ++e) pb[nb][e] = (__bf16)pr[e];
@@ -786,7 +790,7 @@ __device__ __forceinline__ void finish_item(const GqaParams& p, const RowState<N
     qhead[nb] = g * p.h_r + rm.hr[nb];
   }
   for (int nb = 0; nb < NB; ++nb) {
-    const float l = wave_sum16(st.l_part[nb]);
+    const float l = wave_sum16(st.l_part[nb]) / p_scale;  // e4m3 P: l summed p * 448
     if (!rm.ok[nb]) continue;
     const int n = row0 + 16 * nb + r16;
     const int64_t stat_row = ((int64_t)b * p.h_k + g) * p.rows + n;

@@ -504,3 +504,36 @@ def test_even_plan_narrow_format_fused_merge_and_graph():
         torch.cuda.synchronize()
         assert torch.equal(dec.o.view(torch.int16), ref_o.view(torch.int16)), f"replay {rep}"
     assert int(dec.merge_counters.abs().sum()) == 0
+
+
+# ---------------------------------------------------------------------------
+# bf16 query rows of widely different magnitudes (2^-11 .. 2^3 across the
+# rows of one wave) with half of some rows' elements 2^-14 below the rest:
+# every form of the decode keeps each row's own range (a bf16 query is
+# never rescaled or rounded to a narrower format)
+# ---------------------------------------------------------------------------
+def _scale_query_rows_(batch):
+    q = batch.q  # [tokens, h_q, d] bf16
+    t = torch.arange(q.shape[0], device=q.device).view(-1, 1)
+    h = torch.arange(q.shape[1], device=q.device).view(1, -1)
+    expo = ((3 * h + 5 * t) % 15 - 11).to(torch.float32)  # 2^-11 .. 2^3
+    f = torch.exp2(expo).unsqueeze(-1).expand(-1, -1, q.shape[2]).clone()
+    tiny = (h % 3 == 0).expand(q.shape[0], -1)
+    f[..., 64:][tiny] *= 2.0 ** -14
+    q.mul_(f.to(q.dtype))
+
+
+@pytest.mark.parametrize("shape", ["one_row_block", "two_row_blocks"])
+@pytest.mark.parametrize("plan", ["wave", "balanced", "queued"])
+def test_bf16_query_row_magnitudes(shape, plan):
+    if shape == "one_row_block":
+        w = workload(2, num_seqs=5, h_q=32, h_k=2, seq_len_dist=("uniform", 100, 1500))
+    else:
+        w = workload(3, num_seqs=5, seq_len_dist=("lognormal", 700, 1.0, 5, 3000))
+    batch = make_batch(w, device="cuda")
+    _scale_query_rows_(batch)
+    kw = {} if plan == "wave" else (dict(plan="balanced") if plan == "balanced" else
+                                    dict(plan="queued", max_splits=64, wg_per_cu=1, dyn_percent=30))
+    dec = run_batch(batch, **kw)
+    err_o, err_l, _ = compare(batch, dec, what=f"row magnitudes {shape} {plan}")
+    print(f"{shape} {plan}: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
