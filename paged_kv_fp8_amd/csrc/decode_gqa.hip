@@ -1618,11 +1618,12 @@ hipError_t gqa_occupancy(const GqaVariant& v, int* units_per_cu) {
   const hipError_t e =
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&wgs, select_kernel(v), 64 * v.heads_per_wg, gqa_dyn_lds(v));
   const int resident = wgs * v.heads_per_wg;
-  // fp6 K/V: eight units (two waves per SIMD), so that one wave's V
-  // conversion overlaps the other's load waits (measured on the fully-fp8
-  // batch with e2m3 K/V: 178 -> 168 us for the kernel)
-  const bool fp6 = v.kvf == PKV_KV_E2M3 || v.kvf == PKV_KV_E3M2;
-  const int target = v.heads_per_wg > 4 ? v.heads_per_wg : (fp6 ? 8 : 4);
+  // fp6 and NVFP4 K/V: eight units (two waves per SIMD), so that one wave's
+  // conversions overlap the other's load waits (measured on the fully-fp8
+  // batch: e2m3 K/V 178 -> 168 us, NVFP4 K/V 199.5 -> 162 us for the
+  // kernel; fp4 K/V and e4m3 K/V gain nothing or lose)
+  const bool two_waves = v.kvf == PKV_KV_E2M3 || v.kvf == PKV_KV_E3M2 || v.kvf == PKV_KV_NVFP4;
+  const int target = v.heads_per_wg > 4 ? v.heads_per_wg : (two_waves ? 8 : 4);
   *units_per_cu = resident < target ? resident : target;
   return e;
 }
