@@ -157,20 +157,35 @@ __device__ __forceinline__ void merge_rows(const GqaParams& p, int b, int g, int
     const int n = row0 + 16 * nb + r16;
     if (n >= p.rows) continue;
     const int64_t row = ((int64_t)b * p.h_k + g) * p.rows + n;
+    // the separate merge's arithmetic, in the same order (rounds of 16
+    // splits, each weighted by the max so far, earlier sums rescaled when a
+    // round raises it), so that both give the same bits
     float m_star = -INFINITY;
-    for (int j = 0; j < ns; ++j) m_star = fmaxf(m_star, load_coherent(reinterpret_cast<const float*>(p.ws_ml + j * split_stride + row)).x);
     float acc[32];
     for (int e = 0; e < 32; ++e) acc[e] = 0.f;
     float den = 0.f;
-    for (int j = 0; j < ns; ++j) {
-      const float2 ml = load_coherent(reinterpret_cast<const float*>(p.ws_ml + j * split_stride + row));
-      const float wgt = ml.x == -INFINITY ? 0.f : __expf(ml.x - m_star);
-      const float* src = p.ws_o + (j * split_stride + row) * kD + 32 * g4;
-      den += wgt * ml.y;
-      for (int e = 0; e < 32; e += 2) {
-        const float2 v = load_coherent(src + e);
-        acc[e] += wgt * v.x;
-        acc[e + 1] += wgt * v.y;
+    for (int j0 = 0; j0 < ns; j0 += 16) {
+      const int j1 = min(j0 + 16, ns);
+      float m_new = m_star;
+      for (int j = j0; j < j1; ++j)
+        m_new = fmaxf(m_new, load_coherent(reinterpret_cast<const float*>(p.ws_ml + j * split_stride + row)).x);
+      if (m_new == -INFINITY) continue;  // no split of this row saw a key yet
+      if (m_new != m_star) {
+        const float sc = m_star == -INFINITY ? 0.f : __expf(m_star - m_new);
+        for (int e = 0; e < 32; ++e) acc[e] *= sc;
+        den *= sc;
+        m_star = m_new;
+      }
+      for (int j = j0; j < j1; ++j) {
+        const float2 ml = load_coherent(reinterpret_cast<const float*>(p.ws_ml + j * split_stride + row));
+        const float wgt = ml.x == -INFINITY ? 0.f : __expf(ml.x - m_star);
+        const float* src = p.ws_o + (j * split_stride + row) * kD + 32 * g4;
+        den += wgt * ml.y;
+        for (int e = 0; e < 32; e += 2) {
+          const float2 v = load_coherent(src + e);
+          acc[e] += wgt * v.x;
+          acc[e + 1] += wgt * v.y;
+        }
       }
     }
     const float inv = den > 0.f ? p.o_scale / den : 0.f;

@@ -58,12 +58,16 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   ns = min(ns, p.max_splits);
 
   // One round trip for up to kSplitsPerRound splits: the (max, sum) pairs and
-  // the partial rows are independent loads, issued together; the weights
-  // need the overall max, so a longer split list takes the max first.
-  float m_star = -INFINITY;
+  // the partial rows are independent loads, issued together. A longer split
+  // list takes one round trip per round: each round's weights use the max so
+  // far, and what was summed before is rescaled when a round raises it (with
+  // one round, the sums are those of the plain weighted combine).
   float2 ml[kSplitsPerRound];
   f32x4 oj[kSplitsPerRound];
-  auto load_round = [&](int j0) {
+  float m_star = -INFINITY;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  for (int j0 = 0; j0 < ns; j0 += kSplitsPerRound) {
 #pragma unroll
     for (int u = 0; u < kSplitsPerRound; ++u) {
       const bool ok = j0 + u < ns;
@@ -71,25 +75,15 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
       ml[u] = ok ? p.ws_ml[pr] : float2{-INFINITY, 0.f};
       oj[u] = ok ? *reinterpret_cast<const f32x4*>(p.ws_o + pr * DV + 4 * tc) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  };
-  if (ns > kSplitsPerRound) {
-    for (int j0 = 0; j0 < ns; j0 += kSplitsPerRound) {
-      float mj[kSplitsPerRound];
+    float m_new = m_star;
 #pragma unroll
-      for (int u = 0; u < kSplitsPerRound; ++u)
-        mj[u] = j0 + u < ns ? p.ws_ml[(j0 + u) * p.split_stride + row].x : -INFINITY;
-#pragma unroll
-      for (int u = 0; u < kSplitsPerRound; ++u) m_star = fmaxf(m_star, mj[u]);
-    }
-  }
-
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-  for (int j0 = 0; j0 < ns; j0 += kSplitsPerRound) {
-    load_round(j0);
-    if (ns <= kSplitsPerRound) {
-#pragma unroll
-      for (int u = 0; u < kSplitsPerRound; ++u) m_star = fmaxf(m_star, ml[u].x);
+    for (int u = 0; u < kSplitsPerRound; ++u) m_new = fmaxf(m_new, ml[u].x);
+    if (m_new == -INFINITY) continue;  // no split of this row saw a key yet
+    if (m_new != m_star) {
+      const float sc = m_star == -INFINITY ? 0.f : __expf(m_star - m_new);
+      acc *= sc;
+      den *= sc;
+      m_star = m_new;
     }
 #pragma unroll
     for (int u = 0; u < kSplitsPerRound; ++u) {
