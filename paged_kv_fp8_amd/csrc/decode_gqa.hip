@@ -1518,13 +1518,13 @@ const void* kernel_ptr(bool stream) {
                 : reinterpret_cast<const void*>(&gqa_decode_kernel<FP8Q, NB, CT, ring_stages<NB, false>(), HW, false>);
 }
 
-// Packed narrow K/V: one-item form. One row block: a ring of five 4 KB fp4
-// blocks or four 6 KB fp6 blocks (a deeper ring than e4m3's three 8 KB
-// blocks keeps a similar number of bytes in flight; fp6's 15 loads per fetch
-// also bound its depth); two row blocks: three (fp4) or two (fp6, whose
-// conversion needs the registers a third block would take).
+// Packed narrow K/V: one-item form. One row block: a ring of three 4 KB fp4
+// blocks (measured on the fully-fp8 batch with fp4 K/V, ring depths 2-5:
+// 106.8, 105.0, 109.2, 110.6 us) or four 6 KB fp6 blocks (fp6's 15 loads
+// per fetch also bound its depth); two row blocks: three (fp4) or two (fp6,
+// whose conversion needs the registers a third block would take).
 #ifndef PKV_FP4_STAGES
-#define PKV_FP4_STAGES 5
+#define PKV_FP4_STAGES 3
 #endif
 template <int NB, int KVF>
 constexpr int narrow_stages() {
