@@ -1526,11 +1526,19 @@ const void* kernel_ptr(bool stream) {
 #ifndef PKV_FP4_STAGES
 #define PKV_FP4_STAGES 3
 #endif
+#ifndef PKV_FP6_STAGES
+#define PKV_FP6_STAGES 4
+#endif
+// NVFP4, one row block: two blocks (at two waves per SIMD, its plan: 155.6
+// against 164 us with three)
+#ifndef PKV_NV_STAGES
+#define PKV_NV_STAGES 2
+#endif
 template <int NB, int KVF>
 constexpr int narrow_stages() {
   // NVFP4: 23 loads per fetch, so at most two fetches ahead (the load counter holds 63)
-  return KVF == PKV_KV_NVFP4 ? (NB == 2 ? 2 : 3)
-                             : NB == 2 ? (KVF == PKV_KV_E2M1 ? 3 : 2) : KVF == PKV_KV_E2M1 ? PKV_FP4_STAGES : 4;
+  return KVF == PKV_KV_NVFP4 ? (NB == 2 ? 2 : PKV_NV_STAGES)
+                             : NB == 2 ? (KVF == PKV_KV_E2M1 ? 3 : 2) : KVF == PKV_KV_E2M1 ? PKV_FP4_STAGES : PKV_FP6_STAGES;
 }
 
 template <int NB, bool CT, int HW, int KVF>
