@@ -65,7 +65,7 @@ extern "C" {
 typedef int32_t pkv_status;
 #define PKV_OK 0
 #define PKV_ERR_INVALID_ARG (-1) /* null pointer, bad size, misaligned pointer or stride */
-#define PKV_ERR_UNSUPPORTED (-2) /* valid request this build has no kernel for */
+#define PKV_ERR_UNSUPPORTED (-2) /* valid request the library has no kernel for */
 #define PKV_ERR_CAPACITY (-3)    /* an output array is too small (work_cap, pad_to) */
 #define PKV_ERR_WORKSPACE (-4)   /* split workspace missing or too small */
 #define PKV_ERR_HIP (-5)         /* the HIP runtime reported an error */
@@ -437,7 +437,7 @@ typedef struct pkv_quant_q_args {
 
 pkv_status pkv_quantize_q(const pkv_quant_q_args* a, void* stream);
 
-/* sizeof(pkv_quant_q_args) in this build (a binding's layout check) */
+/* sizeof(pkv_quant_q_args) as compiled (a binding's layout check) */
 size_t pkv_quant_q_args_size(void);
 
 /*
@@ -495,7 +495,7 @@ typedef struct pkv_kv_write_args {
 
 pkv_status pkv_write_kv(const pkv_kv_write_args* a, void* stream);
 
-/* sizeof(pkv_kv_write_args) in this build (a binding's layout check) */
+/* sizeof(pkv_kv_write_args) as compiled (a binding's layout check) */
 size_t pkv_kv_write_args_size(void);
 
 /* ------------------------------------------------------------------------ */
@@ -571,7 +571,7 @@ pkv_status pkv_sparse_decode(const pkv_sparse_args* a, void* stream);
 pkv_status pkv_sparse_tiles(const pkv_sparse_args* a, void* stream);
 pkv_status pkv_sparse_merge(const pkv_sparse_args* a, void* stream);
 
-/* sizeof(pkv_sparse_args) in this build (a binding's layout check) */
+/* sizeof(pkv_sparse_args) as compiled (a binding's layout check) */
 size_t pkv_sparse_args_size(void);
 
 #ifdef __cplusplus

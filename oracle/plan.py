@@ -93,7 +93,7 @@ BALANCE_BLOCK_KEYS = 32
 
 
 def plan_balanced(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16):
-    """Balanced contiguous plan (this build's own planner, not the pages'):
+    """Balanced contiguous plan (the library's own planner, not the pages'):
     the 32-key blocks of all sequences (max(1, ceil(L / 32)) each), laid end
     to end in sequence order, are cut into `bins` contiguous shares of
     floor/ceil(total / bins) blocks, bins = the workgroups that run at once
@@ -146,7 +146,7 @@ def plan_balanced(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16
 
 
 def plan_queued(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16, pieces_per_bin=3, dyn_percent=10):
-    """Queued plan (this build's own planner, not the pages'), written out step
+    """Queued plan (the library's own planner, not the pages'), written out step
     by step:
       1. blocks_b = max(1, ceil(L_b / 32)); total = sum; bins = the slots of
          the rule above, at most total;
