@@ -27,3 +27,23 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter):
+    # max|dO| / max|V| of the comparisons run in this session: every case held
+    # to a derived bound above the contract's 1e-2, and the worst of the rest
+    try:
+        from helpers import MARGINS, O_TOL
+    except ImportError:  # pragma: no cover
+        return
+    if not MARGINS:
+        return
+    tr = terminalreporter
+    tr.section("parity margins: max|dO| / max|V|")
+    loose = [m for m in MARGINS if m[2] > O_TOL]
+    strict = [m for m in MARGINS if m[2] <= O_TOL]
+    for case, ratio, bar in loose:
+        tr.write_line(f"{ratio:.3e} (bar {bar}) {case}")
+    if strict:
+        case, ratio, bar = max(strict, key=lambda m: m[1])
+        tr.write_line(f"{len(strict)} comparisons at bar {O_TOL}: worst {ratio:.3e} ({case})")

@@ -35,16 +35,22 @@ def run(batch, **kw):
     return dec
 
 
-def check(batch, dec, what=""):
-    nb = batch.to_numpy()
-    w = batch.spec
-    o_ref, l_ref = sparse_decode_attention(nb["q"], nb["sources"], softmax_scale=w.scale, sink=nb["sink"])
+def listed_vmax(sources):
+    """max|V| over the records the lists name (absent entries name none)."""
     vmax = 0.0
-    for s in nb["sources"]:
+    for s in sources:
         _, V = mla_keys_values(gather_slots(s["latent"], s["slots"].ravel()), gather_slots(s["rope"], s["slots"].ravel()),
                                gather_slots(s["scales"], s["slots"].ravel()))
         if V.size:
             vmax = max(vmax, float(np.abs(V).max()))
+    return vmax
+
+
+def check(batch, dec, what=""):
+    nb = batch.to_numpy()
+    w = batch.spec
+    o_ref, l_ref = sparse_decode_attention(nb["q"], nb["sources"], softmax_scale=w.scale, sink=nb["sink"])
+    vmax = listed_vmax(nb["sources"])
     o = dec.o.float().cpu().numpy()
     lse = dec.lse.cpu().numpy()
     assert np.all(np.isfinite(o)), what
@@ -118,7 +124,9 @@ def test_sparse_one_list_unused():
     torch.cuda.synchronize()
     nb = batch.to_numpy()
     o_ref, l_ref = sparse_decode_attention(nb["q"], nb["sources"][:1], softmax_scale=batch.spec.scale, sink=nb["sink"])
-    assert np.abs(dec.o.float().cpu().numpy() - o_ref).max() <= 1e-2 * 448 * 0.02
+    vmax = listed_vmax(nb["sources"][:1])
+    err_o = float(np.abs(dec.o.float().cpu().numpy() - o_ref).max())
+    assert err_o <= O_TOL * vmax, f"max|dO|={err_o} vmax={vmax}"
     assert np.abs(dec.lse.cpu().numpy() - l_ref).max() <= LSE_TOL
 
 
