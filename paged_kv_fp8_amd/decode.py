@@ -156,7 +156,7 @@ class PagedDecode:
         self.o, self.lse = o, lse
         # keep every bound tensor alive as long as the raw pointers are
         self._keep = (q, k_cache, v_cache, q_descale, k_descale, v_descale, latent, rope, blk_scale, block_table,
-                      seq_lens, o, lse)
+                      seq_lens, o, lse, k_group_scale, v_group_scale)
         self.plan = plan
 
     @property
