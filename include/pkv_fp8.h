@@ -70,7 +70,17 @@ typedef int32_t pkv_status;
 #define PKV_ERR_WORKSPACE (-4)   /* split workspace missing or too small */
 #define PKV_ERR_HIP (-5)         /* the HIP runtime reported an error */
 
-/* Static name of a status code ("PKV_OK", ...). Never NULL. */
+/* Static name of a status code ("PKV_OK", ...). Never NULL; an unknown code
+ * gives "PKV_ERR_UNKNOWN".
+ * The error convention follows the pages' rejections before any launch: the
+ * kernel's can_implement ("mjolnir-kernel 0.1.0 wheel: mjolnir/t5_decode.py",
+ * the decode class's can_implement: unsupported formats, head dim, head
+ * ratio) maps to PKV_ERR_UNSUPPORTED / PKV_ERR_INVALID_ARG, and the plan()
+ * step of "MiniMax MSA fmha_sm100/cute README" (Paged FP8 Decode, Known
+ * Limitations: invalid lengths caught at plan time with a clear error) maps
+ * to a negative status from the planner, with the reason in pkv_last_error().
+ * Here the status is returned instead of raised, so no exception crosses the
+ * C ABI. */
 const char* pkv_status_string(pkv_status s);
 
 /* Reason for the calling thread's most recent failing call (empty string if
@@ -355,7 +365,13 @@ typedef struct pkv_decode_args {
 } pkv_decode_args;
 
 /* Bytes of split workspace: max_splits * num_seqs * h_k * n_rows * (d_v + 2)
- * fp32 values (partial O, max and sum per row and split), rounded up to 256. */
+ * fp32 values (partial O, max and sum per row and split), rounded up to 256.
+ * ("mjolnir-kernel 0.1.0 wheel: mjolnir/t5_decode.py", module docstring,
+ * "Workspace": the o/m/l partials need no initialisation, because the merge
+ * reads only the split slots a sequence used and padding items exit at once.)
+ * The caller allocates it (device memory, 256-B aligned) and keeps it for as
+ * long as the plan is used; its contents between calls do not matter.
+ * Returns 0 when an argument is < 1 (no workspace can be sized). */
 size_t pkv_workspace_bytes(int32_t num_seqs, int32_t h_k, int32_t n_rows, int32_t d_v, int32_t max_splits);
 
 /*

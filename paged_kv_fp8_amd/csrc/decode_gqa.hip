@@ -11,10 +11,12 @@
 // -- is the swap-AB idea of "vLLM PR #62633" (Kernel design, MMA shape).
 //
 // gfx950 design (not the pages'):
-//  * One wavefront per workgroup, one workgroup per (work item, kv head,
-//    q-row tile). Each wave streams its chunk of keys 32 at a time straight
-//    from HBM into registers, one 32-key block ahead of the math; there is no
-//    LDS staging and no barrier.
+//  * One wavefront per kv head: a workgroup of 64 * HW threads holds the HW
+//    kv heads of one (work item, q-row tile) (HW = the largest power of two
+//    dividing h_k, at most 8; 4 with two 16-row blocks per wave), so its
+//    waves read the same pages together. Each wave streams its chunk of keys
+//    32 at a time straight from HBM into registers, a ring of blocks ahead of
+//    the math; there is no LDS staging of K/V and no barrier.
 //  * QK^T: v_mfma_f32_16x16x32_{bf16,fp8}, A = 16 keys x 32 head-dim slots,
 //    B = the q rows. Because the head-dim contraction is order-free, a lane's
 //    A slots are whatever 32 bytes of its key row it loaded with two 16-byte
