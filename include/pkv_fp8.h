@@ -590,6 +590,32 @@ pkv_status pkv_sparse_merge(const pkv_sparse_args* a, void* stream);
 /* sizeof(pkv_sparse_args) as compiled (a binding's layout check) */
 size_t pkv_sparse_args_size(void);
 
+/* ------------------------------------------------------------------------ */
+/* Measurement: streaming-read probe.                                       */
+/* ------------------------------------------------------------------------ */
+/*
+ * Reads `bytes` of device memory at `src` once with plain coalesced 16-byte
+ * loads and does nothing else, so that the HBM read rate of the decode
+ * kernels can be stated as a fraction of what this part reaches for a pure
+ * read in the same session ("mjolnir-kernel 0.1.0 wheel:
+ * mjolnir/t5_decode.py", `run`: GB/s = bytes moved / kernel time; this is
+ * that figure for a kernel that only streams).
+ *
+ * One launch of `workgroups` workgroups of 256 threads; each lane issues
+ * `unroll` (4, 8 or 16) independent 16-byte loads per step, and the
+ * workgroups walk 4 KiB * unroll chunks grid-stride. Nothing the kernel
+ * reads reaches an output; `sink` (device, >= workgroups uint32 values) is
+ * written only in the case that a lane's XOR of its words equals a fixed
+ * pattern, which keeps the loads from being optimised away.
+ *
+ * src   device, 16-B aligned; bytes > 0 and a multiple of 4096 * unroll.
+ * Errors before any launch: PKV_ERR_INVALID_ARG (NULL or misaligned
+ * pointers, sizes out of range); PKV_ERR_HIP (the launch failed). Allocates
+ * nothing, does not synchronise.
+ */
+pkv_status pkv_stream_read_probe(const void* src, size_t bytes, int32_t workgroups, int32_t unroll, uint32_t* sink,
+                                 void* stream);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

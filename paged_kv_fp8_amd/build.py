@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libpkvfp8.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "plan.cpp", "decode_gqa.hip", "decode_mla.hip", "merge.hip", "producers.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "decode_gqa.hip", "decode_mla.hip", "merge.hip", "producers.hip", "probe.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops
 # (v_pk_*_f32); the host pass warns that it does not know the feature.
@@ -29,17 +29,25 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-ta
          "-Wno-unknown-pragmas"]
 
 
-def build(verbose=False, extra_flags=()):
-    objs = []
+def build(verbose=False, extra_flags=(), jobs=None):
+    """Compile every source (in parallel, one hipcc per source) and link the
+    library; returns its path."""
+    from concurrent.futures import ThreadPoolExecutor
+
     build_dir = os.path.join(HERE, "_build")
     os.makedirs(build_dir, exist_ok=True)
+    cmds, objs = [], []
     for src in SOURCES:
         obj = os.path.join(build_dir, src + ".o")
         cmd = [HIPCC, *FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
-        _run(cmd, verbose)
+        cmds.append(cmd)
         objs.append(obj)
+    jobs = jobs or min(len(cmds), max(1, min(os.cpu_count() or 1, 8)))
+    with ThreadPoolExecutor(jobs) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
     tmp = LIB + ".tmp"
     _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)

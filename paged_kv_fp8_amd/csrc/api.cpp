@@ -369,3 +369,16 @@ extern "C" pkv_status pkv_sparse_merge(const pkv_sparse_args* a, void* stream) {
 }
 
 extern "C" size_t pkv_sparse_args_size(void) { return sizeof(pkv_sparse_args); }
+
+extern "C" pkv_status pkv_stream_read_probe(const void* src, size_t bytes, int32_t workgroups, int32_t unroll,
+                                            uint32_t* sink, void* stream) {
+  if (!src || !sink) return fail(PKV_ERR_INVALID_ARG, "src and sink must be non-NULL");
+  if (!aligned(src, 16) || !aligned(sink, 4)) return fail(PKV_ERR_INVALID_ARG, "src must be 16-B aligned, sink 4-B");
+  if (unroll != 4 && unroll != 8 && unroll != 16) return fail(PKV_ERR_INVALID_ARG, "unroll=%d not in {4, 8, 16}", unroll);
+  if (workgroups < 1 || workgroups > (1 << 20))
+    return fail(PKV_ERR_INVALID_ARG, "workgroups=%d not in [1, 2^20]", workgroups);
+  const size_t chunk = (size_t)4096 * unroll;
+  if (bytes == 0 || bytes % chunk) return fail(PKV_ERR_INVALID_ARG, "bytes=%zu not a positive multiple of %zu", bytes, chunk);
+  return hip_status(probe_launch(src, bytes, workgroups, unroll, sink, static_cast<hipStream_t>(stream)),
+                    "probe launch");
+}

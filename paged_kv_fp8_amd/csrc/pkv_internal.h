@@ -51,6 +51,10 @@ hipError_t merge_launch(const pkv_decode_args& a, hipStream_t stream);
 hipError_t quantize_q_launch(const pkv_quant_q_args& a, hipStream_t stream);
 hipError_t write_kv_launch(const pkv_kv_write_args& a, hipStream_t stream);
 
+// Streaming-read probe (measurement only).
+hipError_t probe_launch(const void* src, size_t bytes, int workgroups, int unroll, uint32_t* sink,
+                        hipStream_t stream);
+
 // Workspace partition, in floats: partial O of every (split, seq, head,
 // row) first, then its (max, sum) pair.
 inline int64_t ws_rows(const pkv_decode_args& a) {

@@ -23,7 +23,7 @@ EXPORTS = ("pkv_status_string", "pkv_last_error", "pkv_version", "pkv_decode_arg
            "pkv_plan_even", "pkv_plan_balanced", "pkv_plan_queued", "pkv_workspace_bytes", "pkv_decode_slots", "pkv_paged_decode_attn",
            "pkv_merge_splits", "pkv_quantize_q", "pkv_quant_q_args_size", "pkv_write_kv", "pkv_kv_write_args_size",
            "pkv_decode_kernel_name", "pkv_sparse_workspace_bytes", "pkv_sparse_decode", "pkv_sparse_tiles", "pkv_sparse_merge",
-           "pkv_sparse_args_size")
+           "pkv_sparse_args_size", "pkv_stream_read_probe")
 
 
 class PkvError(RuntimeError):
@@ -171,6 +171,8 @@ def _load():
         getattr(lib, name).restype = _i32
         getattr(lib, name).argtypes = [P(SparseArgs), _vp]
     lib.pkv_sparse_args_size.restype = ctypes.c_size_t
+    lib.pkv_stream_read_probe.restype = _i32
+    lib.pkv_stream_read_probe.argtypes = [_vp, ctypes.c_size_t, _i32, _i32, _vp, _vp]
     for name, st in (("pkv_quant_q_args_size", QuantQArgs), ("pkv_kv_write_args_size", KvWriteArgs),
                      ("pkv_sparse_args_size", SparseArgs)):
         if getattr(lib, name)() != ctypes.sizeof(st):
@@ -321,3 +323,9 @@ def sparse_tiles(args, stream=None):
 
 def sparse_merge(args, stream=None):
     _check(lib.pkv_sparse_merge(ctypes.byref(args), stream), "pkv_sparse_merge")
+
+
+def stream_read_probe(src_ptr, nbytes, workgroups, unroll, sink_ptr, stream=None):
+    """One launch of the streaming-read probe over ``nbytes`` at device
+    address ``src_ptr`` (measurement only)."""
+    _check(lib.pkv_stream_read_probe(src_ptr, nbytes, workgroups, unroll, sink_ptr, stream), "pkv_stream_read_probe")

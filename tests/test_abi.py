@@ -414,3 +414,15 @@ def test_sparse_decode_rejects_invalid_arguments_without_touching_the_gpu(native
 def test_sparse_null_args(native):
     assert native.lib.pkv_sparse_decode(None, None) == native.PKV_ERR_INVALID_ARG
     assert native.lib.pkv_sparse_workspace_bytes(None) == 0
+
+
+@pytest.mark.parametrize("src,nbytes,wg,unroll,sink", [
+    (None, 4096 * 8, 64, 8, 256), (256, 4096 * 8, 64, 8, None),   # NULL pointers
+    (264, 4096 * 8, 64, 8, 256), (256, 4096 * 8, 64, 8, 258),     # misaligned
+    (256, 4096 * 8, 64, 6, 256), (256, 4096 * 8, 0, 8, 256),      # unroll, workgroups
+    (256, 4096 * 8 + 16, 64, 8, 256), (256, 0, 64, 8, 256)])      # size not a whole number of chunks
+def test_stream_read_probe_rejects_invalid_arguments_without_touching_the_gpu(native, src, nbytes, wg, unroll, sink):
+    # fake (never dereferenced) addresses: every check runs before any HIP call
+    st = native.lib.pkv_stream_read_probe(src, nbytes, wg, unroll, sink, None)
+    assert st == native.PKV_ERR_INVALID_ARG, native.last_error()
+    assert native.last_error()
