@@ -591,6 +591,38 @@ pkv_status pkv_sparse_merge(const pkv_sparse_args* a, void* stream);
 size_t pkv_sparse_args_size(void);
 
 /* ------------------------------------------------------------------------ */
+/* Decode step that allocates nothing.                                      */
+/* ------------------------------------------------------------------------ */
+/* Bytes of split workspace the library holds per device for
+ * pkv_paged_decode_noalloc (64 MiB). */
+#define PKV_NOALLOC_WORKSPACE_BYTES (64u << 20)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * decode step as pkv_paged_decode_attn followed by pkv_merge_splits, with the
+ * split workspace taken from a device array the library holds (one per
+ * device, PKV_NOALLOC_WORKSPACE_BYTES, kept from the first call on that
+ * device until the process ends) instead of a->workspace, which is ignored.
+ * The caller still passes every input and output, the work list and
+ * n_splits. The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine); its first call on a device looks the array's address up.
+ *
+ * Every call on a device shares that device's array and finds the previous
+ * call's contents there; the workspace needs no initialisation (the merge
+ * reads only the split slots this call's decode wrote), but calls that
+ * overlap in time on one device (other streams, other threads) race on it
+ * and give undefined results. Serialise them.
+ *
+ * Errors, before any launch: those of pkv_paged_decode_attn;
+ * PKV_ERR_WORKSPACE when pkv_workspace_bytes(num_seqs, h_k, q_len * h_q / h_k,
+ * d_v, max_splits) exceeds PKV_NOALLOC_WORKSPACE_BYTES (max_splits == 1 needs
+ * none); PKV_ERR_UNSUPPORTED with merge_counters or queue set (the in-kernel
+ * merge and the queued plan keep counters of their own).
+ */
+pkv_status pkv_paged_decode_noalloc(const pkv_decode_args* a, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Measurement: streaming-read probe.                                       */
 /* ------------------------------------------------------------------------ */
 /*

@@ -1,9 +1,12 @@
 // Host entry points of libpkvfp8.so: argument validation and dispatch to
 // the kernel launchers. Every check runs before any HIP call, so an invalid
 // request returns its error code without touching the GPU.
+#include <hip/hip_runtime.h>
+
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "pkv_internal.h"
 
@@ -227,6 +230,62 @@ extern "C" pkv_status pkv_merge_splits(const pkv_decode_args* a, void* stream) {
   // the e4m3-cache decode merges in place when given counters
   if (a->max_splits == 1 || (a->merge_counters && a->kv_format != PKV_KV_MLA)) return PKV_OK;
   return hip_status(merge_launch(*a, static_cast<hipStream_t>(stream)), "merge launch");
+}
+
+// ---- decode step without allocation ------------------------------------------
+// The split workspace of pkv_paged_decode_noalloc: a module-scope device array,
+// so each device the library runs on holds one copy from the first call until
+// the process ends. Host code never uses its name as an address: the address
+// on the current device comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[PKV_NOALLOC_WORKSPACE_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+pkv_status scratch_on_current_device(void** out) {
+  int dev = 0;
+  pkv_status st = hip_status(hipGetDevice(&dev), "hipGetDevice");
+  if (st != PKV_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices) return fail(PKV_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if ((st = hip_status(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)")) != PKV_OK)
+      return st;
+    if (!ptr) return fail(PKV_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+}  // namespace
+
+extern "C" pkv_status pkv_paged_decode_noalloc(const pkv_decode_args* a, void* stream) {
+  pkv_status st = check_shapes(a);
+  if (st != PKV_OK) return st;
+  if (a->merge_counters || a->queue)
+    return fail(PKV_ERR_UNSUPPORTED, "no-allocation decode: merge counters and the queued plan are not taken");
+  const size_t need = a->max_splits > 1 ? pkv_workspace_bytes(a->num_seqs, a->h_k, a->q_len * (a->h_q / a->h_k),
+                                                               a->d_v, a->max_splits)
+                                        : 0;
+  if (need > (size_t)PKV_NOALLOC_WORKSPACE_BYTES)
+    return fail(PKV_ERR_WORKSPACE, "no-allocation decode: %zu bytes of split workspace needed, the library holds %zu",
+                need, (size_t)PKV_NOALLOC_WORKSPACE_BYTES);
+  pkv_decode_args b = *a;
+  // validate everything else with a stand-in workspace before any HIP call
+  b.workspace = reinterpret_cast<void*>(uintptr_t{256});
+  b.workspace_bytes = PKV_NOALLOC_WORKSPACE_BYTES;
+  if ((st = check_pointers(&b, false)) != PKV_OK) return st;
+  if (need > 0) {
+    if ((st = scratch_on_current_device(&b.workspace)) != PKV_OK) return st;
+  } else {
+    b.workspace = nullptr;
+    b.workspace_bytes = 0;
+  }
+  if ((st = pkv_paged_decode_attn(&b, stream)) != PKV_OK) return st;
+  return pkv_merge_splits(&b, stream);
 }
 
 namespace {

@@ -17,13 +17,14 @@ PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_CAPACITY, PKV_ERR_WORK
 PKV_Q_BF16, PKV_Q_E4M3 = 0, 1
 PKV_KV_E4M3, PKV_KV_MLA, PKV_KV_E2M1, PKV_KV_E2M3, PKV_KV_E3M2, PKV_KV_NVFP4 = 0, 1, 2, 3, 4, 5
 PKV_MAX_SPLITS = 256
+PKV_NOALLOC_WORKSPACE_BYTES = 64 << 20
 
 # Every function the header declares, in declaration order.
 EXPORTS = ("pkv_status_string", "pkv_last_error", "pkv_version", "pkv_decode_args_size", "pkv_plan_split_kv",
            "pkv_plan_even", "pkv_plan_balanced", "pkv_plan_queued", "pkv_workspace_bytes", "pkv_decode_slots", "pkv_paged_decode_attn",
            "pkv_merge_splits", "pkv_quantize_q", "pkv_quant_q_args_size", "pkv_write_kv", "pkv_kv_write_args_size",
            "pkv_decode_kernel_name", "pkv_sparse_workspace_bytes", "pkv_sparse_decode", "pkv_sparse_tiles", "pkv_sparse_merge",
-           "pkv_sparse_args_size", "pkv_stream_read_probe")
+           "pkv_sparse_args_size", "pkv_paged_decode_noalloc", "pkv_stream_read_probe")
 
 
 class PkvError(RuntimeError):
@@ -171,6 +172,8 @@ def _load():
         getattr(lib, name).restype = _i32
         getattr(lib, name).argtypes = [P(SparseArgs), _vp]
     lib.pkv_sparse_args_size.restype = ctypes.c_size_t
+    lib.pkv_paged_decode_noalloc.restype = _i32
+    lib.pkv_paged_decode_noalloc.argtypes = [P(DecodeArgs), _vp]
     lib.pkv_stream_read_probe.restype = _i32
     lib.pkv_stream_read_probe.argtypes = [_vp, ctypes.c_size_t, _i32, _i32, _vp, _vp]
     for name, st in (("pkv_quant_q_args_size", QuantQArgs), ("pkv_kv_write_args_size", KvWriteArgs),
@@ -323,6 +326,12 @@ def sparse_tiles(args, stream=None):
 
 def sparse_merge(args, stream=None):
     _check(lib.pkv_sparse_merge(ctypes.byref(args), stream), "pkv_sparse_merge")
+
+
+def paged_decode_noalloc(args, stream=None):
+    """Decode + merge with the library's own split workspace (args.workspace
+    is ignored); allocates nothing."""
+    _check(lib.pkv_paged_decode_noalloc(ctypes.byref(args), stream), "pkv_paged_decode_noalloc")
 
 
 def stream_read_probe(src_ptr, nbytes, workgroups, unroll, sink_ptr, stream=None):

@@ -172,6 +172,24 @@ def test_decode_rejects_invalid_arguments_without_touching_the_gpu(native, over,
         assert native.last_error()
 
 
+@pytest.mark.parametrize("over,code", [b for b in BAD if b[1] != -4])
+def test_noalloc_decode_rejects_invalid_arguments_without_touching_the_gpu(native, over, code):
+    st = native.lib.pkv_paged_decode_noalloc(ctypes.byref(_valid_args(native, **over)), None)
+    assert st == code, (over, native.status_string(st), native.last_error())
+
+
+def test_noalloc_decode_limits(native):
+    big = _valid_args(native, num_seqs=64, h_q=32, h_k=8, max_splits=256)
+    need = native.workspace_bytes(64, 8, 4, 128, 256)
+    assert need > native.PKV_NOALLOC_WORKSPACE_BYTES
+    assert native.lib.pkv_paged_decode_noalloc(ctypes.byref(big), None) == native.PKV_ERR_WORKSPACE
+    assert "workspace" in native.last_error()
+    for over in (dict(merge_counters=1 << 43), dict(queue=1 << 43, bin_offsets=1 << 44, num_bins=4)):
+        a = _valid_args(native, max_splits=4, **over)
+        assert native.lib.pkv_paged_decode_noalloc(ctypes.byref(a), None) == native.PKV_ERR_UNSUPPORTED
+    assert native.lib.pkv_paged_decode_noalloc(None, None) == native.PKV_ERR_INVALID_ARG
+
+
 def test_decode_kernel_name_follows_the_shapes(native):
     assert native.decode_kernel_name(_valid_args(native)) == "gqa_decode_kernel"
     mla = dict(kv_format=1, h_k=1, h_q=16, d_qk=576, d_v=512)
