@@ -133,6 +133,10 @@ pkv_status check_pointers(const pkv_decode_args* a, bool for_merge) {
     if (!aligned(a->k_blk_scale, 16) || bad_stride(a->scale_page_stride, 4, 16) ||
         bad_stride(a->scale_row_stride, 4, 16))
       return fail(PKV_ERR_INVALID_ARG, "k_blk_scale must be 16-B aligned with 16-B multiple strides");
+    if ((int64_t)a->page_size * a->k_row_stride >= (int64_t)1 << 30 ||
+        (int64_t)a->page_size * a->rope_row_stride * 2 >= (int64_t)1 << 30 ||
+        (int64_t)a->page_size * a->scale_row_stride * 4 >= (int64_t)1 << 30)
+      return fail(PKV_ERR_UNSUPPORTED, "latent cache: page_size * row stride must be below 2^30 bytes");
     return PKV_OK;
   }
   if (!a->v || !aligned(a->v, 16) || bad_stride(a->v_page_stride, 1, 16) || bad_stride(a->v_row_stride, 1, 16) ||

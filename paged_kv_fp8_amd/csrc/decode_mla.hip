@@ -46,7 +46,6 @@ constexpr int kRope = 64;
 constexpr int kDv = 512;
 constexpr int kTileKeys = 128;  // planner tile
 constexpr int kBlockKeys = 16;  // keys per pair-form step
-constexpr int kQSteps = 18;     // 16 latent + 2 rope k-steps of 32
 constexpr float kLazyLog2 = 8.0f;  // bf16 P: reference max may lag until p would exceed 2^8
 
 struct MlaParams {
@@ -102,9 +101,9 @@ __device__ __forceinline__ float pair32(float x, bool take_max) {
 
 // ---- multi-token form: records staged once per workgroup ---------------------
 // From 64 query rows on, the latent records of each 32-key block are
-// dequantised ONCE per workgroup into LDS (double-buffered) as bf16 key rows
-// (512 latent codes, exact, then the 64 bf16 rope values) plus the block
-// scales. Both MFMA operands come from there:
+// dequantised ONCE per workgroup into LDS as bf16 key rows (512 latent codes,
+// exact, then the 64 bf16 rope values) plus the block scales, in a ring of
+// three stages. Both MFMA operands come from there:
 //  * QK^T reads 16-byte pieces of the key rows (keys on M, two 16-key tiles);
 //  * PV reads V^T straight from the same rows with the LDS transpose load
 //    (ds_read_b64_tr_b16): within each 16-lane group, lane i receives element
@@ -114,14 +113,20 @@ __device__ __forceinline__ float pair32(float x, bool take_max) {
 //    8 keys of a 16x16x32 A operand in the order in which the QK^T
 //    accumulators hold P (keys 4 g4 + i of each tile), so P needs no lane
 //    exchange.
-// Eight waves (two per SIMD): wave w owns query rows 16 (w & 3) .. +15 of the
-// tile and d_v half w >> 2 (64 accumulator registers); the two waves of a row
-// group both compute S, so their softmax statistics agree bit for bit. The
-// 512 threads split a block's loads (32 latent bytes, one rope pair of dwords
-// and one scale dword each), three blocks ahead of the math in a register
-// ring; one barrier per block: a stage is written one block before it is read
-// and read one block before it is rewritten.
-constexpr int kLdsWaves = 8;
+// Four waves, one per SIMD: wave w owns the 32 query rows 32 (w >> 1) .. +31
+// of the workgroup's 64 (two 16-row N blocks, so every K or V^T piece read
+// from LDS feeds two MFMAs) and the half h = w & 1 of the head dims: latent
+// blocks 2h and 2h + 1 (d_v 256 h .. 256 h + 255, its share of PV and of
+// O) and rope k-step h. Its QK^T over that half of d_qk is a partial S; the
+// two waves of a row group swap their partials through LDS and both add the
+// same two numbers, so S, the softmax statistics and P agree bit for bit and
+// no part of S is computed twice.
+// The 256 threads split a block's loads (64 latent bytes, 16 rope bytes and
+// one scale each), RING blocks ahead of the math in a register ring. One
+// barrier per block: stage j is written in step j - 1 and read in step j, and
+// rewritten in step j + 2 after the barrier of step j + 1; the partial-S
+// exchange is double-buffered the same way.
+constexpr int kLdsWaves = 4;
 constexpr int kLdsRows = 64;                            // query rows per workgroup
 constexpr int kStageKeys = 32;                          // keys per step
 // bf16 key row + 32 B: rows sit 8 banks apart, and the 16-byte pieces of rows
@@ -132,12 +137,21 @@ constexpr int kKRowBytes = 2 * (kLatent + kRope) + 32;
 constexpr int kStageK = 0;
 constexpr int kStageScl = kStageKeys * kKRowBytes;
 constexpr int kStageBytes = kStageScl + kStageKeys * 16;
-constexpr int kRing = 3;  // raw blocks per thread: block j+2 is loaded while block j is processed
+constexpr int kStages = 3;
+// partial S of one wave: [key tile][row block][lane] f32x4
+constexpr int kSxWaveBytes = 2 * 2 * 64 * 16;
+constexpr int kSxOffset = kStages * kStageBytes;
+constexpr int kFlagOffset = kSxOffset + 2 * kLdsWaves * kSxWaveBytes;  // restart flag (int)
+constexpr int kLdsBytes = kFlagOffset + 16;
+constexpr float kFixedLog2 = 32.0f;  // p = exp2((s - m_run) c2) stays below 2^32
+constexpr int kAhead = 2;            // LDS operand pieces read ahead of their MFMAs
 
+// One thread's loads of one 32-key block: key t >> 3, latent bytes 8 (t & 7) +
+// 64 i (i < 8, two per uint4), rope bytes 16 (t & 7), scale (t & 7) & 3.
 struct RawPiece {
-  uint2 lat[4];  // key t >> 4: latent bytes 128 i + 8 (t & 15) .. +7
-  uint2 rope;    // key t >> 4: rope bytes 8 (t & 15) .. +7
-  float scl;     // key (t & 127) >> 2: scale t & 3
+  uint4 lat[4];
+  uint4 rope;
+  float scl;
 };
 
 // Byte offset of byte `lane_off + c` of key row `row` in a stage (see
@@ -155,14 +169,14 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
       (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) uint8_t*)p);
 }
 
-template <bool CAUSAL_TAIL>
+template <bool CAUSAL_TAIL, int RING>
 __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int tile, uint8_t* lds) {
   const int t = threadIdx.x;
-  const int w = t >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
   const int lane = t & 63;
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
-  const int half = w >> 2;  // d_v 256 half .. 256 half + 255
+  const int half = w & 1;  // latent blocks 2 half, 2 half + 1; rope k-step half
 
   const int4 wk = p.work[item];
   const int b = wk.x;
@@ -178,38 +192,71 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
   const int k_begin = p.bin_offsets ? wk.y : wk.y * kTileKeys;
   const int k_end = min(p.bin_offsets ? wk.z : wk.z * kTileKeys, L);
 
-  // rows of this wave: n = row0 + r16; a wave past the last row still loads,
-  // stages and meets every barrier
-  const int row0 = tile * kLdsRows + 16 * (w & 3);
-  const bool wave_rows = row0 < p.rows;
-  const int n = row0 + r16;
-  const bool row_ok = n < p.rows;
-  const int qi = n / p.h_q;
-  const int qtok = b * p.q_len + qi;
-  const int qhead = n - qi * p.h_q;
-  const int lim = min(CAUSAL_TAIL ? L - p.q_len + qi : L - 1, k_end - 1);
-  const int qi_min = row0 / p.h_q;
-  const int lim_min = min(CAUSAL_TAIL ? L - p.q_len + qi_min : L - 1, k_end - 1);
+  // rows of this wave: n = row0 + 16 rb + r16; a row group past the last row
+  // runs like the others (on zero query rows) and writes nothing
+  const int row0 = tile * kLdsRows + 32 * (w >> 1);
+  int qtok[2], qhead[2], lim[2];
+  bool row_ok[2];
+  for (int rb = 0; rb < 2; ++rb) {
+    const int n = row0 + 16 * rb + r16;
+    row_ok[rb] = n < p.rows;
+    const int qi = n / p.h_q;
+    qtok[rb] = b * p.q_len + qi;
+    qhead[rb] = n - qi * p.h_q;
+    lim[rb] = min(CAUSAL_TAIL ? L - p.q_len + qi : L - 1, k_end - 1);
+  }
+  const int lim_min = min(CAUSAL_TAIL ? L - p.q_len + row0 / p.h_q : L - 1, k_end - 1);
   const float c2 = p.scale_log2e;
 
-  // Q as the B operand: k-step k holds q[n][32k + 8 g4 .. +7] (latent k < 16,
-  // then rope), the natural order of the bf16 key rows in LDS
-  bf16x8 qv[kQSteps];
-  {
-    const uint8_t* qrow = p.q + (int64_t)qtok * p.q_tok + (int64_t)qhead * p.q_head;
-    for (int k = 0; k < kQSteps; ++k) {
-      if (row_ok) {
-        qv[k] = *reinterpret_cast<const bf16x8*>(qrow + 2 * (32 * k + 8 * g4));
+  // Q as the B operand of this wave's half of d_qk: k-step k < 8 holds
+  // q[n][256 half + 32 k + 8 g4 .. +7] (latent), k = 8 the rope k-step half
+  bf16x8 qv[2][9];
+  for (int rb = 0; rb < 2; ++rb) {
+    const uint8_t* qrow = p.q + (int64_t)qtok[rb] * p.q_tok + (int64_t)qhead[rb] * p.q_head;
+    for (int k = 0; k < 9; ++k) {
+      const int d = k < 8 ? 256 * half + 32 * k + 8 * g4 : kLatent + 32 * half + 8 * g4;
+      if (row_ok[rb]) {
+        qv[rb][k] = *reinterpret_cast<const bf16x8*>(qrow + 2 * d);
       } else {
-        for (int e = 0; e < 8; ++e) qv[k][e] = (__bf16)0.0f;
+        for (int e = 0; e < 8; ++e) qv[rb][k][e] = (__bf16)0.0f;
       }
     }
   }
+  // Q is only ever an MFMA operand, which may sit in AGPRs: place it there (an
+  // empty statement with an AGPR operand, after all of its loads are issued),
+  // so that the VGPRs hold the LDS pieces read ahead of the MFMAs
+  for (int rb = 0; rb < 2; ++rb)
+    for (int k = 0; k < 9; ++k) asm volatile("" : "+a"(qv[rb][k]));
 
-  f32x4 oacc[2][8];  // [128-block gg of this half][16-row tile mt]: O^T[256 half + 128 gg + 16 mt + 4 g4 + i][n]
-  for (int gg = 0; gg < 2; ++gg)
-    for (int mt = 0; mt < 8; ++mt) oacc[gg][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_part = 0.f;
+  f32x4 oacc[2][2][8];  // [row block][128-block gg of this half][16-row tile mt]:
+                        // O^T[256 half + 128 gg + 16 mt + 4 g4 + i][row 16 rb + r16]
+  // m_run: the row's reference max (raw-score units), set by its first visible
+  // block and then fixed, so O is never rescaled inside the loop (a VALU pass
+  // over O would pull it out of the MFMA accumulator registers on every
+  // block). P = exp2((s - m_run) c2) may grow up to 2^kFixedLog2, which bf16
+  // P and the fp32 sums absorb. m_seen: the largest block max seen.
+  float m_run[2] = {-INFINITY, -INFINITY}, l_part[2], m_seen[2] = {-INFINITY, -INFINITY};
+  // an LDS pointer (a generic one would make these FLAT accesses, whose waits
+  // also wait for every global load in flight)
+  volatile __attribute__((address_space(3))) int* restart_flag =
+      (volatile __attribute__((address_space(3))) int*)((__attribute__((address_space(3))) uint8_t*)lds + kFlagOffset);
+  auto barrier = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+  bool again;
+  // A block whose max would put some p past 2^kFixedLog2 (scores rising that
+  // far after a row's first visible block: pathological inputs only) sets the
+  // flag; after the next barrier every wave sees it, and the workgroup runs
+  // the item again from its first key with each row's reference at m_seen.
+  do {
+  again = false;
+  for (int rb = 0; rb < 2; ++rb) {
+    l_part[rb] = 0.f;
+    for (int gg = 0; gg < 2; ++gg)
+      for (int mt = 0; mt < 8; ++mt) oacc[rb][gg][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   if (k_end > k_begin) {
     const int32_t* bt = p.block_table + (int64_t)b * p.bt_row;
@@ -219,41 +266,52 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
     auto page_pair = [&](int kb) -> int { return bt[min(kb + 16 * (lane & 1), last_key) >> p.page_shift]; };
     auto clamp_page = [&](int pg) -> int { return min(max(pg, 0), p.num_pages - 1); };
 
-    // fetch u: the loads of block k_begin + 32u into ring slot u % kRing, with
-    // the pages from page slot u % kRing (loaded two fetches earlier); it
-    // loads the pages of fetch u + 2. Waves 0-3 load keys 0-15 (latent, rope),
-    // waves 4-7 keys 16-31; even waves load the scales of keys 0-15, odd
-    // waves those of keys 16-31, so each wave reads one page per load.
-    int pv[kRing];
+    // fetch u: the loads of block k_begin + 32u into ring slot u % RING, with
+    // the pages from page slot u % 3 (loaded two fetches earlier); it loads
+    // the pages of fetch u + 2. Waves 0-1 load keys 0-15, waves 2-3 keys
+    // 16-31, so each wave reads one page per load.
+    int pv[3];
     pv[0] = page_pair(k_begin);
     pv[1] = page_pair(k_begin + kStageKeys);
-    auto fetch = [&](RawPiece& r, int kb, const int s) {
-      const int pg0 = clamp_page(__builtin_amdgcn_readlane(pv[s], 0));
-      const int pg1 = clamp_page(__builtin_amdgcn_readlane(pv[s], 1));
-      const int pgk = (w >> 2) ? pg1 : pg0;
-      const int key = min(kb + (t >> 4), last_key) & pmask;
-      const uint8_t* lat = p.lat + (int64_t)pgk * p.lat_page + (int64_t)key * p.lat_row + 8 * (t & 15);
-      for (int i = 0; i < 4; ++i) r.lat[i] = *reinterpret_cast<const uint2*>(lat + 128 * i);
-      r.rope = *reinterpret_cast<const uint2*>(p.rope + (int64_t)pgk * p.rope_page + (int64_t)key * p.rope_row +
-                                               8 * (t & 15));
-      const int pgs = (w & 1) ? pg1 : pg0;
-      const int skey = min(kb + ((t & 127) >> 2), last_key) & pmask;
-      r.scl = *reinterpret_cast<const float*>(p.scl + (int64_t)pgs * p.scl_page + (int64_t)skey * p.scl_row +
-                                              4 * (t & 3));
-      pv[(s + 2) % kRing] = page_pair(kb + 2 * kStageKeys);
+    const int my_key = t >> 3, part = t & 7;
+    // A load's address is the wave-uniform page base (scalar registers) plus a
+    // 32-bit lane offset: the key's row inside the page times the row stride
+    // (page_size * row stride < 2^30, as the host checks for the other caches)
+    // plus the lane's bytes in the row.
+    auto fetch = [&](RawPiece& r, int kb, const int ps) {
+      const int pg0 = clamp_page(__builtin_amdgcn_readlane(pv[ps], 0));
+      const int pg1 = clamp_page(__builtin_amdgcn_readlane(pv[ps], 1));
+      const int64_t pgk = (w >> 1) ? pg1 : pg0;
+      const uint32_t key = (uint32_t)(min(kb + my_key, last_key) & pmask);
+      const uint8_t* lat = p.lat + pgk * p.lat_page;
+      const uint8_t* rope = p.rope + pgk * p.rope_page;
+      const uint8_t* scl = p.scl + pgk * p.scl_page;
+      const uint32_t lat_off = key * (uint32_t)p.lat_row + 8u * part;
+      for (int i = 0; i < 4; ++i) {
+        const uint2 c0 = *reinterpret_cast<const uint2*>(lat + (lat_off + 128u * i));
+        const uint2 c1 = *reinterpret_cast<const uint2*>(lat + (lat_off + 128u * i + 64u));
+        r.lat[i] = uint4{c0.x, c0.y, c1.x, c1.y};
+      }
+      r.rope = *reinterpret_cast<const uint4*>(rope + (key * (uint32_t)p.rope_row + 16u * part));
+      r.scl = *reinterpret_cast<const float*>(scl + (key * (uint32_t)p.scl_row + 4u * (part & 3)));
+      pv[(ps + 2) % 3] = page_pair(kb + 2 * kStageKeys);
     };
-    // each store of a 16-lane group covers 256 contiguous bytes of one row
-    const int st_lat = kStageK + krow_base(t >> 4, 16 * (t & 15));
-    const int st_rope = kStageK + krow_base(t >> 4, 8 * (t & 15)) + 2 * kLatent;
+    // 16-byte pieces of the key row: bf16 latent pieces 8 i + part (codes
+    // 64 i + 8 part .., so each 8-lane group stores 128 contiguous bytes),
+    // the rope piece part, and scale part & 3 (threads part and part + 4 store
+    // the same value)
+    auto stage_part = [&](const RawPiece& r, uint8_t* st, int i) {
+      if (i < 8) {
+        const uint2 c = (i & 1) ? uint2{r.lat[i >> 1].z, r.lat[i >> 1].w} : uint2{r.lat[i >> 1].x, r.lat[i >> 1].y};
+        *reinterpret_cast<bf16x8*>(st + kStageK + krow_base(my_key, 128 * i + 16 * part)) = e4m3x8_to_bf16(c);
+      } else if (i == 8) {
+        *reinterpret_cast<uint4*>(st + kStageK + krow_base(my_key, 2 * kLatent + 16 * part)) = r.rope;
+      } else if (i == 9) {
+        *reinterpret_cast<float*>(st + kStageScl + 16 * my_key + 4 * (part & 3)) = r.scl;
+      }
+    };
     auto stage_in = [&](const RawPiece& r, uint8_t* st) {
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<bf16x8*>(st + st_lat + 256 * i) = e4m3x8_to_bf16(r.lat[i]);
-      *reinterpret_cast<uint2*>(st + st_rope) = r.rope;
-      if (t < 128) *reinterpret_cast<float*>(st + kStageScl + 4 * t) = r.scl;
-    };
-    auto barrier = [&]() {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      for (int i = 0; i < 10; ++i) stage_part(r, st, i);
     };
 
     // this lane's QK^T piece (key row r16 of a tile, bytes 16 g4 ..) and
@@ -261,86 +319,168 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
     // rows 16 apart share the swizzle
     const int qk_base = krow_base(r16, 16 * g4);
     const int tr_base = krow_base(4 * g4 + (r16 >> 2), 8 * (r16 & 3));
-    auto compute = [&](const uint8_t* st, int kb) {
-      // ---- S = K Q^T per 16-key tile tt: one accumulator per 128-value block + rope
-      float sv[2][4];
-      float sp[2][2][4];  // [gg][tt][i]: scale of this wave's d_v block 2 half + gg for key 16 tt + 4 g4 + i
-      for (int tt = 0; tt < 2; ++tt) {
-        const uint8_t* krow = st + kStageK + qk_base + tt * 16 * kKRowBytes;
-        f32x4 acc[4], accr = {0.f, 0.f, 0.f, 0.f};
-        for (int blk = 0; blk < 4; ++blk) {
-          acc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
-          for (int s = 0; s < 4; ++s) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 2 * (128 * blk + 32 * s));
-            acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qv[4 * blk + s], acc[blk], 0, 0, 0);
-          }
+    // scales of latent blocks 2 half, 2 half + 1 of key 16 tt + 4 g4 + i (read
+    // where they are used, so no block's scales stay live across a phase)
+    auto scale2 = [&](const uint8_t* st, int tt, int i) -> float2 {
+      return *reinterpret_cast<const float2*>(st + kStageScl + 16 * (16 * tt + 4 * g4 + i) + 8 * half);
+    };
+    // partial S (s_out[tt][rb]: S[key 16 tt + 4 g4 + i][row 16 rb + r16]) of
+    // the block in stage st over this wave's half of d_qk. The 18 K pieces
+    // (per key tile: 8 latent k-steps, then the rope k-step) are read kAhead
+    // pieces ahead of the MFMAs that use them.
+    auto qk_piece = [&](const uint8_t* st, int idx) -> bf16x8 {
+      const int tt = idx / 9, k = idx % 9;
+      const int off = k < 8 ? 2 * (256 * half + 128 * (k >> 2) + 32 * (k & 3)) : 2 * (kLatent + 32 * half);
+      return *reinterpret_cast<const bf16x8*>(st + kStageK + qk_base + tt * 16 * kKRowBytes + off);
+    };
+    // hook(idx) runs after the MFMAs of piece idx: independent work of another
+    // block that the wave issues while the MFMA pipe is busy (the scheduling
+    // barriers keep the order as written)
+    auto qk_half = [&](const uint8_t* st, const float2 (&sc)[2][4], f32x4 (&s_out)[2][2], auto&& hook) {
+      bf16x8 pa[kAhead + 1];
+      for (int i = 0; i < kAhead; ++i) pa[i] = qk_piece(st, i);
+      f32x4 acc[3][2];  // [latent block 0, 1, rope][rb]
+#pragma unroll
+      for (int idx = 0; idx < 18; ++idx) {
+        const int tt = idx / 9, k = idx % 9;
+        const int slot = k < 8 ? k >> 2 : 2;
+        if (idx + kAhead < 18) pa[(idx + kAhead) % (kAhead + 1)] = qk_piece(st, idx + kAhead);
+        for (int rb = 0; rb < 2; ++rb) {
+          const f32x4 c = (k & 3) == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[slot][rb];
+          acc[slot][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[idx % (kAhead + 1)], qv[rb][k], c, 0, 0, 0);
         }
-        for (int r = 0; r < 2; ++r) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 2 * (kLatent + 32 * r));
-          accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qv[16 + r], accr, 0, 0, 0);
-        }
-        // lane holds S[key kb + 16 tt + 4 g4 + i][row n]
-        for (int i = 0; i < 4; ++i) {
-          const float4 sc = *reinterpret_cast<const float4*>(st + kStageScl + 16 * (16 * tt + 4 * g4 + i));
-          sv[tt][i] = accr[i] + sc.x * acc[0][i] + sc.y * acc[1][i] + sc.z * acc[2][i] + sc.w * acc[3][i];
-          sp[0][tt][i] = half ? sc.z : sc.x;
-          sp[1][tt][i] = half ? sc.w : sc.y;
-        }
-      }
-      if (kb + kStageKeys - 1 > lim_min) {
-        for (int tt = 0; tt < 2; ++tt)
+        __builtin_amdgcn_sched_barrier(0);
+        hook(idx);
+        __builtin_amdgcn_sched_barrier(0);
+        if (k == 8) {
           for (int i = 0; i < 4; ++i)
-            if (kb + 16 * tt + 4 * g4 + i > lim) sv[tt][i] = -INFINITY;
-      }
-      // ---- online softmax (bf16 P: the reference max may lag) -----------------
-      float mx = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
-                       fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
-      mx = pair32(pair16(mx, true), true);
-      const float m_max = fmaxf(m_run, mx);
-      const bool move = m_run == -INFINITY ? m_max != -INFINITY : (m_max - m_run) * c2 > kLazyLog2;
-      const float m_new = move ? m_max : m_run;
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float corr = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
-      float pr[2][4], psum = 0.f;
-      for (int tt = 0; tt < 2; ++tt)
-        for (int i = 0; i < 4; ++i) {
-          pr[tt][i] = __builtin_amdgcn_exp2f((sv[tt][i] - m_use) * c2);
-          psum += pr[tt][i];
-        }
-      l_part = l_part * corr + psum;
-      if (__builtin_amdgcn_ballot_w64(move)) {
-        for (int gg = 0; gg < 2; ++gg)
-          for (int mt = 0; mt < 8; ++mt) oacc[gg][mt] *= corr;
-      }
-      m_run = m_new;
-      // ---- O^T += V^T (P * scale)^T for this wave's 256 d_v ------------------
-      // k-slot e of lane group g4: key 4 g4 + e (e < 4) or 16 + 4 g4 + e - 4
-      for (int gg = 0; gg < 2; ++gg) {
-        bf16x8 pb;  // P scaled by the block scale of d_v block 2 half + gg
-        for (int tt = 0; tt < 2; ++tt)
-          for (int i = 0; i < 4; ++i) pb[4 * tt + i] = (__bf16)(pr[tt][i] * sp[gg][tt][i]);
-        for (int mt = 0; mt < 8; ++mt) {
-          const uint8_t* v = st + kStageK + tr_base + 512 * half + 256 * gg + 32 * mt;
-          const s16x4 lo = lds_read_tr16(v);
-          const s16x4 hi = lds_read_tr16(v + 16 * kKRowBytes);
-          const s16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          bf16x8 a;
-          __builtin_memcpy(&a, &a16, 16);
-          oacc[gg][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, oacc[gg][mt], 0, 0, 0);
+            for (int rb = 0; rb < 2; ++rb)
+              s_out[tt][rb][i] = acc[2][rb][i] + sc[tt][i].x * acc[0][rb][i] + sc[tt][i].y * acc[1][rb][i];
         }
       }
     };
-
-    // Block j: fetched at step j - (kRing - 1), staged into LDS stage j % 2 at
-    // step j - 1, processed at step j. Rounds of 2 kRing steps keep the ring
-    // and stage indices compile-time; steps past the last block fetch clamped
-    // rows, stage them and skip the math, so every wave runs the same loads
-    // and barriers.
-    constexpr int kRound = 2 * kRing;
-    const int nblocks = (k_end - k_begin + kStageKeys - 1) / kStageKeys;
-    RawPiece ring[kRing];
+    // S = this wave's partial + the partner's (the same two numbers in both
+    // waves), with the mask of the block at kb
+    auto gather_s = [&](f32x4 (&sv)[2][2], const uint8_t* sx_partner, int kb) {
+      for (int tt = 0; tt < 2; ++tt)
+        for (int rb = 0; rb < 2; ++rb)
+          sv[tt][rb] += *reinterpret_cast<const f32x4*>(sx_partner + ((2 * tt + rb) * 64 + lane) * 16);
+      if (kb + kStageKeys - 1 > lim_min) {
+        for (int tt = 0; tt < 2; ++tt)
+          for (int rb = 0; rb < 2; ++rb)
+            for (int i = 0; i < 4; ++i)
+              if (kb + 16 * tt + 4 * g4 + i > lim[rb]) sv[tt][rb][i] = -INFINITY;
+      }
+    };
+    // Online softmax of one block in 18 parts (run between the MFMAs of the
+    // next block's QK^T): part 0 the row max, part 1 the reference, parts
+    // 2-9 two exponentials each, parts 10-17 four scaled P values each. l and
+    // the reference max are updated; pb[rb][gg] = P scaled by the block scale
+    // of d_v block 2 half + gg; `overflow` is set if some p would pass
+    // 2^kFixedLog2.
+    // Each part's results pass through an empty asm statement where they are
+    // made, which keeps the compiler from sinking the arithmetic down to its
+    // uses in PV (the scheduling barriers order instructions, not values).
+    float sm_mx[2], sm_off[2], sm_pr[2][8];
+    auto softmax_part = [&](int i, const f32x4 (&sv)[2][2], const float2 (&sc2)[2][4], bf16x8 (&pb)[2][2],
+                            bool& overflow) {
+      if (i == 0) {
+        for (int rb = 0; rb < 2; ++rb) {
+          const float mx = fmaxf(fmaxf(fmaxf(sv[0][rb][0], sv[0][rb][1]), fmaxf(sv[0][rb][2], sv[0][rb][3])),
+                                 fmaxf(fmaxf(sv[1][rb][0], sv[1][rb][1]), fmaxf(sv[1][rb][2], sv[1][rb][3])));
+          sm_mx[rb] = pair32(pair16(mx, true), true);
+          asm volatile("" : "+v"(sm_mx[rb]));
+        }
+      } else if (i == 1) {
+        for (int rb = 0; rb < 2; ++rb) {
+          m_seen[rb] = fmaxf(m_seen[rb], sm_mx[rb]);
+          // the first visible block sets the reference (O and l are still zero)
+          m_run[rb] = m_run[rb] == -INFINITY ? sm_mx[rb] : m_run[rb];
+          overflow |= (sm_mx[rb] - m_run[rb]) * c2 > kFixedLog2;
+          // one fma per score: exp2(s c2 - m c2); no visible key yet: exp2(-inf) = 0
+          sm_off[rb] = m_run[rb] == -INFINITY ? 0.f : -m_run[rb] * c2;
+          asm volatile("" : "+v"(sm_off[rb]));
+        }
+      } else if (i < 10) {
+        for (int e = 2 * (i - 2); e < 2 * (i - 2) + 2; ++e) {  // element e = 8 rb + 4 tt + ii
+          const int rb = e >> 3, tt = (e >> 2) & 1, ii = e & 3;
+          sm_pr[rb][4 * tt + ii] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[tt][rb][ii], c2, sm_off[rb]));
+          asm volatile("" : "+v"(sm_pr[rb][4 * tt + ii]));
+        }
+        if (i == 9) {
+          for (int rb = 0; rb < 2; ++rb) {
+            float psum = 0.f;
+            for (int e = 0; e < 8; ++e) psum += sm_pr[rb][e];
+            l_part[rb] += psum;
+            asm volatile("" : "+v"(l_part[rb]));
+          }
+        }
+      } else {
+        const int tt = (i - 10) >> 2, ii = (i - 10) & 3;  // key 16 tt + 4 g4 + ii: k-slot 4 tt + ii
+        const float2 sc = sc2[tt][ii];
+        for (int rb = 0; rb < 2; ++rb) {
+          pb[rb][0][4 * tt + ii] = (__bf16)(sm_pr[rb][4 * tt + ii] * sc.x);
+          pb[rb][1][4 * tt + ii] = (__bf16)(sm_pr[rb][4 * tt + ii] * sc.y);
+          asm volatile("" : "+v"(pb[rb][0]), "+v"(pb[rb][1]));
+        }
+      }
+    };
+    // O^T += V^T (P * scale)^T for this wave's 256 d_v: V^T tile (gg, mt) =
+    // tile 8 gg + mt, read kAhead tiles ahead of its MFMAs
+    auto v_tile = [&](const uint8_t* st, int idx) -> bf16x8 {
+      const uint8_t* v = st + kStageK + tr_base + 512 * half + 256 * (idx >> 3) + 32 * (idx & 7);
+      const s16x4 lo = lds_read_tr16(v);
+      const s16x4 hi = lds_read_tr16(v + 16 * kKRowBytes);
+      const s16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      bf16x8 a;
+      __builtin_memcpy(&a, &a16, 16);
+      return a;
+    };
+    auto pv_step = [&](const uint8_t* st, const bf16x8 (&pb)[2][2]) {
+      bf16x8 va[kAhead + 1];
+      for (int i = 0; i < kAhead; ++i) va[i] = v_tile(st, i);
 #pragma unroll
-    for (int u = 0; u < kRing - 1; ++u) fetch(ring[u], k_begin + u * kStageKeys, u);
+      for (int idx = 0; idx < 16; ++idx) {
+        if (idx + kAhead < 16) va[(idx + kAhead) % (kAhead + 1)] = v_tile(st, idx + kAhead);
+        const int gg = idx >> 3, mt = idx & 7;
+        for (int rb = 0; rb < 2; ++rb)
+          oacc[rb][gg][mt] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[idx % (kAhead + 1)], pb[rb][gg], oacc[rb][gg][mt], 0, 0, 0);
+      }
+    };
+    uint8_t* sx_base = lds + kSxOffset;
+    auto sx_of = [&](int buf, int wave) { return sx_base + (buf * kLdsWaves + wave) * kSxWaveBytes; };
+    auto put_s = [&](uint8_t* sx, const f32x4 (&sv)[2][2]) {
+      for (int tt = 0; tt < 2; ++tt)
+        for (int rb = 0; rb < 2; ++rb) *reinterpret_cast<f32x4*>(sx + ((2 * tt + rb) * 64 + lane) * 16) = sv[tt][rb];
+    };
+
+    // One barrier per step. Block j: fetched in step j - RING, staged into
+    // stage j % 3 in step j - 1; in step j its partial S goes through buffer
+    // j % 2 (written before the barrier, the partner's read after it), then
+    // its softmax and PV. Stage j + 1 is written in step j before the barrier;
+    // its previous block (j - 2) was last read in step j - 2, before the
+    // barrier that ends it. Exchange buffer j % 2 is rewritten in step j + 2,
+    // after the barrier that ends step j + 1, by which the partner has read
+    // it. Rounds of 6 steps keep the ring, stage and buffer indices
+    // compile-time; the loop leaves after the last block's step (a uniform
+    // branch, so every wave meets the same barriers).
+    static_assert(6 % RING == 0, "a round of 6 steps must hold whole rings");
+    constexpr int kRound = 6;
+    const int nblocks = (k_end - k_begin + kStageKeys - 1) / kStageKeys;
+    RawPiece ring[RING];
+    f32x4 sv[2][2];
+    float2 sc[2][4];
+    bf16x8 pb[2][2];
+    auto load_scales = [&](const uint8_t* st, float2 (&out)[2][4]) {
+      for (int tt = 0; tt < 2; ++tt)
+        for (int i = 0; i < 4; ++i) out[tt][i] = scale2(st, tt, i);
+    };
+#pragma unroll
+    for (int u = 0; u < RING; ++u) {
+      fetch(ring[u], k_begin + u * kStageKeys, u % 3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     stage_in(ring[0], lds);
     barrier();
     const int rounds = (nblocks + kRound - 1) / kRound;
@@ -348,37 +488,65 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
 #pragma unroll
       for (int s = 0; s < kRound; ++s) {
         const int j = r * kRound + s;
+        if (j >= nblocks) goto loop_done;
         const int kb = k_begin + j * kStageKeys;
-        fetch(ring[(s + kRing - 1) % kRing], kb + (kRing - 1) * kStageKeys, (s + kRing - 1) % kRing);
-        stage_in(ring[(s + 1) % kRing], lds + ((s + 1) & 1) * kStageBytes);
-        if (wave_rows && j < nblocks) compute(lds + (s & 1) * kStageBytes, kb);
+        fetch(ring[s % RING], kb + RING * kStageKeys, (s + RING) % 3);
+        const uint8_t* st = lds + (s % 3) * kStageBytes;
+        load_scales(st, sc);
+        qk_half(st, sc, sv, [](int) {});
+        put_s(sx_of(s & 1, w), sv);
+        stage_in(ring[(s + 1) % RING], lds + ((s + 1) % 3) * kStageBytes);
         barrier();
+        if (__builtin_amdgcn_readfirstlane(*restart_flag)) {
+          again = true;
+          goto item_end;
+        }
+        gather_s(sv, sx_of(s & 1, w ^ 1), kb);
+        bool overflow = false;
+#pragma unroll
+        for (int i = 0; i < 18; ++i) softmax_part(i, sv, sc, pb, overflow);
+        if (__builtin_amdgcn_ballot_w64(overflow) && lane == 0) *restart_flag = 1;
+        pv_step(st, pb);
       }
     }
+  loop_done:
+    // a flag set by the last block's softmax has met its barrier; re-read it
+    // after one more, which every wave reaches the same way
+    barrier();
+    again = __builtin_amdgcn_readfirstlane(*restart_flag) != 0;
   }
+item_end:
+  if (again) {
+    barrier();  // every wave has read the flag
+    if (t == 0) *restart_flag = 0;
+    for (int rb = 0; rb < 2; ++rb) m_run[rb] = m_seen[rb];
+  }
+  } while (again);
 
   // ---- epilogue: this wave's d_v half; LSE / (max, sum) from the first half -------
-  const float l = pair32(pair16(l_part, false), false);
-  if (!row_ok) return;
-  const int64_t stat_row = (int64_t)b * p.rows + n;
-  const float m_nat = m_run == -INFINITY ? -INFINITY : m_run * p.scale;
-  const int d0 = 256 * half + 4 * g4;
-  if (direct) {
-    const float inv = l > 0.f ? p.o_scale / l : 0.f;
-    uint8_t* orow = p.o + (int64_t)qtok * p.o_tok + (int64_t)qhead * p.o_head;
-    for (int gg = 0; gg < 2; ++gg)
-      for (int mt = 0; mt < 8; ++mt) {
-        bf16x4 out;
-        for (int i = 0; i < 4; ++i) out[i] = (__bf16)(oacc[gg][mt][i] * inv);
-        *reinterpret_cast<bf16x4*>(orow + 2 * (d0 + 128 * gg + 16 * mt)) = out;
-      }
-    if (half == 0 && g4 == 0) p.lse[stat_row] = l > 0.f ? m_nat + logf(l) : -INFINITY;
-  } else {
-    const int64_t prow = (int64_t)slot * p.num_seqs * p.rows + stat_row;
-    float* dst = p.ws_o + prow * kDv + d0;
-    for (int gg = 0; gg < 2; ++gg)
-      for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(dst + 128 * gg + 16 * mt) = oacc[gg][mt];
-    if (half == 0 && g4 == 0) p.ws_ml[prow] = float2{m_nat, l};
+  for (int rb = 0; rb < 2; ++rb) {
+    const float l = pair32(pair16(l_part[rb], false), false);
+    if (!row_ok[rb]) continue;
+    const int64_t stat_row = (int64_t)b * p.rows + row0 + 16 * rb + r16;
+    const float m_nat = m_run[rb] == -INFINITY ? -INFINITY : m_run[rb] * p.scale;
+    const int d0 = 256 * half + 4 * g4;
+    if (direct) {
+      const float inv = l > 0.f ? p.o_scale / l : 0.f;
+      uint8_t* orow = p.o + (int64_t)qtok[rb] * p.o_tok + (int64_t)qhead[rb] * p.o_head;
+      for (int gg = 0; gg < 2; ++gg)
+        for (int mt = 0; mt < 8; ++mt) {
+          bf16x4 out;
+          for (int i = 0; i < 4; ++i) out[i] = (__bf16)(oacc[rb][gg][mt][i] * inv);
+          *reinterpret_cast<bf16x4*>(orow + 2 * (d0 + 128 * gg + 16 * mt)) = out;
+        }
+      if (half == 0 && g4 == 0) p.lse[stat_row] = l > 0.f ? m_nat + logf(l) : -INFINITY;
+    } else {
+      const int64_t prow = (int64_t)slot * p.num_seqs * p.rows + stat_row;
+      float* dst = p.ws_o + prow * kDv + d0;
+      for (int gg = 0; gg < 2; ++gg)
+        for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(dst + 128 * gg + 16 * mt) = oacc[rb][gg][mt];
+      if (half == 0 && g4 == 0) p.ws_ml[prow] = float2{m_nat, l};
+    }
   }
 }
 
@@ -398,9 +566,14 @@ __device__ __forceinline__ void xcd_item_tile(int id, int units, int tiles, int&
   tile = local / left;
 }
 
+constexpr int kLdsRing = 2;  // raw blocks in flight per thread
+
 template <bool CAUSAL_TAIL>
-__global__ __launch_bounds__(64 * kLdsWaves) void mla_lds_kernel(MlaParams p, int units, int tiles) {
+__global__ __launch_bounds__(64 * kLdsWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_lds_kernel(MlaParams p, int units, int tiles) {
   extern __shared__ __attribute__((aligned(16))) uint8_t mla_stage_lds[];
+  if (threadIdx.x == 0) *reinterpret_cast<int*>(mla_stage_lds + kFlagOffset) = 0;
+  __syncthreads();
   int unit, tile;
   xcd_item_tile(blockIdx.x, units, tiles, unit, tile);
   int it = unit, it_end = unit + 1;
@@ -409,7 +582,7 @@ __global__ __launch_bounds__(64 * kLdsWaves) void mla_lds_kernel(MlaParams p, in
     it_end = p.bin_offsets[unit + 1];
   }
   for (; it < it_end; ++it) {
-    mla_lds_item<CAUSAL_TAIL>(p, it, tile, mla_stage_lds);
+    mla_lds_item<CAUSAL_TAIL, kLdsRing>(p, it, tile, mla_stage_lds);
     __syncthreads();  // the next item's first stage overwrites LDS
   }
 }
@@ -990,7 +1163,7 @@ const void* select_kernel(const pkv_decode_args& a) {
 int waves_per_wg(const pkv_decode_args& a) { return staged(a) ? kLdsWaves : 2 * pair_groups(a); }
 
 size_t dyn_lds_bytes(const pkv_decode_args& a) {
-  if (staged(a)) return (size_t)2 * kStageBytes;
+  if (staged(a)) return (size_t)kLdsBytes;
   return (size_t)2 * pair_groups(a) * kPairWaveBytes;
 }
 

@@ -118,3 +118,27 @@ def test_latent_staged_graph_replay():
         torch.cuda.synchronize()
         assert torch.equal(dec.o.view(torch.int16), eager_o.view(torch.int16)), f"replay {rep}"
         assert torch.equal(dec.lse.view(torch.int32), eager_l.view(torch.int32)), f"replay {rep}"
+
+
+@pytest.mark.parametrize("force", [0, 3])
+def test_latent_staged_late_huge_score_restarts(force):
+    # The staged form fixes each row's reference max at its first visible
+    # block; a key whose score lies far above it (here ~5e4 raw units over a
+    # first-block max of ~30, with the softmax scale 1/24) would push some p
+    # past the kernel's bound, so the workgroup runs the item again with the
+    # larger reference. The result must still be the plain softmax.
+    w = workload(5, q_len=4, num_seqs=2, seq_len_dist=("fixed", [900, 700]), max_splits=8)
+    batch = make_batch(w, device="cuda")
+    j0 = 100  # key of sequence 0, in its fourth 32-key block
+    page = int(batch.block_table[0, j0 // w.page_size])
+    row = j0 % w.page_size
+    q0 = batch.q[0, 0, :512].float()  # query token 0, head 0: sees keys 0 .. L - 4
+    codes = (q0 / 0.02).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    batch.mla_latent[page, row, 0] = codes
+    batch.mla_scales[page, row, 0] = 2.0
+    dec = run_batch(batch, force_splits=force)
+    assert dec.kernel_name == "mla_lds_kernel"
+    err_o, err_l, _ = compare(batch, dec, what=f"latent late huge score force={force}")
+    lse = dec.lse[0, 0, 0].item()
+    assert lse > 1000.0, lse  # the planted key dominates row 0
+    print(f"force={force}: LSE row 0 = {lse:.3f}, max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
