@@ -40,6 +40,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kLatent = 512;
 constexpr int kRope = 64;
@@ -88,15 +89,35 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) {
   return r;
 }
 
+// max of two and of three, written out: through fmaxf the compiler first
+// canonicalises each operand that comes from an MFMA or a lane swap (a v_max
+// of the value with itself), which doubles the work. No operand here is a
+// signalling NaN.
+__device__ __forceinline__ float max2f(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// two fp32 values as one packed bf16 pair (round to nearest even)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2));
+}
+
 __device__ __forceinline__ float pair16(float x, bool take_max) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
-  return take_max ? fmaxf(a, b) : a + b;
+  return take_max ? max2f(a, b) : a + b;
 }
 __device__ __forceinline__ float pair32(float x, bool take_max) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
-  return take_max ? fmaxf(a, b) : a + b;
+  return take_max ? max2f(a, b) : a + b;
 }
 
 // ---- multi-token form: records staged once per workgroup ---------------------
@@ -372,9 +393,9 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
               if (kb + 16 * tt + 4 * g4 + i > lim[rb]) sv[tt][rb][i] = -INFINITY;
       }
     };
-    // Online softmax of one block in 18 parts (run between the MFMAs of the
+    // Online softmax of one block in 14 parts (run between the MFMAs of the
     // next block's QK^T): part 0 the row max, part 1 the reference, parts
-    // 2-9 two exponentials each, parts 10-17 four scaled P values each. l and
+    // 2-9 two exponentials each, parts 10-13 eight scaled P values each (four packed pairs). l and
     // the reference max are updated; pb[rb][gg] = P scaled by the block scale
     // of d_v block 2 half + gg; `overflow` is set if some p would pass
     // 2^kFixedLog2.
@@ -382,12 +403,13 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
     // made, which keeps the compiler from sinking the arithmetic down to its
     // uses in PV (the scheduling barriers order instructions, not values).
     float sm_mx[2], sm_off[2], sm_pr[2][8];
-    auto softmax_part = [&](int i, const f32x4 (&sv)[2][2], const float2 (&sc2)[2][4], bf16x8 (&pb)[2][2],
+    auto softmax_part = [&](int i, const f32x4 (&sv)[2][2], const float2 (&sc2)[2][4], u32x4 (&pb)[2][2],
                             bool& overflow) {
       if (i == 0) {
         for (int rb = 0; rb < 2; ++rb) {
-          const float mx = fmaxf(fmaxf(fmaxf(sv[0][rb][0], sv[0][rb][1]), fmaxf(sv[0][rb][2], sv[0][rb][3])),
-                                 fmaxf(fmaxf(sv[1][rb][0], sv[1][rb][1]), fmaxf(sv[1][rb][2], sv[1][rb][3])));
+          const float mx = max3f(max3f(sv[0][rb][0], sv[0][rb][1], sv[0][rb][2]),
+                                 max3f(sv[0][rb][3], sv[1][rb][0], sv[1][rb][1]),
+                                 max3f(sv[1][rb][2], sv[1][rb][3], -INFINITY));
           sm_mx[rb] = pair32(pair16(mx, true), true);
           asm volatile("" : "+v"(sm_mx[rb]));
         }
@@ -415,12 +437,14 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
             asm volatile("" : "+v"(l_part[rb]));
           }
         }
-      } else {
-        const int tt = (i - 10) >> 2, ii = (i - 10) & 3;  // key 16 tt + 4 g4 + ii: k-slot 4 tt + ii
-        const float2 sc = sc2[tt][ii];
+      } else if (i < 14) {
+        // keys 16 tt + 4 g4 + 2 jj, + 1: k-slots 4 tt + 2 jj, + 1 (word 2 tt + jj)
+        const int tt = (i - 10) >> 1, jj = (i - 10) & 1;
+        const float2 s0 = sc2[tt][2 * jj], s1 = sc2[tt][2 * jj + 1];
         for (int rb = 0; rb < 2; ++rb) {
-          pb[rb][0][4 * tt + ii] = (__bf16)(sm_pr[rb][4 * tt + ii] * sc.x);
-          pb[rb][1][4 * tt + ii] = (__bf16)(sm_pr[rb][4 * tt + ii] * sc.y);
+          const float p0 = sm_pr[rb][4 * tt + 2 * jj], p1 = sm_pr[rb][4 * tt + 2 * jj + 1];
+          pb[rb][0][2 * tt + jj] = pack_bf16x2(p0 * s0.x, p1 * s1.x);
+          pb[rb][1][2 * tt + jj] = pack_bf16x2(p0 * s0.y, p1 * s1.y);
           asm volatile("" : "+v"(pb[rb][0]), "+v"(pb[rb][1]));
         }
       }
@@ -436,7 +460,7 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
       __builtin_memcpy(&a, &a16, 16);
       return a;
     };
-    auto pv_step = [&](const uint8_t* st, const bf16x8 (&pb)[2][2]) {
+    auto pv_step = [&](const uint8_t* st, const u32x4 (&pb)[2][2]) {
       bf16x8 va[kAhead + 1];
       for (int i = 0; i < kAhead; ++i) va[i] = v_tile(st, i);
 #pragma unroll
@@ -445,7 +469,8 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
         const int gg = idx >> 3, mt = idx & 7;
         for (int rb = 0; rb < 2; ++rb)
           oacc[rb][gg][mt] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[idx % (kAhead + 1)], pb[rb][gg], oacc[rb][gg][mt], 0, 0, 0);
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[idx % (kAhead + 1)], __builtin_bit_cast(bf16x8, pb[rb][gg]),
+                                                  oacc[rb][gg][mt], 0, 0, 0);
       }
     };
     uint8_t* sx_base = lds + kSxOffset;
@@ -471,7 +496,7 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
     RawPiece ring[RING];
     f32x4 sv[2][2];
     float2 sc[2][4];
-    bf16x8 pb[2][2];
+    u32x4 pb[2][2];  // packed bf16 pairs
     auto load_scales = [&](const uint8_t* st, float2 (&out)[2][4]) {
       for (int tt = 0; tt < 2; ++tt)
         for (int i = 0; i < 4; ++i) out[tt][i] = scale2(st, tt, i);
@@ -504,7 +529,7 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
         gather_s(sv, sx_of(s & 1, w ^ 1), kb);
         bool overflow = false;
 #pragma unroll
-        for (int i = 0; i < 18; ++i) softmax_part(i, sv, sc, pb, overflow);
+        for (int i = 0; i < 14; ++i) softmax_part(i, sv, sc, pb, overflow);
         if (__builtin_amdgcn_ballot_w64(overflow) && lane == 0) *restart_flag = 1;
         pv_step(st, pb);
       }
