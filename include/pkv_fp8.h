@@ -17,7 +17,11 @@
  * reduction kernel). The latent-record variant (kv_format = PKV_KV_MLA;
  * "vLLM PR #62633", Kernel design) has one KV head whose key is 512 e4m3
  * latent values times one fp32 scale per 128-value block followed by 64 bf16
- * rope values, and whose value is the scaled latent part.
+ * rope values, and whose value is the scaled latent part. The page
+ * dequantises a record exactly to bf16, so the record's scales are read as
+ * powers of two; the multi-token form (64 query rows and more) folds a
+ * power-of-two scale into its bf16 key rows exactly and rounds the product
+ * of any other scale to bf16, the other forms are exact for any scale.
  *
  * Call sequence (the page's module docstring, "Split-KV scheduling" and
  * "Workspace"; "MiniMax MSA fmha_sm100/cute README", Paged FP8 Decode,
@@ -269,6 +273,7 @@ pkv_status pkv_plan_queued(const int32_t* seq_lens, int32_t num_seqs, int32_t h_
  *          MLA: k = v = latent [pages][PS][1][512] e4m3 (v may be NULL or equal k)
  *   k_rope MLA only: [pages][PS][1][64] bf16 (page, row strides)
  *   k_blk_scale MLA only: [pages][PS][1][4] fp32, one scale per 128 latent values
+ *          (a power of two in the record format; pkv_write_kv writes such scales)
  *   block_table [num_seqs][max_blocks] int32 (bt_row_stride)
  *   seq_lens    [num_seqs] int32
  *   q/k/v_descale fp32 at [b * seq_stride + g * head_stride] (unused for MLA)
@@ -469,7 +474,8 @@ size_t pkv_quant_q_args_size(void);
  *                likewise v; round to nearest even, |x| beyond 448 saturates to
  *                +-448, NaN gives 0x7F.
  *   PKV_KV_MLA:  h_k = 1 and d = 576; per token and 128-value latent block j:
- *                scale_j = max(amax_j, 1e-6) / 448, k_blk_scale[page][row][j] = scale_j,
+ *                scale_j = the smallest power of two >= max(amax_j, 1e-6) / 448 (fp32),
+ *                k_blk_scale[page][row][j] = scale_j,
  *                k[page][row][128j + i] = e4m3(x[128j + i] / scale_j); the 64
  *                rope values are copied bit for bit into k_rope. v_* unused.
  * One launch, no workspace, no synchronisation (capturable). Tokens written

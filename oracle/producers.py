@@ -19,9 +19,12 @@ tokens included), row pos % page_size of page block_table[b][pos /
 page_size], skipping a token whose position is negative or whose block-table
 entry is missing or outside the pool; the descales are inputs; a value beyond the e4m3 range saturates
 to +-448 and NaN stays NaN (0x7F). The latent-record write computes one scale
-per token and 128-value block (largest |x| of the block, at least 1e-6, over
-448), stores the codes of x / scale, copies the 64 bf16 rope values bitwise
-and stores the four fp32 scales.
+per token and 128-value block, the smallest power of two at or above the
+block's largest |x| (at least 1e-6) over 448 in fp32 ("vLLM PR #62633",
+Kernel design: the kernel dequantises a record exactly to bf16, which a code
+times an arbitrary fp32 scale would not allow: the code carries 4 significant
+bits and bf16 8), stores the codes of x / scale, copies the 64 bf16 rope
+values bitwise and stores the four fp32 scales.
 
 Pinned by tests/test_producers_oracle.py: encode_e4m3 against torch's
 float8_e4m3fn cast over a dense sweep of the finite range, the round trip of
@@ -30,6 +33,8 @@ hand-worked example and its invariants (the largest |q| of a group maps to
 +-448, a zero group gives zero codes); the writes by hand-worked positions and
 by the error bound of the round trip.
 """
+
+import math
 
 import numpy as np
 
@@ -108,6 +113,13 @@ def write_kv_e4m3(cache, x_new, seq_lens, n_new, block_table, descale):
     return out
 
 
+def pow2_ceil(v):
+    """The smallest power of two >= v > 0 (v = m 2^e with m in [0.5, 1): v
+    itself when m = 0.5, else 2^e)."""
+    m, e = math.frexp(float(v))
+    return float(v) if m == 0.5 else math.ldexp(1.0, e)
+
+
 def write_kv_latent(lat, rope, scl, x_new, rope_new, seq_lens, n_new, block_table):
     """Latent-record write. lat uint8 [pages, ps, 512], rope uint16 [pages, ps,
     64] (bf16 bits), scl float32 [pages, ps, 4]; x_new float32 [num_seqs *
@@ -124,7 +136,7 @@ def write_kv_latent(lat, rope, scl, x_new, rope_new, seq_lens, n_new, block_tabl
             if pages[b, t] < 0:
                 continue
             amax = np.maximum(np.abs(x[b, t]).max(axis=1).astype(np.float32), np.float32(1e-6))
-            s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+            s = np.array([pow2_ceil(v) for v in (amax / np.float32(E4M3_MAX)).astype(np.float32)], np.float32)
             lat[pages[b, t], rows[b, t]] = encode_e4m3((x[b, t] / s[:, None]).astype(np.float32)).reshape(-1)
             scl[pages[b, t], rows[b, t]] = s
             rope[pages[b, t], rows[b, t]] = r[b, t]

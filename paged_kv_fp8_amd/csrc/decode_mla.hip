@@ -81,6 +81,35 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint2 x) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// codes x record block scale, as bf16. The scaled convert applies only the
+// exponent of its scale operand, so it is exact, and the product, when the
+// scale is a normal power of two (the record format's scales); any other
+// scale takes the fp32 product, rounded to bf16.
+__device__ __forceinline__ bf16x8 e4m3x8_times_pow2(uint2 x, float s) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, s, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, s, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, s, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, s, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+__device__ __forceinline__ bf16x8 e4m3x8_times_any(uint2 x, float s) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(x.x, false), __builtin_amdgcn_cvt_pk_f32_fp8(x.x, true),
+                        __builtin_amdgcn_cvt_pk_f32_fp8(x.y, false), __builtin_amdgcn_cvt_pk_f32_fp8(x.y, true)};
+  bf16x8 r;
+  for (int h = 0; h < 4; ++h) {
+    const bf16x2 o = __builtin_convertvector((f32x2_t){v[h][0] * s, v[h][1] * s}, bf16x2);
+    r[2 * h] = o[0];
+    r[2 * h + 1] = o[1];
+  }
+  return r;
+}
+// true when every one of the four fp32 scales is a normal power of two
+__device__ __forceinline__ bool pow2_scales(uint4 s) {
+  const uint32_t lo = min(min(s.x, s.y), min(s.z, s.w)), hi = max(max(s.x, s.y), max(s.z, s.w));
+  return ((s.x | s.y | s.z | s.w) & 0x807FFFFFu) == 0 && lo >= 0x00800000u && hi <= 0x7F000000u;
+}
+
 __device__ __forceinline__ uint2 half_of(uint4 x, int h) { return h ? uint2{x.z, x.w} : uint2{x.x, x.y}; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) {
@@ -122,9 +151,9 @@ __device__ __forceinline__ float pair32(float x, bool take_max) {
 
 // ---- multi-token form: records staged once per workgroup ---------------------
 // From 64 query rows on, the latent records of each 32-key block are
-// dequantised ONCE per workgroup into LDS as bf16 key rows (512 latent codes,
-// exact, then the 64 bf16 rope values) plus the block scales, in a ring of
-// three stages. Both MFMA operands come from there:
+// dequantised ONCE per workgroup into LDS as bf16 key rows (512 latent
+// values, code x block scale, exact for the record's power-of-two scales,
+// then the 64 bf16 rope values), in a ring of three stages. Both MFMA operands come from there:
 //  * QK^T reads 16-byte pieces of the key rows (keys on M, two 16-key tiles);
 //  * PV reads V^T straight from the same rows with the LDS transpose load
 //    (ds_read_b64_tr_b16): within each 16-lane group, lane i receives element
@@ -143,7 +172,7 @@ __device__ __forceinline__ float pair32(float x, bool take_max) {
 // same two numbers, so S, the softmax statistics and P agree bit for bit and
 // no part of S is computed twice.
 // The 256 threads split a block's loads (64 latent bytes, 16 rope bytes and
-// one scale each), RING blocks ahead of the math in a register ring. One
+// the key's 16 scale bytes each), RING blocks ahead of the math in a register ring. One
 // barrier per block: stage j is written in step j - 1 and read in step j, and
 // rewritten in step j + 2 after the barrier of step j + 1; the partial-S
 // exchange is double-buffered the same way.
@@ -156,8 +185,7 @@ constexpr int kStageKeys = 32;                          // keys per step
 // transpose loads) both hit distinct banks
 constexpr int kKRowBytes = 2 * (kLatent + kRope) + 32;
 constexpr int kStageK = 0;
-constexpr int kStageScl = kStageKeys * kKRowBytes;
-constexpr int kStageBytes = kStageScl + kStageKeys * 16;
+constexpr int kStageBytes = kStageKeys * kKRowBytes;
 constexpr int kStages = 3;
 // partial S of one wave: [key tile][row block][lane] f32x4
 constexpr int kSxWaveBytes = 2 * 2 * 64 * 16;
@@ -168,11 +196,12 @@ constexpr float kFixedLog2 = 32.0f;  // p = exp2((s - m_run) c2) stays below 2^3
 constexpr int kAhead = 2;            // LDS operand pieces read ahead of their MFMAs
 
 // One thread's loads of one 32-key block: key t >> 3, latent bytes 8 (t & 7) +
-// 64 i (i < 8, two per uint4), rope bytes 16 (t & 7), scale (t & 7) & 3.
+// 64 i (i < 8, two per uint4: lat[i] lies in latent block i), rope bytes
+// 16 (t & 7), and the key's four block scales (fp32 bits).
 struct RawPiece {
   uint4 lat[4];
   uint4 rope;
-  float scl;
+  uint4 scl;
 };
 
 // Byte offset of byte `lane_off + c` of key row `row` in a stage (see
@@ -314,25 +343,28 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
         r.lat[i] = uint4{c0.x, c0.y, c1.x, c1.y};
       }
       r.rope = *reinterpret_cast<const uint4*>(rope + (key * (uint32_t)p.rope_row + 16u * part));
-      r.scl = *reinterpret_cast<const float*>(scl + (key * (uint32_t)p.scl_row + 4u * (part & 3)));
+      r.scl = *reinterpret_cast<const uint4*>(scl + key * (uint32_t)p.scl_row);
       pv[(ps + 2) % 3] = page_pair(kb + 2 * kStageKeys);
     };
     // 16-byte pieces of the key row: bf16 latent pieces 8 i + part (codes
     // 64 i + 8 part .., so each 8-lane group stores 128 contiguous bytes),
-    // the rope piece part, and scale part & 3 (threads part and part + 4 store
-    // the same value)
-    auto stage_part = [&](const RawPiece& r, uint8_t* st, int i) {
-      if (i < 8) {
-        const uint2 c = (i & 1) ? uint2{r.lat[i >> 1].z, r.lat[i >> 1].w} : uint2{r.lat[i >> 1].x, r.lat[i >> 1].y};
-        *reinterpret_cast<bf16x8*>(st + kStageK + krow_base(my_key, 128 * i + 16 * part)) = e4m3x8_to_bf16(c);
-      } else if (i == 8) {
-        *reinterpret_cast<uint4*>(st + kStageK + krow_base(my_key, 2 * kLatent + 16 * part)) = r.rope;
-      } else if (i == 9) {
-        *reinterpret_cast<float*>(st + kStageScl + 16 * my_key + 4 * (part & 3)) = r.scl;
-      }
-    };
+    // then the rope piece part. A wave whose keys all carry power-of-two
+    // scales (the record format) folds them in with the scaled convert;
+    // otherwise the wave takes the fp32 product (a uniform branch).
     auto stage_in = [&](const RawPiece& r, uint8_t* st) {
-      for (int i = 0; i < 10; ++i) stage_part(r, st, i);
+      const float sc[4] = {__uint_as_float(r.scl.x), __uint_as_float(r.scl.y), __uint_as_float(r.scl.z),
+                           __uint_as_float(r.scl.w)};
+      uint8_t* row = st + kStageK;
+      if (__builtin_amdgcn_ballot_w64(!pow2_scales(r.scl)) == 0) {
+        for (int i = 0; i < 8; ++i)
+          *reinterpret_cast<bf16x8*>(row + krow_base(my_key, 128 * i + 16 * part)) =
+              e4m3x8_times_pow2(half_of(r.lat[i >> 1], i & 1), sc[i >> 1]);
+      } else {
+        for (int i = 0; i < 8; ++i)
+          *reinterpret_cast<bf16x8*>(row + krow_base(my_key, 128 * i + 16 * part)) =
+              e4m3x8_times_any(half_of(r.lat[i >> 1], i & 1), sc[i >> 1]);
+      }
+      *reinterpret_cast<uint4*>(row + krow_base(my_key, 2 * kLatent + 16 * part)) = r.rope;
     };
 
     // this lane's QK^T piece (key row r16 of a tile, bytes 16 g4 ..) and
@@ -340,11 +372,6 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
     // rows 16 apart share the swizzle
     const int qk_base = krow_base(r16, 16 * g4);
     const int tr_base = krow_base(4 * g4 + (r16 >> 2), 8 * (r16 & 3));
-    // scales of latent blocks 2 half, 2 half + 1 of key 16 tt + 4 g4 + i (read
-    // where they are used, so no block's scales stay live across a phase)
-    auto scale2 = [&](const uint8_t* st, int tt, int i) -> float2 {
-      return *reinterpret_cast<const float2*>(st + kStageScl + 16 * (16 * tt + 4 * g4 + i) + 8 * half);
-    };
     // partial S (s_out[tt][rb]: S[key 16 tt + 4 g4 + i][row 16 rb + r16]) of
     // the block in stage st over this wave's half of d_qk. The 18 K pieces
     // (per key tile: 8 latent k-steps, then the rope k-step) are read kAhead
@@ -354,30 +381,18 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
       const int off = k < 8 ? 2 * (256 * half + 128 * (k >> 2) + 32 * (k & 3)) : 2 * (kLatent + 32 * half);
       return *reinterpret_cast<const bf16x8*>(st + kStageK + qk_base + tt * 16 * kKRowBytes + off);
     };
-    // hook(idx) runs after the MFMAs of piece idx: independent work of another
-    // block that the wave issues while the MFMA pipe is busy (the scheduling
-    // barriers keep the order as written)
-    auto qk_half = [&](const uint8_t* st, const float2 (&sc)[2][4], f32x4 (&s_out)[2][2], auto&& hook) {
+    auto qk_half = [&](const uint8_t* st, f32x4 (&s_out)[2][2]) {
       bf16x8 pa[kAhead + 1];
       for (int i = 0; i < kAhead; ++i) pa[i] = qk_piece(st, i);
-      f32x4 acc[3][2];  // [latent block 0, 1, rope][rb]
 #pragma unroll
       for (int idx = 0; idx < 18; ++idx) {
         const int tt = idx / 9, k = idx % 9;
-        const int slot = k < 8 ? k >> 2 : 2;
         if (idx + kAhead < 18) pa[(idx + kAhead) % (kAhead + 1)] = qk_piece(st, idx + kAhead);
         for (int rb = 0; rb < 2; ++rb) {
-          const f32x4 c = (k & 3) == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[slot][rb];
-          acc[slot][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[idx % (kAhead + 1)], qv[rb][k], c, 0, 0, 0);
+          const f32x4 c = k == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s_out[tt][rb];
+          s_out[tt][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[idx % (kAhead + 1)], qv[rb][k], c, 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        hook(idx);
-        __builtin_amdgcn_sched_barrier(0);
-        if (k == 8) {
-          for (int i = 0; i < 4; ++i)
-            for (int rb = 0; rb < 2; ++rb)
-              s_out[tt][rb][i] = acc[2][rb][i] + sc[tt][i].x * acc[0][rb][i] + sc[tt][i].y * acc[1][rb][i];
-        }
       }
     };
     // S = this wave's partial + the partner's (the same two numbers in both
@@ -393,18 +408,16 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
               if (kb + 16 * tt + 4 * g4 + i > lim[rb]) sv[tt][rb][i] = -INFINITY;
       }
     };
-    // Online softmax of one block in 14 parts (run between the MFMAs of the
-    // next block's QK^T): part 0 the row max, part 1 the reference, parts
-    // 2-9 two exponentials each, parts 10-13 eight scaled P values each (four packed pairs). l and
-    // the reference max are updated; pb[rb][gg] = P scaled by the block scale
-    // of d_v block 2 half + gg; `overflow` is set if some p would pass
+    // Online softmax of one block in 12 parts: part 0 the row max, part 1 the
+    // reference, parts 2-9 two exponentials each, parts 10-11 four packed bf16
+    // pairs of P each. l and the reference max are updated; pb[rb] = P of row
+    // block rb as the B operand of PV; `overflow` is set if some p would pass
     // 2^kFixedLog2.
     // Each part's results pass through an empty asm statement where they are
     // made, which keeps the compiler from sinking the arithmetic down to its
     // uses in PV (the scheduling barriers order instructions, not values).
     float sm_mx[2], sm_off[2], sm_pr[2][8];
-    auto softmax_part = [&](int i, const f32x4 (&sv)[2][2], const float2 (&sc2)[2][4], u32x4 (&pb)[2][2],
-                            bool& overflow) {
+    auto softmax_part = [&](int i, const f32x4 (&sv)[2][2], u32x4 (&pb)[2], bool& overflow) {
       if (i == 0) {
         for (int rb = 0; rb < 2; ++rb) {
           const float mx = max3f(max3f(sv[0][rb][0], sv[0][rb][1], sv[0][rb][2]),
@@ -437,15 +450,13 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
             asm volatile("" : "+v"(l_part[rb]));
           }
         }
-      } else if (i < 14) {
-        // keys 16 tt + 4 g4 + 2 jj, + 1: k-slots 4 tt + 2 jj, + 1 (word 2 tt + jj)
-        const int tt = (i - 10) >> 1, jj = (i - 10) & 1;
-        const float2 s0 = sc2[tt][2 * jj], s1 = sc2[tt][2 * jj + 1];
+      } else {
+        // keys 16 tt + 4 g4 + 2 jj, + 1 sit in k-slots 4 tt + 2 jj, + 1 (word 2 tt + jj)
+        const int tt = i - 10;
         for (int rb = 0; rb < 2; ++rb) {
-          const float p0 = sm_pr[rb][4 * tt + 2 * jj], p1 = sm_pr[rb][4 * tt + 2 * jj + 1];
-          pb[rb][0][2 * tt + jj] = pack_bf16x2(p0 * s0.x, p1 * s1.x);
-          pb[rb][1][2 * tt + jj] = pack_bf16x2(p0 * s0.y, p1 * s1.y);
-          asm volatile("" : "+v"(pb[rb][0]), "+v"(pb[rb][1]));
+          for (int jj = 0; jj < 2; ++jj)
+            pb[rb][2 * tt + jj] = pack_bf16x2(sm_pr[rb][4 * tt + 2 * jj], sm_pr[rb][4 * tt + 2 * jj + 1]);
+          asm volatile("" : "+v"(pb[rb]));
         }
       }
     };
@@ -460,7 +471,7 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
       __builtin_memcpy(&a, &a16, 16);
       return a;
     };
-    auto pv_step = [&](const uint8_t* st, const u32x4 (&pb)[2][2]) {
+    auto pv_step = [&](const uint8_t* st, const u32x4 (&pb)[2]) {
       bf16x8 va[kAhead + 1];
       for (int i = 0; i < kAhead; ++i) va[i] = v_tile(st, i);
 #pragma unroll
@@ -469,7 +480,7 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
         const int gg = idx >> 3, mt = idx & 7;
         for (int rb = 0; rb < 2; ++rb)
           oacc[rb][gg][mt] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[idx % (kAhead + 1)], __builtin_bit_cast(bf16x8, pb[rb][gg]),
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[idx % (kAhead + 1)], __builtin_bit_cast(bf16x8, pb[rb]),
                                                   oacc[rb][gg][mt], 0, 0, 0);
       }
     };
@@ -495,12 +506,7 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
     const int nblocks = (k_end - k_begin + kStageKeys - 1) / kStageKeys;
     RawPiece ring[RING];
     f32x4 sv[2][2];
-    float2 sc[2][4];
-    u32x4 pb[2][2];  // packed bf16 pairs
-    auto load_scales = [&](const uint8_t* st, float2 (&out)[2][4]) {
-      for (int tt = 0; tt < 2; ++tt)
-        for (int i = 0; i < 4; ++i) out[tt][i] = scale2(st, tt, i);
-    };
+    u32x4 pb[2];  // packed bf16 pairs
 #pragma unroll
     for (int u = 0; u < RING; ++u) {
       fetch(ring[u], k_begin + u * kStageKeys, u % 3);
@@ -517,8 +523,7 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
         const int kb = k_begin + j * kStageKeys;
         fetch(ring[s % RING], kb + RING * kStageKeys, (s + RING) % 3);
         const uint8_t* st = lds + (s % 3) * kStageBytes;
-        load_scales(st, sc);
-        qk_half(st, sc, sv, [](int) {});
+        qk_half(st, sv);
         put_s(sx_of(s & 1, w), sv);
         stage_in(ring[(s + 1) % RING], lds + ((s + 1) % 3) * kStageBytes);
         barrier();
@@ -529,7 +534,7 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
         gather_s(sv, sx_of(s & 1, w ^ 1), kb);
         bool overflow = false;
 #pragma unroll
-        for (int i = 0; i < 14; ++i) softmax_part(i, sv, sc, pb, overflow);
+        for (int i = 0; i < 12; ++i) softmax_part(i, sv, pb, overflow);
         if (__builtin_amdgcn_ballot_w64(overflow) && lane == 0) *restart_flag = 1;
         pv_step(st, pb);
       }

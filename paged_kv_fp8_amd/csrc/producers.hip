@@ -201,7 +201,9 @@ __global__ __launch_bounds__(256) void write_kv_latent_kernel(WriteLatParams p) 
   float m = 0.f;
   for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
   for (int off = 8; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));  // 16 lanes = one 128-value block
-  const float scale = fmaxf(m, kMinAmax) / kE4m3Max;
+  // the smallest power of two >= max(amax, 1e-6) / 448: adding an all-ones
+  // mantissa carries into the exponent unless the mantissa is already zero
+  const float scale = __uint_as_float((__float_as_uint(fmaxf(m, kMinAmax) / kE4m3Max) + 0x007FFFFFu) & 0xFF800000u);
   for (int e = 0; e < 8; ++e) x[e] = x[e] / scale;
   *reinterpret_cast<uint2*>(p.lat + (int64_t)page * p.lat_page + (int64_t)row * p.lat_row + 8 * lane) = encode8(x);
   if ((lane & 15) == 0)

@@ -29,8 +29,9 @@ Data recipe (following the t5_decode page's harness, ``run``):
   * K, V ~ N(0, 1) quantised per (sequence, kv head): descale = max(amax over
     that sequence's L tokens and d, 1e-6) / 448, codes = e4m3(x / descale)
     (round to nearest even, |x / descale| <= 448 by construction);
-  * latent records: 512 latent values ~ N(0, 1) with one descale per token
-    and 128-value block (amax / 448), 64 rope values ~ N(0, 1) in bf16;
+  * latent records: 512 latent values ~ N(0, 1) with one scale per token
+    and 128-value block, the smallest power of two >= max(amax, 1e-6) / 448
+    (so that code x scale is exact in bf16), 64 rope values ~ N(0, 1) in bf16;
   * packed e2m1 (fp4) K/V (the page's narrow KV formats): x ~ N(0, 1) per
     (sequence, kv head) with descale = max(amax, 1e-6) / 6 and the code of
     the nearest e2m1 magnitude (ties to the smaller, as the page's
@@ -237,6 +238,13 @@ class Batch:
         return out
 
 
+def pow2_at_least(x):
+    """The smallest power of two >= x, for positive normal float32 x: a
+    nonzero mantissa carries into the exponent field and is then cleared."""
+    bits = x.float().contiguous().view(torch.int32)
+    return ((bits + 0x7FFFFF) & -0x800000).view(torch.float32)
+
+
 def _page_assignment(w, lens, rng):
     ps = w.page_size
     blocks = [-(-int(L) // ps) for L in lens]
@@ -345,7 +353,7 @@ def make_batch(w: Workload, device="cpu", seq_lens=None) -> Batch:
     if w.kv_format == "mla":
         rec = torch.full((num_pages * ps, MLA_RECORD_BYTES), E4M3_NAN, dtype=torch.uint8, device=device)
         lat = torch.randn(n_tok, MLA_LATENT // MLA_BLOCK, MLA_BLOCK, generator=gen, device=device)
-        desc = lat.abs().amax(dim=-1).clamp(min=1e-6) / E4M3_MAX  # (tokens, 4)
+        desc = pow2_at_least(lat.abs().amax(dim=-1).clamp(min=1e-6) / E4M3_MAX)  # (tokens, 4)
         codes = (lat / desc[:, :, None]).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
         rope = torch.randn(n_tok, MLA_ROPE, generator=gen, device=device).to(torch.bfloat16)
         rec[slot, :MLA_LATENT] = codes.view(torch.uint8).view(n_tok, MLA_LATENT)
@@ -410,7 +418,7 @@ def make_batch(w: Workload, device="cpu", seq_lens=None) -> Batch:
 # pages). Lists are padded with -1; pages are handed out from a seeded
 # permutation, spare pages stay poisoned (e4m3 NaN bytes). Records as for the
 # latent workload: 512 values ~ N(0, 1) quantised per 128-value block
-# (amax / 448), 64 rope values ~ N(0, 1) in bf16. Sink logits ~ N(0, 1) per
+# (power-of-two scale >= amax / 448), 64 rope values ~ N(0, 1) in bf16. Sink logits ~ N(0, 1) per
 # head. Query ~ N(0, 1) in bf16, one token per sequence.
 @dataclass(frozen=True)
 class SparseWorkload:
@@ -473,7 +481,7 @@ def _latent_pool(gen, pages, ps, device):
     n = pages * ps
     rec = torch.empty((n, MLA_RECORD_BYTES), dtype=torch.uint8, device=device)
     lat = torch.randn(n, MLA_LATENT // MLA_BLOCK, MLA_BLOCK, generator=gen, device=device)
-    desc = lat.abs().amax(dim=-1).clamp(min=1e-6) / E4M3_MAX
+    desc = pow2_at_least(lat.abs().amax(dim=-1).clamp(min=1e-6) / E4M3_MAX)
     codes = (lat / desc[:, :, None]).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
     rope = torch.randn(n, MLA_ROPE, generator=gen, device=device).to(torch.bfloat16)
     rec[:, :MLA_LATENT] = codes.view(torch.uint8).view(n, MLA_LATENT)

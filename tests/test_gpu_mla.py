@@ -142,3 +142,49 @@ def test_latent_staged_late_huge_score_restarts(force):
     lse = dec.lse[0, 0, 0].item()
     assert lse > 1000.0, lse  # the planted key dominates row 0
     print(f"force={force}: LSE row 0 = {lse:.3f}, max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
+
+
+def _max_qk_abs_dot(batch, w):
+    """max over (sequence, query row, visible key) of sum_i |q_i| |k_i| over the
+    512 latent dims, k = code x block scale (float64)."""
+    lat = batch.mla_latent.cpu().view(torch.float8_e4m3fn).double().reshape(-1, 4, 128)
+    scl = batch.mla_scales.cpu().double().reshape(-1, 4)
+    kabs = (lat * scl[:, :, None]).abs().reshape(-1, 512)
+    q = batch.q.cpu().double()[..., :512].abs()
+    bt = batch.block_table.cpu()
+    best = 0.0
+    for b, L in enumerate(batch.seq_lens.cpu().tolist()):
+        if L == 0:
+            continue
+        keys = torch.arange(L)
+        slots = bt[b, keys // w.page_size].long() * w.page_size + keys % w.page_size
+        qb = q[b * w.q_len:(b + 1) * w.q_len].reshape(-1, 512)
+        best = max(best, float((qb @ kabs[slots].T).max()))
+    return best
+
+
+@pytest.mark.parametrize("T", [4, 16])
+def test_latent_staged_other_scales_round(T):
+    # The record format's scales are powers of two, which the staged form folds
+    # into its bf16 key rows exactly. A wave that meets any other scale takes
+    # the fp32 product rounded to bf16: each dequantised value then carries a
+    # relative error of at most 2^-9, so a score moves by at most
+    # dS = scale * 2^-9 * sum_i |q_i| |k_i| (latent dims), the LSE by dS, and O
+    # by 2^-9 max|V| from V plus 2 (e^(2 dS) - 1) max|V| from the weights.
+    w = workload(5, q_len=T, num_seqs=4, seq_len_dist=("uniform", 300, 1500))
+    batch = make_batch(w, device="cuda")
+    sc = batch.mla_scales.view(-1, 4)
+    sc[::7, 1] *= 1.3
+    sc[3::11, 3] *= 0.77
+    dec = run_batch(batch)
+    assert dec.kernel_name == "mla_lds_kernel"
+    ds = w.scale * 2.0 ** -9 * _max_qk_abs_dot(batch, w)
+    o_tol = O_TOL + 2.0 ** -9 + 2.0 * np.expm1(2.0 * ds)
+    lse_tol = 1e-3 + ds
+    nb = batch.to_numpy()
+    o_ref, lse_ref = oracle_for(nb, batch.spec)
+    o_g, lse_g = gpu_rows(dec.o, dec.lse, batch.spec)
+    err_o, err_l, _ = assert_matches(o_g, lse_g, o_ref, lse_ref, max_abs_v(nb, batch.spec), o_tol=o_tol,
+                                     lse_tol=lse_tol, what=f"latent other scales T={T}")
+    print(f"T={T}: dS bound {ds:.3e}; max|dO|={err_o:.3e} (bar {o_tol:.3e} max|V|) max|dLSE|={err_l:.3e} "
+          f"(bar {lse_tol:.3e})")

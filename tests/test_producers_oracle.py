@@ -109,7 +109,11 @@ def test_write_kv_latent_scales_and_rope():
     scl = np.zeros((pages, ps, 4), np.float32)
     bt = np.array([[2, 0], [3, 1]])
     x = rng.standard_normal((2 * n_new, 512)).astype(np.float32)
-    x[0, 128:256] = 0.0  # a zero block: scale 1e-6/448, codes 0
+    x[0, 128:256] = 0.0  # a zero block: 1e-6 / 448 = 2.23e-9 rounds up to the scale 2^-28, codes 0
+    x[1, 0:128] = 0.0
+    x[1, 5] = 300.0  # 300 / 448 = 0.67 -> scale 1; e4m3(300) = 288 (step 32 above 256)
+    x[1, 128:256] = 0.0
+    x[1, 130] = -448.0 * 2.0 ** -7  # 448 * 2^-7 / 448 is a power of two already: scale 2^-7, code -448
     rn = rng.integers(0, 65536, size=(2 * n_new, 64), dtype=np.uint16)
     lat2, rope2, scl2 = write_kv_latent(lat, rope, scl, x, rn, [3, 16], n_new, bt)
     pg, rw = write_positions([3, 16], n_new, bt, ps)
@@ -120,11 +124,23 @@ def test_write_kv_latent_scales_and_rope():
             s = scl2[pg[b, t], rw[b, t]]
             amax = np.abs(x[i].reshape(4, 128)).max(axis=1)
             for blk in range(4):
+                m, _ = np.frexp(s[blk])
+                assert m == 0.5, s[blk]  # a power of two
                 if amax[blk] == 0:
-                    assert s[blk] == np.float32(1e-6) / np.float32(448) and np.all(vals[blk] == 0)
+                    assert s[blk] == 2.0 ** -28 and np.all(vals[blk] == 0)
                 else:
-                    assert np.abs(vals[blk]).max() == 448
+                    # the smallest power of two >= amax / 448: amax / s lies in (224, 448], and
+                    # its e4m3 code in [224, 448] (just above 224 the code step is 16)
+                    assert amax[blk] / 448 <= s[blk] < 2 * amax[blk] / 448
+                    assert 224 <= np.abs(vals[blk]).max() <= 448
+                    # every code is the e4m3 rounding of x / s (relative error <= 2^-4)
+                    xs = x[i].reshape(4, 128)[blk] / s[blk]
+                    assert np.all(np.abs(vals[blk] - xs) <= np.abs(xs) * 2.0 ** -4 + 2.0 ** -10)
             assert np.array_equal(rope2[pg[b, t], rw[b, t]], rn[i])
+    s1 = scl2[pg[0, 1], rw[0, 1]]
+    v1 = decode_e4m3(lat2[pg[0, 1], rw[0, 1]]).reshape(4, 128)
+    assert s1[0] == 1.0 and v1[0, 5] == 288.0 and np.count_nonzero(v1[0]) == 1
+    assert s1[1] == 2.0 ** -7 and v1[1, 2] == -448.0
 
 
 def test_write_skips_tokens_without_a_slot():
