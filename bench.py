@@ -412,11 +412,11 @@ def measure_decode(w, args, label=None, plan_kw=None):
         "kv_bytes": ab["kv"], "kv_GB_per_s": round(kv_gbs, 2),
         "merge_us": round(float(np.mean(mrg_us)), 2),
         "roofline": roof,
-        "plan": {"kind": plan_kw.get("plan", "wave"), "chunk_tiles": info.chunk_tiles, "work_items": info.num_real,
+        "plan": {"kind": decs[0].plan, "imbalance": decs[0].imbalance and round(decs[0].imbalance, 3),
+                 "chunk_tiles": info.chunk_tiles, "work_items": info.num_real,
                  "slots": info.slots, "max_n_splits": info.max_n_splits, "wg_per_cu": decs[0].wg_per_cu,
                  "max_splits": w.max_splits, "bins": info.num_bins},
         "pools": pools, "kv_tokens": int(lens.sum()),
-        "merge": "separate launch" if not decs[0].fused_merge else "in decode kernel",
     }
     del graphs, decs, batches
     torch.cuda.empty_cache()
@@ -437,7 +437,7 @@ def decode_line(w, rec, base_q_len, probe, cpu, K, W, as_profiled):
            "d": w.d_qk, "page_size": w.page_size, "causal": w.causal, "kv_format": w.kv_format,
            "q_format": w.q_format, "kv_layout": w.kv_layout, "contiguous_pages": w.contiguous_pages,
            "kv_tokens": rec["kv_tokens"], "kv_bytes": rec["kv_bytes"], "max_splits": w.max_splits,
-           "pools": rec["pools"], "merge": rec["merge"], "plan": rec["plan"]}
+           "pools": rec["pools"], "plan": rec["plan"]}
     return {
         "metric": "achieved HBM GB/s (KV bytes / decode-step time), us per decode step",
         "value": rec["kv_GB_per_s"], "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
@@ -712,15 +712,14 @@ def main():
     ap.add_argument("--page-size", type=int, default=None, help="override the workload's page size")
     ap.add_argument("--contiguous-pages", action="store_true", help="hand out pages in order instead of shuffled")
     ap.add_argument("--seq-len", type=int, default=None, help="give every sequence this length")
-    ap.add_argument("--plan", default="wave", choices=["wave", "even", "balanced", "queued"],
-                    help="wave: one work item per workgroup (occupancy-pinned split plan); even: the same rule with "
+    ap.add_argument("--plan", default="auto", choices=["auto", "wave", "even", "balanced", "queued"],
+                    help="auto: wave, or balanced when pkv_plan_pick finds the wave plan's items imbalanced; "
+                         "wave: one work item per workgroup (occupancy-pinned split plan); even: the same rule with "
                          "equal 32-key-block pieces per sequence; balanced: contiguous "
                          "equal shares of all keys, one per workgroup; queued: persistent workgroups, packed "
                          "static bins then a shared queue")
     ap.add_argument("--dyn-percent", type=int, default=10, help="queued plan: share of the work left to the queue")
     ap.add_argument("--pieces-per-bin", type=int, default=3, help="queued plan: pieces a bin's share is cut into")
-    ap.add_argument("--fused-merge", action="store_true",
-                    help="merge split sequences inside the decode kernel (last split merges) instead of a second launch")
     ap.add_argument("--producers", action="store_true",
                     help="only time the query quantisation and KV-cache write kernels (a separate JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -785,8 +784,8 @@ def run(args, pool):
     w = workload(args.config, **over)
     # counter summaries are taken on the workloads as defined (query length and mode aside)
     as_profiled = (set(over) <= {"q_len", "causal"} and not args.pools and args.wg_per_cu is None
-                   and args.plan == "wave" and not args.fused_merge)
-    plan_kw = {"wg_per_cu": args.wg_per_cu, "fused_merge": args.fused_merge, "plan": args.plan}
+                   and args.plan == "auto")
+    plan_kw = {"wg_per_cu": args.wg_per_cu, "plan": args.plan}
     if args.plan == "queued":
         plan_kw.update(dyn_percent=args.dyn_percent, pieces_per_bin=args.pieces_per_bin)
     probe = None if args.no_probe else stream_probe(args)

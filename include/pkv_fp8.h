@@ -226,6 +226,29 @@ pkv_status pkv_plan_queued(const int32_t* seq_lens, int32_t num_seqs, int32_t h_
                            int32_t dyn_percent, int32_t* work_out, int32_t work_cap, int32_t* n_splits_out,
                            int32_t* bin_offsets_out, int32_t bins_cap, pkv_plan_info* info);
 
+/*
+ * Plan choice ("MiniMax MSA fmha_sm100/cute README", Paged FP8 Decode: the
+ * schedule balances the load when the kv-length distribution is imbalanced,
+ * max / avg >= 1.5). The lengths compared are those of the one-wave plan's
+ * work items (`work`, `num_work` as pkv_plan_split_kv wrote them, padding
+ * entries skipped), in 32-key blocks of existing keys, max(1, ceil((min(end *
+ * 128, L) - begin * 128) / 32)): imbalance = longest / mean. The plan is
+ * PKV_PLAN_BALANCED (pkv_plan_balanced) when the imbalance reaches the
+ * trigger of the decode form: 1.12 for the latent cache with rows >= 64 (its
+ * multi-token form, measured on this part), 1.5 otherwise; always
+ * PKV_PLAN_WAVE for the fp4, fp6 and NVFP4 caches (one-item form only).
+ *
+ * seq_lens   host int32[num_seqs]
+ * work       host int32[num_work][4] (seq, tile_begin, tile_end, split_slot)
+ * kv_format  PKV_KV_*; rows = q_len * h_q / h_k (packed query rows)
+ * plan_out   PKV_PLAN_WAVE or PKV_PLAN_BALANCED; imbalance_out may be NULL
+ * Errors: INVALID_ARG for NULL pointers, num_seqs < 1, num_work < 0, rows < 1.
+ */
+#define PKV_PLAN_WAVE 0
+#define PKV_PLAN_BALANCED 1
+pkv_status pkv_plan_pick(const int32_t* seq_lens, int32_t num_seqs, const int32_t* work, int32_t num_work,
+                         int32_t kv_format, int32_t rows, int32_t* plan_out, float* imbalance_out);
+
 /* ------------------------------------------------------------------------ */
 /* Decode launch arguments                                                   */
 /* ------------------------------------------------------------------------ */
@@ -328,15 +351,6 @@ typedef struct pkv_decode_args {
   int32_t max_splits;
   void* workspace;
   size_t workspace_bytes;
-  /* Optional, device int32[num_seqs * h_k * n_q_tiles] (e4m3, fp4 or fp6 K/V
-   * cache; ignored for the latent cache): when non-NULL the decode merges split
-   * sequences itself (the last split of each (sequence,
-   * kv head, q-row tile) to finish combines the partials, same rule and
-   * order as pkv_merge_splits) and pkv_merge_splits does nothing. The
-   * counters must be zero before the first call; every completed call
-   * leaves them zero, so no per-call clearing is needed. NULL: partials are
-   * left for pkv_merge_splits. Calls that overlap on one counter array race. */
-  int32_t* merge_counters;
   /* Optional, device int32[num_bins + 1] from pkv_plan_balanced: workgroup i
    * streams work items [bin_offsets[i], bin_offsets[i+1]) in order, the grid
    * has num_bins workgroups per (kv-head group, q-row tile), and `work` holds
@@ -421,8 +435,7 @@ pkv_status pkv_paged_decode_attn(const pkv_decode_args* a, void* stream);
  * m_j = -inf), O = o_scale * sum_j w_j O_j / sum_j w_j l_j (0 if the sum is
  * 0), LSE = m* + ln sum_j w_j l_j, over j < n_splits[b] in index order.
  * Sequences with n_splits <= 1 are left as the decode wrote them. A no-op
- * (nothing launched) when max_splits == 1 or when merge_counters is set (the
- * decode merged already). Same arguments as the decode.
+ * (nothing launched) when max_splits == 1. Same arguments as the decode.
  */
 pkv_status pkv_merge_splits(const pkv_decode_args* a, void* stream);
 
@@ -623,8 +636,8 @@ size_t pkv_sparse_args_size(void);
  * Errors, before any launch: those of pkv_paged_decode_attn;
  * PKV_ERR_WORKSPACE when pkv_workspace_bytes(num_seqs, h_k, q_len * h_q / h_k,
  * d_v, max_splits) exceeds PKV_NOALLOC_WORKSPACE_BYTES (max_splits == 1 needs
- * none); PKV_ERR_UNSUPPORTED with merge_counters or queue set (the in-kernel
- * merge and the queued plan keep counters of their own).
+ * none); PKV_ERR_UNSUPPORTED with queue set (the queued plan keeps counters
+ * of its own).
  */
 pkv_status pkv_paged_decode_noalloc(const pkv_decode_args* a, void* stream);
 

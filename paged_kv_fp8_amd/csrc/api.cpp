@@ -89,8 +89,6 @@ pkv_status check_pointers(const pkv_decode_args* a, bool for_merge) {
                   a->max_splits);
     if (!aligned(a->workspace, 16)) return fail(PKV_ERR_INVALID_ARG, "workspace must be 16-B aligned");
   }
-  if (a->merge_counters && !aligned(a->merge_counters, 4))
-    return fail(PKV_ERR_INVALID_ARG, "merge_counters must be 4-B aligned");
   if (for_merge) return PKV_OK;
   if (!a->q || !a->k || !a->block_table || !a->work)
     return fail(PKV_ERR_INVALID_ARG, "q, k, block_table and work must be non-NULL");
@@ -231,8 +229,7 @@ extern "C" pkv_status pkv_merge_splits(const pkv_decode_args* a, void* stream) {
   pkv_status st = check_shapes(a);
   if (st != PKV_OK) return st;
   if ((st = check_pointers(a, true)) != PKV_OK) return st;
-  // the e4m3-cache decode merges in place when given counters
-  if (a->max_splits == 1 || (a->merge_counters && a->kv_format != PKV_KV_MLA)) return PKV_OK;
+  if (a->max_splits == 1) return PKV_OK;
   return hip_status(merge_launch(*a, static_cast<hipStream_t>(stream)), "merge launch");
 }
 
@@ -269,8 +266,7 @@ pkv_status scratch_on_current_device(void** out) {
 extern "C" pkv_status pkv_paged_decode_noalloc(const pkv_decode_args* a, void* stream) {
   pkv_status st = check_shapes(a);
   if (st != PKV_OK) return st;
-  if (a->merge_counters || a->queue)
-    return fail(PKV_ERR_UNSUPPORTED, "no-allocation decode: merge counters and the queued plan are not taken");
+  if (a->queue) return fail(PKV_ERR_UNSUPPORTED, "no-allocation decode: the queued plan is not taken");
   const size_t need = a->max_splits > 1 ? pkv_workspace_bytes(a->num_seqs, a->h_k, a->q_len * (a->h_q / a->h_k),
                                                                a->d_v, a->max_splits)
                                         : 0;

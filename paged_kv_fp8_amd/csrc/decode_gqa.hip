@@ -86,7 +86,6 @@ struct GqaParams {
   const int32_t* n_splits;
   float* ws_o;   // [max_splits][num_seqs][h_k][rows][128]
   float2* ws_ml; // [max_splits][num_seqs][h_k][rows]
-  int32_t* counters;  // [num_seqs][h_k][q-row tiles] or null: merge in a separate launch
   const int32_t* bin_offsets;  // [bins + 1] or null: one work item per workgroup
   int32_t* queue;              // [2][h_k * q tiles] or null: no shared queue (persistent form)
   float scale_log2e, scale, o_scale;
@@ -134,72 +133,6 @@ __device__ __forceinline__ float pair32(float x, bool take_max) {
 }
 __device__ __forceinline__ float wave_max16(float x) { return pair32(pair16(x, true), true); }
 __device__ __forceinline__ float wave_sum16(float x) { return pair32(pair16(x, false), false); }
-
-// 8-byte stores / loads that are coherent across the XCDs of the device
-// (agent-scope relaxed atomics: they go past the XCD-local L2).
-__device__ __forceinline__ void store_coherent(float* dst, float a, float b) {
-  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(dst), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float2 load_coherent(const float* src) {
-  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(src), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return float2{__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32))};
-}
-
-// Combine the partials of splits 0 .. ns-1 for this wave's rows, with the
-// rule and the arithmetic order of the separate merge kernel: m* = max m_j,
-// w_j = exp(m_j - m*) (0 for m_j = -inf), O = o_scale * sum w_j O_j / sum
-// w_j l_j, LSE = m* + ln sum w_j l_j. Lane (r16, g4) owns row r16 of each
-// 16-row block and d_v values 32*g4 .. 32*g4+31.
-template <int NB>
-__device__ __forceinline__ void merge_rows(const GqaParams& p, int b, int g, int row0, int r16, int g4, int ns,
-                                           const int* qtok, const int* qhead) {
-  const int64_t split_stride = (int64_t)p.num_seqs * p.h_k * p.rows;
-  for (int nb = 0; nb < NB; ++nb) {
-    const int n = row0 + 16 * nb + r16;
-    if (n >= p.rows) continue;
-    const int64_t row = ((int64_t)b * p.h_k + g) * p.rows + n;
-    // the separate merge's arithmetic, in the same order (rounds of 16
-    // splits, each weighted by the max so far, earlier sums rescaled when a
-    // round raises it), so that both give the same bits
-    float m_star = -INFINITY;
-    float acc[32];
-    for (int e = 0; e < 32; ++e) acc[e] = 0.f;
-    float den = 0.f;
-    for (int j0 = 0; j0 < ns; j0 += 16) {
-      const int j1 = min(j0 + 16, ns);
-      float m_new = m_star;
-      for (int j = j0; j < j1; ++j)
-        m_new = fmaxf(m_new, load_coherent(reinterpret_cast<const float*>(p.ws_ml + j * split_stride + row)).x);
-      if (m_new == -INFINITY) continue;  // no split of this row saw a key yet
-      if (m_new != m_star) {
-        const float sc = m_star == -INFINITY ? 0.f : __expf(m_star - m_new);
-        for (int e = 0; e < 32; ++e) acc[e] *= sc;
-        den *= sc;
-        m_star = m_new;
-      }
-      for (int j = j0; j < j1; ++j) {
-        const float2 ml = load_coherent(reinterpret_cast<const float*>(p.ws_ml + j * split_stride + row));
-        const float wgt = ml.x == -INFINITY ? 0.f : __expf(ml.x - m_star);
-        const float* src = p.ws_o + (j * split_stride + row) * kD + 32 * g4;
-        den += wgt * ml.y;
-        for (int e = 0; e < 32; e += 2) {
-          const float2 v = load_coherent(src + e);
-          acc[e] += wgt * v.x;
-          acc[e + 1] += wgt * v.y;
-        }
-      }
-    }
-    const float inv = den > 0.f ? p.o_scale / den : 0.f;
-    uint8_t* orow = p.o + (int64_t)qtok[nb] * p.o_tok + (int64_t)qhead[nb] * p.o_head;
-    for (int e0 = 0; e0 < 32; e0 += 8) {
-      bf16x8 out;
-      for (int e = 0; e < 8; ++e) out[e] = (__bf16)(acc[e0 + e] * inv);
-      *reinterpret_cast<bf16x8*>(orow + 2 * (32 * g4 + e0)) = out;
-    }
-    if (g4 == 0) p.lse[row] = den > 0.f ? m_star + logf(den) : -INFINITY;
-  }
-}
 
 // Raw bytes of one 32-key block as this lane loads them.
 struct RawBlock {
@@ -794,11 +727,10 @@ __device__ __forceinline__ void process_block_fp6(const RawBlock6& cur, int kb, 
 
 // Epilogue of one work item for kv head g of sequence b: a sequence with one
 // split writes O and LSE itself; otherwise the rows go to split slot `slot`
-// of the workspace, and with merge counters the split that finishes last for
-// this (sequence, head, q tile) combines all of them.
+// of the workspace for the merge kernel.
 template <bool FP8Q, int NB>
 __device__ __forceinline__ void finish_item(const GqaParams& p, const RowState<NB>& st, const RowMap<NB>& rm, int b,
-                                            int g, int tile, int row0, int r16, int g4, int ns, int slot, float cs, float vdv) {
+                                            int g, int row0, int r16, int g4, int ns, int slot, float cs, float vdv) {
   const bool direct = ns <= 1;
   const float p_scale = FP8Q ? kP8Scale : 1.0f;
   int qtok[NB], qhead[NB];
@@ -825,42 +757,13 @@ __device__ __forceinline__ void finish_item(const GqaParams& p, const RowState<N
       const int64_t prow = (int64_t)slot * p.num_seqs * p.h_k * p.rows + stat_row;
       const float ps = vdv / p_scale;
       float* dst = p.ws_o + prow * kD + 32 * g4;
-      if (p.counters) {
-        // read back by whichever split of this row finishes last, maybe on
-        // another XCD: agent-coherent stores (past the XCD's own L2)
-        for (int i = 0; i < 4; ++i)
-          for (int mt = 0; mt < 8; mt += 2)
-            store_coherent(dst + 8 * i + mt, st.oacc[nb][mt][i] * ps, st.oacc[nb][mt + 1][i] * ps);
-        if (g4 == 0) store_coherent(reinterpret_cast<float*>(p.ws_ml + prow), m_nat, l);
-      } else {
-        for (int i = 0; i < 4; ++i) {
-          f32x4 lo4 = {st.oacc[nb][0][i], st.oacc[nb][1][i], st.oacc[nb][2][i], st.oacc[nb][3][i]};
-          f32x4 hi4 = {st.oacc[nb][4][i], st.oacc[nb][5][i], st.oacc[nb][6][i], st.oacc[nb][7][i]};
-          *reinterpret_cast<f32x4*>(dst + 8 * i) = lo4 * ps;
-          *reinterpret_cast<f32x4*>(dst + 8 * i + 4) = hi4 * ps;
-        }
-        if (g4 == 0) p.ws_ml[prow] = float2{m_nat, l};
+      for (int i = 0; i < 4; ++i) {
+        f32x4 lo4 = {st.oacc[nb][0][i], st.oacc[nb][1][i], st.oacc[nb][2][i], st.oacc[nb][3][i]};
+        f32x4 hi4 = {st.oacc[nb][4][i], st.oacc[nb][5][i], st.oacc[nb][6][i], st.oacc[nb][7][i]};
+        *reinterpret_cast<f32x4*>(dst + 8 * i) = lo4 * ps;
+        *reinterpret_cast<f32x4*>(dst + 8 * i + 4) = hi4 * ps;
       }
-    }
-  }
-
-  // ---- in-kernel merge: the last split of this (sequence, head, q tile) ------
-  if (!direct && p.counters) {
-    // The partials above were written with agent-coherent stores; wait until
-    // they have all completed, then count this split. The split that counts
-    // last reads every partial back with agent-coherent loads. Only the
-    // partials and the counter are shared, so no cache-wide write-back or
-    // invalidate is needed.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    int32_t* ctr = p.counters + ((int64_t)b * p.h_k + g) * p.q_tiles + tile;
-    int last = 0;
-    if ((threadIdx.x & 63) == 0)
-      last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == min(ns, p.max_splits) - 1;
-    last = __builtin_amdgcn_readfirstlane(last);
-    if (last) {
-      asm volatile("" ::: "memory");
-      merge_rows<NB>(p, b, g, row0, r16, g4, min(ns, p.max_splits), qtok, qhead);
-      if ((threadIdx.x & 63) == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (g4 == 0) p.ws_ml[prow] = float2{m_nat, l};
     }
   }
 }
@@ -1045,7 +948,7 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
     }
     round_base += rounds;
   }
-  finish_item<FP8Q, NB>(p, st, rm, b, g, tile, row0, r16, g4, ns, slot, cs, vdv);
+  finish_item<FP8Q, NB>(p, st, rm, b, g, row0, r16, g4, ns, slot, cs, vdv);
 }
 
 // V rows of keys past `vlast` (loaded through planned block-table entries
@@ -1232,7 +1135,7 @@ __device__ __forceinline__ void gqa_decode_persistent(const GqaParams& p, int la
         if (HW == 8) keep_pace(progress, wave, round_base + r, lane);
       }
       round_base += R;
-      if (c_ok) finish_item<FP8Q, NB>(p, st, rm, C.b, g, (int)blockIdx.z, row0, r16, g4, C.ns, C.slot, cs, C.vd);
+      if (c_ok) finish_item<FP8Q, NB>(p, st, rm, C.b, g, row0, r16, g4, C.ns, C.slot, cs, C.vd);
       if (!n_valid) break;
       // ---- N becomes current: its first S - 1 blocks are in the ring and the
       // pairs of its next fetches in pv
@@ -1347,7 +1250,7 @@ __device__ __forceinline__ void gqa_decode_stream(const GqaParams& p, int lane, 
       prefetch_q(i + 1);
     };
     auto end_item = [&]() {
-      if (c_ok) finish_item<FP8Q, NB>(p, st, rm, c_b, g, (int)blockIdx.z, row0, r16, g4, c_ns, c_slot, cs, c_vd);
+      if (c_ok) finish_item<FP8Q, NB>(p, st, rm, c_b, g, row0, r16, g4, c_ns, c_slot, cs, c_vd);
     };
     auto advance_to = [&](int i) {  // finish items before i (empty ones too), begin item i
       while (cur < i) {
@@ -1688,7 +1591,6 @@ hipError_t gqa_launch(const pkv_decode_args& a, const GqaVariant& v, hipStream_t
   const int64_t rows_all = ws_rows(a);
   p.ws_o = static_cast<float*>(a.workspace);
   p.ws_ml = a.workspace ? reinterpret_cast<float2*>(p.ws_o + (int64_t)a.max_splits * rows_all * kD) : nullptr;
-  p.counters = a.max_splits > 1 ? a.merge_counters : nullptr;
   p.bin_offsets = a.bin_offsets;
   p.queue = a.queue;
   p.ks = a.k_group_scale;

@@ -230,7 +230,11 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
 
   const int4 wk = p.work[item];
   const int b = wk.x;
-  if (wk.z <= wk.y || b < 0 || b >= p.num_seqs) return;  // the whole workgroup returns
+  // tile ranges (one-wave plan): an empty range is padding; key ranges
+  // (balanced plan): an empty range is the item of an empty sequence, whose
+  // rows still get O = 0, LSE = -inf
+  const bool empty = p.bin_offsets ? wk.z < wk.y : wk.z <= wk.y;
+  if (empty || b < 0 || b >= p.num_seqs) return;  // the whole workgroup returns
   const int ns = p.n_splits[b];
   const bool direct = ns <= 1;
   const int slot = wk.w;
@@ -656,7 +660,10 @@ __device__ __forceinline__ void mla_pair_item(const MlaParams& p, int item, int 
 
   const int4 wk = p.work[item];
   const int b = wk.x;
-  if (wk.z <= wk.y || b < 0 || b >= p.num_seqs) return;  // the whole workgroup returns
+  // an empty key range (balanced plan) is an empty sequence's item: its rows
+  // still get their output; an empty tile range is padding
+  const bool empty = p.bin_offsets ? wk.z < wk.y : wk.z <= wk.y;
+  if (empty || b < 0 || b >= p.num_seqs) return;  // the whole workgroup returns
   const int k_begin = p.bin_offsets ? wk.y : wk.y * kTileKeys;
   const int k_plan = p.bin_offsets ? wk.z : wk.z * kTileKeys;  // planned end: lengths of the plan are upper bounds
   const int32_t* bt = p.block_table + (int64_t)b * p.bt_row;
@@ -669,7 +676,7 @@ __device__ __forceinline__ void mla_pair_item(const MlaParams& p, int item, int 
   constexpr int kPageAhead = kPairStages - 1;
   int pv[kPairStages];
   for (int u = 0; u < kPageAhead; ++u)
-    pv[u] = bt[min(min(k_begin + kBlockKeys * u, k_plan - 1) >> p.page_shift, p.max_blocks - 1)];
+    pv[u] = bt[min(min(k_begin + kBlockKeys * u, max(k_plan - 1, 0)) >> p.page_shift, p.max_blocks - 1)];
 
   // rows of this wave's group; a group past the last row still runs the loop
   // (on a zero query) and meets every barrier

@@ -362,3 +362,37 @@ extern "C" pkv_status pkv_plan_queued(const int32_t* seq_lens, int32_t num_seqs,
   }
   return PKV_OK;
 }
+
+// Plan choice. "MiniMax MSA fmha_sm100/cute README", Paged FP8 Decode: the
+// schedule switches to load balancing when the kv-length distribution is
+// imbalanced, max / avg >= 1.5. Reading: the lengths are those the one-wave
+// plan hands to its workgroups (its work items, which already cut long
+// sequences into chunks), in 32-key blocks of keys that exist.
+extern "C" pkv_status pkv_plan_pick(const int32_t* seq_lens, int32_t num_seqs, const int32_t* work, int32_t num_work,
+                                    int32_t kv_format, int32_t rows, int32_t* plan_out, float* imbalance_out) {
+  using pkv::fail;
+  if (!seq_lens || !work || !plan_out) return fail(PKV_ERR_INVALID_ARG, "plan pick: NULL argument");
+  if (num_seqs < 1 || num_work < 0 || rows < 1) return fail(PKV_ERR_INVALID_ARG, "plan pick: bad sizes");
+  int64_t total = 0, longest = 0, items = 0;
+  for (int32_t i = 0; i < num_work; ++i) {
+    const int32_t* w = work + 4 * i;
+    if (w[0] < 0 || w[0] >= num_seqs || w[2] <= w[1]) continue;  // padding entries
+    const int64_t L = std::max<int32_t>(seq_lens[w[0]], 0);
+    const int64_t keys = std::min<int64_t>(w[2] * kTileKeys, L) - w[1] * kTileKeys;
+    const int64_t blocks = std::max<int64_t>(1, ceil_div(std::max<int64_t>(keys, 0), kBalanceBlockKeys));
+    total += blocks;
+    longest = std::max(longest, blocks);
+    ++items;
+  }
+  const float ratio = items ? (float)((double)longest * items / (double)total) : 1.0f;
+  // the page's trigger, except where this library's balanced form measured
+  // otherwise: the latent multi-token form (64 rows and more) restarts at an
+  // item boundary at a cost of a few blocks, and gains from 1.12 on; the
+  // narrow formats run the one-item form only
+  const bool narrow = kv_format == PKV_KV_E2M1 || kv_format == PKV_KV_E2M3 || kv_format == PKV_KV_E3M2 ||
+                      kv_format == PKV_KV_NVFP4;
+  const float trigger = (kv_format == PKV_KV_MLA && rows >= 64) ? 1.12f : 1.5f;
+  *plan_out = !narrow && ratio >= trigger ? PKV_PLAN_BALANCED : PKV_PLAN_WAVE;
+  if (imbalance_out) *imbalance_out = ratio;
+  return PKV_OK;
+}

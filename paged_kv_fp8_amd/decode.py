@@ -50,12 +50,16 @@ class PagedDecode:
     lse          (num_seqs, h_k, q_len*h_r) fp32 contiguous output
     plan_seq_lens host lengths the plan is made for (default: seq_lens);
                  the device seq_lens may be shorter at run time.
+    plan         "auto" (default): the one-wave plan, or the balanced plan
+                 when pkv_plan_pick finds the one-wave plan's items
+                 imbalanced (force_splits / pad_to / min_chunk_tiles keep
+                 the one-wave plan); "wave", "even", "balanced", "queued".
     """
 
     def __init__(self, *, q, block_table, seq_lens, o, lse, q_len, softmax_scale, k_cache=None, v_cache=None,
                  q_descale=None, k_descale=None, v_descale=None, latent=None, rope=None, blk_scale=None,
                  num_pages=None, causal=True, o_scale=1.0, max_splits=16, force_splits=0, min_chunk_tiles=1,
-                 pad_to=0, wg_per_cu=None, plan_seq_lens=None, fused_merge=False, plan="wave", pieces_per_bin=3,
+                 pad_to=0, wg_per_cu=None, plan_seq_lens=None, plan="auto", pieces_per_bin=3,
                  dyn_percent=10, plan_cu_count=None, kv_format="e4m3", k_group_scale=None, v_group_scale=None):
         mla = latent is not None
         a = native.DecodeArgs()
@@ -112,6 +116,13 @@ class PagedDecode:
         dev = q.device
         self.bin_offsets = None
         self.queue = None
+        self.imbalance = None
+        if plan == "auto":  # the one-wave plan, or the balanced plan when its items are imbalanced
+            work, n_splits, info = native.plan_split_kv(lens, h_k, n_q_tiles, cu, self.wg_per_cu, max_splits,
+                                                        force_splits, min_chunk_tiles, pad_to)
+            pick, self.imbalance = native.plan_pick(lens, work, a.kv_format, q_len * (h_q // h_k))
+            wave_knobs = force_splits or pad_to or min_chunk_tiles != 1
+            plan = "balanced" if pick == native.PKV_PLAN_BALANCED and not wave_knobs else "wave"
         if plan == "balanced":  # contiguous equal shares, one per resident workgroup
             work, n_splits, offs, info = native.plan_balanced(lens, h_k, n_q_tiles, cu, self.wg_per_cu, max_splits)
             self.bin_offsets = torch.from_numpy(offs).to(dev)
@@ -132,8 +143,9 @@ class PagedDecode:
             work, n_splits, info = native.plan_even(lens, h_k, n_q_tiles, cu, self.wg_per_cu, max_splits)
             a.work_in_keys = 1
         elif plan == "wave":  # the occupancy-pinned one-wave plan
-            work, n_splits, info = native.plan_split_kv(lens, h_k, n_q_tiles, cu, self.wg_per_cu, max_splits,
-                                                        force_splits, min_chunk_tiles, pad_to)
+            if self.imbalance is None:
+                work, n_splits, info = native.plan_split_kv(lens, h_k, n_q_tiles, cu, self.wg_per_cu, max_splits,
+                                                            force_splits, min_chunk_tiles, pad_to)
         else:
             raise ValueError(f"unknown plan {plan!r}")
         self.work = torch.from_numpy(work).to(dev)
@@ -143,12 +155,6 @@ class PagedDecode:
         rows = q_len * (h_q // h_k)
         ws = native.workspace_bytes(num_seqs, h_k, rows, d_v, max_splits) if max_splits > 1 else 0
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)  # never initialised
-        # in-kernel merge (e4m3 cache): counters zeroed once here; every call leaves them zero
-        self.fused_merge = bool(fused_merge) and not mla and max_splits > 1
-        self.merge_counters = None
-        if self.fused_merge:
-            self.merge_counters = torch.zeros(num_seqs * h_k * n_q_tiles, dtype=torch.int32, device=dev)
-            a.merge_counters = _ptr(self.merge_counters)
         a.work, a.num_work = _ptr(self.work), int(info.num_work)
         a.n_splits = _ptr(self.n_splits)
         a.workspace, a.workspace_bytes = _ptr(self.workspace), self.workspace.numel()
@@ -173,14 +179,14 @@ class PagedDecode:
         (default: torch's current stream). No allocation, no sync."""
         s = (stream or torch.cuda.current_stream()).cuda_stream
         native.paged_decode_attn(self.args, s)
-        if self.has_splits and not self.fused_merge:
+        if self.has_splits:
             native.merge_splits(self.args, s)
 
     def run_decode_only(self, stream=None):
         native.paged_decode_attn(self.args, (stream or torch.cuda.current_stream()).cuda_stream)
 
     def run_merge_only(self, stream=None):
-        if self.has_splits and not self.fused_merge:
+        if self.has_splits:
             native.merge_splits(self.args, (stream or torch.cuda.current_stream()).cuda_stream)
 
 

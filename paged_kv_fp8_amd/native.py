@@ -24,7 +24,7 @@ EXPORTS = ("pkv_status_string", "pkv_last_error", "pkv_version", "pkv_decode_arg
            "pkv_plan_even", "pkv_plan_balanced", "pkv_plan_queued", "pkv_workspace_bytes", "pkv_decode_slots", "pkv_paged_decode_attn",
            "pkv_merge_splits", "pkv_quantize_q", "pkv_quant_q_args_size", "pkv_write_kv", "pkv_kv_write_args_size",
            "pkv_decode_kernel_name", "pkv_sparse_workspace_bytes", "pkv_sparse_decode", "pkv_sparse_tiles", "pkv_sparse_merge",
-           "pkv_sparse_args_size", "pkv_paged_decode_noalloc", "pkv_stream_read_probe")
+           "pkv_sparse_args_size", "pkv_paged_decode_noalloc", "pkv_stream_read_probe", "pkv_plan_pick")
 
 
 class PkvError(RuntimeError):
@@ -64,7 +64,6 @@ class DecodeArgs(ctypes.Structure):
         ("work", _vp), ("num_work", _i32),
         ("n_splits", _vp), ("max_splits", _i32),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
-        ("merge_counters", _vp),
         ("bin_offsets", _vp), ("num_bins", _i32),
         ("queue", _vp),
         ("k_group_scale", _vp), ("kgs_page_stride", _i64), ("kgs_row_stride", _i64), ("kgs_head_stride", _i64),
@@ -150,6 +149,8 @@ def _load():
     lib.pkv_plan_queued.restype = _i32
     lib.pkv_plan_queued.argtypes = [P(_i32), _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, P(_i32), _i32, P(_i32),
                                     P(_i32), _i32, P(PlanInfo)]
+    lib.pkv_plan_pick.restype = _i32
+    lib.pkv_plan_pick.argtypes = [P(_i32), _i32, P(_i32), _i32, _i32, _i32, P(_i32), P(_f32)]
     lib.pkv_workspace_bytes.restype = ctypes.c_size_t
     lib.pkv_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
     lib.pkv_decode_kernel_name.restype = ctypes.c_char_p
@@ -223,6 +224,20 @@ def plan_split_kv(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16
                                ns.ctypes.data_as(P), ctypes.byref(info))
     _check(st, "pkv_plan_split_kv")
     return work[:info.num_work].copy(), ns[:nseq].copy(), info
+
+
+PKV_PLAN_WAVE, PKV_PLAN_BALANCED = 0, 1
+
+
+def plan_pick(seq_lens, work, kv_format, rows):
+    """pkv_plan_pick: (PKV_PLAN_WAVE or PKV_PLAN_BALANCED, imbalance) for a one-wave plan's work list."""
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    wk = np.ascontiguousarray(work, dtype=np.int32).reshape(-1, 4)
+    plan, ratio = _i32(0), ctypes.c_float(0.0)
+    P = ctypes.POINTER(_i32)
+    _check(lib.pkv_plan_pick(lens.ctypes.data_as(P), len(lens), wk.ctypes.data_as(P), wk.shape[0], kv_format, rows,
+                             ctypes.byref(plan), ctypes.byref(ratio)), "pkv_plan_pick")
+    return plan.value, ratio.value
 
 
 def plan_even(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16):

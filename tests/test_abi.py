@@ -184,9 +184,8 @@ def test_noalloc_decode_limits(native):
     assert need > native.PKV_NOALLOC_WORKSPACE_BYTES
     assert native.lib.pkv_paged_decode_noalloc(ctypes.byref(big), None) == native.PKV_ERR_WORKSPACE
     assert "workspace" in native.last_error()
-    for over in (dict(merge_counters=1 << 43), dict(queue=1 << 43, bin_offsets=1 << 44, num_bins=4)):
-        a = _valid_args(native, max_splits=4, **over)
-        assert native.lib.pkv_paged_decode_noalloc(ctypes.byref(a), None) == native.PKV_ERR_UNSUPPORTED
+    a = _valid_args(native, max_splits=4, queue=1 << 43, bin_offsets=1 << 44, num_bins=4)
+    assert native.lib.pkv_paged_decode_noalloc(ctypes.byref(a), None) == native.PKV_ERR_UNSUPPORTED
     assert native.lib.pkv_paged_decode_noalloc(None, None) == native.PKV_ERR_INVALID_ARG
 
 
@@ -444,3 +443,33 @@ def test_stream_read_probe_rejects_invalid_arguments_without_touching_the_gpu(na
     st = native.lib.pkv_stream_read_probe(src, nbytes, wg, unroll, sink, None)
     assert st == native.PKV_ERR_INVALID_ARG, native.last_error()
     assert native.last_error()
+
+
+def test_plan_pick_by_hand(native):
+    # items in 32-key blocks of existing keys: seq 0 tiles 0..2 of L = 256 -> 8 blocks;
+    # seq 1 tile 0 of L = 100 -> ceil(100 / 32) = 4; a padding entry (-1, 0, 0, 0) is skipped
+    lens = [256, 100]
+    work = [[0, 0, 2, 0], [1, 0, 1, 0], [-1, 0, 0, 0]]
+    plan, ratio = native.plan_pick(lens, work, native.PKV_KV_E4M3, 4)
+    assert ratio == pytest.approx(8 / 6) and plan == native.PKV_PLAN_WAVE  # 1.33 < 1.5
+    plan, _ = native.plan_pick(lens, work, native.PKV_KV_MLA, 64)
+    assert plan == native.PKV_PLAN_BALANCED  # latent multi-token form: 1.33 >= 1.12
+    plan, _ = native.plan_pick(lens, work, native.PKV_KV_MLA, 32)
+    assert plan == native.PKV_PLAN_WAVE  # latent pair form: the page's 1.5
+    # seq 0 alone against three one-block items: 8 / ((8 + 3) / 4) = 2.9
+    lens = [256, 10, 1, 0]
+    work = [[0, 0, 2, 0], [1, 0, 1, 0], [2, 0, 1, 0], [3, 0, 1, 0]]
+    plan, ratio = native.plan_pick(lens, work, native.PKV_KV_E4M3, 16)
+    assert ratio == pytest.approx(8 * 4 / 11) and plan == native.PKV_PLAN_BALANCED
+    for fmt in (native.PKV_KV_E2M1, native.PKV_KV_E2M3, native.PKV_KV_E3M2, native.PKV_KV_NVFP4):
+        assert native.plan_pick(lens, work, fmt, 16)[0] == native.PKV_PLAN_WAVE  # one-item form only
+    # a chunk past the runtime length counts its existing keys: tiles 1..2 of L = 200 -> 72 keys, 3 blocks
+    plan, ratio = native.plan_pick([200, 300], [[0, 1, 2, 1], [1, 0, 3, 0]], native.PKV_KV_E4M3, 4)
+    assert ratio == pytest.approx(10 / 6.5)
+    assert native.plan_pick([5], np.zeros((0, 4), np.int32), native.PKV_KV_E4M3, 4)[1] == 1.0
+    P = ctypes.POINTER(ctypes.c_int32)
+    out = ctypes.c_int32()
+    assert native.lib.pkv_plan_pick(None, 1, None, 0, 0, 4, ctypes.byref(out), None) == native.PKV_ERR_INVALID_ARG
+    lens_a = np.array([5], np.int32)
+    assert native.lib.pkv_plan_pick(lens_a.ctypes.data_as(P), 1, lens_a.ctypes.data_as(P), 0, 0, 0,
+                                    ctypes.byref(out), None) == native.PKV_ERR_INVALID_ARG

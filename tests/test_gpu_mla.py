@@ -23,6 +23,8 @@ def run_batch(batch, **kw):
     dec = decode.for_batch(batch, **kw)
     if dec.has_splits:
         nan_fill_(dec.workspace)
+    nan_fill_(dec.o)  # every output row must be written
+    nan_fill_(dec.lse)
     dec.run()
     torch.cuda.synchronize()
     return dec
@@ -68,6 +70,16 @@ def test_latent_edge_lengths(T, force):
     batch = make_batch(w, device="cuda")
     dec = run_batch(batch, force_splits=force)
     compare(batch, dec, what=f"latent edge T={T} force={force}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 8])
+def test_latent_edge_lengths_balanced_plan(T):
+    # key-range items, among them the empty item of the L = 0 sequence (its rows: O = 0, LSE = -inf)
+    w = workload(5, q_len=T, num_seqs=len(EDGE), seq_len_dist=("fixed", EDGE), max_splits=8)
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch, plan="balanced")
+    assert dec.plan == "balanced"
+    compare(batch, dec, what=f"latent edge balanced T={T}")
 
 
 @pytest.mark.parametrize("T", [2, 8])
@@ -188,3 +200,14 @@ def test_latent_staged_other_scales_round(T):
                                      lse_tol=lse_tol, what=f"latent other scales T={T}")
     print(f"T={T}: dS bound {ds:.3e}; max|dO|={err_o:.3e} (bar {o_tol:.3e} max|V|) max|dLSE|={err_l:.3e} "
           f"(bar {lse_tol:.3e})")
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_latent_split_count_at_the_library_cap(T):
+    # one latent sequence of 256 tiles in 256 splits (PKV_MAX_SPLITS), one of 3 tiles in 3
+    w = workload(5, q_len=T, num_seqs=2, seq_len_dist=("fixed", [32768, 300]), max_splits=256)
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch, force_splits=256)
+    assert dec.n_splits.cpu().tolist() == [256, 3]
+    err_o, err_l, _ = compare(batch, dec, what=f"latent 256 splits T={T}")
+    print(f"T={T}: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")

@@ -30,6 +30,8 @@ def run(batch, **kw):
     dec = _decode().for_batch(batch, **kw)
     if dec.has_splits:
         nan_fill_(dec.workspace)
+    nan_fill_(dec.o)  # every output row must be written
+    nan_fill_(dec.lse)
     dec.run()
     torch.cuda.synchronize()
     return dec
@@ -90,7 +92,7 @@ def test_narrow_edge_lengths(q_len, causal, ps, force, fmt):
 
 
 @pytest.mark.parametrize("fmt", list(FORMATS))
-def test_narrow_bitwise_repeats_graph_replay_and_fused_merge(fmt):
+def test_narrow_bitwise_repeats_and_graph_replay(fmt):
     w = workload(FORMATS[fmt], num_seqs=12, seq_len_dist=("mix", 0.25, (6000, 20000), (1024, 4096)))
     batch = make_batch(w, device="cuda")
     dec = run(batch)
@@ -107,13 +109,6 @@ def test_narrow_bitwise_repeats_graph_replay_and_fused_merge(fmt):
         torch.cuda.synchronize()
         assert torch.equal(dec.o.view(torch.int16), ref_o.view(torch.int16)), f"replay {rep}"
         assert torch.equal(dec.lse.view(torch.int32), ref_l.view(torch.int32)), f"replay {rep}"
-    fused = _decode().for_batch(batch, fused_merge=True)
-    for rep in range(2):
-        nan_fill_(fused.workspace[: fused.workspace.numel() // 2])
-        fused.run()
-        torch.cuda.synchronize()
-        assert torch.equal(fused.o.view(torch.int16), ref_o.view(torch.int16)), f"fused {rep}"
-        assert int(fused.merge_counters.abs().sum()) == 0
 
 
 @pytest.mark.parametrize("fmt", list(FORMATS))
