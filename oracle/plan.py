@@ -21,9 +21,11 @@ Errors (ValueError) where the page's asserts fire: pad_to below the number of
 work items, more chunks than max_splits. Also rejected here: an empty batch,
 negative lengths, non-positive sizes (the page never passes them).
 
+The chunk is found by a plain upward scan from lo (the library bisects).
+
 Pinned by tests/test_plan_oracle.py: hand-worked examples, the minimality of
-the chunk against a linear scan, coverage/contiguity of every sequence's
-chunks, the wave bound, the ordering and the padding.
+the chunk (it fits, one tile less does not), coverage/contiguity of every
+sequence's chunks, the wave bound, the ordering and the padding.
 """
 
 import bisect
@@ -54,38 +56,35 @@ def plan_split_kv(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16
     slots = max(1, (cu_count * wg_per_cu) // (h_k * n_q_tiles))
     lo = max(min_chunk_tiles, _ceil_div(t_max, max_splits))
 
-    def n_chunks(chunk):
-        return sum(_ceil_div(t, chunk) for t in tiles)
+    def fits_one_wave(chunk):
+        return sum(_ceil_div(t, chunk) for t in tiles) <= slots
 
     if force_splits > 0:
         chunk = max(lo, _ceil_div(t_max, force_splits))
     elif len(tiles) >= slots or max_splits == 1:
         chunk = t_max
     else:
-        # n_chunks is non-increasing in the chunk size: bisect for the
-        # smallest chunk in [lo, t_max] that fits one wave (t_max always fits
-        # here, since it gives one chunk per sequence and num_seqs < slots).
-        a, z = lo, t_max
-        while a < z:
-            mid = (a + z) // 2
-            if n_chunks(mid) <= slots:
-                z = mid
-            else:
-                a = mid + 1
-        chunk = a
+        # scan upward from lo for the first chunk size that fits; t_max fits
+        # (one chunk per sequence, fewer sequences than slots), and when lo
+        # already exceeds t_max the chunk is lo
+        chunk = next((c for c in range(lo, t_max + 1) if fits_one_wave(c)), lo)
 
-    work, n_splits = [], []
+    items = []  # (seq, first tile, end tile, split slot) in construction order
+    n_splits = []
     for b, t in enumerate(tiles):
-        k = _ceil_div(t, chunk)
-        n_splits.append(k)
-        work.extend((b, j * chunk, min((j + 1) * chunk, t), j) for j in range(k))
-    work.sort(key=lambda w: w[1] - w[2])  # longest first; sort is stable
+        cuts = list(range(0, t, chunk)) + [t]
+        n_splits.append(len(cuts) - 1)
+        for slot, (first, end) in enumerate(zip(cuts[:-1], cuts[1:])):
+            items.append((b, first, end, slot))
     if max(n_splits) > max_splits:
         raise ValueError(f"{max(n_splits)} chunks exceed max_splits={max_splits}")
+    # longest first; equal lengths keep construction order
+    order = sorted(range(len(items)), key=lambda i: (items[i][1] - items[i][2], i))
+    work = [items[i] for i in order]
     if pad_to:
         if pad_to < len(work):
             raise ValueError(f"pad_to {pad_to} < {len(work)} work items")
-        work += [(0, 0, 0, 0)] * (pad_to - len(work))
+        work.extend([(0, 0, 0, 0)] * (pad_to - len(work)))
     return work, n_splits, chunk, slots
 
 

@@ -272,58 +272,81 @@ def _token_slots(lens, bt, ps, device):
     return torch.from_numpy(seg).to(device), torch.from_numpy(slot).to(device)
 
 
+def _seq_head_amax(x, seg, num_seqs):
+    """Largest |x| of each (sequence, kv head) over its tokens and head dims:
+    x (tokens, h_k, d), seg (tokens,) sequence of each token -> (b, h_k)."""
+    out = torch.zeros(num_seqs, x.shape[1], device=x.device)
+    per_token = x.abs().amax(dim=-1)  # (tokens, h_k)
+    return out.scatter_reduce_(0, seg[:, None].expand_as(per_token), per_token, "amax")
+
+
 def _quantise_per_seq_head(x, seg, num_seqs):
     """x (tokens, h_k, d) float32 -> (codes uint8, descale (b, h_k))."""
-    h_k = x.shape[1]
-    amax = torch.zeros(num_seqs, h_k, device=x.device)
-    amax.scatter_reduce_(0, seg[:, None].expand(-1, h_k), x.abs().amax(dim=-1), "amax")
-    desc = amax.clamp(min=1e-6) / E4M3_MAX
+    desc = _seq_head_amax(x, seg, num_seqs).clamp(min=1e-6) / E4M3_MAX
     y = (x / desc[seg][:, :, None]).clamp(-E4M3_MAX, E4M3_MAX)
     return y.to(torch.float8_e4m3fn).view(torch.uint8), desc.contiguous()
+
+
+def _nearest_code(y, mags_t, sign_bit):
+    """Sign-magnitude code of the magnitude nearest |y| (a tie goes to the
+    smaller magnitude), the sign bit set for negative nonzero values. A value
+    lies nearest magnitude i exactly when it passes i of the midpoints between
+    consecutive magnitudes (and a value on a midpoint passes none of it);
+    the midpoints of these dyadic tables are exact in float32."""
+    mids = torch.tensor([(a + b) / 2 for a, b in zip(mags_t[:-1], mags_t[1:])], dtype=torch.float32,
+                        device=y.device)
+    mag = torch.searchsorted(mids, y.abs().contiguous(), right=False)  # midpoints strictly below |y|
+    neg = (y < 0) & (mag > 0)
+    return mag + neg.to(mag.dtype) * sign_bit
+
+
+def _pack_codes(code, bits):
+    """Pack codes (..., n) of 4 or 6 bits into a little-endian bitstream of
+    bytes: code i occupies bits bits*i .. bits*i + bits - 1."""
+    per_word = 8 // math.gcd(8, bits)  # codes per whole number of bytes: 2 (fp4) or 4 (fp6)
+    nbytes = per_word * bits // 8
+    c = code.view(*code.shape[:-1], code.shape[-1] // per_word, per_word)
+    word = torch.zeros(c.shape[:-1], dtype=torch.int64, device=code.device)
+    for i in range(per_word):
+        word |= c[..., i].to(torch.int64) << (bits * i)
+    out = [(word >> (8 * k)) & 0xFF for k in range(nbytes)]
+    return torch.stack(out, dim=-1).flatten(-2).to(torch.uint8).contiguous()
 
 
 def _quantise_narrow_per_seq_head(x, seg, num_seqs, kv_format):
     """x (tokens, h_k, d) float32 -> (packed codes uint8 (tokens, h_k, d*bits/8), descale (b, h_k))."""
     mags_t, sign_bit, bits, _ = NARROW_FORMATS[kv_format]
-    h_k = x.shape[1]
-    amax = torch.zeros(num_seqs, h_k, device=x.device)
-    amax.scatter_reduce_(0, seg[:, None].expand(-1, h_k), x.abs().amax(dim=-1), "amax")
-    desc = amax.clamp(min=1e-6) / mags_t[-1]
-    y = (x / desc[seg][:, :, None]).clamp(-mags_t[-1], mags_t[-1])
-    mags = torch.tensor(mags_t, device=x.device)
-    ay = y.abs()
-    hi = torch.bucketize(ay, mags).clamp(max=len(mags_t) - 1)  # first magnitude >= |y|
-    lo = (hi - 1).clamp(min=0)
-    code = torch.where((ay - mags[lo]) <= (mags[hi] - ay), lo, hi)
-    code = code | ((y < 0) & (mags[code] > 0)).to(code.dtype) * sign_bit
-    if bits == 4:
-        packed = code[..., 0::2] | (code[..., 1::2] << 4)
-    else:  # four 6-bit codes -> 24 bits -> 3 bytes, little-endian
-        c = code.view(*code.shape[:-1], code.shape[-1] // 4, 4)
-        w = c[..., 0] | (c[..., 1] << 6) | (c[..., 2] << 12) | (c[..., 3] << 18)
-        packed = torch.stack([w & 0xFF, (w >> 8) & 0xFF, (w >> 16) & 0xFF], dim=-1).flatten(-2)
-    return packed.to(torch.uint8).contiguous(), desc.contiguous()
+    top = mags_t[-1]
+    desc = _seq_head_amax(x, seg, num_seqs).clamp(min=1e-6) / top
+    y = (x / desc[seg][:, :, None]).clamp(-top, top)
+    return _pack_codes(_nearest_code(y, mags_t, sign_bit), bits), desc.contiguous()
 
 
 def _quantise_nvfp4_per_seq_head(x, seg, num_seqs):
     """x (tokens, h_k, d) float32 -> (packed codes (tokens, h_k, d/2), e4m3
     group scales (tokens, h_k, d/16) uint8, descale (b, h_k) = 8 * gs)."""
     tokens, h_k, d = x.shape
-    amax = torch.zeros(num_seqs, h_k, device=x.device)
-    amax.scatter_reduce_(0, seg[:, None].expand(-1, h_k), x.abs().amax(dim=-1), "amax")
-    gs = amax.clamp(min=1e-12) / (6.0 * E4M3_MAX)
-    xg = x.view(tokens, h_k, d // 16, 16)
-    sc = (xg.abs().amax(dim=-1) / 6.0 / gs[seg][:, :, None]).clamp(max=E4M3_MAX).to(torch.float8_e4m3fn)
-    denom = (sc.float() * gs[seg][:, :, None])[..., None]
-    y = torch.where(denom > 0, xg / denom.clamp(min=1e-30), torch.zeros_like(xg)).view(tokens, h_k, d)
-    mags = torch.tensor(E2M1_MAGNITUDES, device=x.device)
-    ay = y.abs().clamp(max=E2M1_MAGNITUDES[-1])
-    hi = torch.bucketize(ay, mags).clamp(max=len(E2M1_MAGNITUDES) - 1)
-    lo = (hi - 1).clamp(min=0)
-    code = torch.where((ay - mags[lo]) <= (mags[hi] - ay), lo, hi)
-    code = code | ((y < 0) & (mags[code] > 0)).to(code.dtype) << 3
-    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).to(torch.uint8).contiguous()
-    return packed, sc.view(torch.uint8).contiguous(), (gs * 8.0).contiguous()
+    gs = _seq_head_amax(x, seg, num_seqs).clamp(min=1e-12) / (6.0 * E4M3_MAX)  # global scale per (seq, head)
+    gtok = gs[seg][:, :, None]  # (tokens, h_k, 1)
+    groups = x.view(tokens, h_k, d // 16, 16)
+    scale = (groups.abs().amax(dim=-1) / 6.0 / gtok).clamp(max=E4M3_MAX).to(torch.float8_e4m3fn)
+    step = scale.float() * gtok  # value of one e2m1 unit in each group; 0 for an all-zero group
+    live = step > 0
+    y = groups / torch.where(live, step, torch.ones_like(step))[..., None] * live[..., None]
+    code = _nearest_code(y.view(tokens, h_k, d).clamp(-E2M1_MAGNITUDES[-1], E2M1_MAGNITUDES[-1]),
+                         E2M1_MAGNITUDES, 0x8)
+    return _pack_codes(code, 4), scale.view(torch.uint8).contiguous(), (gs * 8.0).contiguous()
+
+
+def _quantise_query_e4m3(q, b, q_len, h_k, h_r, d):
+    """bf16 query -> (e4m3 codes, descale (b, h_k)): one descale per
+    (sequence, kv head), its largest |q| over the q_len tokens, h_r heads and
+    d dims (at least 1e-6) over 448."""
+    groups = q.float().view(b, q_len, h_k, h_r, d).permute(0, 2, 1, 3, 4).reshape(b, h_k, -1)
+    desc = (groups.abs().amax(dim=-1).clamp(min=1e-6) / E4M3_MAX).contiguous()
+    codes = (groups / desc[..., None]).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+    codes = codes.view(b, h_k, q_len, h_r, d).permute(0, 2, 1, 3, 4).reshape(b * q_len, h_k * h_r, d)
+    return codes.view(torch.uint8).contiguous(), desc
 
 
 def make_batch(w: Workload, device="cpu", seq_lens=None) -> Batch:
@@ -340,11 +363,7 @@ def make_batch(w: Workload, device="cpu", seq_lens=None) -> Batch:
     q = torch.randn(b * w.q_len, w.h_q, w.d_qk, generator=gen, device=device).to(torch.bfloat16)
     q_descale = torch.ones(b, h_k, device=device)
     if w.q_format == "e4m3":
-        qg = q.float().view(b, w.q_len, h_k, w.h_r, w.d_qk)
-        amax = qg.abs().amax(dim=(1, 3, 4)).clamp(min=1e-6)
-        q_descale = (amax / E4M3_MAX).contiguous()
-        q = (qg / q_descale[:, None, :, None, None]).clamp(-E4M3_MAX, E4M3_MAX)
-        q = q.to(torch.float8_e4m3fn).view(torch.uint8).view(b * w.q_len, w.h_q, w.d_qk).contiguous()
+        q, q_descale = _quantise_query_e4m3(q, b, w.q_len, h_k, w.h_r, w.d_qk)
 
     batch = Batch(spec=w, seq_lens=torch.from_numpy(lens).to(device),
                   block_table=torch.from_numpy(bt).to(device), num_pages=num_pages, q=q,

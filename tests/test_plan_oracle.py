@@ -1,6 +1,7 @@
 """Pins of the split-KV plan oracle (no GPU): hand-worked examples of the
-rule on the t5_decode page (``plan_split_kv``), a linear-scan check of the
-chunk's minimality, and the structural invariants of every plan."""
+rule on the t5_decode page (``plan_split_kv``), the chunk's minimality (it
+fits one wave, one tile less does not), and the structural invariants of
+every plan."""
 
 import math
 
@@ -97,9 +98,12 @@ def test_random_plans_invariants_and_minimal_chunk(seed):
     if len(tiles) >= slots or kw["max_splits"] == 1:
         assert chunk == max(tiles)
     else:
-        scan = next(c for c in range(lo, max(max(tiles), lo) + 1)
-                    if sum(math.ceil(t / c) for t in tiles) <= slots)
-        assert chunk == scan
+        # minimal: the chunk fits one wave and one tile less (when still >= lo) does not; the chunk count
+        # only grows as the chunk shrinks, so no smaller size fits either
+        def count(c):
+            return sum(math.ceil(t / c) for t in tiles)
+        assert chunk >= lo and (count(chunk) <= slots or chunk == lo > max(tiles))
+        assert chunk == lo or count(chunk - 1) > slots
 
 
 # ---------------------------------------------------------------------------
