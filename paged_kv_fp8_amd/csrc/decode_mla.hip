@@ -153,7 +153,8 @@ __device__ __forceinline__ float pair32(float x, bool take_max) {
 // From 64 query rows on, the latent records of each 32-key block are
 // dequantised ONCE per workgroup into LDS as bf16 key rows (512 latent
 // values, code x block scale, exact for the record's power-of-two scales,
-// then the 64 bf16 rope values), in a ring of three stages. Both MFMA operands come from there:
+// then the 64 bf16 rope values), in a ring of three stages. Both MFMA
+// operands come from there:
 //  * QK^T reads 16-byte pieces of the key rows (keys on M, two 16-key tiles);
 //  * PV reads V^T straight from the same rows with the LDS transpose load
 //    (ds_read_b64_tr_b16): within each 16-lane group, lane i receives element
@@ -161,22 +162,27 @@ __device__ __forceinline__ float pair32(float x, bool take_max) {
 //    group g4 reads V[key k0 + 4 g4 + j/4][d + 4 (j % 4) ..], lane i holds
 //    V[keys k0 + 4 g4 .. +3][d + i]. Two such reads (k0 = 0 and 16) give the
 //    8 keys of a 16x16x32 A operand in the order in which the QK^T
-//    accumulators hold P (keys 4 g4 + i of each tile), so P needs no lane
-//    exchange.
-// Four waves, one per SIMD: wave w owns the 32 query rows 32 (w >> 1) .. +31
-// of the workgroup's 64 (two 16-row N blocks, so every K or V^T piece read
-// from LDS feeds two MFMAs) and the half h = w & 1 of the head dims: latent
-// blocks 2h and 2h + 1 (d_v 256 h .. 256 h + 255, its share of PV and of
-// O) and rope k-step h. Its QK^T over that half of d_qk is a partial S; the
-// two waves of a row group swap their partials through LDS and both add the
-// same two numbers, so S, the softmax statistics and P agree bit for bit and
-// no part of S is computed twice.
-// The 256 threads split a block's loads (64 latent bytes, 16 rope bytes and
-// the key's 16 scale bytes each), RING blocks ahead of the math in a register ring. One
-// barrier per block: stage j is written in step j - 1 and read in step j, and
-// rewritten in step j + 2 after the barrier of step j + 1; the partial-S
-// exchange is double-buffered the same way.
-constexpr int kLdsWaves = 4;
+//    accumulators hold the keys (4 g4 + i of each tile).
+// Eight waves, two per SIMD: one wave per SIMD reads LDS at well under half
+// the rate two reach, and two overlap each other's VALU and MFMA work. Wave
+// w = 4 rg + q serves row group rg (32 of the workgroup's 64 query rows, two
+// 16-row N blocks, so every K or V^T piece read from LDS feeds two MFMAs)
+// and head-dim quarter q: latent block q for QK^T (a partial S) and for PV
+// (d_v 128 q .. 128 q + 127, its share of O), plus rope k-step (q + 2 rg) & 3
+// when that is below 2, so the two waves of each SIMD carry nine k-steps.
+// Per 32-key block the four waves of a row group write their partial S to
+// LDS; after a barrier wave q owns rows 8 q .. 8 q + 7 of the group: it adds
+// the four partials of those rows in a fixed order, masks them and runs
+// their softmax alone (a row's statistics live in one wave), and writes P
+// as bf16 in the layout of the PV operand; after a second barrier every wave
+// reads P of all 32 rows for its PV.
+// The 512 threads split a block's loads (32 latent bytes, 8 rope bytes and
+// the key's 16 scale bytes each), RING blocks ahead of the math in a
+// register ring. Stage j is written in step j - 1 and read in step j, and
+// rewritten in step j + 2 (after the barriers of step j + 1). The partial-S
+// and P areas are single: each is rewritten only after the barrier that
+// ends the reads of its previous contents.
+constexpr int kLdsWaves = 8;
 constexpr int kLdsRows = 64;                            // query rows per workgroup
 constexpr int kStageKeys = 32;                          // keys per step
 // bf16 key row + 32 B: rows sit 8 banks apart, and the 16-byte pieces of rows
@@ -184,23 +190,23 @@ constexpr int kStageKeys = 32;                          // keys per step
 // column (the QK^T pieces) and 4 rows read 32 contiguous bytes each (the
 // transpose loads) both hit distinct banks
 constexpr int kKRowBytes = 2 * (kLatent + kRope) + 32;
-constexpr int kStageK = 0;
 constexpr int kStageBytes = kStageKeys * kKRowBytes;
 constexpr int kStages = 3;
-// partial S of one wave: [key tile][row block][lane] f32x4
-constexpr int kSxWaveBytes = 2 * 2 * 64 * 16;
-constexpr int kSxOffset = kStages * kStageBytes;
-constexpr int kFlagOffset = kSxOffset + 2 * kLdsWaves * kSxWaveBytes;  // restart flag (int)
+constexpr int kSpWaveBytes = 2 * 2 * 64 * 16;                    // partial S of a wave: [tt][rb][lane] f32x4
+constexpr int kSpOffset = kStages * kStageBytes;
+constexpr int kPOffset = kSpOffset + kLdsWaves * kSpWaveBytes;  // P: [rg][rb][lane] 8 bf16
+constexpr int kStatOffset = kPOffset + 2 * 2 * 64 * 16;         // (max, sum) of the 64 rows
+constexpr int kFlagOffset = kStatOffset + kLdsRows * 8;          // restart flag (int)
 constexpr int kLdsBytes = kFlagOffset + 16;
 constexpr float kFixedLog2 = 32.0f;  // p = exp2((s - m_run) c2) stays below 2^32
 constexpr int kAhead = 2;            // LDS operand pieces read ahead of their MFMAs
 
-// One thread's loads of one 32-key block: key t >> 3, latent bytes 8 (t & 7) +
-// 64 i (i < 8, two per uint4: lat[i] lies in latent block i), rope bytes
-// 16 (t & 7), and the key's four block scales (fp32 bits).
+// One thread's loads of one 32-key block: key t >> 4, latent bytes
+// 8 (t & 15) + 128 i (lat[i] lies in latent block i), rope bytes 8 (t & 15),
+// and the key's four block scales (fp32 bits).
 struct RawPiece {
-  uint4 lat[4];
-  uint4 rope;
+  uint2 lat[4];
+  uint2 rope;
   uint4 scl;
 };
 
@@ -219,6 +225,14 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
       (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) uint8_t*)p);
 }
 
+// x from the lane 8 apart within its 16-lane row (DPP row rotate by 8)
+__device__ __forceinline__ float lane_xor8(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+// max / sum over the eight lanes that share lane & 7
+__device__ __forceinline__ float max_over8(float x) { return pair32(pair16(max2f(x, lane_xor8(x)), true), true); }
+__device__ __forceinline__ float sum_over8(float x) { return pair32(pair16(x + lane_xor8(x), false), false); }
+
 template <bool CAUSAL_TAIL, int RING>
 __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int tile, uint8_t* lds) {
   const int t = threadIdx.x;
@@ -226,7 +240,9 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
   const int lane = t & 63;
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
-  const int half = w & 1;  // latent blocks 2 half, 2 half + 1; rope k-step half
+  const int rg = w >> 2, q = w & 3;
+  const int rope_step = (q + 2 * rg) & 3;  // this wave's rope k-step, when below 2
+  const bool has_rope = rope_step < 2;
 
   const int4 wk = p.work[item];
   const int b = wk.x;
@@ -246,10 +262,11 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
   const int k_begin = p.bin_offsets ? wk.y : wk.y * kTileKeys;
   const int k_end = min(p.bin_offsets ? wk.z : wk.z * kTileKeys, L);
 
-  // rows of this wave: n = row0 + 16 rb + r16; a row group past the last row
-  // runs like the others (on zero query rows) and writes nothing
-  const int row0 = tile * kLdsRows + 32 * (w >> 1);
-  int qtok[2], qhead[2], lim[2];
+  // rows of the row group in the MFMA layout: n = row0 + 16 rb + r16; a row
+  // group past the last row runs like the others (on zero query rows) and
+  // writes nothing
+  const int row0 = tile * kLdsRows + 32 * rg;
+  int qtok[2], qhead[2];
   bool row_ok[2];
   for (int rb = 0; rb < 2; ++rb) {
     const int n = row0 + 16 * rb + r16;
@@ -257,39 +274,42 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
     const int qi = n / p.h_q;
     qtok[rb] = b * p.q_len + qi;
     qhead[rb] = n - qi * p.h_q;
-    lim[rb] = min(CAUSAL_TAIL ? L - p.q_len + qi : L - 1, k_end - 1);
   }
-  const int lim_min = min(CAUSAL_TAIL ? L - p.q_len + row0 / p.h_q : L - 1, k_end - 1);
+  // the row this lane serves in the softmax: row 16 orb + orow of the group
+  // (rows 8 q .. 8 q + 7), keys 16 ott + okey .. + 3 of a block; those four
+  // values sit in lane olane of the QK^T accumulator layout (tile ott, row
+  // block orb), and their P in lane olane of the PV operand, k-slots 4 ott ..
+  const int orb = q >> 1, orow = 8 * (q & 1) + (lane & 7);
+  const int ott = lane >> 5, okey = 4 * ((lane >> 3) & 3);
+  const int olane = orow + 4 * okey;  // = orow + 16 * ((lane >> 3) & 3)
+  const int on = min(row0 + 16 * orb + orow, p.rows - 1);
+  const int olim = min(CAUSAL_TAIL ? L - p.q_len + on / p.h_q : L - 1, k_end - 1);
+  const int on_min = min(row0 + 16 * orb + 8 * (q & 1), p.rows - 1);  // first row this wave owns
+  const int olim_min = min(CAUSAL_TAIL ? L - p.q_len + on_min / p.h_q : L - 1, k_end - 1);
   const float c2 = p.scale_log2e;
 
-  // Q as the B operand of this wave's half of d_qk: k-step k < 8 holds
-  // q[n][256 half + 32 k + 8 g4 .. +7] (latent), k = 8 the rope k-step half
-  bf16x8 qv[2][9];
+  // Q as the B operand of this wave's quarter of d_qk: k-step k < 4 holds
+  // q[n][128 q + 32 k + 8 g4 .. +7] (latent block q), k = 4 the rope k-step
+  bf16x8 qv[2][5];
   for (int rb = 0; rb < 2; ++rb) {
     const uint8_t* qrow = p.q + (int64_t)qtok[rb] * p.q_tok + (int64_t)qhead[rb] * p.q_head;
-    for (int k = 0; k < 9; ++k) {
-      const int d = k < 8 ? 256 * half + 32 * k + 8 * g4 : kLatent + 32 * half + 8 * g4;
-      if (row_ok[rb]) {
+    for (int k = 0; k < 5; ++k) {
+      const int d = k < 4 ? 128 * q + 32 * k + 8 * g4 : kLatent + 32 * (rope_step & 1) + 8 * g4;
+      if (row_ok[rb] && (k < 4 || has_rope)) {
         qv[rb][k] = *reinterpret_cast<const bf16x8*>(qrow + 2 * d);
       } else {
         for (int e = 0; e < 8; ++e) qv[rb][k][e] = (__bf16)0.0f;
       }
     }
   }
-  // Q is only ever an MFMA operand, which may sit in AGPRs: place it there (an
-  // empty statement with an AGPR operand, after all of its loads are issued),
-  // so that the VGPRs hold the LDS pieces read ahead of the MFMAs
-  for (int rb = 0; rb < 2; ++rb)
-    for (int k = 0; k < 9; ++k) asm volatile("" : "+a"(qv[rb][k]));
 
-  f32x4 oacc[2][2][8];  // [row block][128-block gg of this half][16-row tile mt]:
-                        // O^T[256 half + 128 gg + 16 mt + 4 g4 + i][row 16 rb + r16]
-  // m_run: the row's reference max (raw-score units), set by its first visible
-  // block and then fixed, so O is never rescaled inside the loop (a VALU pass
-  // over O would pull it out of the MFMA accumulator registers on every
-  // block). P = exp2((s - m_run) c2) may grow up to 2^kFixedLog2, which bf16
-  // P and the fp32 sums absorb. m_seen: the largest block max seen.
-  float m_run[2] = {-INFINITY, -INFINITY}, l_part[2], m_seen[2] = {-INFINITY, -INFINITY};
+  f32x4 oacc[2][8];  // [row block][16-row tile mt]: O^T[128 q + 16 mt + 4 g4 + i][row 16 rb + r16]
+  // m_run: the reference max (raw-score units) of the row this lane serves,
+  // set by the row's first visible block and then fixed, so O is never
+  // rescaled inside the loop. P = exp2((s - m_run) c2) may grow up to
+  // 2^kFixedLog2, which bf16 P and the fp32 sums absorb. m_seen: the largest
+  // block max seen. l_part: this lane's share of the row sum.
+  float m_run = -INFINITY, m_seen = -INFINITY, l_part;
   // an LDS pointer (a generic one would make these FLAT accesses, whose waits
   // also wait for every global load in flight)
   volatile __attribute__((address_space(3))) int* restart_flag =
@@ -306,11 +326,9 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
   // the item again from its first key with each row's reference at m_seen.
   do {
   again = false;
-  for (int rb = 0; rb < 2; ++rb) {
-    l_part[rb] = 0.f;
-    for (int gg = 0; gg < 2; ++gg)
-      for (int mt = 0; mt < 8; ++mt) oacc[rb][gg][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  l_part = 0.f;
+  for (int rb = 0; rb < 2; ++rb)
+    for (int mt = 0; mt < 8; ++mt) oacc[rb][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (k_end > k_begin) {
     const int32_t* bt = p.block_table + (int64_t)b * p.bt_row;
@@ -322,53 +340,46 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
 
     // fetch u: the loads of block k_begin + 32u into ring slot u % RING, with
     // the pages from page slot u % 3 (loaded two fetches earlier); it loads
-    // the pages of fetch u + 2. Waves 0-1 load keys 0-15, waves 2-3 keys
+    // the pages of fetch u + 2. Waves 0-3 load keys 0-15, waves 4-7 keys
     // 16-31, so each wave reads one page per load.
     int pv[3];
     pv[0] = page_pair(k_begin);
     pv[1] = page_pair(k_begin + kStageKeys);
-    const int my_key = t >> 3, part = t & 7;
+    const int my_key = t >> 4, part = t & 15;
     // A load's address is the wave-uniform page base (scalar registers) plus a
     // 32-bit lane offset: the key's row inside the page times the row stride
-    // (page_size * row stride < 2^30, as the host checks for the other caches)
-    // plus the lane's bytes in the row.
+    // (page_size * row stride < 2^30, as the host checks) plus the lane's
+    // bytes in the row.
     auto fetch = [&](RawPiece& r, int kb, const int ps) {
       const int pg0 = clamp_page(__builtin_amdgcn_readlane(pv[ps], 0));
       const int pg1 = clamp_page(__builtin_amdgcn_readlane(pv[ps], 1));
-      const int64_t pgk = (w >> 1) ? pg1 : pg0;
+      const int64_t pgk = (w >> 2) ? pg1 : pg0;
       const uint32_t key = (uint32_t)(min(kb + my_key, last_key) & pmask);
       const uint8_t* lat = p.lat + pgk * p.lat_page;
       const uint8_t* rope = p.rope + pgk * p.rope_page;
       const uint8_t* scl = p.scl + pgk * p.scl_page;
       const uint32_t lat_off = key * (uint32_t)p.lat_row + 8u * part;
-      for (int i = 0; i < 4; ++i) {
-        const uint2 c0 = *reinterpret_cast<const uint2*>(lat + (lat_off + 128u * i));
-        const uint2 c1 = *reinterpret_cast<const uint2*>(lat + (lat_off + 128u * i + 64u));
-        r.lat[i] = uint4{c0.x, c0.y, c1.x, c1.y};
-      }
-      r.rope = *reinterpret_cast<const uint4*>(rope + (key * (uint32_t)p.rope_row + 16u * part));
+      for (int i = 0; i < 4; ++i) r.lat[i] = *reinterpret_cast<const uint2*>(lat + (lat_off + 128u * i));
+      r.rope = *reinterpret_cast<const uint2*>(rope + (key * (uint32_t)p.rope_row + 8u * part));
       r.scl = *reinterpret_cast<const uint4*>(scl + key * (uint32_t)p.scl_row);
       pv[(ps + 2) % 3] = page_pair(kb + 2 * kStageKeys);
     };
-    // 16-byte pieces of the key row: bf16 latent pieces 8 i + part (codes
-    // 64 i + 8 part .., so each 8-lane group stores 128 contiguous bytes),
-    // then the rope piece part. A wave whose keys all carry power-of-two
-    // scales (the record format) folds them in with the scaled convert;
-    // otherwise the wave takes the fp32 product (a uniform branch).
+    // The key row's bf16 latent pieces 16 i + part (codes 128 i + 8 part ..,
+    // so each 16-lane group stores 256 contiguous bytes), then its rope bytes
+    // 8 part. A wave whose keys all carry power-of-two scales (the record
+    // format) folds them in with the scaled convert; otherwise the wave takes
+    // the fp32 product (a uniform branch).
     auto stage_in = [&](const RawPiece& r, uint8_t* st) {
       const float sc[4] = {__uint_as_float(r.scl.x), __uint_as_float(r.scl.y), __uint_as_float(r.scl.z),
                            __uint_as_float(r.scl.w)};
-      uint8_t* row = st + kStageK;
       if (__builtin_amdgcn_ballot_w64(!pow2_scales(r.scl)) == 0) {
-        for (int i = 0; i < 8; ++i)
-          *reinterpret_cast<bf16x8*>(row + krow_base(my_key, 128 * i + 16 * part)) =
-              e4m3x8_times_pow2(half_of(r.lat[i >> 1], i & 1), sc[i >> 1]);
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<bf16x8*>(st + krow_base(my_key, 256 * i + 16 * part)) = e4m3x8_times_pow2(r.lat[i], sc[i]);
       } else {
-        for (int i = 0; i < 8; ++i)
-          *reinterpret_cast<bf16x8*>(row + krow_base(my_key, 128 * i + 16 * part)) =
-              e4m3x8_times_any(half_of(r.lat[i >> 1], i & 1), sc[i >> 1]);
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<bf16x8*>(st + krow_base(my_key, 256 * i + 16 * part)) = e4m3x8_times_any(r.lat[i], sc[i]);
       }
-      *reinterpret_cast<uint4*>(row + krow_base(my_key, 2 * kLatent + 16 * part)) = r.rope;
+      *reinterpret_cast<uint2*>(st + krow_base(my_key, 2 * kLatent + 8 * part)) = r.rope;
     };
 
     // this lane's QK^T piece (key row r16 of a tile, bytes 16 g4 ..) and
@@ -376,98 +387,80 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
     // rows 16 apart share the swizzle
     const int qk_base = krow_base(r16, 16 * g4);
     const int tr_base = krow_base(4 * g4 + (r16 >> 2), 8 * (r16 & 3));
-    // partial S (s_out[tt][rb]: S[key 16 tt + 4 g4 + i][row 16 rb + r16]) of
-    // the block in stage st over this wave's half of d_qk. The 18 K pieces
-    // (per key tile: 8 latent k-steps, then the rope k-step) are read kAhead
-    // pieces ahead of the MFMAs that use them.
-    auto qk_piece = [&](const uint8_t* st, int idx) -> bf16x8 {
-      const int tt = idx / 9, k = idx % 9;
-      const int off = k < 8 ? 2 * (256 * half + 128 * (k >> 2) + 32 * (k & 3)) : 2 * (kLatent + 32 * half);
-      return *reinterpret_cast<const bf16x8*>(st + kStageK + qk_base + tt * 16 * kKRowBytes + off);
+    // K piece of tile tt, k-step k of this wave's quarter (k = 4: its rope step)
+    auto qk_piece = [&](const uint8_t* st, int tt, int k) -> bf16x8 {
+      const int off = k < 4 ? 2 * (128 * q + 32 * k) : 2 * (kLatent + 32 * (rope_step & 1));
+      return *reinterpret_cast<const bf16x8*>(st + qk_base + tt * 16 * kKRowBytes + off);
     };
-    auto qk_half = [&](const uint8_t* st, f32x4 (&s_out)[2][2]) {
+    // partial S (s[tt][rb]: S[key 16 tt + 4 g4 + i][row 16 rb + r16]) of the
+    // block in stage st over this wave's quarter of d_qk. The eight latent
+    // pieces are read kAhead ahead of their MFMAs; the two rope pieces first
+    // (every wave reads them, so no load sits in a branch).
+    auto qk_quarter = [&](const uint8_t* st, f32x4 (&s)[2][2]) {
+      const bf16x8 pr0 = qk_piece(st, 0, 4), pr1 = qk_piece(st, 1, 4);
       bf16x8 pa[kAhead + 1];
-      for (int i = 0; i < kAhead; ++i) pa[i] = qk_piece(st, i);
+      for (int i = 0; i < kAhead; ++i) pa[i] = qk_piece(st, i >> 2, i & 3);
 #pragma unroll
-      for (int idx = 0; idx < 18; ++idx) {
-        const int tt = idx / 9, k = idx % 9;
-        if (idx + kAhead < 18) pa[(idx + kAhead) % (kAhead + 1)] = qk_piece(st, idx + kAhead);
+      for (int idx = 0; idx < 8; ++idx) {
+        const int tt = idx >> 2, k = idx & 3;
+        if (idx + kAhead < 8) pa[(idx + kAhead) % (kAhead + 1)] = qk_piece(st, (idx + kAhead) >> 2, (idx + kAhead) & 3);
         for (int rb = 0; rb < 2; ++rb) {
-          const f32x4 c = k == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s_out[tt][rb];
-          s_out[tt][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[idx % (kAhead + 1)], qv[rb][k], c, 0, 0, 0);
+          const f32x4 c = k == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[tt][rb];
+          s[tt][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[idx % (kAhead + 1)], qv[rb][k], c, 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (has_rope) {
+        for (int rb = 0; rb < 2; ++rb) {
+          s[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pr0, qv[rb][4], s[0][rb], 0, 0, 0);
+          s[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pr1, qv[rb][4], s[1][rb], 0, 0, 0);
+        }
+      }
     };
-    // S = this wave's partial + the partner's (the same two numbers in both
-    // waves), with the mask of the block at kb
-    auto gather_s = [&](f32x4 (&sv)[2][2], const uint8_t* sx_partner, int kb) {
+    uint8_t* const sp_own = lds + kSpOffset + w * kSpWaveBytes;
+    auto put_s = [&](const f32x4 (&s)[2][2]) {
       for (int tt = 0; tt < 2; ++tt)
-        for (int rb = 0; rb < 2; ++rb)
-          sv[tt][rb] += *reinterpret_cast<const f32x4*>(sx_partner + ((2 * tt + rb) * 64 + lane) * 16);
-      if (kb + kStageKeys - 1 > lim_min) {
-        for (int tt = 0; tt < 2; ++tt)
-          for (int rb = 0; rb < 2; ++rb)
-            for (int i = 0; i < 4; ++i)
-              if (kb + 16 * tt + 4 * g4 + i > lim[rb]) sv[tt][rb][i] = -INFINITY;
-      }
+        for (int rb = 0; rb < 2; ++rb) *reinterpret_cast<f32x4*>(sp_own + ((2 * tt + rb) * 64 + lane) * 16) = s[tt][rb];
     };
-    // Online softmax of one block in 12 parts: part 0 the row max, part 1 the
-    // reference, parts 2-9 two exponentials each, parts 10-11 four packed bf16
-    // pairs of P each. l and the reference max are updated; pb[rb] = P of row
-    // block rb as the B operand of PV; `overflow` is set if some p would pass
-    // 2^kFixedLog2.
-    // Each part's results pass through an empty asm statement where they are
-    // made, which keeps the compiler from sinking the arithmetic down to its
-    // uses in PV (the scheduling barriers order instructions, not values).
-    float sm_mx[2], sm_off[2], sm_pr[2][8];
-    auto softmax_part = [&](int i, const f32x4 (&sv)[2][2], u32x4 (&pb)[2], bool& overflow) {
-      if (i == 0) {
-        for (int rb = 0; rb < 2; ++rb) {
-          const float mx = max3f(max3f(sv[0][rb][0], sv[0][rb][1], sv[0][rb][2]),
-                                 max3f(sv[0][rb][3], sv[1][rb][0], sv[1][rb][1]),
-                                 max3f(sv[1][rb][2], sv[1][rb][3], -INFINITY));
-          sm_mx[rb] = pair32(pair16(mx, true), true);
-          asm volatile("" : "+v"(sm_mx[rb]));
-        }
-      } else if (i == 1) {
-        for (int rb = 0; rb < 2; ++rb) {
-          m_seen[rb] = fmaxf(m_seen[rb], sm_mx[rb]);
-          // the first visible block sets the reference (O and l are still zero)
-          m_run[rb] = m_run[rb] == -INFINITY ? sm_mx[rb] : m_run[rb];
-          overflow |= (sm_mx[rb] - m_run[rb]) * c2 > kFixedLog2;
-          // one fma per score: exp2(s c2 - m c2); no visible key yet: exp2(-inf) = 0
-          sm_off[rb] = m_run[rb] == -INFINITY ? 0.f : -m_run[rb] * c2;
-          asm volatile("" : "+v"(sm_off[rb]));
-        }
-      } else if (i < 10) {
-        for (int e = 2 * (i - 2); e < 2 * (i - 2) + 2; ++e) {  // element e = 8 rb + 4 tt + ii
-          const int rb = e >> 3, tt = (e >> 2) & 1, ii = e & 3;
-          sm_pr[rb][4 * tt + ii] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[tt][rb][ii], c2, sm_off[rb]));
-          asm volatile("" : "+v"(sm_pr[rb][4 * tt + ii]));
-        }
-        if (i == 9) {
-          for (int rb = 0; rb < 2; ++rb) {
-            float psum = 0.f;
-            for (int e = 0; e < 8; ++e) psum += sm_pr[rb][e];
-            l_part[rb] += psum;
-            asm volatile("" : "+v"(l_part[rb]));
-          }
-        }
-      } else {
-        // keys 16 tt + 4 g4 + 2 jj, + 1 sit in k-slots 4 tt + 2 jj, + 1 (word 2 tt + jj)
-        const int tt = i - 10;
-        for (int rb = 0; rb < 2; ++rb) {
-          for (int jj = 0; jj < 2; ++jj)
-            pb[rb][2 * tt + jj] = pack_bf16x2(sm_pr[rb][4 * tt + 2 * jj], sm_pr[rb][4 * tt + 2 * jj + 1]);
-          asm volatile("" : "+v"(pb[rb]));
-        }
+    // S of this lane's four values: the partials of waves 4 rg + 0 .. 3 added
+    // in that order (the one wave that owns the row computes it), masked
+    const uint8_t* const sp_row = lds + kSpOffset + 4 * rg * kSpWaveBytes + ((2 * ott + orb) * 64 + olane) * 16;
+    auto own_s = [&](int kb) -> f32x4 {
+      f32x4 a = *reinterpret_cast<const f32x4*>(sp_row);
+      f32x4 b1 = *reinterpret_cast<const f32x4*>(sp_row + kSpWaveBytes);
+      f32x4 b2 = *reinterpret_cast<const f32x4*>(sp_row + 2 * kSpWaveBytes);
+      f32x4 b3 = *reinterpret_cast<const f32x4*>(sp_row + 3 * kSpWaveBytes);
+      // all four reads in flight before the first add (one LDS round trip)
+      asm volatile("" : "+v"(a), "+v"(b1), "+v"(b2), "+v"(b3));
+      f32x4 s = a + b1;
+      s += b2;
+      s += b3;
+      if (kb + kStageKeys - 1 > olim_min) {
+        for (int i = 0; i < 4; ++i)
+          if (kb + 16 * ott + okey + i > olim) s[i] = -INFINITY;
       }
+      return s;
     };
-    // O^T += V^T (P * scale)^T for this wave's 256 d_v: V^T tile (gg, mt) =
-    // tile 8 gg + mt, read kAhead tiles ahead of its MFMAs
-    auto v_tile = [&](const uint8_t* st, int idx) -> bf16x8 {
-      const uint8_t* v = st + kStageK + tr_base + 512 * half + 256 * (idx >> 3) + 32 * (idx & 7);
+    // softmax of the served row for this block: block max over its 32 keys,
+    // the reference, four exponentials, P to the PV operand area
+    uint8_t* const p_out = lds + kPOffset + ((2 * rg + orb) * 64 + olane) * 16 + 8 * ott;
+    auto softmax_own = [&](const f32x4& s, bool& overflow) {
+      const float mx = max_over8(max3f(max3f(s[0], s[1], s[2]), s[3], -INFINITY));
+      m_seen = max2f(m_seen, mx);
+      // the first visible block sets the reference (O and l are still zero)
+      m_run = m_run == -INFINITY ? mx : m_run;
+      overflow = (mx - m_run) * c2 > kFixedLog2;
+      // one fma per score: exp2(s c2 - m c2); no visible key yet: exp2(-inf) = 0
+      const float off = m_run == -INFINITY ? 0.f : -m_run * c2;
+      float pr[4];
+      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, off));
+      l_part += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      *reinterpret_cast<uint2*>(p_out) = uint2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+    };
+    // O^T += V^T P^T for this wave's 128 d_v: V^T tile mt read kAhead tiles
+    // ahead of its MFMAs
+    auto v_tile = [&](const uint8_t* st, int mt) -> bf16x8 {
+      const uint8_t* v = st + tr_base + 2 * (128 * q + 16 * mt);
       const s16x4 lo = lds_read_tr16(v);
       const s16x4 hi = lds_read_tr16(v + 16 * kKRowBytes);
       const s16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -475,34 +468,24 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
       __builtin_memcpy(&a, &a16, 16);
       return a;
     };
-    auto pv_step = [&](const uint8_t* st, const u32x4 (&pb)[2]) {
+    const uint8_t* const p_in = lds + kPOffset + 2 * rg * 64 * 16 + lane * 16;
+    auto pv_quarter = [&](const uint8_t* st) {
+      const u32x4 pb[2] = {*reinterpret_cast<const u32x4*>(p_in), *reinterpret_cast<const u32x4*>(p_in + 64 * 16)};
       bf16x8 va[kAhead + 1];
       for (int i = 0; i < kAhead; ++i) va[i] = v_tile(st, i);
 #pragma unroll
-      for (int idx = 0; idx < 16; ++idx) {
-        if (idx + kAhead < 16) va[(idx + kAhead) % (kAhead + 1)] = v_tile(st, idx + kAhead);
-        const int gg = idx >> 3, mt = idx & 7;
+      for (int mt = 0; mt < 8; ++mt) {
+        if (mt + kAhead < 8) va[(mt + kAhead) % (kAhead + 1)] = v_tile(st, mt + kAhead);
         for (int rb = 0; rb < 2; ++rb)
-          oacc[rb][gg][mt] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[idx % (kAhead + 1)], __builtin_bit_cast(bf16x8, pb[rb]),
-                                                  oacc[rb][gg][mt], 0, 0, 0);
+          oacc[rb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mt % (kAhead + 1)],
+                                                                __builtin_bit_cast(bf16x8, pb[rb]), oacc[rb][mt], 0, 0, 0);
       }
     };
-    uint8_t* sx_base = lds + kSxOffset;
-    auto sx_of = [&](int buf, int wave) { return sx_base + (buf * kLdsWaves + wave) * kSxWaveBytes; };
-    auto put_s = [&](uint8_t* sx, const f32x4 (&sv)[2][2]) {
-      for (int tt = 0; tt < 2; ++tt)
-        for (int rb = 0; rb < 2; ++rb) *reinterpret_cast<f32x4*>(sx + ((2 * tt + rb) * 64 + lane) * 16) = sv[tt][rb];
-    };
 
-    // One barrier per step. Block j: fetched in step j - RING, staged into
-    // stage j % 3 in step j - 1; in step j its partial S goes through buffer
-    // j % 2 (written before the barrier, the partner's read after it), then
-    // its softmax and PV. Stage j + 1 is written in step j before the barrier;
-    // its previous block (j - 2) was last read in step j - 2, before the
-    // barrier that ends it. Exchange buffer j % 2 is rewritten in step j + 2,
-    // after the barrier that ends step j + 1, by which the partner has read
-    // it. Rounds of 6 steps keep the ring, stage and buffer indices
+    // Two barriers per step. Block j: fetched in step j - RING, staged into
+    // stage j % 3 in step j - 1. In step j: its partial S is written (with
+    // stage j + 1), B1; the owners reduce, run the softmax and write P, B2;
+    // then PV. Rounds of 6 steps keep the ring and stage indices
     // compile-time; the loop leaves after the last block's step (a uniform
     // branch, so every wave meets the same barriers).
     static_assert(6 % RING == 0, "a round of 6 steps must hold whole rings");
@@ -510,7 +493,6 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
     const int nblocks = (k_end - k_begin + kStageKeys - 1) / kStageKeys;
     RawPiece ring[RING];
     f32x4 sv[2][2];
-    u32x4 pb[2];  // packed bf16 pairs
 #pragma unroll
     for (int u = 0; u < RING; ++u) {
       fetch(ring[u], k_begin + u * kStageKeys, u % 3);
@@ -527,59 +509,60 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
         const int kb = k_begin + j * kStageKeys;
         fetch(ring[s % RING], kb + RING * kStageKeys, (s + RING) % 3);
         const uint8_t* st = lds + (s % 3) * kStageBytes;
-        qk_half(st, sv);
-        put_s(sx_of(s & 1, w), sv);
+        qk_quarter(st, sv);
+        put_s(sv);
         stage_in(ring[(s + 1) % RING], lds + ((s + 1) % 3) * kStageBytes);
         barrier();
-        if (__builtin_amdgcn_readfirstlane(*restart_flag)) {
+        bool overflow;
+        softmax_own(own_s(kb), overflow);
+        if (__builtin_amdgcn_ballot_w64(overflow) && lane == 0) *restart_flag = 1;
+        barrier();
+        // the flag is read once per round: a block past the bound only fills
+        // O, l and P with values the restart throws away
+        if (s == kRound - 1 && __builtin_amdgcn_readfirstlane(*restart_flag)) {
           again = true;
           goto item_end;
         }
-        gather_s(sv, sx_of(s & 1, w ^ 1), kb);
-        bool overflow = false;
-#pragma unroll
-        for (int i = 0; i < 12; ++i) softmax_part(i, sv, pb, overflow);
-        if (__builtin_amdgcn_ballot_w64(overflow) && lane == 0) *restart_flag = 1;
-        pv_step(st, pb);
+        pv_quarter(st);
       }
     }
   loop_done:
-    // a flag set by the last block's softmax has met its barrier; re-read it
-    // after one more, which every wave reaches the same way
-    barrier();
-    again = __builtin_amdgcn_readfirstlane(*restart_flag) != 0;
+    if (__builtin_amdgcn_readfirstlane(*restart_flag)) again = true;
   }
 item_end:
   if (again) {
     barrier();  // every wave has read the flag
     if (t == 0) *restart_flag = 0;
-    for (int rb = 0; rb < 2; ++rb) m_run[rb] = m_seen[rb];
+    m_run = m_seen;
   }
   } while (again);
 
-  // ---- epilogue: this wave's d_v half; LSE / (max, sum) from the first half -------
+  // ---- epilogue: the owners publish each row's (max, sum); every wave
+  // writes its d_v quarter of O; LSE / (max, sum) from quarter 0
+  const float l_row = sum_over8(l_part);
+  float2* const stat = reinterpret_cast<float2*>(lds + kStatOffset);
+  if (((lane >> 3) & 7) == 0) stat[32 * rg + 16 * orb + orow] = float2{m_run == -INFINITY ? -INFINITY : m_run * p.scale, l_row};
+  barrier();
   for (int rb = 0; rb < 2; ++rb) {
-    const float l = pair32(pair16(l_part[rb], false), false);
     if (!row_ok[rb]) continue;
+    const float2 ml = stat[32 * rg + 16 * rb + r16];
+    const float m_nat = ml.x, l = ml.y;
     const int64_t stat_row = (int64_t)b * p.rows + row0 + 16 * rb + r16;
-    const float m_nat = m_run[rb] == -INFINITY ? -INFINITY : m_run[rb] * p.scale;
-    const int d0 = 256 * half + 4 * g4;
+    const int d0 = 128 * q + 4 * g4;
     if (direct) {
       const float inv = l > 0.f ? p.o_scale / l : 0.f;
-      uint8_t* orow = p.o + (int64_t)qtok[rb] * p.o_tok + (int64_t)qhead[rb] * p.o_head;
-      for (int gg = 0; gg < 2; ++gg)
-        for (int mt = 0; mt < 8; ++mt) {
-          bf16x4 out;
-          for (int i = 0; i < 4; ++i) out[i] = (__bf16)(oacc[rb][gg][mt][i] * inv);
-          *reinterpret_cast<bf16x4*>(orow + 2 * (d0 + 128 * gg + 16 * mt)) = out;
-        }
-      if (half == 0 && g4 == 0) p.lse[stat_row] = l > 0.f ? m_nat + logf(l) : -INFINITY;
+      uint8_t* orow_p = p.o + (int64_t)qtok[rb] * p.o_tok + (int64_t)qhead[rb] * p.o_head;
+      for (int mt = 0; mt < 8; ++mt) {
+        bf16x4 out;
+        for (int i = 0; i < 4; ++i) out[i] = (__bf16)(oacc[rb][mt][i] * inv);
+        *reinterpret_cast<bf16x4*>(orow_p + 2 * (d0 + 16 * mt)) = out;
+      }
+      if (q == 0 && g4 == 0) p.lse[stat_row] = l > 0.f ? m_nat + logf(l) : -INFINITY;
     } else {
       const int64_t prow = (int64_t)slot * p.num_seqs * p.rows + stat_row;
       float* dst = p.ws_o + prow * kDv + d0;
-      for (int gg = 0; gg < 2; ++gg)
-        for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(dst + 128 * gg + 16 * mt) = oacc[rb][gg][mt];
-      if (half == 0 && g4 == 0) p.ws_ml[prow] = float2{m_nat, l};
+      for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(dst + 16 * mt) = oacc[rb][mt];
+      if (q == 0 && g4 == 0) p.ws_ml[prow] = float2{m_nat, l};
     }
   }
 }
@@ -603,7 +586,7 @@ __device__ __forceinline__ void xcd_item_tile(int id, int units, int tiles, int&
 constexpr int kLdsRing = 2;  // raw blocks in flight per thread
 
 template <bool CAUSAL_TAIL>
-__global__ __launch_bounds__(64 * kLdsWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * kLdsWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mla_lds_kernel(MlaParams p, int units, int tiles) {
   extern __shared__ __attribute__((aligned(16))) uint8_t mla_stage_lds[];
   if (threadIdx.x == 0) *reinterpret_cast<int*>(mla_stage_lds + kFlagOffset) = 0;
