@@ -322,8 +322,11 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
   bool again;
   // A block whose max would put some p past 2^kFixedLog2 (scores rising that
   // far after a row's first visible block: pathological inputs only) sets the
-  // flag; after the next barrier every wave sees it, and the workgroup runs
-  // the item again from its first key with each row's reference at m_seen.
+  // flag; the waves read it after the second barrier of every sixth block
+  // and after the last, all at the same point, and the workgroup runs the
+  // item again from its first key with each row's reference at m_seen. Each
+  // run gets further than the one before (the blocks it has seen can no
+  // longer pass the bound), so the runs end.
   do {
   again = false;
   l_part = 0.f;

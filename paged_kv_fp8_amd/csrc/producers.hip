@@ -28,8 +28,6 @@ namespace {
 constexpr float kE4m3Max = 448.0f;
 constexpr float kMinAmax = 1e-6f;
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
 // e4m3fn code of one fp32 value: NaN -> 0x7F, |x| > 448 -> +-448, else round
 // to nearest even
 __device__ __forceinline__ unsigned encode_one(float y) {
