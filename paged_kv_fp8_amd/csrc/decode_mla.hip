@@ -1204,8 +1204,16 @@ int mla_rows_per_tile(const pkv_decode_args& a) { return staged(a) ? kLdsRows : 
 
 hipError_t mla_occupancy(const pkv_decode_args& a, int* units_per_cu) {
   // one unit = one workgroup (all rows of one q-row tile of a work item)
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(units_per_cu, select_kernel(a), 64 * waves_per_wg(a),
-                                                      dyn_lds_bytes(a));
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(units_per_cu, select_kernel(a),
+                                                                    64 * waves_per_wg(a), dyn_lds_bytes(a));
+  // the pair form with one row group fits four workgroups per CU, but the
+  // plan is sized for three: a one-wave plan for four left some CUs with four
+  // items and others with three, and the CUs with four set the end
+  // (measured on the latent workload at one query token, same box: decode
+  // 62.8 -> 60.7 us, merge 11.4 -> 9.6 us, step 75.2 -> 72.2 us; two per CU:
+  // 64.8 us)
+  if (e == hipSuccess && !staged(a) && pair_groups(a) == 1 && *units_per_cu > 3) *units_per_cu = 3;
+  return e;
 }
 
 hipError_t mla_launch(const pkv_decode_args& a, hipStream_t stream) {
