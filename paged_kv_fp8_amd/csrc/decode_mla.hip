@@ -21,8 +21,9 @@
 //    lanes that computed it.
 //  * Fewer than 64 rows (one to three query tokens): the pair form, two waves
 //    per 16 rows that split each record by d_v half and exchange partial S.
-//  * 64 rows and more: the staged form, eight waves that share one bf16 copy
-//    of each 32-key block in LDS.
+//  * 64 rows and more: the staged form, four waves (one per SIMD) that share
+//    one bf16 copy of each 32-key block in LDS, with the record's
+//    power-of-two block scales folded into it.
 //  * Load discipline as in the GQA kernel: every fetch issues the same loads
 //    (keys clamped to the chunk's last key), the page of a block comes from a
 //    one-dword vector load issued early enough that its wait covers only the
@@ -163,27 +164,32 @@ __device__ __forceinline__ float pair32(float x, bool take_max) {
 //    V[keys k0 + 4 g4 .. +3][d + i]. Two such reads (k0 = 0 and 16) give the
 //    8 keys of a 16x16x32 A operand in the order in which the QK^T
 //    accumulators hold the keys (4 g4 + i of each tile).
-// Eight waves, two per SIMD: one wave per SIMD reads LDS at well under half
-// the rate two reach, and two overlap each other's VALU and MFMA work. Wave
-// w = 4 rg + q serves row group rg (32 of the workgroup's 64 query rows, two
-// 16-row N blocks, so every K or V^T piece read from LDS feeds two MFMAs)
-// and head-dim quarter q: latent block q for QK^T (a partial S) and for PV
-// (d_v 128 q .. 128 q + 127, its share of O), plus rope k-step (q + 2 rg) & 3
-// when that is below 2, so the two waves of each SIMD carry nine k-steps.
-// Per 32-key block the four waves of a row group write their partial S to
-// LDS; after a barrier wave q owns rows 8 q .. 8 q + 7 of the group: it adds
-// the four partials of those rows in a fixed order, masks them and runs
-// their softmax alone (a row's statistics live in one wave), and writes P
-// as bf16 in the layout of the PV operand; after a second barrier every wave
-// reads P of all 32 rows for its PV.
-// The 512 threads split a block's loads (32 latent bytes, 8 rope bytes and
-// the key's 16 scale bytes each), RING blocks ahead of the math in a
-// register ring. Stage j is written in step j - 1 and read in step j, and
-// rewritten in step j + 2 (after the barriers of step j + 1). The partial-S
-// and P areas are single: each is rewritten only after the barrier that
-// ends the reads of its previous contents.
-constexpr int kLdsWaves = 8;
+// Four waves, one per SIMD, each with all 64 query rows of the workgroup
+// (four 16-row N blocks, so every K or V^T piece read from LDS feeds four
+// MFMAs) and one head-dim quarter q: latent block q for QK^T (a partial S)
+// and for PV (d_v 128 q .. 128 q + 127, its share of O), plus one of the
+// four (16-key tile, rope k-step) pairs. One wave per SIMD has the whole
+// register file (O alone is 128 registers). Against eight waves of 32 rows
+// that read every piece twice (two per SIMD, same box): 4-6% faster.
+// Per 32-key block the four waves write their partial S to LDS; after a
+// barrier wave q owns rows 16 q .. 16 q + 15: it adds the four partials of
+// those rows in a fixed order (each lane holds its row's keys
+// 16 tt + 4 g4 + i, the QK^T accumulator layout), masks them and runs their
+// softmax alone, and writes P as bf16, which in that layout is already the
+// PV operand of its row block; after a second barrier every wave reads P of
+// all 64 rows for its PV.
+// With one wave per SIMD nothing overlaps a wave's phases but its own
+// instruction order, so a step's MFMA work is one basic block: PV of the
+// previous block, the loads of a later one, QK^T of this one, and the next
+// block's stage pieces written between the MFMAs.
+// The 256 threads split a block's loads (the key t >> 3: 16 latent bytes of
+// each 128-value block, 16 rope bytes and the key's 16 scale bytes each),
+// RING blocks ahead of the math in a register ring. The partial-S and P
+// areas are single: each is rewritten only after the barrier that ends the
+// reads of its previous contents.
+constexpr int kLdsWaves = 4;
 constexpr int kLdsRows = 64;                            // query rows per workgroup
+constexpr int kLdsRb = kLdsRows / 16;                   // 16-row blocks per wave
 constexpr int kStageKeys = 32;                          // keys per step
 // bf16 key row + 32 B: rows sit 8 banks apart, and the 16-byte pieces of rows
 // 4..7 (mod 8) are swapped in pairs (piece q -> q ^ 1), so 8 rows read at one
@@ -192,27 +198,29 @@ constexpr int kStageKeys = 32;                          // keys per step
 constexpr int kKRowBytes = 2 * (kLatent + kRope) + 32;
 constexpr int kStageBytes = kStageKeys * kKRowBytes;
 constexpr int kStages = 3;
-constexpr int kSpWaveBytes = 2 * 2 * 64 * 16;                    // partial S of a wave: [tt][rb][lane] f32x4
+constexpr int kSpWaveBytes = 2 * kLdsRb * 64 * 16;              // partial S of a wave: [tt][rb][lane] f32x4
 constexpr int kSpOffset = kStages * kStageBytes;
-constexpr int kPOffset = kSpOffset + kLdsWaves * kSpWaveBytes;  // P: [rg][rb][lane] 8 bf16
-constexpr int kStatOffset = kPOffset + 2 * 2 * 64 * 16;         // (max, sum) of the 64 rows
+constexpr int kPOffset = kSpOffset + kLdsWaves * kSpWaveBytes;  // P: [rb][lane] 8 bf16
+constexpr int kStatOffset = kPOffset + kLdsRb * 64 * 16;        // (max, sum) of the 64 rows
 constexpr int kFlagOffset = kStatOffset + kLdsRows * 8;          // restart flag (int)
 constexpr int kLdsBytes = kFlagOffset + 16;
+static_assert(kLdsBytes <= 160 * 1024, "one workgroup's LDS must fit the CU's 160 KB");
 constexpr float kFixedLog2 = 32.0f;  // p = exp2((s - m_run) c2) stays below 2^32
-constexpr int kAhead = 2;            // LDS operand pieces read ahead of their MFMAs
+constexpr int kQkAhead = 3;          // K pieces read ahead of their MFMAs (source order)
+constexpr int kPvAhead = 3;          // V^T tiles read ahead of their MFMAs (source order)
 
-// One thread's loads of one 32-key block: key t >> 4, latent bytes
-// 8 (t & 15) + 128 i (lat[i] lies in latent block i), rope bytes 8 (t & 15),
+// One thread's loads of one 32-key block: key t >> 3, latent bytes
+// 16 (t & 7) + 128 i (lat[i] lies in latent block i), rope bytes 16 (t & 7),
 // and the key's four block scales (fp32 bits).
 struct RawPiece {
-  uint2 lat[4];
-  uint2 rope;
+  uint4 lat[4];
+  uint4 rope;
   uint4 scl;
 };
 
 // Byte offset of byte `lane_off + c` of key row `row` in a stage (see
 // kKRowBytes) is krow_base(row, lane_off) + c for every c whose bit 4 is
-// clear (all the constant parts of the offsets below are multiples of 32).
+// clear (all the constant parts of the offsets below are multiples of 16).
 __device__ __forceinline__ int krow_base(int row, int lane_off) {
   return row * kKRowBytes + (lane_off ^ (((row >> 2) & 1) << 4));
 }
@@ -225,24 +233,18 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
       (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) uint8_t*)p);
 }
 
-// x from the lane 8 apart within its 16-lane row (DPP row rotate by 8)
-__device__ __forceinline__ float lane_xor8(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
-}
-// max / sum over the eight lanes that share lane & 7
-__device__ __forceinline__ float max_over8(float x) { return pair32(pair16(max2f(x, lane_xor8(x)), true), true); }
-__device__ __forceinline__ float sum_over8(float x) { return pair32(pair16(x + lane_xor8(x), false), false); }
+// max / sum over the four lanes r16 + 16 g4 (a row's lanes in the
+// accumulator layout)
+__device__ __forceinline__ float max_over4(float x) { return pair32(pair16(x, true), true); }
+__device__ __forceinline__ float sum_over4(float x) { return pair32(pair16(x, false), false); }
 
 template <bool CAUSAL_TAIL, int RING>
 __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int tile, uint8_t* lds) {
   const int t = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
+  const int q = __builtin_amdgcn_readfirstlane(t >> 6);  // wave = head-dim quarter (wave-uniform)
   const int lane = t & 63;
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
-  const int rg = w >> 2, q = w & 3;
-  const int rope_step = (q + 2 * rg) & 3;  // this wave's rope k-step, when below 2
-  const bool has_rope = rope_step < 2;
 
   const int4 wk = p.work[item];
   const int b = wk.x;
@@ -262,40 +264,34 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
   const int k_begin = p.bin_offsets ? wk.y : wk.y * kTileKeys;
   const int k_end = min(p.bin_offsets ? wk.z : wk.z * kTileKeys, L);
 
-  // rows of the row group in the MFMA layout: n = row0 + 16 rb + r16; a row
-  // group past the last row runs like the others (on zero query rows) and
-  // writes nothing
-  const int row0 = tile * kLdsRows + 32 * rg;
-  int qtok[2], qhead[2];
-  bool row_ok[2];
-  for (int rb = 0; rb < 2; ++rb) {
+  // rows in the MFMA layout: n = row0 + 16 rb + r16; rows past the last run
+  // like the others (on zero query rows) and write nothing
+  const int row0 = tile * kLdsRows;
+  int qtok[kLdsRb], qhead[kLdsRb];
+  bool row_ok[kLdsRb];
+  for (int rb = 0; rb < kLdsRb; ++rb) {
     const int n = row0 + 16 * rb + r16;
     row_ok[rb] = n < p.rows;
     const int qi = n / p.h_q;
     qtok[rb] = b * p.q_len + qi;
     qhead[rb] = n - qi * p.h_q;
   }
-  // the row this lane serves in the softmax: row 16 orb + orow of the group
-  // (rows 8 q .. 8 q + 7), keys 16 ott + okey .. + 3 of a block; those four
-  // values sit in lane olane of the QK^T accumulator layout (tile ott, row
-  // block orb), and their P in lane olane of the PV operand, k-slots 4 ott ..
-  const int orb = q >> 1, orow = 8 * (q & 1) + (lane & 7);
-  const int ott = lane >> 5, okey = 4 * ((lane >> 3) & 3);
-  const int olane = orow + 4 * okey;  // = orow + 16 * ((lane >> 3) & 3)
-  const int on = min(row0 + 16 * orb + orow, p.rows - 1);
+  // the row this wave owns in the softmax: row block q, row r16; this lane
+  // holds its keys 16 tt + 4 g4 + i
+  const int on = min(row0 + 16 * q + r16, p.rows - 1);
   const int olim = min(CAUSAL_TAIL ? L - p.q_len + on / p.h_q : L - 1, k_end - 1);
-  const int on_min = min(row0 + 16 * orb + 8 * (q & 1), p.rows - 1);  // first row this wave owns
+  const int on_min = min(row0 + 16 * q, p.rows - 1);  // first row this wave owns
   const int olim_min = min(CAUSAL_TAIL ? L - p.q_len + on_min / p.h_q : L - 1, k_end - 1);
   const float c2 = p.scale_log2e;
 
   // Q as the B operand of this wave's quarter of d_qk: k-step k < 4 holds
-  // q[n][128 q + 32 k + 8 g4 .. +7] (latent block q), k = 4 the rope k-step
-  bf16x8 qv[2][5];
-  for (int rb = 0; rb < 2; ++rb) {
+  // q[n][128 q + 32 k + 8 g4 .. +7] (latent block q), k = 4 rope k-step q & 1
+  bf16x8 qv[kLdsRb][5];
+  for (int rb = 0; rb < kLdsRb; ++rb) {
     const uint8_t* qrow = p.q + (int64_t)qtok[rb] * p.q_tok + (int64_t)qhead[rb] * p.q_head;
     for (int k = 0; k < 5; ++k) {
-      const int d = k < 4 ? 128 * q + 32 * k + 8 * g4 : kLatent + 32 * (rope_step & 1) + 8 * g4;
-      if (row_ok[rb] && (k < 4 || has_rope)) {
+      const int d = k < 4 ? 128 * q + 32 * k + 8 * g4 : kLatent + 32 * (q & 1) + 8 * g4;
+      if (row_ok[rb]) {
         qv[rb][k] = *reinterpret_cast<const bf16x8*>(qrow + 2 * d);
       } else {
         for (int e = 0; e < 8; ++e) qv[rb][k][e] = (__bf16)0.0f;
@@ -303,12 +299,12 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
     }
   }
 
-  f32x4 oacc[2][8];  // [row block][16-row tile mt]: O^T[128 q + 16 mt + 4 g4 + i][row 16 rb + r16]
-  // m_run: the reference max (raw-score units) of the row this lane serves,
-  // set by the row's first visible block and then fixed, so O is never
-  // rescaled inside the loop. P = exp2((s - m_run) c2) may grow up to
-  // 2^kFixedLog2, which bf16 P and the fp32 sums absorb. m_seen: the largest
-  // block max seen. l_part: this lane's share of the row sum.
+  f32x4 oacc[kLdsRb][8];  // [row block][16-row tile mt]: O^T[128 q + 16 mt + 4 g4 + i][row 16 rb + r16]
+  // m_run: the reference max (raw-score units) of the owned row, set by the
+  // row's first visible block and then fixed, so O is never rescaled inside
+  // the loop. P = exp2((s - m_run) c2) may grow up to 2^kFixedLog2, which
+  // bf16 P and the fp32 sums absorb. m_seen: the largest score this lane has
+  // seen. l_part: this lane's share of the row sum.
   float m_run = -INFINITY, m_seen = -INFINITY, l_part;
   // an LDS pointer (a generic one would make these FLAT accesses, whose waits
   // also wait for every global load in flight)
@@ -320,17 +316,17 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
   bool again;
-  // A block whose max would put some p past 2^kFixedLog2 (scores rising that
-  // far after a row's first visible block: pathological inputs only) sets the
-  // flag; the waves read it after the second barrier of every sixth block
-  // and after the last, all at the same point, and the workgroup runs the
-  // item again from its first key with each row's reference at m_seen. Each
-  // run gets further than the one before (the blocks it has seen can no
-  // longer pass the bound), so the runs end.
+  // A block with a score that would put its p past 2^kFixedLog2 (scores
+  // rising that far after a row's first visible block: pathological inputs
+  // only) sets the flag; the waves read it after the second barrier of every
+  // sixth block and after the last, all at the same point, and the workgroup
+  // runs the item again from its first key with each row's reference at the
+  // largest score seen. Each run gets further than the one before (the
+  // blocks it has seen can no longer pass the bound), so the runs end.
   do {
   again = false;
   l_part = 0.f;
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < kLdsRb; ++rb)
     for (int mt = 0; mt < 8; ++mt) oacc[rb][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (k_end > k_begin) {
@@ -343,12 +339,12 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
 
     // fetch u: the loads of block k_begin + 32u into ring slot u % RING, with
     // the pages from page slot u % 3 (loaded two fetches earlier); it loads
-    // the pages of fetch u + 2. Waves 0-3 load keys 0-15, waves 4-7 keys
+    // the pages of fetch u + 2. Waves 0-1 load keys 0-15, waves 2-3 keys
     // 16-31, so each wave reads one page per load.
     int pv[3];
     pv[0] = page_pair(k_begin);
     pv[1] = page_pair(k_begin + kStageKeys);
-    const int my_key = t >> 4, part = t & 15;
+    const int my_key = t >> 3, part = t & 7;
     // A load's address is the wave-uniform page base (scalar registers) plus a
     // 32-bit lane offset: the key's row inside the page times the row stride
     // (page_size * row stride < 2^30, as the host checks) plus the lane's
@@ -356,33 +352,51 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
     auto fetch = [&](RawPiece& r, int kb, const int ps) {
       const int pg0 = clamp_page(__builtin_amdgcn_readlane(pv[ps], 0));
       const int pg1 = clamp_page(__builtin_amdgcn_readlane(pv[ps], 1));
-      const int64_t pgk = (w >> 2) ? pg1 : pg0;
+      const int64_t pgk = (q >> 1) ? pg1 : pg0;
       const uint32_t key = (uint32_t)(min(kb + my_key, last_key) & pmask);
       const uint8_t* lat = p.lat + pgk * p.lat_page;
       const uint8_t* rope = p.rope + pgk * p.rope_page;
       const uint8_t* scl = p.scl + pgk * p.scl_page;
-      const uint32_t lat_off = key * (uint32_t)p.lat_row + 8u * part;
-      for (int i = 0; i < 4; ++i) r.lat[i] = *reinterpret_cast<const uint2*>(lat + (lat_off + 128u * i));
-      r.rope = *reinterpret_cast<const uint2*>(rope + (key * (uint32_t)p.rope_row + 8u * part));
+      const uint32_t lat_off = key * (uint32_t)p.lat_row + 16u * part;
+      for (int i = 0; i < 4; ++i) r.lat[i] = *reinterpret_cast<const uint4*>(lat + (lat_off + 128u * i));
+      r.rope = *reinterpret_cast<const uint4*>(rope + (key * (uint32_t)p.rope_row + 16u * part));
       r.scl = *reinterpret_cast<const uint4*>(scl + key * (uint32_t)p.scl_row);
       pv[(ps + 2) % 3] = page_pair(kb + 2 * kStageKeys);
     };
-    // The key row's bf16 latent pieces 16 i + part (codes 128 i + 8 part ..,
-    // so each 16-lane group stores 256 contiguous bytes), then its rope bytes
-    // 8 part. A wave whose keys all carry power-of-two scales (the record
-    // format) folds them in with the scaled convert; otherwise the wave takes
-    // the fp32 product (a uniform branch).
-    auto stage_in = [&](const RawPiece& r, uint8_t* st) {
+    // The key row's bf16 latent values 128 i + 16 part .. +15 (pieces 2 i and
+    // 2 i + 1 of this thread, 16 bytes each), then its rope bytes 16 part
+    // (piece 8). The power-of-two form (the record format: the scaled convert
+    // is exact) is always converted and written; a wave with a key whose
+    // scales are not all powers of two then rewrites the block's pieces with
+    // the fp32 product (a uniform branch after the writes, so the common path
+    // is one basic block with the MFMAs it is interleaved with).
+    auto convert = [&](const RawPiece& r, bf16x8 (&c)[8]) {
       const float sc[4] = {__uint_as_float(r.scl.x), __uint_as_float(r.scl.y), __uint_as_float(r.scl.z),
                            __uint_as_float(r.scl.w)};
-      if (__builtin_amdgcn_ballot_w64(!pow2_scales(r.scl)) == 0) {
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<bf16x8*>(st + krow_base(my_key, 256 * i + 16 * part)) = e4m3x8_times_pow2(r.lat[i], sc[i]);
-      } else {
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<bf16x8*>(st + krow_base(my_key, 256 * i + 16 * part)) = e4m3x8_times_any(r.lat[i], sc[i]);
+      for (int i = 0; i < 4; ++i) {
+        c[2 * i] = e4m3x8_times_pow2(half_of(r.lat[i], 0), sc[i]);
+        c[2 * i + 1] = e4m3x8_times_pow2(half_of(r.lat[i], 1), sc[i]);
       }
-      *reinterpret_cast<uint2*>(st + krow_base(my_key, 2 * kLatent + 8 * part)) = r.rope;
+    };
+    auto piece_at = [&](uint8_t* st, int k) -> uint8_t* {
+      return st + (k < 8 ? krow_base(my_key, 256 * (k >> 1) + 32 * part + 16 * (k & 1))
+                         : krow_base(my_key, 2 * kLatent + 16 * part));
+    };
+    auto write_piece = [&](uint8_t* st, const RawPiece& r, const bf16x8 (&c)[8], int k) {
+      if (k < 8)
+        *reinterpret_cast<bf16x8*>(piece_at(st, k)) = c[k];
+      else
+        *reinterpret_cast<uint4*>(piece_at(st, 8)) = r.rope;
+    };
+    auto stage_fixup = [&](const RawPiece& r, uint8_t* st) {
+      if (__builtin_amdgcn_ballot_w64(!pow2_scales(r.scl)) != 0) {
+        const float sc[4] = {__uint_as_float(r.scl.x), __uint_as_float(r.scl.y), __uint_as_float(r.scl.z),
+                             __uint_as_float(r.scl.w)};
+        for (int i = 0; i < 4; ++i) {
+          *reinterpret_cast<bf16x8*>(piece_at(st, 2 * i)) = e4m3x8_times_any(half_of(r.lat[i], 0), sc[i]);
+          *reinterpret_cast<bf16x8*>(piece_at(st, 2 * i + 1)) = e4m3x8_times_any(half_of(r.lat[i], 1), sc[i]);
+        }
+      }
     };
 
     // this lane's QK^T piece (key row r16 of a tile, bytes 16 g4 ..) and
@@ -390,78 +404,94 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
     // rows 16 apart share the swizzle
     const int qk_base = krow_base(r16, 16 * g4);
     const int tr_base = krow_base(4 * g4 + (r16 >> 2), 8 * (r16 & 3));
-    // K piece of tile tt, k-step k of this wave's quarter (k = 4: its rope step)
-    auto qk_piece = [&](const uint8_t* st, int tt, int k) -> bf16x8 {
-      const int off = k < 4 ? 2 * (128 * q + 32 * k) : 2 * (kLatent + 32 * (rope_step & 1));
+    // Each wave takes one of the four (tile, rope k-step) pairs: rope k-step
+    // q & 1 on tile tr = q >> 1, so every wave runs 36 QK^T MFMAs. It runs
+    // the other tile first (four latent k-steps), then tile tr (four latent
+    // k-steps and its rope step); piece i of that sequence:
+    const int tr_tile = q >> 1;
+    auto qk_piece = [&](const uint8_t* st, int i) -> bf16x8 {
+      const int tt = i < 4 ? 1 - tr_tile : tr_tile;
+      const int off = i < 8 ? 2 * (128 * q + 32 * (i & 3)) : 2 * (kLatent + 32 * (q & 1));
       return *reinterpret_cast<const bf16x8*>(st + qk_base + tt * 16 * kKRowBytes + off);
     };
-    // partial S (s[tt][rb]: S[key 16 tt + 4 g4 + i][row 16 rb + r16]) of the
-    // block in stage st over this wave's quarter of d_qk. The eight latent
-    // pieces are read kAhead ahead of their MFMAs; the two rope pieces first
-    // (every wave reads them, so no load sits in a branch).
-    auto qk_quarter = [&](const uint8_t* st, f32x4 (&s)[2][2]) {
-      const bf16x8 pr0 = qk_piece(st, 0, 4), pr1 = qk_piece(st, 1, 4);
-      bf16x8 pa[kAhead + 1];
-      for (int i = 0; i < kAhead; ++i) pa[i] = qk_piece(st, i >> 2, i & 3);
+    uint8_t* const sp_own = lds + kSpOffset + q * kSpWaveBytes;
+    auto put_s = [&](int tt, const f32x4 (&s)[kLdsRb]) {
+      for (int rb = 0; rb < kLdsRb; ++rb)
+        *reinterpret_cast<f32x4*>(sp_own + ((kLdsRb * tt + rb) * 64 + lane) * 16) = s[rb];
+    };
+    // partial S (sa: the first tile, sb: tile tr; S[key 16 tt + 4 g4 + i][row
+    // 16 rb + r16]) of the block in stage st over this wave's quarter of
+    // d_qk, written to this wave's partial-S area ([tt][rb][lane]); each K
+    // piece is read kQkAhead pieces ahead of its four MFMAs; the first
+    // tile's partial S is written under the second tile's first k-step. The
+    // next block's rope piece is staged at the start.
+    auto qk_quarter = [&](const uint8_t* st, uint8_t* st_next, const RawPiece& nr, const bf16x8 (&nc)[8]) {
+      f32x4 sa[kLdsRb], sb[kLdsRb];
+      bf16x8 pa[kQkAhead + 1];
+      for (int i = 0; i < kQkAhead; ++i) pa[i] = qk_piece(st, i);
+      write_piece(st_next, nr, nc, 8);
 #pragma unroll
-      for (int idx = 0; idx < 8; ++idx) {
-        const int tt = idx >> 2, k = idx & 3;
-        if (idx + kAhead < 8) pa[(idx + kAhead) % (kAhead + 1)] = qk_piece(st, (idx + kAhead) >> 2, (idx + kAhead) & 3);
-        for (int rb = 0; rb < 2; ++rb) {
-          const f32x4 c = k == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[tt][rb];
-          s[tt][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[idx % (kAhead + 1)], qv[rb][k], c, 0, 0, 0);
+      for (int i = 0; i < 9; ++i) {
+        if (i + kQkAhead < 9) pa[(i + kQkAhead) % (kQkAhead + 1)] = qk_piece(st, i + kQkAhead);
+        const bf16x8 k_op = pa[i % (kQkAhead + 1)];
+        for (int rb = 0; rb < kLdsRb; ++rb) {
+          const bf16x8 q_op = qv[rb][i < 8 ? (i & 3) : 4];
+          if (i < 4)
+            sa[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_op, q_op, i == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sa[rb],
+                                                             0, 0, 0);
+          else
+            sb[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_op, q_op, i == 4 ? f32x4{0.f, 0.f, 0.f, 0.f} : sb[rb],
+                                                             0, 0, 0);
         }
-        __builtin_amdgcn_sched_barrier(0);
+        if (i == 4) put_s(1 - tr_tile, sa);
       }
-      if (has_rope) {
-        for (int rb = 0; rb < 2; ++rb) {
-          s[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pr0, qv[rb][4], s[0][rb], 0, 0, 0);
-          s[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pr1, qv[rb][4], s[1][rb], 0, 0, 0);
-        }
-      }
+      put_s(tr_tile, sb);
     };
-    uint8_t* const sp_own = lds + kSpOffset + w * kSpWaveBytes;
-    auto put_s = [&](const f32x4 (&s)[2][2]) {
+    // S of the owned row at this lane's keys of both tiles: the partials of
+    // waves 0 .. 3 added in that order, masked
+    const uint8_t* const sp_row = lds + kSpOffset + (q * 64 + lane) * 16;
+    auto own_s = [&](int kb, f32x4 (&sv)[2]) {
+      f32x4 a[2][4];
       for (int tt = 0; tt < 2; ++tt)
-        for (int rb = 0; rb < 2; ++rb) *reinterpret_cast<f32x4*>(sp_own + ((2 * tt + rb) * 64 + lane) * 16) = s[tt][rb];
-    };
-    // S of this lane's four values: the partials of waves 4 rg + 0 .. 3 added
-    // in that order (the one wave that owns the row computes it), masked
-    const uint8_t* const sp_row = lds + kSpOffset + 4 * rg * kSpWaveBytes + ((2 * ott + orb) * 64 + olane) * 16;
-    auto own_s = [&](int kb) -> f32x4 {
-      f32x4 a = *reinterpret_cast<const f32x4*>(sp_row);
-      f32x4 b1 = *reinterpret_cast<const f32x4*>(sp_row + kSpWaveBytes);
-      f32x4 b2 = *reinterpret_cast<const f32x4*>(sp_row + 2 * kSpWaveBytes);
-      f32x4 b3 = *reinterpret_cast<const f32x4*>(sp_row + 3 * kSpWaveBytes);
-      // all four reads in flight before the first add (one LDS round trip)
-      asm volatile("" : "+v"(a), "+v"(b1), "+v"(b2), "+v"(b3));
-      f32x4 s = a + b1;
-      s += b2;
-      s += b3;
-      if (kb + kStageKeys - 1 > olim_min) {
-        for (int i = 0; i < 4; ++i)
-          if (kb + 16 * ott + okey + i > olim) s[i] = -INFINITY;
+        for (int w = 0; w < 4; ++w)
+          a[tt][w] = *reinterpret_cast<const f32x4*>(sp_row + w * kSpWaveBytes + tt * kLdsRb * 64 * 16);
+      for (int tt = 0; tt < 2; ++tt) {
+        f32x4 s = a[tt][0] + a[tt][1];
+        s += a[tt][2];
+        s += a[tt][3];
+        sv[tt] = s;
       }
-      return s;
+      if (kb + kStageKeys - 1 > olim_min) {
+        for (int tt = 0; tt < 2; ++tt)
+          for (int i = 0; i < 4; ++i)
+            if (kb + 16 * tt + 4 * g4 + i > olim) sv[tt][i] = -INFINITY;
+      }
     };
-    // softmax of the served row for this block: block max over its 32 keys,
-    // the reference, four exponentials, P to the PV operand area
-    uint8_t* const p_out = lds + kPOffset + ((2 * rg + orb) * 64 + olane) * 16 + 8 * ott;
-    auto softmax_own = [&](const f32x4& s, bool& overflow) {
-      const float mx = max_over8(max3f(max3f(s[0], s[1], s[2]), s[3], -INFINITY));
+    // softmax of the owned row for this block: the reference (only while
+    // some row of the wave has none yet, the row max over its four lanes),
+    // eight exponentials, P to the PV operand area of row block q
+    uint8_t* const p_out = lds + kPOffset + (q * 64 + lane) * 16;
+    auto softmax_own = [&](const f32x4 (&s)[2], bool& overflow) {
+      const float mx = max3f(max3f(s[0][0], s[0][1], s[0][2]), max3f(s[0][3], s[1][0], s[1][1]),
+                             max3f(s[1][2], s[1][3], -INFINITY));
       m_seen = max2f(m_seen, mx);
-      // the first visible block sets the reference (O and l are still zero)
-      m_run = m_run == -INFINITY ? mx : m_run;
+      if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY)) {
+        // the first visible block sets the reference (O and l are still zero)
+        const float row_mx = max_over4(mx);
+        m_run = m_run == -INFINITY ? row_mx : m_run;
+      }
       overflow = (mx - m_run) * c2 > kFixedLog2;
       // one fma per score: exp2(s c2 - m c2); no visible key yet: exp2(-inf) = 0
       const float off = m_run == -INFINITY ? 0.f : -m_run * c2;
-      float pr[4];
-      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, off));
-      l_part += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-      *reinterpret_cast<uint2*>(p_out) = uint2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+      float pr[8];
+      for (int tt = 0; tt < 2; ++tt)
+        for (int i = 0; i < 4; ++i) pr[4 * tt + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][i], c2, off));
+      l_part += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+      *reinterpret_cast<uint4*>(p_out) = uint4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                                               pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
     };
-    // O^T += V^T P^T for this wave's 128 d_v: V^T tile mt read kAhead tiles
-    // ahead of its MFMAs
+    // O^T += V^T P^T for this wave's 128 d_v: V^T tile mt read kPvAhead tiles
+    // ahead of its four MFMAs
     auto v_tile = [&](const uint8_t* st, int mt) -> bf16x8 {
       const uint8_t* v = st + tr_base + 2 * (128 * q + 16 * mt);
       const s16x4 lo = lds_read_tr16(v);
@@ -471,54 +501,82 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
       __builtin_memcpy(&a, &a16, 16);
       return a;
     };
-    const uint8_t* const p_in = lds + kPOffset + 2 * rg * 64 * 16 + lane * 16;
-    auto pv_quarter = [&](const uint8_t* st) {
-      const u32x4 pb[2] = {*reinterpret_cast<const u32x4*>(p_in), *reinterpret_cast<const u32x4*>(p_in + 64 * 16)};
-      bf16x8 va[kAhead + 1];
-      for (int i = 0; i < kAhead; ++i) va[i] = v_tile(st, i);
+    const uint8_t* const p_in = lds + kPOffset + lane * 16;
+    // PV of the block in stage st; when given the next block's converted
+    // pieces, one of them is written to st_next after each V^T tile
+    auto pv_quarter = [&](const uint8_t* st, uint8_t* st_next, const RawPiece* nr, const bf16x8 (*nc)[8]) {
+      u32x4 pb[kLdsRb];
+      for (int rb = 0; rb < kLdsRb; ++rb) pb[rb] = *reinterpret_cast<const u32x4*>(p_in + rb * 64 * 16);
+      bf16x8 va[kPvAhead + 1];
+      for (int i = 0; i < kPvAhead; ++i) va[i] = v_tile(st, i);
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
-        if (mt + kAhead < 8) va[(mt + kAhead) % (kAhead + 1)] = v_tile(st, mt + kAhead);
-        for (int rb = 0; rb < 2; ++rb)
-          oacc[rb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mt % (kAhead + 1)],
+        if (mt + kPvAhead < 8) va[(mt + kPvAhead) % (kPvAhead + 1)] = v_tile(st, mt + kPvAhead);
+        for (int rb = 0; rb < kLdsRb; ++rb)
+          oacc[rb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mt % (kPvAhead + 1)],
                                                                 __builtin_bit_cast(bf16x8, pb[rb]), oacc[rb][mt], 0, 0, 0);
+        if (nc) write_piece(st_next, *nr, *nc, mt);
       }
     };
 
-    // Two barriers per step. Block j: fetched in step j - RING, staged into
-    // stage j % 3 in step j - 1. In step j: its partial S is written (with
-    // stage j + 1), B1; the owners reduce, run the softmax and write P, B2;
-    // then PV. Rounds of 6 steps keep the ring and stage indices
-    // compile-time; the loop leaves after the last block's step (a uniform
-    // branch, so every wave meets the same barriers).
-    static_assert(6 % RING == 0, "a round of 6 steps must hold whole rings");
+    // Two barriers per step. Block j: fetched in step j - RING, converted and
+    // staged into stage (j % 3) in step j - 1. Step j: PV of block j - 1,
+    // the loads of block j + RING, QK^T of block j with its partial S
+    // written, block j + 1's pieces written between them (one basic block),
+    // B1; the owners reduce, run the softmax and write P, B2. Stage j is
+    // read by QK^T in step j and by PV in step j + 1 and rewritten in step
+    // j + 2, after the barriers of step j + 1. Step 0 has no PV; rounds of 6
+    // steps from step 1 on keep the ring and stage indices compile-time; PV
+    // of the last block follows the loop.
+    static_assert(RING == 2, "the step indices below assume two blocks in flight");
     constexpr int kRound = 6;
     const int nblocks = (k_end - k_begin + kStageKeys - 1) / kStageKeys;
     RawPiece ring[RING];
-    f32x4 sv[2][2];
-#pragma unroll
-    for (int u = 0; u < RING; ++u) {
-      fetch(ring[u], k_begin + u * kStageKeys, u % 3);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    stage_in(ring[0], lds);
+    bf16x8 nc[8];
+    fetch(ring[0], k_begin, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(ring[1], k_begin + kStageKeys, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    convert(ring[0], nc);
+    for (int k = 0; k < 9; ++k) write_piece(lds, ring[0], nc, k);
+    stage_fixup(ring[0], lds);
     barrier();
-    const int rounds = (nblocks + kRound - 1) / kRound;
+    auto softmax_step = [&](int kb) {
+      f32x4 sv[2];
+      own_s(kb, sv);
+      bool overflow;
+      softmax_own(sv, overflow);
+      if (__builtin_amdgcn_ballot_w64(overflow) && lane == 0) *restart_flag = 1;
+    };
+    // step 0
+    {
+      fetch(ring[0], k_begin + RING * kStageKeys, 2);
+      convert(ring[1], nc);
+      for (int k = 0; k < 8; ++k) write_piece(lds + kStageBytes, ring[1], nc, k);
+      qk_quarter(lds, lds + kStageBytes, ring[1], nc);
+      stage_fixup(ring[1], lds + kStageBytes);
+      barrier();
+      softmax_step(k_begin);
+      barrier();
+    }
+    const int rounds = (nblocks - 1 + kRound - 1) / kRound;
     for (int r = 0; r < rounds; ++r) {
 #pragma unroll
       for (int s = 0; s < kRound; ++s) {
-        const int j = r * kRound + s;
+        const int j = r * kRound + s + 1;
         if (j >= nblocks) goto loop_done;
         const int kb = k_begin + j * kStageKeys;
-        fetch(ring[s % RING], kb + RING * kStageKeys, (s + RING) % 3);
-        const uint8_t* st = lds + (s % 3) * kStageBytes;
-        qk_quarter(st, sv);
-        put_s(sv);
-        stage_in(ring[(s + 1) % RING], lds + ((s + 1) % 3) * kStageBytes);
+        RawPiece& nr = ring[s & 1];  // block j + 1
+        uint8_t* const st_prev = lds + (s % 3) * kStageBytes;
+        uint8_t* const st_cur = lds + ((s + 1) % 3) * kStageBytes;
+        uint8_t* const st_next = lds + ((s + 2) % 3) * kStageBytes;
+        fetch(ring[(s + 1) & 1], kb + RING * kStageKeys, s % 3);
+        convert(nr, nc);
+        pv_quarter(st_prev, st_next, &nr, &nc);
+        qk_quarter(st_cur, st_next, nr, nc);
+        stage_fixup(nr, st_next);
         barrier();
-        bool overflow;
-        softmax_own(own_s(kb), overflow);
-        if (__builtin_amdgcn_ballot_w64(overflow) && lane == 0) *restart_flag = 1;
+        softmax_step(kb);
         barrier();
         // the flag is read once per round: a block past the bound only fills
         // O, l and P with values the restart throws away
@@ -526,29 +584,33 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
           again = true;
           goto item_end;
         }
-        pv_quarter(st);
       }
     }
   loop_done:
-    if (__builtin_amdgcn_readfirstlane(*restart_flag)) again = true;
+    if (__builtin_amdgcn_readfirstlane(*restart_flag)) {
+      again = true;
+    } else {
+      const int jl = nblocks - 1;
+      pv_quarter(lds + (jl % 3) * kStageBytes, nullptr, nullptr, nullptr);
+    }
   }
 item_end:
   if (again) {
     barrier();  // every wave has read the flag
     if (t == 0) *restart_flag = 0;
-    m_run = m_seen;
+    m_run = max_over4(m_seen);
   }
   } while (again);
 
   // ---- epilogue: the owners publish each row's (max, sum); every wave
   // writes its d_v quarter of O; LSE / (max, sum) from quarter 0
-  const float l_row = sum_over8(l_part);
+  const float l_row = sum_over4(l_part);
   float2* const stat = reinterpret_cast<float2*>(lds + kStatOffset);
-  if (((lane >> 3) & 7) == 0) stat[32 * rg + 16 * orb + orow] = float2{m_run == -INFINITY ? -INFINITY : m_run * p.scale, l_row};
+  if (g4 == 0) stat[16 * q + r16] = float2{m_run == -INFINITY ? -INFINITY : m_run * p.scale, l_row};
   barrier();
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < kLdsRb; ++rb) {
     if (!row_ok[rb]) continue;
-    const float2 ml = stat[32 * rg + 16 * rb + r16];
+    const float2 ml = stat[16 * rb + r16];
     const float m_nat = ml.x, l = ml.y;
     const int64_t stat_row = (int64_t)b * p.rows + row0 + 16 * rb + r16;
     const int d0 = 128 * q + 4 * g4;
@@ -589,7 +651,7 @@ __device__ __forceinline__ void xcd_item_tile(int id, int units, int tiles, int&
 constexpr int kLdsRing = 2;  // raw blocks in flight per thread
 
 template <bool CAUSAL_TAIL>
-__global__ __launch_bounds__(64 * kLdsWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * kLdsWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_lds_kernel(MlaParams p, int units, int tiles) {
   extern __shared__ __attribute__((aligned(16))) uint8_t mla_stage_lds[];
   if (threadIdx.x == 0) *reinterpret_cast<int*>(mla_stage_lds + kFlagOffset) = 0;
