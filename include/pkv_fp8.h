@@ -237,17 +237,59 @@ pkv_status pkv_plan_queued(const int32_t* seq_lens, int32_t num_seqs, int32_t h_
  * trigger of the decode form: 1.12 for the latent cache with rows >= 64 (its
  * multi-token form, measured on this part), 1.5 otherwise; always
  * PKV_PLAN_WAVE for the fp4, fp6 and NVFP4 caches (one-item form only).
+ * With four kv heads and at most 16 rows (e4m3, fp4 and fp6 caches) the
+ * balance comes from PKV_PLAN_PAIRED (pkv_plan_paired) instead, whatever the
+ * imbalance: it runs the one-item form, and where the lengths are even it
+ * pairs nothing and equals the one-wave plan (measured on this part, decode
+ * one-wave -> paired on the fully-fp8 batch: e4m3 169.3 -> 165.7 us, fp4
+ * 103.9 -> 94.9, fp6 168 -> 152; NVFP4 154.2 -> 161.3, so NVFP4 stays on
+ * PKV_PLAN_WAVE).
  *
  * seq_lens   host int32[num_seqs]
  * work       host int32[num_work][4] (seq, tile_begin, tile_end, split_slot)
- * kv_format  PKV_KV_*; rows = q_len * h_q / h_k (packed query rows)
- * plan_out   PKV_PLAN_WAVE or PKV_PLAN_BALANCED; imbalance_out may be NULL
- * Errors: INVALID_ARG for NULL pointers, num_seqs < 1, num_work < 0, rows < 1.
+ * kv_format  PKV_KV_*; h_k kv heads; rows = q_len * h_q / h_k (packed query rows)
+ * plan_out   PKV_PLAN_WAVE, PKV_PLAN_BALANCED or PKV_PLAN_PAIRED; imbalance_out
+ *            may be NULL
+ * Errors: INVALID_ARG for NULL pointers, num_seqs < 1, num_work < 0, rows < 1,
+ * h_k < 1.
  */
 #define PKV_PLAN_WAVE 0
 #define PKV_PLAN_BALANCED 1
+#define PKV_PLAN_PAIRED 2
 pkv_status pkv_plan_pick(const int32_t* seq_lens, int32_t num_seqs, const int32_t* work, int32_t num_work,
-                         int32_t kv_format, int32_t rows, int32_t* plan_out, float* imbalance_out);
+                         int32_t kv_format, int32_t h_k, int32_t rows, int32_t* plan_out, float* imbalance_out);
+
+/*
+ * Paired plan (this library's own planner; not from the pages): the work
+ * items of the occupancy-pinned rule (pkv_plan_split_kv) for a chunk of c
+ * tiles, run two per workgroup. With tiles_b = max(1, ceil(L_b / 128)) and
+ * T = max_b tiles_b, c is the smallest value >= ceil(T / max_splits) for
+ * which the n = sum_b ceil(tiles_b / c) items fit 2 * pair_slots places and,
+ * the items sorted longest first (ties in construction order: sequence,
+ * then piece) and padded with empty items to 2 * pair_slots, item k and item
+ * 2 * pair_slots - 1 - k together hold at most c tiles for every
+ * k < pair_slots. Entries 2k and 2k+1 of work_out are the two items of
+ * workgroup k, k < min(pair_slots, n); an empty item is (0, 0, 0, 0).
+ * Run the decode with work_pairs = 1. pair_slots: the workgroups of two
+ * items that run at once (one per CU for four kv heads: 8 waves).
+ *
+ * Why: with one item per workgroup, sequences shorter than the chunk leave
+ * CUs idle while the longest chunks stream at one CU's rate; pairing the
+ * shortest items frees places for a smaller chunk (measured on the
+ * fully-fp8 workload: 171 -> 166-167 us).
+ *
+ * seq_lens      host int32[num_seqs], >= 0
+ * work_out      host int32[work_cap][4] (seq, tile_begin, tile_end, split_slot)
+ * n_splits_out  host int32[num_seqs]
+ * Errors: INVALID_ARG for NULL arrays, num_seqs < 1, pair_slots < 1,
+ * max_splits < 1, negative lengths; UNSUPPORTED for max_splits > PKV_MAX_SPLITS
+ * or when no chunk satisfies the rule (more sequences than the pairs can
+ * hold at one chunk each); CAPACITY when 2 * min(pair_slots, n) > work_cap.
+ * info (optional): num_work = 2 * min(pair_slots, n), num_real = n,
+ * chunk_tiles = c, slots = 2 * pair_slots, max_n_splits, num_bins = 0.
+ */
+pkv_status pkv_plan_paired(const int32_t* seq_lens, int32_t num_seqs, int32_t pair_slots, int32_t max_splits,
+                           int32_t* work_out, int32_t work_cap, int32_t* n_splits_out, pkv_plan_info* info);
 
 /* ------------------------------------------------------------------------ */
 /* Decode launch arguments                                                   */
@@ -381,6 +423,11 @@ typedef struct pkv_decode_args {
    * (pkv_plan_split_kv). The balanced and queued plans are in keys whatever
    * this says. e4m3 and narrow caches only. */
   int32_t work_in_keys;
+  /* 1: `work` holds pairs (pkv_plan_paired): workgroup k runs entries 2k and
+   * 2k+1 with one wave per (entry, kv head), num_work even. Needs h_k = 4,
+   * q_len * h_q / h_k <= 16, an e4m3 or narrow cache, no bin_offsets and
+   * work_in_keys = 0. 0: one entry per workgroup. */
+  int32_t work_pairs;
 } pkv_decode_args;
 
 /* Bytes of split workspace: max_splits * num_seqs * h_k * n_rows * (d_v + 2)

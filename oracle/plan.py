@@ -240,3 +240,42 @@ def plan_even(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16):
         work.extend((b, BALANCE_BLOCK_KEYS * cuts[j], BALANCE_BLOCK_KEYS * cuts[j + 1], j) for j in range(k))
     work.sort(key=lambda w: w[1] - w[2])  # longest first; sort is stable
     return work, n_splits, c, slots
+
+
+def plan_paired(seq_lens, pair_slots, max_splits=16):
+    """Paired plan (the library's own planner, not the pages'): the chunks of
+    the occupancy-pinned rule above, two per workgroup. For a candidate chunk
+    c (in 128-key tiles), sequence b becomes ceil(tiles_b / c) pieces of c
+    tiles (the last one shorter). The pieces are ranked longest first (equal
+    lengths in construction order: sequence, then piece) and the ranking is
+    padded with empty items to 2 * pair_slots places; workgroup k gets places
+    k and 2 * pair_slots - 1 - k. The chunk is the first c counting up from
+    ceil(T / max_splits) for which the pieces fit the places and no
+    workgroup gets more than c tiles. Returns (work as a flat list of
+    2 * min(pair_slots, n) items (seq, tile_begin, tile_end, split_slot),
+    the two items of workgroup k at 2k and 2k + 1; n_splits; chunk)."""
+    seq_lens = [int(x) for x in seq_lens]
+    if not seq_lens:
+        raise ValueError("empty batch")
+    if any(x < 0 for x in seq_lens):
+        raise ValueError("negative sequence length")
+    if min(pair_slots, max_splits) < 1:
+        raise ValueError("sizes must be positive")
+    tiles = [max(1, _ceil_div(L, TILE_KEYS)) for L in seq_lens]
+    places = 2 * pair_slots
+    size = lambda item: item[2] - item[1]  # noqa: E731
+    for chunk in range(_ceil_div(max(tiles), max_splits), max(tiles) + 1):
+        pieces = [(b, s, min(s + chunk, t), j)
+                  for b, t in enumerate(tiles) for j, s in enumerate(range(0, t, chunk))]
+        if len(pieces) > places:
+            continue
+        ranked = [p for _, p in sorted(enumerate(pieces), key=lambda ip: (-size(ip[1]), ip[0]))]
+        ranked += [(0, 0, 0, 0)] * (places - len(ranked))
+        if all(size(ranked[k]) + size(ranked[places - 1 - k]) <= chunk for k in range(pair_slots)):
+            break
+    else:
+        raise ValueError("no chunk puts the batch into pairs of at most one chunk")
+    work = []
+    for k in range(min(pair_slots, len(pieces))):
+        work += [ranked[k], ranked[places - 1 - k]]
+    return work, [_ceil_div(t, chunk) for t in tiles], chunk

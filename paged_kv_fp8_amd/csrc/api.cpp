@@ -103,6 +103,16 @@ pkv_status check_pointers(const pkv_decode_args* a, bool for_merge) {
   if (a->work_in_keys != 0 && a->work_in_keys != 1)
     return fail(PKV_ERR_INVALID_ARG, "work_in_keys=%d must be 0 or 1", a->work_in_keys);
   if (a->work_in_keys && mla) return fail(PKV_ERR_UNSUPPORTED, "latent cache: plans in 128-key tiles only");
+  if (a->work_pairs != 0 && a->work_pairs != 1)
+    return fail(PKV_ERR_INVALID_ARG, "work_pairs=%d must be 0 or 1", a->work_pairs);
+  if (a->work_pairs) {
+    if (mla || a->h_k != 4 || a->q_len * (a->h_q / a->h_k) > 16)
+      return fail(PKV_ERR_UNSUPPORTED, "work_pairs: built for four kv heads of at most 16 rows (h_k=%d, rows=%d)",
+                  a->h_k, a->q_len * (a->h_q / a->h_k));
+    if (a->bin_offsets || a->queue || a->work_in_keys)
+      return fail(PKV_ERR_INVALID_ARG, "work_pairs: a pkv_plan_paired plan (no bins, queue or key ranges)");
+    if (a->num_work % 2) return fail(PKV_ERR_INVALID_ARG, "work_pairs: num_work=%d must be even", a->num_work);
+  }
   if (a->kv_format == PKV_KV_NVFP4) {
     if (!a->k_group_scale || !a->v_group_scale)
       return fail(PKV_ERR_INVALID_ARG, "NVFP4 cache: k_group_scale and v_group_scale must be non-NULL");

@@ -98,6 +98,7 @@ struct GqaParams {
   int64_t ks_page, ks_row, ks_head;  // bytes
   const uint8_t* vs;
   int64_t vs_page, vs_row, vs_head;
+  int paired;  // work in pairs: workgroup x runs items 2x, 2x + 1 (eight waves, four kv heads)
 };
 
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint2 x) {
@@ -944,7 +945,7 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
         else
           process_block<FP8Q, NB, kQLds>(ring[s], kb, q, qlds, st, lim, lim_min, c2, g4);
       }
-      if (HW == 8) keep_pace(progress, wave, round_base + r, lane);
+      if (HW == 8 && !p.paired) keep_pace(progress, wave, round_base + r, lane);
     }
     round_base += rounds;
   }
@@ -1380,10 +1381,15 @@ void gqa_decode_kernel(GqaParams p) {
     if (lane == 0) progress[threadIdx.x >> 6] = -1;
     __syncthreads();
   }
-  const int g = __builtin_amdgcn_readfirstlane(blockIdx.y * HW + (threadIdx.x >> 6));  // wave-uniform
+  int g = __builtin_amdgcn_readfirstlane(blockIdx.y * HW + (threadIdx.x >> 6));  // wave-uniform
   // one-item form: the work item and q-row tile of this workgroup
   int item = blockIdx.x, tile = blockIdx.z;
   if (p.xcd_tiles) xcd_item_tile(blockIdx.x, p.num_work, p.q_tiles, item, tile);
+  if (HW == 8 && p.paired) {  // paired plan: waves 0-3 run item 2x, waves 4-7 item 2x + 1 (kv heads 0-3 each)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    item = 2 * blockIdx.x + (wave >> 2);
+    g = wave & 3;
+  }
   if constexpr (KVF != 0) {  // packed narrow K/V: the one-item form
     int round_base = 0;
     if (g < p.h_k) gqa_decode_item<FP8Q, NB, CAUSAL_TAIL, STAGES, HW, KVF>(p, item, tile, lane, g, progress, round_base);
@@ -1525,6 +1531,9 @@ GqaVariant gqa_variant(const pkv_decode_args& a) {
   const int cap = v.n_blocks == 1 ? 8 : 4;
   v.heads_per_wg = 1;
   while (v.heads_per_wg * 2 <= cap && a.h_k % (v.heads_per_wg * 2) == 0) v.heads_per_wg *= 2;
+  // paired plan (four kv heads, one row block): eight waves, two items
+  v.paired = a.work_pairs != 0;
+  if (v.paired) v.heads_per_wg = 8;
   return v;
 }
 
@@ -1619,8 +1628,10 @@ hipError_t gqa_launch(const pkv_decode_args& a, const GqaVariant& v, hipStream_t
   const int hw = v.heads_per_wg;
   p.q_tiles = tiles;
   p.xcd_tiles = !a.bin_offsets && tiles > 1;
+  p.paired = v.paired ? 1 : 0;
   dim3 grid(a.bin_offsets ? a.num_bins : a.num_work, (a.h_k + hw - 1) / hw, tiles);  // bins: balanced or queued plan
   if (p.xcd_tiles) grid = dim3(a.num_work * tiles, (a.h_k + hw - 1) / hw, 1);
+  if (v.paired) grid = dim3(a.num_work / 2, 1, 1);  // one q-row tile (16 rows), two items per workgroup
   void* args[] = {&p};
   return hipLaunchKernel(select_kernel(v), grid, dim3(64 * hw), args, gqa_dyn_lds(v), stream);
 }

@@ -23,6 +23,7 @@ struct GqaVariant {
   int heads_per_wg; // kv heads (one wave each) per workgroup
   bool stream;      // balanced plan: each workgroup streams the items of its bin
   int kvf;          // K/V format: 0 = e4m3, else the packed narrow format's PKV_KV_* value (one-item form only)
+  bool paired;      // paired plan: two work items per workgroup, one wave per (item, kv head)
 };
 
 // Packed narrow K/V formats (fp4 e2m1, fp6 e2m3 / e3m2).

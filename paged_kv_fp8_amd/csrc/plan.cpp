@@ -368,11 +368,94 @@ extern "C" pkv_status pkv_plan_queued(const int32_t* seq_lens, int32_t num_seqs,
 // imbalanced, max / avg >= 1.5. Reading: the lengths are those the one-wave
 // plan hands to its workgroups (its work items, which already cut long
 // sequences into chunks), in 32-key blocks of keys that exist.
+// Paired plan (this library's own; see pkv_fp8.h): two work items per
+// workgroup. The items of chunk c are those of the occupancy-pinned rule
+// above; sorted longest first (ties in construction order) and padded with
+// empty items to 2 * pair_slots entries, item k shares workgroup k with item
+// 2 * pair_slots - 1 - k. The chunk is the smallest c >= ceil(T / max_splits)
+// whose items fit (n <= 2 * pair_slots) and whose every pair holds at most c
+// tiles, so that no workgroup carries more than a longest item alone.
+extern "C" pkv_status pkv_plan_paired(const int32_t* seq_lens, int32_t num_seqs, int32_t pair_slots,
+                                      int32_t max_splits, int32_t* work_out, int32_t work_cap,
+                                      int32_t* n_splits_out, pkv_plan_info* info) {
+  using pkv::fail;
+  if (!seq_lens || !work_out || !n_splits_out) return fail(PKV_ERR_INVALID_ARG, "plan paired: NULL array");
+  if (num_seqs < 1) return fail(PKV_ERR_INVALID_ARG, "plan paired: num_seqs=%d < 1", num_seqs);
+  if (pair_slots < 1 || max_splits < 1 || work_cap < 0)
+    return fail(PKV_ERR_INVALID_ARG, "plan paired: pair_slots=%d and max_splits=%d must be >= 1, work_cap=%d >= 0",
+                pair_slots, max_splits, work_cap);
+  if (max_splits > PKV_MAX_SPLITS)
+    return fail(PKV_ERR_UNSUPPORTED, "plan paired: max_splits=%d > %d", max_splits, PKV_MAX_SPLITS);
+  std::vector<int64_t> tiles(num_seqs);
+  int64_t t_max = 1;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    if (seq_lens[b] < 0) return fail(PKV_ERR_INVALID_ARG, "plan paired: seq_lens[%d]=%d < 0", b, seq_lens[b]);
+    tiles[b] = std::max<int64_t>(1, ceil_div(seq_lens[b], kTileKeys));
+    t_max = std::max(t_max, tiles[b]);
+  }
+  const int64_t room = 2 * (int64_t)pair_slots;
+  const int64_t lo = ceil_div(t_max, max_splits);
+  std::vector<Item> items;
+  auto build = [&](int64_t c) {
+    items.clear();
+    for (int32_t b = 0; b < num_seqs; ++b)
+      for (int64_t j = 0; j * c < tiles[b]; ++j)
+        items.push_back({b, (int32_t)(j * c), (int32_t)std::min((j + 1) * c, tiles[b]), (int32_t)j});
+    std::stable_sort(items.begin(), items.end(),
+                     [](const Item& x, const Item& y) { return (x.end - x.begin) > (y.end - y.begin); });
+  };
+  auto len_at = [&](int64_t i) -> int64_t { return i < (int64_t)items.size() ? items[i].end - items[i].begin : 0; };
+  int64_t chunk = -1;
+  for (int64_t c = lo; c <= t_max && chunk < 0; ++c) {
+    int64_t n = 0;
+    for (int64_t t : tiles) n += ceil_div(t, c);
+    if (n > room) continue;
+    build(c);
+    bool ok = true;
+    for (int64_t k = 0; k < pair_slots && ok; ++k) ok = len_at(k) + len_at(room - 1 - k) <= c;
+    if (ok) chunk = c;
+  }
+  if (chunk < 0)
+    return fail(PKV_ERR_UNSUPPORTED, "plan paired: no chunk puts %d sequences into %d pairs of at most one chunk",
+                num_seqs, pair_slots);
+  const int64_t n = (int64_t)items.size();
+  const int64_t pairs = std::min<int64_t>(pair_slots, n);
+  if (2 * pairs > work_cap)
+    return fail(PKV_ERR_CAPACITY, "plan paired: %lld work entries > work_cap=%d", (long long)(2 * pairs), work_cap);
+  int32_t max_ns = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    n_splits_out[b] = (int32_t)ceil_div(tiles[b], chunk);
+    max_ns = std::max(max_ns, n_splits_out[b]);
+  }
+  auto put = [&](int64_t e, int64_t i) {
+    const Item it = i < n ? items[i] : Item{0, 0, 0, 0};
+    work_out[4 * e + 0] = it.seq;
+    work_out[4 * e + 1] = it.begin;
+    work_out[4 * e + 2] = it.end;
+    work_out[4 * e + 3] = it.slot;
+  };
+  for (int64_t k = 0; k < pairs; ++k) {
+    put(2 * k, k);
+    put(2 * k + 1, room - 1 - k);
+  }
+  if (info) {
+    info->num_work = (int32_t)(2 * pairs);
+    info->num_real = (int32_t)n;
+    info->chunk_tiles = (int32_t)chunk;
+    info->slots = (int32_t)std::min<int64_t>(room, INT32_MAX);
+    info->max_n_splits = max_ns;
+    info->num_bins = 0;
+    info->num_dynamic = 0;
+  }
+  return PKV_OK;
+}
+
 extern "C" pkv_status pkv_plan_pick(const int32_t* seq_lens, int32_t num_seqs, const int32_t* work, int32_t num_work,
-                                    int32_t kv_format, int32_t rows, int32_t* plan_out, float* imbalance_out) {
+                                    int32_t kv_format, int32_t h_k, int32_t rows, int32_t* plan_out,
+                                    float* imbalance_out) {
   using pkv::fail;
   if (!seq_lens || !work || !plan_out) return fail(PKV_ERR_INVALID_ARG, "plan pick: NULL argument");
-  if (num_seqs < 1 || num_work < 0 || rows < 1) return fail(PKV_ERR_INVALID_ARG, "plan pick: bad sizes");
+  if (num_seqs < 1 || num_work < 0 || rows < 1 || h_k < 1) return fail(PKV_ERR_INVALID_ARG, "plan pick: bad sizes");
   int64_t total = 0, longest = 0, items = 0;
   for (int32_t i = 0; i < num_work; ++i) {
     const int32_t* w = work + 4 * i;
@@ -393,6 +476,14 @@ extern "C" pkv_status pkv_plan_pick(const int32_t* seq_lens, int32_t num_seqs, c
                       kv_format == PKV_KV_NVFP4;
   const float trigger = (kv_format == PKV_KV_MLA && rows >= 64) ? 1.12f : 1.5f;
   *plan_out = !narrow && ratio >= trigger ? PKV_PLAN_BALANCED : PKV_PLAN_WAVE;
+  // four kv heads and one 16-row block: the paired plan, which the one-item
+  // form runs at one eight-wave workgroup per CU (the streaming form behind
+  // the balanced plan spends more per block than it gains). Measured on the
+  // fully-fp8 batch, decode us one-wave -> paired: e4m3 169.3 -> 165.7, fp4
+  // 103.9 -> 94.9, fp6 168 -> 152; NVFP4, whose one-wave plan already runs
+  // two waves per SIMD on a two-block ring, 154.2 -> 161.3, so it keeps the
+  // one-wave plan
+  if (kv_format != PKV_KV_MLA && kv_format != PKV_KV_NVFP4 && h_k == 4 && rows <= 16) *plan_out = PKV_PLAN_PAIRED;
   if (imbalance_out) *imbalance_out = ratio;
   return PKV_OK;
 }

@@ -50,10 +50,12 @@ class PagedDecode:
     lse          (num_seqs, h_k, q_len*h_r) fp32 contiguous output
     plan_seq_lens host lengths the plan is made for (default: seq_lens);
                  the device seq_lens may be shorter at run time.
-    plan         "auto" (default): the one-wave plan, or the balanced plan
-                 when pkv_plan_pick finds the one-wave plan's items
-                 imbalanced (force_splits / pad_to / min_chunk_tiles keep
-                 the one-wave plan); "wave", "even", "balanced", "queued".
+    plan         "auto" (default): what pkv_plan_pick picks: the one-wave
+                 plan, the balanced plan when its items are imbalanced, or
+                 the paired plan (four kv heads, one 16-row block; the
+                 one-wave plan when no chunk pairs the batch);
+                 force_splits / pad_to / min_chunk_tiles keep the one-wave
+                 plan. Or "wave", "even", "balanced", "queued", "paired".
     """
 
     def __init__(self, *, q, block_table, seq_lens, o, lse, q_len, softmax_scale, k_cache=None, v_cache=None,
@@ -117,13 +119,25 @@ class PagedDecode:
         self.bin_offsets = None
         self.queue = None
         self.imbalance = None
-        if plan == "auto":  # the one-wave plan, or the balanced plan when its items are imbalanced
+        if plan == "auto":  # the one-wave plan, or the balanced or paired plan (pkv_plan_pick)
             work, n_splits, info = native.plan_split_kv(lens, h_k, n_q_tiles, cu, self.wg_per_cu, max_splits,
                                                         force_splits, min_chunk_tiles, pad_to)
-            pick, self.imbalance = native.plan_pick(lens, work, a.kv_format, q_len * (h_q // h_k))
+            pick, self.imbalance = native.plan_pick(lens, work, a.kv_format, h_k, q_len * (h_q // h_k))
             wave_knobs = force_splits or pad_to or min_chunk_tiles != 1
-            plan = "balanced" if pick == native.PKV_PLAN_BALANCED and not wave_knobs else "wave"
-        if plan == "balanced":  # contiguous equal shares, one per resident workgroup
+            plan = "wave"
+            if pick == native.PKV_PLAN_BALANCED and not wave_knobs:
+                plan = "balanced"
+            elif pick == native.PKV_PLAN_PAIRED and not wave_knobs:
+                try:  # no chunk may pair the batch (more sequences than pairs): keep the one-wave plan
+                    work, n_splits, info = native.plan_paired(lens, cu, max_splits)
+                    plan = "paired"
+                except native.PkvError:
+                    pass
+        if plan == "paired" and self.imbalance is None:  # two items per eight-wave workgroup, one per CU
+            work, n_splits, info = native.plan_paired(lens, cu, max_splits)
+        if plan == "paired":
+            a.work_pairs = 1
+        elif plan == "balanced":  # contiguous equal shares, one per resident workgroup
             work, n_splits, offs, info = native.plan_balanced(lens, h_k, n_q_tiles, cu, self.wg_per_cu, max_splits)
             self.bin_offsets = torch.from_numpy(offs).to(dev)
             a.bin_offsets, a.num_bins = _ptr(self.bin_offsets), int(info.num_bins)

@@ -24,7 +24,8 @@ EXPORTS = ("pkv_status_string", "pkv_last_error", "pkv_version", "pkv_decode_arg
            "pkv_plan_even", "pkv_plan_balanced", "pkv_plan_queued", "pkv_workspace_bytes", "pkv_decode_slots", "pkv_paged_decode_attn",
            "pkv_merge_splits", "pkv_quantize_q", "pkv_quant_q_args_size", "pkv_write_kv", "pkv_kv_write_args_size",
            "pkv_decode_kernel_name", "pkv_sparse_workspace_bytes", "pkv_sparse_decode", "pkv_sparse_tiles", "pkv_sparse_merge",
-           "pkv_sparse_args_size", "pkv_paged_decode_noalloc", "pkv_stream_read_probe", "pkv_plan_pick")
+           "pkv_sparse_args_size", "pkv_paged_decode_noalloc", "pkv_stream_read_probe", "pkv_plan_pick",
+           "pkv_plan_paired")
 
 
 class PkvError(RuntimeError):
@@ -69,6 +70,7 @@ class DecodeArgs(ctypes.Structure):
         ("k_group_scale", _vp), ("kgs_page_stride", _i64), ("kgs_row_stride", _i64), ("kgs_head_stride", _i64),
         ("v_group_scale", _vp), ("vgs_page_stride", _i64), ("vgs_row_stride", _i64), ("vgs_head_stride", _i64),
         ("work_in_keys", _i32),
+        ("work_pairs", _i32),
     ]
 
 
@@ -150,7 +152,9 @@ def _load():
     lib.pkv_plan_queued.argtypes = [P(_i32), _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, P(_i32), _i32, P(_i32),
                                     P(_i32), _i32, P(PlanInfo)]
     lib.pkv_plan_pick.restype = _i32
-    lib.pkv_plan_pick.argtypes = [P(_i32), _i32, P(_i32), _i32, _i32, _i32, P(_i32), P(_f32)]
+    lib.pkv_plan_pick.argtypes = [P(_i32), _i32, P(_i32), _i32, _i32, _i32, _i32, P(_i32), P(_f32)]
+    lib.pkv_plan_paired.restype = _i32
+    lib.pkv_plan_paired.argtypes = [P(_i32), _i32, _i32, _i32, P(_i32), _i32, P(_i32), P(PlanInfo)]
     lib.pkv_workspace_bytes.restype = ctypes.c_size_t
     lib.pkv_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
     lib.pkv_decode_kernel_name.restype = ctypes.c_char_p
@@ -226,18 +230,33 @@ def plan_split_kv(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16
     return work[:info.num_work].copy(), ns[:nseq].copy(), info
 
 
-PKV_PLAN_WAVE, PKV_PLAN_BALANCED = 0, 1
+PKV_PLAN_WAVE, PKV_PLAN_BALANCED, PKV_PLAN_PAIRED = 0, 1, 2
 
 
-def plan_pick(seq_lens, work, kv_format, rows):
-    """pkv_plan_pick: (PKV_PLAN_WAVE or PKV_PLAN_BALANCED, imbalance) for a one-wave plan's work list."""
+def plan_pick(seq_lens, work, kv_format, h_k, rows):
+    """pkv_plan_pick: (PKV_PLAN_*, imbalance) for a one-wave plan's work list."""
     lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
     wk = np.ascontiguousarray(work, dtype=np.int32).reshape(-1, 4)
     plan, ratio = _i32(0), ctypes.c_float(0.0)
     P = ctypes.POINTER(_i32)
-    _check(lib.pkv_plan_pick(lens.ctypes.data_as(P), len(lens), wk.ctypes.data_as(P), wk.shape[0], kv_format, rows,
-                             ctypes.byref(plan), ctypes.byref(ratio)), "pkv_plan_pick")
+    _check(lib.pkv_plan_pick(lens.ctypes.data_as(P), len(lens), wk.ctypes.data_as(P), wk.shape[0], kv_format, h_k,
+                             rows, ctypes.byref(plan), ctypes.byref(ratio)), "pkv_plan_pick")
     return plan.value, ratio.value
+
+
+def plan_paired(seq_lens, pair_slots, max_splits=16, work_cap=None):
+    """pkv_plan_paired: (work int32[num_work, 4] in pairs, n_splits, PlanInfo)."""
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    nseq = lens.shape[0]
+    if work_cap is None:
+        work_cap = 2 * pair_slots
+    work = np.zeros((max(work_cap, 1), 4), dtype=np.int32)
+    ns = np.zeros(max(nseq, 1), dtype=np.int32)
+    info = PlanInfo()
+    P = ctypes.POINTER(_i32)
+    _check(lib.pkv_plan_paired(lens.ctypes.data_as(P), nseq, pair_slots, max_splits, work.ctypes.data_as(P), work_cap,
+                               ns.ctypes.data_as(P), ctypes.byref(info)), "pkv_plan_paired")
+    return work[:info.num_work].copy(), ns[:nseq].copy(), info
 
 
 def plan_even(seq_lens, h_k, n_q_tiles, cu_count, wg_per_cu=1, max_splits=16):

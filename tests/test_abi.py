@@ -251,6 +251,45 @@ def test_library_even_planner_equals_oracle(native, seed):
     assert (info.chunk_tiles, info.slots, info.num_work, info.max_n_splits) == (c, slots, len(work), max(ns))
 
 
+@pytest.mark.parametrize("seed", range(60))
+def test_library_paired_planner_equals_oracle(native, seed):
+    from oracle.plan import plan_paired
+    rng = np.random.default_rng(6000 + seed)
+    b = int(rng.integers(1, 200))
+    lens = np.where(rng.random(b) < 0.15, rng.integers(8192, 70000, size=b), rng.integers(0, 5000, size=b))
+    pair_slots = int(rng.choice([8, 64, 128, 256]))
+    max_splits = int(rng.choice([1, 2, 8, 16, 64, 256]))
+    try:
+        work, ns, c = plan_paired(lens.tolist(), pair_slots, max_splits)
+    except ValueError:
+        with pytest.raises(native.PkvError) as e:
+            native.plan_paired(lens, pair_slots, max_splits)
+        assert e.value.status == native.PKV_ERR_UNSUPPORTED
+        return
+    w2, ns2, info = native.plan_paired(lens, pair_slots, max_splits)
+    assert w2.tolist() == [list(x) for x in work]
+    assert ns2.tolist() == ns
+    assert (info.chunk_tiles, info.num_work, info.num_real, info.slots, info.max_n_splits) == (
+        c, len(work), sum(1 for x in work if x[2] > x[1]), 2 * pair_slots, max(ns))
+
+
+def test_paired_planner_errors(native):
+    lens = np.array([100, 200], dtype=np.int32)
+    for args in ((lens, 0), (np.array([-5], dtype=np.int32), 4), (lens, 4, 0)):
+        with pytest.raises(native.PkvError) as e:
+            native.plan_paired(*args)
+        assert e.value.status == native.PKV_ERR_INVALID_ARG
+    with pytest.raises(native.PkvError) as e:
+        native.plan_paired(lens, 4, native.PKV_MAX_SPLITS + 1)
+    assert e.value.status == native.PKV_ERR_UNSUPPORTED
+    with pytest.raises(native.PkvError) as e:  # five one-tile sequences never fit two pairs
+        native.plan_paired(np.full(5, 128, np.int32), 2)
+    assert e.value.status == native.PKV_ERR_UNSUPPORTED
+    with pytest.raises(native.PkvError) as e:  # the work array is too small for the pairs
+        native.plan_paired(lens, 4, work_cap=1)
+    assert e.value.status == native.PKV_ERR_CAPACITY
+
+
 def test_even_planner_errors(native):
     lens = np.array([100, 200], dtype=np.int32)
     with pytest.raises(native.PkvError):
@@ -450,26 +489,35 @@ def test_plan_pick_by_hand(native):
     # seq 1 tile 0 of L = 100 -> ceil(100 / 32) = 4; a padding entry (-1, 0, 0, 0) is skipped
     lens = [256, 100]
     work = [[0, 0, 2, 0], [1, 0, 1, 0], [-1, 0, 0, 0]]
-    plan, ratio = native.plan_pick(lens, work, native.PKV_KV_E4M3, 4)
+    plan, ratio = native.plan_pick(lens, work, native.PKV_KV_E4M3, 8, 4)
     assert ratio == pytest.approx(8 / 6) and plan == native.PKV_PLAN_WAVE  # 1.33 < 1.5
-    plan, _ = native.plan_pick(lens, work, native.PKV_KV_MLA, 64)
+    plan, _ = native.plan_pick(lens, work, native.PKV_KV_MLA, 1, 64)
     assert plan == native.PKV_PLAN_BALANCED  # latent multi-token form: 1.33 >= 1.12
-    plan, _ = native.plan_pick(lens, work, native.PKV_KV_MLA, 32)
+    plan, _ = native.plan_pick(lens, work, native.PKV_KV_MLA, 1, 32)
     assert plan == native.PKV_PLAN_WAVE  # latent pair form: the page's 1.5
     # seq 0 alone against three one-block items: 8 / ((8 + 3) / 4) = 2.9
     lens = [256, 10, 1, 0]
     work = [[0, 0, 2, 0], [1, 0, 1, 0], [2, 0, 1, 0], [3, 0, 1, 0]]
-    plan, ratio = native.plan_pick(lens, work, native.PKV_KV_E4M3, 16)
+    plan, ratio = native.plan_pick(lens, work, native.PKV_KV_E4M3, 8, 16)
     assert ratio == pytest.approx(8 * 4 / 11) and plan == native.PKV_PLAN_BALANCED
     for fmt in (native.PKV_KV_E2M1, native.PKV_KV_E2M3, native.PKV_KV_E3M2, native.PKV_KV_NVFP4):
-        assert native.plan_pick(lens, work, fmt, 16)[0] == native.PKV_PLAN_WAVE  # one-item form only
+        assert native.plan_pick(lens, work, fmt, 8, 16)[0] == native.PKV_PLAN_WAVE  # one-item form only
+    # four kv heads and at most 16 rows: the paired plan, whatever the imbalance (e4m3, fp4, fp6 caches)
+    for fmt in (native.PKV_KV_E4M3, native.PKV_KV_E2M1, native.PKV_KV_E2M3, native.PKV_KV_E3M2):
+        assert native.plan_pick(lens, work, fmt, 4, 16)[0] == native.PKV_PLAN_PAIRED
+        assert native.plan_pick([256, 256], [[0, 0, 2, 0], [1, 0, 2, 0]], fmt, 4, 1)[0] == native.PKV_PLAN_PAIRED
+    assert native.plan_pick(lens, work, native.PKV_KV_NVFP4, 4, 16)[0] == native.PKV_PLAN_WAVE  # measured slower
+    assert native.plan_pick(lens, work, native.PKV_KV_E4M3, 4, 32)[0] == native.PKV_PLAN_BALANCED  # two row blocks
+    assert native.plan_pick(lens, work, native.PKV_KV_E4M3, 2, 16)[0] == native.PKV_PLAN_BALANCED  # two kv heads
     # a chunk past the runtime length counts its existing keys: tiles 1..2 of L = 200 -> 72 keys, 3 blocks
-    plan, ratio = native.plan_pick([200, 300], [[0, 1, 2, 1], [1, 0, 3, 0]], native.PKV_KV_E4M3, 4)
+    plan, ratio = native.plan_pick([200, 300], [[0, 1, 2, 1], [1, 0, 3, 0]], native.PKV_KV_E4M3, 8, 4)
     assert ratio == pytest.approx(10 / 6.5)
-    assert native.plan_pick([5], np.zeros((0, 4), np.int32), native.PKV_KV_E4M3, 4)[1] == 1.0
+    assert native.plan_pick([5], np.zeros((0, 4), np.int32), native.PKV_KV_E4M3, 8, 4)[1] == 1.0
     P = ctypes.POINTER(ctypes.c_int32)
     out = ctypes.c_int32()
-    assert native.lib.pkv_plan_pick(None, 1, None, 0, 0, 4, ctypes.byref(out), None) == native.PKV_ERR_INVALID_ARG
+    assert native.lib.pkv_plan_pick(None, 1, None, 0, 0, 8, 4, ctypes.byref(out), None) == native.PKV_ERR_INVALID_ARG
     lens_a = np.array([5], np.int32)
-    assert native.lib.pkv_plan_pick(lens_a.ctypes.data_as(P), 1, lens_a.ctypes.data_as(P), 0, 0, 0,
+    assert native.lib.pkv_plan_pick(lens_a.ctypes.data_as(P), 1, lens_a.ctypes.data_as(P), 0, 0, 8, 0,
+                                    ctypes.byref(out), None) == native.PKV_ERR_INVALID_ARG
+    assert native.lib.pkv_plan_pick(lens_a.ctypes.data_as(P), 1, lens_a.ctypes.data_as(P), 0, 0, 0, 4,
                                     ctypes.byref(out), None) == native.PKV_ERR_INVALID_ARG

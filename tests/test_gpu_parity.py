@@ -449,6 +449,66 @@ def test_even_plan_narrow_format_and_graph():
 
 
 # ---------------------------------------------------------------------------
+# Paired plan (two work items per eight-wave workgroup): few pair slots, so
+# that workgroups hold two real items of different sequences
+# ---------------------------------------------------------------------------
+def _pairs_with_two_items(dec):
+    w = dec.work.cpu().numpy().reshape(-1, 2, 4)
+    return int(((w[:, 0, 2] > w[:, 0, 1]) & (w[:, 1, 2] > w[:, 1, 1])).sum())
+
+
+@pytest.mark.parametrize("q_format", ["e4m3", "bf16"])
+def test_paired_plan_small_every_output(q_format):
+    w = workload(4, num_seqs=14, q_format=q_format, seq_len_dist=("mix", 0.3, (3000, 9000), (100, 1500)))
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch, plan="paired", plan_cu_count=8)
+    assert dec.args.work_pairs == 1 and dec.has_splits and _pairs_with_two_items(dec) > 0
+    err_o, err_l, _ = compare(batch, dec, what=f"paired {q_format}")
+    print(f"paired {q_format}: chunk={dec.plan_info.chunk_tiles} items={dec.plan_info.num_real} "
+          f"pairs with two items={_pairs_with_two_items(dec)} max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
+
+
+def test_paired_plan_edge_lengths():
+    w = workload(4, num_seqs=len(EDGE_LENS), seq_len_dist=("fixed", EDGE_LENS), max_splits=8)
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch, plan="paired", plan_cu_count=12)  # chunk 5 tiles, pairs of two items
+    assert dec.args.work_pairs == 1 and _pairs_with_two_items(dec) > 0
+    check_edges(batch, dec, "e4m3", "paired edge e4m3")
+
+
+def test_paired_plan_is_the_auto_plan_of_the_fully_fp8_batch():
+    batch = make_batch(workload(4), device="cuda")
+    dec = run_batch(batch)
+    assert dec.plan == "paired" and dec.args.work_pairs == 1
+    lens = batch.seq_lens.cpu().numpy()
+    seqs = _sample(lens, np.random.default_rng(91))
+    err_o, err_l, _ = compare(batch, dec, seqs=seqs, what="paired full cfg4")
+    print(f"auto plan cfg4: chunk={dec.plan_info.chunk_tiles} items={dec.plan_info.num_real} "
+          f"pairs with two items={_pairs_with_two_items(dec)} max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
+
+
+def test_paired_plan_narrow_format_bitwise_repeats_and_graph():
+    w = workload(6, num_seqs=12, seq_len_dist=("mix", 0.3, (5000, 15000), (200, 3000)))
+    batch = make_batch(w, device="cuda")
+    dec = run_batch(batch, plan="paired", plan_cu_count=8)
+    assert dec.args.work_pairs == 1 and _pairs_with_two_items(dec) > 0
+    compare(batch, dec, what="paired fp4")
+    ref_o, ref_l = dec.o.clone(), dec.lse.clone()
+    dec.run()
+    torch.cuda.synchronize()
+    assert torch.equal(dec.o.view(torch.int16), ref_o.view(torch.int16)) and torch.equal(dec.lse, ref_l)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dec.run()
+    for rep in range(3):
+        dec.o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dec.o.view(torch.int16), ref_o.view(torch.int16)), f"replay {rep}"
+
+
+# ---------------------------------------------------------------------------
 # bf16 query rows of widely different magnitudes (2^-11 .. 2^3 across the
 # rows of one wave) with half of some rows' elements 2^-14 below the rest:
 # every form of the decode keeps each row's own range (a bf16 query is

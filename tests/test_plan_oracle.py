@@ -294,3 +294,77 @@ def test_even_invariants(seed):
     # never a longer item than the 128-key tile plan of the same batch
     twork = _tile_plan(lens, **kw)[0]
     assert max(lengths) <= max((w[2] - w[1]) * 128 for w in twork)
+
+
+from oracle.plan import plan_paired  # noqa: E402
+
+
+def test_paired_hand_worked():
+    # tiles [8, 1, 2, 4], three pairs. c = 4 fits five pieces into six places but
+    # pairs the second 4-tile piece with the 1-tile one (5 > 4); c = 5 ranks
+    # (seq 0 0-5) 5, (seq 3) 4, (seq 0 5-8) 3, (seq 2) 2, (seq 1) 1, pad:
+    # pairs 5 + 0, 4 + 1, 3 + 2, all <= 5
+    work, ns, chunk = plan_paired([1024, 100, 256, 512], pair_slots=3)
+    assert chunk == 5 and ns == [2, 1, 1, 1]
+    assert work == [(0, 0, 5, 0), (0, 0, 0, 0), (3, 0, 4, 0), (1, 0, 1, 0), (0, 5, 8, 1), (2, 0, 2, 0)]
+
+
+def test_paired_fewer_items_than_pairs_and_errors():
+    # tiles [3, 1], four pairs: c = 1 already fits (four one-tile pieces, each alone)
+    work, ns, chunk = plan_paired([300, 100], pair_slots=4)
+    assert chunk == 1 and ns == [3, 1]
+    pad = (0, 0, 0, 0)
+    assert work == [(0, 0, 1, 0), pad, (0, 1, 2, 1), pad, (0, 2, 3, 2), pad, (1, 0, 1, 0), pad]
+    # max_splits = 1: c starts at the longest, one piece per sequence
+    work, ns, chunk = plan_paired([300, 100], pair_slots=4, max_splits=1)
+    assert chunk == 3 and ns == [1, 1] and work == [(0, 0, 3, 0), pad, (1, 0, 1, 0), pad]
+    # max_splits caps the pieces: 8 tiles with max_splits 2 start at c = 4
+    assert plan_paired([1024], pair_slots=4, max_splits=2)[2] == 4
+    # five sequences of one tile in two pairs can never fit
+    with pytest.raises(ValueError):
+        plan_paired([128] * 5, pair_slots=2)
+    # three sequences of 2 tiles in two pairs: a pair would hold 4 tiles > c = 2
+    with pytest.raises(ValueError):
+        plan_paired([256] * 3, pair_slots=2)
+    for bad in ([], [-1]):
+        with pytest.raises(ValueError):
+            plan_paired(bad, pair_slots=2)
+    with pytest.raises(ValueError):
+        plan_paired([5], pair_slots=0)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_paired_invariants_and_minimal_chunk(seed):
+    rng = np.random.default_rng(2000 + seed)
+    n = int(rng.integers(1, 40))
+    lens = rng.integers(0, 9000, size=n).tolist()
+    pair_slots = int(rng.integers(max(1, n // 2), 64))
+    max_splits = int(rng.integers(1, 40))
+    try:
+        work, ns, chunk = plan_paired(lens, pair_slots, max_splits)
+    except ValueError:
+        return
+    tiles = [max(1, math.ceil(L / 128)) for L in lens]
+    real = [w for w in work if w[2] > w[1]]
+    # coverage: every sequence's tiles exactly once, pieces of `chunk` tiles in order, split slots 0..k-1
+    for b, t in enumerate(tiles):
+        mine = sorted((w for w in real if w[0] == b), key=lambda w: w[1])
+        assert [w[3] for w in mine] == list(range(len(mine))) == list(range(ns[b]))
+        assert mine[0][1] == 0 and mine[-1][2] == t
+        assert all(x[2] == y[1] for x, y in zip(mine, mine[1:]))
+        assert all(w[2] - w[1] == chunk for w in mine[:-1]) and 0 < mine[-1][2] - mine[-1][1] <= chunk
+    assert max(ns) <= max_splits and len(work) == 2 * min(pair_slots, len(real))
+    # the first items of the pairs are the longest, in order; no pair above one chunk
+    firsts = [work[2 * k][2] - work[2 * k][1] for k in range(len(work) // 2)]
+    assert firsts == sorted(firsts, reverse=True)
+    assert all((work[2 * k][2] - work[2 * k][1]) + (work[2 * k + 1][2] - work[2 * k + 1][1]) <= chunk
+               for k in range(len(work) // 2))
+    # minimality, by brute force over every smaller chunk: too many pieces, or some fold pair > c
+    lo = math.ceil(max(tiles) / max_splits)
+    assert chunk >= lo
+    for c in range(lo, chunk):
+        sizes = sorted((min(t, (j + 1) * c) - j * c for t in tiles for j in range(math.ceil(t / c))), reverse=True)
+        if len(sizes) > 2 * pair_slots:
+            continue
+        sizes += [0] * (2 * pair_slots - len(sizes))
+        assert max(sizes[k] + sizes[-1 - k] for k in range(pair_slots)) > c
