@@ -333,15 +333,23 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
     const int32_t* bt = p.block_table + (int64_t)b * p.bt_row;
     const int last_key = k_end - 1;
     const int pmask = page_size - 1;
-    // pages of a 32-key block's two 16-key halves (page_size >= 16): lanes 0 / 1
-    auto page_pair = [&](int kb) -> int { return bt[min(kb + 16 * (lane & 1), last_key) >> p.page_shift]; };
+    // pages of a 32-key block's two 16-key halves (page_size >= 16), read
+    // with scalar loads through the constant address space: their waits count
+    // no vector loads, so none of them waits for the KV loads in flight
+    struct Pages {
+      int h0, h1;
+    };
+    auto page_pair = [&](int kb) -> Pages {
+      const __attribute__((address_space(4))) int32_t* cbt = (const __attribute__((address_space(4))) int32_t*)bt;
+      return Pages{cbt[min(kb, last_key) >> p.page_shift], cbt[min(kb + 16, last_key) >> p.page_shift]};
+    };
     auto clamp_page = [&](int pg) -> int { return min(max(pg, 0), p.num_pages - 1); };
 
     // fetch u: the loads of block k_begin + 32u into ring slot u % RING, with
     // the pages from page slot u % 3 (loaded two fetches earlier); it loads
     // the pages of fetch u + 2. Waves 0-1 load keys 0-15, waves 2-3 keys
     // 16-31, so each wave reads one page per load.
-    int pv[3];
+    Pages pv[3];
     pv[0] = page_pair(k_begin);
     pv[1] = page_pair(k_begin + kStageKeys);
     const int my_key = t >> 3, part = t & 7;
@@ -350,9 +358,7 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
     // (page_size * row stride < 2^30, as the host checks) plus the lane's
     // bytes in the row.
     auto fetch = [&](RawPiece& r, int kb, const int ps) {
-      const int pg0 = clamp_page(__builtin_amdgcn_readlane(pv[ps], 0));
-      const int pg1 = clamp_page(__builtin_amdgcn_readlane(pv[ps], 1));
-      const int64_t pgk = (q >> 1) ? pg1 : pg0;
+      const int64_t pgk = clamp_page((q >> 1) ? pv[ps].h1 : pv[ps].h0);
       const uint32_t key = (uint32_t)(min(kb + my_key, last_key) & pmask);
       const uint8_t* lat = p.lat + pgk * p.lat_page;
       const uint8_t* rope = p.rope + pgk * p.rope_page;
