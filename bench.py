@@ -732,7 +732,7 @@ def main():
     ap.add_argument("--page-size", type=int, default=None, help="override the workload's page size")
     ap.add_argument("--contiguous-pages", action="store_true", help="hand out pages in order instead of shuffled")
     ap.add_argument("--seq-len", type=int, default=None, help="give every sequence this length")
-    ap.add_argument("--plan", default="auto", choices=["auto", "wave", "even", "balanced", "queued"],
+    ap.add_argument("--plan", default="auto", choices=["auto", "wave", "even", "balanced", "queued", "paired"],
                     help="auto: wave, or balanced when pkv_plan_pick finds the wave plan's items imbalanced; "
                          "wave: one work item per workgroup (occupancy-pinned split plan); even: the same rule with "
                          "equal 32-key-block pieces per sequence; balanced: contiguous "

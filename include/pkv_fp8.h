@@ -237,13 +237,13 @@ pkv_status pkv_plan_queued(const int32_t* seq_lens, int32_t num_seqs, int32_t h_
  * trigger of the decode form: 1.12 for the latent cache with rows >= 64 (its
  * multi-token form, measured on this part), 1.5 otherwise; always
  * PKV_PLAN_WAVE for the fp4, fp6 and NVFP4 caches (one-item form only).
- * With four kv heads and at most 16 rows (e4m3, fp4 and fp6 caches) the
- * balance comes from PKV_PLAN_PAIRED (pkv_plan_paired) instead, whatever the
- * imbalance: it runs the one-item form, and where the lengths are even it
+ * With four kv heads and at most 16 rows (e4m3, fp4, fp6 and NVFP4 caches)
+ * the balance comes from PKV_PLAN_PAIRED (pkv_plan_paired) instead, whatever
+ * the imbalance: it runs the one-item form, and where the lengths are even it
  * pairs nothing and equals the one-wave plan (measured on this part, decode
  * one-wave -> paired on the fully-fp8 batch: e4m3 169.3 -> 165.7 us, fp4
- * 103.9 -> 94.9, fp6 168 -> 152; NVFP4 154.2 -> 161.3, so NVFP4 stays on
- * PKV_PLAN_WAVE).
+ * 103.9 -> 94.9, fp6 168 -> 152; NVFP4 146.9 -> 147.7, but decode + merge
+ * 163.2 -> 161.1, with half the splits).
  *
  * seq_lens   host int32[num_seqs]
  * work       host int32[num_work][4] (seq, tile_begin, tile_end, split_slot)

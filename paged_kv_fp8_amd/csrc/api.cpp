@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <mutex>
+#include <unordered_map>
 
 #include "pkv_internal.h"
 
@@ -167,6 +168,25 @@ pkv_status hip_status(hipError_t e, const char* what) {
 }
 
 }  // namespace
+
+hipError_t check_lds(const void* kernel, size_t dyn_lds) {
+  // static LDS per kernel, looked up once
+  static std::mutex mu;
+  static std::unordered_map<const void*, size_t> static_bytes;
+  size_t fixed = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = static_bytes.find(kernel);
+    if (it == static_bytes.end()) {
+      hipFuncAttributes attr;
+      const hipError_t e = hipFuncGetAttributes(&attr, kernel);
+      if (e != hipSuccess) return e;
+      it = static_bytes.emplace(kernel, attr.sharedSizeBytes).first;
+    }
+    fixed = it->second;
+  }
+  return fixed + dyn_lds <= kMaxLdsBytes ? hipSuccess : hipErrorInvalidConfiguration;
+}
 }  // namespace pkv
 
 using namespace pkv;

@@ -397,8 +397,9 @@ __device__ __forceinline__ void fp6x32_to_e4m3(const uint2* win, const LaneOffse
   for (int i = 0; i < 4; ++i) {
     uint32_t w[2];
     for (int hw = 0; hw < 2; ++hw) {
-      s16x2 v = {0, 0};
-      v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(v, f16x2{h[8 * i + 4 * hw], h[8 * i + 4 * hw + 1]}, 1.0f, false);
+      // the first conversion's other word is its own (dead) input: no zeroed register
+      const f16x2 a = {h[8 * i + 4 * hw], h[8 * i + 4 * hw + 1]};
+      s16x2 v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(__builtin_bit_cast(s16x2, a), a, 1.0f, false);
       v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(v, f16x2{h[8 * i + 4 * hw + 2], h[8 * i + 4 * hw + 3]}, 1.0f, true);
       w[hw] = __builtin_bit_cast(uint32_t, v);
     }
@@ -476,9 +477,11 @@ __device__ __forceinline__ void softmax_pv(f32x4 (&sacc)[NB][2], const uint2 (&v
     }
     st.m_run[nb] = m_new;
     if (FP8Q) {
-      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], 0, false);
+      // the first conversion of each word pair keeps its other word from a
+      // dead input (overwritten by the second): no zeroed register
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], __float_as_int(pr[0]), false);
       lo = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], lo, true);
-      int hi = __builtin_amdgcn_cvt_pk_fp8_f32(pr[4], pr[5], 0, false);
+      int hi = __builtin_amdgcn_cvt_pk_fp8_f32(pr[4], pr[5], __float_as_int(pr[4]), false);
       hi = __builtin_amdgcn_cvt_pk_fp8_f32(pr[6], pr[7], hi, true);
       p8[nb] = as_long(uint2{(unsigned)lo, (unsigned)hi});
     } else {
@@ -665,33 +668,45 @@ __device__ __forceinline__ RawBlockN load_blockN(const GqaParams& p, int g, int 
 }
 
 // Eight NVFP4 codes (element 2i in the low nibble of byte i) with their
-// group scale byte -> the e4m3 bytes of e4m3(code * scale * 2^-3): each code
-// pair widened to f32 (v_cvt_scalef32_pk_f32_fp4, exact), times scale / 8
-// (exact in f32: at most 6 significant bits), rounded to e4m3 two at a time
-// by v_cvt_pk_fp8_f32 (round to nearest even; |value| <= 336, no overflow).
-__device__ __forceinline__ uint2 nvfp4x8_to_e4m3(uint32_t codes, uint32_t scale_byte) {
-  const float s = __builtin_amdgcn_cvt_f32_fp8((int)scale_byte, 0) * 0.125f;
-  const auto e01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
-  const auto e23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
-  const auto e45 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
-  const auto e67 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
-  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e01[0] * s, e01[1] * s, 0, false);
-  lo = __builtin_amdgcn_cvt_pk_fp8_f32(e23[0] * s, e23[1] * s, lo, true);
-  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(e45[0] * s, e45[1] * s, 0, false);
-  hi = __builtin_amdgcn_cvt_pk_fp8_f32(e67[0] * s, e67[1] * s, hi, true);
-  return uint2{(uint32_t)lo, (uint32_t)hi};
+// group scale -> the e4m3 bytes of e4m3(code * scale * 2^-3). The products
+// are formed in f16, where they are exact: a code has at most two significant
+// bits and s = scale / 8 at most four, with s in [2^-12, 56] (or 0), so every
+// product is 0 or an f16 normal in [2^-13, 336]. Rounding that exact value to
+// e4m3 (v_cvt_scalef32_pk_fp8_f16, round to nearest even, scale 1) gives the
+// byte the f32 product gives: 12 VALU per 8 codes (codes -> f16 pairs, packed
+// multiply, e4m3 pairs) instead of 16 through f32. Checked on the device for
+// every code pair and scale byte: identical except that a -0 scale byte
+// (which the quantiser never writes) yields +0 codes, an equal value.
+__device__ __forceinline__ _Float16 nvfp4_scale_f16(uint32_t scale_byte) {
+  return (_Float16)(__builtin_amdgcn_cvt_f32_fp8((int)scale_byte, 0) * 0.125f);  // exact
+}
+
+__device__ __forceinline__ uint2 nvfp4x8_to_e4m3(uint32_t codes, _Float16 s) {
+  typedef short i16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 ss = {s, s};
+  const f16x2 e01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * ss;
+  const f16x2 e23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * ss;
+  const f16x2 e45 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * ss;
+  const f16x2 e67 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * ss;
+  // each word is written by one conversion; the first one's other word is
+  // its own (dead) input, so no zeroed register is needed
+  i16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(__builtin_bit_cast(i16x2, e01), e01, 1.0f, false);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(lo, e23, 1.0f, true);
+  i16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(__builtin_bit_cast(i16x2, e45), e45, 1.0f, false);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(hi, e67, 1.0f, true);
+  return uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
 __device__ __forceinline__ RawBlock nvfp4_block_to_e4m3(const RawBlockN& c, int g4) {
   RawBlock r;
   for (int t = 0; t < 2; ++t)
     for (int h = 0; h < 2; ++h) {  // head dims 64 h + 16 g4 ..: group 4 h + g4
-      const uint32_t sb = ((h ? c.ks[t].y : c.ks[t].x) >> (8 * g4)) & 0xFFu;
-      const uint2 lo = nvfp4x8_to_e4m3(c.k[t][h].x, sb);
-      const uint2 hi = nvfp4x8_to_e4m3(c.k[t][h].y, sb);
+      const _Float16 sk = nvfp4_scale_f16(((h ? c.ks[t].y : c.ks[t].x) >> (8 * g4)) & 0xFFu);
+      const uint2 lo = nvfp4x8_to_e4m3(c.k[t][h].x, sk);
+      const uint2 hi = nvfp4x8_to_e4m3(c.k[t][h].y, sk);
       r.k[t][h] = uint4{lo.x, lo.y, hi.x, hi.y};
     }
-  for (int j = 0; j < 8; ++j) r.v[j] = nvfp4x8_to_e4m3(c.v[j], c.vs[j]);
+  for (int j = 0; j < 8; ++j) r.v[j] = nvfp4x8_to_e4m3(c.v[j], nvfp4_scale_f16(c.vs[j]));
   return r;
 }
 
@@ -950,6 +965,12 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
     round_base += rounds;
   }
   finish_item<FP8Q, NB>(p, st, rm, b, g, row0, r16, g4, ns, slot, cs, vdv);
+}
+
+// Bytes of dynamic LDS per wave for the parked query of two row blocks.
+template <bool FP8Q, int NB>
+constexpr int q_park_bytes() {
+  return NB == 2 ? NB * 4 * 64 * (FP8Q ? 8 : 16) : 0;
 }
 
 // V rows of keys past `vlast` (loaded through planned block-table entries
@@ -1330,7 +1351,9 @@ __device__ __forceinline__ void gqa_decode_bin_then_queue(const GqaParams& p, in
   const int col = blockIdx.z * gridDim.y + blockIdx.y;         // < h_k * q tiles
   int* const taken = p.queue + col;                            // queue items handed out (+ one per final take)
   int* const retired = p.queue + gridDim.y * gridDim.z + col;  // workgroups done taking
-  __shared__ int next_item;
+  // the taken index, shared through the dynamic LDS past the parked queries
+  extern __shared__ __attribute__((aligned(16))) uint8_t gqa_q_lds[];
+  int& next_item = *reinterpret_cast<int*>(gqa_q_lds + HW * q_park_bytes<FP8Q, NB>());
   for (;;) {
     if (threadIdx.x == 0)
       next_item = q0 + __hip_atomic_fetch_add(taken, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1372,12 +1395,25 @@ __device__ __forceinline__ void xcd_item_tile(int id, int units, int tiles, int&
   tile = local / left;
 }
 
+// Rounds done per wave, for the eight-wave workgroups that keep their two
+// waves per SIMD in step; no LDS in the other forms (whose dynamic LDS may
+// take all of the CU's).
+template <int HW>
+__device__ __forceinline__ int* wave_progress() {
+  if constexpr (HW == 8) {
+    __shared__ int progress[8];
+    return progress;
+  } else {
+    return nullptr;
+  }
+}
+
 template <bool FP8Q, int NB, bool CAUSAL_TAIL, int STAGES, int HW, bool STREAM, int KVF = 0>
 __global__ __launch_bounds__(64 * HW) __attribute__((amdgpu_waves_per_eu(NB == 1 || !STREAM ? 2 : 1)))
 void gqa_decode_kernel(GqaParams p) {
   const int lane = threadIdx.x & 63;
-  __shared__ int progress[HW];  // rounds done per wave (eight waves)
-  if (HW == 8) {
+  int* const progress = wave_progress<HW>();
+  if constexpr (HW == 8) {
     if (lane == 0) progress[threadIdx.x >> 6] = -1;
     __syncthreads();
   }
@@ -1539,9 +1575,11 @@ GqaVariant gqa_variant(const pkv_decode_args& a) {
 
 int gqa_rows_per_tile(const GqaVariant& v) { return 16 * v.n_blocks; }
 
-// dynamic LDS of a variant: the parked query of two row blocks (one-item form)
+// dynamic LDS of a variant: the parked query of two row blocks (one-item
+// form), then, for e4m3 K/V, the queued form's shared word
 size_t gqa_dyn_lds(const GqaVariant& v) {
-  return (v.n_blocks == 2 && !v.stream) ? (size_t)v.heads_per_wg * 2 * 4 * 64 * (v.fp8_q ? 8 : 16) : 0;
+  if (v.n_blocks != 2 || v.stream) return 0;
+  return (size_t)v.heads_per_wg * 2 * 4 * 64 * (v.fp8_q ? 8 : 16) + (v.kvf == 0 ? 16 : 0);
 }
 
 hipError_t gqa_occupancy(const GqaVariant& v, int* units_per_cu) {
@@ -1633,7 +1671,9 @@ hipError_t gqa_launch(const pkv_decode_args& a, const GqaVariant& v, hipStream_t
   if (p.xcd_tiles) grid = dim3(a.num_work * tiles, (a.h_k + hw - 1) / hw, 1);
   if (v.paired) grid = dim3(a.num_work / 2, 1, 1);  // one q-row tile (16 rows), two items per workgroup
   void* args[] = {&p};
-  return hipLaunchKernel(select_kernel(v), grid, dim3(64 * hw), args, gqa_dyn_lds(v), stream);
+  const void* kernel = select_kernel(v);
+  if (const hipError_t e = check_lds(kernel, gqa_dyn_lds(v)); e != hipSuccess) return e;
+  return hipLaunchKernel(kernel, grid, dim3(64 * hw), args, gqa_dyn_lds(v), stream);
 }
 
 }  // namespace pkv

@@ -1325,15 +1325,16 @@ hipError_t mla_launch(const pkv_decode_args& a, hipStream_t stream) {
   const int wpw = waves_per_wg(a);
   int tiles = (p.rows + mla_rows_per_tile(a) - 1) / mla_rows_per_tile(a);
   int units = a.bin_offsets ? a.num_bins : a.num_work;
+  const void* kernel = select_kernel(a);
+  if (const hipError_t e = check_lds(kernel, dyn_lds_bytes(a)); e != hipSuccess) return e;
   if (staged(a)) {
     void* args[] = {&p, &units, &tiles};
-    return hipLaunchKernel(select_kernel(a), dim3((unsigned)(units * tiles)), dim3(64 * wpw), args,
-                           dyn_lds_bytes(a), stream);
+    return hipLaunchKernel(kernel, dim3((unsigned)(units * tiles)), dim3(64 * wpw), args, dyn_lds_bytes(a), stream);
   }
   int groups = pair_groups(a);
   void* args[] = {&p, &groups};
-  return hipLaunchKernel(select_kernel(a), dim3((unsigned)units, (unsigned)tiles), dim3(64 * wpw), args,
-                         dyn_lds_bytes(a), stream);
+  return hipLaunchKernel(kernel, dim3((unsigned)units, (unsigned)tiles), dim3(64 * wpw), args, dyn_lds_bytes(a),
+                         stream);
 }
 
 int sparse_tiles(const pkv_sparse_args& a) {
@@ -1386,9 +1387,12 @@ hipError_t sparse_launch(const pkv_sparse_args& a, hipStream_t stream, bool tile
   if (tiles > 0 && tiles_kernel) {
     int groups = a.h_q % 32 == 0 ? 2 : 1;
     void* args[] = {&p, &groups};
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&sparse_pair_kernel),
+    const void* kernel = reinterpret_cast<const void*>(&sparse_pair_kernel);
+    const size_t lds = (size_t)2 * groups * kPairWaveBytes;
+    if (const hipError_t e = check_lds(kernel, lds); e != hipSuccess) return e;
+    const hipError_t e = hipLaunchKernel(kernel,
                                          dim3((unsigned)tiles, (unsigned)(a.h_q / (16 * groups)), (unsigned)a.num_tokens),
-                                         dim3(128 * groups), args, (size_t)2 * groups * kPairWaveBytes, stream);
+                                         dim3(128 * groups), args, lds, stream);
     if (e != hipSuccess) return e;
   }
   if (!merge_kernel) return hipSuccess;

@@ -31,6 +31,14 @@ inline bool narrow_kv(int kv_format) {
   return kv_format == PKV_KV_E2M1 || kv_format == PKV_KV_E2M3 || kv_format == PKV_KV_E3M2 ||
          kv_format == PKV_KV_NVFP4;
 }
+// LDS of one CU, the most one workgroup may hold (static + dynamic bytes).
+constexpr size_t kMaxLdsBytes = 160 * 1024;
+// hipSuccess when `kernel` launched with `dyn_lds` bytes of dynamic LDS fits
+// kMaxLdsBytes, else hipErrorInvalidConfiguration (nothing is launched):
+// the command processor rejects a dispatch that asks for more, and that
+// aborts the whole queue rather than failing the launch.
+hipError_t check_lds(const void* kernel, size_t dyn_lds);
+
 GqaVariant gqa_variant(const pkv_decode_args& a);
 int gqa_rows_per_tile(const GqaVariant& v);
 hipError_t gqa_occupancy(const GqaVariant& v, int* units_per_cu);

@@ -481,9 +481,9 @@ extern "C" pkv_status pkv_plan_pick(const int32_t* seq_lens, int32_t num_seqs, c
   // the balanced plan spends more per block than it gains). Measured on the
   // fully-fp8 batch, decode us one-wave -> paired: e4m3 169.3 -> 165.7, fp4
   // 103.9 -> 94.9, fp6 168 -> 152; NVFP4, whose one-wave plan already runs
-  // two waves per SIMD on a two-block ring, 154.2 -> 161.3, so it keeps the
-  // one-wave plan
-  if (kv_format != PKV_KV_MLA && kv_format != PKV_KV_NVFP4 && h_k == 4 && rows <= 16) *plan_out = PKV_PLAN_PAIRED;
+  // two waves per SIMD, 146.9 -> 147.7 for the decode but 163.2 -> 161.1 for
+  // decode + merge (16 splits instead of 32)
+  if (kv_format != PKV_KV_MLA && h_k == 4 && rows <= 16) *plan_out = PKV_PLAN_PAIRED;
   if (imbalance_out) *imbalance_out = ratio;
   return PKV_OK;
 }

@@ -502,11 +502,10 @@ def test_plan_pick_by_hand(native):
     assert ratio == pytest.approx(8 * 4 / 11) and plan == native.PKV_PLAN_BALANCED
     for fmt in (native.PKV_KV_E2M1, native.PKV_KV_E2M3, native.PKV_KV_E3M2, native.PKV_KV_NVFP4):
         assert native.plan_pick(lens, work, fmt, 8, 16)[0] == native.PKV_PLAN_WAVE  # one-item form only
-    # four kv heads and at most 16 rows: the paired plan, whatever the imbalance (e4m3, fp4, fp6 caches)
-    for fmt in (native.PKV_KV_E4M3, native.PKV_KV_E2M1, native.PKV_KV_E2M3, native.PKV_KV_E3M2):
+    # four kv heads and at most 16 rows: the paired plan, whatever the imbalance (e4m3, fp4, fp6, NVFP4 caches)
+    for fmt in (native.PKV_KV_E4M3, native.PKV_KV_E2M1, native.PKV_KV_E2M3, native.PKV_KV_E3M2, native.PKV_KV_NVFP4):
         assert native.plan_pick(lens, work, fmt, 4, 16)[0] == native.PKV_PLAN_PAIRED
         assert native.plan_pick([256, 256], [[0, 0, 2, 0], [1, 0, 2, 0]], fmt, 4, 1)[0] == native.PKV_PLAN_PAIRED
-    assert native.plan_pick(lens, work, native.PKV_KV_NVFP4, 4, 16)[0] == native.PKV_PLAN_WAVE  # measured slower
     assert native.plan_pick(lens, work, native.PKV_KV_E4M3, 4, 32)[0] == native.PKV_PLAN_BALANCED  # two row blocks
     assert native.plan_pick(lens, work, native.PKV_KV_E4M3, 2, 16)[0] == native.PKV_PLAN_BALANCED  # two kv heads
     # a chunk past the runtime length counts its existing keys: tiles 1..2 of L = 200 -> 72 keys, 3 blocks

@@ -487,12 +487,13 @@ def test_paired_plan_is_the_auto_plan_of_the_fully_fp8_batch():
           f"pairs with two items={_pairs_with_two_items(dec)} max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
 
 
-def test_paired_plan_narrow_format_bitwise_repeats_and_graph():
-    w = workload(6, num_seqs=12, seq_len_dist=("mix", 0.3, (5000, 15000), (200, 3000)))
+@pytest.mark.parametrize("cfg,fmt", [(6, "fp4"), (10, "nvfp4")])
+def test_paired_plan_narrow_format_bitwise_repeats_and_graph(cfg, fmt):
+    w = workload(cfg, num_seqs=12, seq_len_dist=("mix", 0.3, (5000, 15000), (200, 3000)))
     batch = make_batch(w, device="cuda")
     dec = run_batch(batch, plan="paired", plan_cu_count=8)
     assert dec.args.work_pairs == 1 and _pairs_with_two_items(dec) > 0
-    compare(batch, dec, what="paired fp4")
+    compare(batch, dec, what=f"paired {fmt}")
     ref_o, ref_l = dec.o.clone(), dec.lse.clone()
     dec.run()
     torch.cuda.synchronize()
