@@ -714,6 +714,29 @@ pkv_status pkv_paged_decode_noalloc(const pkv_decode_args* a, void* stream);
 pkv_status pkv_stream_read_probe(const void* src, size_t bytes, int32_t workgroups, int32_t unroll, uint32_t* sink,
                                  void* stream);
 
+/*
+ * Per-phase timestamps of a decode main loop (measurement only; no passage of
+ * the sources: it shows where the time of a loop step goes). A library built
+ * with -DPKV_STAMPS=1 records, in lane 0 of each wave (at most 8) of
+ * workgroups 0..15 whose blockIdx.y and .z are 0, the shader clock
+ * (s_memtime) at up to 8 points of each of the first 48 steps of the
+ * workgroup's first work item:
+ *   loop 0, the one-item form of the kv-head decode, per 32-key block:
+ *     0 block start, 1 its fetch issued, 2 its loads landed, 3 processed;
+ *   loop 1, the latent staged form, per 32-key step (from the second):
+ *     0 step start, 1 loads issued and converted, 2 MFMA phase done,
+ *     3 past the first barrier, 4 softmax done, 5 past the second barrier.
+ * Stamps of the last launch of that loop are copied (synchronously) to
+ * host_dst, PKV_STAMP_WORDS uint64 values laid out as
+ * [workgroup 16][wave 8][step 48][point 8]; entries never written stay as
+ * the previous launches left them (zero at load).
+ * Errors: PKV_ERR_INVALID_ARG (NULL host_dst, loop not 0 or 1),
+ * PKV_ERR_UNSUPPORTED (a library built without the stamps: the normal
+ * build), PKV_ERR_HIP (the copy failed).
+ */
+#define PKV_STAMP_WORDS (16 * 8 * 48 * 8)
+pkv_status pkv_debug_stamps(int32_t loop, uint64_t* host_dst);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

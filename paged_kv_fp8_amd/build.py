@@ -29,12 +29,12 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-ta
          "-Wno-unknown-pragmas"]
 
 
-def build(verbose=False, extra_flags=(), jobs=None):
+def build(verbose=False, extra_flags=(), jobs=None, out=LIB):
     """Compile every source (in parallel, one hipcc per source) and link the
-    library; returns its path."""
+    library at `out` (default: the in-tree library); returns its path."""
     from concurrent.futures import ThreadPoolExecutor
 
-    build_dir = os.path.join(HERE, "_build")
+    build_dir = os.path.join(HERE, "_build" if out == LIB else "_build_" + os.path.splitext(os.path.basename(out))[0])
     os.makedirs(build_dir, exist_ok=True)
     cmds, objs = [], []
     for src in SOURCES:
@@ -48,10 +48,10 @@ def build(verbose=False, extra_flags=(), jobs=None):
     with ThreadPoolExecutor(jobs) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 def _run(cmd, verbose):

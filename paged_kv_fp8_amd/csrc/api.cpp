@@ -10,6 +10,7 @@
 #include <unordered_map>
 
 #include "pkv_internal.h"
+#include "stamps.h"
 
 namespace pkv {
 
@@ -458,6 +459,17 @@ extern "C" pkv_status pkv_sparse_merge(const pkv_sparse_args* a, void* stream) {
 }
 
 extern "C" size_t pkv_sparse_args_size(void) { return sizeof(pkv_sparse_args); }
+
+extern "C" pkv_status pkv_debug_stamps(int32_t loop, uint64_t* host_dst) {
+  if (!host_dst) return fail(PKV_ERR_INVALID_ARG, "host_dst must be non-NULL");
+  if (loop != 0 && loop != 1) return fail(PKV_ERR_INVALID_ARG, "loop=%d must be 0 (kv-head) or 1 (latent)", loop);
+#if PKV_STAMPS
+  static_assert(PKV_STAMP_WORDS == kStampWords, "stamp layout");
+  return hip_status(loop == 0 ? gqa_copy_stamps(host_dst) : mla_copy_stamps(host_dst), "stamps copy");
+#else
+  return fail(PKV_ERR_UNSUPPORTED, "library built without -DPKV_STAMPS=1");
+#endif
+}
 
 extern "C" pkv_status pkv_stream_read_probe(const void* src, size_t bytes, int32_t workgroups, int32_t unroll,
                                             uint32_t* sink, void* stream) {

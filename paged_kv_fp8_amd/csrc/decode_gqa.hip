@@ -47,6 +47,7 @@
 #include <type_traits>
 
 #include "pkv_internal.h"
+#include "stamps.h"
 
 namespace pkv {
 namespace {
@@ -784,6 +785,18 @@ __device__ __forceinline__ void finish_item(const GqaParams& p, const RowState<N
   }
 }
 
+PKV_STAMP_STORAGE
+
+#if PKV_STAMPS
+// Stamped builds: wait until a block's loads have landed (an empty asm reads
+// the register its last load fills, so the compiler's wait for it, which
+// covers every earlier load, comes first).
+__device__ __forceinline__ void landed(const RawBlock& r) { asm volatile("" ::"v"(r.v[7].x), "v"(r.v[7].y)); }
+__device__ __forceinline__ void landed(const RawBlock4& r) { asm volatile("" ::"v"(r.v[7])); }
+__device__ __forceinline__ void landed(const RawBlock6& r) { asm volatile("" ::"v"(r.v[7].x), "v"(r.v[7].y)); }
+__device__ __forceinline__ void landed(const RawBlockN& r) { asm volatile("" ::"v"(r.vs[7])); }
+#endif
+
 // Load through the constant address space: with a wave-uniform address this
 // is a scalar load, which completes out of order on its own counter, so
 // waiting for it never waits for the KV loads in flight (a vector load
@@ -950,7 +963,15 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
 #pragma unroll
       for (int s = 0; s < STAGES; ++s) {
         const int kb = kb0 + kBlockKeys * s;
+        // stamps (stamped builds): issue 0 -> 1, wait for the block 1 -> 2, processing 2 -> 3
+        PKV_STAMP_VARS
+        PKV_STAMP(0);
         fetch(ring[(s + STAGES - 1) % STAGES], kb + kBlockKeys * (STAGES - 1), (s + STAGES - 1) % STAGES);
+        PKV_STAMP(1);
+#if PKV_STAMPS
+        landed(ring[s]);
+#endif
+        PKV_STAMP(2);
         if constexpr (kFp4)
           process_block_fp4<NB, kQLds>(ring[s], kb, q, qlds, st, lim, lim_min, c2, g4);
         else if constexpr (kFp6)
@@ -959,6 +980,8 @@ __device__ __forceinline__ void gqa_decode_item(const GqaParams& p, int item, in
           process_block<true, NB, kQLds>(nvfp4_block_to_e4m3(ring[s], g4), kb, q, qlds, st, lim, lim_min, c2, g4);
         else
           process_block<FP8Q, NB, kQLds>(ring[s], kb, q, qlds, st, lim, lim_min, c2, g4);
+        PKV_STAMP(3);
+        PKV_STAMP_SAVE(r * STAGES + s, round_base == 0);
       }
       if (HW == 8 && !p.paired) keep_pace(progress, wave, round_base + r, lane);
     }
@@ -1675,5 +1698,8 @@ hipError_t gqa_launch(const pkv_decode_args& a, const GqaVariant& v, hipStream_t
   if (const hipError_t e = check_lds(kernel, gqa_dyn_lds(v)); e != hipSuccess) return e;
   return hipLaunchKernel(kernel, grid, dim3(64 * hw), args, gqa_dyn_lds(v), stream);
 }
+
+// stamps of the one-item loop (stamped builds; hipErrorNotSupported otherwise)
+hipError_t gqa_copy_stamps(void* host_dst) { return PKV_STAMP_COPY(host_dst); }
 
 }  // namespace pkv

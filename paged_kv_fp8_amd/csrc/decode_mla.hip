@@ -33,6 +33,7 @@
 #include <cmath>
 
 #include "pkv_internal.h"
+#include "stamps.h"
 
 namespace pkv {
 namespace {
@@ -238,8 +239,12 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
 __device__ __forceinline__ float max_over4(float x) { return pair32(pair16(x, true), true); }
 __device__ __forceinline__ float sum_over4(float x) { return pair32(pair16(x, false), false); }
 
+PKV_STAMP_STORAGE
+
+// first_item: the workgroup's first work item (only it records stamps, in
+// stamped builds)
 template <bool CAUSAL_TAIL, int RING>
-__device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int tile, uint8_t* lds) {
+__device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int tile, uint8_t* lds, bool first_item) {
   const int t = threadIdx.x;
   const int q = __builtin_amdgcn_readfirstlane(t >> 6);  // wave = head-dim quarter (wave-uniform)
   const int lane = t & 63;
@@ -576,14 +581,24 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
         uint8_t* const st_prev = lds + (s % 3) * kStageBytes;
         uint8_t* const st_cur = lds + ((s + 1) % 3) * kStageBytes;
         uint8_t* const st_next = lds + ((s + 2) % 3) * kStageBytes;
+        // stamps (stamped builds): load issue + conversion 0 -> 1, MFMA phase
+        // 1 -> 2, first barrier 2 -> 3, softmax 3 -> 4, second barrier 4 -> 5
+        PKV_STAMP_VARS
+        PKV_STAMP(0);
         fetch(ring[(s + 1) & 1], kb + RING * kStageKeys, s % 3);
         convert(nr, nc);
+        PKV_STAMP(1);
         pv_quarter(st_prev, st_next, &nr, &nc);
         qk_quarter(st_cur, st_next, nr, nc);
         stage_fixup(nr, st_next);
+        PKV_STAMP(2);
         barrier();
+        PKV_STAMP(3);
         softmax_step(kb);
+        PKV_STAMP(4);
         barrier();
+        PKV_STAMP(5);
+        PKV_STAMP_SAVE(j, first_item);
         // the flag is read once per round: a block past the bound only fills
         // O, l and P with values the restart throws away
         if (s == kRound - 1 && __builtin_amdgcn_readfirstlane(*restart_flag)) {
@@ -669,10 +684,17 @@ void mla_lds_kernel(MlaParams p, int units, int tiles) {
     it = p.bin_offsets[unit];
     it_end = p.bin_offsets[unit + 1];
   }
+#if PKV_STAMPS
+  const int it0 = it;
+#define PKV_FIRST_ITEM (it == it0)
+#else
+#define PKV_FIRST_ITEM true
+#endif
   for (; it < it_end; ++it) {
-    mla_lds_item<CAUSAL_TAIL, kLdsRing>(p, it, tile, mla_stage_lds);
+    mla_lds_item<CAUSAL_TAIL, kLdsRing>(p, it, tile, mla_stage_lds, PKV_FIRST_ITEM);
     __syncthreads();  // the next item's first stage overwrites LDS
   }
+#undef PKV_FIRST_ITEM
 }
 
 // ---- pair form: fewer than 64 query rows -------------------------------------
@@ -1401,5 +1423,8 @@ hipError_t sparse_launch(const pkv_sparse_args& a, hipStream_t stream, bool tile
   return hipLaunchKernel(reinterpret_cast<const void*>(&sparse_merge_kernel), dim3((unsigned)((threads + 255) / 256)),
                          dim3(256), margs, 0, stream);
 }
+
+// stamps of the staged loop (stamped builds; hipErrorNotSupported otherwise)
+hipError_t mla_copy_stamps(void* host_dst) { return PKV_STAMP_COPY(host_dst); }
 
 }  // namespace pkv

@@ -60,6 +60,11 @@ hipError_t merge_launch(const pkv_decode_args& a, hipStream_t stream);
 hipError_t quantize_q_launch(const pkv_quant_q_args& a, hipStream_t stream);
 hipError_t write_kv_launch(const pkv_kv_write_args& a, hipStream_t stream);
 
+// Stamps of the one-item kv-head loop / the latent staged loop (library
+// built with -DPKV_STAMPS=1; hipErrorNotSupported otherwise).
+hipError_t gqa_copy_stamps(void* host_dst);
+hipError_t mla_copy_stamps(void* host_dst);
+
 // Streaming-read probe (measurement only).
 hipError_t probe_launch(const void* src, size_t bytes, int workgroups, int unroll, uint32_t* sink,
                         hipStream_t stream);

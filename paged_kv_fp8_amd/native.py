@@ -11,7 +11,8 @@ import os
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkvfp8.so")
+# PKV_LIB names another build of the library (the stamped one); default: the in-tree build
+LIB_PATH = os.environ.get("PKV_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkvfp8.so")
 
 PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_CAPACITY, PKV_ERR_WORKSPACE, PKV_ERR_HIP = 0, -1, -2, -3, -4, -5
 PKV_Q_BF16, PKV_Q_E4M3 = 0, 1
@@ -25,7 +26,7 @@ EXPORTS = ("pkv_status_string", "pkv_last_error", "pkv_version", "pkv_decode_arg
            "pkv_merge_splits", "pkv_quantize_q", "pkv_quant_q_args_size", "pkv_write_kv", "pkv_kv_write_args_size",
            "pkv_decode_kernel_name", "pkv_sparse_workspace_bytes", "pkv_sparse_decode", "pkv_sparse_tiles", "pkv_sparse_merge",
            "pkv_sparse_args_size", "pkv_paged_decode_noalloc", "pkv_stream_read_probe", "pkv_plan_pick",
-           "pkv_plan_paired")
+           "pkv_plan_paired", "pkv_debug_stamps")
 
 
 class PkvError(RuntimeError):
@@ -181,6 +182,8 @@ def _load():
     lib.pkv_paged_decode_noalloc.argtypes = [P(DecodeArgs), _vp]
     lib.pkv_stream_read_probe.restype = _i32
     lib.pkv_stream_read_probe.argtypes = [_vp, ctypes.c_size_t, _i32, _i32, _vp, _vp]
+    lib.pkv_debug_stamps.restype = _i32
+    lib.pkv_debug_stamps.argtypes = [_i32, _vp]
     for name, st in (("pkv_quant_q_args_size", QuantQArgs), ("pkv_kv_write_args_size", KvWriteArgs),
                      ("pkv_sparse_args_size", SparseArgs)):
         if getattr(lib, name)() != ctypes.sizeof(st):
@@ -366,6 +369,18 @@ def paged_decode_noalloc(args, stream=None):
     """Decode + merge with the library's own split workspace (args.workspace
     is ignored); allocates nothing."""
     _check(lib.pkv_paged_decode_noalloc(ctypes.byref(args), stream), "pkv_paged_decode_noalloc")
+
+
+PKV_STAMP_WORDS = 16 * 8 * 48 * 8
+
+
+def debug_stamps(loop):
+    """Stamps of the last launch of `loop` (0 kv-head one-item form, 1 latent
+    staged form) as int64[16 workgroups][8 waves][48 steps][8 points]; the
+    library must be built with -DPKV_STAMPS=1 (PkvError UNSUPPORTED otherwise)."""
+    out = np.zeros(PKV_STAMP_WORDS, dtype=np.uint64)
+    _check(lib.pkv_debug_stamps(loop, out.ctypes.data_as(ctypes.c_void_p)), "pkv_debug_stamps")
+    return out.astype(np.int64).reshape(16, 8, 48, 8)
 
 
 def stream_read_probe(src_ptr, nbytes, workgroups, unroll, sink_ptr, stream=None):

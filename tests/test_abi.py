@@ -484,6 +484,25 @@ def test_stream_read_probe_rejects_invalid_arguments_without_touching_the_gpu(na
     assert native.last_error()
 
 
+def test_debug_stamps_normal_build_and_argument_errors(native):
+    # the in-tree library is the normal build: no stamps; arguments are
+    # checked first, and no HIP call is made on any of these paths
+    buf = np.zeros(native.PKV_STAMP_WORDS, dtype=np.uint64)
+    ptr = buf.ctypes.data_as(ctypes.c_void_p)
+    assert native.lib.pkv_debug_stamps(0, ptr) == native.PKV_ERR_UNSUPPORTED
+    assert "PKV_STAMPS" in native.last_error()
+    assert native.lib.pkv_debug_stamps(1, ptr) == native.PKV_ERR_UNSUPPORTED
+    assert native.lib.pkv_debug_stamps(2, ptr) == native.PKV_ERR_INVALID_ARG
+    assert native.lib.pkv_debug_stamps(0, None) == native.PKV_ERR_INVALID_ARG
+    with pytest.raises(native.PkvError) as e:
+        native.debug_stamps(0)
+    assert e.value.status == native.PKV_ERR_UNSUPPORTED
+    # the header's layout constant matches the binding's
+    text = open(HEADER).read()
+    assert re.search(r"#define PKV_STAMP_WORDS \(16 \* 8 \* 48 \* 8\)", text)
+    assert native.PKV_STAMP_WORDS == 16 * 8 * 48 * 8
+
+
 def test_plan_pick_by_hand(native):
     # items in 32-key blocks of existing keys: seq 0 tiles 0..2 of L = 256 -> 8 blocks;
     # seq 1 tile 0 of L = 100 -> ceil(100 / 32) = 4; a padding entry (-1, 0, 0, 0) is skipped
