@@ -351,6 +351,9 @@ pkv_status pkv_plan_paired(const int32_t* seq_lens, int32_t num_seqs, int32_t pa
  *          read back); may be NULL when max_splits == 1.
  * Alignment: q, k, v, o and workspace 16-byte aligned, and every stride of
  * q, k, v and o a multiple of 16 bytes (8-byte multiples for e4m3 q).
+ * Limits (UNSUPPORTED beyond them): page_size * row stride below 2^30 bytes
+ * (in-page offsets are 32-bit) and every page stride of k, v and the NVFP4
+ * group scales below 2^32 bytes (page offsets are 32 x 32-bit products).
  */
 typedef struct pkv_decode_args {
   int32_t num_seqs, q_len, h_q, h_k, d_qk, d_v;

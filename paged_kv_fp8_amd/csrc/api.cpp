@@ -155,6 +155,9 @@ pkv_status check_pointers(const pkv_decode_args* a, bool for_merge) {
   if ((int64_t)a->page_size * a->k_row_stride >= (int64_t)1 << 30 ||
       (int64_t)a->page_size * a->v_row_stride >= (int64_t)1 << 30)
     return fail(PKV_ERR_UNSUPPORTED, "page_size * k/v row stride must be below 2^30 bytes");
+  if (a->k_page_stride >= (int64_t)1 << 32 || a->v_page_stride >= (int64_t)1 << 32 ||
+      (a->kv_format == PKV_KV_NVFP4 && (a->kgs_page_stride >= (int64_t)1 << 32 || a->vgs_page_stride >= (int64_t)1 << 32)))
+    return fail(PKV_ERR_UNSUPPORTED, "page strides must be below 2^32 bytes");
   if (!a->k_descale || !a->v_descale || (a->q_format == PKV_Q_E4M3 && !a->q_descale))
     return fail(PKV_ERR_INVALID_ARG, "k/v descale (and q descale for e4m3 q) must be non-NULL");
   if (a->kd_seq_stride < 0 || a->kd_head_stride < 0 || a->vd_seq_stride < 0 || a->vd_head_stride < 0 ||

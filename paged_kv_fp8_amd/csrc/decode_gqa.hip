@@ -226,6 +226,14 @@ __device__ __forceinline__ LaneOffsets lane_offsets(const GqaParams& p, int r16,
   return o;
 }
 
+// Byte offset of page pg in a pool: pg is clamped into [0, num_pages) (so
+// below 2^31) and every page stride is below 2^32 bytes (checked on the
+// host), so one 32 x 32 -> 64-bit product suffices (two scalar multiplies,
+// where a 64-bit product of the signed index takes four and a sign extension).
+__device__ __forceinline__ uint64_t page_off(int64_t pg, int64_t page_stride) {
+  return (uint64_t)(uint32_t)pg * (uint64_t)(uint32_t)page_stride;
+}
+
 // The 13 loads of one 32-key block (keys kb.. clamped to last_key) of kv
 // head g from the two pages pg0 (keys kb..kb+15) and pg1 (kb+16..kb+31).
 // Group t starts at key s_t = min(kb + 16 t, last_key), row s_t & pmask of
@@ -242,8 +250,8 @@ __device__ __forceinline__ RawBlock load_block(const GqaParams& p, int g, int kb
     const uint32_t lim = (uint32_t)max(last_key - st, 0);
     const int64_t pg = t ? pg1 : pg0;
     const uint32_t row = (uint32_t)(st & pmask);
-    const uint8_t* kbase = p.k + pg * p.k_page + (int64_t)g * p.k_head + row * (uint32_t)p.k_row;
-    const uint8_t* vbase = p.v + pg * p.v_page + (int64_t)g * p.v_head + row * (uint32_t)p.v_row;
+    const uint8_t* kbase = p.k + page_off(pg, p.k_page) + (int64_t)g * p.k_head + row * (uint32_t)p.k_row;
+    const uint8_t* vbase = p.v + page_off(pg, p.v_page) + (int64_t)g * p.v_head + row * (uint32_t)p.v_row;
     const uint32_t koff = min(lo.k, lim * (uint32_t)p.k_row + lo.kb);
     r.k[t][0] = *reinterpret_cast<const uint4*>(kbase + koff);
     r.k[t][1] = *reinterpret_cast<const uint4*>(kbase + (koff + 64u));
@@ -294,8 +302,8 @@ __device__ __forceinline__ RawBlock4 load_block4(const GqaParams& p, int g, int 
     const uint32_t lim = (uint32_t)max(last_key - st, 0);
     const int64_t pg = t ? pg1 : pg0;
     const uint32_t row = (uint32_t)(st & pmask);
-    const uint8_t* kbase = p.k + pg * p.k_page + (int64_t)g * p.k_head + row * (uint32_t)p.k_row;
-    const uint8_t* vbase = p.v + pg * p.v_page + (int64_t)g * p.v_head + row * (uint32_t)p.v_row;
+    const uint8_t* kbase = p.k + page_off(pg, p.k_page) + (int64_t)g * p.k_head + row * (uint32_t)p.k_row;
+    const uint8_t* vbase = p.v + page_off(pg, p.v_page) + (int64_t)g * p.v_head + row * (uint32_t)p.v_row;
     const uint32_t koff = min(lo.k, lim * (uint32_t)p.k_row + lo.kb);
     r.k[t] = *reinterpret_cast<const uint4*>(kbase + koff);
     const uint32_t vlim = lim * (uint32_t)p.v_row + lo.vb;
@@ -364,8 +372,8 @@ __device__ __forceinline__ RawBlock6 load_block6(const GqaParams& p, int g, int 
     const uint32_t lim = (uint32_t)max(last_key - st, 0);
     const int64_t pg = t ? pg1 : pg0;
     const uint32_t row = (uint32_t)(st & pmask);
-    const uint8_t* kbase = p.k + pg * p.k_page + (int64_t)g * p.k_head + row * (uint32_t)p.k_row;
-    const uint8_t* vbase = p.v + pg * p.v_page + (int64_t)g * p.v_head + row * (uint32_t)p.v_row;
+    const uint8_t* kbase = p.k + page_off(pg, p.k_page) + (int64_t)g * p.k_head + row * (uint32_t)p.k_row;
+    const uint8_t* vbase = p.v + page_off(pg, p.v_page) + (int64_t)g * p.v_head + row * (uint32_t)p.v_row;
     const uint32_t koff = min(lo.k, lim * (uint32_t)p.k_row + lo.kb);
     for (int j = 0; j < 3; ++j) r.k[t][j] = *reinterpret_cast<const uint2*>(kbase + (koff + 8u * j));
     const uint32_t vlim = lim * (uint32_t)p.v_row + lo.vb;
@@ -650,10 +658,10 @@ __device__ __forceinline__ RawBlockN load_blockN(const GqaParams& p, int g, int 
     const uint32_t lim = (uint32_t)max(last_key - st, 0);
     const int64_t pg = t ? pg1 : pg0;
     const uint32_t row = (uint32_t)(st & pmask);
-    const uint8_t* kbase = p.k + pg * p.k_page + (int64_t)g * p.k_head + row * (uint32_t)p.k_row;
-    const uint8_t* vbase = p.v + pg * p.v_page + (int64_t)g * p.v_head + row * (uint32_t)p.v_row;
-    const uint8_t* ksbase = p.ks + pg * p.ks_page + (int64_t)g * p.ks_head + row * (uint32_t)p.ks_row;
-    const uint8_t* vsbase = p.vs + pg * p.vs_page + (int64_t)g * p.vs_head + row * (uint32_t)p.vs_row;
+    const uint8_t* kbase = p.k + page_off(pg, p.k_page) + (int64_t)g * p.k_head + row * (uint32_t)p.k_row;
+    const uint8_t* vbase = p.v + page_off(pg, p.v_page) + (int64_t)g * p.v_head + row * (uint32_t)p.v_row;
+    const uint8_t* ksbase = p.ks + page_off(pg, p.ks_page) + (int64_t)g * p.ks_head + row * (uint32_t)p.ks_row;
+    const uint8_t* vsbase = p.vs + page_off(pg, p.vs_page) + (int64_t)g * p.vs_head + row * (uint32_t)p.vs_row;
     const uint32_t koff = min(lo.k, lim * (uint32_t)p.k_row + lo.kb);
     r.k[t][0] = *reinterpret_cast<const uint2*>(kbase + koff);
     r.k[t][1] = *reinterpret_cast<const uint2*>(kbase + (koff + 32u));

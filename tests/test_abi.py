@@ -160,6 +160,8 @@ BAD = [
     (dict(kv_format=5, q_format=1, q_descale=1 << 42, k_group_scale=1 << 43, v_group_scale=1 << 44,
           kgs_row_stride=4), -1),
     (dict(kv_format=6), -1),
+    (dict(k_page_stride=1 << 32), -2),  # page offsets are 32 x 32-bit products
+    (dict(v_page_stride=(1 << 32) + 2048), -2),
 ]
 
 
