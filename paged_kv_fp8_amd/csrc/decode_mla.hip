@@ -181,8 +181,8 @@ __device__ __forceinline__ float pair32(float x, bool take_max) {
 // all 64 rows for its PV.
 // With one wave per SIMD nothing overlaps a wave's phases but its own
 // instruction order, so a step's MFMA work is one basic block: PV of the
-// previous block, the loads of a later one, QK^T of this one, and the next
-// block's stage pieces written between the MFMAs.
+// previous block, the next block's stage pieces, the loads of a later one,
+// and QK^T of this one.
 // The 256 threads split a block's loads (the key t >> 3: 16 latent bytes of
 // each 128-value block, 16 rope bytes and the key's 16 scale bytes each),
 // RING blocks ahead of the math in a register ring. The partial-S and P
@@ -514,7 +514,10 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
     };
     const uint8_t* const p_in = lds + kPOffset + lane * 16;
     // PV of the block in stage st; when given the next block's converted
-    // pieces, one of them is written to st_next after each V^T tile
+    // pieces, they are written to st_next after PV's MFMAs are issued (the
+    // LDS serves a wave's accesses in order, so stores placed between the
+    // MFMAs delayed the V^T and K reads behind them: T = 16 261.7 -> 256.7
+    // us, T = 8 142.0 -> 138.8 against one store after each V^T tile)
     auto pv_quarter = [&](const uint8_t* st, uint8_t* st_next, const RawPiece* nr, const bf16x8 (*nc)[8]) {
       u32x4 pb[kLdsRb];
       for (int rb = 0; rb < kLdsRb; ++rb) pb[rb] = *reinterpret_cast<const u32x4*>(p_in + rb * 64 * 16);
@@ -526,8 +529,9 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
         for (int rb = 0; rb < kLdsRb; ++rb)
           oacc[rb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mt % (kPvAhead + 1)],
                                                                 __builtin_bit_cast(bf16x8, pb[rb]), oacc[rb][mt], 0, 0, 0);
-        if (nc) write_piece(st_next, *nr, *nc, mt);
       }
+      if (nc)
+        for (int k = 0; k < 8; ++k) write_piece(st_next, *nr, *nc, k);
     };
 
     // Two barriers per step. Block j: fetched in step j - RING, converted and
