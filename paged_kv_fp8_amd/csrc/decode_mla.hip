@@ -433,9 +433,11 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
     // partial S (sa: the first tile, sb: tile tr; S[key 16 tt + 4 g4 + i][row
     // 16 rb + r16]) of the block in stage st over this wave's quarter of
     // d_qk, written to this wave's partial-S area ([tt][rb][lane]); each K
-    // piece is read kQkAhead pieces ahead of its four MFMAs; the first
-    // tile's partial S is written under the second tile's first k-step. The
-    // next block's rope piece is staged at the start.
+    // piece is read kQkAhead pieces ahead of its four MFMAs; both tiles'
+    // partial S are stored after the last MFMA is issued (stored under the
+    // second tile's first k-step, the first tile's delayed the K reads queued
+    // behind it: T = 16 256.4 -> 253.8 us). The next block's rope piece is
+    // staged at the start.
     auto qk_quarter = [&](const uint8_t* st, uint8_t* st_next, const RawPiece& nr, const bf16x8 (&nc)[8]) {
       f32x4 sa[kLdsRb], sb[kLdsRb];
       bf16x8 pa[kQkAhead + 1];
@@ -454,8 +456,8 @@ __device__ __forceinline__ void mla_lds_item(const MlaParams& p, int item, int t
             sb[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_op, q_op, i == 4 ? f32x4{0.f, 0.f, 0.f, 0.f} : sb[rb],
                                                              0, 0, 0);
         }
-        if (i == 4) put_s(1 - tr_tile, sa);
       }
+      put_s(1 - tr_tile, sa);
       put_s(tr_tile, sb);
     };
     // S of the owned row at this lane's keys of both tiles: the partials of
