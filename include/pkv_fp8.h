@@ -726,9 +726,13 @@ pkv_status pkv_stream_read_probe(const void* src, size_t bytes, int32_t workgrou
  * workgroup's first work item:
  *   loop 0, the one-item form of the kv-head decode, per 32-key block:
  *     0 block start, 1 its fetch issued, 2 its loads landed, 3 processed;
- *   loop 1, the latent staged form, per 32-key step (from the second):
- *     0 step start, 1 loads issued and converted, 2 MFMA phase done,
- *     3 past the first barrier, 4 softmax done, 5 past the second barrier.
+ *   loop 1, the latent kernels (one buffer for both forms):
+ *     the staged form, per 32-key step (from the second): 0 step start,
+ *     1 loads issued and converted, 2 MFMA phase done, 3 past the first
+ *     barrier, 4 softmax done, 5 past the second barrier;
+ *     the pair form, per 16-key block: 0 block start, 1 its fetch issued,
+ *     2 its loads landed, 3 partial S stored, 4 past the exchange barrier,
+ *     5 softmax done, 6 PV issued.
  * Stamps of the last launch of that loop are copied (synchronously) to
  * host_dst, PKV_STAMP_WORDS uint64 values laid out as
  * [workgroup 16][wave 8][step 48][point 8]; entries never written stay as

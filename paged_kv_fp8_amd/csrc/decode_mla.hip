@@ -733,7 +733,8 @@ __device__ __forceinline__ int hrow_base(int row, int lane_off) {
 }
 
 template <bool CAUSAL_TAIL, int HALF>
-__device__ __forceinline__ void mla_pair_item(const MlaParams& p, int item, int tile, int groups, uint8_t* lds) {
+__device__ __forceinline__ void mla_pair_item(const MlaParams& p, int item, int tile, int groups, uint8_t* lds,
+                                              bool first_item) {
   const int w = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;
@@ -842,6 +843,9 @@ __device__ __forceinline__ void mla_pair_item(const MlaParams& p, int item, int 
 
     // this lane's transpose-read piece: key row 4 g4 + r16 / 4, bytes 8 (r16 % 4) ..
     const int tr_base = hrow_base(4 * g4 + (r16 >> 2), 8 * (r16 & 3));
+    // stamps (stamped builds): issue 0 -> 1, wait for the block 1 -> 2, conversion and
+    // partial S 2 -> 3, exchange barrier 3 -> 4, softmax 4 -> 5, PV 5 -> 6
+    PKV_STAMP_VARS
     auto process = [&](const HalfRec& cur, int kb, const int xs) {
       asm volatile("" ::: "memory");
       // the four lanes of a key store the same scales (no branch: a divergent
@@ -868,7 +872,9 @@ __device__ __forceinline__ void mla_pair_item(const MlaParams& p, int item, int 
       f32x4 part;
       for (int i = 0; i < 4; ++i) part[i] = accr[i] + scl[i].x * acc[0][i] + scl[i].y * acc[1][i];
       *reinterpret_cast<f32x4*>(wl + kPairX + xs * 1024 + 16 * lane) = part;
+      PKV_STAMP(3);
       __syncthreads();
+      PKV_STAMP(4);
       const f32x4 other = *reinterpret_cast<const f32x4*>(xl + xs * 1024 + 16 * lane);
       float sv[4];
       for (int i = 0; i < 4; ++i) sv[i] = part[i] + other[i];  // the same sum in both waves
@@ -895,6 +901,7 @@ __device__ __forceinline__ void mla_pair_item(const MlaParams& p, int item, int 
           for (int mt = 0; mt < 8; ++mt) oacc[j][mt] *= corr;
       }
       m_run = m_new;
+      PKV_STAMP(5);
       // ---- O^T += V^T (P * scale)^T for this wave's 256 d_v -------------------
       for (int j = 0; j < 2; ++j) {
         bf16x4 pb;  // P scaled by the block scale of latent block 2 HALF + j
@@ -926,9 +933,17 @@ __device__ __forceinline__ void mla_pair_item(const MlaParams& p, int item, int 
 #pragma unroll
       for (int s = 0; s < kPairStages; ++s) {
         const int kb = kb0 + kBlockKeys * s;
+        PKV_STAMP(0);
         fetch(ring[(s + kPairStages - 1) % kPairStages], kb + kBlockKeys * (kPairStages - 1),
               (s + kPairStages - 1) % kPairStages);
+        PKV_STAMP(1);
+#if PKV_STAMPS
+        asm volatile("" ::"v"(ring[s].sc.x), "v"(ring[s].sc.y));  // the block's last load has landed
+#endif
+        PKV_STAMP(2);
         process(ring[s], kb, s & 1);
+        PKV_STAMP(6);
+        PKV_STAMP_SAVE(r * kPairStages + s, first_item);
       }
     }
   }
@@ -971,11 +986,12 @@ void mla_pair_kernel(MlaParams p, int groups) {
     it_end = p.bin_offsets[blockIdx.x + 1];
   }
   const bool odd = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1;
+  const int it0 = it;
   for (; it < it_end; ++it) {
     if (odd)
-      mla_pair_item<CAUSAL_TAIL, 1>(p, it, blockIdx.y, groups, mla_pair_lds);
+      mla_pair_item<CAUSAL_TAIL, 1>(p, it, blockIdx.y, groups, mla_pair_lds, it == it0);
     else
-      mla_pair_item<CAUSAL_TAIL, 0>(p, it, blockIdx.y, groups, mla_pair_lds);
+      mla_pair_item<CAUSAL_TAIL, 0>(p, it, blockIdx.y, groups, mla_pair_lds, it == it0);
     __syncthreads();  // the next item's query overwrites LDS
   }
 }

@@ -12,6 +12,7 @@ left out (it carries the item's start-up). ``pkv_debug_stamps`` in
   python -m paged_kv_fp8_amd.stamps --build               # compile only (no GPU needed)
   python -m paged_kv_fp8_amd.stamps --config 4            # kv-head loop, fully-fp8 batch
   python -m paged_kv_fp8_amd.stamps --config 5 --q-len 16 # latent staged loop
+  python -m paged_kv_fp8_amd.stamps --config 5 --q-len 1  # latent pair loop
 
 The stamped kernels keep their phases apart with scheduling barriers, so
 they run somewhat slower than the normal build, and the phases cannot
@@ -28,7 +29,15 @@ STAMP_LIB = os.path.join(HERE, "libpkvfp8_stamps.so")
 PHASES = {
     0: ("kv-head one-item loop, per 32-key block", ["issue", "wait", "process"], 4),
     1: ("latent staged loop, per 32-key step", ["loads+convert", "MFMA phase", "barrier 1", "softmax", "barrier 2"], 6),
+    2: ("latent pair loop, per 16-key block", ["issue", "wait", "convert+QK^T", "barrier", "softmax", "PV"], 7),
 }
+# the stamp buffer each loop's kernel writes (pkv_debug_stamps' loop argument):
+# both latent kernels sit in one source and share one
+COPY_LOOP = {0: 0, 1: 1, 2: 1}
+
+
+def phases_for(kernel_name):
+    return {"gqa_decode_kernel": 0, "mla_lds_kernel": 1, "mla_pair_kernel": 2}[kernel_name]
 
 
 def build_stamped():
@@ -79,15 +88,15 @@ def main(argv=None):
     assert native.LIB_PATH == STAMP_LIB, native.LIB_PATH
     over = {} if args.q_len is None else {"q_len": args.q_len}
     w = workload(args.config, **over)
-    loop = 1 if w.kv_format == "mla" else 0
     batch = make_batch(w, device="cuda")
     dec = decode.for_batch(batch, plan=args.plan)
+    loop = phases_for(dec.kernel_name)
     print(f"workload {w.name} (q_len {w.q_len}), plan {dec.plan}, kernel {dec.kernel_name}, library {native.LIB_PATH}",
           flush=True)
     for _ in range(args.runs):
         dec.run()
     torch.cuda.synchronize()
-    print(summarize(native.debug_stamps(loop), loop))
+    print(summarize(native.debug_stamps(COPY_LOOP[loop]), loop))
     return 0
 
 

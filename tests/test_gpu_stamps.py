@@ -13,7 +13,7 @@ import pytest
 import torch
 
 from paged_kv_fp8_amd import decode, native
-from paged_kv_fp8_amd.stamps import PHASES, STAMP_LIB, summarize
+from paged_kv_fp8_amd.stamps import COPY_LOOP, PHASES, STAMP_LIB, phases_for, summarize
 from paged_kv_fp8_amd.workloads import make_batch, workload
 
 
@@ -31,11 +31,12 @@ def _stamped():
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("cfg,over,loop", [(2, {}, 0), (5, {"q_len": 4}, 1)])
+@pytest.mark.parametrize("cfg,over,loop", [(2, {}, 0), (5, {"q_len": 4}, 1), (5, {"q_len": 1}, 2)])
 def test_stamped_library_records_phases_and_matches(cfg, over, loop):
     lib = _stamped()
     batch = make_batch(workload(cfg, **over), device="cuda")
     dec = decode.for_batch(batch)
+    assert phases_for(dec.kernel_name) == loop, dec.kernel_name
     dec.run()
     torch.cuda.synchronize()
     ref_o, ref_l = dec.o.clone(), dec.lse.clone()
@@ -49,7 +50,7 @@ def test_stamped_library_records_phases_and_matches(cfg, over, loop):
     assert torch.equal(dec.o.view(torch.int16), ref_o.view(torch.int16)), "stamped build changed O"
     assert torch.equal(dec.lse, ref_l), "stamped build changed LSE"
     buf = np.zeros(native.PKV_STAMP_WORDS, dtype=np.uint64)
-    assert lib.pkv_debug_stamps(loop, buf.ctypes.data_as(ctypes.c_void_p)) == native.PKV_OK
+    assert lib.pkv_debug_stamps(COPY_LOOP[loop], buf.ctypes.data_as(ctypes.c_void_p)) == native.PKV_OK
     ts = buf.astype(np.int64).reshape(16, 8, 48, 8)
     n = PHASES[loop][2]
     rec = (ts[..., 0] > 0) & (ts[..., n - 1] > 0)
