@@ -821,14 +821,18 @@ __device__ __forceinline__ void mla_pair_item(const MlaParams& p, int item, int 
       for (int u = 0; u < kPageAhead; ++u) pv[u] = page_of(k_begin + kBlockKeys * u);
     auto load_block = [&](int kb, int pg) {
       HalfRec r;
-      const int row = min(kb + r16, last_key) & pmask;
-      const uint8_t* lr = p.lat + (int64_t)pg * p.lat_page + (int64_t)row * p.lat_row + 256 * HALF;
+      // page bases are wave-uniform (scalar); a lane's row offset fits 32 bits
+      // (page_size * row stride < 2^30, checked on the host), so each load is
+      // a scalar base plus one 32-bit offset and an immediate
+      const uint32_t row = (uint32_t)(min(kb + r16, last_key) & pmask);
+      const uint8_t* lat = p.lat + (int64_t)pg * p.lat_page;
+      const uint8_t* rope = p.rope + (int64_t)pg * p.rope_page;
+      const uint8_t* scl = p.scl + (int64_t)pg * p.scl_page;
+      const uint8_t* lr = lat + (row * (uint32_t)p.lat_row + 16u * (uint32_t)g4);
       for (int j = 0; j < 2; ++j)
-        for (int h = 0; h < 2; ++h) r.kl[j][h] = *reinterpret_cast<const uint4*>(lr + 128 * j + 64 * h + 16 * g4);
-      r.kr = *reinterpret_cast<const uint4*>(p.rope + (int64_t)pg * p.rope_page + (int64_t)row * p.rope_row +
-                                             2 * (32 * HALF + 8 * g4));
-      r.sc = *reinterpret_cast<const float2*>(p.scl + (int64_t)pg * p.scl_page + (int64_t)row * p.scl_row +
-                                              8 * HALF);
+        for (int h = 0; h < 2; ++h) r.kl[j][h] = *reinterpret_cast<const uint4*>(lr + (256 * HALF + 128 * j + 64 * h));
+      r.kr = *reinterpret_cast<const uint4*>(rope + (row * (uint32_t)p.rope_row + 16u * (uint32_t)g4) + 64 * HALF);
+      r.sc = *reinterpret_cast<const float2*>(scl + row * (uint32_t)p.scl_row + 8 * HALF);
       return r;
     };
     // page ring: fetch u reads slot u % kPairStages and loads the page of
