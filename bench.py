@@ -355,7 +355,9 @@ def measure_decode(w, args, label=None, plan_kw=None):
     torch.cuda.synchronize()
     eager_us_step = start.elapsed_time(end) * 1e3 / K
     dec_us = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
-    mrg_us = [e[1].elapsed_time(e[2]) * 1e3 for e in ev]
+    # a plan that split no sequence launches no merge: the two events with
+    # nothing between them would time only their own gap
+    mrg_us = [e[1].elapsed_time(e[2]) * 1e3 for e in ev] if decs[0].has_splits else [0.0] * K
     # the decode kernel's duration: K decode launches back to back (pools
     # rotated) between two events, so no launch gap is counted (an event pair
     # around each launch adds the gap in front of it)
